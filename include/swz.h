@@ -1,0 +1,192 @@
+/*
+ * swz.h -- swizzled on-chip tile movement for AMD gfx950 (MI355X).
+ *
+ * C ABI of libswz.so.  Plain pointers and sizes only.  Every call that moves
+ * data is asynchronous on the caller's HIP stream (a hipStream_t passed as
+ * void*; NULL is the default stream).  Device buffers belong to the caller;
+ * the library allocates no device memory and keeps no pointer after a call
+ * returns.  Errors are negative return codes, detected on the host before
+ * any launch; no call aborts or throws.  All calls are thread-safe.
+ *
+ * The method follows four pages on CuTe's swizzle:
+ *   "NVIDIA CuTe Swizzle", "CuTe Swizzle 学习手册", "cutlass 入门",
+ *   "CUDA 013 - Swizzle 的工作原理".
+ */
+#ifndef SWZ_H
+#define SWZ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Swizzle<B,M,S> on element offsets: the B-bit field at bit M+S is XORed
+ * into the B-bit field at bit M ("CuTe Swizzle 学习手册", section on the
+ * swizzle formula; "CUDA 013 - Swizzle 的工作原理", section 计算公式, where
+ * the same triple is written (base, bits, shift) = (M, B, S)).  M counts
+ * elements: 2^M consecutive elements stay together. */
+typedef struct swz_params {
+    int32_t B;
+    int32_t M;
+    int32_t S;
+} swz_params;
+
+enum swz_status {
+    SWZ_OK = 0,
+    SWZ_EINVAL = -1,       /* bad argument: size, pointer, alignment, overlap, parameters */
+    SWZ_EUNSUPPORTED = -2, /* valid request this build does not handle */
+    SWZ_EHIP = -3          /* the HIP runtime reported an error at launch */
+};
+
+/* Layout of a tile in LDS.  PAD and PLAIN are the ablations: PAD adds one
+ * element (4-byte elements) or one 16-byte vector (2-byte elements) to each
+ * row ("CUDA 013 - Swizzle 的工作原理", section 如何避免 Bank Conflict, the
+ * 32x33 array); PLAIN is the row-major tile with no remapping. */
+enum swz_layout { SWZ_LAYOUT_SWIZZLE = 0, SWZ_LAYOUT_PAD = 1, SWZ_LAYOUT_PLAIN = 2 };
+
+/* How a staged tile is read back from LDS.
+ *  SCALAR_COL : 4-byte elements, 32x32 tile, each lane reads one element
+ *               of a column (two columns per 64-lane wave).
+ *  B64_4X4    : 2-byte elements, 64x64 tile, each lane reads 8-byte row
+ *               pieces of 8 rows and transposes 4x4 blocks in registers.
+ *  B128_8X8   : 2-byte elements, 64x128 tile, each lane reads 16-byte row
+ *               pieces of 8 rows and transposes an 8x8 block in registers.
+ *  MFMA_16X16X32 : operand staging; see swz_stage_operand.
+ *  AUTO       : 4-byte -> SCALAR_COL; 2-byte -> B128_8X8 when cols <= 128,
+ *               else B64_4X4. */
+enum swz_read_kind {
+    SWZ_READ_AUTO = -1,
+    SWZ_READ_SCALAR_COL = 0,
+    SWZ_READ_B64_4X4 = 1,
+    SWZ_READ_B128_8X8 = 2,
+    SWZ_READ_MFMA_16X16X32 = 3
+};
+
+enum swz_frag_kind { SWZ_FRAG_MFMA_F32_16X16X32_BF16 = 0 };
+
+/* What a call will do: tile shape, read kind, LDS layout and parameters. */
+typedef struct swz_plan_info {
+    int32_t read_kind;   /* resolved read kind */
+    int32_t tile_rows;   /* source rows per tile */
+    int32_t tile_cols;   /* source columns per tile */
+    int32_t layout;      /* as requested */
+    swz_params params;   /* swizzle actually used (B = 0 for PAD / PLAIN) */
+    int32_t pad_elems;   /* extra elements per LDS row (PAD only) */
+    int32_t lds_bytes;   /* LDS bytes one tile occupies */
+    int32_t vec_bytes;   /* width of the LDS stores of the staging pass */
+    int32_t aligned;     /* 1 if the 16-byte vector path is used */
+} swz_plan_info;
+
+/* out[i] = Swizzle<B,M,S>(in[i]) for i < n, on the 32-bit bit patterns
+ * ("CuTe Swizzle 学习手册", swizzle formula; "CUDA 013 - Swizzle 的工作原理",
+ * section 计算公式).
+ *   d_in, d_out : device int32 arrays of n elements; may be the same
+ *                 pointer (in place) but must not otherwise overlap.
+ *   p           : B, M, S >= 0 and B + M + S <= 32; B = 0 is the identity.
+ * Errors: SWZ_EINVAL for n < 0, NULL with n > 0, partial overlap, or
+ * parameters out of range. */
+int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p, void* stream);
+
+/* dst = transpose of src: src is [rows][cols] row-major, dst is
+ * [cols][rows] row-major (the column-major image of src), bit-exact.  Tiles
+ * are loaded with coalesced row reads into LDS in the requested layout, read
+ * back along columns, and written out with coalesced row writes
+ * ("CuTe Swizzle 学习手册", typical scenario: column access of a row-major
+ * tile; "CUDA 013 - Swizzle 的工作原理", sections 如何避免 Bank Conflict and
+ * Swizzle 技术).  Exactly swz_convert_layout with batch = 1.
+ *   elem_bytes : 2 or 4.
+ *   layout     : enum swz_layout.
+ *   read_kind  : enum swz_read_kind (AUTO picks by element size and width).
+ *   p_or_null  : swizzle to use with SWZ_LAYOUT_SWIZZLE, or NULL to let
+ *                swz_choose pick; ignored for PAD and PLAIN.
+ * Any rows, cols >= 0 are accepted (partial edge tiles are handled); 0 is a
+ * no-op.  src and dst must not overlap; they must be aligned to elem_bytes.
+ * Errors: SWZ_EINVAL (sizes, NULL, overlap, misalignment, a read kind that
+ * does not fit elem_bytes, parameters that split a vector or leave the tile). */
+int swz_transpose(const void* d_src, void* d_dst, int64_t rows, int64_t cols, int32_t elem_bytes,
+                  int32_t layout, int32_t read_kind, const swz_params* p_or_null, void* stream);
+
+/* Batched layout conversion src[batch][rows][cols] -> dst[batch][cols][rows],
+ * each batch entry transposed as in swz_transpose; same arguments and errors. */
+int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, int64_t rows, int64_t cols,
+                       int32_t elem_bytes, int32_t layout, int32_t read_kind,
+                       const swz_params* p_or_null, void* stream);
+
+/* GEMM operand staging without compute.  d_src is a K-contiguous operand
+ * [mn][k] (A row-major, or B column-major, which is B^T row-major), 16-bit
+ * elements.  Tiles of 256 x 64 are loaded coalesced into LDS in the requested
+ * layout and read back in the operand-register pattern of the 16x16x32
+ * 16-bit matrix instruction: lane l holds row l%16 of a 16-row block and
+ * k = 8*(l/16) .. +7 of a 32-wide k step.  Each 64-lane fragment is written
+ * in lane order:
+ *   d_frag[i][j][l][e] = src[16*i + l%16][32*j + 8*(l/16) + e],
+ *   i < mn/16, j < k/32, l < 64, e < 8  (same byte count as src).
+ * The pages' version of this step is the ldmatrix / WGMMA read of a swizzled
+ * tile ("NVIDIA CuTe Swizzle", on cp.async and ldmatrix; "CuTe Swizzle
+ * 学习手册", usage steps 3 and 5).
+ *   elem_bytes must be 2; frag_kind must be SWZ_FRAG_MFMA_F32_16X16X32_BF16.
+ *   mn must be a multiple of 16 and k of 32 (partial 256x64 tiles are fine).
+ *   d_src and d_frag must be 16-byte aligned and must not overlap.
+ * Errors: SWZ_EINVAL otherwise. */
+int swz_stage_operand(const void* d_src, void* d_frag, int64_t mn, int64_t k, int32_t elem_bytes,
+                      int32_t frag_kind, int32_t layout, const swz_params* p_or_null, void* stream);
+
+/* Host only.  The swizzle the library uses for a tile of tile_rows x
+ * tile_cols elements of elem_bytes, staged by vec_bytes-wide stores and read
+ * back by read_kind, under the built-in gfx950 LDS bank model:
+ * M = log2(vec_bytes / elem_bytes), B = log2(vectors per bank row) (bounded
+ * by the tile), S the smallest shift >= B with the fewest predicted
+ * bank-conflict cycles over the kernel's write and read lane patterns
+ * ("NVIDIA CuTe Swizzle", derivation of the three parameters; "CUDA 013 -
+ * Swizzle 的工作原理", section CuTe 通用 swizzle 映射规则解析).  Only the
+ * (elem_bytes, vec_bytes, tile, read_kind) combinations the kernels use are
+ * accepted; others return SWZ_EUNSUPPORTED. */
+int swz_choose(int32_t elem_bytes, int32_t vec_bytes, int32_t tile_rows, int32_t tile_cols,
+               int32_t read_kind, swz_params* out);
+
+/* Host only.  Predicted conflict cycles (write + read, summed over one
+ * tile) of the kernel pattern for read_kind under the built-in bank model,
+ * for the given layout and parameters (params ignored unless SWIZZLE). */
+int swz_predict_conflicts(int32_t read_kind, int32_t layout, const swz_params* p_or_null,
+                          int64_t* write_cycles, int64_t* read_cycles);
+
+/* Host only.  The LDS accesses one tile of the kernel for read_kind issues,
+ * as byte addresses per lane: the staging stores (is_write = 1) or the reads
+ * (is_write = 0), one 64-lane access after another (all waves, all steps),
+ * in the given layout.  Writes min(count, max_accesses) x 64 addresses to
+ * addrs (int32, -1 = lane idle), the total count to *n_accesses and the
+ * bytes per lane to *width.  Lets tests and the bank microbenchmark check
+ * the exact patterns the kernels use. */
+int swz_kernel_accesses(int32_t read_kind, int32_t layout, const swz_params* p_or_null, int32_t is_write,
+                        int32_t* addrs, int32_t max_accesses, int32_t* n_accesses, int32_t* width);
+
+/* Host only.  Fill *out with what swz_convert_layout (op = 0) or
+ * swz_stage_operand (op = 1) would do for these arguments, without
+ * launching anything; pointers are not inspected (aligned is reported for
+ * 16-byte aligned pointers).  Same validation and errors as the call. */
+int swz_plan(int32_t op, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t layout,
+             int32_t read_kind, const swz_params* p_or_null, swz_plan_info* out);
+
+/* Host only.  Static text for a status code. */
+const char* swz_strerror(int status);
+
+/* LDS bank microbenchmark (diagnostic; used to measure the bank model the
+ * chooser relies on).  Launches n_patterns workgroups of `waves` 64-lane
+ * waves.  Workgroup g runs pattern g: lane l of every wave accesses LDS byte
+ * d_addrs[64*g + l] (masked into the probe's 64 KiB LDS window and aligned
+ * down to width_bytes) if bit l of d_masks[g] is set, with ds_read_b32/b64/
+ * b128 (is_write = 0) or ds_write_b32/b64/b128 (is_write = 1), 8 accesses
+ * per iteration for `iters` iterations, and writes the wave's elapsed
+ * shader-clock cycles to d_cycles[g * waves + w].
+ *   width_bytes: 4, 8 or 16; waves: 1..16; iters: 1..1<<20.
+ * Errors: SWZ_EINVAL on any other value or NULL pointer. */
+int swz_lds_probe(const uint32_t* d_addrs, const uint64_t* d_masks, int32_t n_patterns,
+                  int32_t width_bytes, int32_t is_write, int32_t iters, int32_t waves,
+                  uint64_t* d_cycles, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWZ_H */

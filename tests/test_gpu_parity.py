@@ -1,0 +1,242 @@
+"""Bit-exact parity of the HIP path against the CPU oracle (needs a GPU).
+
+Every call goes through the C ABI (libswz.so) via the thin ctypes binding.
+Inputs come from the seeded generators in ``workloads``; expected values from
+``oracle`` only.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+torch = pytest.importorskip("torch")
+T = pytest.importorskip("tiled_movement_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+SIGNED = {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32, np.dtype(np.int32): np.int32}
+
+
+def to_dev(a):
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(SIGNED[a.dtype])).to(DEV)
+
+
+def from_dev(t, like):
+    return t.cpu().numpy().view(like.dtype)
+
+
+def announce(*what):
+    print("case:", *what, flush=True)
+
+
+# ------------------------------------------------------------------ map
+
+
+def test_map_every_triple_full_range():
+    x = W.map_offsets()
+    xin = to_dev(x)
+    out = torch.empty_like(xin)
+    for B, M, S in W.map_triples():
+        T.swz_map(xin, out, x.size, (B, M, S))
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(out, x), O.swizzle_map(x, B, M, S)), (B, M, S)
+
+
+def test_map_worked_example_and_edges():
+    announce("map edges")
+    x = W.map_offsets(4099)
+    xin = to_dev(x)
+    out = torch.empty_like(xin)
+    T.swz_map(xin, out, x.size, (5, 0, 6))
+    torch.cuda.synchronize()
+    got = from_dev(out, x)
+    assert got[673] == 683
+    assert np.array_equal(got, O.swizzle_map(x, 5, 0, 6))
+    # misaligned (4-byte offset) pointers take the scalar path; odd length
+    T.swz_map(xin[1:], out[1:], x.size - 1, (3, 2, 4))
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out, x)[1:], O.swizzle_map(x[1:], 3, 2, 4))
+    # in place
+    y = xin.clone()
+    T.swz_map(y, y, x.size, (4, 1, 5))
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(y, x), O.swizzle_map(x, 4, 1, 5))
+    # identity and the whole 32-bit range of bit patterns
+    rng = np.random.default_rng(11)
+    z = rng.integers(-(2**31), 2**31, size=1000, dtype=np.int64).astype(np.int32)
+    zin = to_dev(z)
+    zout = torch.empty_like(zin)
+    for p in [(0, 0, 0), (5, 4, 7), (8, 16, 8), (1, 30, 1)]:
+        T.swz_map(zin, zout, z.size, p)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(zout, z), O.swizzle_map(z, *p)), p
+    T.swz_map(zin, zout, 0, (5, 0, 5))  # n = 0 is a no-op
+
+
+# ----------------------------------------------------------- transposes
+
+KINDS = [
+    (T.READ_SCALAR_COL, 4, 32, 32, W.fp32_matrix),
+    (T.READ_B64_4X4, 2, 64, 64, W.fp16_matrix),
+    (T.READ_B128_8X8, 2, 64, 128, lambda r, c, seed: W.bf16_tensor((r, c), seed=seed)),
+]
+LAYOUTS = ["swizzle", "pad", "plain"]
+
+
+def shapes_for(tr, tc):
+    return [
+        (3 * tr, 2 * tc),  # whole tiles
+        (2 * tr + 5, 3 * tc + 3),  # ragged tails in both directions
+        (tr - 1, tc + 1),
+        (1, 1),
+        (1, 5 * tc + 7),
+        (4 * tr + 3, 1),
+        (0, 7),
+        (7, 0),
+    ]
+
+
+def check_transpose(a, esz, layout, kind, params=None):
+    rows, cols = a.shape
+    src = to_dev(a)
+    dst = torch.empty((cols, rows), dtype=src.dtype, device=DEV)
+    T.swz_transpose(src, dst, rows, cols, esz, layout, kind, params)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(dst, a), O.transpose(a)), (a.shape, layout, kind, params)
+
+
+@pytest.mark.parametrize("kind,esz,tr,tc,gen", KINDS)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_transpose_shapes(kind, esz, tr, tc, gen, layout):
+    for seed, (rows, cols) in enumerate(shapes_for(tr, tc)):
+        announce("transpose", kind, layout, rows, cols)
+        check_transpose(gen(rows, cols, seed=seed), esz, layout, kind)
+
+
+@pytest.mark.parametrize("kind,esz,tr,tc,gen", KINDS)
+def test_transpose_unaligned_pointers(kind, esz, tr, tc, gen):
+    """Sources and destinations one element off a 16-byte boundary."""
+    rows, cols = 2 * tr + 8, 2 * tc + 8
+    a = gen(rows, cols, seed=3)
+    flat = to_dev(a.reshape(-1))
+    buf = torch.empty(a.size + 1, dtype=flat.dtype, device=DEV)
+    buf[1:] = flat
+    out = torch.empty(a.size + 1, dtype=flat.dtype, device=DEV)
+    announce("unaligned", kind)
+    T.swz_transpose(buf[1:], out[1:], rows, cols, esz, "swizzle", kind)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out[1:], a).reshape(cols, rows), O.transpose(a))
+
+
+@pytest.mark.parametrize("kind,esz,tr,tc,gen", KINDS)
+def test_transpose_any_valid_swizzle(kind, esz, tr, tc, gen):
+    """The swizzle only moves data inside LDS: every admissible (B, M, S)
+    gives the same bits out."""
+    rows, cols = 2 * tr + 3, 2 * tc + 5
+    a = gen(rows, cols, seed=4)
+    m_min = {4: 0, 2: 3}[esz]
+    log_tile = (tr * tc).bit_length() - 1
+    rng = np.random.default_rng(kind)
+    triples = [(B, M, S) for B in range(1, 6) for M in range(m_min, 6) for S in range(1, 9)
+               if M + B <= log_tile]
+    for idx in rng.choice(len(triples), size=min(12, len(triples)), replace=False):
+        announce("params", kind, triples[idx])
+        check_transpose(a, esz, "swizzle", kind, triples[idx])
+
+
+def test_convert_layout_batches():
+    cases = [
+        (T.READ_B128_8X8, 2, W.bf16_tensor((3, 200, 128), seed=5)),
+        (T.READ_B128_8X8, 2, W.bf16_tensor((2, 64, 100), seed=6)),  # ragged rows of 100
+        (T.READ_B64_4X4, 2, W.bf16_tensor((2, 70, 130), seed=7)),
+        (T.READ_SCALAR_COL, 4, W.fp32_matrix(3 * 40, 50, seed=8).reshape(3, 40, 50)),
+    ]
+    for kind, esz, a in cases:
+        for layout in LAYOUTS:
+            announce("convert", kind, layout, a.shape)
+            b, r, c = a.shape
+            src = to_dev(a)
+            dst = torch.empty((b, c, r), dtype=src.dtype, device=DEV)
+            T.swz_convert_layout(src, dst, b, r, c, esz, layout, kind)
+            torch.cuda.synchronize()
+            assert np.array_equal(from_dev(dst, a), O.convert_layout(a))
+
+
+def test_auto_read_kind():
+    a = W.bf16_tensor((4, 96, 128), seed=9)
+    src = to_dev(a)
+    dst = torch.empty((4, 128, 96), dtype=src.dtype, device=DEV)
+    T.swz_convert_layout(src, dst, 4, 96, 128, 2)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(dst, a), O.convert_layout(a))
+
+
+# ------------------------------------------------------- operand staging
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_stage_operand_shapes(layout):
+    for mn, k in [(16, 32), (256, 64), (272, 96), (512, 4096 // 8), (48, 608)]:
+        a, bt = W.bf16_operands(mn, mn, k, seed=mn + k)
+        for op in (a, bt):
+            announce("stage", layout, mn, k)
+            src = to_dev(op)
+            frag = torch.empty(op.size, dtype=src.dtype, device=DEV)
+            T.swz_stage_operand(src, frag, mn, k, layout=layout)
+            torch.cuda.synchronize()
+            ref = O.stage_operand(op).reshape(-1)
+            assert np.array_equal(from_dev(frag, op), ref), (mn, k, layout)
+
+
+def test_stage_operand_any_valid_swizzle():
+    a, _ = W.bf16_operands(272, 16, 96, seed=12)
+    src = to_dev(a)
+    ref = O.stage_operand(a).reshape(-1)
+    for p in [(3, 3, 3), (3, 3, 4), (4, 3, 4), (2, 4, 7), (5, 3, 6), (1, 3, 1)]:
+        frag = torch.empty(a.size, dtype=src.dtype, device=DEV)
+        T.swz_stage_operand(src, frag, 272, 96, params=p)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(frag, a), ref), p
+
+
+# --------------------------------------------- full sizes of the workloads
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_full_fp32_4096(layout):
+    announce("full fp32 4096", layout)
+    check_transpose(W.fp32_matrix(4096, 4096, seed=0), 4, layout, T.READ_AUTO)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_full_fp16_8192(layout):
+    announce("full fp16 8192", layout)
+    check_transpose(W.fp16_matrix(8192, 8192, seed=0), 2, layout, T.READ_B64_4X4)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_full_bf16_convert(layout):
+    announce("full bf16 convert", layout)
+    a = W.bf16_tensor((64, 4096, 128), seed=0)
+    src = to_dev(a)
+    dst = torch.empty((64, 128, 4096), dtype=src.dtype, device=DEV)
+    T.swz_convert_layout(src, dst, 64, 4096, 128, 2, layout, T.READ_B128_8X8)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(dst, a), O.convert_layout(a))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_full_operand_staging(layout):
+    announce("full staging", layout)
+    a, bt = W.bf16_operands(8192, 8192, 4096, seed=0)
+    for op in (a, bt):
+        src = to_dev(op)
+        frag = torch.empty(op.size, dtype=src.dtype, device=DEV)
+        T.swz_stage_operand(src, frag, op.shape[0], op.shape[1], layout=layout)
+        torch.cuda.synchronize()
+        got = from_dev(frag, op).reshape(op.shape[0] // 16, op.shape[1] // 32, 64, 8)
+        assert np.array_equal(got, O.stage_operand(op))

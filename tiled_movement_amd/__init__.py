@@ -1,0 +1,222 @@
+"""Python binding of libswz.so: swizzled LDS tile movement on gfx950.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+libswz.so; there is no Python or CPU fallback, and importing this package
+raises if the library has not been built (``python tiled_movement_amd/build.py``).
+
+Functions take torch tensors (or raw device addresses as ints) and the
+library's enum values; they run on the current torch stream unless a stream
+is given, and raise ``SwzError`` on a negative status.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libswz.so")
+
+# enum values of include/swz.h
+SWZ_OK, SWZ_EINVAL, SWZ_EUNSUPPORTED, SWZ_EHIP = 0, -1, -2, -3
+LAYOUT_SWIZZLE, LAYOUT_PAD, LAYOUT_PLAIN = 0, 1, 2
+READ_AUTO, READ_SCALAR_COL, READ_B64_4X4, READ_B128_8X8, READ_MFMA_16X16X32 = -1, 0, 1, 2, 3
+FRAG_MFMA_F32_16X16X32_BF16 = 0
+LAYOUTS = {"swizzle": LAYOUT_SWIZZLE, "pad": LAYOUT_PAD, "plain": LAYOUT_PLAIN}
+
+EXPORTS = (
+    "swz_map",
+    "swz_transpose",
+    "swz_convert_layout",
+    "swz_stage_operand",
+    "swz_choose",
+    "swz_predict_conflicts",
+    "swz_kernel_accesses",
+    "swz_plan",
+    "swz_strerror",
+    "swz_lds_probe",
+)
+
+
+class SwzError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        super().__init__(f"{call}: {strerror(status)} ({status})")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("M", ctypes.c_int32), ("S", ctypes.c_int32)]
+
+    def tuple(self) -> Tuple[int, int, int]:
+        return (self.B, self.M, self.S)
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("read_kind", ctypes.c_int32),
+        ("tile_rows", ctypes.c_int32),
+        ("tile_cols", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("params", Params),
+        ("pad_elems", ctypes.c_int32),
+        ("lds_bytes", ctypes.c_int32),
+        ("vec_bytes", ctypes.c_int32),
+        ("aligned", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {
+            "read_kind": self.read_kind,
+            "tile": (self.tile_rows, self.tile_cols),
+            "layout": self.layout,
+            "params": self.params.tuple(),
+            "pad_elems": self.pad_elems,
+            "lds_bytes": self.lds_bytes,
+            "vec_bytes": self.vec_bytes,
+            "aligned": bool(self.aligned),
+        }
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python tiled_movement_amd/build.py` "
+            "(there is no fallback path)"
+        )
+    try:  # bind to the HIP runtime torch already loaded, if torch is present
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    P = ctypes.POINTER
+    lib.swz_map.argtypes = [vp, vp, i64, Params, vp]
+    lib.swz_transpose.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
+    lib.swz_convert_layout.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, P(Params), vp]
+    lib.swz_stage_operand.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
+    lib.swz_choose.argtypes = [i32, i32, i32, i32, i32, P(Params)]
+    lib.swz_predict_conflicts.argtypes = [i32, i32, P(Params), P(i64), P(i64)]
+    lib.swz_kernel_accesses.argtypes = [i32, i32, P(Params), i32, P(i32), i32, P(i32), P(i32)]
+    lib.swz_plan.argtypes = [i32, i64, i64, i32, i32, i32, P(Params), P(PlanInfo)]
+    lib.swz_strerror.argtypes = [ctypes.c_int]
+    lib.swz_strerror.restype = ctypes.c_char_p
+    lib.swz_lds_probe.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    for name in EXPORTS:
+        if name != "swz_strerror":
+            getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.swz_strerror(status).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != SWZ_OK:
+        raise SwzError(status, call)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    for t in tensors:
+        if hasattr(t, "is_cuda") and t.is_cuda:
+            import torch
+
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _params(p) -> Optional[ctypes.pointer]:
+    if p is None:
+        return None
+    if isinstance(p, Params):
+        return ctypes.pointer(p)
+    B, M, S = p
+    return ctypes.pointer(Params(B, M, S))
+
+
+def _layout(layout) -> int:
+    return LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+
+
+def swz_map(inp, out, n: int, params, stream=None) -> None:
+    B, M, S = params
+    _check(lib.swz_map(_ptr(inp), _ptr(out), n, Params(B, M, S), _stream(stream, inp, out)), "swz_map")
+
+
+def swz_transpose(src, dst, rows: int, cols: int, elem_bytes: int, layout="swizzle", read_kind: int = READ_AUTO,
+                  params=None, stream=None) -> None:
+    _check(lib.swz_transpose(_ptr(src), _ptr(dst), rows, cols, elem_bytes, _layout(layout), read_kind,
+                             _params(params), _stream(stream, src, dst)), "swz_transpose")
+
+
+def swz_convert_layout(src, dst, batch: int, rows: int, cols: int, elem_bytes: int, layout="swizzle",
+                       read_kind: int = READ_AUTO, params=None, stream=None) -> None:
+    _check(lib.swz_convert_layout(_ptr(src), _ptr(dst), batch, rows, cols, elem_bytes, _layout(layout), read_kind,
+                                  _params(params), _stream(stream, src, dst)), "swz_convert_layout")
+
+
+def swz_stage_operand(src, frag, mn: int, k: int, elem_bytes: int = 2, frag_kind: int = FRAG_MFMA_F32_16X16X32_BF16,
+                      layout="swizzle", params=None, stream=None) -> None:
+    _check(lib.swz_stage_operand(_ptr(src), _ptr(frag), mn, k, elem_bytes, frag_kind, _layout(layout),
+                                 _params(params), _stream(stream, src, frag)), "swz_stage_operand")
+
+
+def swz_choose(elem_bytes: int, vec_bytes: int, tile_rows: int, tile_cols: int, read_kind: int) -> Tuple[int, int, int]:
+    out = Params()
+    _check(lib.swz_choose(elem_bytes, vec_bytes, tile_rows, tile_cols, read_kind, ctypes.byref(out)), "swz_choose")
+    return out.tuple()
+
+
+def swz_predict_conflicts(read_kind: int, layout="swizzle", params=None) -> Tuple[int, int]:
+    w, r = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.swz_predict_conflicts(read_kind, _layout(layout), _params(params), ctypes.byref(w), ctypes.byref(r)),
+           "swz_predict_conflicts")
+    return w.value, r.value
+
+
+def swz_kernel_accesses(read_kind: int, layout="swizzle", params=None, is_write: int = 0):
+    """List of (addresses[64], width) for one tile of the kernel; -1 = idle lane."""
+    n, w = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.swz_kernel_accesses(read_kind, _layout(layout), _params(params), is_write, None, 0, ctypes.byref(n),
+                                   ctypes.byref(w)), "swz_kernel_accesses")
+    buf = (ctypes.c_int32 * (64 * max(n.value, 1)))()
+    _check(lib.swz_kernel_accesses(read_kind, _layout(layout), _params(params), is_write, buf, n.value,
+                                   ctypes.byref(n), ctypes.byref(w)), "swz_kernel_accesses")
+    flat = list(buf)
+    return [(flat[64 * i:64 * i + 64], w.value) for i in range(n.value)]
+
+
+def swz_plan(op: int, rows: int, cols: int, elem_bytes: int, layout="swizzle", read_kind: int = READ_AUTO,
+             params=None) -> dict:
+    out = PlanInfo()
+    _check(lib.swz_plan(op, rows, cols, elem_bytes, _layout(layout), read_kind, _params(params), ctypes.byref(out)),
+           "swz_plan")
+    return out.as_dict()
+
+
+def swz_strerror(status: int) -> str:
+    return strerror(status)
+
+
+def swz_lds_probe(addrs, masks, n_patterns: int, width_bytes: int, is_write: int, iters: int, waves: int, cycles,
+                  stream=None) -> None:
+    _check(lib.swz_lds_probe(_ptr(addrs), _ptr(masks), n_patterns, width_bytes, is_write, iters, waves,
+                             _ptr(cycles), _stream(stream, addrs, masks, cycles)), "swz_lds_probe")
+
+
+# Status-returning raw entry points, for callers that test error paths.
+raw = lib

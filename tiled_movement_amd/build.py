@@ -1,0 +1,76 @@
+"""Build libswz.so in-tree with hipcc for gfx950.
+
+Usage: python tiled_movement_amd/build.py [--verbose]
+
+Run by path (not with -m): importing the package loads the library, which
+may not exist yet.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libswz.so")
+
+SOURCES = [
+    "capi.cpp",
+    "chooser.cpp",
+    "bank_model.cpp",
+    "kernels_tile.hip",
+    "kernels_map.hip",
+    "lds_probe.hip",
+]
+
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def flags():
+    return [
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-fvisibility=hidden",
+        "-Wall",
+        "-Wno-unused-function",
+        # Packed fp32 VALU ops stay off: the path has no float arithmetic,
+        # and the compiler must not introduce them.
+        "-Xclang",
+        "-target-feature",
+        "-Xclang",
+        "-packed-fp32-ops",
+        f"-I{INCLUDE}",
+        f"-I{CSRC}",
+    ]
+
+
+def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
+    """Compile every source into one shared library; returns its path."""
+    cmd = [hipcc()] + flags() + list(extra) + ["-shared", "-o", out + ".tmp"]
+    for s in SOURCES:
+        path = os.path.join(CSRC, s)
+        # hipcc compiles .cpp as HIP too; the host files include hip_runtime.h.
+        cmd += ["-x", "hip", path]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

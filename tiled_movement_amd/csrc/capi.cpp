@@ -1,0 +1,230 @@
+// C ABI of libswz.so: argument checks, parameter choice and launches.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "chooser.h"
+#include "launch.h"
+#include "swz.h"
+
+#define SWZ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using swz::KindInfo;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const auto pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + static_cast<uintptr_t>(bbytes) && pb < pa + static_cast<uintptr_t>(abytes);
+}
+
+int ilog2(int64_t v) {
+    int r = -1;
+    while (v > 0) {
+        v >>= 1;
+        ++r;
+    }
+    return r;
+}
+
+// Resolve read kind, layout and parameters into a plan; shared by the calls
+// and by swz_plan.
+int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, int32_t read_kind,
+              const swz_params* p, bool aligned, swz_plan_info* out) {
+    if (layout < SWZ_LAYOUT_SWIZZLE || layout > SWZ_LAYOUT_PLAIN) return SWZ_EINVAL;
+    int kind = read_kind;
+    if (op == 0) {
+        if (esz != 2 && esz != 4) return SWZ_EINVAL;
+        if (kind == SWZ_READ_AUTO) kind = esz == 4 ? SWZ_READ_SCALAR_COL : (cols <= 128 ? SWZ_READ_B128_8X8 : SWZ_READ_B64_4X4);
+        if (kind == SWZ_READ_MFMA_16X16X32) return SWZ_EINVAL;
+    } else {
+        if (esz != 2) return SWZ_EINVAL;
+        if (kind != SWZ_READ_AUTO && kind != SWZ_READ_MFMA_16X16X32) return SWZ_EINVAL;
+        kind = SWZ_READ_MFMA_16X16X32;
+    }
+    KindInfo k;
+    if (!swz::kind_info(kind, &k)) return SWZ_EINVAL;
+    if (k.esz != esz) return SWZ_EINVAL;
+
+    swz_params q{0, 0, 0};
+    int pad = 0;
+    if (layout == SWZ_LAYOUT_SWIZZLE) {
+        if (p) {
+            if (!swz::params_ok_for_kind(kind, *p)) return SWZ_EINVAL;
+            q = *p;
+        } else {
+            q = swz::cached_choice(kind);
+        }
+    } else if (layout == SWZ_LAYOUT_PAD) {
+        pad = swz::pad_elems(kind);
+    }
+    std::memset(out, 0, sizeof(*out));
+    out->read_kind = kind;
+    out->tile_rows = k.tr;
+    out->tile_cols = k.tc;
+    out->layout = layout;
+    out->params = q;
+    out->pad_elems = pad;
+    out->lds_bytes = k.tr * (k.tc + pad) * k.esz;
+    out->vec_bytes = k.vec;
+    out->aligned = aligned ? 1 : 0;
+    (void)rows;
+    return SWZ_OK;
+}
+
+swz::LdsLayout layout_of(const swz_plan_info& pl) {
+    return swz::LdsLayout{static_cast<uint32_t>(pl.tile_cols + pl.pad_elems), static_cast<uint32_t>(pl.params.B),
+                          static_cast<uint32_t>(pl.params.M), static_cast<uint32_t>(pl.params.S)};
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SWZ_OK : SWZ_EHIP; }
+
+}  // namespace
+
+SWZ_API const char* swz_strerror(int status) {
+    switch (status) {
+        case SWZ_OK: return "ok";
+        case SWZ_EINVAL: return "invalid argument";
+        case SWZ_EUNSUPPORTED: return "unsupported request";
+        case SWZ_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+SWZ_API int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p, void* stream) {
+    if (n < 0) return SWZ_EINVAL;
+    if (p.B < 0 || p.M < 0 || p.S < 0 || static_cast<int64_t>(p.B) + p.M + p.S > 32) return SWZ_EINVAL;
+    if (n == 0) return SWZ_OK;
+    if (!d_in || !d_out) return SWZ_EINVAL;
+    if (reinterpret_cast<uintptr_t>(d_in) % 4 || reinterpret_cast<uintptr_t>(d_out) % 4) return SWZ_EINVAL;
+    int64_t bytes;
+    if (!mul_ok(n, 4, &bytes)) return SWZ_EINVAL;
+    if (d_in != d_out && overlaps(d_in, bytes, d_out, bytes)) return SWZ_EINVAL;
+    return hip_status(swz::launch_map(d_in, d_out, n, p, static_cast<hipStream_t>(stream)));
+}
+
+SWZ_API int swz_plan(int32_t op, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t layout, int32_t read_kind,
+                     const swz_params* p_or_null, swz_plan_info* out) {
+    if (!out || (op != 0 && op != 1) || rows < 0 || cols < 0) return SWZ_EINVAL;
+    if (op == 1 && (rows % 16 || cols % 32)) return SWZ_EINVAL;
+    return make_plan(op, rows, cols, elem_bytes, layout, read_kind, p_or_null, true, out);
+}
+
+SWZ_API int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, int64_t rows, int64_t cols,
+                               int32_t elem_bytes, int32_t layout, int32_t read_kind, const swz_params* p_or_null,
+                               void* stream) {
+    if (batch < 0 || rows < 0 || cols < 0) return SWZ_EINVAL;
+    if (elem_bytes != 2 && elem_bytes != 4) return SWZ_EINVAL;
+    int64_t n, n2, bytes;
+    if (!mul_ok(batch, rows, &n) || !mul_ok(n, cols, &n2) || !mul_ok(n2, elem_bytes, &bytes)) return SWZ_EINVAL;
+    const auto ps = reinterpret_cast<uintptr_t>(d_src), pd = reinterpret_cast<uintptr_t>(d_dst);
+    const bool aligned = ps % 16 == 0 && pd % 16 == 0 && (cols * elem_bytes) % 16 == 0 && (rows * elem_bytes) % 16 == 0;
+    swz_plan_info pl;
+    const int st = make_plan(0, rows, cols, elem_bytes, layout, read_kind, p_or_null, aligned, &pl);
+    if (st != SWZ_OK) return st;
+    if (bytes == 0) return SWZ_OK;
+    if (!d_src || !d_dst) return SWZ_EINVAL;
+    if (ps % elem_bytes || pd % elem_bytes) return SWZ_EINVAL;
+    if (overlaps(d_src, bytes, d_dst, bytes)) return SWZ_EINVAL;
+    swz::ConvertJob job{d_src, d_dst, batch, rows, cols, layout_of(pl), aligned};
+    return hip_status(swz::launch_convert(pl.read_kind, job, static_cast<hipStream_t>(stream)));
+}
+
+SWZ_API int swz_transpose(const void* d_src, void* d_dst, int64_t rows, int64_t cols, int32_t elem_bytes,
+                          int32_t layout, int32_t read_kind, const swz_params* p_or_null, void* stream) {
+    return swz_convert_layout(d_src, d_dst, 1, rows, cols, elem_bytes, layout, read_kind, p_or_null, stream);
+}
+
+SWZ_API int swz_stage_operand(const void* d_src, void* d_frag, int64_t mn, int64_t k, int32_t elem_bytes,
+                              int32_t frag_kind, int32_t layout, const swz_params* p_or_null, void* stream) {
+    if (mn < 0 || k < 0 || mn % 16 || k % 32) return SWZ_EINVAL;
+    if (elem_bytes != 2 || frag_kind != SWZ_FRAG_MFMA_F32_16X16X32_BF16) return SWZ_EINVAL;
+    int64_t n, bytes;
+    if (!mul_ok(mn, k, &n) || !mul_ok(n, 2, &bytes)) return SWZ_EINVAL;
+    swz_plan_info pl;
+    const int st = make_plan(1, mn, k, elem_bytes, layout, SWZ_READ_MFMA_16X16X32, p_or_null, true, &pl);
+    if (st != SWZ_OK) return st;
+    if (bytes == 0) return SWZ_OK;
+    if (!d_src || !d_frag) return SWZ_EINVAL;
+    if (reinterpret_cast<uintptr_t>(d_src) % 16 || reinterpret_cast<uintptr_t>(d_frag) % 16) return SWZ_EINVAL;
+    if (overlaps(d_src, bytes, d_frag, bytes)) return SWZ_EINVAL;
+    swz::StageJob job{d_src, d_frag, mn, k, layout_of(pl)};
+    return hip_status(swz::launch_stage(job, static_cast<hipStream_t>(stream)));
+}
+
+SWZ_API int swz_choose(int32_t elem_bytes, int32_t vec_bytes, int32_t tile_rows, int32_t tile_cols, int32_t read_kind,
+                       swz_params* out) {
+    if (!out) return SWZ_EINVAL;
+    KindInfo k;
+    if (!swz::kind_info(read_kind, &k)) return SWZ_EINVAL;
+    if (k.esz != elem_bytes || k.vec != vec_bytes || k.tr != tile_rows || k.tc != tile_cols) return SWZ_EUNSUPPORTED;
+    *out = swz::cached_choice(read_kind);
+    return SWZ_OK;
+}
+
+SWZ_API int swz_predict_conflicts(int32_t read_kind, int32_t layout, const swz_params* p_or_null, int64_t* wcyc,
+                                  int64_t* rcyc) {
+    if (!wcyc || !rcyc) return SWZ_EINVAL;
+    KindInfo k;
+    if (!swz::kind_info(read_kind, &k)) return SWZ_EINVAL;
+    swz_params q{0, 0, 0};
+    uint32_t ld = static_cast<uint32_t>(k.tc);
+    if (layout == SWZ_LAYOUT_SWIZZLE) {
+        if (p_or_null) {
+            if (!swz::params_ok_for_kind(read_kind, *p_or_null)) return SWZ_EINVAL;
+            q = *p_or_null;
+        } else {
+            q = swz::cached_choice(read_kind);
+        }
+    } else if (layout == SWZ_LAYOUT_PAD) {
+        ld += static_cast<uint32_t>(swz::pad_elems(read_kind));
+    } else if (layout != SWZ_LAYOUT_PLAIN) {
+        return SWZ_EINVAL;
+    }
+    swz::predict_tile(read_kind, swz::gfx950_bank_model(), ld, q, wcyc, rcyc);
+    return SWZ_OK;
+}
+
+SWZ_API int swz_kernel_accesses(int32_t read_kind, int32_t layout, const swz_params* p_or_null, int32_t is_write,
+                                int32_t* addrs, int32_t max_accesses, int32_t* n_accesses, int32_t* width) {
+    if (!n_accesses || !width || max_accesses < 0 || (max_accesses > 0 && !addrs)) return SWZ_EINVAL;
+    if (is_write != 0 && is_write != 1) return SWZ_EINVAL;
+    KindInfo k;
+    if (!swz::kind_info(read_kind, &k)) return SWZ_EINVAL;
+    swz_params q{0, 0, 0};
+    uint32_t ld = static_cast<uint32_t>(k.tc);
+    if (layout == SWZ_LAYOUT_SWIZZLE) {
+        if (p_or_null) {
+            if (!swz::params_ok_for_kind(read_kind, *p_or_null)) return SWZ_EINVAL;
+            q = *p_or_null;
+        } else {
+            q = swz::cached_choice(read_kind);
+        }
+    } else if (layout == SWZ_LAYOUT_PAD) {
+        ld += static_cast<uint32_t>(swz::pad_elems(read_kind));
+    } else if (layout != SWZ_LAYOUT_PLAIN) {
+        return SWZ_EINVAL;
+    }
+    int w = 0;
+    *n_accesses = swz::kernel_accesses(read_kind, ld, q, is_write != 0, addrs, max_accesses, &w);
+    *width = w;
+    return SWZ_OK;
+}
+
+SWZ_API int swz_lds_probe(const uint32_t* d_addrs, const uint64_t* d_masks, int32_t n_patterns, int32_t width_bytes,
+                          int32_t is_write, int32_t iters, int32_t waves, uint64_t* d_cycles, void* stream) {
+    if (n_patterns < 0 || (width_bytes != 4 && width_bytes != 8 && width_bytes != 16)) return SWZ_EINVAL;
+    if (iters < 1 || iters > (1 << 20) || waves < 1 || waves > 16 || (is_write != 0 && is_write != 1))
+        return SWZ_EINVAL;
+    if (n_patterns == 0) return SWZ_OK;
+    if (!d_addrs || !d_masks || !d_cycles) return SWZ_EINVAL;
+    return hip_status(swz::launch_lds_probe(d_addrs, d_masks, n_patterns, width_bytes, is_write != 0, iters, waves,
+                                            d_cycles, static_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,202 @@
+// Swizzle<B,M,S> chooser for gfx950 LDS (host).
+//
+// The pages derive the three parameters from the hardware ("NVIDIA CuTe
+// Swizzle", derivation of MBase / BBits / SShift; "CUDA 013 - Swizzle 的
+// 工作原理", section CuTe 通用 swizzle 映射规则解析): M keeps one vector
+// whole, B spans one bank row of vectors, S reaches the row bits.  Their bank
+// row is 32 x 4 bytes; here it comes from the measured gfx950 model, and S is
+// picked by predicting the conflicts of the kernel's own lane patterns, since
+// which row bits vary inside one LDS phase depends on how lanes are assigned.
+#include "chooser.h"
+
+#include <mutex>
+
+#include "swz_common.h"
+
+namespace swz {
+
+namespace {
+
+int ilog2(int64_t v) {
+    int r = -1;
+    while (v > 0) {
+        v >>= 1;
+        ++r;
+    }
+    return r;
+}
+
+template <int KIND>
+void predict_kind(const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, int64_t* rcyc) {
+    using K = Kind<KIND>;
+    const LdsLayout L{ld, static_cast<uint32_t>(p.B), static_cast<uint32_t>(p.M), static_cast<uint32_t>(p.S)};
+    int64_t w = 0, r = 0;
+    Access a;
+    for (int wave = 0; wave < K::NT / 64; ++wave) {
+        for (int i = 0; i < K::WSTEPS; ++i) {
+            a.width = K::VEC;
+            a.write = true;
+            for (int l = 0; l < 64; ++l) {
+                int rr, cc;
+                K::wcoord(wave * 64 + l, i, rr, cc);
+                a.addr[l] = static_cast<int32_t>(lds_elem(L, rr, cc) * K::ESZ);
+            }
+            w += conflict_cycles(m, a);
+        }
+        for (int i = 0; i < K::RSTEPS; ++i) {
+            a.width = K::RWIDTH;
+            a.write = false;
+            for (int l = 0; l < 64; ++l) {
+                int rr, cc;
+                K::rcoord(wave * 64 + l, i, rr, cc);
+                a.addr[l] = static_cast<int32_t>(lds_elem(L, rr, cc) * K::ESZ);
+            }
+            r += conflict_cycles(m, a);
+        }
+    }
+    *wcyc = w;
+    *rcyc = r;
+}
+
+template <int KIND>
+int accesses_kind(uint32_t ld, swz_params p, bool write, int32_t* addrs, int max_acc, int* width) {
+    using K = Kind<KIND>;
+    const LdsLayout L{ld, static_cast<uint32_t>(p.B), static_cast<uint32_t>(p.M), static_cast<uint32_t>(p.S)};
+    const int steps = write ? K::WSTEPS : K::RSTEPS;
+    *width = write ? K::VEC : K::RWIDTH;
+    int n = 0;
+    for (int wave = 0; wave < K::NT / 64; ++wave) {
+        for (int i = 0; i < steps; ++i, ++n) {
+            if (n >= max_acc || !addrs) continue;
+            for (int l = 0; l < 64; ++l) {
+                int rr, cc;
+                if (write)
+                    K::wcoord(wave * 64 + l, i, rr, cc);
+                else
+                    K::rcoord(wave * 64 + l, i, rr, cc);
+                addrs[64 * n + l] = static_cast<int32_t>(lds_elem(L, rr, cc) * K::ESZ);
+            }
+        }
+    }
+    return n;
+}
+
+}  // namespace
+
+int kernel_accesses(int kind, uint32_t ld, swz_params p, bool write, int32_t* addrs, int max_acc, int* width) {
+    switch (kind) {
+        case SWZ_READ_SCALAR_COL: return accesses_kind<SWZ_READ_SCALAR_COL>(ld, p, write, addrs, max_acc, width);
+        case SWZ_READ_B64_4X4: return accesses_kind<SWZ_READ_B64_4X4>(ld, p, write, addrs, max_acc, width);
+        case SWZ_READ_B128_8X8: return accesses_kind<SWZ_READ_B128_8X8>(ld, p, write, addrs, max_acc, width);
+        case SWZ_READ_MFMA_16X16X32: return accesses_kind<SWZ_READ_MFMA_16X16X32>(ld, p, write, addrs, max_acc, width);
+        default: return -1;
+    }
+}
+
+bool kind_info(int kind, KindInfo* o) {
+    switch (kind) {
+#define SWZ_KIND_CASE(KD)                                                                           \
+    case KD: {                                                                                      \
+        using K = Kind<KD>;                                                                         \
+        *o = KindInfo{K::ESZ, K::TR, K::TC, K::NT, K::VEC, K::RWIDTH, K::WSTEPS, K::RSTEPS};        \
+        return true;                                                                                \
+    }
+        SWZ_KIND_CASE(SWZ_READ_SCALAR_COL)
+        SWZ_KIND_CASE(SWZ_READ_B64_4X4)
+        SWZ_KIND_CASE(SWZ_READ_B128_8X8)
+        SWZ_KIND_CASE(SWZ_READ_MFMA_16X16X32)
+#undef SWZ_KIND_CASE
+        default:
+            return false;
+    }
+}
+
+int pad_elems(int kind) {
+    KindInfo k;
+    if (!kind_info(kind, &k)) return 0;
+    // One element for scalar staging (the 32x33 array of the pages); one
+    // 16-byte vector for vector staging so every row stays 16-byte aligned.
+    return k.vec == k.esz ? 1 : k.vec / k.esz;
+}
+
+void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, int64_t* rcyc) {
+    switch (kind) {
+        case SWZ_READ_SCALAR_COL: predict_kind<SWZ_READ_SCALAR_COL>(m, ld, p, wcyc, rcyc); break;
+        case SWZ_READ_B64_4X4: predict_kind<SWZ_READ_B64_4X4>(m, ld, p, wcyc, rcyc); break;
+        case SWZ_READ_B128_8X8: predict_kind<SWZ_READ_B128_8X8>(m, ld, p, wcyc, rcyc); break;
+        case SWZ_READ_MFMA_16X16X32: predict_kind<SWZ_READ_MFMA_16X16X32>(m, ld, p, wcyc, rcyc); break;
+        default: *wcyc = *rcyc = -1;
+    }
+}
+
+bool params_ok_for_kind(int kind, swz_params p) {
+    KindInfo k;
+    if (!kind_info(kind, &k)) return false;
+    if (p.B < 0 || p.M < 0 || p.S < 0) return false;
+    if (p.B == 0) return p.M + p.S <= 32;
+    if (p.B + p.M + p.S > 32) return false;
+    if (p.S < 1) return false;
+    const int min_vec = k.vec > k.rwidth ? k.vec : k.rwidth;
+    if ((1 << p.M) < min_vec / k.esz) return false;
+    if (p.M + p.B > ilog2(static_cast<int64_t>(k.tr) * k.tc)) return false;
+    return true;
+}
+
+swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles) {
+    KindInfo k;
+    swz_params none{0, 0, 0};
+    if (!kind_info(kind, &k)) return none;
+    const int M = ilog2(k.vec / k.esz);
+    const int log_tile = ilog2(static_cast<int64_t>(k.tr) * k.tc);
+    const int b_max = (log_tile - M) / 2;
+    const int row_bytes = m.n_banks * m.bank_bytes;
+    int b_rule = row_bytes >= k.vec ? ilog2(row_bytes / k.vec) : 0;
+    if (b_rule > b_max) b_rule = b_max;
+
+    auto cost = [&](int B, int S) {
+        int64_t w, r;
+        predict_tile(kind, m, static_cast<uint32_t>(k.tc), swz_params{B, M, S}, &w, &r);
+        return w + r;
+    };
+
+    swz_params best{b_rule, M, b_rule};
+    int64_t best_cyc = -1;
+    for (int S = b_rule; S <= log_tile - M - b_rule; ++S) {
+        const int64_t c = cost(b_rule, S);
+        if (best_cyc < 0 || c < best_cyc) {
+            best = swz_params{b_rule, M, S};
+            best_cyc = c;
+        }
+        if (c == 0) {
+            if (cycles) *cycles = 0;
+            return best;
+        }
+    }
+    // No zero-conflict shift at the rule's B: widest search, ties to the B
+    // nearest the rule, then the smaller S.
+    for (int B = 1; B <= b_max; ++B) {
+        for (int S = B; S <= log_tile - M - B; ++S) {
+            const int64_t c = cost(B, S);
+            const int db = B > b_rule ? B - b_rule : b_rule - B;
+            const int dbest = best.B > b_rule ? best.B - b_rule : b_rule - best.B;
+            if (c < best_cyc || (c == best_cyc && (db < dbest || (db == dbest && S < best.S)))) {
+                best = swz_params{B, M, S};
+                best_cyc = c;
+            }
+        }
+    }
+    if (cycles) *cycles = best_cyc;
+    return best;
+}
+
+swz_params cached_choice(int kind) {
+    static std::once_flag once;
+    static swz_params table[4];
+    std::call_once(once, [] {
+        for (int kd = 0; kd < 4; ++kd) table[kd] = choose_for_kind(kd, gfx950_bank_model(), nullptr);
+    });
+    if (kind < 0 || kind > 3) return swz_params{0, 0, 0};
+    return table[kind];
+}
+
+}  // namespace swz

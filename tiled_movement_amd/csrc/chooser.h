@@ -1,0 +1,39 @@
+// Swizzle parameter chooser and per-tile conflict prediction (host).
+#pragma once
+
+#include <stdint.h>
+
+#include "bank_model.h"
+#include "swz.h"
+
+namespace swz {
+
+struct KindInfo {
+    int esz, tr, tc, nt, vec, rwidth, wsteps, rsteps;
+};
+
+// Static facts of a read kind; false for an unknown kind.
+bool kind_info(int kind, KindInfo* out);
+
+// Predicted conflict cycles over one tile for the kind's staging writes and
+// reads, with LDS row pitch ld and swizzle p (B = 0 for none).
+void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, int64_t* rcyc);
+
+// Chooser: see swz_choose in swz.h.  Result cached per kind for the gfx950
+// model; the model argument form is uncached.
+swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles);
+swz_params cached_choice(int kind);
+
+// The kernel's LDS accesses for one tile (see swz_kernel_accesses).
+int kernel_accesses(int kind, uint32_t ld, swz_params p, bool write, int32_t* addrs, int max_acc, int* width);
+
+// Pad (elements per LDS row) of the padded layout for a kind.
+int pad_elems(int kind);
+
+// Validate caller parameters for a kind: non-negative, fields inside 32 bits,
+// S >= 1 when B > 0 (S = 0 would not be one-to-one), vectors kept whole
+// (2^M >= elements per LDS store and per LDS load) and the permuted block
+// inside the tile (M + B <= log2(tile elements)).
+bool params_ok_for_kind(int kind, swz_params p);
+
+}  // namespace swz

@@ -1,0 +1,32 @@
+// Kernel launchers (defined in the .hip files, called by the C ABI layer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "swz_common.h"
+
+namespace swz {
+
+struct ConvertJob {
+    const void* src;
+    void* dst;
+    int64_t batch, rows, cols;
+    LdsLayout layout;
+    bool aligned;  // 16-byte vector path allowed (pointers and pitches)
+};
+
+struct StageJob {
+    const void* src;
+    void* frag;
+    int64_t mn, k;
+    LdsLayout layout;
+};
+
+hipError_t launch_convert(int kind, const ConvertJob& job, hipStream_t stream);
+hipError_t launch_stage(const StageJob& job, hipStream_t stream);
+hipError_t launch_map(const int32_t* in, int32_t* out, int64_t n, swz_params p, hipStream_t stream);
+hipError_t launch_lds_probe(const uint32_t* addrs, const uint64_t* masks, int n_patterns, int width, bool write,
+                            int iters, int waves, uint64_t* cycles, hipStream_t stream);
+
+}  // namespace swz
