@@ -2,15 +2,21 @@
 
 Headline workload: fp32 4096x4096 row-major -> column-major transpose through
 32x32 LDS tiles with the chosen Swizzle<B,M,S>.  One step = one call of
-swz_transpose on that matrix.  Inputs are resident in HBM before timing; the
-calls rotate over enough source/destination pairs (>= 512 MiB) that the
-256 MB Infinity Cache cannot hold the working set, so traffic reaches HBM.
+swz_transpose on that matrix (one kernel launch).  Inputs are resident in HBM
+before timing; the calls rotate over enough source/destination pairs
+(>= 512 MiB) that the 256 MB Infinity Cache cannot hold the working set, so
+traffic reaches HBM.
 
 Prints ONE JSON line.  Extra fields: the other workloads and layouts
-(swizzle / pad / plain), a device-to-device copy of the same bytes as the
-practical ceiling, and the CPU oracle as a reported baseline.
+(swizzle / pad / plain), the library's reference copy of the same bytes (the
+practical read-once / write-once ceiling), and the CPU oracle as a reported
+baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+  python bench.py --workload NAME --layout swizzle|pad|plain [--steps K]
+      time one workload only (used for profiler runs); NAME is one of
+      fp32_transpose, fp16_transpose, bf16_convert, bf16_stage, map, copy
 """
 
 from __future__ import annotations
@@ -28,6 +34,15 @@ if ROOT not in sys.path:
 METRIC = "effective HBM GB/s (% of 8 TB/s) for swizzled LDS transpose; LDS conflict cycles"
 HBM_PEAK_GBS = 8000.0
 CACHE_DEFEAT_BYTES = 512 * 2**20  # 2x the 256 MB Infinity Cache
+
+WORKLOADS = {
+    "fp32_transpose": "fp32 4096x4096 row-major -> column-major transpose, 32x32 LDS tiles, 4-byte column reads",
+    "fp16_transpose": "fp16 8192x8192 row-major -> column-major transpose, 64x64 LDS tiles, 8-byte reads of 4x4 blocks",
+    "bf16_convert": "bf16 [64,4096,128] -> [64,128,4096] layout conversion, 64x128 LDS tiles, 16-byte reads of 8x8 blocks",
+    "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
+    "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
+    "copy": "reference 16-byte vector copy of 64 MiB (read once, write once)",
+}
 
 
 def log(*a):
@@ -54,8 +69,7 @@ def time_steps(step, steps, warmup):
     end.record()
     end.synchronize()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return start.elapsed_time(end), wall
+    return start.elapsed_time(end), time.perf_counter() - t0
 
 
 def median_rate(step, bytes_per_step, steps=50, warmup=10, batches=3):
@@ -64,9 +78,153 @@ def median_rate(step, bytes_per_step, steps=50, warmup=10, batches=3):
         ms, _ = time_steps(step, steps, warmup)
         mss.append(ms / steps)
         rates.append(bytes_per_step * steps / (ms * 1e-3) / 1e9)
-    order = sorted(range(batches), key=lambda i: rates[i])
-    mid = order[batches // 2]
+    mid = sorted(range(batches), key=lambda i: rates[i])[batches // 2]
     return rates[mid], mss[mid]
+
+
+class Ctx:
+    """Device, stream and helpers shared by the workload builders."""
+
+    def __init__(self):
+        import numpy as np
+        import torch
+
+        import tiled_movement_amd as T
+
+        self.np, self.torch, self.T = np, torch, T
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+        self.lib = T.lib
+        self.stream = torch.cuda.current_stream(self.dev).cuda_stream
+
+    def copies(self, a, k):
+        np, torch = self.np, self.torch
+        base = torch.from_numpy(np.ascontiguousarray(a).view(np.int32 if a.itemsize == 4 else np.int16)).to(self.dev)
+        return [base] + [base.clone() for _ in range(k - 1)]
+
+    def check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {self.T.strerror(rc)}")
+
+
+def build(ctx, name, layout):
+    """Return (step, bytes_per_step, info) for one workload.  Timed steps call
+    the C ABI with pointers and stream resolved up front, so host-side
+    marshalling stays far below the kernel time."""
+    import workloads as W
+
+    T, lib, stream = ctx.T, ctx.lib, ctx.stream
+    lay = T.LAYOUTS[layout]
+    info = {"workload": WORKLOADS[name], "layout": layout}
+
+    if name in ("fp32_transpose", "fp16_transpose", "bf16_convert"):
+        if name == "fp32_transpose":
+            a, esz, kind, (batch, r, c) = W.fp32_matrix(4096, 4096, seed=0), 4, T.READ_SCALAR_COL, (1, 4096, 4096)
+        elif name == "fp16_transpose":
+            a, esz, kind, (batch, r, c) = W.fp16_matrix(8192, 8192, seed=0), 2, T.READ_B64_4X4, (1, 8192, 8192)
+        else:
+            a, esz, kind, (batch, r, c) = W.bf16_tensor((64, 4096, 128), seed=0), 2, T.READ_B128_8X8, (64, 4096, 128)
+        k = n_pairs(2 * a.nbytes)
+        srcs = ctx.copies(a, k)
+        dsts = [ctx.torch.empty_like(srcs[0]) for _ in range(k)]
+        sp, dp = [t.data_ptr() for t in srcs], [t.data_ptr() for t in dsts]
+
+        def step(i):
+            j = i % k
+            rc = lib.swz_convert_layout(sp[j], dp[j], batch, r, c, esz, lay, kind, None, stream)
+            if rc:
+                ctx.check(rc, "swz_convert_layout")
+
+        pl = T.swz_plan(0, r, c, esz, layout, kind)
+        wc, rc_ = T.swz_predict_conflicts(kind, layout)
+        info.update({"shape": [batch, r, c], "elem_bytes": esz, "params": list(pl["params"]),
+                     "pad_elems": pl["pad_elems"], "lds_bytes": pl["lds_bytes"], "threads": pl["threads"],
+                     "buffer_pairs": k, "predicted_conflict_cycles_per_tile": {"write": wc, "read": rc_}})
+        info["_io"] = (a, srcs, dsts, step)
+        return step, 2 * a.nbytes, info
+
+    if name == "bf16_stage":
+        ao, bo = W.bf16_operands(8192, 8192, 4096, seed=0)
+        k = n_pairs(2 * (ao.nbytes + bo.nbytes))
+        sa, sb = ctx.copies(ao, k), ctx.copies(bo, k)
+        fa = [ctx.torch.empty_like(sa[0]) for _ in range(k)]
+        fb = [ctx.torch.empty_like(sb[0]) for _ in range(k)]
+        pa, pb = [t.data_ptr() for t in sa], [t.data_ptr() for t in sb]
+        pfa, pfb = [t.data_ptr() for t in fa], [t.data_ptr() for t in fb]
+        frag = T.FRAG_MFMA_F32_16X16X32_BF16
+
+        def step(i):
+            j = i % k
+            rc = lib.swz_stage_operand(pa[j], pfa[j], 8192, 4096, 2, frag, lay, None, stream)
+            rc |= lib.swz_stage_operand(pb[j], pfb[j], 8192, 4096, 2, frag, lay, None, stream)
+            if rc:
+                ctx.check(rc, "swz_stage_operand")
+
+        pl = T.swz_plan(1, 8192, 4096, 2, layout)
+        wc, rc_ = T.swz_predict_conflicts(T.READ_MFMA_16X16X32, layout)
+        info.update({"params": list(pl["params"]), "pad_elems": pl["pad_elems"], "lds_bytes": pl["lds_bytes"],
+                     "threads": pl["threads"], "buffer_pairs": k, "launches_per_step": 2,
+                     "predicted_conflict_cycles_per_tile": {"write": wc, "read": rc_}})
+        info["_keep"] = (sa, sb, fa, fb)
+        return step, 2 * (ao.nbytes + bo.nbytes), info
+
+    if name == "map":
+        x = ctx.torch.arange(65536, dtype=ctx.torch.int32, device=ctx.dev)
+        y = ctx.torch.empty_like(x)
+        cparams = [T.Params(*t) for t in W.map_triples()]
+        xp, yp = x.data_ptr(), y.data_ptr()
+
+        def step(i):
+            rc = lib.swz_map(xp, yp, 65536, cparams[i % len(cparams)], stream)
+            if rc:
+                ctx.check(rc, "swz_map")
+
+        info["_keep"] = (x, y)
+        return step, 2 * 65536 * 4, info
+
+    if name == "copy":
+        nbytes = 64 * 2**20
+        k = n_pairs(2 * nbytes)
+        srcs = [ctx.torch.zeros(nbytes // 4, dtype=ctx.torch.int32, device=ctx.dev) for _ in range(k)]
+        dsts = [ctx.torch.empty_like(s) for s in srcs]
+        sp, dp = [t.data_ptr() for t in srcs], [t.data_ptr() for t in dsts]
+
+        def step(i):
+            j = i % k
+            rc = lib.swz_copy(sp[j], dp[j], nbytes, stream)
+            if rc:
+                ctx.check(rc, "swz_copy")
+
+        info["_keep"] = (srcs, dsts)
+        info["buffer_pairs"] = k
+        return step, 2 * nbytes, info
+
+    raise ValueError(name)
+
+
+def cpu_baseline(a, dst_dev, seconds):
+    """The oracle's transpose of the headline input, timed on the host (one
+    thread), bounded to about `seconds`; also checks the GPU result."""
+    import numpy as np
+
+    import oracle
+
+    got = dst_dev.cpu().numpy().view(np.uint32)
+    reps, t_cpu, ref = 0, 0.0, None
+    while t_cpu < seconds or reps == 0:
+        t1 = time.perf_counter()
+        ref = oracle.transpose(a)
+        t_cpu += time.perf_counter() - t1
+        reps += 1
+    return {
+        "value": round(a.nbytes * 2 * reps / t_cpu / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{reps} full 4096x4096 fp32 transposes by the oracle (NumPy strided copy, one thread), "
+                  f"{t_cpu:.1f} s",
+        "matches_gpu": bool(np.array_equal(ref, got)),
+    }
 
 
 def main(argv=None):
@@ -75,6 +233,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline only, no other workloads")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=None)
+    ap.add_argument("--layout", choices=["swizzle", "pad", "plain"], default="swizzle")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle leg")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -82,177 +242,46 @@ def main(argv=None):
               "multi-GPU part: each GPU would run the same kernel on its own shard).", file=sys.stderr)
         return 2
 
-    import numpy as np
-    import torch
-
-    import tiled_movement_amd as T
-    import workloads as W
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    def dev_copy(a, k):
-        base = torch.from_numpy(np.ascontiguousarray(a).view(np.int32 if a.itemsize == 4 else np.int16)).to(dev)
-        return [base] + [base.clone() for _ in range(k - 1)]
-
-    # ---------------------------------------------------------------- headline
-    rows = cols = 4096
-    a = W.fp32_matrix(rows, cols, seed=0)
-    nbytes = a.nbytes
-    k = n_pairs(2 * nbytes)
-    srcs = dev_copy(a, k)
-    dsts = [torch.empty((cols, rows), dtype=torch.int32, device=dev) for _ in range(k)]
-    plan = T.swz_plan(0, rows, cols, 4, "swizzle", T.READ_AUTO)
-    log(f"headline plan: {plan}, {k} buffer pairs")
-
-    # Timed loops call the C ABI with pointers and stream resolved up front, so
-    # host-side marshalling stays far below the kernel time.
-    lib = T.lib
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    sp, dp = [s.data_ptr() for s in srcs], [d.data_ptr() for d in dsts]
-
-    def check(rc, what):
-        if rc != 0:
-            raise RuntimeError(f"{what}: {T.strerror(rc)}")
-
-    def step(i):
-        j = i % k
-        rc = lib.swz_transpose(sp[j], dp[j], rows, cols, 4, T.LAYOUT_SWIZZLE, T.READ_AUTO, None, stream)
-        if rc:
-            check(rc, "swz_transpose")
-
+    ctx = Ctx()
+    name = args.workload or "fp32_transpose"
+    layout = args.layout if args.workload else "swizzle"
+    step, nbytes, info = build(ctx, name, layout)
+    log(f"{name}/{layout}: {({k: v for k, v in info.items() if not k.startswith('_')})}")
     ms, wall = time_steps(step, args.steps, args.warmup)
-    bytes_per_step = 2 * nbytes
+    launches = info.get("launches_per_step", 1)
     ms_per_step = ms / args.steps
-    value = bytes_per_step * args.steps / (ms * 1e-3) / 1e9
-    log(f"headline: {value:.1f} GB/s, {ms_per_step * 1e3:.2f} us/step, wall {wall:.3f} s")
+    value = nbytes * args.steps / (ms * 1e-3) / 1e9
+    log(f"{name}/{layout}: {value:.1f} GB/s, {ms_per_step * 1e3:.2f} us/step, wall {wall:.3f} s")
 
     extra = {}
-    if not args.quick:
-        # Practical ceiling: device-to-device copy of the same bytes.
-        def copy_step(i):
-            j = i % k
-            dsts[j].view(-1).copy_(srcs[j].view(-1))
+    if not args.quick and args.workload is None:
+        for wname in ("copy", "fp32_transpose", "fp16_transpose", "bf16_convert", "bf16_stage", "map"):
+            for lay in (("swizzle",) if wname in ("copy", "map") else ("swizzle", "pad", "plain")):
+                s2, nb2, inf2 = build(ctx, wname, lay)
+                if wname == "map":
+                    rate, ms2 = median_rate(s2, nb2, steps=250, warmup=25)
+                    extra["map/swizzle"] = {"us_per_call": round(ms2 * 1e3, 3)}
+                    log(f"map: {ms2 * 1e3:.2f} us/call")
+                    continue
+                rate, ms2 = median_rate(s2, nb2)
+                rec = {k: v for k, v in inf2.items() if not k.startswith("_") and k != "workload"}
+                rec.update({"GBps": round(rate, 1), "frac": round(rate / HBM_PEAK_GBS, 4),
+                            "us_per_step": round(ms2 * 1e3, 2)})
+                extra[f"{wname}/{lay}"] = rec
+                log(f"{wname}/{lay}: {rate:.1f} GB/s")
+                del s2, inf2
+                ctx.torch.cuda.empty_cache()
 
-        rate, msc = median_rate(copy_step, 2 * nbytes)
-        extra["d2d_copy_64MiB"] = {"GBps": round(rate, 1), "us": round(msc * 1e3, 2)}
-        log(f"d2d copy: {rate:.1f} GB/s")
-
-        configs = []
-        for layout in ("swizzle", "pad", "plain"):
-            configs.append(("fp32_4096x4096_transpose", layout, (rows, cols), 4, T.READ_SCALAR_COL, 1))
-        for layout in ("swizzle", "pad", "plain"):
-            configs.append(("fp16_8192x8192_transpose", layout, (8192, 8192), 2, T.READ_B64_4X4, 1))
-        for layout in ("swizzle", "pad", "plain"):
-            configs.append(("bf16_64x4096x128_convert", layout, (4096, 128), 2, T.READ_B128_8X8, 64))
-        inputs = {}
-        for name, layout, (r, c), esz, kind, batch in configs:
-            if name not in inputs:
-                if name.startswith("fp32"):
-                    arr = a
-                elif name.startswith("fp16"):
-                    arr = W.fp16_matrix(r, c, seed=0)
-                else:
-                    arr = W.bf16_tensor((batch, r, c), seed=0)
-                kk = n_pairs(2 * arr.nbytes)
-                s_ = dev_copy(arr, kk)
-                d_ = [torch.empty_like(s_[0]) for _ in range(kk)]
-                inputs[name] = (s_, d_, arr.nbytes)
-            s_, d_, nb = inputs[name]
-            kk = len(s_)
-
-            lay = T.LAYOUTS[layout]
-            sps, dps = [t.data_ptr() for t in s_], [t.data_ptr() for t in d_]
-
-            def cstep(i, sps=sps, dps=dps, r=r, c=c, esz=esz, kind=kind, batch=batch, lay=lay, kk=kk):
-                j = i % kk
-                rc = lib.swz_convert_layout(sps[j], dps[j], batch, r, c, esz, lay, kind, None, stream)
-                if rc:
-                    check(rc, "swz_convert_layout")
-
-            rate, msc = median_rate(cstep, 2 * nb)
-            pl = T.swz_plan(0, r, c, esz, layout, kind)
-            wc, rc = T.swz_predict_conflicts(kind, layout)
-            extra[f"{name}/{layout}"] = {
-                "GBps": round(rate, 1), "frac": round(rate / HBM_PEAK_GBS, 4), "us": round(msc * 1e3, 2),
-                "params": pl["params"], "pad": pl["pad_elems"], "lds_bytes": pl["lds_bytes"],
-                "predicted_conflict_cycles_per_tile": {"write": wc, "read": rc},
-            }
-            log(f"{name}/{layout}: {rate:.1f} GB/s")
-        del inputs
-
-        # operand staging: A then B^T, one call each per step
-        ao, bo = W.bf16_operands(8192, 8192, 4096, seed=0)
-        for layout in ("swizzle", "pad", "plain"):
-            kk = n_pairs(2 * ao.nbytes)
-            sa, sb = dev_copy(ao, kk), dev_copy(bo, kk)
-            fa = [torch.empty_like(sa[0]) for _ in range(kk)]
-            fb = [torch.empty_like(sb[0]) for _ in range(kk)]
-
-            lay = T.LAYOUTS[layout]
-            pa, pb = [t.data_ptr() for t in sa], [t.data_ptr() for t in sb]
-            pfa, pfb = [t.data_ptr() for t in fa], [t.data_ptr() for t in fb]
-
-            def sstep(i, lay=lay, pa=pa, pb=pb, pfa=pfa, pfb=pfb, kk=kk):
-                j = i % kk
-                rc = lib.swz_stage_operand(pa[j], pfa[j], 8192, 4096, 2, T.FRAG_MFMA_F32_16X16X32_BF16, lay, None,
-                                           stream)
-                rc |= lib.swz_stage_operand(pb[j], pfb[j], 8192, 4096, 2, T.FRAG_MFMA_F32_16X16X32_BF16, lay, None,
-                                            stream)
-                if rc:
-                    check(rc, "swz_stage_operand")
-
-            rate, msc = median_rate(sstep, 2 * (ao.nbytes + bo.nbytes))
-            pl = T.swz_plan(1, 8192, 4096, 2, layout)
-            extra[f"bf16_operand_staging_A8192x4096_B4096x8192/{layout}"] = {
-                "GBps": round(rate, 1), "frac": round(rate / HBM_PEAK_GBS, 4), "us_per_A_plus_B": round(msc * 1e3, 2),
-                "params": pl["params"], "pad": pl["pad_elems"],
-            }
-            log(f"staging/{layout}: {rate:.1f} GB/s")
-            del sa, sb, fa, fb
-
-        # swizzle map: 125 calls of 65536 offsets (launch-bound)
-        x = torch.arange(65536, dtype=torch.int32, device=dev)
-        y = torch.empty_like(x)
-        triples = W.map_triples()
-
-        cparams = [T.Params(*t) for t in triples]
-        xp, yp = x.data_ptr(), y.data_ptr()
-
-        def mstep(i):
-            rc = lib.swz_map(xp, yp, 65536, cparams[i % len(cparams)], stream)
-            if rc:
-                check(rc, "swz_map")
-
-        rate, msm = median_rate(mstep, 2 * 65536 * 4, steps=250, warmup=25)
-        extra["map_65536_x125"] = {"us_per_call": round(msm * 1e3, 3), "GBps": round(rate, 1)}
-        log(f"map: {msm * 1e3:.2f} us/call")
-
-    # -------------------------------------------------------------- CPU oracle
     cpu = None
-    try:
-        import oracle
-
-        got = dsts[0].cpu().numpy().view(np.uint32)
-        reps, t_cpu = 0, 0.0
-        ref = None
-        while t_cpu < args.cpu_seconds or reps == 0:
-            t1 = time.perf_counter()
-            ref = oracle.transpose(a)
-            t_cpu += time.perf_counter() - t1
-            reps += 1
-        cpu = {
-            "value": round(2 * nbytes * reps / t_cpu / 1e9, 3),
-            "unit": "GB/s",
-            "cores": 1,
-            "kind": "oracle",
-            "sample": f"{reps} full 4096x4096 fp32 transposes by the oracle (NumPy strided copy, one thread), "
-                      f"{t_cpu:.1f} s",
-            "matches_gpu": bool(np.array_equal(ref, got)),
-        }
-        log(f"cpu oracle: {cpu['value']} GB/s over {reps} reps; GPU output matches: {cpu['matches_gpu']}")
-    except Exception as e:  # the oracle leg is a reported baseline only
-        log(f"cpu baseline skipped: {e!r}")
+    if name == "fp32_transpose" and "_io" in info:
+        a, srcs, dsts, st = info["_io"]
+        st(0)  # buffer pair 0 holds the transpose of the input again
+        ctx.torch.cuda.synchronize()
+        try:
+            cpu = cpu_baseline(a, dsts[0], args.cpu_seconds)
+            log(f"cpu oracle: {cpu['value']} GB/s; GPU output matches: {cpu['matches_gpu']}")
+        except Exception as e:  # a reported baseline only
+            log(f"cpu baseline skipped: {e!r}")
 
     line = {
         "metric": METRIC,
@@ -265,16 +294,17 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": {"fp32_transpose": "f32", "fp16_transpose": "f16", "map": "int32", "copy": "u8"}.get(name, "bf16"),
         "data": "synthetic",
-        "config": {
-            "workload": "fp32 4096x4096 row-major -> column-major transpose, 32x32 LDS tiles, scalar column reads",
-            "rows": rows, "cols": cols, "elem_bytes": 4, "layout": "swizzle",
-            "swizzle_BMS": list(plan["params"]), "buffer_pairs": k,
-        },
+        "config": {k: v for k, v in info.items() if not k.startswith("_")},
         "roofline": {
-            "bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+            "bound": "hbm",
+            "achieved": round(value, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "launches_per_step": launches,
         },
         "cpu_baseline": cpu,
         "extra": extra,

@@ -76,6 +76,7 @@ typedef struct swz_plan_info {
     int32_t lds_bytes;   /* LDS bytes one tile occupies */
     int32_t vec_bytes;   /* width of the LDS stores of the staging pass */
     int32_t aligned;     /* 1 if the 16-byte vector path is used */
+    int32_t threads;     /* threads per workgroup (one tile at a time) */
 } swz_plan_info;
 
 /* out[i] = Swizzle<B,M,S>(in[i]) for i < n, on the 32-bit bit patterns
@@ -161,6 +162,21 @@ int swz_predict_conflicts(int32_t read_kind, int32_t layout, const swz_params* p
 int swz_kernel_accesses(int32_t read_kind, int32_t layout, const swz_params* p_or_null, int32_t is_write,
                         int32_t* addrs, int32_t max_accesses, int32_t* n_accesses, int32_t* width);
 
+/* The LDS bank model the chooser uses, per access direction d (0 = read,
+ * 1 = write) and width w (4 << w bytes per lane): n_banks banks of
+ * bank_bytes, byte a in bank (a / bank_bytes) % n_banks ("CuTe Swizzle
+ * 学习手册", bank structure, gives one geometry, 32 x 4 bytes, for NVIDIA;
+ * gfx950's depends on the access and is measured with swz_lds_probe), and
+ * phase[d][w][l], the group of lanes served together. */
+typedef struct swz_bank_model {
+    int32_t n_banks[2][3];
+    int32_t bank_bytes[2][3];
+    uint8_t phase[2][3][64];
+} swz_bank_model;
+
+/* Host only.  Copy the built-in gfx950 model to *out.  SWZ_EINVAL on NULL. */
+int swz_bank_model_get(swz_bank_model* out);
+
 /* Host only.  Fill *out with what swz_convert_layout (op = 0) or
  * swz_stage_operand (op = 1) would do for these arguments, without
  * launching anything; pointers are not inspected (aligned is reported for
@@ -170,6 +186,14 @@ int swz_plan(int32_t op, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t
 
 /* Host only.  Static text for a status code. */
 const char* swz_strerror(int status);
+
+/* Reference copy (diagnostic): d_dst[0..bytes) = d_src[0..bytes) with plain
+ * 16-byte vector loads and stores and the same launch policy as the tile
+ * kernels.  It is the read-once / write-once ceiling the tile kernels are
+ * compared with, and the kernel of known size HBM byte counters are scaled
+ * by.  bytes must be a multiple of 16, pointers 16-byte aligned, buffers
+ * disjoint.  Errors: SWZ_EINVAL otherwise. */
+int swz_copy(const void* d_src, void* d_dst, int64_t bytes, void* stream);
 
 /* LDS bank microbenchmark (diagnostic; used to measure the bank model the
  * chooser relies on).  Launches n_patterns workgroups of `waves` 64-lane

@@ -44,6 +44,7 @@ __all__ = [
     "stage_operand",
     "stage_operand_loops",
     "BankModel",
+    "LdsModel",
     "nvidia_model",
     "conflict_report",
     "access_addresses",
@@ -234,6 +235,21 @@ class BankModel:
         return [list(range(s, min(s + per, self.n_lanes))) for s in range(0, self.n_lanes, per)]
 
 
+@dataclass
+class LdsModel:
+    """A bank model per access direction and width.
+
+    The pages give one geometry for every access ([Handbook] §Shared Memory 的
+    Bank 结构).  Reading taken for hardware where the geometry depends on the
+    access: each (direction, bytes per lane) has its own BankModel."""
+
+    read: Dict[int, BankModel]
+    write: Dict[int, BankModel]
+
+    def for_access(self, width: int, write: bool) -> BankModel:
+        return (self.write if write else self.read)[width]
+
+
 def nvidia_model() -> BankModel:
     """32 banks x 4 bytes, 32-thread warps: the model every page assumes."""
     return BankModel(n_banks=32, bank_bytes=4, n_lanes=32)
@@ -282,15 +298,17 @@ def access_addresses(coords, width_elems: int, tile_cols: int, esz: int, layout:
     return out
 
 
-def pattern_cycles(instrs, tile_cols: int, esz: int, layout: str, model: BankModel,
-                   params=None, pad: int = 0):
+def pattern_cycles(instrs, tile_cols: int, esz: int, layout: str, model,
+                   params=None, pad: int = 0, write: bool = False):
     """Total conflict cycles and worst degree over a list of instructions,
-    each given as (coords, width_bytes)."""
+    each given as (coords, width_bytes).  ``model`` is a BankModel, or an
+    LdsModel from which the (direction, width) geometry is taken."""
     total = 0
     worst = 0
     for coords, width in instrs:
         addrs = access_addresses(coords, width // esz, tile_cols, esz, layout, params, pad)
-        c, w, _ = conflict_report(addrs, width, model)
+        m = model.for_access(width, write) if isinstance(model, LdsModel) else model
+        c, w, _ = conflict_report(addrs, width, m)
         total += c
         worst = max(worst, w)
     return total, worst
@@ -319,7 +337,7 @@ def rule_bits(esz: int, vec_bytes: int, model: BankModel) -> int:
 
 
 def choose(esz: int, vec_bytes: int, tile_rows: int, tile_cols: int, write_instrs, read_instrs,
-           model: BankModel):
+           model):
     """(B, M, S) for a tile staged by ``write_instrs`` and read by ``read_instrs``.
 
     The pages' derivation ([CuTe-DSL]; [HowItWorks] §CuTe 通用 swizzle 映射规则解析
@@ -335,15 +353,19 @@ def choose(esz: int, vec_bytes: int, tile_rows: int, tile_cols: int, write_instr
     If no S reaches zero cycles at that B, every B in 1..Bmax is tried and
     the least-cycles triple wins, ties to the B nearest the rule, then the
     smaller S.  Returns ((B, M, S), cycles).
+
+    ``model`` is one BankModel for every access, or an LdsModel; then the bank
+    row that sets B is the one the reads see (the layout exists for them).
     """
     M = _log2_exact(max(vec_bytes // esz, 1))
     log_tile = _log2_exact(tile_rows * tile_cols)
     b_max = (log_tile - M) // 2
-    b_rule = min(rule_bits(esz, vec_bytes, model), b_max)
+    row_model = model.for_access(read_instrs[0][1], False) if isinstance(model, LdsModel) else model
+    b_rule = min(rule_bits(esz, vec_bytes, row_model), b_max)
 
     def cost(B, S):
-        cw, _ = pattern_cycles(write_instrs, tile_cols, esz, "swizzle", model, (B, M, S))
-        cr, _ = pattern_cycles(read_instrs, tile_cols, esz, "swizzle", model, (B, M, S))
+        cw, _ = pattern_cycles(write_instrs, tile_cols, esz, "swizzle", model, (B, M, S), write=True)
+        cr, _ = pattern_cycles(read_instrs, tile_cols, esz, "swizzle", model, (B, M, S), write=False)
         return cw + cr
 
     best = None

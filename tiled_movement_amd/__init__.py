@@ -33,9 +33,11 @@ EXPORTS = (
     "swz_choose",
     "swz_predict_conflicts",
     "swz_kernel_accesses",
+    "swz_bank_model_get",
     "swz_plan",
     "swz_strerror",
     "swz_lds_probe",
+    "swz_copy",
 )
 
 
@@ -52,6 +54,14 @@ class Params(ctypes.Structure):
         return (self.B, self.M, self.S)
 
 
+class BankModelInfo(ctypes.Structure):
+    _fields_ = [
+        ("n_banks", (ctypes.c_int32 * 3) * 2),
+        ("bank_bytes", (ctypes.c_int32 * 3) * 2),
+        ("phase", ((ctypes.c_uint8 * 64) * 3) * 2),
+    ]
+
+
 class PlanInfo(ctypes.Structure):
     _fields_ = [
         ("read_kind", ctypes.c_int32),
@@ -63,6 +73,7 @@ class PlanInfo(ctypes.Structure):
         ("lds_bytes", ctypes.c_int32),
         ("vec_bytes", ctypes.c_int32),
         ("aligned", ctypes.c_int32),
+        ("threads", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -75,6 +86,7 @@ class PlanInfo(ctypes.Structure):
             "lds_bytes": self.lds_bytes,
             "vec_bytes": self.vec_bytes,
             "aligned": bool(self.aligned),
+            "threads": self.threads,
         }
 
 
@@ -98,9 +110,11 @@ def _load() -> ctypes.CDLL:
     lib.swz_choose.argtypes = [i32, i32, i32, i32, i32, P(Params)]
     lib.swz_predict_conflicts.argtypes = [i32, i32, P(Params), P(i64), P(i64)]
     lib.swz_kernel_accesses.argtypes = [i32, i32, P(Params), i32, P(i32), i32, P(i32), P(i32)]
+    lib.swz_bank_model_get.argtypes = [P(BankModelInfo)]
     lib.swz_plan.argtypes = [i32, i64, i64, i32, i32, i32, P(Params), P(PlanInfo)]
     lib.swz_strerror.argtypes = [ctypes.c_int]
     lib.swz_strerror.restype = ctypes.c_char_p
+    lib.swz_copy.argtypes = [vp, vp, i64, vp]
     lib.swz_lds_probe.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
     for name in EXPORTS:
         if name != "swz_strerror":
@@ -200,6 +214,23 @@ def swz_kernel_accesses(read_kind: int, layout="swizzle", params=None, is_write:
     return [(flat[64 * i:64 * i + 64], w.value) for i in range(n.value)]
 
 
+def swz_bank_model_get() -> dict:
+    """The built-in bank model, keyed by (direction, bytes per lane) with
+    direction "read" or "write": banks, bytes per bank and the phase number
+    of every lane."""
+    m = BankModelInfo()
+    _check(lib.swz_bank_model_get(ctypes.byref(m)), "swz_bank_model_get")
+    out = {}
+    for d, dname in enumerate(("read", "write")):
+        for w, width in enumerate((4, 8, 16)):
+            out[(dname, width)] = {
+                "n_banks": m.n_banks[d][w],
+                "bank_bytes": m.bank_bytes[d][w],
+                "phase": list(m.phase[d][w]),
+            }
+    return out
+
+
 def swz_plan(op: int, rows: int, cols: int, elem_bytes: int, layout="swizzle", read_kind: int = READ_AUTO,
              params=None) -> dict:
     out = PlanInfo()
@@ -216,6 +247,10 @@ def swz_lds_probe(addrs, masks, n_patterns: int, width_bytes: int, is_write: int
                   stream=None) -> None:
     _check(lib.swz_lds_probe(_ptr(addrs), _ptr(masks), n_patterns, width_bytes, is_write, iters, waves,
                              _ptr(cycles), _stream(stream, addrs, masks, cycles)), "swz_lds_probe")
+
+
+def swz_copy(src, dst, nbytes: int, stream=None) -> None:
+    _check(lib.swz_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream, src, dst)), "swz_copy")
 
 
 # Status-returning raw entry points, for callers that test error paths.

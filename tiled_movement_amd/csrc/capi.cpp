@@ -75,6 +75,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     out->lds_bytes = k.tr * (k.tc + pad) * k.esz;
     out->vec_bytes = k.vec;
     out->aligned = aligned ? 1 : 0;
+    out->threads = k.nt;
     (void)rows;
     return SWZ_OK;
 }
@@ -215,6 +216,28 @@ SWZ_API int swz_kernel_accesses(int32_t read_kind, int32_t layout, const swz_par
     int w = 0;
     *n_accesses = swz::kernel_accesses(read_kind, ld, q, is_write != 0, addrs, max_accesses, &w);
     *width = w;
+    return SWZ_OK;
+}
+
+SWZ_API int swz_copy(const void* d_src, void* d_dst, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16) return SWZ_EINVAL;
+    if (bytes == 0) return SWZ_OK;
+    if (!d_src || !d_dst) return SWZ_EINVAL;
+    if (reinterpret_cast<uintptr_t>(d_src) % 16 || reinterpret_cast<uintptr_t>(d_dst) % 16) return SWZ_EINVAL;
+    if (overlaps(d_src, bytes, d_dst, bytes)) return SWZ_EINVAL;
+    return hip_status(swz::launch_copy(d_src, d_dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+SWZ_API int swz_bank_model_get(swz_bank_model* out) {
+    if (!out) return SWZ_EINVAL;
+    const swz::BankModel& m = swz::gfx950_bank_model();
+    for (int d = 0; d < 2; ++d) {
+        for (int w = 0; w < 3; ++w) {
+            out->n_banks[d][w] = m.n_banks[d][w];
+            out->bank_bytes[d][w] = m.bank_bytes[d][w];
+        }
+    }
+    std::memcpy(out->phase, m.phase, sizeof(out->phase));
     return SWZ_OK;
 }
 

@@ -149,7 +149,9 @@ swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles) {
     const int M = ilog2(k.vec / k.esz);
     const int log_tile = ilog2(static_cast<int64_t>(k.tr) * k.tc);
     const int b_max = (log_tile - M) / 2;
-    const int row_bytes = m.n_banks * m.bank_bytes;
+    // B spans one bank row as the reads see it (the layout exists for them).
+    const int rw = k.rwidth == 4 ? 0 : k.rwidth == 8 ? 1 : 2;
+    const int row_bytes = m.n_banks[0][rw] * m.bank_bytes[0][rw];
     int b_rule = row_bytes >= k.vec ? ilog2(row_bytes / k.vec) : 0;
     if (b_rule > b_max) b_rule = b_max;
 

@@ -10,6 +10,20 @@
 
 #include "swz.h"
 
+// Threads per tile of each kernel (tuning knobs; 64 = one wave per tile).
+#ifndef SWZ_NT_SCALAR
+#define SWZ_NT_SCALAR 64
+#endif
+#ifndef SWZ_NT_B64
+#define SWZ_NT_B64 64
+#endif
+#ifndef SWZ_NT_B128
+#define SWZ_NT_B128 128
+#endif
+#ifndef SWZ_NT_STAGE
+#define SWZ_NT_STAGE 256
+#endif
+
 namespace swz {
 
 // Swizzle<B,M,S> of a 32-bit element offset: the B-bit field at bit M+S is
@@ -34,68 +48,161 @@ __host__ __device__ __forceinline__ uint32_t lds_elem(const LdsLayout& L, uint32
 }
 
 // ---------------------------------------------------------------------------
-// Tile shapes and thread counts of each read kind.
+// Tile shapes, thread counts and lane maps of each read kind.
+//
+// Every kernel stages a tile with 16-byte global loads (VEC bytes of LDS per
+// store, SUB stores per global load) and reads it back with RWIDTH-byte LDS
+// loads, RPER of them per output piece.  wcoord(t, i, r, c): the tile element
+// thread t's i-th LDS store starts at; rcoord(t, i, r, c): the same for its
+// i-th LDS load.  Step counts are per thread per tile.
 // ---------------------------------------------------------------------------
 template <int KIND> struct Kind;
 
-// 4-byte elements, 32x32 tile.  Staging: each thread writes single elements,
-// a wave covering two full 128-byte rows.  Read: each thread reads single
-// elements down a column, a wave covering two columns.
+// 4-byte elements, 32x32 tile (128-byte rows).  Staging: thread vector
+// v = t + NT*j (j < 256/NT) holds row v/8, columns 4(v%8)..+3 and stores them
+// as four 4-byte LDS writes (step i = 4j + e writes column 4(v%8)+e).  Read:
+// task u = t + NT*j owns source column u/8 and rows 4(u%8)..+3, read as four
+// 4-byte column reads (step i = 4j + e reads row 4(u%8)+e), and writes them
+// as one 16-byte piece of output row u/8.
 template <> struct Kind<SWZ_READ_SCALAR_COL> {
-    static constexpr int ESZ = 4, TR = 32, TC = 32, NT = 256;
-    static constexpr int VEC = 4;                        // LDS store width (bytes)
-    static constexpr int WSTEPS = TR * TC / NT;          // element stores per thread
-    static constexpr int RSTEPS = TR * TC / NT;          // element loads per thread
-    static constexpr int RWIDTH = 4;                     // LDS load width (bytes)
-    __host__ __device__ static void wcoord(int t, int i, int& r, int& c) { r = t / 32 + i * (NT / 32); c = t % 32; }
-    __host__ __device__ static void rcoord(int t, int i, int& r, int& c) { r = t % 32; c = t / 32 + i * (NT / 32); }
+    static constexpr int ESZ = 4, TR = 32, TC = 32, NT = SWZ_NT_SCALAR;
+    static constexpr int VEC = 4;                     // LDS store width (bytes)
+    static constexpr int RWIDTH = 4;                  // LDS load width (bytes)
+    static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;  // 16-byte global loads per thread
+    static constexpr int WSTEPS = GLOADS * 4;
+    static constexpr int TASKS = TR * TC / 4 / NT;    // 16-byte output pieces per thread
+    static constexpr int RSTEPS = TASKS * 4;
+    __host__ __device__ static constexpr void wcoord(int t, int i, int& r, int& c) {
+        const int v = t + NT * (i / 4);
+        r = v / 8;
+        c = 4 * (v % 8) + i % 4;
+    }
+    __host__ __device__ static constexpr void rcoord(int t, int i, int& r, int& c) {
+        const int u = t + NT * (i / 4);
+        r = 4 * (u % 8) + i % 4;
+        c = u / 8;
+    }
 };
 
-// 2-byte elements, 64x64 tile (128-byte rows).  Staging: 16-byte vectors,
-// 8 lanes per row.  Read: thread q owns row block k = q%8 (rows 8k..8k+7)
-// and column group g = q/8 (columns 4g..4g+3); step i reads the 8 bytes of
-// row 8k+i in that group.
+// 2-byte elements, 64x64 tile (128-byte rows).  Staging: vector v = t + NT*j
+// is row v/8, 16-byte chunk v%8 (one 16-byte LDS write).  Read: task
+// u = t + NT*j owns row block k = u%8 (rows 8k..8k+7) and column group
+// g = u/8 (columns 4g..4g+3); step 8j + s reads the 8 bytes of row 8k+s.
 template <> struct Kind<SWZ_READ_B64_4X4> {
-    static constexpr int ESZ = 2, TR = 64, TC = 64, NT = 128;
+    static constexpr int ESZ = 2, TR = 64, TC = 64, NT = SWZ_NT_B64;
     static constexpr int VEC = 16;
-    static constexpr int WSTEPS = TR * TC * ESZ / VEC / NT;  // 4
-    static constexpr int RSTEPS = 8;
     static constexpr int RWIDTH = 8;
-    __host__ __device__ static void wcoord(int t, int i, int& r, int& c) { r = t / 8 + i * (NT / 8); c = 8 * (t % 8); }
-    __host__ __device__ static void rcoord(int t, int i, int& r, int& c) { r = 8 * (t % 8) + i; c = 4 * (t / 8); }
+    static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
+    static constexpr int WSTEPS = GLOADS;
+    static constexpr int TASKS = 128 / NT;
+    static constexpr int RSTEPS = TASKS * 8;
+    __host__ __device__ static constexpr void wcoord(int t, int i, int& r, int& c) {
+        const int v = t + NT * i;
+        r = v / 8;
+        c = 8 * (v % 8);
+    }
+    __host__ __device__ static constexpr void rcoord(int t, int i, int& r, int& c) {
+        const int u = t + NT * (i / 8);
+        r = 8 * (u % 8) + i % 8;
+        c = 4 * (u / 8);
+    }
 };
 
-// 2-byte elements, 64x128 tile (256-byte rows).  Staging: 16-byte vectors,
-// 16 lanes per row.  Read: thread q owns row block rb = q%8 and 16-byte
-// column chunk ch = q/8; step i reads chunk ch of row 8rb+i.
+// 2-byte elements, 64x128 tile (256-byte rows).  Staging: vector v = t + NT*j
+// is row v/16, chunk v%16.  Read: task u owns row block rb = u%8 and 16-byte
+// chunk ch = u/8; step 8j + s reads chunk ch of row 8rb+s.
 template <> struct Kind<SWZ_READ_B128_8X8> {
-    static constexpr int ESZ = 2, TR = 64, TC = 128, NT = 128;
+    static constexpr int ESZ = 2, TR = 64, TC = 128, NT = SWZ_NT_B128;
     static constexpr int VEC = 16;
-    static constexpr int WSTEPS = TR * TC * ESZ / VEC / NT;  // 8
-    static constexpr int RSTEPS = 8;
     static constexpr int RWIDTH = 16;
-    __host__ __device__ static void wcoord(int t, int i, int& r, int& c) { r = t / 16 + i * (NT / 16); c = 8 * (t % 16); }
-    __host__ __device__ static void rcoord(int t, int i, int& r, int& c) { r = 8 * (t % 8) + i; c = 8 * (t / 8); }
+    static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
+    static constexpr int WSTEPS = GLOADS;
+    static constexpr int TASKS = 128 / NT;
+    static constexpr int RSTEPS = TASKS * 8;
+    __host__ __device__ static constexpr void wcoord(int t, int i, int& r, int& c) {
+        const int v = t + NT * i;
+        r = v / 16;
+        c = 8 * (v % 16);
+    }
+    __host__ __device__ static constexpr void rcoord(int t, int i, int& r, int& c) {
+        const int u = t + NT * (i / 8);
+        r = 8 * (u % 8) + i % 8;
+        c = 8 * (u / 8);
+    }
 };
 
 // Operand staging: 2-byte elements, 256x64 tile (256 rows of the MN
-// dimension, 64 of K; 128-byte rows).  Staging: 16-byte vectors, 8 lanes per
-// row.  Read: the 32 fragments of the tile (16 row blocks x 2 k steps); wave
-// w reads fragments f = w + 4*i; lane l of fragment f reads row
-// 16*(f%16) + l%16, k = 32*(f/16) + 8*(l/16) .. +7.
+// dimension, 64 of K; 128-byte rows).  Staging: vector v = t + NT*j is row
+// v/8, chunk v%8.  Read: the 32 fragments of the tile (16 row blocks x 2 k
+// steps); wave w reads fragments f = w + (NT/64)*i; lane l of fragment f
+// reads row 16*(f%16) + l%16, k = 32*(f/16) + 8*(l/16) .. +7.
 template <> struct Kind<SWZ_READ_MFMA_16X16X32> {
-    static constexpr int ESZ = 2, TR = 256, TC = 64, NT = 256;
+    static constexpr int ESZ = 2, TR = 256, TC = 64, NT = SWZ_NT_STAGE;
     static constexpr int VEC = 16;
-    static constexpr int WSTEPS = TR * TC * ESZ / VEC / NT;  // 8
-    static constexpr int RSTEPS = 8;                          // fragments per wave
     static constexpr int RWIDTH = 16;
-    __host__ __device__ static int frag_of(int t, int i) { return (t / 64) + 4 * i; }
-    __host__ __device__ static void wcoord(int t, int i, int& r, int& c) { r = t / 8 + i * (NT / 8); c = 8 * (t % 8); }
-    __host__ __device__ static void rcoord(int t, int i, int& r, int& c) {
+    static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
+    static constexpr int WSTEPS = GLOADS;
+    static constexpr int RSTEPS = 32 / (NT / 64);  // fragments per wave
+    __host__ __device__ static constexpr int frag_of(int t, int i) { return (t / 64) + (NT / 64) * i; }
+    __host__ __device__ static constexpr void wcoord(int t, int i, int& r, int& c) {
+        const int v = t + NT * i;
+        r = v / 8;
+        c = 8 * (v % 8);
+    }
+    __host__ __device__ static constexpr void rcoord(int t, int i, int& r, int& c) {
         const int f = frag_of(t, i), l = t % 64;
         r = 16 * (f % 16) + l % 16;
         c = 32 * (f / 16) + 8 * (l / 16);
     }
 };
+
+// ---------------------------------------------------------------------------
+// Offsets of a lane's later steps from its first one.
+//
+// In every lane map above, step i's element is the first step's element
+// moved by an amount that does not depend on the lane, and (with rows of TC
+// elements) that amount's offset bits never overlap the first step's offset
+// bits.  The swizzle is linear over GF(2) (x -> x ^ ((x >> (M+S)) & mask) << M),
+// so swizzle(base + d) = swizzle(base ^ d) = swizzle(base) ^ swizzle(d): each
+// access is the lane's one swizzled base XOR a value shared by the whole
+// wave.  For padded rows the same holds with + in place of ^.  The checks
+// below prove the property for every lane and step at compile time.
+// ---------------------------------------------------------------------------
+template <int KIND, bool WRITE>
+__host__ __device__ constexpr void coord(int t, int i, int& r, int& c) {
+    if (WRITE)
+        Kind<KIND>::wcoord(t, i, r, c);
+    else
+        Kind<KIND>::rcoord(t, i, r, c);
+}
+
+template <int KIND, bool WRITE>
+constexpr bool steps_decompose() {
+    using K = Kind<KIND>;
+    const int steps = WRITE ? K::WSTEPS : K::RSTEPS;
+    for (int t = 0; t < K::NT; ++t) {
+        int r0 = 0, c0 = 0;
+        coord<KIND, WRITE>(t, 0, r0, c0);
+        const int base = r0 * K::TC + c0;
+        for (int i = 0; i < steps; ++i) {
+            int r = 0, c = 0, dr = 0, dc = 0;
+            coord<KIND, WRITE>(t, i, r, c);
+            coord<KIND, WRITE>(0, i, dr, dc);  // lane 0 starts at (0, 0)
+            if (r - r0 != dr || c - c0 != dc) return false;
+            if (base & (dr * K::TC + dc)) return false;
+            if (r >= K::TR || c >= K::TC || r < 0 || c < 0) return false;
+        }
+    }
+    return true;
+}
+
+static_assert(steps_decompose<SWZ_READ_SCALAR_COL, true>() && steps_decompose<SWZ_READ_SCALAR_COL, false>(),
+              "scalar-column lane map");
+static_assert(steps_decompose<SWZ_READ_B64_4X4, true>() && steps_decompose<SWZ_READ_B64_4X4, false>(),
+              "4x4 lane map");
+static_assert(steps_decompose<SWZ_READ_B128_8X8, true>() && steps_decompose<SWZ_READ_B128_8X8, false>(),
+              "8x8 lane map");
+static_assert(steps_decompose<SWZ_READ_MFMA_16X16X32, true>() && steps_decompose<SWZ_READ_MFMA_16X16X32, false>(),
+              "fragment lane map");
 
 }  // namespace swz

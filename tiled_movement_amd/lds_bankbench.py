@@ -10,7 +10,7 @@ Pattern families:
   pairc   the same lanes on neighbouring words (control)
   bank    lanes 0 and j, lane j at byte 128 / 256 / 512: which distances
           are bank-equal tells the bank count
-  stride  all lanes, lane l at byte 4*s*l
+  stride  all lanes, lane l at byte width*s*l
   kernel  every LDS access of one tile of each kernel, in each layout
 
 Usage:
@@ -73,9 +73,10 @@ def patterns(families):
                         addrs[0], addrs[j] = 0, dist
                         out.append(pat(f"bank/{tag}/{dist}/{j}", w, wr, addrs))
     if "stride" in families:
-        for wr in (0, 1):
-            for s in (1, 2, 4, 8, 16, 32, 33, 64, 65):
-                out.append(pat(f"stride/{'w' if wr else 'r'}32/{s}", 4, wr, [4 * s * l for l in range(64)]))
+        for w in WIDTHS:
+            for wr in (0, 1):
+                for s in (1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64, 65):
+                    out.append(pat(f"stride/{'w' if wr else 'r'}{8 * w}/{s}", w, wr, [w * s * l for l in range(64)]))
     if "kernel" in families:
         for kind, kname in [(T.READ_SCALAR_COL, "scalar_col"), (T.READ_B64_4X4, "b64_4x4"),
                             (T.READ_B128_8X8, "b128_8x8"), (T.READ_MFMA_16X16X32, "mfma")]:
