@@ -1,60 +1,35 @@
-// Reference device copy (16-byte vectors, several loads in flight per
-// thread) and the resident-grid helper shared by the tile kernels.  The copy
-// is the plain kernel against which HBM byte counters are calibrated and
-// the practical bandwidth ceiling of a read-once / write-once pass.
-#include <map>
-#include <mutex>
-#include <utility>
-
+// Reference device copy: plain 16-byte vector loads and stores, several in
+// flight per thread, non-temporal like the tile kernels' global accesses.
+// It is the read-once / write-once bandwidth ceiling the tile kernels are
+// compared with, and the kernel of known size HBM byte counters are scaled
+// by.
 #include "launch.h"
 
 namespace swz {
-
-int64_t resident_grid(const void* kernel, int threads, int64_t want) {
-    static std::mutex mu;
-    static std::map<std::pair<const void*, int>, int64_t> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    const auto key = std::make_pair(kernel, dev);
-    int64_t cap = 0;
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        auto it = cache.find(key);
-        if (it != cache.end()) cap = it->second;
-    }
-    if (cap == 0) {
-        int cus = 0, per_cu = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu <= 0)
-            per_cu = 1;
-        cap = static_cast<int64_t>(cus) * per_cu;
-        std::lock_guard<std::mutex> lock(mu);
-        cache[key] = cap;
-    }
-    return want < cap ? want : cap;
-}
-
 namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
+constexpr int64_t kCopyChunk = int64_t(kCopyThreads) * kCopyUnroll;  // 16-byte vectors per block step
+constexpr int64_t kMaxGrid = int64_t(1) << 22;
 
-__global__ __launch_bounds__(kCopyThreads) void k_copy(const uint4* __restrict__ s, uint4* __restrict__ d,
+__global__ __launch_bounds__(kCopyThreads) void k_copy(const u32x4* __restrict__ s, u32x4* __restrict__ d,
                                                        int64_t n16) {
-    const int64_t chunk = static_cast<int64_t>(kCopyThreads) * kCopyUnroll;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * chunk + threadIdx.x; base < n16;
-         base += static_cast<int64_t>(gridDim.x) * chunk) {
-        uint4 v[kCopyUnroll];
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyChunk + threadIdx.x; base < n16;
+         base += static_cast<int64_t>(gridDim.x) * kCopyChunk) {
+        if (base + (kCopyUnroll - 1) * kCopyThreads < n16) {
+            u32x4 v[kCopyUnroll];
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
-            const int64_t i = base + u * kCopyThreads;
-            if (i < n16) v[u] = s[i];
-        }
+            for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(&s[base + u * kCopyThreads]);
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
-            const int64_t i = base + u * kCopyThreads;
-            if (i < n16) d[i] = v[u];
+            for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], &d[base + u * kCopyThreads]);
+        } else {
+            for (int u = 0; u < kCopyUnroll; ++u) {
+                const int64_t i = base + u * kCopyThreads;
+                if (i < n16) d[i] = s[i];
+            }
         }
     }
 }
@@ -64,10 +39,10 @@ __global__ __launch_bounds__(kCopyThreads) void k_copy(const uint4* __restrict__
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
     const int64_t n16 = bytes / 16;
     if (n16 == 0) return hipSuccess;
-    const int64_t blocks = (n16 + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
-    const int64_t grid = resident_grid(reinterpret_cast<const void*>(k_copy), kCopyThreads, blocks);
-    hipLaunchKernelGGL(k_copy, dim3(static_cast<unsigned>(grid)), dim3(kCopyThreads), 0, stream,
-                       static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
+    int64_t blocks = (n16 + kCopyChunk - 1) / kCopyChunk;
+    if (blocks > kMaxGrid) blocks = kMaxGrid;
+    hipLaunchKernelGGL(k_copy, dim3(static_cast<unsigned>(blocks)), dim3(kCopyThreads), 0, stream,
+                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
     return hipGetLastError();
 }
 

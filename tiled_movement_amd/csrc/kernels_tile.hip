@@ -9,41 +9,79 @@
 // remap the flat offset of each tile element so that the rows written by a
 // wave and the columns read by a wave both spread over all LDS banks.
 //
-// Each workgroup loops over tiles (grid sized to the resident capacity of
-// the GPU).  The next tile's global loads are issued as soon as the current
-// tile sits in LDS, so they are in flight while the current tile is read
-// back and stored.
+// HBM side (measured on MI355X): with row-major tile order every tile in
+// flight writes the same column offset of rows 2^k bytes apart, so the
+// writes pile onto a few memory channels.  Tiles are therefore visited in
+// diagonal order (consecutive tiles differ in both tile row and tile
+// column), and global loads and stores are non-temporal: every byte is read
+// once and written once.
 #include <type_traits>
 
 #include "launch.h"
 
+#ifndef SWZ_TILE_ORDER  // transposes: 1 = diagonal tile order, 0 = row-major
+#define SWZ_TILE_ORDER 1
+#endif
+#ifndef SWZ_STAGE_ORDER  // operand staging: row-major keeps reads and writes contiguous
+#define SWZ_STAGE_ORDER 0
+#endif
+#ifndef SWZ_NONTEMPORAL  // 1: non-temporal global loads and stores
+#define SWZ_NONTEMPORAL 1
+#endif
+
 namespace swz {
 namespace {
 
-__device__ __forceinline__ void decode_tile(int64_t t, int64_t tiles_r, int64_t tiles_c, int64_t& b, int64_t& tr,
-                                            int64_t& tc) {
-    tc = t % tiles_c;
-    const int64_t q = t / tiles_c;
-    tr = q % tiles_r;
-    b = q / tiles_r;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Tiles per launch; larger jobs are launched in chunks, one tile per
+// workgroup (no loop in the kernel, so nothing is kept live across tiles).
+constexpr int64_t kMaxGrid = int64_t(1) << 22;
+
+__device__ __forceinline__ u32x4 gload16(const uint8_t* p) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+    if (SWZ_NONTEMPORAL) return __builtin_nontemporal_load(q);
+    return *q;
 }
 
-// Word `w` of an 8- or 16-byte register group.
-__device__ __forceinline__ uint32_t word(const uint2& x, int w) { return w == 0 ? x.x : x.y; }
-__device__ __forceinline__ uint32_t word(const uint4& x, int w) {
-    return w == 0 ? x.x : w == 1 ? x.y : w == 2 ? x.z : x.w;
+__device__ __forceinline__ void gstore16(uint8_t* p, u32x4 v) {
+    u32x4* q = reinterpret_cast<u32x4*>(p);
+    if (SWZ_NONTEMPORAL)
+        __builtin_nontemporal_store(v, q);
+    else
+        *q = v;
+}
+
+// Tile (batch b, tile row tr, tile column tc) of linear tile index t.
+// Diagonal order: t -> tr = t % tiles_r, tc = (t / tiles_r + tr) % tiles_c,
+// one-to-one for any grid shape (for each tr, the map q -> (q + tr) mod
+// tiles_c is a permutation).  Row-major: tc fastest.
+template <bool DIAGONAL>
+__device__ __forceinline__ void decode_tile(int64_t t, int64_t tiles_r, int64_t tiles_c, int64_t& b, int64_t& tr,
+                                            int64_t& tc) {
+    const int64_t per = tiles_r * tiles_c;
+    b = t / per;
+    const int64_t w = t - b * per;
+    if (DIAGONAL) {
+        tr = w % tiles_r;
+        tc = (w / tiles_r + tr) % tiles_c;
+    } else {
+        tr = w / tiles_c;
+        tc = w % tiles_c;
+    }
 }
 
 // Element j of row a in the low half, element j of row b in the high half.
 template <typename V>
 __device__ __forceinline__ uint32_t pair_col(const V& a, const V& b, int j) {
-    const uint32_t wa = word(a, j >> 1), wb = word(b, j >> 1);
+    const uint32_t wa = a[j >> 1], wb = b[j >> 1];
     return (j & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
 }
 
 // 16 bytes = 16/ESZ consecutive elements of one row, zero outside the matrix.
 template <int ESZ>
-__device__ __forceinline__ uint4 load16_guarded(const uint8_t* S, int64_t row, int64_t col, int64_t rows,
+__device__ __forceinline__ u32x4 load16_guarded(const uint8_t* S, int64_t row, int64_t col, int64_t rows,
                                                 int64_t cols) {
     constexpr int N = 16 / ESZ;
     uint32_t e[N];
@@ -55,50 +93,26 @@ __device__ __forceinline__ uint4 load16_guarded(const uint8_t* S, int64_t row, i
         else
             e[k] = in ? reinterpret_cast<const uint16_t*>(S)[row * cols + col + k] : 0u;
     }
-    if (ESZ == 4) return make_uint4(e[0], e[1], e[2], e[3]);
-    return make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+    if (ESZ == 4) return u32x4{e[0], e[1], e[2], e[3]};
+    return u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
 }
 
 template <int ESZ>
 __device__ __forceinline__ void store16_guarded(uint8_t* D, int64_t row, int64_t col, int64_t nrows, int64_t ncols,
-                                                const uint4& o) {
+                                                const u32x4& o) {
     if (row >= nrows) return;
-    const uint32_t w[4] = {o.x, o.y, o.z, o.w};
     if (ESZ == 4) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            if (col + k < ncols) reinterpret_cast<uint32_t*>(D)[row * ncols + col + k] = w[k];
+            if (col + k < ncols) reinterpret_cast<uint32_t*>(D)[row * ncols + col + k] = o[k];
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             if (col + k < ncols)
-                reinterpret_cast<uint16_t*>(D)[row * ncols + col + k] = static_cast<uint16_t>(w[k >> 1] >> (16 * (k & 1)));
+                reinterpret_cast<uint16_t*>(D)[row * ncols + col + k] = static_cast<uint16_t>(o[k >> 1] >> (16 * (k & 1)));
     }
 }
 
-// Global loads of one tile into registers.  VEC: unguarded 16-byte loads
-// (whole tile inside the matrix, 16-byte aligned rows); else per element.
-template <int KIND, bool VEC>
-__device__ __forceinline__ void load_tile(const uint8_t* __restrict__ S, int64_t rows, int64_t cols, int64_t r0,
-                                          int64_t c0, int t, uint4* v) {
-    using K = Kind<KIND>;
-    constexpr int PER = 16 / K::ESZ;  // elements per global load
-#pragma unroll
-    for (int j = 0; j < K::GLOADS; ++j) {
-        int r, c;
-        K::wcoord(t, j * (K::WSTEPS / K::GLOADS), r, c);
-        c -= c % PER;  // the vector's first column
-        if (VEC)
-            v[j] = *reinterpret_cast<const uint4*>(S + ((r0 + r) * cols + c0 + c) * K::ESZ);
-        else
-            v[j] = load16_guarded<K::ESZ>(S, r0 + r, c0 + c, rows, cols);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Transpose / layout conversion.  One kernel template for the three read
-// kinds; D holds the transposed tile of every batch entry.
-// ---------------------------------------------------------------------------
 template <int KIND>
 struct LdsTile {
     using K = Kind<KIND>;
@@ -130,22 +144,43 @@ __device__ __forceinline__ uint32_t lane_base(int t, const LdsLayout& L) {
     return swizzle(static_cast<uint32_t>(r * K::TC + c), L.B, L.M, L.S);
 }
 
-// Write the staged registers into LDS.
+// ---------------------------------------------------------------------------
+// Transpose / layout conversion of one tile.
+// ---------------------------------------------------------------------------
+
+// Global loads of one tile into registers.  FULL: unguarded 16-byte loads
+// (whole tile inside the matrix, 16-byte aligned rows); else per element.
+template <int KIND, bool FULL>
+__device__ __forceinline__ void load_tile(const uint8_t* __restrict__ S, int64_t rows, int64_t cols, int64_t r0,
+                                          int64_t c0, int t, u32x4* v) {
+    using K = Kind<KIND>;
+    constexpr int PER = 16 / K::ESZ;  // elements per global load
+#pragma unroll
+    for (int j = 0; j < K::GLOADS; ++j) {
+        int r = 0, c = 0;
+        K::wcoord(t, j * (K::WSTEPS / K::GLOADS), r, c);
+        c -= c % PER;  // the vector's first column
+        if (FULL)
+            v[j] = gload16(S + ((r0 + r) * cols + c0 + c) * K::ESZ);
+        else
+            v[j] = load16_guarded<K::ESZ>(S, r0 + r, c0 + c, rows, cols);
+    }
+}
+
 template <int KIND, bool PADDED>
-__device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const LdsLayout& L, const uint4* v) {
+__device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const LdsLayout& L, const u32x4* v) {
     using K = Kind<KIND>;
     if constexpr (K::ESZ == 4) {
 #pragma unroll
         for (int j = 0; j < K::GLOADS; ++j) {
-            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                reinterpret_cast<uint32_t*>(lds)[step_off<KIND, true, PADDED>(wbase, 4 * j + e, L)] = w[e];
+                reinterpret_cast<uint32_t*>(lds)[step_off<KIND, true, PADDED>(wbase, 4 * j + e, L)] = v[j][e];
         }
     } else {
 #pragma unroll
         for (int j = 0; j < K::GLOADS; ++j)
-            *reinterpret_cast<uint4*>(lds + 2 * step_off<KIND, true, PADDED>(wbase, j, L)) = v[j];
+            *reinterpret_cast<u32x4*>(lds + 2 * step_off<KIND, true, PADDED>(wbase, j, L)) = v[j];
     }
 }
 
@@ -160,23 +195,22 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
         // Task j: four rows of one source column -> 16 bytes of an output row.
 #pragma unroll
         for (int j = 0; j < K::TASKS; ++j) {
-            uint32_t x[4];
+            u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                x[e] = reinterpret_cast<const uint32_t*>(lds)[step_off<KIND, false, PADDED>(rbase, 4 * j + e, L)];
+                o[e] = reinterpret_cast<const uint32_t*>(lds)[step_off<KIND, false, PADDED>(rbase, 4 * j + e, L)];
             int r = 0, c = 0;
             K::rcoord(t, 4 * j, r, c);
-            const uint4 o = make_uint4(x[0], x[1], x[2], x[3]);
             const int64_t orow = c0 + c, ocol = r0 + r;
             if (FULL)
-                *reinterpret_cast<uint4*>(D + (orow * rows + ocol) * 4) = o;
+                gstore16(D + (orow * rows + ocol) * 4, o);
             else
                 store16_guarded<4>(D, orow, ocol, cols, rows, o);
         }
     } else {
         // Task j: 8 rows of a column block; transpose 16-bit elements in
         // registers and write one 16-byte piece of each output row.
-        using R = typename std::conditional<K::RWIDTH == 8, uint2, uint4>::type;
+        using R = typename std::conditional<K::RWIDTH == 8, u32x2, u32x4>::type;
         constexpr int kCols = K::RWIDTH / 2;
 #pragma unroll
         for (int j = 0; j < K::TASKS; ++j) {
@@ -188,11 +222,11 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             K::rcoord(t, 8 * j, rb, cb);
 #pragma unroll
             for (int q = 0; q < kCols; ++q) {
-                const uint4 o = make_uint4(pair_col(x[0], x[1], q), pair_col(x[2], x[3], q),
-                                           pair_col(x[4], x[5], q), pair_col(x[6], x[7], q));
+                const u32x4 o{pair_col(x[0], x[1], q), pair_col(x[2], x[3], q), pair_col(x[4], x[5], q),
+                              pair_col(x[6], x[7], q)};
                 const int64_t orow = c0 + cb + q, ocol = r0 + rb;
                 if (FULL)
-                    *reinterpret_cast<uint4*>(D + (orow * rows + ocol) * 2) = o;
+                    gstore16(D + (orow * rows + ocol) * 2, o);
                 else
                     store16_guarded<2>(D, orow, ocol, cols, rows, o);
             }
@@ -200,151 +234,111 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
     }
 }
 
+template <int KIND, bool PADDED, bool FULL>
+__device__ __forceinline__ void convert_tile(const uint8_t* __restrict__ S, uint8_t* __restrict__ D, int64_t rows,
+                                             int64_t cols, int64_t r0, int64_t c0, uint8_t* lds, uint32_t wbase,
+                                             uint32_t rbase, const LdsLayout& L, int t) {
+    using K = Kind<KIND>;
+    u32x4 v[K::GLOADS];
+    load_tile<KIND, FULL>(S, rows, cols, r0, c0, t, v);
+    lds_store<KIND, PADDED>(lds, wbase, L, v);
+    __syncthreads();
+    lds_read_store<KIND, PADDED, FULL>(lds, rbase, L, D, rows, cols, r0, c0, t);
+}
+
 template <int KIND, bool PADDED, bool ALIGNED>
 __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                             int64_t rows, int64_t cols, int64_t tiles_r,
-                                                            int64_t tiles_c, int64_t n_tiles, LdsLayout L) {
+                                                            int64_t tiles_c, int64_t tile0, LdsLayout L) {
     using K = Kind<KIND>;
-    __shared__ uint4 lds_v[LdsTile<KIND>::BYTES / 16];
+    __shared__ u32x4 lds_v[LdsTile<KIND>::BYTES / 16];
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
     const int t = threadIdx.x;
     const int64_t plane = rows * cols * K::ESZ;  // bytes of one batch entry
     const uint32_t wbase = lane_base<KIND, true, PADDED>(t, L);
     const uint32_t rbase = lane_base<KIND, false, PADDED>(t, L);
 
-    auto full_tile = [&](int64_t r0, int64_t c0) { return ALIGNED && r0 + K::TR <= rows && c0 + K::TC <= cols; };
-
-    int64_t tile = blockIdx.x;
-    if (tile >= n_tiles) return;
-    uint4 v[K::GLOADS];
     int64_t b, tr, tc;
-    decode_tile(tile, tiles_r, tiles_c, b, tr, tc);
-    int64_t r0 = tr * K::TR, c0 = tc * K::TC;
-    if (full_tile(r0, c0))
-        load_tile<KIND, true>(src + b * plane, rows, cols, r0, c0, t, v);
+    decode_tile<SWZ_TILE_ORDER != 0>(tile0 + blockIdx.x, tiles_r, tiles_c, b, tr, tc);
+    const int64_t r0 = tr * K::TR, c0 = tc * K::TC;
+    const uint8_t* S = src + b * plane;
+    uint8_t* D = dst + b * plane;
+    if (ALIGNED && r0 + K::TR <= rows && c0 + K::TC <= cols)
+        convert_tile<KIND, PADDED, true>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
     else
-        load_tile<KIND, false>(src + b * plane, rows, cols, r0, c0, t, v);
-
-    for (;;) {
-        lds_store<KIND, PADDED>(lds, wbase, L, v);
-        __syncthreads();
-
-        // Prefetch the next tile while this one is read back and stored.
-        const int64_t next = tile + gridDim.x;
-        int64_t nb = 0, ntr = 0, ntc = 0;
-        if (next < n_tiles) {
-            decode_tile(next, tiles_r, tiles_c, nb, ntr, ntc);
-            if (full_tile(ntr * K::TR, ntc * K::TC))
-                load_tile<KIND, true>(src + nb * plane, rows, cols, ntr * K::TR, ntc * K::TC, t, v);
-            else
-                load_tile<KIND, false>(src + nb * plane, rows, cols, ntr * K::TR, ntc * K::TC, t, v);
-        }
-
-        if (full_tile(r0, c0))
-            lds_read_store<KIND, PADDED, true>(lds, rbase, L, dst + b * plane, rows, cols, r0, c0, t);
-        else
-            lds_read_store<KIND, PADDED, false>(lds, rbase, L, dst + b * plane, rows, cols, r0, c0, t);
-        __syncthreads();
-
-        if (next >= n_tiles) break;
-        tile = next;
-        b = nb;
-        r0 = ntr * K::TR;
-        c0 = ntc * K::TC;
-    }
+        convert_tile<KIND, PADDED, false>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
 }
 
 // ---------------------------------------------------------------------------
 // Operand staging: 256x64 K-tiles of a K-contiguous 16-bit operand, read
 // back as 16x16x32 operand fragments and written out in lane order.
 // ---------------------------------------------------------------------------
-template <bool FULL>
-__device__ __forceinline__ void stage_load(const uint16_t* __restrict__ src, int64_t mn, int64_t k, int64_t r0,
-                                           int64_t k0, int t, uint4* v) {
-    using K = Kind<SWZ_READ_MFMA_16X16X32>;
+template <bool PADDED, bool FULL>
+__device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint8_t* __restrict__ frag, int64_t mn,
+                                           int64_t k, int64_t r0, int64_t k0, uint8_t* lds, uint32_t wbase,
+                                           uint32_t rbase, const LdsLayout& L, int t) {
+    constexpr int KD = SWZ_READ_MFMA_16X16X32;
+    using K = Kind<KD>;
+    u32x4 v[K::GLOADS];
 #pragma unroll
     for (int j = 0; j < K::GLOADS; ++j) {
-        int r, c;
+        int r = 0, c = 0;
         K::wcoord(t, j, r, c);
         // mn and k are multiples of 16 and 32, so a 16-byte chunk is either
         // wholly inside the operand or wholly outside.
-        v[j] = (FULL || (r0 + r < mn && k0 + c < k)) ? *reinterpret_cast<const uint4*>(src + (r0 + r) * k + k0 + c)
-                                                     : make_uint4(0u, 0u, 0u, 0u);
+        v[j] = (FULL || (r0 + r < mn && k0 + c < k)) ? gload16(src + ((r0 + r) * k + k0 + c) * 2) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < K::GLOADS; ++j) *reinterpret_cast<u32x4*>(lds + 2 * step_off<KD, true, PADDED>(wbase, j, L)) = v[j];
+    __syncthreads();
+    const int64_t ksteps = k / 32;
+    const int lane = t % 64;
+#pragma unroll
+    for (int i = 0; i < K::RSTEPS; ++i) {
+        const int f = K::frag_of(t, i);
+        const int blk = f % 16, ks = f / 16;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(lds + 2 * step_off<KD, false, PADDED>(rbase, i, L));
+        if (FULL || (r0 + 16 * blk < mn && k0 + 32 * ks < k)) {
+            const int64_t fi = (r0 / 16 + blk) * ksteps + (k0 / 32 + ks);
+            gstore16(frag + (fi * 64 + lane) * 16, x);
+        }
     }
 }
 
 template <bool PADDED>
-__global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(const uint16_t* __restrict__ src,
-                                                                            uint4* __restrict__ frag, int64_t mn,
-                                                                            int64_t k, int64_t tiles_k,
-                                                                            int64_t n_tiles, LdsLayout L) {
-    using K = Kind<SWZ_READ_MFMA_16X16X32>;
-    __shared__ uint4 lds_v[LdsTile<SWZ_READ_MFMA_16X16X32>::BYTES / 16];
-    uint16_t* lds = reinterpret_cast<uint16_t*>(lds_v);
-    const int t = threadIdx.x, lane = t % 64;
-
+__global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(const uint8_t* __restrict__ src,
+                                                                            uint8_t* __restrict__ frag, int64_t mn,
+                                                                            int64_t k, int64_t tiles_m,
+                                                                            int64_t tiles_k, int64_t tile0,
+                                                                            LdsLayout L) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
+    using K = Kind<KD>;
+    __shared__ u32x4 lds_v[LdsTile<KD>::BYTES / 16];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
+    const int t = threadIdx.x;
     const uint32_t wbase = lane_base<KD, true, PADDED>(t, L);
     const uint32_t rbase = lane_base<KD, false, PADDED>(t, L);
-    const int64_t ksteps = k / 32;
-    auto full_tile = [&](int64_t r0, int64_t k0) { return r0 + K::TR <= mn && k0 + K::TC <= k; };
 
-    int64_t tile = blockIdx.x;
-    if (tile >= n_tiles) return;
-    int64_t r0 = (tile / tiles_k) * K::TR, k0 = (tile % tiles_k) * K::TC;
-    uint4 v[K::GLOADS];
-    if (full_tile(r0, k0))
-        stage_load<true>(src, mn, k, r0, k0, t, v);
+    int64_t b, tm, tk;
+    decode_tile<SWZ_STAGE_ORDER != 0>(tile0 + blockIdx.x, tiles_m, tiles_k, b, tm, tk);
+    const int64_t r0 = tm * K::TR, k0 = tk * K::TC;
+    if (r0 + K::TR <= mn && k0 + K::TC <= k)
+        stage_tile<PADDED, true>(src, frag, mn, k, r0, k0, lds, wbase, rbase, L, t);
     else
-        stage_load<false>(src, mn, k, r0, k0, t, v);
-
-    for (;;) {
-#pragma unroll
-        for (int j = 0; j < K::GLOADS; ++j) *reinterpret_cast<uint4*>(lds + step_off<KD, true, PADDED>(wbase, j, L)) = v[j];
-        __syncthreads();
-
-        const int64_t next = tile + gridDim.x;
-        const int64_t nr0 = (next / tiles_k) * K::TR, nk0 = (next % tiles_k) * K::TC;
-        if (next < n_tiles) {
-            if (full_tile(nr0, nk0))
-                stage_load<true>(src, mn, k, nr0, nk0, t, v);
-            else
-                stage_load<false>(src, mn, k, nr0, nk0, t, v);
-        }
-
-        const bool full = full_tile(r0, k0);
-#pragma unroll
-        for (int i = 0; i < K::RSTEPS; ++i) {
-            const int f = K::frag_of(t, i);
-            const int blk = f % 16, ks = f / 16;
-            const uint4 x = *reinterpret_cast<const uint4*>(lds + step_off<KD, false, PADDED>(rbase, i, L));
-            if (full || (r0 + 16 * blk < mn && k0 + 32 * ks < k)) {
-                const int64_t fi = (r0 / 16 + blk) * ksteps + (k0 / 32 + ks);
-                frag[fi * 64 + lane] = x;
-            }
-        }
-        __syncthreads();
-        if (next >= n_tiles) break;
-        tile = next;
-        r0 = nr0;
-        k0 = nk0;
-    }
+        stage_tile<PADDED, false>(src, frag, mn, k, r0, k0, lds, wbase, rbase, L, t);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <typename F>
-int64_t grid_for(F kernel, int threads, int64_t n_tiles) {
-    return resident_grid(reinterpret_cast<const void*>(kernel), threads, n_tiles);
-}
-
 template <int KIND, bool PADDED, bool ALIGNED>
 void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64_t n_tiles, hipStream_t stream) {
     using K = Kind<KIND>;
-    const int64_t grid = grid_for(k_convert<KIND, PADDED, ALIGNED>, K::NT, n_tiles);
-    hipLaunchKernelGGL((k_convert<KIND, PADDED, ALIGNED>), dim3(static_cast<unsigned>(grid)), dim3(K::NT), 0, stream,
-                       static_cast<const uint8_t*>(j.src), static_cast<uint8_t*>(j.dst), j.rows, j.cols, tiles_r,
-                       tiles_c, n_tiles, j.layout);
+    for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
+        const int64_t n = n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid;
+        hipLaunchKernelGGL((k_convert<KIND, PADDED, ALIGNED>), dim3(static_cast<unsigned>(n)), dim3(K::NT), 0, stream,
+                           static_cast<const uint8_t*>(j.src), static_cast<uint8_t*>(j.dst), j.rows, j.cols, tiles_r,
+                           tiles_c, t0, j.layout);
+    }
 }
 
 template <int KIND>
@@ -381,23 +375,23 @@ hipError_t launch_convert(int kind, const ConvertJob& j, hipStream_t stream) {
 }
 
 hipError_t launch_stage(const StageJob& j, hipStream_t stream) {
-    using K = Kind<SWZ_READ_MFMA_16X16X32>;
+    constexpr int KD = SWZ_READ_MFMA_16X16X32;
+    using K = Kind<KD>;
     const int64_t tiles_m = ceil_div(j.mn, K::TR), tiles_k = ceil_div(j.k, K::TC);
     const int64_t n_tiles = tiles_m * tiles_k;
     if (n_tiles == 0) return hipSuccess;
     const bool padded = j.layout.ld != static_cast<uint32_t>(K::TC);
-    if (padded && j.layout.ld != static_cast<uint32_t>(K::TC + LdsTile<SWZ_READ_MFMA_16X16X32>::PAD))
-        return hipErrorInvalidValue;
-    const auto* s = static_cast<const uint16_t*>(j.src);
-    auto* f = static_cast<uint4*>(j.frag);
-    if (padded) {
-        const int64_t grid = grid_for(k_stage<true>, K::NT, n_tiles);
-        hipLaunchKernelGGL(k_stage<true>, dim3(static_cast<unsigned>(grid)), dim3(K::NT), 0, stream, s, f, j.mn, j.k,
-                           tiles_k, n_tiles, j.layout);
-    } else {
-        const int64_t grid = grid_for(k_stage<false>, K::NT, n_tiles);
-        hipLaunchKernelGGL(k_stage<false>, dim3(static_cast<unsigned>(grid)), dim3(K::NT), 0, stream, s, f, j.mn, j.k,
-                           tiles_k, n_tiles, j.layout);
+    if (padded && j.layout.ld != static_cast<uint32_t>(K::TC + LdsTile<KD>::PAD)) return hipErrorInvalidValue;
+    const auto* s = static_cast<const uint8_t*>(j.src);
+    auto* f = static_cast<uint8_t*>(j.frag);
+    for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
+        const dim3 grid(static_cast<unsigned>(n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid));
+        if (padded)
+            hipLaunchKernelGGL(k_stage<true>, grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k, t0,
+                               j.layout);
+        else
+            hipLaunchKernelGGL(k_stage<false>, grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k, t0,
+                               j.layout);
     }
     return hipGetLastError();
 }

@@ -23,11 +23,6 @@ struct StageJob {
     LdsLayout layout;
 };
 
-// Workgroups to launch for `want` independent work items: all of them if
-// that fits the resident capacity of the current device (CUs x workgroups
-// per CU for this kernel), else that capacity.  Cached per kernel and device.
-int64_t resident_grid(const void* kernel, int threads, int64_t want);
-
 hipError_t launch_convert(int kind, const ConvertJob& job, hipStream_t stream);
 hipError_t launch_stage(const StageJob& job, hipStream_t stream);
 hipError_t launch_map(const int32_t* in, int32_t* out, int64_t n, swz_params p, hipStream_t stream);

@@ -12,10 +12,10 @@
 
 // Threads per tile of each kernel (tuning knobs; 64 = one wave per tile).
 #ifndef SWZ_NT_SCALAR
-#define SWZ_NT_SCALAR 64
+#define SWZ_NT_SCALAR 128
 #endif
 #ifndef SWZ_NT_B64
-#define SWZ_NT_B64 64
+#define SWZ_NT_B64 128
 #endif
 #ifndef SWZ_NT_B128
 #define SWZ_NT_B128 128
@@ -28,11 +28,12 @@ namespace swz {
 
 // Swizzle<B,M,S> of a 32-bit element offset: the B-bit field at bit M+S is
 // XORed into the B-bit field at bit M ("CuTe Swizzle 学习手册", swizzle
-// formula).  B == 0 is the identity.  Callers guarantee M+S+B <= 32.
+// formula).  B == 0 is the identity.  Written without branches (selects
+// only) and without shifts by 32 or more, which C++ leaves undefined.
 __host__ __device__ __forceinline__ uint32_t swizzle(uint32_t x, uint32_t B, uint32_t M, uint32_t S) {
-    if (B == 0) return x;
-    const uint32_t mask = (B >= 32u) ? 0xffffffffu : ((1u << B) - 1u);
-    return x ^ (((x >> (M + S)) & mask) << M);
+    const uint32_t mask = B >= 32u ? 0xffffffffu : ((1u << B) - 1u);
+    const uint32_t src = (M + S) >= 32u ? 0u : ((x >> (M + S)) & mask);
+    return x ^ (M >= 32u ? 0u : (src << M));
 }
 
 // How a tile sits in LDS: element (r, c) lives at element offset
