@@ -22,6 +22,7 @@ Usage:
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -45,8 +46,36 @@ WORKLOADS = {
 }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ("kernels_tile.hip", "kernels_copy.hip", "swz_common.h")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_digest():
+    """sha256 of the kernel sources the HBM counters in TRAFFIC_FILE were taken on."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tiled_movement_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, each
+    scaled by the same counter's reading for the reference copy; None when
+    no such record exists or the kernels changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None
+    rec = data.get("workloads", {}).get(name)
+    return None if rec is None else rec.get("bytes_per_launch")
 
 
 def n_pairs(bytes_per_pair):
@@ -303,7 +332,8 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(value / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(name),
+            "algorithmic_bytes_per_launch": nbytes // launches,
             "launches_per_step": launches,
         },
         "cpu_baseline": cpu,

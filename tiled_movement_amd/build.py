@@ -59,6 +59,18 @@ def flags():
     ]
 
 
+def build_test_helper(verbose: bool = False) -> str:
+    """The tests' hardware probe (tests/mfma_probe.hip -> tests/libmfma_probe.so)."""
+    src = os.path.join(ROOT, "tests", "mfma_probe.hip")
+    out = os.path.join(ROOT, "tests", "libmfma_probe.so")
+    cmd = [hipcc()] + flags() + ["-shared", "-o", out + ".tmp", "-x", "hip", src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
     """Compile every source into one shared library; returns its path."""
     cmd = [hipcc()] + flags() + list(extra) + ["-shared", "-o", out + ".tmp"]
@@ -75,3 +87,4 @@ def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
 
 if __name__ == "__main__":
     print(build(verbose="--verbose" in sys.argv))
+    print(build_test_helper(verbose="--verbose" in sys.argv))

@@ -123,15 +123,22 @@ struct LdsTile {
 
 // Element offset in LDS of step i of this lane: the lane's first offset
 // `base` combined with the step's lane-independent move (see steps_decompose).
-// PADDED: rows of TC + PAD elements, offsets add (compile-time constants).
-// Otherwise rows of TC elements under Swizzle<B,M,S> (B = 0: plain rows),
-// offsets combine by XOR with a value uniform across the wave.
+// PADDED: rows of L.ld = TC + PAD elements, offsets add.  Otherwise rows of
+// TC elements under Swizzle<B,M,S> (B = 0: plain rows), offsets combine by
+// XOR.  Either way the move is one value shared by the wave; the row pitch
+// is a run-time value in both, so the three layouts issue the same LDS
+// instructions (no pairing into two-address forms for one of them) and
+// differ only in the addresses.
 template <int KIND, bool WRITE, bool PADDED>
 __device__ __forceinline__ uint32_t step_off(uint32_t base, int i, const LdsLayout& L) {
     using K = Kind<KIND>;
     int dr = 0, dc = 0;
     coord<KIND, WRITE>(0, i, dr, dc);
-    if (PADDED) return base + static_cast<uint32_t>(dr * (K::TC + LdsTile<KIND>::PAD) + dc);
+    if (PADDED) {
+        uint32_t d = static_cast<uint32_t>(dr) * L.ld + static_cast<uint32_t>(dc);
+        asm volatile("" : "+s"(d));  // keep the move opaque: no two-address pairing
+        return base + d;
+    }
     return base ^ swizzle(static_cast<uint32_t>(dr * K::TC + dc), L.B, L.M, L.S);
 }
 
@@ -140,7 +147,7 @@ __device__ __forceinline__ uint32_t lane_base(int t, const LdsLayout& L) {
     using K = Kind<KIND>;
     int r = 0, c = 0;
     coord<KIND, WRITE>(t, 0, r, c);
-    if (PADDED) return static_cast<uint32_t>(r * (K::TC + LdsTile<KIND>::PAD) + c);
+    if (PADDED) return static_cast<uint32_t>(r) * L.ld + static_cast<uint32_t>(c);
     return swizzle(static_cast<uint32_t>(r * K::TC + c), L.B, L.M, L.S);
 }
 
