@@ -25,6 +25,9 @@
 #ifndef SWZ_STAGE_ORDER  // operand staging: row-major keeps reads and writes contiguous
 #define SWZ_STAGE_ORDER 0
 #endif
+#ifndef SWZ_GRID3D  // 1: 3-D grids (tile row, tile column, batch) where they fit
+#define SWZ_GRID3D 1
+#endif
 #ifndef SWZ_NONTEMPORAL  // 1: non-temporal global loads and stores
 #define SWZ_NONTEMPORAL 1
 #endif
@@ -253,7 +256,29 @@ __device__ __forceinline__ void convert_tile(const uint8_t* __restrict__ S, uint
     lds_read_store<KIND, PADDED, FULL>(lds, rbase, L, D, rows, cols, r0, c0, t);
 }
 
-template <int KIND, bool PADDED, bool ALIGNED>
+// Which tile this workgroup moves.  GRID3D: blockIdx = (tile row, tile
+// column step, batch entry), the diagonal order needing one 32-bit modulo;
+// otherwise a 1-D chunk of the linear tile order (grids beyond the
+// hardware's y / z limits).
+template <bool DIAGONAL, bool GRID3D>
+__device__ __forceinline__ void my_tile(int64_t tiles_r, int64_t tiles_c, int64_t tile0, int64_t& b, int64_t& tr,
+                                        int64_t& tc) {
+    if (GRID3D) {
+        b = blockIdx.z;
+        if (DIAGONAL) {
+            tr = blockIdx.x;
+            tc = static_cast<int64_t>((blockIdx.y + blockIdx.x % static_cast<uint32_t>(tiles_c)) %
+                                      static_cast<uint32_t>(tiles_c));
+        } else {
+            tc = blockIdx.x;
+            tr = blockIdx.y;
+        }
+    } else {
+        decode_tile<DIAGONAL>(tile0 + blockIdx.x, tiles_r, tiles_c, b, tr, tc);
+    }
+}
+
+template <int KIND, bool PADDED, bool ALIGNED, bool GRID3D>
 __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                             int64_t rows, int64_t cols, int64_t tiles_r,
                                                             int64_t tiles_c, int64_t tile0, LdsLayout L) {
@@ -266,7 +291,7 @@ __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __res
     const uint32_t rbase = lane_base<KIND, false, PADDED>(t, L);
 
     int64_t b, tr, tc;
-    decode_tile<SWZ_TILE_ORDER != 0>(tile0 + blockIdx.x, tiles_r, tiles_c, b, tr, tc);
+    my_tile<SWZ_TILE_ORDER != 0, GRID3D>(tiles_r, tiles_c, tile0, b, tr, tc);
     const int64_t r0 = tr * K::TR, c0 = tc * K::TC;
     const uint8_t* S = src + b * plane;
     uint8_t* D = dst + b * plane;
@@ -312,7 +337,7 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint
     }
 }
 
-template <bool PADDED>
+template <bool PADDED, bool GRID3D>
 __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(const uint8_t* __restrict__ src,
                                                                             uint8_t* __restrict__ frag, int64_t mn,
                                                                             int64_t k, int64_t tiles_m,
@@ -327,7 +352,7 @@ __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(cons
     const uint32_t rbase = lane_base<KD, false, PADDED>(t, L);
 
     int64_t b, tm, tk;
-    decode_tile<SWZ_STAGE_ORDER != 0>(tile0 + blockIdx.x, tiles_m, tiles_k, b, tm, tk);
+    my_tile<SWZ_STAGE_ORDER != 0, GRID3D>(tiles_m, tiles_k, tile0, b, tm, tk);
     const int64_t r0 = tm * K::TR, k0 = tk * K::TC;
     if (r0 + K::TR <= mn && k0 + K::TC <= k)
         stage_tile<PADDED, true>(src, frag, mn, k, r0, k0, lds, wbase, rbase, L, t);
@@ -337,14 +362,29 @@ __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(cons
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Grid limits of a 3-D launch: work-items along x below 2^31, y and z up to
+// 65535 workgroups.
+bool fits_3d(int64_t x, int64_t y, int64_t z, int threads) {
+    return SWZ_GRID3D && x * threads < (int64_t(1) << 31) && y <= 65535 && z <= 65535;
+}
+
 template <int KIND, bool PADDED, bool ALIGNED>
 void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64_t n_tiles, hipStream_t stream) {
     using K = Kind<KIND>;
+    const auto* s = static_cast<const uint8_t*>(j.src);
+    auto* d = static_cast<uint8_t*>(j.dst);
+    const bool diag = SWZ_TILE_ORDER != 0;
+    const int64_t gx = diag ? tiles_r : tiles_c, gy = diag ? tiles_c : tiles_r;
+    if (fits_3d(gx, gy, j.batch, K::NT)) {
+        hipLaunchKernelGGL((k_convert<KIND, PADDED, ALIGNED, true>),
+                           dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(j.batch)),
+                           dim3(K::NT), 0, stream, s, d, j.rows, j.cols, tiles_r, tiles_c, int64_t(0), j.layout);
+        return;
+    }
     for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
         const int64_t n = n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid;
-        hipLaunchKernelGGL((k_convert<KIND, PADDED, ALIGNED>), dim3(static_cast<unsigned>(n)), dim3(K::NT), 0, stream,
-                           static_cast<const uint8_t*>(j.src), static_cast<uint8_t*>(j.dst), j.rows, j.cols, tiles_r,
-                           tiles_c, t0, j.layout);
+        hipLaunchKernelGGL((k_convert<KIND, PADDED, ALIGNED, false>), dim3(static_cast<unsigned>(n)), dim3(K::NT), 0,
+                           stream, s, d, j.rows, j.cols, tiles_r, tiles_c, t0, j.layout);
     }
 }
 
@@ -391,14 +431,26 @@ hipError_t launch_stage(const StageJob& j, hipStream_t stream) {
     if (padded && j.layout.ld != static_cast<uint32_t>(K::TC + LdsTile<KD>::PAD)) return hipErrorInvalidValue;
     const auto* s = static_cast<const uint8_t*>(j.src);
     auto* f = static_cast<uint8_t*>(j.frag);
+    const bool diag = SWZ_STAGE_ORDER != 0;
+    const int64_t gx = diag ? tiles_m : tiles_k, gy = diag ? tiles_k : tiles_m;
+    if (fits_3d(gx, gy, 1, K::NT)) {
+        const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy), 1);
+        if (padded)
+            hipLaunchKernelGGL((k_stage<true, true>), grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k,
+                               int64_t(0), j.layout);
+        else
+            hipLaunchKernelGGL((k_stage<false, true>), grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k,
+                               int64_t(0), j.layout);
+        return hipGetLastError();
+    }
     for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
         const dim3 grid(static_cast<unsigned>(n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid));
         if (padded)
-            hipLaunchKernelGGL(k_stage<true>, grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k, t0,
-                               j.layout);
+            hipLaunchKernelGGL((k_stage<true, false>), grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m,
+                               tiles_k, t0, j.layout);
         else
-            hipLaunchKernelGGL(k_stage<false>, grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k, t0,
-                               j.layout);
+            hipLaunchKernelGGL((k_stage<false, false>), grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m,
+                               tiles_k, t0, j.layout);
     }
     return hipGetLastError();
 }

@@ -12,7 +12,7 @@
 
 // Threads per tile of each kernel (tuning knobs; 64 = one wave per tile).
 #ifndef SWZ_NT_SCALAR
-#define SWZ_NT_SCALAR 128
+#define SWZ_NT_SCALAR 256
 #endif
 #ifndef SWZ_NT_B64
 #define SWZ_NT_B64 128
@@ -196,6 +196,22 @@ constexpr bool steps_decompose() {
     }
     return true;
 }
+
+// Thread counts must split each tile's loads and read-back tasks evenly.
+template <int KIND>
+constexpr bool even_split() {
+    using K = Kind<KIND>;
+    return K::NT % 64 == 0 && K::GLOADS >= 1 && K::GLOADS * K::NT * 16 == K::TR * K::TC * K::ESZ &&
+           K::RSTEPS >= 1;
+}
+static_assert(even_split<SWZ_READ_SCALAR_COL>() && Kind<SWZ_READ_SCALAR_COL>::TASKS * Kind<SWZ_READ_SCALAR_COL>::NT * 4 == 32 * 32,
+              "scalar-column thread count");
+static_assert(even_split<SWZ_READ_B64_4X4>() && Kind<SWZ_READ_B64_4X4>::TASKS * Kind<SWZ_READ_B64_4X4>::NT == 128,
+              "4x4 thread count");
+static_assert(even_split<SWZ_READ_B128_8X8>() && Kind<SWZ_READ_B128_8X8>::TASKS * Kind<SWZ_READ_B128_8X8>::NT == 128,
+              "8x8 thread count");
+static_assert(even_split<SWZ_READ_MFMA_16X16X32>() && Kind<SWZ_READ_MFMA_16X16X32>::RSTEPS * (Kind<SWZ_READ_MFMA_16X16X32>::NT / 64) == 32,
+              "fragment thread count");
 
 static_assert(steps_decompose<SWZ_READ_SCALAR_COL, true>() && steps_decompose<SWZ_READ_SCALAR_COL, false>(),
               "scalar-column lane map");
