@@ -43,6 +43,8 @@ WORKLOADS = {
     "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
     "copy": "reference 16-byte vector copy of 64 MiB (read once, write once)",
+    "copy_128": "reference 16-byte vector copy of 128 MiB (the byte count of the 256 MiB workloads)",
+    "memcpy_d2d": "runtime device-to-device copy (hipMemcpyAsync through torch) of 64 MiB, for context",
 }
 
 
@@ -211,8 +213,8 @@ def build(ctx, name, layout):
         info["_keep"] = (x, y)
         return step, 2 * 65536 * 4, info
 
-    if name == "copy":
-        nbytes = 64 * 2**20
+    if name in ("copy", "copy_128", "memcpy_d2d"):
+        nbytes = (128 if name == "copy_128" else 64) * 2**20
         k = n_pairs(2 * nbytes)
         srcs = [ctx.torch.zeros(nbytes // 4, dtype=ctx.torch.int32, device=ctx.dev) for _ in range(k)]
         dsts = [ctx.torch.empty_like(s) for s in srcs]
@@ -220,6 +222,9 @@ def build(ctx, name, layout):
 
         def step(i):
             j = i % k
+            if name == "memcpy_d2d":
+                dsts[j].copy_(srcs[j])
+                return
             rc = lib.swz_copy(sp[j], dp[j], nbytes, stream)
             if rc:
                 ctx.check(rc, "swz_copy")
@@ -232,27 +237,41 @@ def build(ctx, name, layout):
 
 
 def cpu_baseline(a, dst_dev, seconds):
-    """The oracle's transpose of the headline input, timed on the host (one
-    thread), bounded to about `seconds`; also checks the GPU result."""
+    """The oracle's transpose of the headline input, timed on the host cores
+    and bounded to about `seconds` in all: the plain C oracle with one thread
+    per host core (at most 16, the machine's CPU share), then with one thread,
+    then the NumPy oracle; also checks the GPU result against it."""
     import numpy as np
 
     import oracle
+    from oracle import c_ref
 
     got = dst_dev.cpu().numpy().view(np.uint32)
-    reps, t_cpu, ref = 0, 0.0, None
-    while t_cpu < seconds or reps == 0:
-        t1 = time.perf_counter()
-        ref = oracle.transpose(a)
-        t_cpu += time.perf_counter() - t1
-        reps += 1
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def rate(fn, budget):
+        reps, t, out = 0, 0.0, None
+        while t < budget or reps == 0:
+            t1 = time.perf_counter()
+            out = fn()
+            t += time.perf_counter() - t1
+            reps += 1
+        return a.nbytes * 2 * reps / t / 1e9, reps, t, out
+
+    c_ref.lib()  # compile outside the timed loop
+    v_n, reps_n, t_n, ref = rate(lambda: c_ref.convert_layout(a, threads), 0.5 * seconds)
+    v_1, reps_1, t_1, _ = rate(lambda: c_ref.convert_layout(a, 1), 0.25 * seconds)
+    v_np, reps_np, t_np, ref_np = rate(lambda: oracle.transpose(a), 0.25 * seconds)
     return {
-        "value": round(a.nbytes * 2 * reps / t_cpu / 1e9, 3),
+        "value": round(v_n, 3),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{reps} full 4096x4096 fp32 transposes by the oracle (NumPy strided copy, one thread), "
-                  f"{t_cpu:.1f} s",
-        "matches_gpu": bool(np.array_equal(ref, got)),
+        "sample": f"{reps_n} full 4096x4096 fp32 transposes by the plain C oracle (scalar loops, gcc -O2, "
+                  f"{threads} threads), {t_n:.1f} s",
+        "single_thread_GBps": round(v_1, 3),
+        "numpy_oracle_GBps": round(v_np, 3),
+        "matches_gpu": bool(np.array_equal(ref.view(np.uint32), got) and np.array_equal(ref_np.view(np.uint32), got)),
     }
 
 
@@ -284,8 +303,8 @@ def main(argv=None):
 
     extra = {}
     if not args.quick and args.workload is None:
-        for wname in ("copy", "fp32_transpose", "fp16_transpose", "bf16_convert", "bf16_stage", "map"):
-            for lay in (("swizzle",) if wname in ("copy", "map") else ("swizzle", "pad", "plain")):
+        for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "bf16_convert", "bf16_stage", "map"):
+            for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map") else ("swizzle", "pad", "plain")):
                 s2, nb2, inf2 = build(ctx, wname, lay)
                 if wname == "map":
                     rate, ms2 = median_rate(s2, nb2, steps=250, warmup=25)
@@ -323,7 +342,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32_transpose": "f32", "fp16_transpose": "f16", "map": "int32", "copy": "u8"}.get(name, "bf16"),
+        "dtype": {"fp32_transpose": "f32", "fp16_transpose": "f16", "map": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
         "data": "synthetic",
         "config": {k: v for k, v in info.items() if not k.startswith("_")},
         "roofline": {
