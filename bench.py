@@ -278,11 +278,11 @@ def cpu_baseline(a, dst_dev, seconds):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only, no other workloads")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=None)
-    ap.add_argument("--layout", choices=["swizzle", "pad", "plain"], default="swizzle")
+    ap.add_argument("--layout", choices=["swizzle", "pad", "plain", "direct"], default="swizzle")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle leg")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -304,7 +304,8 @@ def main(argv=None):
     extra = {}
     if not args.quick and args.workload is None:
         for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "bf16_convert", "bf16_stage", "map"):
-            for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map") else ("swizzle", "pad", "plain")):
+            for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map")
+                        else ("swizzle", "pad", "plain", "direct")):
                 s2, nb2, inf2 = build(ctx, wname, lay)
                 if wname == "map":
                     rate, ms2 = median_rate(s2, nb2, steps=250, warmup=25)

@@ -42,8 +42,22 @@ enum swz_status {
 /* Layout of a tile in LDS.  PAD and PLAIN are the ablations: PAD adds one
  * element (4-byte elements) or one 16-byte vector (2-byte elements) to each
  * row ("CUDA 013 - Swizzle 的工作原理", section 如何避免 Bank Conflict, the
- * 32x33 array); PLAIN is the row-major tile with no remapping. */
-enum swz_layout { SWZ_LAYOUT_SWIZZLE = 0, SWZ_LAYOUT_PAD = 1, SWZ_LAYOUT_PLAIN = 2 };
+ * 32x33 array); PLAIN is the row-major tile with no remapping.
+ * SWIZZLE_DIRECT is the SWIZZLE layout filled without a trip through
+ * registers: the tile moves from HBM straight into LDS (the gfx950 direct
+ * load, the role cp.async plays in "NVIDIA CuTe Swizzle" and "CuTe Swizzle
+ * 学习手册", usage step 2).  Such a load writes each lane's bytes at
+ * consecutive LDS addresses, so the swizzle is applied on the HBM side
+ * instead: the lane that fills LDS slot p fetches tile element swizzle(p),
+ * which places every element exactly where SWIZZLE puts it (the swizzle is
+ * its own inverse when S >= B).  It needs S >= B (or B = 0, plain rows), and
+ * 16-byte aligned pointers and row pitches (SWZ_EUNSUPPORTED otherwise). */
+enum swz_layout {
+    SWZ_LAYOUT_SWIZZLE = 0,
+    SWZ_LAYOUT_PAD = 1,
+    SWZ_LAYOUT_PLAIN = 2,
+    SWZ_LAYOUT_SWIZZLE_DIRECT = 3
+};
 
 /* How a staged tile is read back from LDS.
  *  SCALAR_COL : 4-byte elements, 32x32 tile, each lane reads one element
@@ -74,7 +88,8 @@ typedef struct swz_plan_info {
     swz_params params;   /* swizzle actually used (B = 0 for PAD / PLAIN) */
     int32_t pad_elems;   /* extra elements per LDS row (PAD only) */
     int32_t lds_bytes;   /* LDS bytes one tile occupies */
-    int32_t vec_bytes;   /* width of the LDS stores of the staging pass */
+    int32_t vec_bytes;   /* width of the LDS stores of the staging pass (the
+                            direct fill: bytes each lane's load writes) */
     int32_t aligned;     /* 1 if the 16-byte vector path is used */
     int32_t threads;     /* threads per workgroup (one tile at a time) */
 } swz_plan_info;
@@ -99,12 +114,15 @@ int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p, void* 
  *   elem_bytes : 2 or 4.
  *   layout     : enum swz_layout.
  *   read_kind  : enum swz_read_kind (AUTO picks by element size and width).
- *   p_or_null  : swizzle to use with SWZ_LAYOUT_SWIZZLE, or NULL to let
- *                swz_choose pick; ignored for PAD and PLAIN.
+ *   p_or_null  : swizzle to use with SWZ_LAYOUT_SWIZZLE(_DIRECT), or NULL to
+ *                let swz_choose pick; ignored for PAD and PLAIN.
  * Any rows, cols >= 0 are accepted (partial edge tiles are handled); 0 is a
  * no-op.  src and dst must not overlap; they must be aligned to elem_bytes.
  * Errors: SWZ_EINVAL (sizes, NULL, overlap, misalignment, a read kind that
- * does not fit elem_bytes, parameters that split a vector or leave the tile). */
+ * does not fit elem_bytes, parameters that split a vector or leave the tile,
+ * S < B with SWZ_LAYOUT_SWIZZLE_DIRECT); SWZ_EUNSUPPORTED for
+ * SWZ_LAYOUT_SWIZZLE_DIRECT when a pointer or a row pitch (cols * elem_bytes
+ * or rows * elem_bytes) is not a multiple of 16 bytes. */
 int swz_transpose(const void* d_src, void* d_dst, int64_t rows, int64_t cols, int32_t elem_bytes,
                   int32_t layout, int32_t read_kind, const swz_params* p_or_null, void* stream);
 
@@ -148,7 +166,8 @@ int swz_choose(int32_t elem_bytes, int32_t vec_bytes, int32_t tile_rows, int32_t
 
 /* Host only.  Predicted conflict cycles (write + read, summed over one
  * tile) of the kernel pattern for read_kind under the built-in bank model,
- * for the given layout and parameters (params ignored unless SWIZZLE). */
+ * for the given layout and parameters (params ignored for PAD and PLAIN;
+ * with SWIZZLE_DIRECT the writes are the direct fill's lane-linear ones). */
 int swz_predict_conflicts(int32_t read_kind, int32_t layout, const swz_params* p_or_null,
                           int64_t* write_cycles, int64_t* read_cycles);
 
@@ -179,8 +198,9 @@ int swz_bank_model_get(swz_bank_model* out);
 
 /* Host only.  Fill *out with what swz_convert_layout (op = 0) or
  * swz_stage_operand (op = 1) would do for these arguments, without
- * launching anything; pointers are not inspected (aligned is reported for
- * 16-byte aligned pointers).  Same validation and errors as the call. */
+ * launching anything; pointers are not inspected (they are taken to be
+ * 16-byte aligned, so aligned reflects the row pitches).  Same validation and
+ * errors as the call. */
 int swz_plan(int32_t op, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t layout,
              int32_t read_kind, const swz_params* p_or_null, swz_plan_info* out);
 

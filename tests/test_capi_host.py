@@ -252,3 +252,68 @@ def test_model_matches_measured_geometry():
     first = [0, 1, 2, 3, 12, 13, 14, 15, 20, 21, 22, 23, 24, 25, 26, 27]
     assert sorted(l for l in range(64) if ph[l] == ph[0]) == first
     assert len(set(ph)) == 4
+
+
+# ------------------------------------------------- direct HBM -> LDS fill
+
+
+def test_direct_validation():
+    f = lib.swz_convert_layout
+    D = T.LAYOUT_SWIZZLE_DIRECT
+    # row pitch of 100 bf16 elements (200 bytes) is not a multiple of 16
+    assert f(A, B, 2, 64, 100, 2, D, T.READ_B128_8X8, None, None) == EUNSUP
+    assert f(A, B, 1, 60, 64, 2, D, T.READ_B64_4X4, None, None) == EUNSUP  # output pitch
+    assert f(A + 4, B, 1, 64, 64, 4, D, T.READ_SCALAR_COL, None, None) == EUNSUP  # pointer
+    # the same arguments are fine for the register fill (no launch: empty batch)
+    assert f(A, B, 0, 64, 100, 2, 0, T.READ_B128_8X8, None, None) == T.SWZ_OK
+    # S < B: the swizzle is not its own inverse, the direct fill cannot place it
+    assert f(A, B, 1, 64, 64, 2, D, T.READ_B64_4X4, ctypes.byref(P(3, 3, 2)), None) == EINVAL
+    assert lib.swz_stage_operand(A, B, 16, 32, 2, 0, D, ctypes.byref(P(4, 3, 2)), None) == EINVAL
+    with pytest.raises(T.SwzError):
+        T.swz_plan(0, 64, 100, 2, "direct", T.READ_B128_8X8)
+    p = T.swz_plan(0, 8192, 8192, 2, "direct", T.READ_B64_4X4)
+    assert p["layout"] == T.LAYOUT_SWIZZLE_DIRECT and p["vec_bytes"] == 16 and p["pad_elems"] == 0
+    assert p["params"] == T.swz_plan(0, 8192, 8192, 2, "swizzle", T.READ_B64_4X4)["params"]
+    assert T.swz_plan(0, 4096, 4096, 4, "direct")["vec_bytes"] == 4
+
+
+@pytest.mark.parametrize("kind", list(KIND_GEOM))
+def test_direct_fill_writes_lane_linear_and_reads_like_swizzle(kind):
+    esz, tr, tc, _ = KIND_GEOM[kind]
+    nt = threads_of(kind)
+    vb = 4 if esz == 4 else 16
+    loads = tr * tc * esz // vb // nt
+    acc = T.swz_kernel_accesses(kind, "direct", None, 1)
+    assert len(acc) == loads * nt // 64
+    n = 0
+    for w in range(nt // 64):
+        for j in range(loads):
+            addrs, width = acc[n]
+            assert width == vb
+            assert addrs == [vb * (64 * w + l + nt * j) for l in range(64)]
+            n += 1
+    assert T.swz_kernel_accesses(kind, "direct", None, 0) == T.swz_kernel_accesses(kind, "swizzle", None, 0)
+    assert T.swz_predict_conflicts(kind, "direct") == (0, 0)
+
+
+@pytest.mark.parametrize("kind", list(KIND_GEOM))
+def test_direct_fill_places_every_element_where_swizzle_does(kind):
+    """Reading of the direct fill: the lane filling LDS slot p fetches tile
+    element swizzle(p).  With the oracle's swizzle and tile offset, that
+    element's swizzled-layout address is p again, for every slot of the tile
+    and for every S >= B the chooser could emit -- so the fill reproduces
+    the swizzled tile exactly, and covers each element once."""
+    esz, tr, tc, _ = KIND_GEOM[kind]
+    epl = 1 if esz == 4 else 8
+    m_min = 0 if esz == 4 else 3
+    log_tile = (tr * tc).bit_length() - 1
+    for B, M, S in [(b, m, s) for b in range(1, 6) for m in (m_min, m_min + 1) for s in range(b, 8)
+                    if m + b <= log_tile]:
+        fetched = []
+        for p in range(0, tr * tc, epl):
+            e = O.swizzle(p, B, M, S)
+            assert e % epl == 0  # a 16-byte slot stays one run of 8 elements
+            r, c = divmod(e, tc)
+            assert O.tile_offset(r, c, tc, "swizzle", (B, M, S)) == p
+            fetched.append(e)
+        assert sorted(fetched) == list(range(0, tr * tc, epl))

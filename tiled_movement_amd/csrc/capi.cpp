@@ -34,11 +34,34 @@ int ilog2(int64_t v) {
     return r;
 }
 
+// Parameters and LDS row pitch of a layout for a kind: the caller's swizzle
+// or the chooser's for SWIZZLE and SWIZZLE_DIRECT (the direct fill also needs
+// S >= B, so that the swizzle is its own inverse), the pad for PAD.
+int resolve_layout(int kind, int32_t layout, const swz_params* p, swz_params* q, int* pad) {
+    *q = swz_params{0, 0, 0};
+    *pad = 0;
+    switch (layout) {
+        case SWZ_LAYOUT_SWIZZLE:
+        case SWZ_LAYOUT_SWIZZLE_DIRECT:
+            if (p) {
+                if (!swz::params_ok_for_kind(kind, *p)) return SWZ_EINVAL;
+                if (layout == SWZ_LAYOUT_SWIZZLE_DIRECT && p->B > 0 && p->S < p->B) return SWZ_EINVAL;
+                *q = *p;
+            } else {
+                *q = swz::cached_choice(kind);
+            }
+            return SWZ_OK;
+        case SWZ_LAYOUT_PAD: *pad = swz::pad_elems(kind); return SWZ_OK;
+        case SWZ_LAYOUT_PLAIN: return SWZ_OK;
+        default: return SWZ_EINVAL;
+    }
+}
+
 // Resolve read kind, layout and parameters into a plan; shared by the calls
 // and by swz_plan.
 int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, int32_t read_kind,
               const swz_params* p, bool aligned, swz_plan_info* out) {
-    if (layout < SWZ_LAYOUT_SWIZZLE || layout > SWZ_LAYOUT_PLAIN) return SWZ_EINVAL;
+    if (layout < SWZ_LAYOUT_SWIZZLE || layout > SWZ_LAYOUT_SWIZZLE_DIRECT) return SWZ_EINVAL;
     int kind = read_kind;
     if (op == 0) {
         if (esz != 2 && esz != 4) return SWZ_EINVAL;
@@ -53,18 +76,11 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     if (!swz::kind_info(kind, &k)) return SWZ_EINVAL;
     if (k.esz != esz) return SWZ_EINVAL;
 
-    swz_params q{0, 0, 0};
-    int pad = 0;
-    if (layout == SWZ_LAYOUT_SWIZZLE) {
-        if (p) {
-            if (!swz::params_ok_for_kind(kind, *p)) return SWZ_EINVAL;
-            q = *p;
-        } else {
-            q = swz::cached_choice(kind);
-        }
-    } else if (layout == SWZ_LAYOUT_PAD) {
-        pad = swz::pad_elems(kind);
-    }
+    swz_params q;
+    int pad;
+    const int st = resolve_layout(kind, layout, p, &q, &pad);
+    if (st != SWZ_OK) return st;
+    if (layout == SWZ_LAYOUT_SWIZZLE_DIRECT && !aligned) return SWZ_EUNSUPPORTED;
     std::memset(out, 0, sizeof(*out));
     out->read_kind = kind;
     out->tile_rows = k.tr;
@@ -73,7 +89,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     out->params = q;
     out->pad_elems = pad;
     out->lds_bytes = k.tr * (k.tc + pad) * k.esz;
-    out->vec_bytes = k.vec;
+    out->vec_bytes = layout == SWZ_LAYOUT_SWIZZLE_DIRECT ? (k.esz == 4 ? 4 : 16) : k.vec;
     out->aligned = aligned ? 1 : 0;
     out->threads = k.nt;
     (void)rows;
@@ -115,7 +131,9 @@ SWZ_API int swz_plan(int32_t op, int64_t rows, int64_t cols, int32_t elem_bytes,
                      const swz_params* p_or_null, swz_plan_info* out) {
     if (!out || (op != 0 && op != 1) || rows < 0 || cols < 0) return SWZ_EINVAL;
     if (op == 1 && (rows % 16 || cols % 32)) return SWZ_EINVAL;
-    return make_plan(op, rows, cols, elem_bytes, layout, read_kind, p_or_null, true, out);
+    // Pointers are taken as 16-byte aligned; the row pitches decide the rest.
+    const bool aligned = op == 1 || ((cols * elem_bytes) % 16 == 0 && (rows * elem_bytes) % 16 == 0);
+    return make_plan(op, rows, cols, elem_bytes, layout, read_kind, p_or_null, aligned, out);
 }
 
 SWZ_API int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, int64_t rows, int64_t cols,
@@ -134,7 +152,7 @@ SWZ_API int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, in
     if (!d_src || !d_dst) return SWZ_EINVAL;
     if (ps % elem_bytes || pd % elem_bytes) return SWZ_EINVAL;
     if (overlaps(d_src, bytes, d_dst, bytes)) return SWZ_EINVAL;
-    swz::ConvertJob job{d_src, d_dst, batch, rows, cols, layout_of(pl), aligned};
+    swz::ConvertJob job{d_src, d_dst, batch, rows, cols, layout_of(pl), aligned, layout == SWZ_LAYOUT_SWIZZLE_DIRECT};
     return hip_status(swz::launch_convert(pl.read_kind, job, static_cast<hipStream_t>(stream)));
 }
 
@@ -156,7 +174,7 @@ SWZ_API int swz_stage_operand(const void* d_src, void* d_frag, int64_t mn, int64
     if (!d_src || !d_frag) return SWZ_EINVAL;
     if (reinterpret_cast<uintptr_t>(d_src) % 16 || reinterpret_cast<uintptr_t>(d_frag) % 16) return SWZ_EINVAL;
     if (overlaps(d_src, bytes, d_frag, bytes)) return SWZ_EINVAL;
-    swz::StageJob job{d_src, d_frag, mn, k, layout_of(pl)};
+    swz::StageJob job{d_src, d_frag, mn, k, layout_of(pl), layout == SWZ_LAYOUT_SWIZZLE_DIRECT};
     return hip_status(swz::launch_stage(job, static_cast<hipStream_t>(stream)));
 }
 
@@ -175,21 +193,12 @@ SWZ_API int swz_predict_conflicts(int32_t read_kind, int32_t layout, const swz_p
     if (!wcyc || !rcyc) return SWZ_EINVAL;
     KindInfo k;
     if (!swz::kind_info(read_kind, &k)) return SWZ_EINVAL;
-    swz_params q{0, 0, 0};
-    uint32_t ld = static_cast<uint32_t>(k.tc);
-    if (layout == SWZ_LAYOUT_SWIZZLE) {
-        if (p_or_null) {
-            if (!swz::params_ok_for_kind(read_kind, *p_or_null)) return SWZ_EINVAL;
-            q = *p_or_null;
-        } else {
-            q = swz::cached_choice(read_kind);
-        }
-    } else if (layout == SWZ_LAYOUT_PAD) {
-        ld += static_cast<uint32_t>(swz::pad_elems(read_kind));
-    } else if (layout != SWZ_LAYOUT_PLAIN) {
-        return SWZ_EINVAL;
-    }
-    swz::predict_tile(read_kind, swz::gfx950_bank_model(), ld, q, wcyc, rcyc);
+    swz_params q;
+    int pad;
+    const int st = resolve_layout(read_kind, layout, p_or_null, &q, &pad);
+    if (st != SWZ_OK) return st;
+    swz::predict_tile(read_kind, swz::gfx950_bank_model(), static_cast<uint32_t>(k.tc + pad), q, wcyc, rcyc,
+                      layout == SWZ_LAYOUT_SWIZZLE_DIRECT);
     return SWZ_OK;
 }
 
@@ -199,22 +208,13 @@ SWZ_API int swz_kernel_accesses(int32_t read_kind, int32_t layout, const swz_par
     if (is_write != 0 && is_write != 1) return SWZ_EINVAL;
     KindInfo k;
     if (!swz::kind_info(read_kind, &k)) return SWZ_EINVAL;
-    swz_params q{0, 0, 0};
-    uint32_t ld = static_cast<uint32_t>(k.tc);
-    if (layout == SWZ_LAYOUT_SWIZZLE) {
-        if (p_or_null) {
-            if (!swz::params_ok_for_kind(read_kind, *p_or_null)) return SWZ_EINVAL;
-            q = *p_or_null;
-        } else {
-            q = swz::cached_choice(read_kind);
-        }
-    } else if (layout == SWZ_LAYOUT_PAD) {
-        ld += static_cast<uint32_t>(swz::pad_elems(read_kind));
-    } else if (layout != SWZ_LAYOUT_PLAIN) {
-        return SWZ_EINVAL;
-    }
+    swz_params q;
+    int pad;
+    const int st = resolve_layout(read_kind, layout, p_or_null, &q, &pad);
+    if (st != SWZ_OK) return st;
     int w = 0;
-    *n_accesses = swz::kernel_accesses(read_kind, ld, q, is_write != 0, addrs, max_accesses, &w);
+    *n_accesses = swz::kernel_accesses(read_kind, static_cast<uint32_t>(k.tc + pad), q,
+                                       layout == SWZ_LAYOUT_SWIZZLE_DIRECT, is_write != 0, addrs, max_accesses, &w);
     *width = w;
     return SWZ_OK;
 }

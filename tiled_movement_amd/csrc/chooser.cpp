@@ -26,14 +26,27 @@ int ilog2(int64_t v) {
     return r;
 }
 
+// LDS addresses of the direct fill's load j of one wave (lane-linear).
 template <int KIND>
-void predict_kind(const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, int64_t* rcyc) {
+void direct_write(int wave, int j, int32_t* addr) {
+    using D = Direct<KIND>;
+    for (int l = 0; l < 64; ++l) addr[l] = D::VB * (64 * wave + l + Kind<KIND>::NT * j);
+}
+
+template <int KIND>
+void predict_kind(const BankModel& m, uint32_t ld, swz_params p, bool direct, int64_t* wcyc, int64_t* rcyc) {
     using K = Kind<KIND>;
     const LdsLayout L{ld, static_cast<uint32_t>(p.B), static_cast<uint32_t>(p.M), static_cast<uint32_t>(p.S)};
     int64_t w = 0, r = 0;
     Access a;
     for (int wave = 0; wave < K::NT / 64; ++wave) {
-        for (int i = 0; i < K::WSTEPS; ++i) {
+        for (int j = 0; direct && j < Direct<KIND>::LOADS; ++j) {
+            a.width = Direct<KIND>::VB;
+            a.write = true;
+            direct_write<KIND>(wave, j, a.addr);
+            w += conflict_cycles(m, a);
+        }
+        for (int i = 0; !direct && i < K::WSTEPS; ++i) {
             a.width = K::VEC;
             a.write = true;
             for (int l = 0; l < 64; ++l) {
@@ -59,15 +72,20 @@ void predict_kind(const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, 
 }
 
 template <int KIND>
-int accesses_kind(uint32_t ld, swz_params p, bool write, int32_t* addrs, int max_acc, int* width) {
+int accesses_kind(uint32_t ld, swz_params p, bool direct, bool write, int32_t* addrs, int max_acc, int* width) {
     using K = Kind<KIND>;
     const LdsLayout L{ld, static_cast<uint32_t>(p.B), static_cast<uint32_t>(p.M), static_cast<uint32_t>(p.S)};
-    const int steps = write ? K::WSTEPS : K::RSTEPS;
-    *width = write ? K::VEC : K::RWIDTH;
+    const bool dw = direct && write;
+    const int steps = dw ? Direct<KIND>::LOADS : write ? K::WSTEPS : K::RSTEPS;
+    *width = dw ? Direct<KIND>::VB : write ? K::VEC : K::RWIDTH;
     int n = 0;
     for (int wave = 0; wave < K::NT / 64; ++wave) {
         for (int i = 0; i < steps; ++i, ++n) {
             if (n >= max_acc || !addrs) continue;
+            if (dw) {
+                direct_write<KIND>(wave, i, addrs + 64 * n);
+                continue;
+            }
             for (int l = 0; l < 64; ++l) {
                 int rr, cc;
                 if (write)
@@ -83,12 +101,14 @@ int accesses_kind(uint32_t ld, swz_params p, bool write, int32_t* addrs, int max
 
 }  // namespace
 
-int kernel_accesses(int kind, uint32_t ld, swz_params p, bool write, int32_t* addrs, int max_acc, int* width) {
+int kernel_accesses(int kind, uint32_t ld, swz_params p, bool direct, bool write, int32_t* addrs, int max_acc,
+                    int* width) {
     switch (kind) {
-        case SWZ_READ_SCALAR_COL: return accesses_kind<SWZ_READ_SCALAR_COL>(ld, p, write, addrs, max_acc, width);
-        case SWZ_READ_B64_4X4: return accesses_kind<SWZ_READ_B64_4X4>(ld, p, write, addrs, max_acc, width);
-        case SWZ_READ_B128_8X8: return accesses_kind<SWZ_READ_B128_8X8>(ld, p, write, addrs, max_acc, width);
-        case SWZ_READ_MFMA_16X16X32: return accesses_kind<SWZ_READ_MFMA_16X16X32>(ld, p, write, addrs, max_acc, width);
+        case SWZ_READ_SCALAR_COL: return accesses_kind<SWZ_READ_SCALAR_COL>(ld, p, direct, write, addrs, max_acc, width);
+        case SWZ_READ_B64_4X4: return accesses_kind<SWZ_READ_B64_4X4>(ld, p, direct, write, addrs, max_acc, width);
+        case SWZ_READ_B128_8X8: return accesses_kind<SWZ_READ_B128_8X8>(ld, p, direct, write, addrs, max_acc, width);
+        case SWZ_READ_MFMA_16X16X32:
+            return accesses_kind<SWZ_READ_MFMA_16X16X32>(ld, p, direct, write, addrs, max_acc, width);
         default: return -1;
     }
 }
@@ -119,12 +139,13 @@ int pad_elems(int kind) {
     return k.vec == k.esz ? 1 : k.vec / k.esz;
 }
 
-void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, int64_t* rcyc) {
+void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, int64_t* rcyc,
+                  bool direct) {
     switch (kind) {
-        case SWZ_READ_SCALAR_COL: predict_kind<SWZ_READ_SCALAR_COL>(m, ld, p, wcyc, rcyc); break;
-        case SWZ_READ_B64_4X4: predict_kind<SWZ_READ_B64_4X4>(m, ld, p, wcyc, rcyc); break;
-        case SWZ_READ_B128_8X8: predict_kind<SWZ_READ_B128_8X8>(m, ld, p, wcyc, rcyc); break;
-        case SWZ_READ_MFMA_16X16X32: predict_kind<SWZ_READ_MFMA_16X16X32>(m, ld, p, wcyc, rcyc); break;
+        case SWZ_READ_SCALAR_COL: predict_kind<SWZ_READ_SCALAR_COL>(m, ld, p, direct, wcyc, rcyc); break;
+        case SWZ_READ_B64_4X4: predict_kind<SWZ_READ_B64_4X4>(m, ld, p, direct, wcyc, rcyc); break;
+        case SWZ_READ_B128_8X8: predict_kind<SWZ_READ_B128_8X8>(m, ld, p, direct, wcyc, rcyc); break;
+        case SWZ_READ_MFMA_16X16X32: predict_kind<SWZ_READ_MFMA_16X16X32>(m, ld, p, direct, wcyc, rcyc); break;
         default: *wcyc = *rcyc = -1;
     }
 }

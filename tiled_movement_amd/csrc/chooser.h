@@ -16,8 +16,10 @@ struct KindInfo {
 bool kind_info(int kind, KindInfo* out);
 
 // Predicted conflict cycles over one tile for the kind's staging writes and
-// reads, with LDS row pitch ld and swizzle p (B = 0 for none).
-void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, int64_t* rcyc);
+// reads, with LDS row pitch ld and swizzle p (B = 0 for none).  direct: the
+// writes are those of the direct fill (lane-linear), not the register fill's.
+void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, int64_t* rcyc,
+                  bool direct = false);
 
 // Chooser: see swz_choose in swz.h.  Result cached per kind for the gfx950
 // model; the model argument form is uncached.
@@ -25,7 +27,8 @@ swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles);
 swz_params cached_choice(int kind);
 
 // The kernel's LDS accesses for one tile (see swz_kernel_accesses).
-int kernel_accesses(int kind, uint32_t ld, swz_params p, bool write, int32_t* addrs, int max_acc, int* width);
+int kernel_accesses(int kind, uint32_t ld, swz_params p, bool direct, bool write, int32_t* addrs, int max_acc,
+                    int* width);
 
 // Pad (elements per LDS row) of the padded layout for a kind.
 int pad_elems(int kind);

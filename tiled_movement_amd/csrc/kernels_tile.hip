@@ -42,6 +42,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // workgroup (no loop in the kernel, so nothing is kept live across tiles).
 constexpr int64_t kMaxGrid = int64_t(1) << 22;
 
+// Cache-policy operand of the direct load for a non-temporal access.
+constexpr int kDirectNT = 2;
+
 __device__ __forceinline__ u32x4 gload16(const uint8_t* p) {
     const u32x4* q = reinterpret_cast<const u32x4*>(p);
     if (SWZ_NONTEMPORAL) return __builtin_nontemporal_load(q);
@@ -116,12 +119,17 @@ __device__ __forceinline__ void store16_guarded(uint8_t* D, int64_t row, int64_t
     }
 }
 
-template <int KIND>
+// How a kernel fills the LDS tile: through registers into swizzled (or
+// plain) rows, through registers into padded rows, or by direct loads into
+// swizzled (or plain) rows.
+enum Fill { kRegs = 0, kPadded = 1, kDirect = 2 };
+
+template <int KIND, int FILL>
 struct LdsTile {
     using K = Kind<KIND>;
-    // Room for the padded layout: one extra element (4-byte) or vector.
+    // The padded layout adds one element (4-byte) or one vector per row.
     static constexpr int PAD = K::ESZ == 4 ? 1 : 8;
-    static constexpr int BYTES = K::TR * (K::TC + PAD) * K::ESZ;
+    static constexpr int BYTES = K::TR * (K::TC + (FILL == kPadded ? PAD : 0)) * K::ESZ;
 };
 
 // Element offset in LDS of step i of this lane: the lane's first offset
@@ -152,6 +160,34 @@ __device__ __forceinline__ uint32_t lane_base(int t, const LdsLayout& L) {
     coord<KIND, WRITE>(t, 0, r, c);
     if (PADDED) return static_cast<uint32_t>(r) * L.ld + static_cast<uint32_t>(c);
     return swizzle(static_cast<uint32_t>(r * K::TC + c), L.B, L.M, L.S);
+}
+
+// Direct fill of one tile (see Direct in swz_common.h): each load writes
+// VB bytes per lane to consecutive LDS slots starting at a wave-uniform
+// address, and the lane fetches the tile element the swizzled layout keeps in
+// its slot.  rows x cols is the source matrix (r0, c0 the tile's corner);
+// with FULL false, slots whose element lies outside the matrix are filled
+// from the tile's corner element instead, which is always inside and never
+// stored.  Rows must be 16-byte aligned for 2-byte elements, so a 16-byte
+// slot is wholly inside or wholly outside.  Waits for its own loads; the
+// caller's barrier then publishes the tile.
+template <int KIND, bool FULL>
+__device__ __forceinline__ void direct_fill(const uint8_t* __restrict__ S, int64_t rows, int64_t cols, int64_t r0,
+                                            int64_t c0, uint8_t* lds, const LdsLayout& L, int t) {
+    using K = Kind<KIND>;
+    using D = Direct<KIND>;
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    const uint32_t base = swizzle(static_cast<uint32_t>(D::EPL * t), L.B, L.M, L.S);
+    const int wave = __builtin_amdgcn_readfirstlane(t / 64);
+#pragma unroll
+    for (int j = 0; j < D::LOADS; ++j) {
+        const uint32_t e = base ^ swizzle(static_cast<uint32_t>(D::EPL * K::NT * j), L.B, L.M, L.S);
+        const int64_t r = r0 + static_cast<int64_t>(e / K::TC), c = c0 + static_cast<int64_t>(e % K::TC);
+        const uint8_t* g = (FULL || (r < rows && c < cols)) ? S + (r * cols + c) * K::ESZ : S + (r0 * cols + c0) * K::ESZ;
+        lds_u8* slot = (lds_u8*)lds + D::VB * (64 * wave + K::NT * j);
+        __builtin_amdgcn_global_load_lds(g, slot, D::VB, 0, SWZ_NONTEMPORAL ? kDirectNT : 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -244,14 +280,19 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
     }
 }
 
-template <int KIND, bool PADDED, bool FULL>
+template <int KIND, int FILL, bool FULL>
 __device__ __forceinline__ void convert_tile(const uint8_t* __restrict__ S, uint8_t* __restrict__ D, int64_t rows,
                                              int64_t cols, int64_t r0, int64_t c0, uint8_t* lds, uint32_t wbase,
                                              uint32_t rbase, const LdsLayout& L, int t) {
     using K = Kind<KIND>;
-    u32x4 v[K::GLOADS];
-    load_tile<KIND, FULL>(S, rows, cols, r0, c0, t, v);
-    lds_store<KIND, PADDED>(lds, wbase, L, v);
+    constexpr bool PADDED = FILL == kPadded;
+    if constexpr (FILL == kDirect) {
+        direct_fill<KIND, FULL>(S, rows, cols, r0, c0, lds, L, t);
+    } else {
+        u32x4 v[K::GLOADS];
+        load_tile<KIND, FULL>(S, rows, cols, r0, c0, t, v);
+        lds_store<KIND, PADDED>(lds, wbase, L, v);
+    }
     __syncthreads();
     lds_read_store<KIND, PADDED, FULL>(lds, rbase, L, D, rows, cols, r0, c0, t);
 }
@@ -278,16 +319,18 @@ __device__ __forceinline__ void my_tile(int64_t tiles_r, int64_t tiles_c, int64_
     }
 }
 
-template <int KIND, bool PADDED, bool ALIGNED, bool GRID3D>
+template <int KIND, int FILL, bool ALIGNED, bool GRID3D>
 __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                             int64_t rows, int64_t cols, int64_t tiles_r,
                                                             int64_t tiles_c, int64_t tile0, LdsLayout L) {
     using K = Kind<KIND>;
-    __shared__ u32x4 lds_v[LdsTile<KIND>::BYTES / 16];
+    constexpr bool PADDED = FILL == kPadded;
+    static_assert(FILL != kDirect || ALIGNED, "the direct fill needs 16-byte aligned rows");
+    __shared__ u32x4 lds_v[(LdsTile<KIND, FILL>::BYTES + 15) / 16];
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
     const int t = threadIdx.x;
     const int64_t plane = rows * cols * K::ESZ;  // bytes of one batch entry
-    const uint32_t wbase = lane_base<KIND, true, PADDED>(t, L);
+    const uint32_t wbase = FILL == kDirect ? 0u : lane_base<KIND, true, PADDED>(t, L);
     const uint32_t rbase = lane_base<KIND, false, PADDED>(t, L);
 
     int64_t b, tr, tc;
@@ -296,32 +339,39 @@ __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __res
     const uint8_t* S = src + b * plane;
     uint8_t* D = dst + b * plane;
     if (ALIGNED && r0 + K::TR <= rows && c0 + K::TC <= cols)
-        convert_tile<KIND, PADDED, true>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
+        convert_tile<KIND, FILL, true>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
     else
-        convert_tile<KIND, PADDED, false>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
+        convert_tile<KIND, FILL, false>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
 }
 
 // ---------------------------------------------------------------------------
 // Operand staging: 256x64 K-tiles of a K-contiguous 16-bit operand, read
 // back as 16x16x32 operand fragments and written out in lane order.
 // ---------------------------------------------------------------------------
-template <bool PADDED, bool FULL>
+template <int FILL, bool FULL>
 __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint8_t* __restrict__ frag, int64_t mn,
                                            int64_t k, int64_t r0, int64_t k0, uint8_t* lds, uint32_t wbase,
                                            uint32_t rbase, const LdsLayout& L, int t) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
+    constexpr bool PADDED = FILL == kPadded;
     using K = Kind<KD>;
-    u32x4 v[K::GLOADS];
+    if constexpr (FILL == kDirect) {
+        direct_fill<KD, FULL>(src, mn, k, r0, k0, lds, L, t);
+    } else {
+        u32x4 v[K::GLOADS];
 #pragma unroll
-    for (int j = 0; j < K::GLOADS; ++j) {
-        int r = 0, c = 0;
-        K::wcoord(t, j, r, c);
-        // mn and k are multiples of 16 and 32, so a 16-byte chunk is either
-        // wholly inside the operand or wholly outside.
-        v[j] = (FULL || (r0 + r < mn && k0 + c < k)) ? gload16(src + ((r0 + r) * k + k0 + c) * 2) : u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < K::GLOADS; ++j) {
+            int r = 0, c = 0;
+            K::wcoord(t, j, r, c);
+            // mn and k are multiples of 16 and 32, so a 16-byte chunk is either
+            // wholly inside the operand or wholly outside.
+            v[j] = (FULL || (r0 + r < mn && k0 + c < k)) ? gload16(src + ((r0 + r) * k + k0 + c) * 2)
+                                                         : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < K::GLOADS; ++j)
+            *reinterpret_cast<u32x4*>(lds + 2 * step_off<KD, true, PADDED>(wbase, j, L)) = v[j];
     }
-#pragma unroll
-    for (int j = 0; j < K::GLOADS; ++j) *reinterpret_cast<u32x4*>(lds + 2 * step_off<KD, true, PADDED>(wbase, j, L)) = v[j];
     __syncthreads();
     const int64_t ksteps = k / 32;
     const int lane = t % 64;
@@ -337,27 +387,28 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint
     }
 }
 
-template <bool PADDED, bool GRID3D>
+template <int FILL, bool GRID3D>
 __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(const uint8_t* __restrict__ src,
                                                                             uint8_t* __restrict__ frag, int64_t mn,
                                                                             int64_t k, int64_t tiles_m,
                                                                             int64_t tiles_k, int64_t tile0,
                                                                             LdsLayout L) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
+    constexpr bool PADDED = FILL == kPadded;
     using K = Kind<KD>;
-    __shared__ u32x4 lds_v[LdsTile<KD>::BYTES / 16];
+    __shared__ u32x4 lds_v[LdsTile<KD, FILL>::BYTES / 16];
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
     const int t = threadIdx.x;
-    const uint32_t wbase = lane_base<KD, true, PADDED>(t, L);
+    const uint32_t wbase = FILL == kDirect ? 0u : lane_base<KD, true, PADDED>(t, L);
     const uint32_t rbase = lane_base<KD, false, PADDED>(t, L);
 
     int64_t b, tm, tk;
     my_tile<SWZ_STAGE_ORDER != 0, GRID3D>(tiles_m, tiles_k, tile0, b, tm, tk);
     const int64_t r0 = tm * K::TR, k0 = tk * K::TC;
     if (r0 + K::TR <= mn && k0 + K::TC <= k)
-        stage_tile<PADDED, true>(src, frag, mn, k, r0, k0, lds, wbase, rbase, L, t);
+        stage_tile<FILL, true>(src, frag, mn, k, r0, k0, lds, wbase, rbase, L, t);
     else
-        stage_tile<PADDED, false>(src, frag, mn, k, r0, k0, lds, wbase, rbase, L, t);
+        stage_tile<FILL, false>(src, frag, mn, k, r0, k0, lds, wbase, rbase, L, t);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -368,7 +419,7 @@ bool fits_3d(int64_t x, int64_t y, int64_t z, int threads) {
     return SWZ_GRID3D && x * threads < (int64_t(1) << 31) && y <= 65535 && z <= 65535;
 }
 
-template <int KIND, bool PADDED, bool ALIGNED>
+template <int KIND, int FILL, bool ALIGNED>
 void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64_t n_tiles, hipStream_t stream) {
     using K = Kind<KIND>;
     const auto* s = static_cast<const uint8_t*>(j.src);
@@ -376,14 +427,14 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
     const bool diag = SWZ_TILE_ORDER != 0;
     const int64_t gx = diag ? tiles_r : tiles_c, gy = diag ? tiles_c : tiles_r;
     if (fits_3d(gx, gy, j.batch, K::NT)) {
-        hipLaunchKernelGGL((k_convert<KIND, PADDED, ALIGNED, true>),
+        hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, true>),
                            dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(j.batch)),
                            dim3(K::NT), 0, stream, s, d, j.rows, j.cols, tiles_r, tiles_c, int64_t(0), j.layout);
         return;
     }
     for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
         const int64_t n = n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid;
-        hipLaunchKernelGGL((k_convert<KIND, PADDED, ALIGNED, false>), dim3(static_cast<unsigned>(n)), dim3(K::NT), 0,
+        hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, false>), dim3(static_cast<unsigned>(n)), dim3(K::NT), 0,
                            stream, s, d, j.rows, j.cols, tiles_r, tiles_c, t0, j.layout);
     }
 }
@@ -395,19 +446,43 @@ hipError_t launch_kind(const ConvertJob& j, hipStream_t stream) {
     const int64_t n_tiles = j.batch * tiles_r * tiles_c;
     if (n_tiles == 0) return hipSuccess;
     const bool padded = j.layout.ld != static_cast<uint32_t>(K::TC);
-    if (padded && j.layout.ld != static_cast<uint32_t>(K::TC + LdsTile<KIND>::PAD)) return hipErrorInvalidValue;
-    if (padded) {
+    if (padded && j.layout.ld != static_cast<uint32_t>(K::TC + LdsTile<KIND, kPadded>::PAD)) return hipErrorInvalidValue;
+    if (j.direct) {
+        if (padded || !j.aligned) return hipErrorInvalidValue;
+        launch_variant<KIND, kDirect, true>(j, tiles_r, tiles_c, n_tiles, stream);
+    } else if (padded) {
         if (j.aligned)
-            launch_variant<KIND, true, true>(j, tiles_r, tiles_c, n_tiles, stream);
+            launch_variant<KIND, kPadded, true>(j, tiles_r, tiles_c, n_tiles, stream);
         else
-            launch_variant<KIND, true, false>(j, tiles_r, tiles_c, n_tiles, stream);
+            launch_variant<KIND, kPadded, false>(j, tiles_r, tiles_c, n_tiles, stream);
     } else {
         if (j.aligned)
-            launch_variant<KIND, false, true>(j, tiles_r, tiles_c, n_tiles, stream);
+            launch_variant<KIND, kRegs, true>(j, tiles_r, tiles_c, n_tiles, stream);
         else
-            launch_variant<KIND, false, false>(j, tiles_r, tiles_c, n_tiles, stream);
+            launch_variant<KIND, kRegs, false>(j, tiles_r, tiles_c, n_tiles, stream);
     }
     return hipGetLastError();
+}
+
+template <int FILL>
+void launch_stage_fill(const StageJob& j, int64_t tiles_m, int64_t tiles_k, hipStream_t stream) {
+    constexpr int KD = SWZ_READ_MFMA_16X16X32;
+    using K = Kind<KD>;
+    const auto* s = static_cast<const uint8_t*>(j.src);
+    auto* f = static_cast<uint8_t*>(j.frag);
+    const bool diag = SWZ_STAGE_ORDER != 0;
+    const int64_t gx = diag ? tiles_m : tiles_k, gy = diag ? tiles_k : tiles_m;
+    if (fits_3d(gx, gy, 1, K::NT)) {
+        hipLaunchKernelGGL((k_stage<FILL, true>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy), 1),
+                           dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k, int64_t(0), j.layout);
+        return;
+    }
+    const int64_t n_tiles = tiles_m * tiles_k;
+    for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
+        const dim3 grid(static_cast<unsigned>(n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid));
+        hipLaunchKernelGGL((k_stage<FILL, false>), grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k,
+                           t0, j.layout);
+    }
 }
 
 }  // namespace
@@ -425,32 +500,16 @@ hipError_t launch_stage(const StageJob& j, hipStream_t stream) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
     using K = Kind<KD>;
     const int64_t tiles_m = ceil_div(j.mn, K::TR), tiles_k = ceil_div(j.k, K::TC);
-    const int64_t n_tiles = tiles_m * tiles_k;
-    if (n_tiles == 0) return hipSuccess;
+    if (tiles_m * tiles_k == 0) return hipSuccess;
     const bool padded = j.layout.ld != static_cast<uint32_t>(K::TC);
-    if (padded && j.layout.ld != static_cast<uint32_t>(K::TC + LdsTile<KD>::PAD)) return hipErrorInvalidValue;
-    const auto* s = static_cast<const uint8_t*>(j.src);
-    auto* f = static_cast<uint8_t*>(j.frag);
-    const bool diag = SWZ_STAGE_ORDER != 0;
-    const int64_t gx = diag ? tiles_m : tiles_k, gy = diag ? tiles_k : tiles_m;
-    if (fits_3d(gx, gy, 1, K::NT)) {
-        const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy), 1);
-        if (padded)
-            hipLaunchKernelGGL((k_stage<true, true>), grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k,
-                               int64_t(0), j.layout);
-        else
-            hipLaunchKernelGGL((k_stage<false, true>), grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k,
-                               int64_t(0), j.layout);
-        return hipGetLastError();
-    }
-    for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
-        const dim3 grid(static_cast<unsigned>(n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid));
-        if (padded)
-            hipLaunchKernelGGL((k_stage<true, false>), grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m,
-                               tiles_k, t0, j.layout);
-        else
-            hipLaunchKernelGGL((k_stage<false, false>), grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m,
-                               tiles_k, t0, j.layout);
+    if (padded && j.layout.ld != static_cast<uint32_t>(K::TC + LdsTile<KD, kPadded>::PAD)) return hipErrorInvalidValue;
+    if (j.direct) {
+        if (padded) return hipErrorInvalidValue;
+        launch_stage_fill<kDirect>(j, tiles_m, tiles_k, stream);
+    } else if (padded) {
+        launch_stage_fill<kPadded>(j, tiles_m, tiles_k, stream);
+    } else {
+        launch_stage_fill<kRegs>(j, tiles_m, tiles_k, stream);
     }
     return hipGetLastError();
 }

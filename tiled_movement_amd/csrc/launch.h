@@ -14,6 +14,7 @@ struct ConvertJob {
     int64_t batch, rows, cols;
     LdsLayout layout;
     bool aligned;  // 16-byte vector path allowed (pointers and pitches)
+    bool direct;   // direct HBM -> LDS fill (needs aligned and an unpadded layout)
 };
 
 struct StageJob {
@@ -21,6 +22,7 @@ struct StageJob {
     void* frag;
     int64_t mn, k;
     LdsLayout layout;
+    bool direct;  // direct HBM -> LDS fill
 };
 
 hipError_t launch_convert(int kind, const ConvertJob& job, hipStream_t stream);

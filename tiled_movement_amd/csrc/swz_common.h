@@ -222,4 +222,37 @@ static_assert(steps_decompose<SWZ_READ_B128_8X8, true>() && steps_decompose<SWZ_
 static_assert(steps_decompose<SWZ_READ_MFMA_16X16X32, true>() && steps_decompose<SWZ_READ_MFMA_16X16X32, false>(),
               "fragment lane map");
 
+// ---------------------------------------------------------------------------
+// Direct fill (SWZ_LAYOUT_SWIZZLE_DIRECT): the tile goes from HBM straight
+// into LDS.  Load j of thread t writes VB bytes at LDS byte VB * (t + NT*j),
+// so each wave's load fills one contiguous stretch of LDS, lane after lane.
+// The slot at element offset p = EPL * (t + NT*j) must hold the tile element
+// the swizzled layout keeps there, swizzle^-1(p) = swizzle(p) (S >= B makes
+// the swizzle an involution: the XOR source bits are left as they are).
+// 16-byte loads for 2-byte elements (M >= 3 keeps the 8 elements of a slot
+// consecutive in one tile row); 4-byte loads, one element each, for 4-byte
+// elements, whose swizzle moves single elements.  As with the lane maps,
+// swizzle(EPL*(t + NT*j)) = swizzle(EPL*t) ^ swizzle(EPL*NT*j): the bits of
+// the two terms are disjoint, so each lane keeps one base and every load
+// adds a wave-uniform XOR.
+// ---------------------------------------------------------------------------
+template <int KIND>
+struct Direct {
+    using K = Kind<KIND>;
+    static constexpr int VB = K::ESZ == 4 ? 4 : 16;  // bytes per lane per load
+    static constexpr int EPL = VB / K::ESZ;          // elements per lane per load
+    static constexpr int LOADS = K::TR * K::TC / EPL / K::NT;
+};
+
+template <int KIND>
+constexpr bool direct_split() {
+    using D = Direct<KIND>;
+    using K = Kind<KIND>;
+    return D::LOADS >= 1 && D::LOADS * D::EPL * K::NT == K::TR * K::TC && (K::NT & (K::NT - 1)) == 0 &&
+           (K::TC & (K::TC - 1)) == 0;
+}
+static_assert(direct_split<SWZ_READ_SCALAR_COL>() && direct_split<SWZ_READ_B64_4X4>() &&
+                  direct_split<SWZ_READ_B128_8X8>() && direct_split<SWZ_READ_MFMA_16X16X32>(),
+              "direct fill split");
+
 }  // namespace swz
