@@ -8,15 +8,16 @@ before timing; the calls rotate over enough source/destination pairs
 traffic reaches HBM.
 
 Prints ONE JSON line.  Extra fields: the other workloads and layouts
-(swizzle / pad / plain), the library's reference copy of the same bytes (the
-practical read-once / write-once ceiling), and the CPU oracle as a reported
-baseline.
+(swizzle / pad / plain / direct), the library's reference copy of the same
+bytes (the practical read-once / write-once ceiling), the runtime's own
+device copy, and the CPU oracle as a reported baseline.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
-  python bench.py --workload NAME --layout swizzle|pad|plain [--steps K]
+  python bench.py --workload NAME --layout swizzle|pad|plain|direct [--steps K]
       time one workload only (used for profiler runs); NAME is one of
-      fp32_transpose, fp16_transpose, bf16_convert, bf16_stage, map, copy
+      fp32_transpose, fp16_transpose, fp16_transpose_tr, bf16_convert,
+      bf16_stage, map, copy, copy_128, memcpy_d2d
 """
 
 from __future__ import annotations
@@ -39,6 +40,7 @@ CACHE_DEFEAT_BYTES = 512 * 2**20  # 2x the 256 MB Infinity Cache
 WORKLOADS = {
     "fp32_transpose": "fp32 4096x4096 row-major -> column-major transpose, 32x32 LDS tiles, 4-byte column reads",
     "fp16_transpose": "fp16 8192x8192 row-major -> column-major transpose, 64x64 LDS tiles, 8-byte reads of 4x4 blocks",
+    "fp16_transpose_tr": "fp16 8192x8192 row-major -> column-major transpose, 64x64 LDS tiles, gfx950 8-byte transpose reads",
     "bf16_convert": "bf16 [64,4096,128] -> [64,128,4096] layout conversion, 64x128 LDS tiles, 16-byte reads of 8x8 blocks",
     "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
@@ -148,11 +150,13 @@ def build(ctx, name, layout):
     lay = T.LAYOUTS[layout]
     info = {"workload": WORKLOADS[name], "layout": layout}
 
-    if name in ("fp32_transpose", "fp16_transpose", "bf16_convert"):
+    if name in ("fp32_transpose", "fp16_transpose", "fp16_transpose_tr", "bf16_convert"):
         if name == "fp32_transpose":
             a, esz, kind, (batch, r, c) = W.fp32_matrix(4096, 4096, seed=0), 4, T.READ_SCALAR_COL, (1, 4096, 4096)
         elif name == "fp16_transpose":
             a, esz, kind, (batch, r, c) = W.fp16_matrix(8192, 8192, seed=0), 2, T.READ_B64_4X4, (1, 8192, 8192)
+        elif name == "fp16_transpose_tr":
+            a, esz, kind, (batch, r, c) = W.fp16_matrix(8192, 8192, seed=0), 2, T.READ_B64_TR16, (1, 8192, 8192)
         else:
             a, esz, kind, (batch, r, c) = W.bf16_tensor((64, 4096, 128), seed=0), 2, T.READ_B128_8X8, (64, 4096, 128)
         k = n_pairs(2 * a.nbytes)
@@ -303,7 +307,8 @@ def main(argv=None):
 
     extra = {}
     if not args.quick and args.workload is None:
-        for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "bf16_convert", "bf16_stage", "map"):
+        for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "fp16_transpose_tr",
+                      "bf16_convert", "bf16_stage", "map"):
             for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map")
                         else ("swizzle", "pad", "plain", "direct")):
                 s2, nb2, inf2 = build(ctx, wname, lay)
@@ -343,7 +348,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32_transpose": "f32", "fp16_transpose": "f16", "map": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
+        "dtype": {"fp32_transpose": "f32", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "map": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
         "data": "synthetic",
         "config": {k: v for k, v in info.items() if not k.startswith("_")},
         "roofline": {

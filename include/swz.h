@@ -67,6 +67,12 @@ enum swz_layout {
  *  B128_8X8   : 2-byte elements, 64x128 tile, each lane reads 16-byte row
  *               pieces of 8 rows and transposes an 8x8 block in registers.
  *  MFMA_16X16X32 : operand staging; see swz_stage_operand.
+ *  B64_TR16   : 2-byte elements, 64x64 tile, read with the gfx950 LDS
+ *               transpose read (ds_read_b64_tr_b16, the role ldmatrix .trans
+ *               plays in "NVIDIA CuTe Swizzle"): each 16-lane group
+ *               addresses 8-byte row pieces and every lane receives four
+ *               consecutive rows of one column, so two reads give a lane one
+ *               16-byte output piece with no register shuffles.
  *  AUTO       : 4-byte -> SCALAR_COL; 2-byte -> B128_8X8 when cols <= 128,
  *               else B64_4X4. */
 enum swz_read_kind {
@@ -74,7 +80,8 @@ enum swz_read_kind {
     SWZ_READ_SCALAR_COL = 0,
     SWZ_READ_B64_4X4 = 1,
     SWZ_READ_B128_8X8 = 2,
-    SWZ_READ_MFMA_16X16X32 = 3
+    SWZ_READ_MFMA_16X16X32 = 3,
+    SWZ_READ_B64_TR16 = 4
 };
 
 enum swz_frag_kind { SWZ_FRAG_MFMA_F32_16X16X32_BF16 = 0 };

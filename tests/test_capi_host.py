@@ -163,6 +163,24 @@ def restated_accesses(kind, write):
                     for s_ in range(8):
                         coords = [(8 * ((t + nt * j) % 8) + s_, (width // 2) * ((t + nt * j) // 8)) for t in ts]
                         out.append((coords, width))
+        elif kind == T.READ_B64_TR16:  # 64x64 2-byte tile, transpose reads
+            if write:
+                for j in range(4096 * 2 // 16 // nt):
+                    coords = [((t + nt * j) // 8, 8 * ((t + nt * j) % 8)) for t in ts]
+                    out.append((coords, 16))
+            else:
+                # group g = lanes 16g..16g+15 covers rows 16g..16g+15 of one
+                # 8-column chunk; loader q addresses row 16g + 8*((q%4)//2) +
+                # 4*h + q//4 at column 8*chunk + 4*(q%2), h = step ^ (g odd)
+                for k in range(8 // (nt // 64)):
+                    ch = w + (nt // 64) * k
+                    for step in range(2):
+                        coords = []
+                        for l in range(64):
+                            g, q = divmod(l, 16)
+                            h = step ^ (g % 2)
+                            coords.append((16 * g + 8 * ((q % 4) // 2) + 4 * h + q // 4, 8 * ch + 4 * (q % 2)))
+                        out.append((coords, 8))
         else:  # operand staging, 256x64 tile
             if write:
                 for j in range(2048 // nt):
@@ -181,6 +199,7 @@ KIND_GEOM = {
     T.READ_B64_4X4: (2, 64, 64, 8),
     T.READ_B128_8X8: (2, 64, 128, 8),
     T.READ_MFMA_16X16X32: (2, 256, 64, 8),
+    T.READ_B64_TR16: (2, 64, 64, 8),
 }
 
 

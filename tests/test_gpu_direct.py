@@ -38,6 +38,7 @@ KINDS = [
     (T.READ_SCALAR_COL, 4, 32, 32, W.fp32_matrix, 4),
     (T.READ_B64_4X4, 2, 64, 64, W.fp16_matrix, 8),
     (T.READ_B128_8X8, 2, 64, 128, lambda r, c, seed: W.bf16_tensor((r, c), seed=seed), 8),
+    (T.READ_B64_TR16, 2, 64, 64, W.fp16_matrix, 8),
 ]
 
 
@@ -134,6 +135,11 @@ def test_direct_full_fp32_4096():
 def test_direct_full_fp16_8192():
     announce("direct full fp16 8192")
     check(W.fp16_matrix(8192, 8192, seed=0), 2, T.READ_B64_4X4)
+
+
+def test_direct_full_fp16_8192_transpose_read():
+    announce("direct full fp16 8192 transpose read")
+    check(W.fp16_matrix(8192, 8192, seed=0), 2, T.READ_B64_TR16)
 
 
 def test_direct_full_bf16_convert():

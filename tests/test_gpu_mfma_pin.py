@@ -28,9 +28,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 @pytest.fixture(scope="module")
 def probe():
-    path = os.path.join(HERE, "libmfma_probe.so")
+    path = os.path.join(HERE, "libhw_probe.so")
     if not os.path.exists(path):
-        pytest.fail("tests/libmfma_probe.so is missing: run __graft_entry__.build()")
+        pytest.fail("tests/libhw_probe.so is missing: run __graft_entry__.build()")
     lib = ctypes.CDLL(path)
     lib.mfma_probe_16x16x32_bf16.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p]
     lib.mfma_probe_16x16x32_bf16.restype = ctypes.c_int

@@ -83,6 +83,7 @@ KINDS = [
     (T.READ_SCALAR_COL, 4, 32, 32, W.fp32_matrix),
     (T.READ_B64_4X4, 2, 64, 64, W.fp16_matrix),
     (T.READ_B128_8X8, 2, 64, 128, lambda r, c, seed: W.bf16_tensor((r, c), seed=seed)),
+    (T.READ_B64_TR16, 2, 64, 64, W.fp16_matrix),
 ]
 LAYOUTS = ["swizzle", "pad", "plain"]
 
@@ -153,6 +154,7 @@ def test_convert_layout_batches():
         (T.READ_B128_8X8, 2, W.bf16_tensor((3, 200, 128), seed=5)),
         (T.READ_B128_8X8, 2, W.bf16_tensor((2, 64, 100), seed=6)),  # ragged rows of 100
         (T.READ_B64_4X4, 2, W.bf16_tensor((2, 70, 130), seed=7)),
+        (T.READ_B64_TR16, 2, W.bf16_tensor((2, 70, 130), seed=10)),
         (T.READ_SCALAR_COL, 4, W.fp32_matrix(3 * 40, 50, seed=8).reshape(3, 40, 50)),
     ]
     for kind, esz, a in cases:
@@ -216,6 +218,12 @@ def test_full_fp32_4096(layout):
 def test_full_fp16_8192(layout):
     announce("full fp16 8192", layout)
     check_transpose(W.fp16_matrix(8192, 8192, seed=0), 2, layout, T.READ_B64_4X4)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_full_fp16_8192_transpose_read(layout):
+    announce("full fp16 8192 transpose read", layout)
+    check_transpose(W.fp16_matrix(8192, 8192, seed=0), 2, layout, T.READ_B64_TR16)
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)

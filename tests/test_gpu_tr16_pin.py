@@ -1,0 +1,89 @@
+"""Pin of the gfx950 LDS transpose read's lane semantics (needs a GPU).
+
+No page describes this instruction; the transpose-read kernel relies on the
+following reading, measured with a probe: within each group of 16 lanes,
+lane q receives element q % 4 of the 8-byte pieces addressed by lanes
+q//4, q//4 + 4, q//4 + 8 and q//4 + 12 of the same group (in that order).
+The probe fills LDS with halfword i = i, so every received value names the
+LDS halfword it came from.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+torch = pytest.importorskip("torch")
+T = pytest.importorskip("tiled_movement_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def probe():
+    path = os.path.join(HERE, "libhw_probe.so")
+    if not os.path.exists(path):
+        pytest.fail("tests/libhw_probe.so is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.tr16_probe.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p, ctypes.c_void_p]
+    lib.tr16_probe.restype = ctypes.c_int
+    return lib
+
+
+def run(probe, addrs):
+    a = (ctypes.c_int32 * 64)(*[int(x) for x in addrs])
+    out = torch.zeros(256, dtype=torch.int16, device=DEV)
+    assert probe.tr16_probe(a, out.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16).reshape(64, 4).astype(np.int64)
+
+
+def expected(addrs):
+    """The stated reading: halfword index each (lane, element) receives."""
+    exp = np.empty((64, 4), dtype=np.int64)
+    for lane in range(64):
+        g, q = divmod(lane, 16)
+        for j in range(4):
+            src = 16 * g + q // 4 + 4 * j
+            exp[lane, j] = addrs[src] // 2 + q % 4
+    return exp
+
+
+@pytest.mark.parametrize("pattern", ["linear", "rows", "random"])
+def test_transpose_read_lane_semantics(probe, pattern):
+    if pattern == "linear":
+        addrs = [8 * l for l in range(64)]
+    elif pattern == "rows":
+        addrs = [128 * l for l in range(64)]
+    else:
+        rng = np.random.default_rng(31)
+        addrs = [8 * int(b) for b in rng.choice(2047, size=64, replace=False)]
+    assert np.array_equal(run(probe, addrs), expected(addrs))
+
+
+def test_kernel_lane_map_hands_each_lane_eight_rows_of_one_column(probe):
+    """Feed the kernel's own read addresses (swizzled 64x64 tile, first
+    wave) to the instruction and decode what each lane receives back into
+    tile coordinates with the oracle's swizzle: lane q of group g must hold
+    rows 16g + 8(q//8) + 4h .. +3 of column 8*chunk + 4((q//4)%2) + q%4."""
+    B, M, S = T.swz_plan(0, 64, 64, 2, "swizzle", T.READ_B64_TR16)["params"]
+    accesses = T.swz_kernel_accesses(T.READ_B64_TR16, "swizzle", None, 0)
+    nt = T.swz_plan(0, 64, 64, 2, "swizzle", T.READ_B64_TR16)["threads"]
+    steps_per_wave = len(accesses) // (nt // 64)
+    for i in range(steps_per_wave):  # wave 0
+        addrs, width = accesses[i]
+        assert width == 8
+        got = run(probe, addrs)
+        k, step = divmod(i, 2)
+        for lane in range(64):
+            g, q = divmod(lane, 16)
+            h = step ^ (g % 2)
+            for j in range(4):
+                elem = O.swizzle(int(got[lane, j]), B, M, S)  # LDS slot -> tile element
+                r, c = divmod(elem, 64)
+                assert (r, c) == (16 * g + 8 * (q // 8) + 4 * h + j, 8 * (nt // 64) * k + 4 * ((q // 4) % 2) + q % 4)

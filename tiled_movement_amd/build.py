@@ -60,9 +60,9 @@ def flags():
 
 
 def build_test_helper(verbose: bool = False) -> str:
-    """The tests' hardware probe (tests/mfma_probe.hip -> tests/libmfma_probe.so)."""
-    src = os.path.join(ROOT, "tests", "mfma_probe.hip")
-    out = os.path.join(ROOT, "tests", "libmfma_probe.so")
+    """The tests' hardware probes (tests/hw_probe.hip -> tests/libhw_probe.so)."""
+    src = os.path.join(ROOT, "tests", "hw_probe.hip")
+    out = os.path.join(ROOT, "tests", "libhw_probe.so")
     cmd = [hipcc()] + flags() + ["-shared", "-o", out + ".tmp", "-x", "hip", src]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -109,6 +109,7 @@ int kernel_accesses(int kind, uint32_t ld, swz_params p, bool direct, bool write
         case SWZ_READ_B128_8X8: return accesses_kind<SWZ_READ_B128_8X8>(ld, p, direct, write, addrs, max_acc, width);
         case SWZ_READ_MFMA_16X16X32:
             return accesses_kind<SWZ_READ_MFMA_16X16X32>(ld, p, direct, write, addrs, max_acc, width);
+        case SWZ_READ_B64_TR16: return accesses_kind<SWZ_READ_B64_TR16>(ld, p, direct, write, addrs, max_acc, width);
         default: return -1;
     }
 }
@@ -125,6 +126,7 @@ bool kind_info(int kind, KindInfo* o) {
         SWZ_KIND_CASE(SWZ_READ_B64_4X4)
         SWZ_KIND_CASE(SWZ_READ_B128_8X8)
         SWZ_KIND_CASE(SWZ_READ_MFMA_16X16X32)
+        SWZ_KIND_CASE(SWZ_READ_B64_TR16)
 #undef SWZ_KIND_CASE
         default:
             return false;
@@ -146,6 +148,7 @@ void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64
         case SWZ_READ_B64_4X4: predict_kind<SWZ_READ_B64_4X4>(m, ld, p, direct, wcyc, rcyc); break;
         case SWZ_READ_B128_8X8: predict_kind<SWZ_READ_B128_8X8>(m, ld, p, direct, wcyc, rcyc); break;
         case SWZ_READ_MFMA_16X16X32: predict_kind<SWZ_READ_MFMA_16X16X32>(m, ld, p, direct, wcyc, rcyc); break;
+        case SWZ_READ_B64_TR16: predict_kind<SWZ_READ_B64_TR16>(m, ld, p, direct, wcyc, rcyc); break;
         default: *wcyc = *rcyc = -1;
     }
 }
@@ -214,11 +217,12 @@ swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles) {
 
 swz_params cached_choice(int kind) {
     static std::once_flag once;
-    static swz_params table[4];
+    constexpr int kKinds = SWZ_READ_B64_TR16 + 1;
+    static swz_params table[kKinds];
     std::call_once(once, [] {
-        for (int kd = 0; kd < 4; ++kd) table[kd] = choose_for_kind(kd, gfx950_bank_model(), nullptr);
+        for (int kd = 0; kd < kKinds; ++kd) table[kd] = choose_for_kind(kd, gfx950_bank_model(), nullptr);
     });
-    if (kind < 0 || kind > 3) return swz_params{0, 0, 0};
+    if (kind < 0 || kind >= kKinds) return swz_params{0, 0, 0};
     return table[kind];
 }
 

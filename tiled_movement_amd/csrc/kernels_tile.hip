@@ -253,6 +253,42 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             else
                 store16_guarded<4>(D, orow, ocol, cols, rows, o);
         }
+    } else if constexpr (KIND == SWZ_READ_B64_TR16) {
+        // Task j: two transpose reads give this lane 8 consecutive rows of
+        // one column (the lane map in swz_common.h); odd 16-lane groups read
+        // their upper four rows first, so their halves are swapped back.
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+        const int l = t % 64, g = l / 16, q = l % 16;
+        const bool odd = g & 1;
+        int lr0 = 0, lc0 = 0;
+        K::rcoord(t, 0, lr0, lc0);
+#pragma unroll
+        for (int j = 0; j < K::TASKS; ++j) {
+            u32x2 h[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                uint32_t off;
+                if constexpr (PADDED) {
+                    int dr = 0, dc = 0;
+                    K::rcoord(0, 2 * j + s, dr, dc);
+                    off = static_cast<uint32_t>(lr0 ^ dr) * L.ld + static_cast<uint32_t>(lc0 ^ dc);
+                } else {
+                    off = step_off<KIND, false, false>(rbase, 2 * j + s, L);
+                }
+                const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((__attribute__((address_space(3))) uint8_t*)lds + 2 * off));
+                h[s] = __builtin_bit_cast(u32x2, v);
+            }
+            const u32x2 lo = odd ? h[1] : h[0], hi = odd ? h[0] : h[1];
+            const u32x4 o{lo[0], lo[1], hi[0], hi[1]};
+            const int ch = t / 64 + (K::NT / 64) * j;
+            const int64_t orow = c0 + 8 * ch + 4 * ((q / 4) % 2) + q % 4;
+            const int64_t ocol = r0 + 16 * g + 8 * (q / 8);
+            if (FULL)
+                gstore16(D + (orow * rows + ocol) * 2, o);
+            else
+                store16_guarded<2>(D, orow, ocol, cols, rows, o);
+        }
     } else {
         // Task j: 8 rows of a column block; transpose 16-bit elements in
         // registers and write one 16-byte piece of each output row.
@@ -492,6 +528,7 @@ hipError_t launch_convert(int kind, const ConvertJob& j, hipStream_t stream) {
         case SWZ_READ_SCALAR_COL: return launch_kind<SWZ_READ_SCALAR_COL>(j, stream);
         case SWZ_READ_B64_4X4: return launch_kind<SWZ_READ_B64_4X4>(j, stream);
         case SWZ_READ_B128_8X8: return launch_kind<SWZ_READ_B128_8X8>(j, stream);
+        case SWZ_READ_B64_TR16: return launch_kind<SWZ_READ_B64_TR16>(j, stream);
         default: return hipErrorInvalidValue;
     }
 }

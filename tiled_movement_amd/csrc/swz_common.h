@@ -23,6 +23,9 @@
 #ifndef SWZ_NT_STAGE
 #define SWZ_NT_STAGE 256
 #endif
+#ifndef SWZ_NT_TR16
+#define SWZ_NT_TR16 128
+#endif
 
 namespace swz {
 
@@ -157,17 +160,57 @@ template <> struct Kind<SWZ_READ_MFMA_16X16X32> {
     }
 };
 
+// 2-byte elements, 64x64 tile read back with the gfx950 transpose read
+// (ds_read_b64_tr_b16).  Its lane semantics, measured on the hardware: in
+// each group of 16 lanes, lane q receives element q%4 of the 8-byte pieces
+// that lanes q/4, q/4 + 4, q/4 + 8 and q/4 + 12 of its group addressed.  So
+// if loader lane s = a + 4j (a = s%4) addresses row R_a + j of the 4-column
+// block at column C_a, receiver q = 4a + e gets rows R_a .. R_a + 3 of
+// column C_a + e in order: a 4x4 transpose inside the read.
+// Staging as for the 4x4 read.  Read: wave w's task k covers 16-byte chunk
+// ch = w + (NT/64)*k (8 columns) of all 64 rows; group g of the wave takes
+// rows 16g .. 16g + 15.  Loader q of group g reads row
+// 16g + 8*((q%4)/2) + 4*h + q/4, columns 8ch + 4*(q%2), in two steps
+// h = s ^ (g%2), s = 0, 1: odd groups read their upper four rows first.
+// Receiver q then holds rows 16g + 8*(q/8) + 0..7 of column
+// 8ch + 4*((q/4)%2) + q%4 after both steps -- one 16-byte output piece --
+// and a wave's store covers 8 output rows of 64 source rows each (whole
+// 128-byte rows).  The swapped order puts the two groups of one LDS phase
+// on different row bit 2, which the swizzle can turn into different banks.
+template <> struct Kind<SWZ_READ_B64_TR16> {
+    static constexpr int ESZ = 2, TR = 64, TC = 64, NT = SWZ_NT_TR16;
+    static constexpr int VEC = 16;
+    static constexpr int RWIDTH = 8;
+    static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
+    static constexpr int WSTEPS = GLOADS;
+    static constexpr int TASKS = (TC / 8) / (NT / 64);  // 16-byte chunks per wave
+    static constexpr int RSTEPS = 2 * TASKS;
+    __host__ __device__ static constexpr void wcoord(int t, int i, int& r, int& c) {
+        const int v = t + NT * i;
+        r = v / 8;
+        c = 8 * (v % 8);
+    }
+    __host__ __device__ static constexpr void rcoord(int t, int i, int& r, int& c) {
+        const int w = t / 64, l = t % 64, g = l / 16, q = l % 16;
+        const int k = i / 2, h = (i % 2) ^ (g % 2);
+        r = 16 * g + 8 * ((q % 4) / 2) + 4 * h + q / 4;
+        c = 8 * (w + (NT / 64) * k) + 4 * (q % 2);
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Offsets of a lane's later steps from its first one.
 //
-// In every lane map above, step i's element is the first step's element
-// moved by an amount that does not depend on the lane, and (with rows of TC
-// elements) that amount's offset bits never overlap the first step's offset
-// bits.  The swizzle is linear over GF(2) (x -> x ^ ((x >> (M+S)) & mask) << M),
-// so swizzle(base + d) = swizzle(base ^ d) = swizzle(base) ^ swizzle(d): each
-// access is the lane's one swizzled base XOR a value shared by the whole
-// wave.  For padded rows the same holds with + in place of ^.  The checks
-// below prove the property for every lane and step at compile time.
+// In every lane map above, step i's row and column are the first step's
+// XORed with amounts that do not depend on the lane, so (rows of TC
+// elements, TC a power of two) the flat offset is the first one XOR a
+// wave-wide value d.  The swizzle is linear over GF(2)
+// (x -> x ^ ((x >> (M+S)) & mask) << M), so swizzle(base ^ d) =
+// swizzle(base) ^ swizzle(d): each access is the lane's one swizzled base XOR
+// a value shared by the whole wave.  Except in the transpose read, the
+// moved bits never overlap the first step's, so the same amounts also add,
+// which is what padded rows use.  The checks below prove these properties
+// for every lane and step at compile time.
 // ---------------------------------------------------------------------------
 template <int KIND, bool WRITE>
 __host__ __device__ constexpr void coord(int t, int i, int& r, int& c) {
@@ -177,20 +220,24 @@ __host__ __device__ constexpr void coord(int t, int i, int& r, int& c) {
         Kind<KIND>::rcoord(t, i, r, c);
 }
 
+// ADDITIVE: also r = r0 + dr and c = c0 + dc (what the padded layout's
+// offsets need); the transpose read's steps only combine by XOR, and its
+// padded variant computes each step's row and column instead.
 template <int KIND, bool WRITE>
-constexpr bool steps_decompose() {
+constexpr bool steps_decompose(bool additive = true) {
     using K = Kind<KIND>;
     const int steps = WRITE ? K::WSTEPS : K::RSTEPS;
     for (int t = 0; t < K::NT; ++t) {
-        int r0 = 0, c0 = 0;
+        int r0 = 0, c0 = 0, z0 = 0, z1 = 0;
         coord<KIND, WRITE>(t, 0, r0, c0);
-        const int base = r0 * K::TC + c0;
+        coord<KIND, WRITE>(0, 0, z0, z1);
+        if (t == 0 && (z0 != 0 || z1 != 0)) return false;  // lane 0 starts at (0, 0)
         for (int i = 0; i < steps; ++i) {
             int r = 0, c = 0, dr = 0, dc = 0;
             coord<KIND, WRITE>(t, i, r, c);
-            coord<KIND, WRITE>(0, i, dr, dc);  // lane 0 starts at (0, 0)
-            if (r - r0 != dr || c - c0 != dc) return false;
-            if (base & (dr * K::TC + dc)) return false;
+            coord<KIND, WRITE>(0, i, dr, dc);
+            if (r != (r0 ^ dr) || c != (c0 ^ dc)) return false;
+            if (additive && (r - r0 != dr || c - c0 != dc)) return false;
             if (r >= K::TR || c >= K::TC || r < 0 || c < 0) return false;
         }
     }
@@ -221,6 +268,10 @@ static_assert(steps_decompose<SWZ_READ_B128_8X8, true>() && steps_decompose<SWZ_
               "8x8 lane map");
 static_assert(steps_decompose<SWZ_READ_MFMA_16X16X32, true>() && steps_decompose<SWZ_READ_MFMA_16X16X32, false>(),
               "fragment lane map");
+static_assert(even_split<SWZ_READ_B64_TR16>() && Kind<SWZ_READ_B64_TR16>::TASKS * (Kind<SWZ_READ_B64_TR16>::NT / 64) == 8,
+              "transpose-read thread count");
+static_assert(steps_decompose<SWZ_READ_B64_TR16, true>() && steps_decompose<SWZ_READ_B64_TR16, false>(false),
+              "transpose-read lane map");
 
 // ---------------------------------------------------------------------------
 // Direct fill (SWZ_LAYOUT_SWIZZLE_DIRECT): the tile goes from HBM straight
@@ -252,7 +303,8 @@ constexpr bool direct_split() {
            (K::TC & (K::TC - 1)) == 0;
 }
 static_assert(direct_split<SWZ_READ_SCALAR_COL>() && direct_split<SWZ_READ_B64_4X4>() &&
-                  direct_split<SWZ_READ_B128_8X8>() && direct_split<SWZ_READ_MFMA_16X16X32>(),
+                  direct_split<SWZ_READ_B128_8X8>() && direct_split<SWZ_READ_MFMA_16X16X32>() &&
+                  direct_split<SWZ_READ_B64_TR16>(),
               "direct fill split");
 
 }  // namespace swz
