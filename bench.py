@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "effective HBM GB/s (% of 8 TB/s) for swizzled LDS transpose; LDS conflict cycles"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 CACHE_DEFEAT_BYTES = 512 * 2**20  # 2x the 256 MB Infinity Cache
 
 WORKLOADS = {
@@ -44,6 +45,7 @@ WORKLOADS = {
     "bf16_convert": "bf16 [64,4096,128] -> [64,128,4096] layout conversion, 64x128 LDS tiles, 16-byte reads of 8x8 blocks",
     "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
+    "bf16_gemm": "C[8192x8192] fp32 = A * B^T from the staged fragments of A[8192x4096] and B[4096x8192] (16x16x32 bf16 MFMA)",
     "copy": "reference 16-byte vector copy of 64 MiB (read once, write once)",
     "copy_128": "reference 16-byte vector copy of 128 MiB (the byte count of the 256 MiB workloads)",
     "memcpy_d2d": "runtime device-to-device copy (hipMemcpyAsync through torch) of 64 MiB, for context",
@@ -203,6 +205,27 @@ def build(ctx, name, layout):
         info["_keep"] = (sa, sb, fa, fb)
         return step, 2 * (ao.nbytes + bo.nbytes), info
 
+    if name == "bf16_gemm":
+        m = n = 8192
+        k = 4096
+        ao, bo = W.bf16_operands(m, n, k, seed=0)
+        fa = ctx.torch.empty(ao.size, dtype=ctx.torch.int16, device=ctx.dev)
+        fb = ctx.torch.empty(bo.size, dtype=ctx.torch.int16, device=ctx.dev)
+        T.swz_stage_operand(ctx.copies(ao, 1)[0], fa, m, k)
+        T.swz_stage_operand(ctx.copies(bo, 1)[0], fb, n, k)
+        c = ctx.torch.empty((m, n), dtype=ctx.torch.float32, device=ctx.dev)
+        pfa, pfb, pc = fa.data_ptr(), fb.data_ptr(), c.data_ptr()
+        frag = T.FRAG_MFMA_F32_16X16X32_BF16
+
+        def step(i):
+            rc = lib.swz_gemm_frag(pfa, pfb, pc, m, n, k, frag, stream)
+            if rc:
+                ctx.check(rc, "swz_gemm_frag")
+
+        info.update({"m": m, "n": n, "k": k, "flops_per_step": 2 * m * n * k, "unit_of_value": "TFLOP/s"})
+        info["_keep"] = (fa, fb, c)
+        return step, 2 * m * n * k, info
+
     if name == "map":
         x = ctx.torch.arange(65536, dtype=ctx.torch.int32, device=ctx.dev)
         y = ctx.torch.empty_like(x)
@@ -308,14 +331,22 @@ def main(argv=None):
     extra = {}
     if not args.quick and args.workload is None:
         for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "fp16_transpose_tr",
-                      "bf16_convert", "bf16_stage", "map"):
-            for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map")
+                      "bf16_convert", "bf16_stage", "map", "bf16_gemm"):
+            for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map", "bf16_gemm")
                         else ("swizzle", "pad", "plain", "direct")):
                 s2, nb2, inf2 = build(ctx, wname, lay)
                 if wname == "map":
                     rate, ms2 = median_rate(s2, nb2, steps=250, warmup=25)
                     extra["map/swizzle"] = {"us_per_call": round(ms2 * 1e3, 3)}
                     log(f"map: {ms2 * 1e3:.2f} us/call")
+                    continue
+                if wname == "bf16_gemm":
+                    rate, ms2 = median_rate(s2, nb2, steps=20, warmup=5)
+                    tflops = rate / 1e3  # nb2 counts flops, so rate is GFLOP/s
+                    extra["bf16_gemm"] = {"TFLOPs": round(tflops, 1), "frac_of_mfma_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                                          "us_per_step": round(ms2 * 1e3, 1), "m": 8192, "n": 8192, "k": 4096}
+                    log(f"bf16_gemm: {tflops:.1f} TFLOP/s")
+                    del s2, inf2
                     continue
                 rate, ms2 = median_rate(s2, nb2)
                 rec = {k: v for k, v in inf2.items() if not k.startswith("_") and k != "workload"}
@@ -364,6 +395,13 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "extra": extra,
     }
+    if name == "bf16_gemm":  # a contraction: flops, against the bf16 matrix peak
+        tflops = value / 1e3
+        line.update({"metric": "bf16 GEMM from staged fragments, TFLOP/s", "value": round(tflops, 1),
+                     "unit": "TFLOP/s", "dtype": "bf16"})
+        line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                            "algorithmic_flops_per_launch": nbytes}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -74,7 +74,7 @@ enum swz_layout {
  *               consecutive rows of one column, so two reads give a lane one
  *               16-byte output piece with no register shuffles.
  *  AUTO       : 4-byte -> SCALAR_COL; 2-byte -> B128_8X8 when cols <= 128,
- *               else B64_4X4. */
+ *               else B64_TR16 (the faster of the two 64x64 kinds). */
 enum swz_read_kind {
     SWZ_READ_AUTO = -1,
     SWZ_READ_SCALAR_COL = 0,
@@ -157,6 +157,25 @@ int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, int64_t ro
  * Errors: SWZ_EINVAL otherwise. */
 int swz_stage_operand(const void* d_src, void* d_frag, int64_t mn, int64_t k, int32_t elem_bytes,
                       int32_t frag_kind, int32_t layout, const swz_params* p_or_null, void* stream);
+
+/* Consumer of staged fragments: d_c = A * B^T in fp32, where d_fa and d_fb
+ * are what swz_stage_operand wrote for A [m][k] and for B^T [n][k] (B
+ * column-major), on the 16x16x32 bf16 matrix instruction with fp32
+ * accumulation.  The operand read that feeds the matrix unit is the step
+ * the pages put after the swizzled staging ("NVIDIA CuTe Swizzle", ldmatrix
+ * and WGMMA; "CuTe Swizzle 学习手册", usage step 5); since the fragments are
+ * already in lane order, each is one contiguous KiB, loaded straight into
+ * LDS and read back lane-linearly (every bank once).
+ *   d_c : [m][n] row-major fp32, written (not accumulated into); must not
+ *         overlap the inputs.
+ *   m, n multiples of 16, k a multiple of 32 (the fragment format); k = 0
+ *   writes zeros.  All pointers 16-byte aligned.  frag_kind must be
+ *   SWZ_FRAG_MFMA_F32_16X16X32_BF16.
+ * The sum over k is taken 32 at a time by the instruction and accumulated
+ * in fp32 in increasing k order.
+ * Errors: SWZ_EINVAL (sizes, alignment, NULL, overlap, fragment kind). */
+int swz_gemm_frag(const void* d_fa, const void* d_fb, float* d_c, int64_t m, int64_t n, int64_t k,
+                  int32_t frag_kind, void* stream);
 
 /* Host only.  The swizzle the library uses for a tile of tile_rows x
  * tile_cols elements of elem_bytes, staged by vec_bytes-wide stores and read

@@ -43,6 +43,9 @@ __all__ = [
     "convert_layout",
     "stage_operand",
     "stage_operand_loops",
+    "bf16_to_f64",
+    "gemm_bf16",
+    "gemm_error_bound",
     "BankModel",
     "LdsModel",
     "nvidia_model",
@@ -192,6 +195,31 @@ def stage_operand(x: np.ndarray) -> np.ndarray:
     row = FRAG_ROWS * i + lane % 16
     col = FRAG_K * j + 8 * (lane // 16) + e
     return x[row, col]
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns: the upper half of an fp32 word."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def gemm_bf16(a_bits: np.ndarray, bt_bits: np.ndarray) -> np.ndarray:
+    """C = A * B^T of bf16 operands (A [m][k], B^T [n][k], as bit patterns),
+    in fp64 -- the product the staged fragments feed to the matrix unit
+    ([CuTe-DSL] ldmatrix / WGMMA as the consumer of the staged tile;
+    [Handbook] ⑤).  The step is a library matmul over exact fp64 values."""
+    return bf16_to_f64(a_bits) @ bf16_to_f64(bt_bits).T
+
+
+def gemm_error_bound(a_bits: np.ndarray, bt_bits: np.ndarray, chunk: int = 32) -> np.ndarray:
+    """Per-element bound on |fp32 result - exact| for a sum of k products
+    taken `chunk` at a time and accumulated in fp32: each of the k/chunk
+    accumulations and each chunk's own summation round at most once per
+    step, so |error| <= (k/chunk + chunk) * 2^-24 * sum_k |a| |b| (a
+    first-order bound; tests use it with a factor of 2 of margin)."""
+    k = np.asarray(a_bits).shape[1]
+    steps = k // chunk + chunk
+    return steps * 2.0 ** -24 * (np.abs(bf16_to_f64(a_bits)) @ np.abs(bf16_to_f64(bt_bits)).T)
 
 
 def stage_operand_loops(x: np.ndarray) -> np.ndarray:

@@ -49,7 +49,7 @@ def test_strerror():
 # ------------------------------------------------------ argument checking
 # Fake, never-dereferenced device addresses: every call below must be
 # rejected (or be a no-op) before anything reaches the HIP runtime.
-A, B = 0x7F0000000000, 0x7F0100000000
+A, B, C = 0x7F0000000000, 0x7F0100000000, 0x7F0200000000
 
 
 def test_map_validation():
@@ -115,7 +115,7 @@ def test_plans():
     p = T.swz_plan(0, 4096, 4096, 4, "swizzle")
     assert p["read_kind"] == T.READ_SCALAR_COL and p["tile"] == (32, 32) and p["lds_bytes"] == 4096
     assert T.swz_plan(0, 4096, 4096, 4, "pad")["lds_bytes"] == 32 * 33 * 4
-    assert T.swz_plan(0, 8192, 8192, 2)["read_kind"] == T.READ_B64_4X4
+    assert T.swz_plan(0, 8192, 8192, 2)["read_kind"] == T.READ_B64_TR16
     assert T.swz_plan(0, 4096, 128, 2)["read_kind"] == T.READ_B128_8X8
     assert T.swz_plan(0, 64, 64, 2, "pad", T.READ_B64_4X4)["lds_bytes"] == 64 * 72 * 2
     assert T.swz_plan(0, 64, 64, 2, "plain", T.READ_B64_4X4)["params"] == (0, 0, 0)
@@ -336,3 +336,17 @@ def test_direct_fill_places_every_element_where_swizzle_does(kind):
             assert O.tile_offset(r, c, tc, "swizzle", (B, M, S)) == p
             fetched.append(e)
         assert sorted(fetched) == list(range(0, tr * tc, epl))
+
+
+def test_gemm_validation():
+    f = lib.swz_gemm_frag
+    assert f(A, B, C, 24, 32, 32, 0, None) == EINVAL  # m not a multiple of 16
+    assert f(A, B, C, 32, 24, 32, 0, None) == EINVAL  # n
+    assert f(A, B, C, 32, 32, 48, 0, None) == EINVAL  # k not a multiple of 32
+    assert f(A, B, C, 32, 32, 32, 1, None) == EINVAL  # fragment kind
+    assert f(A + 8, B, C, 32, 32, 32, 0, None) == EINVAL  # alignment
+    assert f(A, B, None, 32, 32, 32, 0, None) == EINVAL
+    assert f(A, B, A + 64, 32, 32, 32, 0, None) == EINVAL  # C overlaps A's fragments
+    assert f(A, B, C, -16, 32, 32, 0, None) == EINVAL
+    assert f(A, B, C, 0, 32, 32, 0, None) == T.SWZ_OK  # empty: no launch
+    assert f(A, B, C, 1 << 40, 1 << 40, 32, 0, None) == EINVAL  # size overflow

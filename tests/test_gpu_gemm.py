@@ -1,0 +1,94 @@
+"""The consumer of the staged fragments (needs a GPU): swz_stage_operand
+for A and for B^T, then swz_gemm_frag, against the oracle's fp64 product.
+
+Integer-valued operands make every partial sum exact in fp32, so those
+cases must match bit for bit; random operands must stay within the
+oracle's bound for fp32 accumulation in 32-wide chunks (with a factor of 2
+of margin).
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+torch = pytest.importorskip("torch")
+T = pytest.importorskip("tiled_movement_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def announce(*what):
+    print("case:", *what, flush=True)
+
+
+def int_bf16(shape, seed, lo=-2, hi=3):
+    v = np.random.default_rng(seed).integers(lo, hi, size=shape).astype(np.float32)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def gemm_on_gpu(a, bt, layout="swizzle"):
+    m, k = a.shape
+    n = bt.shape[0]
+    fa = torch.empty(a.size, dtype=torch.int16, device=DEV)
+    fb = torch.empty(bt.size, dtype=torch.int16, device=DEV)
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    if k:
+        T.swz_stage_operand(torch.from_numpy(a.view(np.int16)).to(DEV), fa, m, k, layout=layout)
+        T.swz_stage_operand(torch.from_numpy(bt.view(np.int16)).to(DEV), fb, n, k, layout=layout)
+    T.swz_gemm_frag(fa, fb, c, m, n, k)
+    torch.cuda.synchronize()
+    return c.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 16, 32), (256, 256, 64), (272, 400, 96), (512, 256, 4096), (48, 784, 160)])
+def test_integer_operands_exact(m, n, k):
+    announce("gemm exact", m, n, k)
+    a, bt = int_bf16((m, k), m + k), int_bf16((n, k), n + 3 * k)
+    got = gemm_on_gpu(a, bt)
+    assert np.array_equal(got, O.gemm_bf16(a, bt))
+
+
+def test_fragments_from_every_layout_give_the_same_product():
+    a, bt = int_bf16((272, 96), 1), int_bf16((144, 96), 2)
+    ref = O.gemm_bf16(a, bt)
+    for layout in ("swizzle", "pad", "plain", "direct"):
+        announce("gemm after staging", layout)
+        assert np.array_equal(gemm_on_gpu(a, bt, layout), ref)
+
+
+def test_k_zero_writes_zeros():
+    announce("gemm k=0")
+    got = gemm_on_gpu(np.zeros((32, 0), np.uint16), np.zeros((48, 0), np.uint16))
+    assert got.shape == (32, 48) and np.all(got == 0)
+
+
+def test_random_operands_within_fp32_bound():
+    announce("gemm random 512x768x4096")
+    a, bt = W.bf16_operands(512, 768, 4096, seed=5, std=1.0)
+    got = gemm_on_gpu(a, bt)
+    err = np.abs(got - O.gemm_bf16(a, bt))
+    assert np.all(err <= 2 * O.gemm_error_bound(a, bt))
+
+
+def test_full_size_sampled_rows():
+    """A [8192 x 4096] and B^T [8192 x 4096] (the staging workload's
+    operands): rows sampled across the first, middle and last 256-row tiles
+    are compared with the oracle within the bound."""
+    announce("gemm full 8192x8192x4096")
+    a, bt = W.bf16_operands(8192, 8192, 4096, seed=0)
+    got_dev = None
+    fa = torch.empty(a.size, dtype=torch.int16, device=DEV)
+    fb = torch.empty(bt.size, dtype=torch.int16, device=DEV)
+    T.swz_stage_operand(torch.from_numpy(a.view(np.int16)).to(DEV), fa, 8192, 4096)
+    T.swz_stage_operand(torch.from_numpy(bt.view(np.int16)).to(DEV), fb, 8192, 4096)
+    c = torch.empty((8192, 8192), dtype=torch.float32, device=DEV)
+    T.swz_gemm_frag(fa, fb, c, 8192, 8192, 4096)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 15, 16, 255, 256, 4095, 4100, 8191, 8190, 7936, 3333])
+    got_dev = c[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    ref = O.gemm_bf16(a[rows], bt)
+    bound = O.gemm_error_bound(a[rows], bt)
+    assert np.all(np.abs(got_dev - ref) <= 2 * bound)

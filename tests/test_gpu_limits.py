@@ -1,0 +1,73 @@
+"""Launch-shape limits (needs a GPU): grids beyond the hardware's 3-D limits
+take the 1-D chunked launch path, and jobs above 2^22 tiles are split over
+several launches.  Outputs are compared with the oracle on whole batch
+entries or row blocks sampled at the start, at the chunk boundary and at
+the end.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+torch = pytest.importorskip("torch")
+T = pytest.importorskip("tiled_movement_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def announce(*what):
+    print("case:", *what, flush=True)
+
+
+def test_transpose_with_more_tile_columns_than_a_grid_dimension():
+    rows, cols = 40, 32 * 65537 + 8  # 65,538 tile columns > 65,535
+    a = W.fp32_matrix(rows, cols, seed=40)
+    for layout in ("swizzle", "direct"):
+        announce("wide transpose", layout, rows, cols)
+        src = torch.from_numpy(a.view(np.int32)).to(DEV)
+        dst = torch.empty((cols, rows), dtype=torch.int32, device=DEV)
+        T.swz_transpose(src, dst, rows, cols, 4, layout)
+        torch.cuda.synchronize()
+        assert np.array_equal(dst.cpu().numpy().view(np.uint32), O.transpose(a))
+
+
+def test_batch_beyond_grid_limit_and_more_than_2_22_tiles():
+    """65,537 batch entries of 256 x 256 fp32 = 4,194,368 tiles of 32 x 32:
+    a batch beyond the 65,535 grid limit and one tile chunk past 2^22."""
+    batch, rows, cols = 65537, 256, 256
+    free, _ = torch.cuda.mem_get_info()
+    need = 2 * batch * rows * cols * 4
+    if free < need + (4 << 30):
+        pytest.skip(f"needs {need >> 30} GiB of free device memory")
+    announce("huge batch", batch, rows, cols)
+    src = W.index_pattern_device((batch, rows, cols), DEV, 4)
+    dst = torch.empty((batch, cols, rows), dtype=torch.int32, device=DEV)
+    T.swz_convert_layout(src, dst, batch, rows, cols, 4, "swizzle")
+    torch.cuda.synchronize()
+    tiles_per_entry = (rows // 32) * (cols // 32)
+    boundary = (1 << 22) // tiles_per_entry  # first entry of the second launch chunk
+    for b in sorted({0, 1, 12345, boundary - 1, boundary, batch - 1}):
+        a = W.index_pattern_host((batch, rows, cols), b, 4)
+        got = dst[b].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, O.transpose(a)), b
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def test_stage_with_more_row_tiles_than_a_grid_dimension():
+    mn, k = 256 * 65537, 64  # 65,537 row tiles of 256 > 65,535
+    announce("tall staging", mn, k)
+    src = W.index_pattern_device((mn // 16, 16 * k), DEV, 2)  # rows of 16 x k, same bytes as [mn][k]
+    frag = torch.empty(mn * k, dtype=torch.int16, device=DEV)
+    for layout in ("swizzle", "direct"):
+        frag.zero_()
+        T.swz_stage_operand(src, frag, mn, k, layout=layout)
+        torch.cuda.synchronize()
+        f = frag.view(mn // 16, k // 32, 64, 8)
+        for blk in sorted({0, 7, 16 * 65535, mn // 16 - 1}):
+            x = W.index_pattern_host((mn // 16, 16 * k), blk, 2).reshape(16, k)
+            got = f[blk].cpu().numpy().view(np.uint16)
+            assert np.array_equal(got, O.stage_operand(x)[0]), (layout, blk)

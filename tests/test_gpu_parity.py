@@ -169,12 +169,15 @@ def test_convert_layout_batches():
 
 
 def test_auto_read_kind():
-    a = W.bf16_tensor((4, 96, 128), seed=9)
-    src = to_dev(a)
-    dst = torch.empty((4, 128, 96), dtype=src.dtype, device=DEV)
-    T.swz_convert_layout(src, dst, 4, 96, 128, 2)
-    torch.cuda.synchronize()
-    assert np.array_equal(from_dev(dst, a), O.convert_layout(a))
+    for shape in [(4, 96, 128), (2, 100, 300)]:  # narrow rows -> 8x8 reads; wide -> transpose reads
+        a = W.bf16_tensor(shape, seed=9)
+        b, r, c = shape
+        announce("auto", shape, T.swz_plan(0, r, c, 2)["read_kind"])
+        src = to_dev(a)
+        dst = torch.empty((b, c, r), dtype=src.dtype, device=DEV)
+        T.swz_convert_layout(src, dst, b, r, c, 2)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(dst, a), O.convert_layout(a))
 
 
 # ------------------------------------------------------- operand staging

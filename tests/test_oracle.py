@@ -350,3 +350,64 @@ def test_stage_operand_fragments_multiply_like_the_operands():
 def test_stage_operand_rejects_partial_fragments():
     with pytest.raises(ValueError):
         O.stage_operand(np.zeros((17, 32), dtype=np.uint16))
+
+
+# ------------------------------------------------- consumer of the fragments
+
+
+def test_bf16_decode_known_values():
+    # bf16 patterns of 1.0, -2.0, 0.5 and the smallest normal
+    bits = np.array([0x3F80, 0xC000, 0x3F00, 0x0080], dtype=np.uint16)
+    assert list(O.bf16_to_f64(bits)) == [1.0, -2.0, 0.5, 2.0 ** -126]
+
+
+def _bf16_bits_of_ints(v):
+    return (np.asarray(v, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_gemm_matches_brute_force_integer_products():
+    """Small integers are exact in bf16; the product is checked against a
+    pure-Python triple loop, with A and B of different shapes so a swapped
+    or untransposed operand cannot pass."""
+    rng = np.random.default_rng(8)
+    a = rng.integers(-3, 4, size=(5, 7))
+    bt = rng.integers(-3, 4, size=(3, 7))
+    got = O.gemm_bf16(_bf16_bits_of_ints(a), _bf16_bits_of_ints(bt))
+    assert got.shape == (5, 3)
+    for i in range(5):
+        for j in range(3):
+            assert got[i, j] == sum(int(a[i, t]) * int(bt[j, t]) for t in range(7))
+
+
+def test_gemm_through_fragments_equals_gemm():
+    """Multiplying the oracle's fragments block by block, lane group by lane
+    group, reproduces the oracle's product (the fragment layout is what the
+    consumer relies on)."""
+    rng = np.random.default_rng(9)
+    a = _bf16_bits_of_ints(rng.integers(-2, 3, size=(32, 64)))
+    bt = _bf16_bits_of_ints(rng.integers(-2, 3, size=(48, 64)))
+    fa, fb = O.stage_operand(a), O.stage_operand(bt)
+    ref = O.gemm_bf16(a, bt)
+    for i in range(2):
+        for n in range(3):
+            acc = np.zeros((16, 16))
+            for j in range(2):
+                for g in range(4):
+                    acc += O.bf16_to_f64(fa[i, j, 16 * g:16 * g + 16]) @ O.bf16_to_f64(fb[n, j, 16 * g:16 * g + 16]).T
+            assert np.array_equal(acc, ref[16 * i:16 * i + 16, 16 * n:16 * n + 16])
+
+
+def test_gemm_error_bound_covers_fp32_accumulation():
+    """The bound holds for an actual fp32 chunked accumulation of random
+    bf16 data (computed here with float32 NumPy arithmetic)."""
+    rng = np.random.default_rng(10)
+    a32 = rng.standard_normal((8, 256)).astype(np.float32)
+    b32 = rng.standard_normal((6, 256)).astype(np.float32)
+    a = (a32.view(np.uint32) >> 16).astype(np.uint16)
+    bt = (b32.view(np.uint32) >> 16).astype(np.uint16)
+    av, bv = O.bf16_to_f64(a).astype(np.float32), O.bf16_to_f64(bt).astype(np.float32)
+    acc = np.zeros((8, 6), dtype=np.float32)
+    for c0 in range(0, 256, 32):
+        acc = acc + (av[:, c0:c0 + 32] @ bv[:, c0:c0 + 32].T).astype(np.float32)
+    err = np.abs(acc.astype(np.float64) - O.gemm_bf16(a, bt))
+    assert np.all(err <= O.gemm_error_bound(a, bt))

@@ -30,6 +30,7 @@ EXPORTS = (
     "swz_transpose",
     "swz_convert_layout",
     "swz_stage_operand",
+    "swz_gemm_frag",
     "swz_choose",
     "swz_predict_conflicts",
     "swz_kernel_accesses",
@@ -107,6 +108,7 @@ def _load() -> ctypes.CDLL:
     lib.swz_transpose.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_convert_layout.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_stage_operand.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
+    lib.swz_gemm_frag.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
     lib.swz_choose.argtypes = [i32, i32, i32, i32, i32, P(Params)]
     lib.swz_predict_conflicts.argtypes = [i32, i32, P(Params), P(i64), P(i64)]
     lib.swz_kernel_accesses.argtypes = [i32, i32, P(Params), i32, P(i32), i32, P(i32), P(i32)]
@@ -187,6 +189,12 @@ def swz_stage_operand(src, frag, mn: int, k: int, elem_bytes: int = 2, frag_kind
                       layout="swizzle", params=None, stream=None) -> None:
     _check(lib.swz_stage_operand(_ptr(src), _ptr(frag), mn, k, elem_bytes, frag_kind, _layout(layout),
                                  _params(params), _stream(stream, src, frag)), "swz_stage_operand")
+
+
+def swz_gemm_frag(fa, fb, c, m: int, n: int, k: int, frag_kind: int = FRAG_MFMA_F32_16X16X32_BF16,
+                  stream=None) -> None:
+    _check(lib.swz_gemm_frag(_ptr(fa), _ptr(fb), _ptr(c), m, n, k, frag_kind, _stream(stream, fa, fb, c)),
+           "swz_gemm_frag")
 
 
 def swz_choose(elem_bytes: int, vec_bytes: int, tile_rows: int, tile_cols: int, read_kind: int) -> Tuple[int, int, int]:

@@ -24,6 +24,7 @@ SOURCES = [
     "chooser.cpp",
     "bank_model.cpp",
     "kernels_tile.hip",
+    "kernels_gemm.hip",
     "kernels_map.hip",
     "kernels_copy.hip",
     "lds_probe.hip",

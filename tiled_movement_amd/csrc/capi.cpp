@@ -65,7 +65,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     int kind = read_kind;
     if (op == 0) {
         if (esz != 2 && esz != 4) return SWZ_EINVAL;
-        if (kind == SWZ_READ_AUTO) kind = esz == 4 ? SWZ_READ_SCALAR_COL : (cols <= 128 ? SWZ_READ_B128_8X8 : SWZ_READ_B64_4X4);
+        if (kind == SWZ_READ_AUTO) kind = esz == 4 ? SWZ_READ_SCALAR_COL : (cols <= 128 ? SWZ_READ_B128_8X8 : SWZ_READ_B64_TR16);
         if (kind == SWZ_READ_MFMA_16X16X32) return SWZ_EINVAL;
     } else {
         if (esz != 2) return SWZ_EINVAL;
@@ -176,6 +176,24 @@ SWZ_API int swz_stage_operand(const void* d_src, void* d_frag, int64_t mn, int64
     if (overlaps(d_src, bytes, d_frag, bytes)) return SWZ_EINVAL;
     swz::StageJob job{d_src, d_frag, mn, k, layout_of(pl), layout == SWZ_LAYOUT_SWIZZLE_DIRECT};
     return hip_status(swz::launch_stage(job, static_cast<hipStream_t>(stream)));
+}
+
+SWZ_API int swz_gemm_frag(const void* d_fa, const void* d_fb, float* d_c, int64_t m, int64_t n, int64_t k,
+                          int32_t frag_kind, void* stream) {
+    if (m < 0 || n < 0 || k < 0 || m % 16 || n % 16 || k % 32) return SWZ_EINVAL;
+    if (frag_kind != SWZ_FRAG_MFMA_F32_16X16X32_BF16) return SWZ_EINVAL;
+    int64_t a_elems, b_elems, c_elems, a_bytes, b_bytes, c_bytes;
+    if (!mul_ok(m, k, &a_elems) || !mul_ok(n, k, &b_elems) || !mul_ok(m, n, &c_elems)) return SWZ_EINVAL;
+    if (!mul_ok(a_elems, 2, &a_bytes) || !mul_ok(b_elems, 2, &b_bytes) || !mul_ok(c_elems, 4, &c_bytes))
+        return SWZ_EINVAL;
+    if (m == 0 || n == 0) return SWZ_OK;
+    if (!d_c) return SWZ_EINVAL;
+    if (k > 0 && (!d_fa || !d_fb)) return SWZ_EINVAL;
+    const auto pa = reinterpret_cast<uintptr_t>(d_fa), pb = reinterpret_cast<uintptr_t>(d_fb),
+               pc = reinterpret_cast<uintptr_t>(d_c);
+    if (pa % 16 || pb % 16 || pc % 16) return SWZ_EINVAL;
+    if (k > 0 && (overlaps(d_c, c_bytes, d_fa, a_bytes) || overlaps(d_c, c_bytes, d_fb, b_bytes))) return SWZ_EINVAL;
+    return hip_status(swz::launch_gemm_frag(d_fa, d_fb, d_c, m, n, k, static_cast<hipStream_t>(stream)));
 }
 
 SWZ_API int swz_choose(int32_t elem_bytes, int32_t vec_bytes, int32_t tile_rows, int32_t tile_cols, int32_t read_kind,

@@ -24,7 +24,7 @@
 #define SWZ_NT_STAGE 256
 #endif
 #ifndef SWZ_NT_TR16
-#define SWZ_NT_TR16 128
+#define SWZ_NT_TR16 256
 #endif
 
 namespace swz {

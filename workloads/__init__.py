@@ -25,6 +25,7 @@ __all__ = [
     "bf16_tensor",
     "bf16_operands",
     "bf16_bits",
+    "index_pattern_device",
     "FULL",
 ]
 
@@ -85,3 +86,38 @@ def bf16_operands(m: int, n: int, k: int, seed: int = 0, std: float = 0.02):
     a = rng.standard_normal((m, k), dtype=np.float32) * np.float32(std)
     bt = rng.standard_normal((n, k), dtype=np.float32) * np.float32(std)
     return bf16_bits(a), bf16_bits(bt)
+
+
+def index_pattern_device(shape, device, elem_bytes: int = 4):
+    """A large input made on the GPU without a host copy: element
+    (i0, ..., in) of a C-contiguous tensor of `shape` holds
+    (7 * i0 + flat index inside the first dimension) mod 2^(8*elem_bytes - 1),
+    as int32 (elem_bytes 4) or int16 (elem_bytes 2).  Every value is
+    recomputable on the host from the element's coordinates, so sampled
+    outputs of very large calls can be checked without generating the whole
+    input twice.  No randomness: used where the input is too large for the
+    seeded host generators."""
+    import torch
+
+    first = shape[0]
+    inner = 1
+    for d in shape[1:]:
+        inner *= d
+    mask = (1 << (8 * elem_bytes - 1)) - 1
+    base = (torch.arange(first, dtype=torch.int64, device=device) * 7).view(first, 1)
+    flat = torch.arange(inner, dtype=torch.int64, device=device).view(1, inner)
+    out_dtype = torch.int32 if elem_bytes == 4 else torch.int16
+    out = torch.empty((first, inner), dtype=out_dtype, device=device)
+    step = max(1, (1 << 26) // max(inner, 1))  # bound the int64 temporaries
+    for b0 in range(0, first, step):
+        out[b0:b0 + step] = ((base[b0:b0 + step] + flat) & mask).to(out_dtype)
+    return out.view(*shape)
+
+
+def index_pattern_host(shape, index, elem_bytes: int = 4) -> np.ndarray:
+    """The values index_pattern_device puts at the given leading index
+    (a sub-array of shape[1:]), as uint32 / uint16 bits."""
+    inner = int(np.prod(shape[1:]))
+    mask = (1 << (8 * elem_bytes - 1)) - 1
+    v = (7 * int(index) + np.arange(inner, dtype=np.int64)) & mask
+    return v.astype(np.uint32 if elem_bytes == 4 else np.uint16).reshape(shape[1:])
