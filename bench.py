@@ -17,7 +17,7 @@ Usage:
   python bench.py --workload NAME --layout swizzle|pad|plain|direct [--steps K]
       time one workload only (used for profiler runs); NAME is one of
       fp32_transpose, fp16_transpose, fp16_transpose_tr, bf16_convert,
-      bf16_stage, map, copy, copy_128, memcpy_d2d
+      bf16_stage, map, copy, copy_128, memcpy_d2d, bf16_gemm, torch_mm_bf16
 """
 
 from __future__ import annotations
@@ -46,6 +46,7 @@ WORKLOADS = {
     "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
     "bf16_gemm": "C[8192x8192] fp32 = A * B^T from the staged fragments of A[8192x4096] and B[4096x8192] (16x16x32 bf16 MFMA)",
+    "torch_mm_bf16": "runtime library GEMM (torch.mm, bf16 in and out) of the same 8192x8192x4096 product, for context",
     "copy": "reference 16-byte vector copy of 64 MiB (read once, write once)",
     "copy_128": "reference 16-byte vector copy of 128 MiB (the byte count of the 256 MiB workloads)",
     "memcpy_d2d": "runtime device-to-device copy (hipMemcpyAsync through torch) of 64 MiB, for context",
@@ -226,6 +227,21 @@ def build(ctx, name, layout):
         info["_keep"] = (fa, fb, c)
         return step, 2 * m * n * k, info
 
+    if name == "torch_mm_bf16":
+        m = n = 8192
+        k = 4096
+        ao, bo = W.bf16_operands(m, n, k, seed=0)
+        a = ctx.copies(ao, 1)[0].view(ctx.torch.bfloat16)
+        b = ctx.copies(bo, 1)[0].view(ctx.torch.bfloat16).t().contiguous()  # B [k][n]
+        out = ctx.torch.empty((m, n), dtype=ctx.torch.bfloat16, device=ctx.dev)
+
+        def step(i):
+            ctx.torch.mm(a, b, out=out)
+
+        info.update({"m": m, "n": n, "k": k})
+        info["_keep"] = (a, b, out)
+        return step, 2 * m * n * k, info
+
     if name == "map":
         x = ctx.torch.arange(65536, dtype=ctx.torch.int32, device=ctx.dev)
         y = ctx.torch.empty_like(x)
@@ -331,8 +347,8 @@ def main(argv=None):
     extra = {}
     if not args.quick and args.workload is None:
         for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "fp16_transpose_tr",
-                      "bf16_convert", "bf16_stage", "map", "bf16_gemm"):
-            for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map", "bf16_gemm")
+                      "bf16_convert", "bf16_stage", "map", "bf16_gemm", "torch_mm_bf16"):
+            for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map", "bf16_gemm", "torch_mm_bf16")
                         else ("swizzle", "pad", "plain", "direct")):
                 s2, nb2, inf2 = build(ctx, wname, lay)
                 if wname == "map":
@@ -340,13 +356,14 @@ def main(argv=None):
                     extra["map/swizzle"] = {"us_per_call": round(ms2 * 1e3, 3)}
                     log(f"map: {ms2 * 1e3:.2f} us/call")
                     continue
-                if wname == "bf16_gemm":
+                if wname in ("bf16_gemm", "torch_mm_bf16"):
                     rate, ms2 = median_rate(s2, nb2, steps=20, warmup=5)
                     tflops = rate / 1e3  # nb2 counts flops, so rate is GFLOP/s
-                    extra["bf16_gemm"] = {"TFLOPs": round(tflops, 1), "frac_of_mfma_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                                          "us_per_step": round(ms2 * 1e3, 1), "m": 8192, "n": 8192, "k": 4096}
-                    log(f"bf16_gemm: {tflops:.1f} TFLOP/s")
+                    extra[wname] = {"TFLOPs": round(tflops, 1), "frac_of_mfma_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                                    "us_per_step": round(ms2 * 1e3, 1), "m": 8192, "n": 8192, "k": 4096}
+                    log(f"{wname}: {tflops:.1f} TFLOP/s")
                     del s2, inf2
+                    ctx.torch.cuda.empty_cache()
                     continue
                 rate, ms2 = median_rate(s2, nb2)
                 rec = {k: v for k, v in inf2.items() if not k.startswith("_") and k != "workload"}
@@ -395,7 +412,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "extra": extra,
     }
-    if name == "bf16_gemm":  # a contraction: flops, against the bf16 matrix peak
+    if name in ("bf16_gemm", "torch_mm_bf16"):  # a contraction: flops, against the bf16 matrix peak
         tflops = value / 1e3
         line.update({"metric": "bf16 GEMM from staged fragments, TFLOP/s", "value": round(tflops, 1),
                      "unit": "TFLOP/s", "dtype": "bf16"})

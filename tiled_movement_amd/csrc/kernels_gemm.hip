@@ -13,10 +13,13 @@
 // did the reordering.
 //
 // Workgroup tile of (waves along m x WB_M) x (waves along n x WB_N) blocks of
-// 16 x 16 (the defaults: 256 x 256 of C, four waves in 2 x 2, each wave
-// 128 x 128 = 8 x 8 blocks, 256 fp32 accumulators per lane).  The k loop
-// moves STAGE_STEPS 32-wide steps per stage; stages are double-buffered in
-// LDS: the loads of stage s+1 are in flight while stage s is multiplied.
+// 16 x 16.  The defaults, from a sweep on MI355X at 8192 x 8192 x 4096: a
+// 256 x 256 tile of C, eight waves in 4 x 2, each wave 64 x 128 = 4 x 8
+// blocks (128 fp32 accumulators per lane, two waves per SIMD); one 32-wide k
+// step per stage, two stage buffers (64 KiB of LDS): the loads of stage s+1
+// are in flight while stage s is multiplied.  Larger wave tiles spill
+// registers (8 x 8 blocks with two k steps per stage ran at half the rate),
+// and deeper pipelines (three or four buffers) did not help.
 #include "launch.h"
 
 namespace swz {
@@ -27,19 +30,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 #ifndef SWZ_GEMM_WAVES_M  // waves along m / n; each wave owns WB_M x WB_N blocks of 16 x 16
-#define SWZ_GEMM_WAVES_M 2
+#define SWZ_GEMM_WAVES_M 4
 #endif
 #ifndef SWZ_GEMM_WAVES_N
 #define SWZ_GEMM_WAVES_N 2
 #endif
 #ifndef SWZ_GEMM_WB_M
-#define SWZ_GEMM_WB_M 8
+#define SWZ_GEMM_WB_M 4
 #endif
 #ifndef SWZ_GEMM_WB_N
 #define SWZ_GEMM_WB_N 8
 #endif
 #ifndef SWZ_GEMM_STAGE_STEPS  // 32-wide k steps per LDS stage
-#define SWZ_GEMM_STAGE_STEPS 2
+#define SWZ_GEMM_STAGE_STEPS 1
+#endif
+#ifndef SWZ_GEMM_XCD  // 1: give each of the 8 XCDs (own L2) a contiguous run of tiles
+#define SWZ_GEMM_XCD 0
+#endif
+#ifndef SWZ_GEMM_BUFS  // LDS stage buffers (2 to 4): up to BUFS - 1 stages of loads in flight
+#define SWZ_GEMM_BUFS 2
 #endif
 
 constexpr int kWavesM = SWZ_GEMM_WAVES_M, kWavesN = SWZ_GEMM_WAVES_N;
@@ -52,7 +61,31 @@ constexpr int kFragBytes = 64 * 16;                              // one fragment
 constexpr int kStageFragsA = kTileM * kStageSteps, kStageFragsB = kTileN * kStageSteps;
 constexpr int kBufBytes = (kStageFragsA + kStageFragsB) * kFragBytes;  // A and B of one stage
 static_assert((kStageFragsA + kStageFragsB) % kWaves == 0, "stage loads split over the waves");
-static_assert(2 * kBufBytes <= 160 * 1024, "two stages fit in LDS");
+constexpr int kBufs = SWZ_GEMM_BUFS;
+constexpr int kPerWave = (kStageFragsA + kStageFragsB) / kWaves;  // direct loads per wave per stage
+static_assert(kBufs >= 2 && kBufs <= 4, "two to four stage buffers");
+static_assert(kBufs * kBufBytes <= 160 * 1024, "the stage buffers fit in LDS");
+static_assert((kBufs - 2) * kPerWave <= 63, "the load counter holds the loads left in flight");
+
+// Wait until at most `later` stages' loads of this wave are still in flight
+// (the counter retires loads in issue order).
+__device__ __forceinline__ void wait_stages(int later) {
+    if (later <= 0)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPerWave) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPerWave) : "memory");
+}
+
+// Workgroup barrier without the memory fence __syncthreads adds: the fence
+// would wait for every direct load in flight, including the later stages
+// the pipeline keeps going; each wave has already waited for what it needs.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 constexpr int64_t kMaxGridY = 65535;
 
 // Issue this wave's share of stage s's direct loads into LDS buffer buf.
@@ -63,7 +96,6 @@ constexpr int64_t kMaxGridY = 65535;
 __device__ __forceinline__ void load_stage(const uint8_t* __restrict__ fa, const uint8_t* __restrict__ fb,
                                            int64_t bm0, int64_t bn0, int64_t mb, int64_t nb, int64_t kb, int64_t s,
                                            lds_u8* buf, int wave, int lane) {
-    constexpr int kPerWave = (kStageFragsA + kStageFragsB) / kWaves;
 #pragma unroll
     for (int q = 0; q < kPerWave; ++q) {
         const int f = wave * kPerWave + q;
@@ -83,13 +115,34 @@ __device__ __forceinline__ void load_stage(const uint8_t* __restrict__ fa, const
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __restrict__ fa,
                                                              const uint8_t* __restrict__ fb, float* __restrict__ c,
                                                              int64_t m, int64_t n, int64_t k, int64_t tile_row0) {
-    __shared__ bf16x8 lds_v[2 * kBufBytes / 16];
+    __shared__ bf16x8 lds_v[kBufs * kBufBytes / 16];
     lds_u8* lds = (lds_u8*)(reinterpret_cast<uint8_t*>(lds_v));
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / 64);
     const int lane = threadIdx.x % 64;
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int64_t mb = m / 16, nb = n / 16, kb = k / 32;
-    const int64_t bm0 = (tile_row0 + blockIdx.y) * kTileM, bn0 = static_cast<int64_t>(blockIdx.x) * kTileN;
+    int64_t ty = blockIdx.y, tx = blockIdx.x;
+    if (SWZ_GEMM_XCD == 1) {
+        // Workgroups are handed to the 8 XCDs in turn; renumber so that the
+        // ones on one XCD cover neighbouring tiles and share operand blocks
+        // in that XCD's L2.
+        const uint32_t nt = gridDim.x * gridDim.y, id = blockIdx.y * gridDim.x + blockIdx.x;
+        if (nt % 8 == 0) {
+            const uint32_t t = (id % 8) * (nt / 8) + id / 8;
+            ty = t / gridDim.x;
+            tx = t % gridDim.x;
+        }
+    } else if (SWZ_GEMM_XCD == 2) {
+        // The same, in 4 x 8 groups of tiles: the workgroups one XCD runs at
+        // a time (one per CU) share 4 bands of A and 8 of B.
+        const uint32_t gx = gridDim.x, gy = gridDim.y, id = blockIdx.y * gx + blockIdx.x;
+        if (gx % 8 == 0 && gy % 4 == 0 && (gx / 8) * (gy / 4) % 8 == 0) {
+            const uint32_t j = id / 8, sb = id % 8 + 8 * (j / 32), w = j % 32;
+            ty = 4 * (sb / (gx / 8)) + w / 8;
+            tx = 8 * (sb % (gx / 8)) + w % 8;
+        }
+    }
+    const int64_t bm0 = (tile_row0 + ty) * kTileM, bn0 = tx * kTileN;
     const int64_t stages = (kb + kStageSteps - 1) / kStageSteps;
 
     f32x4 acc[kWbM][kWbN];
@@ -98,13 +151,22 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __res
 #pragma unroll
         for (int y = 0; y < kWbN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (stages > 0) load_stage(fa, fb, bm0, bn0, mb, nb, kb, 0, lds, wave, lane);  // k = 0: C = 0
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // Prologue: stages 0 .. kBufs-2 in flight (k = 0 issues nothing: C = 0).
+#pragma unroll
+    for (int p = 0; p < kBufs - 1; ++p)
+        if (p < stages) load_stage(fa, fb, bm0, bn0, mb, nb, kb, p, lds + p * kBufBytes, wave, lane);
 
     for (int64_t s = 0; s < stages; ++s) {
-        lds_u8* cur = lds + (s & 1) * kBufBytes;
-        if (s + 1 < stages) load_stage(fa, fb, bm0, bn0, mb, nb, kb, s + 1, lds + ((s + 1) & 1) * kBufBytes, wave, lane);
+        // Stage s has landed once only the later stages' loads are pending;
+        // the barrier then also says every wave is done with stage s - 1,
+        // whose buffer the next loads reuse.
+        const int64_t later = stages - 1 - s < kBufs - 2 ? stages - 1 - s : kBufs - 2;
+        wait_stages(static_cast<int>(later));
+        stage_barrier();
+        if (s + kBufs - 1 < stages)
+            load_stage(fa, fb, bm0, bn0, mb, nb, kb, s + kBufs - 1, lds + ((s + kBufs - 1) % kBufs) * kBufBytes, wave,
+                       lane);
+        lds_u8* cur = lds + (s % kBufs) * kBufBytes;
 #pragma unroll
         for (int ks = 0; ks < kStageSteps; ++ks) {
             if (s * kStageSteps + ks >= kb) break;  // uniform: a k tail of one step
@@ -121,23 +183,38 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __res
                 for (int y = 0; y < kWbN; ++y)
                     acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
     }
 
     // Lane l holds rows 4*(l/16) .. +3 of column l%16 of each 16 x 16 block.
+    // Each wave turns its accumulators into whole rows through its own slice
+    // of the (now idle) stage buffers, one row of blocks at a time: 16 rows
+    // of WB_N * 16 floats, stored 16 bytes per lane, so every store
+    // instruction writes whole 64-byte runs of C rows.
+    stage_barrier();  // every wave is done reading the last stage
+    constexpr int kRowFloats = kWbN * 16;
+    static_assert(kWaves * 16 * kRowFloats * 4 <= kBufs * kBufBytes, "the epilogue slices fit in the stage buffers");
+    __attribute__((address_space(3))) float* slice = (__attribute__((address_space(3))) float*)(lds + wave * 16 * kRowFloats * 4);
     const int r4 = 4 * (lane / 16), col = lane % 16;
 #pragma unroll
     for (int x = 0; x < kWbM; ++x) {
         const int64_t bi = bm0 + wm * kWbM + x;
-        if (bi >= mb) continue;
 #pragma unroll
-        for (int y = 0; y < kWbN; ++y) {
-            const int64_t bj = bn0 + wn * kWbN + y;
-            if (bj >= nb) continue;
-            float* out = c + (16 * bi + r4) * n + 16 * bj + col;
+        for (int y = 0; y < kWbN; ++y)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(acc[x][y][i], out + i * n);
+            for (int i = 0; i < 4; ++i) slice[(r4 + i) * kRowFloats + 16 * y + col] = acc[x][y][i];
+        // A wave's LDS operations complete in order: its reads below see
+        // these writes, and the next row of blocks overwrites the slice only
+        // after these reads.
+        if (bi < mb) {
+            constexpr int kLanesPerRow = kRowFloats / 4;
+#pragma unroll
+            for (int q = 0; q < 16 * kLanesPerRow / 64; ++q) {
+                const int t = q * 64 + lane, r = t / kLanesPerRow, c4 = 4 * (t % kLanesPerRow);
+                const int64_t bj = bn0 + wn * kWbN + c4 / 16;
+                const f32x4 v = *(__attribute__((address_space(3))) f32x4*)(slice + r * kRowFloats + c4);
+                if (bj < nb)
+                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(c + (16 * bi + r) * n + 16 * (bn0 + wn * kWbN) + c4));
+            }
         }
     }
 }
