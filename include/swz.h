@@ -25,7 +25,10 @@ extern "C" {
  * into the B-bit field at bit M ("CuTe Swizzle 学习手册", section on the
  * swizzle formula; "CUDA 013 - Swizzle 的工作原理", section 计算公式, where
  * the same triple is written (base, bits, shift) = (M, B, S)).  M counts
- * elements: 2^M consecutive elements stay together. */
+ * elements: 2^M consecutive elements stay together.  A negative S moves the
+ * field the other way ("NVIDIA CuTe Swizzle", the SShift comment: a negative
+ * shift moves the mask to the left): the B-bit field at bit M is XORed into
+ * the field at bit M + |S|. */
 typedef struct swz_params {
     int32_t B;
     int32_t M;
@@ -50,7 +53,7 @@ enum swz_status {
  * consecutive LDS addresses, so the swizzle is applied on the HBM side
  * instead: the lane that fills LDS slot p fetches tile element swizzle(p),
  * which places every element exactly where SWIZZLE puts it (the swizzle is
- * its own inverse when S >= B).  It needs S >= B (or B = 0, plain rows), and
+ * its own inverse when |S| >= B).  It needs |S| >= B (or B = 0, plain rows), and
  * 16-byte aligned pointers and row pitches (SWZ_EUNSUPPORTED otherwise). */
 enum swz_layout {
     SWZ_LAYOUT_SWIZZLE = 0,
@@ -106,7 +109,9 @@ typedef struct swz_plan_info {
  * section 计算公式).
  *   d_in, d_out : device int32 arrays of n elements; may be the same
  *                 pointer (in place) but must not otherwise overlap.
- *   p           : B, M, S >= 0 and B + M + S <= 32; B = 0 is the identity.
+ *   p           : B, M >= 0, any S, and B + M + |S| <= 32; B = 0 is the
+ *                 identity (S = 0 with B > 0 clears the field, computed as
+ *                 written).
  * Errors: SWZ_EINVAL for n < 0, NULL with n > 0, partial overlap, or
  * parameters out of range. */
 int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p, void* stream);
@@ -126,8 +131,9 @@ int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p, void* 
  * Any rows, cols >= 0 are accepted (partial edge tiles are handled); 0 is a
  * no-op.  src and dst must not overlap; they must be aligned to elem_bytes.
  * Errors: SWZ_EINVAL (sizes, NULL, overlap, misalignment, a read kind that
- * does not fit elem_bytes, parameters that split a vector or leave the tile,
- * S < B with SWZ_LAYOUT_SWIZZLE_DIRECT); SWZ_EUNSUPPORTED for
+ * does not fit elem_bytes, parameters that split a vector or move bits
+ * outside the tile, S = 0 with B > 0 (not one-to-one), |S| < B with
+ * SWZ_LAYOUT_SWIZZLE_DIRECT); negative S is accepted; SWZ_EUNSUPPORTED for
  * SWZ_LAYOUT_SWIZZLE_DIRECT when a pointer or a row pitch (cols * elem_bytes
  * or rows * elem_bytes) is not a multiple of 16 bytes. */
 int swz_transpose(const void* d_src, void* d_dst, int64_t rows, int64_t cols, int32_t elem_bytes,
@@ -189,6 +195,25 @@ int swz_gemm_frag(const void* d_fa, const void* d_fb, float* d_c, int64_t m, int
  * accepted; others return SWZ_EUNSUPPORTED. */
 int swz_choose(int32_t elem_bytes, int32_t vec_bytes, int32_t tile_rows, int32_t tile_cols,
                int32_t read_kind, swz_params* out);
+
+/* Host only.  Folding a swizzle into a plain layout over a slice ("cutlass
+ * 入门", section swizzle 融入 layout 优化).  A slice is the set of offsets
+ * base | x with x ranging over the subsets of the bit mask `active` (the bits
+ * a slice's coordinates can change; base has none of them).  The page's test:
+ * collision = active & ~swizzle(active) marks every target bit whose source
+ * bit is also active; when it is zero the swizzle restricted to the slice is
+ * a plain (strided) layout:
+ *   swizzle(base | x) = swizzle(base) + sum over set bits b of x of strides[b].
+ *   p          : the swizzle (S of either sign; B + M + |S| <= 32).
+ *   *collision : the collision bits (always written).
+ *   *folded_base, strides[32] : swizzle(base) and the signed per-bit strides
+ *                (strides[b] = 0 for bits outside `active`), written only
+ *                when the slice folds; either may be NULL.
+ * Returns SWZ_OK when the slice folds, SWZ_EUNSUPPORTED when it does not
+ * (collision != 0), SWZ_EINVAL for bad parameters, base & active != 0 or a
+ * NULL collision pointer. */
+int swz_fold(const swz_params* p, uint32_t base, uint32_t active, uint32_t* collision, uint32_t* folded_base,
+             int64_t* strides);
 
 /* Host only.  Predicted conflict cycles (write + read, summed over one
  * tile) of the kernel pattern for read_kind under the built-in bank model,

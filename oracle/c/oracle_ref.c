@@ -18,9 +18,13 @@
 #include <stdint.h>
 #include <string.h>
 
+/* S >= 0: the field at M+S is XORed into the field at M; S < 0: the field
+ * at M is XORed into the field at M+|S| ("NVIDIA CuTe Swizzle", SShift). */
 uint32_t oref_swizzle(uint32_t x, int32_t B, int32_t M, int32_t S) {
-    uint32_t yy = (x >> (M + S)) & ((1u << B) - 1u);
-    return x ^ (yy << M);
+    int32_t src = S >= 0 ? M + S : M;
+    int32_t dst = S >= 0 ? M : M - S;
+    uint32_t yy = (x >> src) & ((1u << B) - 1u);
+    return x ^ (yy << dst);
 }
 
 void oref_swizzle_map(const int32_t* in, int32_t* out, int64_t n, int32_t B, int32_t M, int32_t S) {

@@ -54,8 +54,8 @@ def _ptr(a):
 
 def swizzle_map(x, B, M, S):
     """out[i] = Swizzle<B,M,S>(x[i]) on uint32 bit patterns ("CuTe Swizzle 学习手册", swizzle formula)."""
-    if min(B, M, S) < 0 or B + M + S > 31:
-        raise ValueError("need B, M, S >= 0 and B + M + S <= 31")
+    if min(B, M) < 0 or B + M + abs(S) > 31:
+        raise ValueError("need B, M >= 0 and B + M + |S| <= 31")
     x = np.ascontiguousarray(x, dtype=np.int32)
     out = np.empty_like(x)
     lib().oref_swizzle_map(_ptr(x), _ptr(out), x.size, B, M, S)

@@ -37,7 +37,10 @@ import numpy as np
 __all__ = [
     "swizzle",
     "swizzle_clear_set",
+    "swizzle_signed",
     "swizzle_map",
+    "fold_collision",
+    "fold_strides",
     "tile_offset",
     "transpose",
     "convert_layout",
@@ -98,12 +101,61 @@ def swizzle_clear_set(offset, base: int, bits: int, shift: int):
     return cleared | ((zz ^ yy) << base)
 
 
+def swizzle_signed(x, B: int, M: int, S: int):
+    """Swizzle<B,M,S> for a shift of either sign.
+
+    [CuTe-DSL] (the SShift comment of its bit diagram): the shift says how
+    far the YYY mask sits from the ZZZ mask that keeps MBase low bits
+    constant; a positive shift puts YYY above ZZZ (the XOR moves YYY right,
+    onto ZZZ), a negative shift puts it below (the XOR moves YYY left).  So
+    for S >= 0 the source field is bits [M+S, M+S+B) and the target [M, M+B);
+    for S < 0 the source is [M, M+B) and the target [M+|S|, M+|S|+B).  The
+    target becomes target XOR source; all other bits pass through.  Scalar
+    ints or NumPy integer arrays (taken as uint32).
+    """
+    if B < 0 or M < 0:
+        raise ValueError("B and M must be non-negative")
+    src_lo = M + max(S, 0)
+    dst_lo = M + max(-S, 0)
+    mask = (1 << B) - 1
+    if isinstance(x, (int, np.integer)):
+        x = int(x) & 0xFFFFFFFF
+        return (x ^ (((x >> src_lo) & mask) << dst_lo)) & 0xFFFFFFFF
+    u = np.asarray(x).astype(np.int64) & 0xFFFFFFFF
+    return ((u ^ (((u >> src_lo) & mask) << dst_lo)) & 0xFFFFFFFF).astype(np.uint32)
+
+
 def swizzle_map(offsets: np.ndarray, B: int, M: int, S: int) -> np.ndarray:
-    """Elementwise swizzle of int32 offsets, output int32 (same bit pattern)."""
+    """Elementwise swizzle of int32 offsets, output int32 (same bit pattern);
+    S may be negative (``swizzle_signed``)."""
     a = np.asarray(offsets)
     if a.dtype != np.int32:
         raise TypeError("swizzle_map takes int32 offsets")
+    if S < 0:
+        return swizzle_signed(a.view(np.uint32), B, M, S).view(np.int32)
     return swizzle(a.view(np.uint32), B, M, S).view(np.int32)
+
+
+def fold_collision(active: int, B: int, M: int, S: int) -> int:
+    """[Intro] §swizzle 融入 layout 优化: with A the OR of every offset a
+    slice can reach (its active bits), collision = A & ~sw(A) has a one at
+    each target bit whose source bit is also active; the slice folds into a
+    plain layout exactly when it is zero."""
+    a = int(active) & 0xFFFFFFFF
+    return a & ~swizzle_signed(a, B, M, S) & 0xFFFFFFFF
+
+
+def fold_strides(base: int, active: int, B: int, M: int, S: int):
+    """The folded layout of a collision-free slice: (sw(base), {bit: stride})
+    with sw(base | x) = sw(base) + sum of the strides of x's bits.  Each
+    stride is the signed change of sw(base) when that one active bit is set
+    (computed directly from the map, one bit at a time)."""
+    sb = swizzle_signed(base, B, M, S)
+    out = {}
+    for b in range(32):
+        if (active >> b) & 1:
+            out[b] = int(swizzle_signed(base | (1 << b), B, M, S)) - int(sb)
+    return int(sb), out
 
 
 # --------------------------------------------------------------------------

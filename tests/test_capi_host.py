@@ -350,3 +350,59 @@ def test_gemm_validation():
     assert f(A, B, C, -16, 32, 32, 0, None) == EINVAL
     assert f(A, B, C, 0, 32, 32, 0, None) == T.SWZ_OK  # empty: no launch
     assert f(A, B, C, 1 << 40, 1 << 40, 32, 0, None) == EINVAL  # size overflow
+
+
+
+def test_negative_shift_validation():
+    assert lib.swz_map(A, B, 16, P(5, 20, -8), None) == EINVAL  # fields leave 32 bits
+    f = lib.swz_convert_layout
+    # the changed field [M+|S|, M+|S|+B) = [3+6, 13) leaves the 64x64 tile (12 bits)
+    assert f(A, B, 1, 64, 64, 2, 0, T.READ_B64_4X4, ctypes.byref(P(4, 3, -6)), None) == EINVAL
+    # |S| < B cannot be placed by the direct fill
+    assert f(A, B, 1, 64, 64, 2, T.LAYOUT_SWIZZLE_DIRECT, T.READ_B64_4X4, ctypes.byref(P(3, 3, -2)), None) == EINVAL
+    p = T.swz_plan(0, 64, 64, 2, "swizzle", T.READ_B64_4X4, (3, 3, -4))
+    assert p["params"] == (3, 3, -4)
+    w, r = T.swz_predict_conflicts(T.READ_B64_4X4, "swizzle", (3, 3, -4))
+    assert w >= 0 and r >= 0
+
+
+@pytest.mark.parametrize("kind", list(KIND_GEOM))
+def test_kernel_accesses_negative_shift(kind):
+    esz, tr, tc, pad = KIND_GEOM[kind]
+    params = (3, 0, -4) if esz == 4 else (3, 3, -4)
+    for write in (1, 0):
+        lib_acc = T.swz_kernel_accesses(kind, "swizzle", params, write)
+        mine = restated_accesses(kind, write)
+        for (addrs, width), (coords, w2) in zip(lib_acc, mine):
+            expect = [esz * int(O.swizzle_signed(a // esz, *params)) for a in
+                      O.access_addresses(coords, width // esz, tc, esz, "plain", (0, 0, 0), 0)]
+            assert addrs == expect
+
+
+def test_fold_matches_oracle():
+    rng = np.random.default_rng(22)
+    for _ in range(500):
+        B = int(rng.integers(1, 6))
+        M = int(rng.integers(0, 6))
+        S = int(rng.choice([-1, 1])) * int(rng.integers(1, 9))
+        active = int(rng.integers(0, 1 << 20))
+        base = int(rng.integers(0, 1 << 24)) & ~active
+        coll, fb, strides = T.swz_fold((B, M, S), base, active)
+        assert coll == O.fold_collision(active, B, M, S)
+        if coll == 0:
+            ob, ostr = O.fold_strides(base, active, B, M, S)
+            assert fb == ob and strides == ostr
+        else:
+            assert fb is None
+
+
+def test_fold_validation():
+    c = ctypes.c_uint32()
+    assert lib.swz_fold(ctypes.byref(P(3, 0, 3)), 1, 1, ctypes.byref(c), None, None) == EINVAL  # base & active
+    assert lib.swz_fold(ctypes.byref(P(3, 20, 12)), 0, 1, ctypes.byref(c), None, None) == EINVAL
+    assert lib.swz_fold(ctypes.byref(P(3, 0, 3)), 0, 1, None, None, None) == EINVAL
+    # the 32x32 fp32 tile's (5,0,5) over a whole tile collides; over one row it folds
+    assert T.swz_fold((5, 0, 5), 0, 1023)[1] is None
+    coll, fb, strides = T.swz_fold((5, 0, 5), 7 * 32, 31)  # row 7: column bits only
+    assert coll == 0 and fb == 7 * 32 + 7
+    assert strides == {b: (-(1 << b) if (7 >> b) & 1 else (1 << b)) for b in range(5)}

@@ -77,6 +77,18 @@ def test_map_worked_example_and_edges():
     T.swz_map(zin, zout, 0, (5, 0, 5))  # n = 0 is a no-op
 
 
+def test_map_negative_shifts():
+    announce("map negative shifts")
+    rng = np.random.default_rng(13)
+    z = rng.integers(-(2**31), 2**31, size=4099, dtype=np.int64).astype(np.int32)
+    zin = to_dev(z)
+    zout = torch.empty_like(zin)
+    for p in [(3, 0, -3), (5, 0, -5), (4, 3, -7), (2, 1, -1), (8, 8, -16), (1, 0, -31)]:
+        T.swz_map(zin, zout, z.size, p)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(zout, z), O.swizzle_map(z, *p)), p
+
+
 # ----------------------------------------------------------- transposes
 
 KINDS = [
@@ -147,6 +159,22 @@ def test_transpose_any_valid_swizzle(kind, esz, tr, tc, gen):
     for idx in rng.choice(len(triples), size=min(12, len(triples)), replace=False):
         announce("params", kind, triples[idx])
         check_transpose(a, esz, "swizzle", kind, triples[idx])
+
+
+@pytest.mark.parametrize("kind,esz,tr,tc,gen", KINDS)
+def test_transpose_negative_shifts(kind, esz, tr, tc, gen):
+    """Negative shifts XOR a low field into a higher one; the data still only
+    moves inside LDS, so the transpose is unchanged."""
+    rows, cols = 2 * tr + 8, 2 * tc + 8
+    a = gen(rows, cols, seed=24)
+    m0 = 0 if esz == 4 else 3
+    log_tile = (tr * tc).bit_length() - 1
+    for B, M, S in [(3, m0, -3), (2, m0, -5), (3, m0 + 1, -4), (1, m0, -1)]:
+        if M - S + B > log_tile:
+            continue
+        for layout in ("swizzle", "direct") if -S >= B else ("swizzle",):
+            announce("negative shift", kind, layout, (B, M, S))
+            check_transpose(a, esz, layout, kind, (B, M, S))
 
 
 def test_convert_layout_batches():

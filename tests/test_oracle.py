@@ -411,3 +411,90 @@ def test_gemm_error_bound_covers_fp32_accumulation():
         acc = acc + (av[:, c0:c0 + 32] @ bv[:, c0:c0 + 32].T).astype(np.float32)
     err = np.abs(acc.astype(np.float64) - O.gemm_bf16(a, bt))
     assert np.all(err <= O.gemm_error_bound(a, bt))
+
+
+# ------------------------------------------------------ negative shifts
+
+
+def _parity(v):
+    return bin(int(v)).count("1") & 1
+
+
+@pytest.mark.parametrize("B,M,S", [(3, 0, 3), (3, 3, 4), (2, 5, 7), (5, 0, 5), (4, 2, 1), (1, 9, 11)])
+def test_negative_shift_is_the_transpose_of_the_positive_one(B, M, S):
+    """Over GF(2) the swizzle is I + N, where N copies the source field onto
+    the target; reversing the shift swaps source and target, i.e. replaces N
+    by its transpose.  So <sw(x; -S), y> = <x, sw(y; S)> for the bitwise dot
+    product -- a fact about the maps, not a restatement of the formula."""
+    rng = np.random.default_rng(B * 100 + M * 10 + S)
+    for x, y in rng.integers(0, 2 ** 31, size=(300, 2)):
+        lhs = _parity(O.swizzle_signed(int(x), B, M, -S) & int(y))
+        rhs = _parity(int(x) & O.swizzle_signed(int(y), B, M, S))
+        assert lhs == rhs
+
+
+def test_negative_shift_moves_the_low_field_left():
+    """The SShift comment: a negative shift moves the YYY mask left.  With
+    only the low field (at M) set, the result also carries it |S| higher."""
+    for B, M, S in [(3, 4, -6), (2, 3, -11), (5, 0, -5)]:
+        low = ((1 << B) - 1) << M
+        assert O.swizzle_signed(low, B, M, S) == low | (low << -S)
+        high = low << -S
+        assert O.swizzle_signed(high, B, M, S) == high  # the target alone is left alone
+
+
+def test_signed_form_agrees_with_the_positive_form():
+    rng = np.random.default_rng(3)
+    x = rng.integers(0, 2 ** 31, size=500)
+    for B, M, S in [(3, 3, 3), (5, 0, 6), (2, 4, 1)]:
+        assert np.array_equal(O.swizzle_signed(x, B, M, S), O.swizzle(x, B, M, S))
+
+
+@pytest.mark.parametrize("B,M,S", [(3, 0, -3), (4, 3, -5), (2, 1, -1), (5, 0, -2)])
+def test_negative_shift_bijective_and_involutive_when_fields_apart(B, M, S):
+    x = np.arange(1 << 14, dtype=np.int64)
+    y = O.swizzle_signed(x, B, M, S).astype(np.int64)
+    assert np.array_equal(np.sort(y), x)  # one-to-one
+    if -S >= B:
+        assert np.array_equal(O.swizzle_signed(y, B, M, S).astype(np.int64), x)
+
+
+# ---------------------------------------------- folding into a plain layout
+
+
+def test_fold_collision_truth_table():
+    """[Intro] swizzle 融入 layout 优化: for one source/target bit pair, the
+    collision bit is set only when both are active (the page's table)."""
+    B, M, S = 1, 2, 3  # target bit 2, source bit 5
+    for a_z in (0, 1):
+        for a_y in (0, 1):
+            active = (a_z << 2) | (a_y << 5)
+            assert O.fold_collision(active, B, M, S) == (a_z & a_y) << 2
+
+
+def _subsets(mask):
+    bits = [b for b in range(32) if (mask >> b) & 1]
+    for r in range(1 << len(bits)):
+        yield sum(1 << bits[i] for i in range(len(bits)) if (r >> i) & 1)
+
+
+def test_fold_matches_brute_force_additivity():
+    """Brute force over every offset of small slices: the swizzle is a plain
+    (additive) layout on the slice exactly when there is no collision, and
+    then the folded strides reproduce every offset."""
+    rng = np.random.default_rng(21)
+    seen = {True: 0, False: 0}
+    for _ in range(300):
+        B = int(rng.integers(1, 4))
+        M = int(rng.integers(0, 4))
+        S = int(rng.choice([-1, 1])) * int(rng.integers(1, 6))
+        bits = rng.choice(12, size=int(rng.integers(1, 7)), replace=False)
+        active = sum(1 << int(b) for b in bits)
+        base = int(rng.integers(0, 1 << 12)) & ~active
+        coll = O.fold_collision(active, B, M, S)
+        sb, strides = O.fold_strides(base, active, B, M, S)
+        additive = all(int(O.swizzle_signed(base | x, B, M, S)) ==
+                       sb + sum(strides[b] for b in strides if (x >> b) & 1) for x in _subsets(active))
+        assert additive == (coll == 0), (B, M, S, active, base)
+        seen[coll == 0] += 1
+    assert seen[True] > 20 and seen[False] > 20

@@ -88,3 +88,13 @@ def test_stage_operand_lane_contents():
 def test_stage_operand_rejects_partial_fragments():
     with pytest.raises(ValueError):
         C.stage_operand(np.zeros((24, 32), np.uint16))
+
+
+def test_negative_shift_matches_python_oracle_and_adjoint():
+    import oracle as O
+
+    rng = np.random.default_rng(12)
+    x = rng.integers(0, 2 ** 31, size=2000).astype(np.int32)
+    for B, M, S in [(3, 0, -3), (4, 3, -5), (2, 1, -1), (5, 2, -7)]:
+        got = C.swizzle_map(x, B, M, S).view(np.uint32)
+        assert np.array_equal(got, O.swizzle_signed(x.view(np.uint32), B, M, S))

@@ -31,6 +31,7 @@ EXPORTS = (
     "swz_convert_layout",
     "swz_stage_operand",
     "swz_gemm_frag",
+    "swz_fold",
     "swz_choose",
     "swz_predict_conflicts",
     "swz_kernel_accesses",
@@ -109,6 +110,8 @@ def _load() -> ctypes.CDLL:
     lib.swz_convert_layout.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_stage_operand.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_gemm_frag.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.swz_fold.argtypes = [P(Params), ctypes.c_uint32, ctypes.c_uint32, P(ctypes.c_uint32), P(ctypes.c_uint32),
+                             P(i64)]
     lib.swz_choose.argtypes = [i32, i32, i32, i32, i32, P(Params)]
     lib.swz_predict_conflicts.argtypes = [i32, i32, P(Params), P(i64), P(i64)]
     lib.swz_kernel_accesses.argtypes = [i32, i32, P(Params), i32, P(i32), i32, P(i32), P(i32)]
@@ -195,6 +198,17 @@ def swz_gemm_frag(fa, fb, c, m: int, n: int, k: int, frag_kind: int = FRAG_MFMA_
                   stream=None) -> None:
     _check(lib.swz_gemm_frag(_ptr(fa), _ptr(fb), _ptr(c), m, n, k, frag_kind, _stream(stream, fa, fb, c)),
            "swz_gemm_frag")
+
+
+def swz_fold(params, base: int, active: int):
+    """(collision, folded_base or None, strides dict {bit: stride} or None)."""
+    c, fb = ctypes.c_uint32(), ctypes.c_uint32()
+    st = (ctypes.c_int64 * 32)()
+    rc = lib.swz_fold(ctypes.byref(Params(*params)), base, active, ctypes.byref(c), ctypes.byref(fb), st)
+    if rc == SWZ_EUNSUPPORTED:
+        return c.value, None, None
+    _check(rc, "swz_fold")
+    return c.value, fb.value, {b: st[b] for b in range(32) if (active >> b) & 1}
 
 
 def swz_choose(elem_bytes: int, vec_bytes: int, tile_rows: int, tile_cols: int, read_kind: int) -> Tuple[int, int, int]:

@@ -45,7 +45,8 @@ int resolve_layout(int kind, int32_t layout, const swz_params* p, swz_params* q,
         case SWZ_LAYOUT_SWIZZLE_DIRECT:
             if (p) {
                 if (!swz::params_ok_for_kind(kind, *p)) return SWZ_EINVAL;
-                if (layout == SWZ_LAYOUT_SWIZZLE_DIRECT && p->B > 0 && p->S < p->B) return SWZ_EINVAL;
+                if (layout == SWZ_LAYOUT_SWIZZLE_DIRECT && p->B > 0 && (p->S < 0 ? -p->S : p->S) < p->B)
+                    return SWZ_EINVAL;  // only |S| >= B makes the swizzle its own inverse
                 *q = *p;
             } else {
                 *q = swz::cached_choice(kind);
@@ -98,7 +99,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
 
 swz::LdsLayout layout_of(const swz_plan_info& pl) {
     return swz::LdsLayout{static_cast<uint32_t>(pl.tile_cols + pl.pad_elems), static_cast<uint32_t>(pl.params.B),
-                          static_cast<uint32_t>(pl.params.M), static_cast<uint32_t>(pl.params.S)};
+                          static_cast<uint32_t>(pl.params.M), pl.params.S};
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SWZ_OK : SWZ_EHIP; }
@@ -117,7 +118,8 @@ SWZ_API const char* swz_strerror(int status) {
 
 SWZ_API int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p, void* stream) {
     if (n < 0) return SWZ_EINVAL;
-    if (p.B < 0 || p.M < 0 || p.S < 0 || static_cast<int64_t>(p.B) + p.M + p.S > 32) return SWZ_EINVAL;
+    const int64_t abs_s = p.S < 0 ? -static_cast<int64_t>(p.S) : p.S;
+    if (p.B < 0 || p.M < 0 || static_cast<int64_t>(p.B) + p.M + abs_s > 32) return SWZ_EINVAL;
     if (n == 0) return SWZ_OK;
     if (!d_in || !d_out) return SWZ_EINVAL;
     if (reinterpret_cast<uintptr_t>(d_in) % 4 || reinterpret_cast<uintptr_t>(d_out) % 4) return SWZ_EINVAL;
@@ -194,6 +196,35 @@ SWZ_API int swz_gemm_frag(const void* d_fa, const void* d_fb, float* d_c, int64_
     if (pa % 16 || pb % 16 || pc % 16) return SWZ_EINVAL;
     if (k > 0 && (overlaps(d_c, c_bytes, d_fa, a_bytes) || overlaps(d_c, c_bytes, d_fb, b_bytes))) return SWZ_EINVAL;
     return hip_status(swz::launch_gemm_frag(d_fa, d_fb, d_c, m, n, k, static_cast<hipStream_t>(stream)));
+}
+
+SWZ_API int swz_fold(const swz_params* p, uint32_t base, uint32_t active, uint32_t* collision,
+                     uint32_t* folded_base, int64_t* strides) {
+    if (!p || !collision) return SWZ_EINVAL;
+    const int64_t abs_s = p->S < 0 ? -static_cast<int64_t>(p->S) : p->S;
+    if (p->B < 0 || p->M < 0 || p->B + p->M + abs_s > 32) return SWZ_EINVAL;
+    if (base & active) return SWZ_EINVAL;
+    const auto B = static_cast<uint32_t>(p->B), M = static_cast<uint32_t>(p->M);
+    *collision = active & ~swz::swizzle(active, B, M, p->S);
+    if (*collision) return SWZ_EUNSUPPORTED;
+    const uint32_t sb = swz::swizzle(base, B, M, p->S);
+    if (folded_base) *folded_base = sb;
+    if (strides) {
+        for (int b = 0; b < 32; ++b) {
+            strides[b] = 0;
+            if (!((active >> b) & 1u)) continue;
+            // Flipping bit b flips the bits of swizzle(1 << b) in swizzle(base):
+            // each flip adds its power of two where that bit was clear and
+            // subtracts it where it was set.  Without collisions the bits
+            // flipped by different active bits never meet, so the moves add.
+            const uint32_t v = swz::swizzle(1u << b, B, M, p->S);
+            int64_t d = 0;
+            for (int t = 0; t < 32; ++t)
+                if ((v >> t) & 1u) d += ((sb >> t) & 1u) ? -(int64_t(1) << t) : (int64_t(1) << t);
+            strides[b] = d;
+        }
+    }
+    return SWZ_OK;
 }
 
 SWZ_API int swz_choose(int32_t elem_bytes, int32_t vec_bytes, int32_t tile_rows, int32_t tile_cols, int32_t read_kind,

@@ -36,7 +36,7 @@ void direct_write(int wave, int j, int32_t* addr) {
 template <int KIND>
 void predict_kind(const BankModel& m, uint32_t ld, swz_params p, bool direct, int64_t* wcyc, int64_t* rcyc) {
     using K = Kind<KIND>;
-    const LdsLayout L{ld, static_cast<uint32_t>(p.B), static_cast<uint32_t>(p.M), static_cast<uint32_t>(p.S)};
+    const LdsLayout L{ld, static_cast<uint32_t>(p.B), static_cast<uint32_t>(p.M), p.S};
     int64_t w = 0, r = 0;
     Access a;
     for (int wave = 0; wave < K::NT / 64; ++wave) {
@@ -74,7 +74,7 @@ void predict_kind(const BankModel& m, uint32_t ld, swz_params p, bool direct, in
 template <int KIND>
 int accesses_kind(uint32_t ld, swz_params p, bool direct, bool write, int32_t* addrs, int max_acc, int* width) {
     using K = Kind<KIND>;
-    const LdsLayout L{ld, static_cast<uint32_t>(p.B), static_cast<uint32_t>(p.M), static_cast<uint32_t>(p.S)};
+    const LdsLayout L{ld, static_cast<uint32_t>(p.B), static_cast<uint32_t>(p.M), p.S};
     const bool dw = direct && write;
     const int steps = dw ? Direct<KIND>::LOADS : write ? K::WSTEPS : K::RSTEPS;
     *width = dw ? Direct<KIND>::VB : write ? K::VEC : K::RWIDTH;
@@ -156,13 +156,17 @@ void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64
 bool params_ok_for_kind(int kind, swz_params p) {
     KindInfo k;
     if (!kind_info(kind, &k)) return false;
-    if (p.B < 0 || p.M < 0 || p.S < 0) return false;
-    if (p.B == 0) return p.M + p.S <= 32;
-    if (p.B + p.M + p.S > 32) return false;
-    if (p.S < 1) return false;
+    if (p.B < 0 || p.M < 0) return false;
+    const int64_t abs_s = p.S < 0 ? -static_cast<int64_t>(p.S) : p.S;
+    if (p.B == 0) return p.M + abs_s <= 32;
+    if (p.B + p.M + abs_s > 32) return false;
+    if (abs_s < 1) return false;
     const int min_vec = k.vec > k.rwidth ? k.vec : k.rwidth;
     if ((1 << p.M) < min_vec / k.esz) return false;
-    if (p.M + p.B > ilog2(static_cast<int64_t>(k.tr) * k.tc)) return false;
+    // The field that changes starts at M (S > 0) or M + |S| (S < 0); it must
+    // stay inside the tile.
+    const int64_t target = p.S > 0 ? p.M : p.M + abs_s;
+    if (target + p.B > ilog2(static_cast<int64_t>(k.tr) * k.tc)) return false;
     return true;
 }
 

@@ -33,10 +33,10 @@ int kernel_accesses(int kind, uint32_t ld, swz_params p, bool direct, bool write
 // Pad (elements per LDS row) of the padded layout for a kind.
 int pad_elems(int kind);
 
-// Validate caller parameters for a kind: non-negative, fields inside 32 bits,
-// S >= 1 when B > 0 (S = 0 would not be one-to-one), vectors kept whole
-// (2^M >= elements per LDS store and per LDS load) and the permuted block
-// inside the tile (M + B <= log2(tile elements)).
+// Validate caller parameters for a kind: B, M non-negative, fields inside
+// 32 bits, S != 0 when B > 0 (S = 0 would not be one-to-one; S may be
+// negative), vectors kept whole (2^M >= elements per LDS store and per LDS
+// load) and the field that changes inside the tile.
 bool params_ok_for_kind(int kind, swz_params p);
 
 }  // namespace swz

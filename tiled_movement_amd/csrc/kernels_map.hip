@@ -8,7 +8,7 @@ namespace {
 // No __restrict__: in and out may be the same buffer (in place).
 template <bool VEC4>
 __global__ __launch_bounds__(256) void k_map(const uint32_t* in, uint32_t* out, int64_t n, uint32_t B, uint32_t M,
-                                             uint32_t S) {
+                                             int32_t S) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (VEC4) {
@@ -37,7 +37,8 @@ hipError_t launch_map(const int32_t* in, int32_t* out, int64_t n, swz_params p, 
     const int64_t items = vec4 ? (n + 3) / 4 : n;
     int64_t blocks = (items + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    const auto B = static_cast<uint32_t>(p.B), M = static_cast<uint32_t>(p.M), S = static_cast<uint32_t>(p.S);
+    const auto B = static_cast<uint32_t>(p.B), M = static_cast<uint32_t>(p.M);
+    const int32_t S = p.S;
     const auto* ui = reinterpret_cast<const uint32_t*>(in);
     auto* uo = reinterpret_cast<uint32_t*>(out);
     if (vec4)

@@ -31,12 +31,16 @@ namespace swz {
 
 // Swizzle<B,M,S> of a 32-bit element offset: the B-bit field at bit M+S is
 // XORed into the B-bit field at bit M ("CuTe Swizzle 学习手册", swizzle
-// formula).  B == 0 is the identity.  Written without branches (selects
-// only) and without shifts by 32 or more, which C++ leaves undefined.
-__host__ __device__ __forceinline__ uint32_t swizzle(uint32_t x, uint32_t B, uint32_t M, uint32_t S) {
+// formula); for S < 0 the field at bit M is XORed into the one at bit
+// M + |S| ("NVIDIA CuTe Swizzle", a negative shift moves the mask left).
+// B == 0 is the identity.  Written without branches (selects only) and
+// without shifts by 32 or more, which C++ leaves undefined.
+__host__ __device__ __forceinline__ uint32_t swizzle(uint32_t x, uint32_t B, uint32_t M, int32_t S) {
     const uint32_t mask = B >= 32u ? 0xffffffffu : ((1u << B) - 1u);
-    const uint32_t src = (M + S) >= 32u ? 0u : ((x >> (M + S)) & mask);
-    return x ^ (M >= 32u ? 0u : (src << M));
+    const uint32_t up = S >= 0 ? static_cast<uint32_t>(S) : 0u;    // source above the target
+    const uint32_t dn = S >= 0 ? 0u : static_cast<uint32_t>(-S);   // source below the target
+    const uint32_t src = (M + up) >= 32u ? 0u : ((x >> (M + up)) & mask);
+    return x ^ ((M + dn) >= 32u ? 0u : (src << (M + dn)));
 }
 
 // How a tile sits in LDS: element (r, c) lives at element offset
@@ -44,7 +48,8 @@ __host__ __device__ __forceinline__ uint32_t swizzle(uint32_t x, uint32_t B, uin
 // swizzle is the identity (B = 0) for PAD and PLAIN.
 struct LdsLayout {
     uint32_t ld;  // LDS row pitch in elements
-    uint32_t B, M, S;
+    uint32_t B, M;
+    int32_t S;
 };
 
 __host__ __device__ __forceinline__ uint32_t lds_elem(const LdsLayout& L, uint32_t r, uint32_t c) {
