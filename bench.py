@@ -16,7 +16,7 @@ Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
   python bench.py --workload NAME --layout swizzle|pad|plain|direct [--steps K]
       time one workload only (used for profiler runs); NAME is one of
-      fp32_transpose, fp16_transpose, fp16_transpose_tr, bf16_convert,
+      fp32_transpose, fp16_transpose, fp16_transpose_tr, u8_transpose, bf16_convert,
       bf16_stage, map, copy, copy_128, memcpy_d2d, bf16_gemm, torch_mm_bf16
 """
 
@@ -43,6 +43,7 @@ WORKLOADS = {
     "fp16_transpose": "fp16 8192x8192 row-major -> column-major transpose, 64x64 LDS tiles, 8-byte reads of 4x4 blocks",
     "fp16_transpose_tr": "fp16 8192x8192 row-major -> column-major transpose, 64x64 LDS tiles, gfx950 8-byte transpose reads",
     "bf16_convert": "bf16 [64,4096,128] -> [64,128,4096] layout conversion, 64x128 LDS tiles, 16-byte reads of 8x8 blocks",
+    "u8_transpose": "1-byte (int8 / fp8 bits) 8192x8192 row-major -> column-major transpose, 128x128 LDS tiles, gfx950 8-bit transpose reads",
     "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
     "bf16_gemm": "C[8192x8192] fp32 = A * B^T from the staged fragments of A[8192x4096] and B[4096x8192] (16x16x32 bf16 MFMA)",
@@ -135,7 +136,7 @@ class Ctx:
 
     def copies(self, a, k):
         np, torch = self.np, self.torch
-        base = torch.from_numpy(np.ascontiguousarray(a).view(np.int32 if a.itemsize == 4 else np.int16)).to(self.dev)
+        base = torch.from_numpy(np.ascontiguousarray(a).view({4: np.int32, 2: np.int16, 1: np.uint8}[a.itemsize])).to(self.dev)
         return [base] + [base.clone() for _ in range(k - 1)]
 
     def check(self, rc, what):
@@ -153,13 +154,15 @@ def build(ctx, name, layout):
     lay = T.LAYOUTS[layout]
     info = {"workload": WORKLOADS[name], "layout": layout}
 
-    if name in ("fp32_transpose", "fp16_transpose", "fp16_transpose_tr", "bf16_convert"):
+    if name in ("fp32_transpose", "fp16_transpose", "fp16_transpose_tr", "bf16_convert", "u8_transpose"):
         if name == "fp32_transpose":
             a, esz, kind, (batch, r, c) = W.fp32_matrix(4096, 4096, seed=0), 4, T.READ_SCALAR_COL, (1, 4096, 4096)
         elif name == "fp16_transpose":
             a, esz, kind, (batch, r, c) = W.fp16_matrix(8192, 8192, seed=0), 2, T.READ_B64_4X4, (1, 8192, 8192)
         elif name == "fp16_transpose_tr":
             a, esz, kind, (batch, r, c) = W.fp16_matrix(8192, 8192, seed=0), 2, T.READ_B64_TR16, (1, 8192, 8192)
+        elif name == "u8_transpose":
+            a, esz, kind, (batch, r, c) = W.u8_matrix(8192, 8192, seed=0), 1, T.READ_B64_TR8, (1, 8192, 8192)
         else:
             a, esz, kind, (batch, r, c) = W.bf16_tensor((64, 4096, 128), seed=0), 2, T.READ_B128_8X8, (64, 4096, 128)
         k = n_pairs(2 * a.nbytes)
@@ -347,7 +350,7 @@ def main(argv=None):
     extra = {}
     if not args.quick and args.workload is None:
         for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "fp16_transpose_tr",
-                      "bf16_convert", "bf16_stage", "map", "bf16_gemm", "torch_mm_bf16"):
+                      "u8_transpose", "bf16_convert", "bf16_stage", "map", "bf16_gemm", "torch_mm_bf16"):
             for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map", "bf16_gemm", "torch_mm_bf16")
                         else ("swizzle", "pad", "plain", "direct")):
                 s2, nb2, inf2 = build(ctx, wname, lay)
@@ -396,7 +399,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32_transpose": "f32", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "map": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
+        "dtype": {"fp32_transpose": "f32", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
         "data": "synthetic",
         "config": {k: v for k, v in info.items() if not k.startswith("_")},
         "roofline": {

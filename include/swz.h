@@ -76,15 +76,22 @@ enum swz_layout {
  *               addresses 8-byte row pieces and every lane receives four
  *               consecutive rows of one column, so two reads give a lane one
  *               16-byte output piece with no register shuffles.
+ *  B64_TR8    : 1-byte elements, 128x128 tile, read with the gfx950 8-bit
+ *               transpose read (ds_read_b64_tr_b8): each lane receives eight
+ *               consecutive rows of one column per read.  The 1-byte case of
+ *               "CUDA 013 - Swizzle 的工作原理", usage example 2 (char rows
+ *               with the low bits kept together), here with 8-byte runs.
  *  AUTO       : 4-byte -> SCALAR_COL; 2-byte -> B128_8X8 when cols <= 128,
- *               else B64_TR16 (the faster of the two 64x64 kinds). */
+ *               else B64_TR16 (the faster of the two 64x64 kinds); 1-byte ->
+ *               B64_TR8. */
 enum swz_read_kind {
     SWZ_READ_AUTO = -1,
     SWZ_READ_SCALAR_COL = 0,
     SWZ_READ_B64_4X4 = 1,
     SWZ_READ_B128_8X8 = 2,
     SWZ_READ_MFMA_16X16X32 = 3,
-    SWZ_READ_B64_TR16 = 4
+    SWZ_READ_B64_TR16 = 4,
+    SWZ_READ_B64_TR8 = 5
 };
 
 enum swz_frag_kind { SWZ_FRAG_MFMA_F32_16X16X32_BF16 = 0 };
@@ -123,7 +130,7 @@ int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p, void* 
  * ("CuTe Swizzle 学习手册", typical scenario: column access of a row-major
  * tile; "CUDA 013 - Swizzle 的工作原理", sections 如何避免 Bank Conflict and
  * Swizzle 技术).  Exactly swz_convert_layout with batch = 1.
- *   elem_bytes : 2 or 4.
+ *   elem_bytes : 1, 2 or 4.
  *   layout     : enum swz_layout.
  *   read_kind  : enum swz_read_kind (AUTO picks by element size and width).
  *   p_or_null  : swizzle to use with SWZ_LAYOUT_SWIZZLE(_DIRECT), or NULL to

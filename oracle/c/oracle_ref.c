@@ -31,7 +31,7 @@ void oref_swizzle_map(const int32_t* in, int32_t* out, int64_t n, int32_t B, int
     for (int64_t i = 0; i < n; ++i) out[i] = (int32_t)oref_swizzle((uint32_t)in[i], B, M, S);
 }
 
-/* ---- dst[b][c][r] = src[b][r][c], element size 2 or 4 bytes ---- */
+/* ---- dst[b][c][r] = src[b][r][c], element size 1, 2 or 4 bytes ---- */
 struct tr_job {
     const uint8_t* src;
     uint8_t* dst;
@@ -74,7 +74,7 @@ static void* st_run(void* arg) {
 
 /* Returns 0, or -1 for a bad argument. */
 int oref_convert(const void* src, void* dst, int64_t batch, int64_t rows, int64_t cols, int32_t esz, int32_t nthreads) {
-    if ((esz != 2 && esz != 4) || batch < 0 || rows < 0 || cols < 0 || nthreads < 1 || nthreads > OREF_MAX_THREADS) return -1;
+    if ((esz != 1 && esz != 2 && esz != 4) || batch < 0 || rows < 0 || cols < 0 || nthreads < 1 || nthreads > OREF_MAX_THREADS) return -1;
     pthread_t th[OREF_MAX_THREADS];
     int started[OREF_MAX_THREADS] = {0};
     struct tr_job jobs[OREF_MAX_THREADS];

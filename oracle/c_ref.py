@@ -64,11 +64,11 @@ def swizzle_map(x, B, M, S):
 
 def convert_layout(a, threads: int = 1):
     """dst[b][c][r] = src[b][r][c] for a [batch, rows, cols] (or [rows, cols])
-    array of 2- or 4-byte elements, as raw bits ("CUDA 013 - Swizzle 的工作原理",
+    array of 1-, 2- or 4-byte elements, as raw bits ("CUDA 013 - Swizzle 的工作原理",
     problem statement)."""
     a = np.ascontiguousarray(a)
-    if a.itemsize not in (2, 4) or a.ndim not in (2, 3):
-        raise ValueError("2- or 4-byte elements, 2-D or 3-D")
+    if a.itemsize not in (1, 2, 4) or a.ndim not in (2, 3):
+        raise ValueError("1-, 2- or 4-byte elements, 2-D or 3-D")
     a3 = a.reshape((1,) + a.shape) if a.ndim == 2 else a
     b, r, c = a3.shape
     out = np.empty((b, c, r), dtype=a.dtype)

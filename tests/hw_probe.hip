@@ -11,6 +11,11 @@
 // issues one ds_read_b64_tr_b16 at its own byte address, and the four
 // halfwords every lane receives are written out, so the tests can check the
 // instruction's lane semantics.
+//
+// tr8_probe: the same for the 8-bit transpose read ds_read_b64_tr_b8: LDS
+// byte i holds (i >> shift) & 0xff (two runs, shift 0 and 8, name every byte
+// of a 16 KiB window), each lane reads at its own address and the eight
+// bytes every lane receives are written out.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,5 +68,30 @@ extern "C" __attribute__((visibility("default"))) int tr16_probe(const int32_t* 
     }
     hipLaunchKernelGGL(k_tr16_probe, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), t,
                        static_cast<uint16_t*>(d_out));
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+__global__ __launch_bounds__(64) void k_tr8_probe(TrAddrs addrs, int shift, uint8_t* __restrict__ out) {
+    typedef int v2i32 __attribute__((ext_vector_type(2)));
+    __shared__ uint8_t lds[16384];
+    for (int i = threadIdx.x; i < 16384; i += 64) lds[i] = static_cast<uint8_t>(i >> shift);
+    __syncthreads();
+    const int a = addrs.a[threadIdx.x];
+    const v2i32 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i32*)((__attribute__((address_space(3))) uint8_t*)lds + a));
+    for (int j = 0; j < 8; ++j) out[threadIdx.x * 8 + j] = static_cast<uint8_t>(v[j / 4] >> (8 * (j % 4)));
+}
+
+// As tr16_probe; shift is 0 or 8; d_out holds 512 bytes.
+extern "C" __attribute__((visibility("default"))) int tr8_probe(const int32_t* addrs, int shift, void* d_out,
+                                                               void* stream) {
+    if (!addrs || !d_out || (shift != 0 && shift != 8)) return -1;
+    TrAddrs t;
+    for (int l = 0; l < 64; ++l) {
+        if (addrs[l] < 0 || addrs[l] > 16384 - 8 || addrs[l] % 8) return -1;
+        t.a[l] = addrs[l];
+    }
+    hipLaunchKernelGGL(k_tr8_probe, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), t, shift,
+                       static_cast<uint8_t*>(d_out));
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }

@@ -131,7 +131,7 @@ def test_plans():
 
 def threads_of(kind):
     op = 1 if kind == T.READ_MFMA_16X16X32 else 0
-    esz = 4 if kind == T.READ_SCALAR_COL else 2
+    esz = KIND_GEOM[kind][0]
     return T.swz_plan(op, 4096, 4096, esz, "swizzle", kind)["threads"]
 
 
@@ -163,6 +163,26 @@ def restated_accesses(kind, write):
                     for s_ in range(8):
                         coords = [(8 * ((t + nt * j) % 8) + s_, (width // 2) * ((t + nt * j) // 8)) for t in ts]
                         out.append((coords, width))
+        elif kind == T.READ_B64_TR8:  # 128x128 1-byte tile, 8-bit transpose reads
+            if write:  # vector v: row v/8, bytes 16(v%8)..; step h writes half h ^ (row odd)
+                for j in range(128 * 128 // 16 // nt):
+                    for h in range(2):
+                        coords = []
+                        for t in ts:
+                            v = t + nt * j
+                            coords.append((v // 8, 16 * (v % 8) + 8 * (h ^ ((v // 8) % 2))))
+                        out.append((coords, 8))
+            else:
+                # group g (16 lanes) of the wave: loader q addresses row
+                # 64h + 16g + 8(q%2) + q//2 of the 8-byte column block
+                for k in range(16 // (nt // 64)):
+                    ch = w + (nt // 64) * k
+                    for h in range(2):
+                        coords = []
+                        for l in range(64):
+                            g, q = divmod(l, 16)
+                            coords.append((64 * h + 16 * g + 8 * (q % 2) + q // 2, 8 * ch))
+                        out.append((coords, 8))
         elif kind == T.READ_B64_TR16:  # 64x64 2-byte tile, transpose reads
             if write:
                 for j in range(4096 * 2 // 16 // nt):
@@ -200,6 +220,7 @@ KIND_GEOM = {
     T.READ_B128_8X8: (2, 64, 128, 8),
     T.READ_MFMA_16X16X32: (2, 256, 64, 8),
     T.READ_B64_TR16: (2, 64, 64, 8),
+    T.READ_B64_TR8: (1, 128, 128, 8),
 }
 
 
@@ -253,7 +274,7 @@ def test_chooser_matches_oracle_chooser(kind):
     the pages' own choices under their bank model) picks the same triple,
     and it is predicted conflict-free."""
     esz, tr, tc, _ = KIND_GEOM[kind]
-    vec = 16 if esz == 2 else 4
+    vec = {4: 4, 2: 16, 1: 8}[esz]
     (b, m, s), cyc = O.choose(esz, vec, tr, tc, restated_accesses(kind, 1), restated_accesses(kind, 0), oracle_model())
     assert T.swz_choose(esz, vec, tr, tc, kind) == (b, m, s)
     assert cyc == 0
@@ -271,6 +292,10 @@ def test_model_matches_measured_geometry():
     first = [0, 1, 2, 3, 12, 13, 14, 15, 20, 21, 22, 23, 24, 25, 26, 27]
     assert sorted(l for l in range(64) if ph[l] == ph[0]) == first
     assert len(set(ph)) == 4
+    # writes: 16 contiguous lanes for 4- and 8-byte writes, 8 for 16-byte ones
+    assert m[("write", 4)]["phase"] == [l // 16 for l in range(64)]
+    assert m[("write", 8)]["phase"] == [l // 16 for l in range(64)]
+    assert m[("write", 16)]["phase"] == [l // 8 for l in range(64)]
 
 
 # ------------------------------------------------- direct HBM -> LDS fill
@@ -300,7 +325,7 @@ def test_direct_validation():
 def test_direct_fill_writes_lane_linear_and_reads_like_swizzle(kind):
     esz, tr, tc, _ = KIND_GEOM[kind]
     nt = threads_of(kind)
-    vb = 4 if esz == 4 else 16
+    vb = 16 if esz == 2 else 4
     loads = tr * tc * esz // vb // nt
     acc = T.swz_kernel_accesses(kind, "direct", None, 1)
     assert len(acc) == loads * nt // 64
@@ -323,7 +348,7 @@ def test_direct_fill_places_every_element_where_swizzle_does(kind):
     and for every S >= B the chooser could emit -- so the fill reproduces
     the swizzled tile exactly, and covers each element once."""
     esz, tr, tc, _ = KIND_GEOM[kind]
-    epl = 1 if esz == 4 else 8
+    epl = {4: 1, 2: 8, 1: 4}[esz]
     m_min = 0 if esz == 4 else 3
     log_tile = (tr * tc).bit_length() - 1
     for B, M, S in [(b, m, s) for b in range(1, 6) for m in (m_min, m_min + 1) for s in range(b, 8)

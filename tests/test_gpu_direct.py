@@ -18,7 +18,7 @@ T = pytest.importorskip("tiled_movement_amd")
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-SIGNED = {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32}
+SIGNED = {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32, np.dtype(np.uint8): np.uint8}
 
 
 def to_dev(a):
@@ -39,6 +39,7 @@ KINDS = [
     (T.READ_B64_4X4, 2, 64, 64, W.fp16_matrix, 8),
     (T.READ_B128_8X8, 2, 64, 128, lambda r, c, seed: W.bf16_tensor((r, c), seed=seed), 8),
     (T.READ_B64_TR16, 2, 64, 64, W.fp16_matrix, 8),
+    (T.READ_B64_TR8, 1, 128, 128, W.u8_matrix, 16),
 ]
 
 
@@ -76,7 +77,7 @@ def test_direct_transpose_shapes(kind, esz, tr, tc, gen, q):
 def test_direct_transpose_any_involutive_swizzle(kind, esz, tr, tc, gen, q):
     rows, cols = 2 * tr + q, 2 * tc + q
     a = gen(rows, cols, seed=14)
-    m_min = 0 if esz == 4 else 3
+    m_min = 0 if esz == 4 else 3  # 1-byte: the swizzle keeps 8-byte runs (M >= 3)
     log_tile = (tr * tc).bit_length() - 1
     triples = [(B, M, S) for B in range(0, 6) for M in range(m_min, 6) for S in range(max(B, 1), 9)
                if M + B <= log_tile]
@@ -140,6 +141,11 @@ def test_direct_full_fp16_8192():
 def test_direct_full_fp16_8192_transpose_read():
     announce("direct full fp16 8192 transpose read")
     check(W.fp16_matrix(8192, 8192, seed=0), 2, T.READ_B64_TR16)
+
+
+def test_direct_full_u8_8192_transpose_read():
+    announce("direct full u8 8192")
+    check(W.u8_matrix(8192, 8192, seed=0), 1, T.READ_B64_TR8)
 
 
 def test_direct_full_bf16_convert():

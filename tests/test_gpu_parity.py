@@ -17,7 +17,8 @@ T = pytest.importorskip("tiled_movement_amd")
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
-SIGNED = {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32, np.dtype(np.int32): np.int32}
+SIGNED = {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32, np.dtype(np.int32): np.int32,
+          np.dtype(np.uint8): np.uint8}
 
 
 def to_dev(a):
@@ -96,6 +97,7 @@ KINDS = [
     (T.READ_B64_4X4, 2, 64, 64, W.fp16_matrix),
     (T.READ_B128_8X8, 2, 64, 128, lambda r, c, seed: W.bf16_tensor((r, c), seed=seed)),
     (T.READ_B64_TR16, 2, 64, 64, W.fp16_matrix),
+    (T.READ_B64_TR8, 1, 128, 128, W.u8_matrix),
 ]
 LAYOUTS = ["swizzle", "pad", "plain"]
 
@@ -151,7 +153,7 @@ def test_transpose_any_valid_swizzle(kind, esz, tr, tc, gen):
     gives the same bits out."""
     rows, cols = 2 * tr + 3, 2 * tc + 5
     a = gen(rows, cols, seed=4)
-    m_min = {4: 0, 2: 3}[esz]
+    m_min = {4: 0, 2: 3, 1: 3}[esz]
     log_tile = (tr * tc).bit_length() - 1
     rng = np.random.default_rng(kind)
     triples = [(B, M, S) for B in range(1, 6) for M in range(m_min, 6) for S in range(1, 9)
@@ -165,9 +167,10 @@ def test_transpose_any_valid_swizzle(kind, esz, tr, tc, gen):
 def test_transpose_negative_shifts(kind, esz, tr, tc, gen):
     """Negative shifts XOR a low field into a higher one; the data still only
     moves inside LDS, so the transpose is unchanged."""
-    rows, cols = 2 * tr + 8, 2 * tc + 8
+    q = 16 // esz  # ragged by one 16-byte run, so the direct layout's pitch rule holds
+    rows, cols = 2 * tr + q, 2 * tc + q
     a = gen(rows, cols, seed=24)
-    m0 = 0 if esz == 4 else 3
+    m0 = 0 if esz == 4 else 3  # 2-byte: 16-byte vectors; 1-byte: 8-byte runs
     log_tile = (tr * tc).bit_length() - 1
     for B, M, S in [(3, m0, -3), (2, m0, -5), (3, m0 + 1, -4), (1, m0, -1)]:
         if M - S + B > log_tile:
@@ -183,6 +186,7 @@ def test_convert_layout_batches():
         (T.READ_B128_8X8, 2, W.bf16_tensor((2, 64, 100), seed=6)),  # ragged rows of 100
         (T.READ_B64_4X4, 2, W.bf16_tensor((2, 70, 130), seed=7)),
         (T.READ_B64_TR16, 2, W.bf16_tensor((2, 70, 130), seed=10)),
+        (T.READ_B64_TR8, 1, W.u8_matrix(3 * 130, 200, seed=11).reshape(3, 130, 200)),
         (T.READ_SCALAR_COL, 4, W.fp32_matrix(3 * 40, 50, seed=8).reshape(3, 40, 50)),
     ]
     for kind, esz, a in cases:
@@ -255,6 +259,12 @@ def test_full_fp16_8192(layout):
 def test_full_fp16_8192_transpose_read(layout):
     announce("full fp16 8192 transpose read", layout)
     check_transpose(W.fp16_matrix(8192, 8192, seed=0), 2, layout, T.READ_B64_TR16)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_full_u8_8192_transpose_read(layout):
+    announce("full u8 8192 transpose read", layout)
+    check_transpose(W.u8_matrix(8192, 8192, seed=0), 1, layout, T.READ_B64_TR8)
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)

@@ -87,3 +87,70 @@ def test_kernel_lane_map_hands_each_lane_eight_rows_of_one_column(probe):
                 elem = O.swizzle(int(got[lane, j]), B, M, S)  # LDS slot -> tile element
                 r, c = divmod(elem, 64)
                 assert (r, c) == (16 * g + 8 * (q // 8) + 4 * h + j, 8 * (nt // 64) * k + 4 * ((q // 4) % 2) + q % 4)
+
+
+# ------------------------------------------------ the 8-bit transpose read
+
+
+@pytest.fixture(scope="module")
+def probe8():
+    path = os.path.join(HERE, "libhw_probe.so")
+    if not os.path.exists(path):
+        pytest.fail("tests/libhw_probe.so is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.tr8_probe.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tr8_probe.restype = ctypes.c_int
+    return lib
+
+
+def run8(probe8, addrs):
+    """Byte address every (lane, byte) received: two runs name the low and
+    the high byte of each LDS byte's address."""
+    a = (ctypes.c_int32 * 64)(*[int(x) for x in addrs])
+    parts = []
+    for shift in (0, 8):
+        out = torch.zeros(512, dtype=torch.uint8, device=DEV)
+        assert probe8.tr8_probe(a, shift, out.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        parts.append(out.cpu().numpy().astype(np.int64))
+    return (parts[0] | (parts[1] << 8)).reshape(64, 8)
+
+
+def expected8(addrs):
+    """Reading of the 8-bit transpose read: within each group of 16 lanes,
+    lane q receives byte q % 8 of the pieces addressed by lanes q//8 + 2j."""
+    exp = np.empty((64, 8), dtype=np.int64)
+    for lane in range(64):
+        g, q = divmod(lane, 16)
+        for j in range(8):
+            exp[lane, j] = addrs[16 * g + q // 8 + 2 * j] + q % 8
+    return exp
+
+
+@pytest.mark.parametrize("pattern", ["linear", "rows", "random"])
+def test_8bit_transpose_read_lane_semantics(probe8, pattern):
+    if pattern == "linear":
+        addrs = [8 * l for l in range(64)]
+    elif pattern == "rows":
+        addrs = [128 * l for l in range(64)]
+    else:
+        rng = np.random.default_rng(33)
+        addrs = [8 * int(b) for b in rng.choice(2047, size=64, replace=False)]
+    assert np.array_equal(run8(probe8, addrs), expected8(addrs))
+
+
+def test_8bit_kernel_lane_map_hands_each_lane_eight_rows_of_one_column(probe8):
+    plan = T.swz_plan(0, 128, 128, 1, "swizzle", T.READ_B64_TR8)
+    B, M, S = plan["params"]
+    nt = plan["threads"]
+    accesses = T.swz_kernel_accesses(T.READ_B64_TR8, "swizzle", None, 0)
+    for i in range(len(accesses) // (nt // 64)):  # wave 0
+        addrs, width = accesses[i]
+        assert width == 8
+        got = run8(probe8, addrs)
+        k, h = divmod(i, 2)
+        for lane in range(64):
+            g, q = divmod(lane, 16)
+            for j in range(8):
+                r, c = divmod(O.swizzle(int(got[lane, j]), B, M, S), 128)
+                assert (r, c) == (64 * h + 16 * g + 8 * (q // 8) + j, 8 * (nt // 64) * k + q % 8)

@@ -49,6 +49,7 @@ def test_map_rejects_out_of_range_triples():
 
 @pytest.mark.parametrize("threads", [1, 3, 8])
 @pytest.mark.parametrize("shape,dtype", [((96, 160), np.float32), ((130, 200), np.float16), ((1, 7), np.float32),
+                                         ((77, 300), np.uint8),
                                          ((33, 1), np.uint16), ((0, 5), np.float32)])
 def test_transpose_equals_library_transpose(shape, dtype, threads):
     rng = np.random.default_rng(3)

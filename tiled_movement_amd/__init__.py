@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libswz.so")
 # enum values of include/swz.h
 SWZ_OK, SWZ_EINVAL, SWZ_EUNSUPPORTED, SWZ_EHIP = 0, -1, -2, -3
 LAYOUT_SWIZZLE, LAYOUT_PAD, LAYOUT_PLAIN, LAYOUT_SWIZZLE_DIRECT = 0, 1, 2, 3
-READ_AUTO, READ_SCALAR_COL, READ_B64_4X4, READ_B128_8X8, READ_MFMA_16X16X32, READ_B64_TR16 = -1, 0, 1, 2, 3, 4
+READ_AUTO, READ_SCALAR_COL, READ_B64_4X4, READ_B128_8X8, READ_MFMA_16X16X32, READ_B64_TR16, READ_B64_TR8 = (
+    -1, 0, 1, 2, 3, 4, 5)
 FRAG_MFMA_F32_16X16X32_BF16 = 0
 LAYOUTS = {"swizzle": LAYOUT_SWIZZLE, "pad": LAYOUT_PAD, "plain": LAYOUT_PLAIN, "direct": LAYOUT_SWIZZLE_DIRECT}
 

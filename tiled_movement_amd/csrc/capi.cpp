@@ -65,8 +65,10 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     if (layout < SWZ_LAYOUT_SWIZZLE || layout > SWZ_LAYOUT_SWIZZLE_DIRECT) return SWZ_EINVAL;
     int kind = read_kind;
     if (op == 0) {
-        if (esz != 2 && esz != 4) return SWZ_EINVAL;
-        if (kind == SWZ_READ_AUTO) kind = esz == 4 ? SWZ_READ_SCALAR_COL : (cols <= 128 ? SWZ_READ_B128_8X8 : SWZ_READ_B64_TR16);
+        if (esz != 1 && esz != 2 && esz != 4) return SWZ_EINVAL;
+        if (kind == SWZ_READ_AUTO)
+            kind = esz == 4 ? SWZ_READ_SCALAR_COL
+                            : esz == 1 ? SWZ_READ_B64_TR8 : (cols <= 128 ? SWZ_READ_B128_8X8 : SWZ_READ_B64_TR16);
         if (kind == SWZ_READ_MFMA_16X16X32) return SWZ_EINVAL;
     } else {
         if (esz != 2) return SWZ_EINVAL;
@@ -90,7 +92,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     out->params = q;
     out->pad_elems = pad;
     out->lds_bytes = k.tr * (k.tc + pad) * k.esz;
-    out->vec_bytes = layout == SWZ_LAYOUT_SWIZZLE_DIRECT ? (k.esz == 4 ? 4 : 16) : k.vec;
+    out->vec_bytes = layout == SWZ_LAYOUT_SWIZZLE_DIRECT ? (k.esz == 2 ? 16 : 4) : k.vec;
     out->aligned = aligned ? 1 : 0;
     out->threads = k.nt;
     (void)rows;
@@ -142,7 +144,7 @@ SWZ_API int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, in
                                int32_t elem_bytes, int32_t layout, int32_t read_kind, const swz_params* p_or_null,
                                void* stream) {
     if (batch < 0 || rows < 0 || cols < 0) return SWZ_EINVAL;
-    if (elem_bytes != 2 && elem_bytes != 4) return SWZ_EINVAL;
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return SWZ_EINVAL;
     int64_t n, n2, bytes;
     if (!mul_ok(batch, rows, &n) || !mul_ok(n, cols, &n2) || !mul_ok(n2, elem_bytes, &bytes)) return SWZ_EINVAL;
     const auto ps = reinterpret_cast<uintptr_t>(d_src), pd = reinterpret_cast<uintptr_t>(d_dst);

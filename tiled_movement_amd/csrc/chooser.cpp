@@ -110,6 +110,7 @@ int kernel_accesses(int kind, uint32_t ld, swz_params p, bool direct, bool write
         case SWZ_READ_MFMA_16X16X32:
             return accesses_kind<SWZ_READ_MFMA_16X16X32>(ld, p, direct, write, addrs, max_acc, width);
         case SWZ_READ_B64_TR16: return accesses_kind<SWZ_READ_B64_TR16>(ld, p, direct, write, addrs, max_acc, width);
+        case SWZ_READ_B64_TR8: return accesses_kind<SWZ_READ_B64_TR8>(ld, p, direct, write, addrs, max_acc, width);
         default: return -1;
     }
 }
@@ -127,6 +128,7 @@ bool kind_info(int kind, KindInfo* o) {
         SWZ_KIND_CASE(SWZ_READ_B128_8X8)
         SWZ_KIND_CASE(SWZ_READ_MFMA_16X16X32)
         SWZ_KIND_CASE(SWZ_READ_B64_TR16)
+        SWZ_KIND_CASE(SWZ_READ_B64_TR8)
 #undef SWZ_KIND_CASE
         default:
             return false;
@@ -149,6 +151,7 @@ void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64
         case SWZ_READ_B128_8X8: predict_kind<SWZ_READ_B128_8X8>(m, ld, p, direct, wcyc, rcyc); break;
         case SWZ_READ_MFMA_16X16X32: predict_kind<SWZ_READ_MFMA_16X16X32>(m, ld, p, direct, wcyc, rcyc); break;
         case SWZ_READ_B64_TR16: predict_kind<SWZ_READ_B64_TR16>(m, ld, p, direct, wcyc, rcyc); break;
+        case SWZ_READ_B64_TR8: predict_kind<SWZ_READ_B64_TR8>(m, ld, p, direct, wcyc, rcyc); break;
         default: *wcyc = *rcyc = -1;
     }
 }
@@ -221,7 +224,7 @@ swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles) {
 
 swz_params cached_choice(int kind) {
     static std::once_flag once;
-    constexpr int kKinds = SWZ_READ_B64_TR16 + 1;
+    constexpr int kKinds = SWZ_READ_B64_TR8 + 1;
     static swz_params table[kKinds];
     std::call_once(once, [] {
         for (int kd = 0; kd < kKinds; ++kd) table[kd] = choose_for_kind(kd, gfx950_bank_model(), nullptr);

@@ -96,18 +96,35 @@ __device__ __forceinline__ u32x4 load16_guarded(const uint8_t* S, int64_t row, i
         const bool in = row < rows && col + k < cols;
         if (ESZ == 4)
             e[k] = in ? reinterpret_cast<const uint32_t*>(S)[row * cols + col + k] : 0u;
-        else
+        else if (ESZ == 2)
             e[k] = in ? reinterpret_cast<const uint16_t*>(S)[row * cols + col + k] : 0u;
+        else
+            e[k] = in ? S[row * cols + col + k] : 0u;
     }
-    if (ESZ == 4) return u32x4{e[0], e[1], e[2], e[3]};
-    return u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+    if constexpr (ESZ == 4) {
+        return u32x4{e[0], e[1], e[2], e[3]};
+    } else if constexpr (ESZ == 2) {
+        return u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+    } else {
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            o[w] = e[4 * w] | (e[4 * w + 1] << 8) | (e[4 * w + 2] << 16) | (e[4 * w + 3] << 24);
+        return o;
+    }
 }
 
+// 16 bytes = 16/ESZ consecutive elements of one output row; only those
+// inside the matrix are written.
 template <int ESZ>
 __device__ __forceinline__ void store16_guarded(uint8_t* D, int64_t row, int64_t col, int64_t nrows, int64_t ncols,
                                                 const u32x4& o) {
     if (row >= nrows) return;
-    if (ESZ == 4) {
+    if (ESZ == 1) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (col + k < ncols) D[row * ncols + col + k] = static_cast<uint8_t>(o[k >> 2] >> (8 * (k & 3)));
+    } else if (ESZ == 4) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (col + k < ncols) reinterpret_cast<uint32_t*>(D)[row * ncols + col + k] = o[k];
@@ -223,6 +240,30 @@ __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const Ld
             for (int e = 0; e < 4; ++e)
                 reinterpret_cast<uint32_t*>(lds)[step_off<KIND, true, PADDED>(wbase, 4 * j + e, L)] = v[j][e];
         }
+    } else if constexpr (K::ESZ == 1) {
+        // Two 8-byte writes per 16-byte vector (the swizzle keeps 8-byte
+        // runs); step 2j + h writes half h ^ (row % 2) (lane map in
+        // swz_common.h).  The steps combine by XOR only, so padded rows
+        // compute each step's row and column.
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int j = 0; j < K::GLOADS; ++j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t off;
+                if constexpr (PADDED) {
+                    int r = 0, c = 0;
+                    K::wcoord(t, 2 * j + h, r, c);
+                    off = static_cast<uint32_t>(r) * L.ld + static_cast<uint32_t>(c);
+                } else {
+                    off = step_off<KIND, true, false>(wbase, 2 * j + h, L);
+                }
+                int r0 = 0, c0 = 0;
+                K::wcoord(t, 2 * j, r0, c0);
+                const int half = (c0 / 8) % 2 ^ h;  // which half of the vector this step writes
+                *reinterpret_cast<u32x2*>(lds + off) = half ? u32x2{v[j][2], v[j][3]} : u32x2{v[j][0], v[j][1]};
+            }
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < K::GLOADS; ++j)
@@ -252,6 +293,42 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
                 gstore16(D + (orow * rows + ocol) * 4, o);
             else
                 store16_guarded<4>(D, orow, ocol, cols, rows, o);
+        }
+    } else if constexpr (KIND == SWZ_READ_B64_TR8) {
+        // Task j: in each of two steps h the 8-bit transpose read gives this
+        // lane rows 64h + 16g + 8(q/8) .. +7 of one column (the lane map in
+        // swz_common.h).  Lanes q and q+8 of a 16-lane group hold the two
+        // 8-row halves of the same 16 rows; they swap one piece (a DPP
+        // rotate by 8 within the row of 16 lanes) so that lane q ends up
+        // with rows 16g .. 16g + 15 and lane q+8 with rows 64 + 16g .. +15:
+        // one 16-byte output piece each, eight lanes per 128-byte output row.
+        typedef int v2i32 __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+        const int l = t % 64, g = l / 16, q = l % 16;
+        const bool upper = q >= 8;
+#pragma unroll
+        for (int j = 0; j < K::TASKS; ++j) {
+            const int ch = t / 64 + (K::NT / 64) * j;
+            u32x2 h[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint32_t off = step_off<KIND, false, PADDED>(rbase, 2 * j + s, L);
+                h[s] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)((__attribute__((address_space(3))) uint8_t*)lds + off)));
+            }
+            // lane q < 8 sends its step-1 piece and keeps step 0; lane q >= 8
+            // sends step 0 and keeps step 1
+            const u32x2 send = upper ? h[0] : h[1];
+            u32x2 got;
+            got[0] = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(send[0]), 0x128, 0xf, 0xf, false));
+            got[1] = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(send[1]), 0x128, 0xf, 0xf, false));
+            const u32x4 o = upper ? u32x4{got[0], got[1], h[1][0], h[1][1]} : u32x4{h[0][0], h[0][1], got[0], got[1]};
+            const int64_t orow = c0 + 8 * ch + q % 8;
+            const int64_t ocol = r0 + (upper ? 64 : 0) + 16 * g;
+            if (FULL)
+                gstore16(D + orow * rows + ocol, o);
+            else
+                store16_guarded<1>(D, orow, ocol, cols, rows, o);
         }
     } else if constexpr (KIND == SWZ_READ_B64_TR16) {
         // Task j: two transpose reads give this lane 8 consecutive rows of
@@ -529,6 +606,7 @@ hipError_t launch_convert(int kind, const ConvertJob& j, hipStream_t stream) {
         case SWZ_READ_B64_4X4: return launch_kind<SWZ_READ_B64_4X4>(j, stream);
         case SWZ_READ_B128_8X8: return launch_kind<SWZ_READ_B128_8X8>(j, stream);
         case SWZ_READ_B64_TR16: return launch_kind<SWZ_READ_B64_TR16>(j, stream);
+        case SWZ_READ_B64_TR8: return launch_kind<SWZ_READ_B64_TR8>(j, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -26,6 +26,9 @@
 #ifndef SWZ_NT_TR16
 #define SWZ_NT_TR16 256
 #endif
+#ifndef SWZ_NT_TR8
+#define SWZ_NT_TR8 256
+#endif
 
 namespace swz {
 
@@ -203,6 +206,46 @@ template <> struct Kind<SWZ_READ_B64_TR16> {
     }
 };
 
+// 1-byte elements, 128x128 tile (128-byte rows) read back with the gfx950
+// 8-bit transpose read (ds_read_b64_tr_b8).  Its lane semantics, measured
+// on the hardware: in each group of 16 lanes, lane q receives byte q%8 of
+// the 8-byte pieces that lanes q/8, q/8 + 2, ..., q/8 + 14 of its group
+// addressed.  So if loader lane s = a + 2j (a = s%2) addresses row R_a + j
+// of the 8-byte column block C_a, receiver q = 8a + e gets rows
+// R_a .. R_a + 7 of column C_a + e: an 8x8 byte transpose inside the read.
+// Staging: 16-byte global loads stored as two 8-byte LDS writes (the
+// swizzle keeps 8-byte runs whole, M >= 3): vector v = t + NT*j is row v/8,
+// bytes 16(v%8) .. +15, and write step 2j + h writes its half h ^ (row % 2)
+// -- odd rows write their upper halves first, so the two 128-byte rows one
+// 16-lane write phase covers use complementary 8-byte chunks.  Read: wave
+// w's task k covers the 8-byte column block ch = w + (NT/64)*k of all 128
+// rows in two steps h; loader q of group g reads row
+// 64h + 16g + 8(q%2) + q/2 of that block, so receiver q holds rows
+// 64h + 16g + 8(q/8) .. +7 of column 8ch + q%8: one 8-byte output piece per
+// step.  Within one LDS phase (two groups) the rows read differ in their
+// five low bits, which a 4-bit swizzle field over 8-byte chunks (source: row
+// bits 1-4) spreads over all 64 banks.
+template <> struct Kind<SWZ_READ_B64_TR8> {
+    static constexpr int ESZ = 1, TR = 128, TC = 128, NT = SWZ_NT_TR8;
+    static constexpr int VEC = 8;
+    static constexpr int RWIDTH = 8;
+    static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
+    static constexpr int WSTEPS = 2 * GLOADS;
+    static constexpr int TASKS = (TC / 8) / (NT / 64);  // 8-byte column blocks per wave
+    static constexpr int RSTEPS = 2 * TASKS;
+    __host__ __device__ static constexpr void wcoord(int t, int i, int& r, int& c) {
+        const int v = t + NT * (i / 2);
+        r = v / 8;
+        c = 16 * (v % 8) + 8 * ((i % 2) ^ (r % 2));
+    }
+    __host__ __device__ static constexpr void rcoord(int t, int i, int& r, int& c) {
+        const int w = t / 64, l = t % 64, g = l / 16, q = l % 16;
+        const int k = i / 2, h = i % 2;
+        r = 64 * h + 16 * g + 8 * (q % 2) + q / 2;
+        c = 8 * (w + (NT / 64) * k);
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Offsets of a lane's later steps from its first one.
 //
@@ -212,9 +255,10 @@ template <> struct Kind<SWZ_READ_B64_TR16> {
 // wave-wide value d.  The swizzle is linear over GF(2)
 // (x -> x ^ ((x >> (M+S)) & mask) << M), so swizzle(base ^ d) =
 // swizzle(base) ^ swizzle(d): each access is the lane's one swizzled base XOR
-// a value shared by the whole wave.  Except in the transpose read, the
-// moved bits never overlap the first step's, so the same amounts also add,
-// which is what padded rows use.  The checks below prove these properties
+// a value shared by the whole wave.  Except in the 16-bit transpose read and
+// the 8-bit kind's staging writes, the moved bits never overlap the first
+// step's, so the same amounts also add, which is what padded rows use (those
+// two compute each step's row and column instead).  The checks below prove these properties
 // for every lane and step at compile time.
 // ---------------------------------------------------------------------------
 template <int KIND, bool WRITE>
@@ -277,6 +321,12 @@ static_assert(even_split<SWZ_READ_B64_TR16>() && Kind<SWZ_READ_B64_TR16>::TASKS 
               "transpose-read thread count");
 static_assert(steps_decompose<SWZ_READ_B64_TR16, true>() && steps_decompose<SWZ_READ_B64_TR16, false>(false),
               "transpose-read lane map");
+static_assert(Kind<SWZ_READ_B64_TR8>::GLOADS * Kind<SWZ_READ_B64_TR8>::NT * 16 == 128 * 128 &&
+                  Kind<SWZ_READ_B64_TR8>::TASKS * (Kind<SWZ_READ_B64_TR8>::NT / 64) == 16 &&
+                  Kind<SWZ_READ_B64_TR8>::NT % 64 == 0,
+              "8-bit transpose-read thread count");
+static_assert(steps_decompose<SWZ_READ_B64_TR8, true>(false) && steps_decompose<SWZ_READ_B64_TR8, false>(),
+              "8-bit transpose-read lane map");
 
 // ---------------------------------------------------------------------------
 // Direct fill (SWZ_LAYOUT_SWIZZLE_DIRECT): the tile goes from HBM straight
@@ -295,7 +345,11 @@ static_assert(steps_decompose<SWZ_READ_B64_TR16, true>() && steps_decompose<SWZ_
 template <int KIND>
 struct Direct {
     using K = Kind<KIND>;
-    static constexpr int VB = K::ESZ == 4 ? 4 : 16;  // bytes per lane per load
+    // bytes per lane per load: 16 for 2-byte elements (M >= 3 keeps 8 of
+    // them together); 4 otherwise (one 4-byte element; four 1-byte ones,
+    // whose swizzle keeps only 8-byte runs together and no 8-byte direct
+    // load exists)
+    static constexpr int VB = K::ESZ == 2 ? 16 : 4;
     static constexpr int EPL = VB / K::ESZ;          // elements per lane per load
     static constexpr int LOADS = K::TR * K::TC / EPL / K::NT;
 };
@@ -309,7 +363,7 @@ constexpr bool direct_split() {
 }
 static_assert(direct_split<SWZ_READ_SCALAR_COL>() && direct_split<SWZ_READ_B64_4X4>() &&
                   direct_split<SWZ_READ_B128_8X8>() && direct_split<SWZ_READ_MFMA_16X16X32>() &&
-                  direct_split<SWZ_READ_B64_TR16>(),
+                  direct_split<SWZ_READ_B64_TR16>() && direct_split<SWZ_READ_B64_TR8>(),
               "direct fill split");
 
 }  // namespace swz

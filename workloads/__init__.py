@@ -22,6 +22,7 @@ __all__ = [
     "map_triples",
     "fp32_matrix",
     "fp16_matrix",
+    "u8_matrix",
     "bf16_tensor",
     "bf16_operands",
     "bf16_bits",
@@ -54,6 +55,12 @@ def fp32_matrix(rows: int, cols: int, seed: int = 0) -> np.ndarray:
     rng = np.random.default_rng(seed)
     x = rng.random((rows, cols), dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
     return x.view(np.uint32)
+
+
+def u8_matrix(rows: int, cols: int, seed: int = 0) -> np.ndarray:
+    """Uniform random bytes (an int8 / fp8 matrix as raw bits), uint8."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
 
 
 def fp16_matrix(rows: int, cols: int, seed: int = 0) -> np.ndarray:
