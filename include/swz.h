@@ -8,6 +8,15 @@
  * returns.  Errors are negative return codes, detected on the host before
  * any launch; no call aborts or throws.  All calls are thread-safe.
  *
+ * Calls: the swizzle map (swz_map); transposes and batched layout
+ * conversions of 1-, 2- and 4-byte elements through swizzled, padded or
+ * plain LDS tiles (swz_transpose, swz_convert_layout); GEMM operand staging
+ * into matrix-instruction fragments (swz_stage_operand) and their consumer
+ * (swz_gemm_frag); host-only planning, bank-conflict prediction and layout
+ * algebra (swz_choose, swz_plan, swz_predict_conflicts, swz_kernel_accesses,
+ * swz_bank_model_get, swz_fold); and two diagnostics (swz_copy,
+ * swz_lds_probe).
+ *
  * The method follows four pages on CuTe's swizzle:
  *   "NVIDIA CuTe Swizzle", "CuTe Swizzle 学习手册", "cutlass 入门",
  *   "CUDA 013 - Swizzle 的工作原理".

@@ -289,3 +289,19 @@ def test_full_operand_staging(layout):
         torch.cuda.synchronize()
         got = from_dev(frag, op).reshape(op.shape[0] // 16, op.shape[1] // 32, 64, 8)
         assert np.array_equal(got, O.stage_operand(op))
+
+
+# ---------------------------------------------------- the reference copy
+
+
+def test_reference_copy():
+    """swz_copy (the bandwidth ceiling the kernels are compared with, and the
+    byte-counter scale) moves every byte, for sizes with and without a
+    partial workgroup."""
+    for nbytes in (16, 4096 + 48, 64 * 2**20, 64 * 2**20 + 16 * 37):
+        announce("copy", nbytes)
+        src = torch.randint(-128, 128, (nbytes,), dtype=torch.int8, device=DEV)
+        dst = torch.zeros_like(src)
+        T.swz_copy(src, dst, nbytes)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst), nbytes

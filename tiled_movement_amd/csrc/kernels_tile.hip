@@ -1,6 +1,9 @@
 // Tile staging kernels for gfx950: coalesced 16-byte row loads from HBM into
-// an LDS tile laid out by Swizzle<B,M,S> (or padded / plain rows), a read back
-// along columns or in the operand-fragment pattern, and coalesced 16-byte
+// an LDS tile laid out by Swizzle<B,M,S> (or padded / plain rows) -- through
+// registers, or by direct HBM -> LDS loads that apply the swizzle on the HBM
+// side -- a read back along columns (4-byte column reads, 8- and 16-byte
+// row pieces with in-register transposes, or gfx950's 16- and 8-bit LDS
+// transpose reads) or in the operand-fragment pattern, and coalesced 16-byte
 // row stores.
 //
 // The method is the one of "CuTe Swizzle 学习手册" (typical scenario: column
