@@ -139,6 +139,57 @@ __device__ __forceinline__ void store16_guarded(uint8_t* D, int64_t row, int64_t
     }
 }
 
+// Workgroups per CU.  The transposed HBM pattern of the 16-bit and 8-bit
+// tiles runs faster with fewer tiles in flight (measured with an LDS-free
+// probe of the same pattern: 64 x 64 16-bit tiles at 8 to 16 workgroups per
+// CU 5.41-5.48 TB/s, at 4-5 per CU 5.69).  Each launch reserves extra LDS so
+// that a CU holds at most this many workgroups of the kind (0: no limit).
+// Values from a sweep of the kernels themselves (2 to 8 per CU): 4 for the
+// 64-row 16-bit kinds (+3 to +8%), 5 for the byte kind (+4%); the fp32 tile
+// loses bandwidth when limited and staging's 32 KiB tile already sits at 5.
+#ifndef SWZ_OCC_SCALAR
+#define SWZ_OCC_SCALAR 0
+#endif
+#ifndef SWZ_OCC_B64
+#define SWZ_OCC_B64 4
+#endif
+#ifndef SWZ_OCC_B128
+#define SWZ_OCC_B128 4
+#endif
+#ifndef SWZ_OCC_STAGE
+#define SWZ_OCC_STAGE 0
+#endif
+#ifndef SWZ_OCC_TR16
+#define SWZ_OCC_TR16 4
+#endif
+#ifndef SWZ_OCC_TR8
+#define SWZ_OCC_TR8 5
+#endif
+
+template <int KIND>
+constexpr int occupancy_limit() {
+    return KIND == SWZ_READ_SCALAR_COL ? SWZ_OCC_SCALAR
+           : KIND == SWZ_READ_B64_4X4  ? SWZ_OCC_B64
+           : KIND == SWZ_READ_B128_8X8 ? SWZ_OCC_B128
+           : KIND == SWZ_READ_MFMA_16X16X32 ? SWZ_OCC_STAGE
+           : KIND == SWZ_READ_B64_TR16 ? SWZ_OCC_TR16
+                                       : SWZ_OCC_TR8;
+}
+
+constexpr int kLdsPerCu = 160 * 1024;
+
+// Dynamic LDS to add to a launch whose kernel uses `static_bytes` so that at
+// most occupancy_limit<KIND>() workgroups fit on a CU.
+template <int KIND>
+constexpr unsigned occupancy_pad(int static_bytes) {
+    const int limit = occupancy_limit<KIND>();
+    if (limit <= 0) return 0;
+    // floor(kLdsPerCu / per_wg) == limit for per_wg = kLdsPerCu / limit, and
+    // rounding the pad up can only lower the count further.
+    const int per_wg = kLdsPerCu / limit;
+    return static_cast<unsigned>(per_wg > static_bytes ? (per_wg - static_bytes + 511) / 512 * 512 : 0);
+}
+
 // How a kernel fills the LDS tile: through registers into swizzled (or
 // plain) rows, through registers into padded rows, or by direct loads into
 // swizzled (or plain) rows.
@@ -545,12 +596,13 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
     if (fits_3d(gx, gy, j.batch, K::NT)) {
         hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, true>),
                            dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(j.batch)),
-                           dim3(K::NT), 0, stream, s, d, j.rows, j.cols, tiles_r, tiles_c, int64_t(0), j.layout);
+                           dim3(K::NT), occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES), stream, s, d, j.rows, j.cols, tiles_r, tiles_c, int64_t(0), j.layout);
         return;
     }
     for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
         const int64_t n = n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid;
-        hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, false>), dim3(static_cast<unsigned>(n)), dim3(K::NT), 0,
+        hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, false>), dim3(static_cast<unsigned>(n)), dim3(K::NT),
+                           occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES),
                            stream, s, d, j.rows, j.cols, tiles_r, tiles_c, t0, j.layout);
     }
 }
@@ -590,13 +642,14 @@ void launch_stage_fill(const StageJob& j, int64_t tiles_m, int64_t tiles_k, hipS
     const int64_t gx = diag ? tiles_m : tiles_k, gy = diag ? tiles_k : tiles_m;
     if (fits_3d(gx, gy, 1, K::NT)) {
         hipLaunchKernelGGL((k_stage<FILL, true>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy), 1),
-                           dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k, int64_t(0), j.layout);
+                           dim3(K::NT), occupancy_pad<KD>(LdsTile<KD, FILL>::BYTES), stream, s, f, j.mn, j.k, tiles_m, tiles_k, int64_t(0), j.layout);
         return;
     }
     const int64_t n_tiles = tiles_m * tiles_k;
     for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
         const dim3 grid(static_cast<unsigned>(n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid));
-        hipLaunchKernelGGL((k_stage<FILL, false>), grid, dim3(K::NT), 0, stream, s, f, j.mn, j.k, tiles_m, tiles_k,
+        hipLaunchKernelGGL((k_stage<FILL, false>), grid, dim3(K::NT), occupancy_pad<KD>(LdsTile<KD, FILL>::BYTES), stream,
+                           s, f, j.mn, j.k, tiles_m, tiles_k,
                            t0, j.layout);
     }
 }
