@@ -17,7 +17,8 @@ Usage:
   python bench.py --workload NAME --layout swizzle|pad|plain|direct [--steps K]
       time one workload only (used for profiler runs); NAME is one of
       fp32_transpose, fp16_transpose, fp16_transpose_tr, u8_transpose, bf16_convert,
-      bf16_stage, map, copy, copy_128, memcpy_d2d, bf16_gemm, torch_mm_bf16
+      bf16_stage, map, copy, copy_128, memcpy_d2d, bf16_gemm, bf16_gemm_fused,
+      torch_mm_bf16
 """
 
 from __future__ import annotations
@@ -47,6 +48,7 @@ WORKLOADS = {
     "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
     "bf16_gemm": "C[8192x8192] fp32 = A * B^T from the staged fragments of A[8192x4096] and B[4096x8192] (16x16x32 bf16 MFMA)",
+    "bf16_gemm_fused": "C[8192x8192] fp32 = A * B^T, A[8192x4096] row-major and B[4096x8192] column-major staged through swizzled 256x64 LDS tiles inside the GEMM (16x16x32 bf16 MFMA)",
     "torch_mm_bf16": "runtime library GEMM (torch.mm, bf16 in and out) of the same 8192x8192x4096 product, for context",
     "copy": "reference 16-byte vector copy of 64 MiB (read once, write once)",
     "copy_128": "reference 16-byte vector copy of 128 MiB (the byte count of the 256 MiB workloads)",
@@ -230,6 +232,25 @@ def build(ctx, name, layout):
         info["_keep"] = (fa, fb, c)
         return step, 2 * m * n * k, info
 
+    if name == "bf16_gemm_fused":
+        m = n = 8192
+        k = 4096
+        ao, bo = W.bf16_operands(m, n, k, seed=0)
+        a, bt = ctx.copies(ao, 1)[0], ctx.copies(bo, 1)[0]
+        c = ctx.torch.empty((m, n), dtype=ctx.torch.float32, device=ctx.dev)
+        pa, pb, pc = a.data_ptr(), bt.data_ptr(), c.data_ptr()
+
+        def step(i):
+            rc = lib.swz_gemm(pa, pb, pc, m, n, k, lay, None, stream)
+            if rc:
+                ctx.check(rc, "swz_gemm")
+
+        pl = T.swz_plan(1, m, k, 2, "direct" if layout == "swizzle" else layout)
+        info.update({"m": m, "n": n, "k": k, "flops_per_step": 2 * m * n * k, "unit_of_value": "TFLOP/s",
+                     "params": list(pl["params"])})
+        info["_keep"] = (a, bt, c)
+        return step, 2 * m * n * k, info
+
     if name == "torch_mm_bf16":
         m = n = 8192
         k = 4096
@@ -350,8 +371,10 @@ def main(argv=None):
     extra = {}
     if not args.quick and args.workload is None:
         for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "fp16_transpose_tr",
-                      "u8_transpose", "bf16_convert", "bf16_stage", "map", "bf16_gemm", "torch_mm_bf16"):
+                      "u8_transpose", "bf16_convert", "bf16_stage", "map", "bf16_gemm", "bf16_gemm_fused",
+                      "torch_mm_bf16"):
             for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map", "bf16_gemm", "torch_mm_bf16")
+                        else ("swizzle", "plain") if wname == "bf16_gemm_fused"
                         else ("swizzle", "pad", "plain", "direct")):
                 s2, nb2, inf2 = build(ctx, wname, lay)
                 if wname == "map":
@@ -359,12 +382,13 @@ def main(argv=None):
                     extra["map/swizzle"] = {"us_per_call": round(ms2 * 1e3, 3)}
                     log(f"map: {ms2 * 1e3:.2f} us/call")
                     continue
-                if wname in ("bf16_gemm", "torch_mm_bf16"):
+                if wname in ("bf16_gemm", "bf16_gemm_fused", "torch_mm_bf16"):
                     rate, ms2 = median_rate(s2, nb2, steps=20, warmup=5)
                     tflops = rate / 1e3  # nb2 counts flops, so rate is GFLOP/s
-                    extra[wname] = {"TFLOPs": round(tflops, 1), "frac_of_mfma_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    key = f"{wname}/{lay}" if wname == "bf16_gemm_fused" else wname
+                    extra[key] = {"TFLOPs": round(tflops, 1), "frac_of_mfma_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                                     "us_per_step": round(ms2 * 1e3, 1), "m": 8192, "n": 8192, "k": 4096}
-                    log(f"{wname}: {tflops:.1f} TFLOP/s")
+                    log(f"{key}: {tflops:.1f} TFLOP/s")
                     del s2, inf2
                     ctx.torch.cuda.empty_cache()
                     continue
@@ -415,9 +439,9 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "extra": extra,
     }
-    if name in ("bf16_gemm", "torch_mm_bf16"):  # a contraction: flops, against the bf16 matrix peak
+    if name in ("bf16_gemm", "bf16_gemm_fused", "torch_mm_bf16"):  # a contraction: flops, against the bf16 matrix peak
         tflops = value / 1e3
-        line.update({"metric": "bf16 GEMM from staged fragments, TFLOP/s", "value": round(tflops, 1),
+        line.update({"metric": "bf16 GEMM, TFLOP/s", "value": round(tflops, 1),
                      "unit": "TFLOP/s", "dtype": "bf16"})
         line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,

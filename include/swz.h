@@ -12,7 +12,8 @@
  * conversions of 1-, 2- and 4-byte elements through swizzled, padded or
  * plain LDS tiles (swz_transpose, swz_convert_layout); GEMM operand staging
  * into matrix-instruction fragments (swz_stage_operand) and their consumer
- * (swz_gemm_frag); host-only planning, bank-conflict prediction and layout
+ * (swz_gemm_frag); the GEMM that stages its own operands through swizzled
+ * tiles (swz_gemm); host-only planning, bank-conflict prediction and layout
  * algebra (swz_choose, swz_plan, swz_predict_conflicts, swz_kernel_accesses,
  * swz_bank_model_get, swz_fold); and two diagnostics (swz_copy,
  * swz_lds_probe).
@@ -198,6 +199,34 @@ int swz_stage_operand(const void* d_src, void* d_frag, int64_t mn, int64_t k, in
  * Errors: SWZ_EINVAL (sizes, alignment, NULL, overlap, fragment kind). */
 int swz_gemm_frag(const void* d_fa, const void* d_fb, float* d_c, int64_t m, int64_t n, int64_t k,
                   int32_t frag_kind, void* stream);
+
+/* GEMM with the staging inside: d_c = A * B^T in fp32 from bf16 operands in
+ * their natural layouts, A [m][k] row-major (d_a) and B^T [n][k] row-major
+ * (d_bt; B column-major).  This is the use the pages build the swizzle for:
+ * each k stage copies a 256 x 64 tile of A and one of B^T from HBM straight
+ * into a swizzled LDS tile (the cp.async step), and the operand reads take
+ * the 16x16x32 instruction's fragments out of it (the ldmatrix step) --
+ * "NVIDIA CuTe Swizzle", cp.async, ldmatrix and the MMA; "CuTe Swizzle
+ * 学习手册", usage steps 2, 3 and 5.  The tile is the one swz_stage_operand
+ * stages, read in the same pattern.
+ *   layout    : SWZ_LAYOUT_SWIZZLE or SWZ_LAYOUT_SWIZZLE_DIRECT (the same
+ *               here: the fill is always direct), or SWZ_LAYOUT_PLAIN (the
+ *               ablation: row-major tiles, whose fragment reads conflict).
+ *               SWZ_LAYOUT_PAD returns SWZ_EUNSUPPORTED (a direct load
+ *               writes whole unpadded rows).
+ *   p_or_null : the swizzle for the SWIZZLE layouts (|S| >= B, as for
+ *               SWZ_LAYOUT_SWIZZLE_DIRECT), or NULL for the chooser's.
+ *   d_c       : [m][n] row-major fp32, written (not accumulated into); must
+ *               not overlap the inputs.
+ *   m, n multiples of 16, k a multiple of 32; k = 0 writes zeros.  All
+ *   pointers 16-byte aligned.
+ * The products are exact in fp32 and the sum over k is accumulated in fp32,
+ * 32 at a time by the instruction, in increasing k order -- the same result
+ * as swz_gemm_frag on the staged operands.
+ * Errors: SWZ_EINVAL (sizes, alignment, NULL, overlap, parameters),
+ * SWZ_EUNSUPPORTED (PAD). */
+int swz_gemm(const void* d_a, const void* d_bt, float* d_c, int64_t m, int64_t n, int64_t k, int32_t layout,
+             const swz_params* p_or_null, void* stream);
 
 /* Host only.  The swizzle the library uses for a tile of tile_rows x
  * tile_cols elements of elem_bytes, staged by vec_bytes-wide stores and read

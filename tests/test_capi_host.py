@@ -378,6 +378,25 @@ def test_gemm_validation():
 
 
 
+def test_fused_gemm_validation():
+    f = lib.swz_gemm
+    assert f(A, B, C, 24, 32, 32, 0, None, None) == EINVAL  # m not a multiple of 16
+    assert f(A, B, C, 32, 24, 32, 0, None, None) == EINVAL  # n
+    assert f(A, B, C, 32, 32, 48, 0, None, None) == EINVAL  # k not a multiple of 32
+    assert f(A + 8, B, C, 32, 32, 32, 0, None, None) == EINVAL  # alignment
+    assert f(A, B, None, 32, 32, 32, 0, None, None) == EINVAL
+    assert f(A, B, A + 64, 32, 32, 32, 0, None, None) == EINVAL  # C overlaps A
+    assert f(A, B, C, -16, 32, 32, 0, None, None) == EINVAL
+    assert f(A, B, C, 1 << 40, 1 << 40, 32, 0, None, None) == EINVAL  # size overflow
+    assert f(A, B, C, 32, 32, 32, 7, None, None) == EINVAL  # layout
+    assert f(A, B, C, 32, 32, 32, T.LAYOUT_PAD, None, None) == EUNSUP
+    # |S| < B: the direct fill cannot place it; a field leaving the 256x64 tile
+    assert f(A, B, C, 32, 32, 32, 0, ctypes.byref(P(4, 3, 2)), None) == EINVAL
+    assert f(A, B, C, 32, 32, 32, 0, ctypes.byref(P(4, 3, -8)), None) == EINVAL
+    for layout in (0, T.LAYOUT_PLAIN, T.LAYOUT_SWIZZLE_DIRECT):
+        assert f(A, B, C, 0, 32, 32, layout, None, None) == T.SWZ_OK  # empty: no launch
+
+
 def test_negative_shift_validation():
     assert lib.swz_map(A, B, 16, P(5, 20, -8), None) == EINVAL  # fields leave 32 bits
     f = lib.swz_convert_layout

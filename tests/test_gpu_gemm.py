@@ -92,3 +92,72 @@ def test_full_size_sampled_rows():
     ref = O.gemm_bf16(a[rows], bt)
     bound = O.gemm_error_bound(a[rows], bt)
     assert np.all(np.abs(got_dev - ref) <= 2 * bound)
+
+
+# ------------------------------------------ swz_gemm: staging inside the GEMM
+def fused_on_gpu(a, bt, layout="swizzle", params=None):
+    m, k = a.shape
+    n = bt.shape[0]
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    da = torch.from_numpy(a.view(np.int16)).to(DEV)
+    db = torch.from_numpy(bt.view(np.int16)).to(DEV)
+    T.swz_gemm(da, db, c, m, n, k, layout=layout, params=params)
+    torch.cuda.synchronize()
+    return c.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 16, 32), (256, 256, 64), (272, 400, 96), (512, 256, 4096), (48, 784, 160),
+                                   (784, 48, 32), (512, 512, 2080)])
+@pytest.mark.parametrize("layout", ["swizzle", "plain"])
+def test_fused_integer_operands_exact(m, n, k, layout):
+    announce("fused gemm exact", layout, m, n, k)
+    a, bt = int_bf16((m, k), m + k + 7), int_bf16((n, k), n + 3 * k + 7)
+    assert np.array_equal(fused_on_gpu(a, bt, layout), O.gemm_bf16(a, bt))
+
+
+@pytest.mark.parametrize("params", [(4, 3, 4), (4, 3, -4), (3, 3, 3), (2, 3, 5), (0, 0, 0)])
+def test_fused_explicit_params_exact(params):
+    """Any swizzle the direct fill can place gives the same product: the
+    layout only decides where each element sits in LDS."""
+    announce("fused gemm params", params)
+    a, bt = int_bf16((272, 192), 11), int_bf16((528, 192), 12)
+    assert np.array_equal(fused_on_gpu(a, bt, "swizzle", params), O.gemm_bf16(a, bt))
+
+
+def test_fused_direct_is_swizzle():
+    announce("fused gemm direct layout")
+    a, bt = int_bf16((256, 128), 13), int_bf16((256, 128), 14)
+    assert np.array_equal(fused_on_gpu(a, bt, "direct"), fused_on_gpu(a, bt, "swizzle"))
+
+
+def test_fused_k_zero_writes_zeros():
+    announce("fused gemm k=0")
+    got = fused_on_gpu(np.zeros((32, 0), np.uint16), np.zeros((48, 0), np.uint16))
+    assert got.shape == (32, 48) and np.all(got == 0)
+
+
+def test_fused_equals_fragment_path_bitwise():
+    """Same instruction, same k order: the fused GEMM and the staged-fragment
+    GEMM give bit-identical fp32 results on random operands."""
+    announce("fused vs fragment 512x768x4096")
+    a, bt = W.bf16_operands(512, 768, 4096, seed=5, std=1.0)
+    fused = fused_on_gpu(a, bt)
+    assert np.array_equal(fused, gemm_on_gpu(a, bt))
+    err = np.abs(fused - O.gemm_bf16(a, bt))
+    assert np.all(err <= 2 * O.gemm_error_bound(a, bt))
+
+
+@pytest.mark.parametrize("layout", ["swizzle", "plain"])
+def test_fused_full_size_sampled_rows(layout):
+    """A [8192 x 4096] row-major and B^T [8192 x 4096] (B column-major) at
+    full size: sampled rows within the bound of the oracle's fp64 product."""
+    announce("fused gemm full 8192x8192x4096", layout)
+    a, bt = W.bf16_operands(8192, 8192, 4096, seed=0)
+    c = torch.empty((8192, 8192), dtype=torch.float32, device=DEV)
+    T.swz_gemm(torch.from_numpy(a.view(np.int16)).to(DEV), torch.from_numpy(bt.view(np.int16)).to(DEV), c,
+               8192, 8192, 4096, layout=layout)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 15, 16, 255, 256, 4095, 4100, 8191, 8190, 7936, 3333])
+    got = c[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    ref = O.gemm_bf16(a[rows], bt)
+    assert np.all(np.abs(got - ref) <= 2 * O.gemm_error_bound(a[rows], bt))

@@ -32,6 +32,7 @@ EXPORTS = (
     "swz_convert_layout",
     "swz_stage_operand",
     "swz_gemm_frag",
+    "swz_gemm",
     "swz_fold",
     "swz_choose",
     "swz_predict_conflicts",
@@ -111,6 +112,7 @@ def _load() -> ctypes.CDLL:
     lib.swz_convert_layout.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_stage_operand.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_gemm_frag.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.swz_gemm.argtypes = [vp, vp, vp, i64, i64, i64, i32, P(Params), vp]
     lib.swz_fold.argtypes = [P(Params), ctypes.c_uint32, ctypes.c_uint32, P(ctypes.c_uint32), P(ctypes.c_uint32),
                              P(i64)]
     lib.swz_choose.argtypes = [i32, i32, i32, i32, i32, P(Params)]
@@ -199,6 +201,11 @@ def swz_gemm_frag(fa, fb, c, m: int, n: int, k: int, frag_kind: int = FRAG_MFMA_
                   stream=None) -> None:
     _check(lib.swz_gemm_frag(_ptr(fa), _ptr(fb), _ptr(c), m, n, k, frag_kind, _stream(stream, fa, fb, c)),
            "swz_gemm_frag")
+
+
+def swz_gemm(a, bt, c, m: int, n: int, k: int, layout: str = "swizzle", params=None, stream=None) -> None:
+    _check(lib.swz_gemm(_ptr(a), _ptr(bt), _ptr(c), m, n, k, _layout(layout), _params(params),
+                        _stream(stream, a, bt, c)), "swz_gemm")
 
 
 def swz_fold(params, base: int, active: int):

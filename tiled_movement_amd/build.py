@@ -25,6 +25,7 @@ SOURCES = [
     "bank_model.cpp",
     "kernels_tile.hip",
     "kernels_gemm.hip",
+    "kernels_gemm_tiles.hip",
     "kernels_map.hip",
     "kernels_copy.hip",
     "lds_probe.hip",

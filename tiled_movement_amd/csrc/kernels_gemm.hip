@@ -20,6 +20,7 @@
 // are in flight while stage s is multiplied.  Larger wave tiles spill
 // registers (8 x 8 blocks with two k steps per stage ran at half the rate),
 // and deeper pipelines (three or four buffers) did not help.
+#include "gemm_epilogue.h"
 #include "launch.h"
 
 namespace swz {
@@ -185,38 +186,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __res
         }
     }
 
-    // Lane l holds rows 4*(l/16) .. +3 of column l%16 of each 16 x 16 block.
-    // Each wave turns its accumulators into whole rows through its own slice
-    // of the (now idle) stage buffers, one row of blocks at a time: 16 rows
-    // of WB_N * 16 floats, stored 16 bytes per lane, so every store
-    // instruction writes whole 64-byte runs of C rows.
-    stage_barrier();  // every wave is done reading the last stage
-    constexpr int kRowFloats = kWbN * 16;
-    static_assert(kWaves * 16 * kRowFloats * 4 <= kBufs * kBufBytes, "the epilogue slices fit in the stage buffers");
-    __attribute__((address_space(3))) float* slice = (__attribute__((address_space(3))) float*)(lds + wave * 16 * kRowFloats * 4);
-    const int r4 = 4 * (lane / 16), col = lane % 16;
-#pragma unroll
-    for (int x = 0; x < kWbM; ++x) {
-        const int64_t bi = bm0 + wm * kWbM + x;
-#pragma unroll
-        for (int y = 0; y < kWbN; ++y)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) slice[(r4 + i) * kRowFloats + 16 * y + col] = acc[x][y][i];
-        // A wave's LDS operations complete in order: its reads below see
-        // these writes, and the next row of blocks overwrites the slice only
-        // after these reads.
-        if (bi < mb) {
-            constexpr int kLanesPerRow = kRowFloats / 4;
-#pragma unroll
-            for (int q = 0; q < 16 * kLanesPerRow / 64; ++q) {
-                const int t = q * 64 + lane, r = t / kLanesPerRow, c4 = 4 * (t % kLanesPerRow);
-                const int64_t bj = bn0 + wn * kWbN + c4 / 16;
-                const f32x4 v = *(__attribute__((address_space(3))) f32x4*)(slice + r * kRowFloats + c4);
-                if (bj < nb)
-                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(c + (16 * bi + r) * n + 16 * (bn0 + wn * kWbN) + c4));
-            }
-        }
-    }
+    // Epilogue: through each wave's own LDS slice of the (now idle) stage
+    // buffers, once every wave is done reading the last stage.
+    stage_barrier();
+    static_assert(kWaves * 16 * kWbN * 16 * 4 <= kBufs * kBufBytes, "the epilogue slices fit in the stage buffers");
+    store_c_blocks<kWbM, kWbN>(acc, (lds_f32*)(lds + wave * 16 * kWbN * 16 * 4), c, n, bm0 + wm * kWbM,
+                               bn0 + wn * kWbN, mb, nb, lane);
 }
 
 }  // namespace
