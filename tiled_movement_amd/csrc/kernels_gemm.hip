@@ -65,7 +65,11 @@ static_assert((kStageFragsA + kStageFragsB) % kWaves == 0, "stage loads split ov
 constexpr int kBufs = SWZ_GEMM_BUFS;
 constexpr int kPerWave = (kStageFragsA + kStageFragsB) / kWaves;  // direct loads per wave per stage
 static_assert(kBufs >= 2 && kBufs <= 4, "two to four stage buffers");
-static_assert(kBufs * kBufBytes <= 160 * 1024, "the stage buffers fit in LDS");
+// The stage buffers, reused by the epilogue's slices once the last stage is
+// done (the slices may need a little more).
+constexpr int kSliceBytes = kWaves * epilogue_slice_bytes<kWbN>();
+constexpr int kLdsBytes = kBufs * kBufBytes > kSliceBytes ? kBufs * kBufBytes : kSliceBytes;
+static_assert(kLdsBytes <= 160 * 1024, "the stage buffers fit in LDS");
 static_assert((kBufs - 2) * kPerWave <= 63, "the load counter holds the loads left in flight");
 
 // Wait until at most `later` stages' loads of this wave are still in flight
@@ -116,7 +120,7 @@ __device__ __forceinline__ void load_stage(const uint8_t* __restrict__ fa, const
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __restrict__ fa,
                                                              const uint8_t* __restrict__ fb, float* __restrict__ c,
                                                              int64_t m, int64_t n, int64_t k, int64_t tile_row0) {
-    __shared__ bf16x8 lds_v[kBufs * kBufBytes / 16];
+    __shared__ bf16x8 lds_v[kLdsBytes / 16];
     lds_u8* lds = (lds_u8*)(reinterpret_cast<uint8_t*>(lds_v));
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / 64);
     const int lane = threadIdx.x % 64;
@@ -189,8 +193,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __res
     // Epilogue: through each wave's own LDS slice of the (now idle) stage
     // buffers, once every wave is done reading the last stage.
     stage_barrier();
-    static_assert(kWaves * 16 * kWbN * 16 * 4 <= kBufs * kBufBytes, "the epilogue slices fit in the stage buffers");
-    store_c_blocks<kWbM, kWbN>(acc, (lds_f32*)(lds + wave * 16 * kWbN * 16 * 4), c, n, bm0 + wm * kWbM,
+    store_c_blocks<kWbM, kWbN>(acc, (lds_f32*)(lds + wave * epilogue_slice_bytes<kWbN>()), c, n, bm0 + wm * kWbM,
                                bn0 + wn * kWbN, mb, nb, lane);
 }
 

@@ -37,9 +37,22 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 #define SWZ_GT_PRIO 0
 #endif
 
-constexpr int kWavesM = 4, kWavesN = 2, kWaves = kWavesM * kWavesN;
+#ifndef SWZ_GT_WAVES_M  // waves along m / n; each wave owns WB_M x WB_N blocks of 16 x 16
+#define SWZ_GT_WAVES_M 4
+#endif
+#ifndef SWZ_GT_WAVES_N
+#define SWZ_GT_WAVES_N 2
+#endif
+#ifndef SWZ_GT_WB_M
+#define SWZ_GT_WB_M 4
+#endif
+#ifndef SWZ_GT_WB_N
+#define SWZ_GT_WB_N 8
+#endif
+
+constexpr int kWavesM = SWZ_GT_WAVES_M, kWavesN = SWZ_GT_WAVES_N, kWaves = kWavesM * kWavesN;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWbM = 4, kWbN = 8;                     // 16x16 blocks per wave
+constexpr int kWbM = SWZ_GT_WB_M, kWbN = SWZ_GT_WB_N;  // 16x16 blocks per wave
 constexpr int kTileRows = 256;                        // rows of A / of B^T per workgroup tile
 constexpr int kTileK = 64;                            // k per stage (two 32-wide steps)
 constexpr int kTileBytes = kTileRows * kTileK * 2;    // one operand tile: 32 KiB
@@ -193,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restri
     // Epilogue: through each wave's own LDS slice of the (now idle) stage
     // buffers, once every wave is done reading the last stage.
     stage_barrier();
-    static_assert(kWaves * 16 * kWbN * 16 * 4 <= 2 * kBufBytes, "the epilogue slices fit in LDS");
-    store_c_blocks<kWbM, kWbN>(acc, (lds_f32*)(lds + wave * 16 * kWbN * 16 * 4), c, n, bm0 + wm * kWbM,
+    static_assert(kWaves * epilogue_slice_bytes<kWbN>() <= 2 * kBufBytes, "the epilogue slices fit in LDS");
+    store_c_blocks<kWbM, kWbN>(acc, (lds_f32*)(lds + wave * epilogue_slice_bytes<kWbN>()), c, n, bm0 + wm * kWbM,
                                bn0 + wn * kWbN, mb, nb, lane);
 }
 
