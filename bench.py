@@ -111,7 +111,7 @@ def time_steps(step, steps, warmup):
     return start.elapsed_time(end), time.perf_counter() - t0
 
 
-def median_rate(step, bytes_per_step, steps=50, warmup=10, batches=3):
+def median_rate(step, bytes_per_step, steps=50, warmup=10, batches=5):
     rates, mss = [], []
     for _ in range(batches):
         ms, _ = time_steps(step, steps, warmup)
@@ -303,6 +303,17 @@ def build(ctx, name, layout):
     raise ValueError(name)
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(a, dst_dev, seconds):
     """The oracle's transpose of the headline input, timed on the host cores
     and bounded to about `seconds` in all: the plain C oracle with one thread
@@ -338,6 +349,7 @@ def cpu_baseline(a, dst_dev, seconds):
                   f"{threads} threads), {t_n:.1f} s",
         "single_thread_GBps": round(v_1, 3),
         "numpy_oracle_GBps": round(v_np, 3),
+        "cpu_model": host_cpu_model(),
         "matches_gpu": bool(np.array_equal(ref.view(np.uint32), got) and np.array_equal(ref_np.view(np.uint32), got)),
     }
 
