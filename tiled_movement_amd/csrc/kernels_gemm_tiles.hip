@@ -18,8 +18,14 @@
 //
 // Workgroup tile 256 x 256 of C, eight waves in 4 x 2, each wave 64 x 128
 // (4 x 8 blocks); two stage buffers of 64 KiB; the same epilogue as the
-// fragment GEMM (accumulators out through swizzled LDS slices as whole
-// 64-byte row runs).
+// fragment GEMM (accumulators out through padded per-wave LDS slices as
+// whole 64-byte row runs).  From sweeps on MI355X at 8192 x 8192 x 4096:
+// four waves of 128 x 128 (one per SIMD) ran 1.10 PFLOP/s against 1.15-1.21
+// for these eight; raising the wave priority around the products and giving
+// each XCD a contiguous run of tiles did not help; with every workgroup
+// reading the same (cache-resident) operands it ran only 3% faster, so the
+// time goes to the schedule around the stage barrier, not to operand
+// latency.
 #include "gemm_epilogue.h"
 #include "launch.h"
 
