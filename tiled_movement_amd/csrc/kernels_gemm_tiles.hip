@@ -20,12 +20,15 @@
 // (4 x 8 blocks); two stage buffers of 64 KiB; the same epilogue as the
 // fragment GEMM (accumulators out through padded per-wave LDS slices as
 // whole 64-byte row runs).  From sweeps on MI355X at 8192 x 8192 x 4096:
-// four waves of 128 x 128 (one per SIMD) ran 1.10 PFLOP/s against 1.15-1.21
-// for these eight; raising the wave priority around the products and giving
-// each XCD a contiguous run of tiles did not help; with every workgroup
-// reading the same (cache-resident) operands it ran only 3% faster, so the
-// time goes to the schedule around the stage barrier, not to operand
-// latency.
+// with every workgroup reading the same (cache-resident) operands the
+// kernel ran only 3% faster, so the time goes to the schedule around the
+// stage barrier, not to operand latency: after each barrier all eight waves
+// asked LDS for fragments at once and the two waves of a SIMD waited
+// together.  Running half of the waves half a stage behind (the ping-pong
+// schedule below) took it from 1.15-1.23 to 1.22-1.28 PFLOP/s.  Four waves
+// of 128 x 128 (one per SIMD) ran 1.10; raising the wave priority around the
+// products, letting only the lagging waves issue the loads and giving each
+// XCD a contiguous run of tiles did not help.
 #include "gemm_epilogue.h"
 #include "launch.h"
 
@@ -41,6 +44,9 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 #endif
 #ifndef SWZ_GT_PRIO  // 1: raise the wave's issue priority while it issues products
 #define SWZ_GT_PRIO 0
+#endif
+#ifndef SWZ_GT_PINGPONG  // 1: the second half of the waves runs half a stage behind the first
+#define SWZ_GT_PINGPONG 1
 #endif
 
 #ifndef SWZ_GT_WAVES_M  // waves along m / n; each wave owns WB_M x WB_N blocks of 16 x 16
@@ -64,10 +70,8 @@ constexpr int kTileK = 64;                            // k per stage (two 32-wid
 constexpr int kTileBytes = kTileRows * kTileK * 2;    // one operand tile: 32 KiB
 constexpr int kBufBytes = 2 * kTileBytes;             // A and B^T of one stage
 constexpr int kChunks = kTileBytes / 16;              // 16-byte slots per operand tile
-constexpr int kLoadsPerThread = kChunks / kThreads;   // per operand per stage
 constexpr int64_t kMaxGridY = 65535;
 static_assert(kWavesM * kWbM * 16 == kTileRows && kWavesN * kWbN * 16 == kTileRows, "wave tiles cover the tile");
-static_assert(kLoadsPerThread * kThreads == kChunks, "direct loads split evenly");
 static_assert(2 * kBufBytes <= 160 * 1024, "two stages fit in LDS");
 
 __device__ __forceinline__ void stage_barrier() {
@@ -82,15 +86,17 @@ __device__ __forceinline__ void stage_barrier() {
 // filled from X's first element (their rows are never stored; their k
 // columns are never multiplied).  swizzle(8(t + 512q)) = swizzle(8t) ^
 // swizzle(4096q): one per-lane base, one wave-uniform XOR per load.
+template <int NT>  // NT threads share the fill; t < NT, wave = t / 64
 __device__ __forceinline__ void fill_tile(const uint8_t* __restrict__ X, int64_t rows, int64_t k, int64_t r0,
                                           int64_t k0, lds_u8* dst, const LdsLayout& L, int t, int wave) {
+    static_assert(kChunks % NT == 0, "the fill splits evenly");
     const uint32_t base = swizzle(static_cast<uint32_t>(8 * t), L.B, L.M, L.S);
 #pragma unroll
-    for (int q = 0; q < kLoadsPerThread; ++q) {
-        const uint32_t e = base ^ swizzle(static_cast<uint32_t>(8 * kThreads * q), L.B, L.M, L.S);
+    for (int q = 0; q < kChunks / NT; ++q) {
+        const uint32_t e = base ^ swizzle(static_cast<uint32_t>(8 * NT * q), L.B, L.M, L.S);
         const int64_t r = r0 + e / kTileK, c = k0 + e % kTileK;
         const uint8_t* g = (r < rows && c < k) ? X + (r * k + c) * 2 : X;
-        __builtin_amdgcn_global_load_lds(g, dst + 16 * (64 * wave + kThreads * q), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(g, dst + 16 * (64 * wave + NT * q), 16, 0, 0);
     }
 }
 
@@ -161,22 +167,89 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restri
         for (int y = 0; y < kWbN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (stages > 0) {
-        fill_tile(a, m, k, r0a, 0, lds, L, t, wave);
-        fill_tile(bt, n, k, r0b, 0, lds + kTileBytes, L, t, wave);
+        fill_tile<kThreads>(a, m, k, r0a, 0, lds, L, t, wave);
+        fill_tile<kThreads>(bt, n, k, r0b, 0, lds + kTileBytes, L, t, wave);
     }
     // Stage s: wait until it has landed (this wave's loads; the barrier
     // covers the others) and every wave is done with stage s - 1, whose
     // buffer the next loads reuse; then start stage s + 1's loads.
     auto begin_stage = [&](int64_t s) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // (LDS reads of the buffer the next loads overwrite have all
+        // returned: their results are used before this point, or, for
+        // fragments held over a barrier, waited for here.)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         stage_barrier();
         if (s + 1 < stages) {
             lds_u8* nxt = lds + ((s + 1) & 1) * kBufBytes;
-            fill_tile(a, m, k, r0a, (s + 1) * kTileK, nxt, L, t, wave);
-            fill_tile(bt, n, k, r0b, (s + 1) * kTileK, nxt + kTileBytes, L, t, wave);
+            fill_tile<kThreads>(a, m, k, r0a, (s + 1) * kTileK, nxt, L, t, wave);
+            fill_tile<kThreads>(bt, n, k, r0b, (s + 1) * kTileK, nxt + kTileBytes, L, t, wave);
         }
     };
     const int64_t full = kb / 2;  // stages with both 32-wide k steps
+#if SWZ_GT_PINGPONG
+    // Waves 0-3 and 4-7 share the SIMDs pairwise.  The first half starts
+    // each stage with its fragment reads; the second half starts it with the
+    // products of the previous stage's second k step, whose fragments it
+    // read before the barrier, so one wave of each SIMD feeds the matrix
+    // unit while the other waits for LDS.  The k steps still accumulate in
+    // increasing order.
+    const bool lag = wave >= kWaves / 2;
+    if (!lag) {
+        for (int64_t s = 0; s < full; ++s) {
+            begin_stage(s);
+            const lds_u8* ta = lds + (s & 1) * kBufBytes;
+            const lds_u8* tb = ta + kTileBytes;
+            bf16x8 a0[kWbM], bq[kWbN], a1[kWbM];
+            read_a(ta, 0, wm, fbase, L, a0);
+            read_b(tb, 0, wn, fbase, L, bq);
+            read_a(ta, 1, wm, fbase, L, a1);
+            if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int y = 0; y < kWbN; ++y) {
+#pragma unroll
+                for (int x = 0; x < kWbM; ++x)
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[x], bq[y], acc[x][y], 0, 0, 0);
+                bq[y] = read_b1(tb, 1, wn, y, fbase, L);
+            }
+            mma_step(acc, a1, bq);
+            if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(0);
+        }
+    } else {
+        bf16x8 a1[kWbM], bq[kWbN];
+        for (int64_t s = 0; s < full; ++s) {
+            begin_stage(s);
+            const lds_u8* ta = lds + (s & 1) * kBufBytes;
+            const lds_u8* tb = ta + kTileBytes;
+            bf16x8 a0[kWbM];
+            read_a(ta, 0, wm, fbase, L, a0);
+            if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(1);
+            if (s > 0) {
+#pragma unroll
+                for (int y = 0; y < kWbN; ++y) {
+#pragma unroll
+                    for (int x = 0; x < kWbM; ++x)
+                        acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[x], bq[y], acc[x][y], 0, 0, 0);
+                    bq[y] = read_b1(tb, 0, wn, y, fbase, L);
+                }
+            } else {
+                read_b(tb, 0, wn, fbase, L, bq);
+            }
+            read_a(ta, 1, wm, fbase, L, a1);
+#pragma unroll
+            for (int y = 0; y < kWbN; ++y) {
+#pragma unroll
+                for (int x = 0; x < kWbM; ++x)
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[x], bq[y], acc[x][y], 0, 0, 0);
+                bq[y] = read_b1(tb, 1, wn, y, fbase, L);
+            }
+            if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(0);
+            // a1 and bq now hold this stage's second k step, multiplied at
+            // the start of the next stage.  Every read of this buffer has
+            // returned before the next barrier (begin_stage waits for them).
+        }
+        if (full > 0) mma_step(acc, a1, bq);
+    }
+#else
     for (int64_t s = 0; s < full; ++s) {
         begin_stage(s);
         const lds_u8* ta = lds + (s & 1) * kBufBytes;
@@ -200,6 +273,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restri
         mma_step(acc, a1, bv);
         if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(0);
     }
+#endif
     if (kb % 2) {  // a last stage with one 32-wide k step
         begin_stage(full);
         const lds_u8* ta = lds + (full & 1) * kBufBytes;
