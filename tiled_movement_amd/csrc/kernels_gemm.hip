@@ -19,7 +19,9 @@
 // step per stage, two stage buffers (64 KiB of LDS): the loads of stage s+1
 // are in flight while stage s is multiplied.  Larger wave tiles spill
 // registers (8 x 8 blocks with two k steps per stage ran at half the rate),
-// and deeper pipelines (three or four buffers) did not help.
+// and deeper pipelines (three or four buffers) did not help.  Running half
+// of the waves one stage's products behind the other half (the ping-pong
+// schedule below, as in the fused GEMM) gained 2-3%.
 #include "gemm_epilogue.h"
 #include "launch.h"
 
@@ -50,6 +52,9 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 #endif
 #ifndef SWZ_GEMM_BUFS  // LDS stage buffers (2 to 4): up to BUFS - 1 stages of loads in flight
 #define SWZ_GEMM_BUFS 2
+#endif
+#ifndef SWZ_GEMM_PINGPONG  // 1: the second half of the waves runs one stage's products behind
+#define SWZ_GEMM_PINGPONG 1
 #endif
 
 constexpr int kWavesM = SWZ_GEMM_WAVES_M, kWavesN = SWZ_GEMM_WAVES_N;
@@ -161,6 +166,75 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __res
     for (int p = 0; p < kBufs - 1; ++p)
         if (p < stages) load_stage(fa, fb, bm0, bn0, mb, nb, kb, p, lds + p * kBufBytes, wave, lane);
 
+#if SWZ_GEMM_PINGPONG
+    static_assert(kStageSteps == 1, "the ping-pong schedule holds one k step over the barrier");
+    // Waves 0-3 and 4-7 share the SIMDs pairwise.  The second half holds
+    // each stage's fragments over the next barrier and multiplies them
+    // while reading the next stage's, so one wave of each SIMD feeds the
+    // matrix unit while the other waits for LDS.  The k steps still
+    // accumulate in increasing order.
+    const bool lag = wave >= kWaves / 2;
+    auto begin = [&](int64_t s) {
+        const int64_t later = stages - 1 - s < kBufs - 2 ? stages - 1 - s : kBufs - 2;
+        wait_stages(static_cast<int>(later));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // held fragments have arrived
+        stage_barrier();
+        if (s + kBufs - 1 < stages)
+            load_stage(fa, fb, bm0, bn0, mb, nb, kb, s + kBufs - 1, lds + ((s + kBufs - 1) % kBufs) * kBufBytes, wave,
+                       lane);
+        return lds + (s % kBufs) * kBufBytes;
+    };
+    auto frag_a = [&](lds_u8* cur, int x) {
+        return *(__attribute__((address_space(3))) bf16x8*)(cur + (wm * kWbM + x) * kFragBytes + lane * 16);
+    };
+    auto frag_b = [&](lds_u8* cur, int y) {
+        return *(__attribute__((address_space(3))) bf16x8*)(cur + (kStageFragsA + wn * kWbN + y) * kFragBytes + lane * 16);
+    };
+    if (!lag) {
+        for (int64_t s = 0; s < stages; ++s) {
+            lds_u8* cur = begin(s);
+            bf16x8 a[kWbM], b[kWbN];
+#pragma unroll
+            for (int x = 0; x < kWbM; ++x) a[x] = frag_a(cur, x);
+#pragma unroll
+            for (int y = 0; y < kWbN; ++y) b[y] = frag_b(cur, y);
+#pragma unroll
+            for (int x = 0; x < kWbM; ++x)
+#pragma unroll
+                for (int y = 0; y < kWbN; ++y)
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
+        }
+    } else {
+        bf16x8 ha[kWbM], hb[kWbN];  // the previous stage's fragments, held over the barrier
+        for (int64_t s = 0; s < stages; ++s) {
+            lds_u8* cur = begin(s);
+            bf16x8 na[kWbM];
+#pragma unroll
+            for (int x = 0; x < kWbM; ++x) na[x] = frag_a(cur, x);
+            if (s > 0) {
+#pragma unroll
+                for (int y = 0; y < kWbN; ++y) {
+#pragma unroll
+                    for (int x = 0; x < kWbM; ++x)
+                        acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[x], hb[y], acc[x][y], 0, 0, 0);
+                    hb[y] = frag_b(cur, y);
+                }
+            } else {
+#pragma unroll
+                for (int y = 0; y < kWbN; ++y) hb[y] = frag_b(cur, y);
+            }
+#pragma unroll
+            for (int x = 0; x < kWbM; ++x) ha[x] = na[x];
+        }
+        if (stages > 0) {
+#pragma unroll
+            for (int x = 0; x < kWbM; ++x)
+#pragma unroll
+                for (int y = 0; y < kWbN; ++y)
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[x], hb[y], acc[x][y], 0, 0, 0);
+        }
+    }
+#else
     for (int64_t s = 0; s < stages; ++s) {
         // Stage s has landed once only the later stages' loads are pending;
         // the barrier then also says every wave is done with stage s - 1,
@@ -189,6 +263,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __res
                     acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
         }
     }
+
+#endif
 
     // Epilogue: through each wave's own LDS slice of the (now idle) stage
     // buffers, once every wave is done reading the last stage.
