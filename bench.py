@@ -14,8 +14,9 @@ device copy, and the CPU oracle as a reported baseline.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
-  python bench.py --workload NAME --layout swizzle|pad|plain|direct [--steps K]
-      time one workload only (used for profiler runs); NAME is one of
+  python bench.py --workload NAME --layout swizzle|pad|plain|direct [--steps K] [--pairs P]
+      time one workload only (used for profiler runs), optionally rotating over
+      exactly P buffer pairs; NAME is one of
       fp32_transpose, fp16_transpose, fp16_transpose_tr, u8_transpose, bf16_convert,
       bf16_stage, map, copy, copy_128, memcpy_d2d, bf16_gemm, bf16_gemm_fused,
       torch_mm_bf16
@@ -88,7 +89,12 @@ def measured_traffic(name):
     return None if rec is None else rec.get("bytes_per_launch")
 
 
+PAIRS_OVERRIDE = None  # --pairs: rotate over exactly this many buffer pairs
+
+
 def n_pairs(bytes_per_pair):
+    if PAIRS_OVERRIDE:
+        return PAIRS_OVERRIDE
     return max(2, -(-CACHE_DEFEAT_BYTES // bytes_per_pair))
 
 
@@ -363,7 +369,11 @@ def main(argv=None):
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=None)
     ap.add_argument("--layout", choices=["swizzle", "pad", "plain", "direct"], default="swizzle")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle leg")
+    ap.add_argument("--pairs", type=int, default=None,
+                    help="rotate over this many source/destination pairs (default: enough for 512 MiB)")
     args = ap.parse_args(argv)
+    global PAIRS_OVERRIDE
+    PAIRS_OVERRIDE = args.pairs
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
               "multi-GPU part: each GPU would run the same kernel on its own shard).", file=sys.stderr)
@@ -412,6 +422,19 @@ def main(argv=None):
                 log(f"{wname}/{lay}: {rate:.1f} GB/s")
                 del s2, inf2
                 ctx.torch.cuda.empty_cache()
+        # The headline and its copy ceiling again with 16 buffer pairs (2 GiB
+        # rotating): no reuse of the Infinity Cache or of address
+        # translations between calls of one pair.
+        saved, PAIRS_OVERRIDE = PAIRS_OVERRIDE, 16
+        for wname in ("fp32_transpose", "copy"):
+            s2, nb2, inf2 = build(ctx, wname, "swizzle")
+            rate, ms2 = median_rate(s2, nb2)
+            extra[f"{wname}/swizzle@16pairs"] = {"GBps": round(rate, 1), "frac": round(rate / HBM_PEAK_GBS, 4),
+                                                 "us_per_step": round(ms2 * 1e3, 2), "buffer_pairs": 16}
+            log(f"{wname}/swizzle, 16 buffer pairs: {rate:.1f} GB/s")
+            del s2, inf2
+            ctx.torch.cuda.empty_cache()
+        PAIRS_OVERRIDE = saved
 
     cpu = None
     if name == "fp32_transpose" and "_io" in info:
