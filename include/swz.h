@@ -64,7 +64,9 @@ enum swz_status {
  * instead: the lane that fills LDS slot p fetches tile element swizzle(p),
  * which places every element exactly where SWIZZLE puts it (the swizzle is
  * its own inverse when |S| >= B).  It needs |S| >= B (or B = 0, plain rows), and
- * 16-byte aligned pointers and row pitches (SWZ_EUNSUPPORTED otherwise). */
+ * 16-byte aligned pointers and row pitches (SWZ_EUNSUPPORTED otherwise; for
+ * the NARROW kinds, whose tiles are contiguous stretches of the input, only
+ * the output row pitch counts). */
 enum swz_layout {
     SWZ_LAYOUT_SWIZZLE = 0,
     SWZ_LAYOUT_PAD = 1,
@@ -91,8 +93,18 @@ enum swz_layout {
  *               consecutive rows of one column per read.  The 1-byte case of
  *               "CUDA 013 - Swizzle 的工作原理", usage example 2 (char rows
  *               with the low bits kept together), here with 8-byte runs.
- *  AUTO       : 4-byte -> SCALAR_COL; 2-byte -> B128_8X8 when cols <= 128,
- *               else B64_TR16 (the faster of the two 64x64 kinds); 1-byte ->
+ *  NARROW1 .. NARROW16 : 4-byte elements in matrices of exactly 1, 2, 4, 8
+ *               or 16 columns.  Each tile is 4096 bytes of whole rows
+ *               (1024/cols rows), contiguous in the source, and its
+ *               transpose is cols output runs of 4096/cols bytes.  A row is
+ *               narrower than a bank row, so the swizzle acts on the flat
+ *               offset and its source bits come from rows above the ones
+ *               that form one 32-element line: it spans several rows
+ *               ("CUDA 013 - Swizzle 的工作原理", usage example 4).  Reads as
+ *               SCALAR_COL: each lane reads four rows of one column.
+ *  AUTO       : 4-byte -> NARROW<cols> when cols is 1, 2, 4, 8 or 16, else
+ *               SCALAR_COL; 2-byte -> B128_8X8 when cols <= 128, else
+ *               B64_TR16 (the faster of the two 64x64 kinds); 1-byte ->
  *               B64_TR8. */
 enum swz_read_kind {
     SWZ_READ_AUTO = -1,
@@ -101,7 +113,12 @@ enum swz_read_kind {
     SWZ_READ_B128_8X8 = 2,
     SWZ_READ_MFMA_16X16X32 = 3,
     SWZ_READ_B64_TR16 = 4,
-    SWZ_READ_B64_TR8 = 5
+    SWZ_READ_B64_TR8 = 5,
+    SWZ_READ_NARROW1 = 6,
+    SWZ_READ_NARROW2 = 7,
+    SWZ_READ_NARROW4 = 8,
+    SWZ_READ_NARROW8 = 9,
+    SWZ_READ_NARROW16 = 10
 };
 
 enum swz_frag_kind { SWZ_FRAG_MFMA_F32_16X16X32_BF16 = 0 };
@@ -150,9 +167,11 @@ int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p, void* 
  * Errors: SWZ_EINVAL (sizes, NULL, overlap, misalignment, a read kind that
  * does not fit elem_bytes, parameters that split a vector or move bits
  * outside the tile, S = 0 with B > 0 (not one-to-one), |S| < B with
- * SWZ_LAYOUT_SWIZZLE_DIRECT); negative S is accepted; SWZ_EUNSUPPORTED for
+ * SWZ_LAYOUT_SWIZZLE_DIRECT, a NARROW kind whose width differs from cols);
+ * negative S is accepted; SWZ_EUNSUPPORTED for
  * SWZ_LAYOUT_SWIZZLE_DIRECT when a pointer or a row pitch (cols * elem_bytes
- * or rows * elem_bytes) is not a multiple of 16 bytes. */
+ * or rows * elem_bytes; only the latter for the NARROW kinds) is not a
+ * multiple of 16 bytes. */
 int swz_transpose(const void* d_src, void* d_dst, int64_t rows, int64_t cols, int32_t elem_bytes,
                   int32_t layout, int32_t read_kind, const swz_params* p_or_null, void* stream);
 

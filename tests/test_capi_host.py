@@ -103,8 +103,8 @@ def test_probe_and_query_validation():
     assert lib.swz_lds_probe(A, B, 4, 4, 2, 8, 4, A + 4096, None) == EINVAL
     assert lib.swz_lds_probe(A, B, 4, 4, 0, 0, 4, A + 4096, None) == EINVAL
     assert lib.swz_lds_probe(A, B, 0, 4, 0, 8, 4, A + 4096, None) == T.SWZ_OK
-    assert lib.swz_predict_conflicts(9, 0, None, ctypes.byref(c), ctypes.byref(c)) == EINVAL
-    assert lib.swz_choose(2, 16, 64, 64, 9, ctypes.byref(P())) == EINVAL
+    assert lib.swz_predict_conflicts(11, 0, None, ctypes.byref(c), ctypes.byref(c)) == EINVAL  # no such kind
+    assert lib.swz_choose(2, 16, 64, 64, 11, ctypes.byref(P())) == EINVAL  # no such kind
     assert lib.swz_choose(2, 16, 64, 32, T.READ_B64_4X4, ctypes.byref(P())) == EUNSUP
     assert lib.swz_bank_model_get(None) == EINVAL
     with pytest.raises(T.SwzError):
@@ -129,10 +129,18 @@ def test_plans():
 # design describes each kernel; coordinates are of the first element.
 
 
+NARROW = (T.READ_NARROW1, T.READ_NARROW2, T.READ_NARROW4, T.READ_NARROW8, T.READ_NARROW16)
+
+
+def plan_cols(kind):
+    """A width the kind accepts: narrow kinds take exactly their row width."""
+    return KIND_GEOM[kind][2] if kind in NARROW else 4096
+
+
 def threads_of(kind):
     op = 1 if kind == T.READ_MFMA_16X16X32 else 0
     esz = KIND_GEOM[kind][0]
-    return T.swz_plan(op, 4096, 4096, esz, "swizzle", kind)["threads"]
+    return T.swz_plan(op, 4096, plan_cols(kind), esz, "swizzle", kind)["threads"]
 
 
 def restated_accesses(kind, write):
@@ -142,7 +150,17 @@ def restated_accesses(kind, write):
     out = []
     for w in range(nt // 64):
         ts = [64 * w + l for l in range(64)]
-        if kind == T.READ_SCALAR_COL:  # 32x32 4-byte tile
+        if kind in NARROW:  # 4096-byte tile of whole rows of C 4-byte elements
+            c_ = KIND_GEOM[kind][2]
+            tr_ = 1024 // c_
+            for j in range(256 // nt):
+                for e in range(4):
+                    if write:  # vector v: flat elements 4v..4v+3, one element per store
+                        coords = [divmod(4 * (t + nt * j) + e, c_) for t in ts]
+                    else:  # piece u: column u // (TR/4), rows 4(u % (TR/4))..+3, one row per load
+                        coords = [(4 * ((t + nt * j) % (tr_ // 4)) + e, (t + nt * j) // (tr_ // 4)) for t in ts]
+                    out.append((coords, 4))
+        elif kind == T.READ_SCALAR_COL:  # 32x32 4-byte tile
             for j in range(256 // nt):
                 for e in range(4):
                     if write:  # vector v: row v/8, columns 4(v%8)..+3, one element per store
@@ -221,6 +239,11 @@ KIND_GEOM = {
     T.READ_MFMA_16X16X32: (2, 256, 64, 8),
     T.READ_B64_TR16: (2, 64, 64, 8),
     T.READ_B64_TR8: (1, 128, 128, 8),
+    T.READ_NARROW1: (4, 1024, 1, 1),
+    T.READ_NARROW2: (4, 512, 2, 1),
+    T.READ_NARROW4: (4, 256, 4, 1),
+    T.READ_NARROW8: (4, 128, 8, 1),
+    T.READ_NARROW16: (4, 64, 16, 1),
 }
 
 
@@ -246,7 +269,8 @@ def test_kernel_accesses_match_restated_lane_maps(kind, layout, params):
     esz, tr, tc, pad = KIND_GEOM[kind]
     if params == "alt":
         params = (3, 0, 6) if esz == 4 else (3, 3, 6)
-    chosen = T.swz_plan(1 if kind == T.READ_MFMA_16X16X32 else 0, 4096, 4096, esz, layout, kind, params)["params"]
+    chosen = T.swz_plan(1 if kind == T.READ_MFMA_16X16X32 else 0, 4096, plan_cols(kind), esz, layout, kind,
+                        params)["params"]
     for write in (1, 0):
         lib_acc = T.swz_kernel_accesses(kind, layout, params, write)
         mine = restated_accesses(kind, write)
@@ -376,6 +400,26 @@ def test_gemm_validation():
     assert f(A, B, C, 0, 32, 32, 0, None) == T.SWZ_OK  # empty: no launch
     assert f(A, B, C, 1 << 40, 1 << 40, 32, 0, None) == EINVAL  # size overflow
 
+
+
+def test_narrow_kind_validation():
+    f = lib.swz_convert_layout
+    # a narrow kind takes exactly its row width; AUTO picks it for 1, 2, 4, 8, 16 columns
+    assert f(A, B, 1, 256, 12, 4, 0, T.READ_NARROW8, None, None) == EINVAL
+    assert f(A, B, 1, 256, 8, 2, 0, T.READ_NARROW8, None, None) == EINVAL  # 4-byte elements only
+    for c, kind in ((1, T.READ_NARROW1), (2, T.READ_NARROW2), (4, T.READ_NARROW4), (8, T.READ_NARROW8),
+                    (16, T.READ_NARROW16)):
+        p = T.swz_plan(0, 1000, c, 4, "swizzle")
+        assert p["read_kind"] == kind and p["tile"] == (1024 // c, c) and p["lds_bytes"] == 4096
+    for c in (3, 12, 32, 64):
+        assert T.swz_plan(0, 1000, c, 4, "swizzle")["read_kind"] == T.READ_SCALAR_COL
+    # whole-row tiles need only the output pitch aligned for the vector path
+    assert T.swz_plan(0, 4096, 1, 4, "swizzle")["aligned"] and T.swz_plan(0, 4096, 2, 4, "direct")["aligned"]
+    assert not T.swz_plan(0, 4093, 8, 4, "swizzle")["aligned"]
+    assert f(A, B, 1, 4093, 8, 4, T.LAYOUT_SWIZZLE_DIRECT, T.READ_NARROW8, None, None) == EUNSUP
+    # the flat-offset swizzle spans rows: Swizzle<5,0,5> on a 128x8 tile XORs
+    # row bits 2-6 into the element bits (the pages' int num[32][8] example)
+    assert T.swz_choose(4, 4, 128, 8, T.READ_NARROW8) == (5, 0, 5)
 
 
 def test_fused_gemm_validation():

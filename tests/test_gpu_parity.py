@@ -212,6 +212,65 @@ def test_auto_read_kind():
         assert np.array_equal(from_dev(dst, a), O.convert_layout(a))
 
 
+# --------------------------------------- narrow rows (1, 2, 4, 8 or 16 columns)
+NARROW_KINDS = [(T.READ_NARROW1, 1), (T.READ_NARROW2, 2), (T.READ_NARROW4, 4), (T.READ_NARROW8, 8),
+                (T.READ_NARROW16, 16)]
+
+
+@pytest.mark.parametrize("kind,c", NARROW_KINDS)
+@pytest.mark.parametrize("layout", LAYOUTS + ["direct"])
+def test_narrow_rows(kind, c, layout):
+    """Whole-row tiles of 1024 / c rows, the swizzle spanning several rows:
+    whole tiles, ragged last tiles, fewer rows than one tile, empty."""
+    tr = 1024 // c
+    for seed, rows in enumerate([3 * tr, 2 * tr + 4, 2 * tr + 3, tr - 4, 5, 1, 0]):
+        if layout == "direct" and rows % 4:
+            continue  # the direct fill needs a 16-byte output pitch (rows * 4 bytes)
+        announce("narrow", kind, layout, rows, c)
+        check_transpose(W.fp32_matrix(rows, c, seed=seed), 4, layout, kind)
+
+
+@pytest.mark.parametrize("kind,c", NARROW_KINDS)
+def test_narrow_auto_unaligned_and_batched(kind, c):
+    rows = 3 * (1024 // c) + 9
+    assert T.swz_plan(0, rows, c, 4)["read_kind"] == kind
+    a = W.fp32_matrix(rows, c, seed=c)
+    announce("narrow auto", c)
+    check_transpose(a, 4, "swizzle", T.READ_AUTO)
+    # one element off a 16-byte boundary on both sides
+    flat = to_dev(a.reshape(-1))
+    buf = torch.empty(a.size + 1, dtype=flat.dtype, device=DEV)
+    buf[1:] = flat
+    out = torch.empty(a.size + 1, dtype=flat.dtype, device=DEV)
+    announce("narrow unaligned", c)
+    T.swz_transpose(buf[1:], out[1:], rows, c, 4, "swizzle", kind)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out[1:], a).reshape(c, rows), O.transpose(a))
+    # a batch of narrow matrices
+    b = W.fp32_matrix(3 * 200, c, seed=c + 1).reshape(3, 200, c)
+    for layout in LAYOUTS:
+        announce("narrow batch", c, layout)
+        src = to_dev(b)
+        dst = torch.empty((3, c, 200), dtype=src.dtype, device=DEV)
+        T.swz_convert_layout(src, dst, 3, 200, c, 4, layout, kind)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(dst, b), O.convert_layout(b))
+
+
+@pytest.mark.parametrize("kind,c", NARROW_KINDS)
+def test_narrow_any_valid_swizzle(kind, c):
+    """Every admissible (B, M, S) of either sign moves data only inside LDS."""
+    a = W.fp32_matrix(2 * (1024 // c) + 8, c, seed=30 + c)
+    rng = np.random.default_rng(c)
+    triples = [(B, M, S) for B in range(1, 6) for M in range(0, 5) for S in range(-9, 10)
+               if S != 0 and M + B <= 10 and (M + B if S > 0 else M - S + B) <= 10]
+    for idx in rng.choice(len(triples), size=12, replace=False):
+        B, M, S = triples[idx]
+        for layout in ("swizzle", "direct") if abs(S) >= B else ("swizzle",):
+            announce("narrow params", c, layout, (B, M, S))
+            check_transpose(a, 4, layout, kind, (B, M, S))
+
+
 # ------------------------------------------------------- operand staging
 
 
@@ -292,6 +351,14 @@ def test_full_operand_staging(layout):
 
 
 # ---------------------------------------------------- the reference copy
+
+
+@pytest.mark.parametrize("layout", LAYOUTS + ["direct"])
+def test_full_fp32_narrow8(layout):
+    """fp32 [2^21][8] -> [8][2^21] (64 MiB), the narrow-row workload."""
+    a = W.fp32_matrix(1 << 21, 8, seed=0)
+    announce("full narrow8", layout)
+    check_transpose(a, 4, layout, T.READ_AUTO)
 
 
 def test_reference_copy():

@@ -23,6 +23,7 @@ SWZ_OK, SWZ_EINVAL, SWZ_EUNSUPPORTED, SWZ_EHIP = 0, -1, -2, -3
 LAYOUT_SWIZZLE, LAYOUT_PAD, LAYOUT_PLAIN, LAYOUT_SWIZZLE_DIRECT = 0, 1, 2, 3
 READ_AUTO, READ_SCALAR_COL, READ_B64_4X4, READ_B128_8X8, READ_MFMA_16X16X32, READ_B64_TR16, READ_B64_TR8 = (
     -1, 0, 1, 2, 3, 4, 5)
+READ_NARROW1, READ_NARROW2, READ_NARROW4, READ_NARROW8, READ_NARROW16 = 6, 7, 8, 9, 10
 FRAG_MFMA_F32_16X16X32_BF16 = 0
 LAYOUTS = {"swizzle": LAYOUT_SWIZZLE, "pad": LAYOUT_PAD, "plain": LAYOUT_PLAIN, "direct": LAYOUT_SWIZZLE_DIRECT}
 

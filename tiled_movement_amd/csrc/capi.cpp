@@ -59,16 +59,27 @@ int resolve_layout(int kind, int32_t layout, const swz_params* p, swz_params* q,
 }
 
 // Resolve read kind, layout and parameters into a plan; shared by the calls
-// and by swz_plan.
+// and by swz_plan.  aligned_out: pointers and the output row pitch allow
+// 16-byte vectors; aligned_in: so does the input row pitch.  Whole-row
+// (narrow) tiles are contiguous stretches of the input, so they need only
+// the first.
 int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, int32_t read_kind,
-              const swz_params* p, bool aligned, swz_plan_info* out) {
+              const swz_params* p, bool aligned_out, bool aligned_in, swz_plan_info* out) {
     if (layout < SWZ_LAYOUT_SWIZZLE || layout > SWZ_LAYOUT_SWIZZLE_DIRECT) return SWZ_EINVAL;
     int kind = read_kind;
     if (op == 0) {
         if (esz != 1 && esz != 2 && esz != 4) return SWZ_EINVAL;
-        if (kind == SWZ_READ_AUTO)
-            kind = esz == 4 ? SWZ_READ_SCALAR_COL
-                            : esz == 1 ? SWZ_READ_B64_TR8 : (cols <= 128 ? SWZ_READ_B128_8X8 : SWZ_READ_B64_TR16);
+        if (kind == SWZ_READ_AUTO) {
+            if (esz == 4)
+                kind = cols == 1   ? SWZ_READ_NARROW1
+                       : cols == 2 ? SWZ_READ_NARROW2
+                       : cols == 4 ? SWZ_READ_NARROW4
+                       : cols == 8 ? SWZ_READ_NARROW8
+                       : cols == 16 ? SWZ_READ_NARROW16
+                                    : SWZ_READ_SCALAR_COL;
+            else
+                kind = esz == 1 ? SWZ_READ_B64_TR8 : (cols <= 128 ? SWZ_READ_B128_8X8 : SWZ_READ_B64_TR16);
+        }
         if (kind == SWZ_READ_MFMA_16X16X32) return SWZ_EINVAL;
     } else {
         if (esz != 2) return SWZ_EINVAL;
@@ -78,6 +89,8 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     KindInfo k;
     if (!swz::kind_info(kind, &k)) return SWZ_EINVAL;
     if (k.esz != esz) return SWZ_EINVAL;
+    if (swz::is_narrow(kind) && cols != k.tc) return SWZ_EINVAL;  // whole rows per tile
+    const bool aligned = aligned_out && (aligned_in || swz::is_narrow(kind));
 
     swz_params q;
     int pad;
@@ -136,8 +149,8 @@ SWZ_API int swz_plan(int32_t op, int64_t rows, int64_t cols, int32_t elem_bytes,
     if (!out || (op != 0 && op != 1) || rows < 0 || cols < 0) return SWZ_EINVAL;
     if (op == 1 && (rows % 16 || cols % 32)) return SWZ_EINVAL;
     // Pointers are taken as 16-byte aligned; the row pitches decide the rest.
-    const bool aligned = op == 1 || ((cols * elem_bytes) % 16 == 0 && (rows * elem_bytes) % 16 == 0);
-    return make_plan(op, rows, cols, elem_bytes, layout, read_kind, p_or_null, aligned, out);
+    return make_plan(op, rows, cols, elem_bytes, layout, read_kind, p_or_null, op == 1 || (rows * elem_bytes) % 16 == 0,
+                     op == 1 || (cols * elem_bytes) % 16 == 0, out);
 }
 
 SWZ_API int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, int64_t rows, int64_t cols,
@@ -148,15 +161,17 @@ SWZ_API int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, in
     int64_t n, n2, bytes;
     if (!mul_ok(batch, rows, &n) || !mul_ok(n, cols, &n2) || !mul_ok(n2, elem_bytes, &bytes)) return SWZ_EINVAL;
     const auto ps = reinterpret_cast<uintptr_t>(d_src), pd = reinterpret_cast<uintptr_t>(d_dst);
-    const bool aligned = ps % 16 == 0 && pd % 16 == 0 && (cols * elem_bytes) % 16 == 0 && (rows * elem_bytes) % 16 == 0;
     swz_plan_info pl;
-    const int st = make_plan(0, rows, cols, elem_bytes, layout, read_kind, p_or_null, aligned, &pl);
+    const int st = make_plan(0, rows, cols, elem_bytes, layout, read_kind, p_or_null,
+                             ps % 16 == 0 && pd % 16 == 0 && (rows * elem_bytes) % 16 == 0,
+                             (cols * elem_bytes) % 16 == 0, &pl);
     if (st != SWZ_OK) return st;
     if (bytes == 0) return SWZ_OK;
     if (!d_src || !d_dst) return SWZ_EINVAL;
     if (ps % elem_bytes || pd % elem_bytes) return SWZ_EINVAL;
     if (overlaps(d_src, bytes, d_dst, bytes)) return SWZ_EINVAL;
-    swz::ConvertJob job{d_src, d_dst, batch, rows, cols, layout_of(pl), aligned, layout == SWZ_LAYOUT_SWIZZLE_DIRECT};
+    swz::ConvertJob job{d_src, d_dst, batch, rows, cols, layout_of(pl), pl.aligned != 0,
+                        layout == SWZ_LAYOUT_SWIZZLE_DIRECT};
     return hip_status(swz::launch_convert(pl.read_kind, job, static_cast<hipStream_t>(stream)));
 }
 
@@ -172,7 +187,7 @@ SWZ_API int swz_stage_operand(const void* d_src, void* d_frag, int64_t mn, int64
     int64_t n, bytes;
     if (!mul_ok(mn, k, &n) || !mul_ok(n, 2, &bytes)) return SWZ_EINVAL;
     swz_plan_info pl;
-    const int st = make_plan(1, mn, k, elem_bytes, layout, SWZ_READ_MFMA_16X16X32, p_or_null, true, &pl);
+    const int st = make_plan(1, mn, k, elem_bytes, layout, SWZ_READ_MFMA_16X16X32, p_or_null, true, true, &pl);
     if (st != SWZ_OK) return st;
     if (bytes == 0) return SWZ_OK;
     if (!d_src || !d_frag) return SWZ_EINVAL;
@@ -206,7 +221,7 @@ SWZ_API int swz_gemm(const void* d_a, const void* d_bt, float* d_c, int64_t m, i
     if (layout == SWZ_LAYOUT_PAD) return SWZ_EUNSUPPORTED;  // the direct fill writes whole rows
     swz_plan_info pl;
     const int st = make_plan(1, m, k, 2, layout == SWZ_LAYOUT_SWIZZLE ? SWZ_LAYOUT_SWIZZLE_DIRECT : layout,
-                             SWZ_READ_MFMA_16X16X32, p_or_null, true, &pl);
+                             SWZ_READ_MFMA_16X16X32, p_or_null, true, true, &pl);
     if (st != SWZ_OK) return st;
     int64_t a_elems, b_elems, c_elems, a_bytes, b_bytes, c_bytes;
     if (!mul_ok(m, k, &a_elems) || !mul_ok(n, k, &b_elems) || !mul_ok(m, n, &c_elems)) return SWZ_EINVAL;

@@ -111,6 +111,11 @@ int kernel_accesses(int kind, uint32_t ld, swz_params p, bool direct, bool write
             return accesses_kind<SWZ_READ_MFMA_16X16X32>(ld, p, direct, write, addrs, max_acc, width);
         case SWZ_READ_B64_TR16: return accesses_kind<SWZ_READ_B64_TR16>(ld, p, direct, write, addrs, max_acc, width);
         case SWZ_READ_B64_TR8: return accesses_kind<SWZ_READ_B64_TR8>(ld, p, direct, write, addrs, max_acc, width);
+        case SWZ_READ_NARROW1: return accesses_kind<SWZ_READ_NARROW1>(ld, p, direct, write, addrs, max_acc, width);
+        case SWZ_READ_NARROW2: return accesses_kind<SWZ_READ_NARROW2>(ld, p, direct, write, addrs, max_acc, width);
+        case SWZ_READ_NARROW4: return accesses_kind<SWZ_READ_NARROW4>(ld, p, direct, write, addrs, max_acc, width);
+        case SWZ_READ_NARROW8: return accesses_kind<SWZ_READ_NARROW8>(ld, p, direct, write, addrs, max_acc, width);
+        case SWZ_READ_NARROW16: return accesses_kind<SWZ_READ_NARROW16>(ld, p, direct, write, addrs, max_acc, width);
         default: return -1;
     }
 }
@@ -129,6 +134,11 @@ bool kind_info(int kind, KindInfo* o) {
         SWZ_KIND_CASE(SWZ_READ_MFMA_16X16X32)
         SWZ_KIND_CASE(SWZ_READ_B64_TR16)
         SWZ_KIND_CASE(SWZ_READ_B64_TR8)
+        SWZ_KIND_CASE(SWZ_READ_NARROW1)
+        SWZ_KIND_CASE(SWZ_READ_NARROW2)
+        SWZ_KIND_CASE(SWZ_READ_NARROW4)
+        SWZ_KIND_CASE(SWZ_READ_NARROW8)
+        SWZ_KIND_CASE(SWZ_READ_NARROW16)
 #undef SWZ_KIND_CASE
         default:
             return false;
@@ -152,6 +162,11 @@ void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64
         case SWZ_READ_MFMA_16X16X32: predict_kind<SWZ_READ_MFMA_16X16X32>(m, ld, p, direct, wcyc, rcyc); break;
         case SWZ_READ_B64_TR16: predict_kind<SWZ_READ_B64_TR16>(m, ld, p, direct, wcyc, rcyc); break;
         case SWZ_READ_B64_TR8: predict_kind<SWZ_READ_B64_TR8>(m, ld, p, direct, wcyc, rcyc); break;
+        case SWZ_READ_NARROW1: predict_kind<SWZ_READ_NARROW1>(m, ld, p, direct, wcyc, rcyc); break;
+        case SWZ_READ_NARROW2: predict_kind<SWZ_READ_NARROW2>(m, ld, p, direct, wcyc, rcyc); break;
+        case SWZ_READ_NARROW4: predict_kind<SWZ_READ_NARROW4>(m, ld, p, direct, wcyc, rcyc); break;
+        case SWZ_READ_NARROW8: predict_kind<SWZ_READ_NARROW8>(m, ld, p, direct, wcyc, rcyc); break;
+        case SWZ_READ_NARROW16: predict_kind<SWZ_READ_NARROW16>(m, ld, p, direct, wcyc, rcyc); break;
         default: *wcyc = *rcyc = -1;
     }
 }
@@ -224,7 +239,7 @@ swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles) {
 
 swz_params cached_choice(int kind) {
     static std::once_flag once;
-    constexpr int kKinds = SWZ_READ_B64_TR8 + 1;
+    constexpr int kKinds = SWZ_READ_NARROW16 + 1;
     static swz_params table[kKinds];
     std::call_once(once, [] {
         for (int kd = 0; kd < kKinds; ++kd) table[kd] = choose_for_kind(kd, gfx950_bank_model(), nullptr);

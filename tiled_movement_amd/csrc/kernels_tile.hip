@@ -165,6 +165,9 @@ __device__ __forceinline__ void store16_guarded(uint8_t* D, int64_t row, int64_t
 #ifndef SWZ_OCC_TR8
 #define SWZ_OCC_TR8 5
 #endif
+#ifndef SWZ_OCC_NARROW
+#define SWZ_OCC_NARROW 0
+#endif
 
 template <int KIND>
 constexpr int occupancy_limit() {
@@ -173,7 +176,8 @@ constexpr int occupancy_limit() {
            : KIND == SWZ_READ_B128_8X8 ? SWZ_OCC_B128
            : KIND == SWZ_READ_MFMA_16X16X32 ? SWZ_OCC_STAGE
            : KIND == SWZ_READ_B64_TR16 ? SWZ_OCC_TR16
-                                       : SWZ_OCC_TR8;
+           : KIND == SWZ_READ_B64_TR8  ? SWZ_OCC_TR8
+                                       : SWZ_OCC_NARROW;
 }
 
 constexpr int kLdsPerCu = 160 * 1024;
@@ -279,6 +283,8 @@ __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ S, int64_t
         c -= c % PER;  // the vector's first column
         if (FULL)
             v[j] = gload16(S + ((r0 + r) * cols + c0 + c) * K::ESZ);
+        else if (is_narrow(KIND))  // whole-row tiles: a vector may span rows, guard the flat index
+            v[j] = load16_guarded<K::ESZ>(S, 0, (r0 + r) * cols + c0 + c, 1, rows * cols);
         else
             v[j] = load16_guarded<K::ESZ>(S, r0 + r, c0 + c, rows, cols);
     }
@@ -332,7 +338,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
                                                uint8_t* __restrict__ D, int64_t rows, int64_t cols, int64_t r0,
                                                int64_t c0, int t) {
     using K = Kind<KIND>;
-    if constexpr (KIND == SWZ_READ_SCALAR_COL) {
+    if constexpr (KIND == SWZ_READ_SCALAR_COL || is_narrow(KIND)) {
         // Task j: four rows of one source column -> 16 bytes of an output row.
 #pragma unroll
         for (int j = 0; j < K::TASKS; ++j) {
@@ -663,6 +669,11 @@ hipError_t launch_convert(int kind, const ConvertJob& j, hipStream_t stream) {
         case SWZ_READ_B128_8X8: return launch_kind<SWZ_READ_B128_8X8>(j, stream);
         case SWZ_READ_B64_TR16: return launch_kind<SWZ_READ_B64_TR16>(j, stream);
         case SWZ_READ_B64_TR8: return launch_kind<SWZ_READ_B64_TR8>(j, stream);
+        case SWZ_READ_NARROW1: return launch_kind<SWZ_READ_NARROW1>(j, stream);
+        case SWZ_READ_NARROW2: return launch_kind<SWZ_READ_NARROW2>(j, stream);
+        case SWZ_READ_NARROW4: return launch_kind<SWZ_READ_NARROW4>(j, stream);
+        case SWZ_READ_NARROW8: return launch_kind<SWZ_READ_NARROW8>(j, stream);
+        case SWZ_READ_NARROW16: return launch_kind<SWZ_READ_NARROW16>(j, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -29,6 +29,9 @@
 #ifndef SWZ_NT_TR8
 #define SWZ_NT_TR8 256
 #endif
+#ifndef SWZ_NT_NARROW
+#define SWZ_NT_NARROW 256
+#endif
 
 namespace swz {
 
@@ -246,6 +249,49 @@ template <> struct Kind<SWZ_READ_B64_TR8> {
     }
 };
 
+// 4-byte elements in narrow rows of C = 1, 2, 4, 8 or 16 columns, whole rows
+// per tile: TR = 1024 / C rows of C, 4096 bytes, one contiguous stretch of the
+// source.  A row is narrower than a bank row, so the tile is treated as the
+// flat offsets r*C + c and the swizzle's source field comes from the row
+// bits above the ones that make up a 32-element line: it spans several rows
+// ("CUDA 013 - Swizzle 的工作原理", usage example 4, int num[32][8] taken four
+// rows at a time).  Staging: vector v = t + NT*j is flat elements 4v..4v+3
+// (a row piece for C >= 4, several whole rows below), stored as four 4-byte
+// LDS writes.  Read: task
+// u = t + NT*j owns column u / (TR/4) and rows 4(u % (TR/4)) .. +3, read as
+// four 4-byte loads and written as 16 bytes of output row u / (TR/4); each
+// output row is a run of TR elements, 4096 / C bytes.
+template <int C>
+struct NarrowKind {
+    static_assert(C == 1 || C == 2 || C == 4 || C == 8 || C == 16, "narrow rows of 1 to 16 elements");
+    static constexpr int ESZ = 4, TR = 1024 / C, TC = C, NT = SWZ_NT_NARROW;
+    static constexpr int VEC = 4;
+    static constexpr int RWIDTH = 4;
+    static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
+    static constexpr int WSTEPS = GLOADS * 4;
+    static constexpr int TASKS = TR * TC / 4 / NT;
+    static constexpr int RSTEPS = TASKS * 4;
+    __host__ __device__ static constexpr void wcoord(int t, int i, int& r, int& c) {
+        const int e = 4 * (t + NT * (i / 4)) + i % 4;
+        r = e / C;
+        c = e % C;
+    }
+    __host__ __device__ static constexpr void rcoord(int t, int i, int& r, int& c) {
+        const int u = t + NT * (i / 4);
+        r = 4 * (u % (TR / 4)) + i % 4;
+        c = u / (TR / 4);
+    }
+};
+template <> struct Kind<SWZ_READ_NARROW1> : NarrowKind<1> {};
+template <> struct Kind<SWZ_READ_NARROW2> : NarrowKind<2> {};
+template <> struct Kind<SWZ_READ_NARROW4> : NarrowKind<4> {};
+template <> struct Kind<SWZ_READ_NARROW8> : NarrowKind<8> {};
+template <> struct Kind<SWZ_READ_NARROW16> : NarrowKind<16> {};
+
+__host__ __device__ constexpr bool is_narrow(int kind) {
+    return kind >= SWZ_READ_NARROW1 && kind <= SWZ_READ_NARROW16;
+}
+
 // ---------------------------------------------------------------------------
 // Offsets of a lane's later steps from its first one.
 //
@@ -327,6 +373,15 @@ static_assert(Kind<SWZ_READ_B64_TR8>::GLOADS * Kind<SWZ_READ_B64_TR8>::NT * 16 =
               "8-bit transpose-read thread count");
 static_assert(steps_decompose<SWZ_READ_B64_TR8, true>(false) && steps_decompose<SWZ_READ_B64_TR8, false>(),
               "8-bit transpose-read lane map");
+template <int KIND>
+constexpr bool narrow_ok() {
+    using K = Kind<KIND>;
+    return even_split<KIND>() && K::TASKS * K::NT * 4 == K::TR * K::TC && steps_decompose<KIND, true>() &&
+           steps_decompose<KIND, false>();
+}
+static_assert(narrow_ok<SWZ_READ_NARROW1>() && narrow_ok<SWZ_READ_NARROW2>() && narrow_ok<SWZ_READ_NARROW4>() &&
+                  narrow_ok<SWZ_READ_NARROW8>() && narrow_ok<SWZ_READ_NARROW16>(),
+              "narrow-row lane maps and thread counts");
 
 // ---------------------------------------------------------------------------
 // Direct fill (SWZ_LAYOUT_SWIZZLE_DIRECT): the tile goes from HBM straight
@@ -363,7 +418,10 @@ constexpr bool direct_split() {
 }
 static_assert(direct_split<SWZ_READ_SCALAR_COL>() && direct_split<SWZ_READ_B64_4X4>() &&
                   direct_split<SWZ_READ_B128_8X8>() && direct_split<SWZ_READ_MFMA_16X16X32>() &&
-                  direct_split<SWZ_READ_B64_TR16>() && direct_split<SWZ_READ_B64_TR8>(),
+                  direct_split<SWZ_READ_B64_TR16>() && direct_split<SWZ_READ_B64_TR8>() &&
+                  direct_split<SWZ_READ_NARROW1>() && direct_split<SWZ_READ_NARROW2>() &&
+                  direct_split<SWZ_READ_NARROW4>() && direct_split<SWZ_READ_NARROW8>() &&
+                  direct_split<SWZ_READ_NARROW16>(),
               "direct fill split");
 
 }  // namespace swz
