@@ -349,6 +349,9 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             int r = 0, c = 0;
             K::rcoord(t, 4 * j, r, c);
             const int64_t orow = c0 + c, ocol = r0 + r;
+            // Assembled from four loads, the vector is otherwise rebuilt at
+            // the store in a way that drops the store's non-temporal hint.
+            asm volatile("" : "+v"(o));
             if (FULL)
                 gstore16(D + (orow * rows + ocol) * 4, o);
             else
