@@ -139,6 +139,33 @@ __device__ __forceinline__ void store16_guarded(uint8_t* D, int64_t row, int64_t
     }
 }
 
+// How a tile's 16-byte pieces are guarded at the matrix edge.  kFull: the
+// whole tile is inside, no guards.  kVec: the tile sticks out, but every row
+// pitch is a multiple of 16 bytes, so each piece is wholly inside or wholly
+// outside the matrix: one test per piece, whole-vector accesses.  kElem: row
+// pitches that are not multiples of 16 bytes: element by element.
+enum Edge { kFull = 0, kVec = 1, kElem = 2 };
+
+template <int EDGE, int ESZ>
+__device__ __forceinline__ u32x4 load16_edge(const uint8_t* S, int64_t row, int64_t col, int64_t rows,
+                                             int64_t cols) {
+    if constexpr (EDGE == kFull) return gload16(S + (row * cols + col) * ESZ);
+    if constexpr (EDGE == kVec) return row < rows && col < cols ? gload16(S + (row * cols + col) * ESZ) : u32x4{0u, 0u, 0u, 0u};
+    return load16_guarded<ESZ>(S, row, col, rows, cols);
+}
+
+template <int EDGE, int ESZ>
+__device__ __forceinline__ void store16_edge(uint8_t* D, int64_t row, int64_t col, int64_t nrows, int64_t ncols,
+                                             u32x4 v) {
+    if constexpr (EDGE == kFull) {
+        gstore16(D + (row * ncols + col) * ESZ, v);
+    } else if constexpr (EDGE == kVec) {
+        if (row < nrows && col < ncols) gstore16(D + (row * ncols + col) * ESZ, v);
+    } else {
+        store16_guarded<ESZ>(D, row, col, nrows, ncols, v);
+    }
+}
+
 // Workgroups per CU.  The transposed HBM pattern of the 16-bit and 8-bit
 // tiles runs faster with fewer tiles in flight (measured with an LDS-free
 // probe of the same pattern: 64 x 64 16-bit tiles at 8 to 16 workgroups per
@@ -269,9 +296,9 @@ __device__ __forceinline__ void direct_fill(const uint8_t* __restrict__ S, int64
 // Transpose / layout conversion of one tile.
 // ---------------------------------------------------------------------------
 
-// Global loads of one tile into registers.  FULL: unguarded 16-byte loads
-// (whole tile inside the matrix, 16-byte aligned rows); else per element.
-template <int KIND, bool FULL>
+// Global loads of one tile into registers, guarded at the matrix edge as EDGE
+// says (Edge above).
+template <int KIND, int EDGE>
 __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ S, int64_t rows, int64_t cols, int64_t r0,
                                           int64_t c0, int t, u32x4* v) {
     using K = Kind<KIND>;
@@ -281,12 +308,10 @@ __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ S, int64_t
         int r = 0, c = 0;
         K::wcoord(t, j * (K::WSTEPS / K::GLOADS), r, c);
         c -= c % PER;  // the vector's first column
-        if (FULL)
-            v[j] = gload16(S + ((r0 + r) * cols + c0 + c) * K::ESZ);
-        else if (is_narrow(KIND))  // whole-row tiles: a vector may span rows, guard the flat index
-            v[j] = load16_guarded<K::ESZ>(S, 0, (r0 + r) * cols + c0 + c, 1, rows * cols);
+        if (is_narrow(KIND))  // whole-row tiles: a vector may span rows, guard the flat index
+            v[j] = load16_edge<EDGE, K::ESZ>(S, 0, (r0 + r) * cols + c0 + c, 1, rows * cols);
         else
-            v[j] = load16_guarded<K::ESZ>(S, r0 + r, c0 + c, rows, cols);
+            v[j] = load16_edge<EDGE, K::ESZ>(S, r0 + r, c0 + c, rows, cols);
     }
 }
 
@@ -332,8 +357,8 @@ __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const Ld
 }
 
 // Read this thread's pieces of the tile back from LDS, transposed, and store
-// them to the output.  FULL: unguarded 16-byte stores.
-template <int KIND, bool PADDED, bool FULL>
+// them to the output, guarded at the matrix edge as EDGE says.
+template <int KIND, bool PADDED, int EDGE>
 __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbase, const LdsLayout& L,
                                                uint8_t* __restrict__ D, int64_t rows, int64_t cols, int64_t r0,
                                                int64_t c0, int t) {
@@ -352,10 +377,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             // Assembled from four loads, the vector is otherwise rebuilt at
             // the store in a way that drops the store's non-temporal hint.
             asm volatile("" : "+v"(o));
-            if (FULL)
-                gstore16(D + (orow * rows + ocol) * 4, o);
-            else
-                store16_guarded<4>(D, orow, ocol, cols, rows, o);
+            store16_edge<EDGE, 4>(D, orow, ocol, cols, rows, o);
         }
     } else if constexpr (KIND == SWZ_READ_B64_TR8) {
         // Task j: in each of two steps h the 8-bit transpose read gives this
@@ -388,10 +410,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             const u32x4 o = upper ? u32x4{got[0], got[1], h[1][0], h[1][1]} : u32x4{h[0][0], h[0][1], got[0], got[1]};
             const int64_t orow = c0 + 8 * ch + q % 8;
             const int64_t ocol = r0 + (upper ? 64 : 0) + 16 * g;
-            if (FULL)
-                gstore16(D + orow * rows + ocol, o);
-            else
-                store16_guarded<1>(D, orow, ocol, cols, rows, o);
+            store16_edge<EDGE, 1>(D, orow, ocol, cols, rows, o);
         }
     } else if constexpr (KIND == SWZ_READ_B64_TR16) {
         // Task j: two transpose reads give this lane 8 consecutive rows of
@@ -424,10 +443,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             const int ch = t / 64 + (K::NT / 64) * j;
             const int64_t orow = c0 + 8 * ch + 4 * ((q / 4) % 2) + q % 4;
             const int64_t ocol = r0 + 16 * g + 8 * (q / 8);
-            if (FULL)
-                gstore16(D + (orow * rows + ocol) * 2, o);
-            else
-                store16_guarded<2>(D, orow, ocol, cols, rows, o);
+            store16_edge<EDGE, 2>(D, orow, ocol, cols, rows, o);
         }
     } else {
         // Task j: 8 rows of a column block; transpose 16-bit elements in
@@ -447,30 +463,28 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
                 const u32x4 o{pair_col(x[0], x[1], q), pair_col(x[2], x[3], q), pair_col(x[4], x[5], q),
                               pair_col(x[6], x[7], q)};
                 const int64_t orow = c0 + cb + q, ocol = r0 + rb;
-                if (FULL)
-                    gstore16(D + (orow * rows + ocol) * 2, o);
-                else
-                    store16_guarded<2>(D, orow, ocol, cols, rows, o);
+                store16_edge<EDGE, 2>(D, orow, ocol, cols, rows, o);
             }
         }
     }
 }
 
-template <int KIND, int FILL, bool FULL>
+template <int KIND, int FILL, int EDGE>
 __device__ __forceinline__ void convert_tile(const uint8_t* __restrict__ S, uint8_t* __restrict__ D, int64_t rows,
                                              int64_t cols, int64_t r0, int64_t c0, uint8_t* lds, uint32_t wbase,
                                              uint32_t rbase, const LdsLayout& L, int t) {
     using K = Kind<KIND>;
     constexpr bool PADDED = FILL == kPadded;
     if constexpr (FILL == kDirect) {
-        direct_fill<KIND, FULL>(S, rows, cols, r0, c0, lds, L, t);
+        static_assert(EDGE != kElem, "the direct fill needs 16-byte aligned rows");
+        direct_fill<KIND, EDGE == kFull>(S, rows, cols, r0, c0, lds, L, t);
     } else {
         u32x4 v[K::GLOADS];
-        load_tile<KIND, FULL>(S, rows, cols, r0, c0, t, v);
+        load_tile<KIND, EDGE>(S, rows, cols, r0, c0, t, v);
         lds_store<KIND, PADDED>(lds, wbase, L, v);
     }
     __syncthreads();
-    lds_read_store<KIND, PADDED, FULL>(lds, rbase, L, D, rows, cols, r0, c0, t);
+    lds_read_store<KIND, PADDED, EDGE>(lds, rbase, L, D, rows, cols, r0, c0, t);
 }
 
 // Which tile this workgroup moves.  GRID3D: blockIdx = (tile row, tile
@@ -514,10 +528,14 @@ __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __res
     const int64_t r0 = tr * K::TR, c0 = tc * K::TC;
     const uint8_t* S = src + b * plane;
     uint8_t* D = dst + b * plane;
-    if (ALIGNED && r0 + K::TR <= rows && c0 + K::TC <= cols)
-        convert_tile<KIND, FILL, true>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
-    else
-        convert_tile<KIND, FILL, false>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
+    if constexpr (ALIGNED) {
+        if (r0 + K::TR <= rows && c0 + K::TC <= cols)
+            convert_tile<KIND, FILL, kFull>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
+        else
+            convert_tile<KIND, FILL, kVec>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
+    } else {
+        convert_tile<KIND, FILL, kElem>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
+    }
 }
 
 // ---------------------------------------------------------------------------
