@@ -53,9 +53,13 @@ enum swz_status {
 };
 
 /* Layout of a tile in LDS.  PAD and PLAIN are the ablations: PAD adds one
- * element (4-byte elements) or one 16-byte vector (2-byte elements) to each
- * row ("CUDA 013 - Swizzle 的工作原理", section 如何避免 Bank Conflict, the
- * 32x33 array); PLAIN is the row-major tile with no remapping.
+ * LDS store's width to each row: one element where the tile is staged an
+ * element at a time (4-byte elements), else one vector (16 bytes for the
+ * 2-byte tile kinds, 8 for the 8-bit one, 4 for the narrow-row kinds of
+ * smaller elements) ("CUDA 013 - Swizzle 的工作原理", section 如何避免 Bank
+ * Conflict, the 32x33 array); SWZ_EUNSUPPORTED for narrow rows under 4
+ * bytes (HNARROW1, BNARROW1, BNARROW2), whose 4-byte stores span rows.
+ * PLAIN is the row-major tile with no remapping.
  * SWIZZLE_DIRECT is the SWIZZLE layout filled without a trip through
  * registers: the tile moves from HBM straight into LDS (the gfx950 direct
  * load, the role cp.async plays in "NVIDIA CuTe Swizzle" and "CuTe Swizzle
@@ -65,8 +69,8 @@ enum swz_status {
  * which places every element exactly where SWIZZLE puts it (the swizzle is
  * its own inverse when |S| >= B).  It needs |S| >= B (or B = 0, plain rows), and
  * 16-byte aligned pointers and row pitches (SWZ_EUNSUPPORTED otherwise; for
- * the NARROW kinds, whose tiles are contiguous stretches of the input, only
- * the output row pitch counts). */
+ * the narrow-row kinds (NARROW, HNARROW, BNARROW), whose tiles are
+ * contiguous stretches of the input, only the output row pitch counts). */
 enum swz_layout {
     SWZ_LAYOUT_SWIZZLE = 0,
     SWZ_LAYOUT_PAD = 1,
@@ -102,10 +106,21 @@ enum swz_layout {
  *               that form one 32-element line: it spans several rows
  *               ("CUDA 013 - Swizzle 的工作原理", usage example 4).  Reads as
  *               SCALAR_COL: each lane reads four rows of one column.
+ *  HNARROW1 .. HNARROW32 : the same for 2-byte elements in matrices of 1,
+ *               2, 4, 8, 16 or 32 columns: 4096-byte tiles of 2048/cols
+ *               rows.  Staged as 4-byte LDS writes (so M >= 1); each lane
+ *               reads eight rows of one column with 2-byte loads and writes
+ *               them as 16 bytes of one output row.
+ *  BNARROW1 .. BNARROW64 : the same for 1-byte elements in matrices of 1 to
+ *               64 columns (powers of two): 4096-byte tiles of 4096/cols
+ *               rows, 4-byte LDS writes (M >= 2), 16 rows of one column per
+ *               lane read with 1-byte loads.
  *  AUTO       : 4-byte -> NARROW<cols> when cols is 1, 2, 4, 8 or 16, else
- *               SCALAR_COL; 2-byte -> B128_8X8 when cols <= 128, else
- *               B64_TR16 (the faster of the two 64x64 kinds); 1-byte ->
- *               B64_TR8. */
+ *               SCALAR_COL; 2-byte -> HNARROW<cols> when cols is a power of
+ *               two up to 32, else B64_TR16 when cols <= 64, B128_8X8 when
+ *               cols <= 128, B64_TR16 above (the faster of the two 64x64
+ *               kinds); 1-byte -> BNARROW<cols> when cols is a power of two
+ *               up to 64, else B64_TR8. */
 enum swz_read_kind {
     SWZ_READ_AUTO = -1,
     SWZ_READ_SCALAR_COL = 0,
@@ -118,7 +133,20 @@ enum swz_read_kind {
     SWZ_READ_NARROW2 = 7,
     SWZ_READ_NARROW4 = 8,
     SWZ_READ_NARROW8 = 9,
-    SWZ_READ_NARROW16 = 10
+    SWZ_READ_NARROW16 = 10,
+    SWZ_READ_HNARROW1 = 11,
+    SWZ_READ_HNARROW2 = 12,
+    SWZ_READ_HNARROW4 = 13,
+    SWZ_READ_HNARROW8 = 14,
+    SWZ_READ_HNARROW16 = 15,
+    SWZ_READ_HNARROW32 = 16,
+    SWZ_READ_BNARROW1 = 17,
+    SWZ_READ_BNARROW2 = 18,
+    SWZ_READ_BNARROW4 = 19,
+    SWZ_READ_BNARROW8 = 20,
+    SWZ_READ_BNARROW16 = 21,
+    SWZ_READ_BNARROW32 = 22,
+    SWZ_READ_BNARROW64 = 23
 };
 
 enum swz_frag_kind { SWZ_FRAG_MFMA_F32_16X16X32_BF16 = 0 };
@@ -167,10 +195,10 @@ int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p, void* 
  * Errors: SWZ_EINVAL (sizes, NULL, overlap, misalignment, a read kind that
  * does not fit elem_bytes, parameters that split a vector or move bits
  * outside the tile, S = 0 with B > 0 (not one-to-one), |S| < B with
- * SWZ_LAYOUT_SWIZZLE_DIRECT, a NARROW kind whose width differs from cols);
- * negative S is accepted; SWZ_EUNSUPPORTED for
+ * SWZ_LAYOUT_SWIZZLE_DIRECT, a narrow-row kind whose width differs from
+ * cols); negative S is accepted; SWZ_EUNSUPPORTED for
  * SWZ_LAYOUT_SWIZZLE_DIRECT when a pointer or a row pitch (cols * elem_bytes
- * or rows * elem_bytes; only the latter for the NARROW kinds) is not a
+ * or rows * elem_bytes; only the latter for the narrow-row kinds) is not a
  * multiple of 16 bytes. */
 int swz_transpose(const void* d_src, void* d_dst, int64_t rows, int64_t cols, int32_t elem_bytes,
                   int32_t layout, int32_t read_kind, const swz_params* p_or_null, void* stream);

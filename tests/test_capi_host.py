@@ -103,8 +103,8 @@ def test_probe_and_query_validation():
     assert lib.swz_lds_probe(A, B, 4, 4, 2, 8, 4, A + 4096, None) == EINVAL
     assert lib.swz_lds_probe(A, B, 4, 4, 0, 0, 4, A + 4096, None) == EINVAL
     assert lib.swz_lds_probe(A, B, 0, 4, 0, 8, 4, A + 4096, None) == T.SWZ_OK
-    assert lib.swz_predict_conflicts(11, 0, None, ctypes.byref(c), ctypes.byref(c)) == EINVAL  # no such kind
-    assert lib.swz_choose(2, 16, 64, 64, 11, ctypes.byref(P())) == EINVAL  # no such kind
+    assert lib.swz_predict_conflicts(24, 0, None, ctypes.byref(c), ctypes.byref(c)) == EINVAL  # no such kind
+    assert lib.swz_choose(2, 16, 64, 64, 24, ctypes.byref(P())) == EINVAL  # no such kind
     assert lib.swz_choose(2, 16, 64, 32, T.READ_B64_4X4, ctypes.byref(P())) == EUNSUP
     assert lib.swz_bank_model_get(None) == EINVAL
     with pytest.raises(T.SwzError):
@@ -129,7 +129,12 @@ def test_plans():
 # design describes each kernel; coordinates are of the first element.
 
 
-NARROW = (T.READ_NARROW1, T.READ_NARROW2, T.READ_NARROW4, T.READ_NARROW8, T.READ_NARROW16)
+NARROW4 = (T.READ_NARROW1, T.READ_NARROW2, T.READ_NARROW4, T.READ_NARROW8, T.READ_NARROW16)
+NARROW2 = (T.READ_HNARROW1, T.READ_HNARROW2, T.READ_HNARROW4, T.READ_HNARROW8, T.READ_HNARROW16, T.READ_HNARROW32)
+NARROW1 = (T.READ_BNARROW1, T.READ_BNARROW2, T.READ_BNARROW4, T.READ_BNARROW8, T.READ_BNARROW16, T.READ_BNARROW32,
+           T.READ_BNARROW64)
+NARROW = NARROW4 + NARROW2 + NARROW1
+NO_PAD = (T.READ_HNARROW1, T.READ_BNARROW1, T.READ_BNARROW2)  # rows under one 4-byte LDS store
 
 
 def plan_cols(kind):
@@ -150,16 +155,19 @@ def restated_accesses(kind, write):
     out = []
     for w in range(nt // 64):
         ts = [64 * w + l for l in range(64)]
-        if kind in NARROW:  # 4096-byte tile of whole rows of C 4-byte elements
-            c_ = KIND_GEOM[kind][2]
-            tr_ = 1024 // c_
-            for j in range(256 // nt):
-                for e in range(4):
-                    if write:  # vector v: flat elements 4v..4v+3, one element per store
-                        coords = [divmod(4 * (t + nt * j) + e, c_) for t in ts]
-                    else:  # piece u: column u // (TR/4), rows 4(u % (TR/4))..+3, one row per load
-                        coords = [(4 * ((t + nt * j) % (tr_ // 4)) + e, (t + nt * j) // (tr_ // 4)) for t in ts]
-                    out.append((coords, 4))
+        if kind in NARROW:  # 4096-byte tile of whole rows of C elements of esz bytes
+            esz_, tr_, c_, _ = KIND_GEOM[kind]
+            per = 16 // esz_  # elements per 16 bytes
+            if write:  # vector v: flat elements per*v .., one 4-byte word per store
+                for j in range(256 // nt):
+                    for e in range(4):
+                        coords = [divmod(per * (t + nt * j) + e * (4 // esz_), c_) for t in ts]
+                        out.append((coords, 4))
+            else:  # piece u: column u // (TR/per), rows per*(u % (TR/per)) .., one row per load
+                for j in range(256 // nt):
+                    for e in range(per):
+                        coords = [(per * ((t + nt * j) % (tr_ // per)) + e, (t + nt * j) // (tr_ // per)) for t in ts]
+                        out.append((coords, esz_))
         elif kind == T.READ_SCALAR_COL:  # 32x32 4-byte tile
             for j in range(256 // nt):
                 for e in range(4):
@@ -244,6 +252,8 @@ KIND_GEOM = {
     T.READ_NARROW4: (4, 256, 4, 1),
     T.READ_NARROW8: (4, 128, 8, 1),
     T.READ_NARROW16: (4, 64, 16, 1),
+    **{k: (2, 2048 // c, c, 2) for k, c in zip(NARROW2, (1, 2, 4, 8, 16, 32))},
+    **{k: (1, 4096 // c, c, 4) for k, c in zip(NARROW1, (1, 2, 4, 8, 16, 32, 64))},
 }
 
 
@@ -257,6 +267,10 @@ def oracle_model():
             groups.setdefault(ph, []).append(lane)
         bm = O.BankModel(g["n_banks"], g["bank_bytes"], 64, {width: [groups[k] for k in sorted(groups)]})
         (read if dname == "read" else write)[width] = bm
+    # Reading: 1- and 2-byte loads are served like 4-byte ones, lanes that
+    # touch the same 4-byte word sharing it (the library's model does this).
+    for w in (1, 2):
+        read[w] = O.BankModel(read[4].n_banks, read[4].bank_bytes, 64, {w: read[4].phase_groups(4)})
     return O.LdsModel(read, write)
 
 
@@ -267,6 +281,10 @@ LAYOUT_CASES = [("swizzle", None), ("pad", None), ("plain", None), ("swizzle", "
 @pytest.mark.parametrize("layout,params", LAYOUT_CASES)
 def test_kernel_accesses_match_restated_lane_maps(kind, layout, params):
     esz, tr, tc, pad = KIND_GEOM[kind]
+    if layout == "pad" and kind in NO_PAD:
+        with pytest.raises(T.SwzError):
+            T.swz_kernel_accesses(kind, layout, None, 1)
+        return
     if params == "alt":
         params = (3, 0, 6) if esz == 4 else (3, 3, 6)
     chosen = T.swz_plan(1 if kind == T.READ_MFMA_16X16X32 else 0, 4096, plan_cols(kind), esz, layout, kind,
@@ -284,6 +302,10 @@ def test_kernel_accesses_match_restated_lane_maps(kind, layout, params):
 @pytest.mark.parametrize("kind", list(KIND_GEOM))
 @pytest.mark.parametrize("layout", ["swizzle", "pad", "plain"])
 def test_predictor_matches_oracle_counter(kind, layout):
+    if layout == "pad" and kind in NO_PAD:
+        with pytest.raises(T.SwzError):
+            T.swz_predict_conflicts(kind, layout)
+        return
     model = oracle_model()
     wc, rc = T.swz_predict_conflicts(kind, layout)
     ow = sum(O.conflict_report(a, w, model.for_access(w, True))[0] for a, w in T.swz_kernel_accesses(kind, layout, None, 1))
@@ -298,7 +320,7 @@ def test_chooser_matches_oracle_chooser(kind):
     the pages' own choices under their bank model) picks the same triple,
     and it is predicted conflict-free."""
     esz, tr, tc, _ = KIND_GEOM[kind]
-    vec = {4: 4, 2: 16, 1: 8}[esz]
+    vec = 4 if kind in NARROW else {4: 4, 2: 16, 1: 8}[esz]
     (b, m, s), cyc = O.choose(esz, vec, tr, tc, restated_accesses(kind, 1), restated_accesses(kind, 0), oracle_model())
     assert T.swz_choose(esz, vec, tr, tc, kind) == (b, m, s)
     assert cyc == 0
@@ -349,7 +371,7 @@ def test_direct_validation():
 def test_direct_fill_writes_lane_linear_and_reads_like_swizzle(kind):
     esz, tr, tc, _ = KIND_GEOM[kind]
     nt = threads_of(kind)
-    vb = 16 if esz == 2 else 4
+    vb = 16 if esz == 2 and kind not in NARROW else 4
     loads = tr * tc * esz // vb // nt
     acc = T.swz_kernel_accesses(kind, "direct", None, 1)
     assert len(acc) == loads * nt // 64
@@ -372,8 +394,10 @@ def test_direct_fill_places_every_element_where_swizzle_does(kind):
     and for every S >= B the chooser could emit -- so the fill reproduces
     the swizzled tile exactly, and covers each element once."""
     esz, tr, tc, _ = KIND_GEOM[kind]
-    epl = {4: 1, 2: 8, 1: 4}[esz]
-    m_min = 0 if esz == 4 else 3
+    vb = 16 if esz == 2 and kind not in NARROW else 4  # bytes per direct load
+    epl = vb // esz
+    # M keeps a load's elements together (and, for the 8-bit kind, its 8-byte LDS writes)
+    m_min = (epl.bit_length() - 1) if kind in NARROW or esz != 1 else 3
     log_tile = (tr * tc).bit_length() - 1
     for B, M, S in [(b, m, s) for b in range(1, 6) for m in (m_min, m_min + 1) for s in range(b, 8)
                     if m + b <= log_tile]:
@@ -413,6 +437,27 @@ def test_narrow_kind_validation():
         assert p["read_kind"] == kind and p["tile"] == (1024 // c, c) and p["lds_bytes"] == 4096
     for c in (3, 12, 32, 64):
         assert T.swz_plan(0, 1000, c, 4, "swizzle")["read_kind"] == T.READ_SCALAR_COL
+    # 2- and 1-byte elements: whole-row tiles for rows of up to 64 bytes
+    for esz, kinds in ((2, NARROW2), (1, NARROW1)):
+        for i, kind in enumerate(kinds):
+            c = 1 << i
+            p = T.swz_plan(0, 1000, c, esz, "swizzle")
+            assert p["read_kind"] == kind and p["tile"] == (4096 // esz // c, c) and p["lds_bytes"] == 4096
+            assert p["vec_bytes"] == 4 and p["params"][1] == {2: 1, 1: 2}[esz]
+        assert f(A, B, 1, 256, 2 * c, esz, 0, kinds[-1], None, None) == EINVAL  # width differs
+        assert f(A, B, 1, 256, c, 6 - esz, 0, kinds[-1], None, None) == EINVAL  # element size differs
+    assert T.swz_plan(0, 1000, 64, 2)["read_kind"] == T.READ_B64_TR16
+    assert T.swz_plan(0, 1000, 48, 2)["read_kind"] == T.READ_B64_TR16
+    assert T.swz_plan(0, 1000, 128, 2)["read_kind"] == T.READ_B128_8X8
+    assert T.swz_plan(0, 1000, 96, 1)["read_kind"] == T.READ_B64_TR8
+    assert T.swz_plan(0, 1000, 128, 1)["read_kind"] == T.READ_B64_TR8
+    # rows under one 4-byte LDS store get no padded layout
+    for kind, c, esz in ((T.READ_HNARROW1, 1, 2), (T.READ_BNARROW1, 1, 1), (T.READ_BNARROW2, 2, 1)):
+        assert f(A, B, 1, 256, c, esz, T.LAYOUT_PAD, kind, None, None) == EUNSUP
+    assert T.swz_plan(0, 256, 4, 1, "pad")["pad_elems"] == 4 and T.swz_plan(0, 256, 2, 2, "pad")["pad_elems"] == 2
+    # M too small to keep a 4-byte LDS write whole
+    assert f(A, B, 1, 256, 8, 2, 0, T.READ_HNARROW8, ctypes.byref(P(4, 0, 5)), None) == EINVAL
+    assert f(A, B, 1, 256, 8, 1, 0, T.READ_BNARROW8, ctypes.byref(P(4, 1, 5)), None) == EINVAL
     # whole-row tiles need only the output pitch aligned for the vector path
     assert T.swz_plan(0, 4096, 1, 4, "swizzle")["aligned"] and T.swz_plan(0, 4096, 2, 4, "direct")["aligned"]
     assert not T.swz_plan(0, 4093, 8, 4, "swizzle")["aligned"]

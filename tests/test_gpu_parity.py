@@ -212,63 +212,77 @@ def test_auto_read_kind():
         assert np.array_equal(from_dev(dst, a), O.convert_layout(a))
 
 
-# --------------------------------------- narrow rows (1, 2, 4, 8 or 16 columns)
-NARROW_KINDS = [(T.READ_NARROW1, 1), (T.READ_NARROW2, 2), (T.READ_NARROW4, 4), (T.READ_NARROW8, 8),
-                (T.READ_NARROW16, 16)]
+# ------------------------------- narrow rows (whole-row tiles, 1 to 64 bytes)
+GEN = {4: W.fp32_matrix, 2: W.fp16_matrix, 1: W.u8_matrix}
+NARROW_KINDS = ([(k, 4, c) for k, c in zip((T.READ_NARROW1, T.READ_NARROW2, T.READ_NARROW4, T.READ_NARROW8,
+                                             T.READ_NARROW16), (1, 2, 4, 8, 16))] +
+                [(k, 2, c) for k, c in zip((T.READ_HNARROW1, T.READ_HNARROW2, T.READ_HNARROW4, T.READ_HNARROW8,
+                                             T.READ_HNARROW16, T.READ_HNARROW32), (1, 2, 4, 8, 16, 32))] +
+                [(k, 1, c) for k, c in zip((T.READ_BNARROW1, T.READ_BNARROW2, T.READ_BNARROW4, T.READ_BNARROW8,
+                                             T.READ_BNARROW16, T.READ_BNARROW32, T.READ_BNARROW64),
+                                            (1, 2, 4, 8, 16, 32, 64))])
 
 
-@pytest.mark.parametrize("kind,c", NARROW_KINDS)
+@pytest.mark.parametrize("kind,esz,c", NARROW_KINDS)
 @pytest.mark.parametrize("layout", LAYOUTS + ["direct"])
-def test_narrow_rows(kind, c, layout):
-    """Whole-row tiles of 1024 / c rows, the swizzle spanning several rows:
-    whole tiles, ragged last tiles, fewer rows than one tile, empty."""
-    tr = 1024 // c
-    for seed, rows in enumerate([3 * tr, 2 * tr + 4, 2 * tr + 3, tr - 4, 5, 1, 0]):
-        if layout == "direct" and rows % 4:
-            continue  # the direct fill needs a 16-byte output pitch (rows * 4 bytes)
+def test_narrow_rows(kind, esz, c, layout):
+    """Whole-row tiles of 4096 bytes, the swizzle spanning several rows:
+    whole tiles, ragged last tiles (on and off a 16-byte output pitch),
+    fewer rows than one tile, empty."""
+    tr = 4096 // esz // c
+    if layout == "pad" and c * esz < 4:  # rows under one 4-byte LDS store get no pad
+        with pytest.raises(T.SwzError):
+            check_transpose(GEN[esz](tr, c, seed=0), esz, layout, kind)
+        return
+    for seed, rows in enumerate([3 * tr, 2 * tr + 16, 2 * tr + 4, 2 * tr + 3, tr - 16, tr - 4, 5, 1, 0]):
+        if layout == "direct" and (rows * esz) % 16:
+            continue  # the direct fill needs a 16-byte output pitch
         announce("narrow", kind, layout, rows, c)
-        check_transpose(W.fp32_matrix(rows, c, seed=seed), 4, layout, kind)
+        check_transpose(GEN[esz](rows, c, seed=seed), esz, layout, kind)
 
 
-@pytest.mark.parametrize("kind,c", NARROW_KINDS)
-def test_narrow_auto_unaligned_and_batched(kind, c):
-    rows = 3 * (1024 // c) + 9
-    assert T.swz_plan(0, rows, c, 4)["read_kind"] == kind
-    a = W.fp32_matrix(rows, c, seed=c)
-    announce("narrow auto", c)
-    check_transpose(a, 4, "swizzle", T.READ_AUTO)
+@pytest.mark.parametrize("kind,esz,c", NARROW_KINDS)
+def test_narrow_auto_unaligned_and_batched(kind, esz, c):
+    rows = 3 * (4096 // esz // c) + 9
+    assert T.swz_plan(0, rows, c, esz)["read_kind"] == kind
+    a = GEN[esz](rows, c, seed=c)
+    announce("narrow auto", esz, c)
+    check_transpose(a, esz, "swizzle", T.READ_AUTO)
     # one element off a 16-byte boundary on both sides
     flat = to_dev(a.reshape(-1))
     buf = torch.empty(a.size + 1, dtype=flat.dtype, device=DEV)
     buf[1:] = flat
     out = torch.empty(a.size + 1, dtype=flat.dtype, device=DEV)
-    announce("narrow unaligned", c)
-    T.swz_transpose(buf[1:], out[1:], rows, c, 4, "swizzle", kind)
+    announce("narrow unaligned", esz, c)
+    T.swz_transpose(buf[1:], out[1:], rows, c, esz, "swizzle", kind)
     torch.cuda.synchronize()
     assert np.array_equal(from_dev(out[1:], a).reshape(c, rows), O.transpose(a))
     # a batch of narrow matrices
-    b = W.fp32_matrix(3 * 200, c, seed=c + 1).reshape(3, 200, c)
-    for layout in LAYOUTS:
-        announce("narrow batch", c, layout)
+    b = GEN[esz](3 * 208, c, seed=c + 1).reshape(3, 208, c)
+    for layout in [x for x in LAYOUTS + ["direct"] if x != "pad" or c * esz >= 4]:
+        announce("narrow batch", esz, c, layout)
         src = to_dev(b)
-        dst = torch.empty((3, c, 200), dtype=src.dtype, device=DEV)
-        T.swz_convert_layout(src, dst, 3, 200, c, 4, layout, kind)
+        dst = torch.empty((3, c, 208), dtype=src.dtype, device=DEV)
+        T.swz_convert_layout(src, dst, 3, 208, c, esz, layout, kind)
         torch.cuda.synchronize()
         assert np.array_equal(from_dev(dst, b), O.convert_layout(b))
 
 
-@pytest.mark.parametrize("kind,c", NARROW_KINDS)
-def test_narrow_any_valid_swizzle(kind, c):
-    """Every admissible (B, M, S) of either sign moves data only inside LDS."""
-    a = W.fp32_matrix(2 * (1024 // c) + 8, c, seed=30 + c)
-    rng = np.random.default_rng(c)
-    triples = [(B, M, S) for B in range(1, 6) for M in range(0, 5) for S in range(-9, 10)
-               if S != 0 and M + B <= 10 and (M + B if S > 0 else M - S + B) <= 10]
+@pytest.mark.parametrize("kind,esz,c", NARROW_KINDS)
+def test_narrow_any_valid_swizzle(kind, esz, c):
+    """Every admissible (B, M, S) of either sign moves data only inside LDS
+    (M keeps the 4-byte LDS writes whole: M >= log2(4 / esz))."""
+    a = GEN[esz](2 * (4096 // esz // c) + 16, c, seed=30 + c)
+    rng = np.random.default_rng(c + 100 * esz)
+    log_tile = (4096 // esz).bit_length() - 1
+    m_min = {4: 0, 2: 1, 1: 2}[esz]
+    triples = [(B, M, S) for B in range(1, 6) for M in range(m_min, 5) for S in range(-9, 10)
+               if S != 0 and M + B <= log_tile and (M + B if S > 0 else M - S + B) <= log_tile]
     for idx in rng.choice(len(triples), size=12, replace=False):
         B, M, S = triples[idx]
         for layout in ("swizzle", "direct") if abs(S) >= B else ("swizzle",):
-            announce("narrow params", c, layout, (B, M, S))
-            check_transpose(a, 4, layout, kind, (B, M, S))
+            announce("narrow params", esz, c, layout, (B, M, S))
+            check_transpose(a, esz, layout, kind, (B, M, S))
 
 
 # ------------------------------------------------------- operand staging
@@ -359,6 +373,16 @@ def test_full_fp32_narrow8(layout):
     a = W.fp32_matrix(1 << 21, 8, seed=0)
     announce("full narrow8", layout)
     check_transpose(a, 4, layout, T.READ_AUTO)
+
+
+@pytest.mark.parametrize("esz,c", [(2, 8), (1, 16)])
+@pytest.mark.parametrize("layout", ["swizzle", "direct"])
+def test_full_small_narrow(esz, c, layout):
+    """fp16 [2^22][8] and u8 [2^22][16] (64 MiB each), whole-row tiles of
+    2- and 1-byte elements."""
+    a = GEN[esz](1 << 22, c, seed=1)
+    announce("full small narrow", esz, c, layout)
+    check_transpose(a, esz, layout, T.READ_AUTO)
 
 
 def test_reference_copy():

@@ -24,6 +24,9 @@ LAYOUT_SWIZZLE, LAYOUT_PAD, LAYOUT_PLAIN, LAYOUT_SWIZZLE_DIRECT = 0, 1, 2, 3
 READ_AUTO, READ_SCALAR_COL, READ_B64_4X4, READ_B128_8X8, READ_MFMA_16X16X32, READ_B64_TR16, READ_B64_TR8 = (
     -1, 0, 1, 2, 3, 4, 5)
 READ_NARROW1, READ_NARROW2, READ_NARROW4, READ_NARROW8, READ_NARROW16 = 6, 7, 8, 9, 10
+READ_HNARROW1, READ_HNARROW2, READ_HNARROW4, READ_HNARROW8, READ_HNARROW16, READ_HNARROW32 = 11, 12, 13, 14, 15, 16
+READ_BNARROW1, READ_BNARROW2, READ_BNARROW4, READ_BNARROW8, READ_BNARROW16, READ_BNARROW32, READ_BNARROW64 = (
+    17, 18, 19, 20, 21, 22, 23)
 FRAG_MFMA_F32_16X16X32_BF16 = 0
 LAYOUTS = {"swizzle": LAYOUT_SWIZZLE, "pad": LAYOUT_PAD, "plain": LAYOUT_PLAIN, "direct": LAYOUT_SWIZZLE_DIRECT}
 

@@ -52,7 +52,14 @@ int resolve_layout(int kind, int32_t layout, const swz_params* p, swz_params* q,
                 *q = swz::cached_choice(kind);
             }
             return SWZ_OK;
-        case SWZ_LAYOUT_PAD: *pad = swz::pad_elems(kind); return SWZ_OK;
+        case SWZ_LAYOUT_PAD: {
+            // A row narrower than one 4-byte LDS write cannot get a pad of
+            // its own: the write would straddle the gap.
+            KindInfo k;
+            if (swz::is_narrow(kind) && swz::kind_info(kind, &k) && k.tc * k.esz < 4) return SWZ_EUNSUPPORTED;
+            *pad = swz::pad_elems(kind);
+            return SWZ_OK;
+        }
         case SWZ_LAYOUT_PLAIN: return SWZ_OK;
         default: return SWZ_EINVAL;
     }
@@ -70,15 +77,18 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     if (op == 0) {
         if (esz != 1 && esz != 2 && esz != 4) return SWZ_EINVAL;
         if (kind == SWZ_READ_AUTO) {
+            // whole-row tiles for rows of 1 to 64 bytes (a power of two)
+            const bool narrow = cols >= 1 && (cols & (cols - 1)) == 0 && cols * esz <= 64;
+            const int lc = ilog2(cols);
             if (esz == 4)
-                kind = cols == 1   ? SWZ_READ_NARROW1
-                       : cols == 2 ? SWZ_READ_NARROW2
-                       : cols == 4 ? SWZ_READ_NARROW4
-                       : cols == 8 ? SWZ_READ_NARROW8
-                       : cols == 16 ? SWZ_READ_NARROW16
-                                    : SWZ_READ_SCALAR_COL;
+                kind = narrow ? SWZ_READ_NARROW1 + lc : SWZ_READ_SCALAR_COL;
+            else if (esz == 2)
+                kind = narrow        ? SWZ_READ_HNARROW1 + lc
+                       : cols <= 64  ? SWZ_READ_B64_TR16
+                       : cols <= 128 ? SWZ_READ_B128_8X8
+                                     : SWZ_READ_B64_TR16;
             else
-                kind = esz == 1 ? SWZ_READ_B64_TR8 : (cols <= 128 ? SWZ_READ_B128_8X8 : SWZ_READ_B64_TR16);
+                kind = narrow ? SWZ_READ_BNARROW1 + lc : SWZ_READ_B64_TR8;
         }
         if (kind == SWZ_READ_MFMA_16X16X32) return SWZ_EINVAL;
     } else {

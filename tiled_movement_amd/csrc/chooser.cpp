@@ -103,46 +103,16 @@ int accesses_kind(uint32_t ld, swz_params p, bool direct, bool write, int32_t* a
 
 int kernel_accesses(int kind, uint32_t ld, swz_params p, bool direct, bool write, int32_t* addrs, int max_acc,
                     int* width) {
-    switch (kind) {
-        case SWZ_READ_SCALAR_COL: return accesses_kind<SWZ_READ_SCALAR_COL>(ld, p, direct, write, addrs, max_acc, width);
-        case SWZ_READ_B64_4X4: return accesses_kind<SWZ_READ_B64_4X4>(ld, p, direct, write, addrs, max_acc, width);
-        case SWZ_READ_B128_8X8: return accesses_kind<SWZ_READ_B128_8X8>(ld, p, direct, write, addrs, max_acc, width);
-        case SWZ_READ_MFMA_16X16X32:
-            return accesses_kind<SWZ_READ_MFMA_16X16X32>(ld, p, direct, write, addrs, max_acc, width);
-        case SWZ_READ_B64_TR16: return accesses_kind<SWZ_READ_B64_TR16>(ld, p, direct, write, addrs, max_acc, width);
-        case SWZ_READ_B64_TR8: return accesses_kind<SWZ_READ_B64_TR8>(ld, p, direct, write, addrs, max_acc, width);
-        case SWZ_READ_NARROW1: return accesses_kind<SWZ_READ_NARROW1>(ld, p, direct, write, addrs, max_acc, width);
-        case SWZ_READ_NARROW2: return accesses_kind<SWZ_READ_NARROW2>(ld, p, direct, write, addrs, max_acc, width);
-        case SWZ_READ_NARROW4: return accesses_kind<SWZ_READ_NARROW4>(ld, p, direct, write, addrs, max_acc, width);
-        case SWZ_READ_NARROW8: return accesses_kind<SWZ_READ_NARROW8>(ld, p, direct, write, addrs, max_acc, width);
-        case SWZ_READ_NARROW16: return accesses_kind<SWZ_READ_NARROW16>(ld, p, direct, write, addrs, max_acc, width);
-        default: return -1;
-    }
+    int n = -1;
+    with_kind(kind, [&](auto kd) { n = accesses_kind<decltype(kd)::value>(ld, p, direct, write, addrs, max_acc, width); });
+    return n;
 }
 
 bool kind_info(int kind, KindInfo* o) {
-    switch (kind) {
-#define SWZ_KIND_CASE(KD)                                                                           \
-    case KD: {                                                                                      \
-        using K = Kind<KD>;                                                                         \
-        *o = KindInfo{K::ESZ, K::TR, K::TC, K::NT, K::VEC, K::RWIDTH, K::WSTEPS, K::RSTEPS};        \
-        return true;                                                                                \
-    }
-        SWZ_KIND_CASE(SWZ_READ_SCALAR_COL)
-        SWZ_KIND_CASE(SWZ_READ_B64_4X4)
-        SWZ_KIND_CASE(SWZ_READ_B128_8X8)
-        SWZ_KIND_CASE(SWZ_READ_MFMA_16X16X32)
-        SWZ_KIND_CASE(SWZ_READ_B64_TR16)
-        SWZ_KIND_CASE(SWZ_READ_B64_TR8)
-        SWZ_KIND_CASE(SWZ_READ_NARROW1)
-        SWZ_KIND_CASE(SWZ_READ_NARROW2)
-        SWZ_KIND_CASE(SWZ_READ_NARROW4)
-        SWZ_KIND_CASE(SWZ_READ_NARROW8)
-        SWZ_KIND_CASE(SWZ_READ_NARROW16)
-#undef SWZ_KIND_CASE
-        default:
-            return false;
-    }
+    return with_kind(kind, [&](auto kd) {
+        using K = Kind<decltype(kd)::value>;
+        *o = KindInfo{K::ESZ, K::TR, K::TC, K::NT, K::VEC, K::RWIDTH, K::WSTEPS, K::RSTEPS};
+    });
 }
 
 int pad_elems(int kind) {
@@ -155,20 +125,8 @@ int pad_elems(int kind) {
 
 void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, int64_t* rcyc,
                   bool direct) {
-    switch (kind) {
-        case SWZ_READ_SCALAR_COL: predict_kind<SWZ_READ_SCALAR_COL>(m, ld, p, direct, wcyc, rcyc); break;
-        case SWZ_READ_B64_4X4: predict_kind<SWZ_READ_B64_4X4>(m, ld, p, direct, wcyc, rcyc); break;
-        case SWZ_READ_B128_8X8: predict_kind<SWZ_READ_B128_8X8>(m, ld, p, direct, wcyc, rcyc); break;
-        case SWZ_READ_MFMA_16X16X32: predict_kind<SWZ_READ_MFMA_16X16X32>(m, ld, p, direct, wcyc, rcyc); break;
-        case SWZ_READ_B64_TR16: predict_kind<SWZ_READ_B64_TR16>(m, ld, p, direct, wcyc, rcyc); break;
-        case SWZ_READ_B64_TR8: predict_kind<SWZ_READ_B64_TR8>(m, ld, p, direct, wcyc, rcyc); break;
-        case SWZ_READ_NARROW1: predict_kind<SWZ_READ_NARROW1>(m, ld, p, direct, wcyc, rcyc); break;
-        case SWZ_READ_NARROW2: predict_kind<SWZ_READ_NARROW2>(m, ld, p, direct, wcyc, rcyc); break;
-        case SWZ_READ_NARROW4: predict_kind<SWZ_READ_NARROW4>(m, ld, p, direct, wcyc, rcyc); break;
-        case SWZ_READ_NARROW8: predict_kind<SWZ_READ_NARROW8>(m, ld, p, direct, wcyc, rcyc); break;
-        case SWZ_READ_NARROW16: predict_kind<SWZ_READ_NARROW16>(m, ld, p, direct, wcyc, rcyc); break;
-        default: *wcyc = *rcyc = -1;
-    }
+    *wcyc = *rcyc = -1;
+    with_kind(kind, [&](auto kd) { predict_kind<decltype(kd)::value>(m, ld, p, direct, wcyc, rcyc); });
 }
 
 bool params_ok_for_kind(int kind, swz_params p) {
@@ -196,7 +154,7 @@ swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles) {
     const int log_tile = ilog2(static_cast<int64_t>(k.tr) * k.tc);
     const int b_max = (log_tile - M) / 2;
     // B spans one bank row as the reads see it (the layout exists for them).
-    const int rw = k.rwidth == 4 ? 0 : k.rwidth == 8 ? 1 : 2;
+    const int rw = k.rwidth <= 4 ? 0 : k.rwidth == 8 ? 1 : 2;
     const int row_bytes = m.n_banks[0][rw] * m.bank_bytes[0][rw];
     int b_rule = row_bytes >= k.vec ? ilog2(row_bytes / k.vec) : 0;
     if (b_rule > b_max) b_rule = b_max;
@@ -239,7 +197,7 @@ swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles) {
 
 swz_params cached_choice(int kind) {
     static std::once_flag once;
-    constexpr int kKinds = SWZ_READ_NARROW16 + 1;
+    constexpr int kKinds = kNumKinds;
     static swz_params table[kKinds];
     std::call_once(once, [] {
         for (int kd = 0; kd < kKinds; ++kd) table[kd] = choose_for_kind(kd, gfx950_bank_model(), nullptr);

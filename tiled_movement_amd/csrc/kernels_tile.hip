@@ -229,8 +229,9 @@ enum Fill { kRegs = 0, kPadded = 1, kDirect = 2 };
 template <int KIND, int FILL>
 struct LdsTile {
     using K = Kind<KIND>;
-    // The padded layout adds one element (4-byte) or one vector per row.
-    static constexpr int PAD = K::ESZ == 4 ? 1 : 8;
+    // The padded layout adds one element (element-wide LDS stores) or one
+    // LDS store's width per row.
+    static constexpr int PAD = K::VEC == K::ESZ ? 1 : K::VEC / K::ESZ;
     static constexpr int BYTES = K::TR * (K::TC + (FILL == kPadded ? PAD : 0)) * K::ESZ;
 };
 
@@ -318,12 +319,15 @@ __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ S, int64_t
 template <int KIND, bool PADDED>
 __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const LdsLayout& L, const u32x4* v) {
     using K = Kind<KIND>;
-    if constexpr (K::ESZ == 4) {
+    if constexpr (K::VEC == 4) {
+        // 4-byte writes: one element each, or a 4-byte run of the narrow-row
+        // kinds' smaller elements (M >= 1 resp. 2 keeps it together)
 #pragma unroll
         for (int j = 0; j < K::GLOADS; ++j) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                reinterpret_cast<uint32_t*>(lds)[step_off<KIND, true, PADDED>(wbase, 4 * j + e, L)] = v[j][e];
+                *reinterpret_cast<uint32_t*>(lds + K::ESZ * step_off<KIND, true, PADDED>(wbase, 4 * j + e, L)) =
+                    v[j][e];
         }
     } else if constexpr (K::ESZ == 1) {
         // Two 8-byte writes per 16-byte vector (the swizzle keeps 8-byte
@@ -363,7 +367,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
                                                uint8_t* __restrict__ D, int64_t rows, int64_t cols, int64_t r0,
                                                int64_t c0, int t) {
     using K = Kind<KIND>;
-    if constexpr (KIND == SWZ_READ_SCALAR_COL || is_narrow(KIND)) {
+    if constexpr (K::ESZ == 4 && (KIND == SWZ_READ_SCALAR_COL || is_narrow(KIND))) {
         // Task j: four rows of one source column -> 16 bytes of an output row.
 #pragma unroll
         for (int j = 0; j < K::TASKS; ++j) {
@@ -378,6 +382,28 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             // the store in a way that drops the store's non-temporal hint.
             asm volatile("" : "+v"(o));
             store16_edge<EDGE, 4>(D, orow, ocol, cols, rows, o);
+        }
+    } else if constexpr (is_narrow(KIND)) {
+        // Narrow rows of 2- or 1-byte elements.  Task j: PER rows of one
+        // source column, read one element at a time and packed into 16
+        // bytes of an output row.
+        constexpr int PER = K::PER, EPW = 4 / K::ESZ;  // elements per 16 bytes / per word
+#pragma unroll
+        for (int j = 0; j < K::TASKS; ++j) {
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const uint32_t off = K::ESZ * step_off<KIND, false, PADDED>(rbase, PER * j + e, L);
+                const uint32_t x = K::ESZ == 2 ? static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(lds + off))
+                                               : static_cast<uint32_t>(lds[off]);
+                w[e / EPW] |= x << (8 * K::ESZ * (e % EPW));
+            }
+            u32x4 o{w[0], w[1], w[2], w[3]};
+            int r = 0, c = 0;
+            K::rcoord(t, PER * j, r, c);
+            const int64_t orow = c0 + c, ocol = r0 + r;
+            asm volatile("" : "+v"(o));
+            store16_edge<EDGE, K::ESZ>(D, orow, ocol, cols, rows, o);
         }
     } else if constexpr (KIND == SWZ_READ_B64_TR8) {
         // Task j: in each of two steps h the 8-bit transpose read gives this
@@ -646,10 +672,15 @@ hipError_t launch_kind(const ConvertJob& j, hipStream_t stream) {
         if (padded || !j.aligned) return hipErrorInvalidValue;
         launch_variant<KIND, kDirect, true>(j, tiles_r, tiles_c, n_tiles, stream);
     } else if (padded) {
-        if (j.aligned)
-            launch_variant<KIND, kPadded, true>(j, tiles_r, tiles_c, n_tiles, stream);
-        else
-            launch_variant<KIND, kPadded, false>(j, tiles_r, tiles_c, n_tiles, stream);
+        // no padded rows narrower than one 4-byte LDS write
+        if constexpr (is_narrow(KIND) && K::TC * K::ESZ < 4) {
+            return hipErrorInvalidValue;
+        } else {
+            if (j.aligned)
+                launch_variant<KIND, kPadded, true>(j, tiles_r, tiles_c, n_tiles, stream);
+            else
+                launch_variant<KIND, kPadded, false>(j, tiles_r, tiles_c, n_tiles, stream);
+        }
     } else {
         if (j.aligned)
             launch_variant<KIND, kRegs, true>(j, tiles_r, tiles_c, n_tiles, stream);
@@ -695,6 +726,19 @@ hipError_t launch_convert(int kind, const ConvertJob& j, hipStream_t stream) {
         case SWZ_READ_NARROW4: return launch_kind<SWZ_READ_NARROW4>(j, stream);
         case SWZ_READ_NARROW8: return launch_kind<SWZ_READ_NARROW8>(j, stream);
         case SWZ_READ_NARROW16: return launch_kind<SWZ_READ_NARROW16>(j, stream);
+        case SWZ_READ_HNARROW1: return launch_kind<SWZ_READ_HNARROW1>(j, stream);
+        case SWZ_READ_HNARROW2: return launch_kind<SWZ_READ_HNARROW2>(j, stream);
+        case SWZ_READ_HNARROW4: return launch_kind<SWZ_READ_HNARROW4>(j, stream);
+        case SWZ_READ_HNARROW8: return launch_kind<SWZ_READ_HNARROW8>(j, stream);
+        case SWZ_READ_HNARROW16: return launch_kind<SWZ_READ_HNARROW16>(j, stream);
+        case SWZ_READ_HNARROW32: return launch_kind<SWZ_READ_HNARROW32>(j, stream);
+        case SWZ_READ_BNARROW1: return launch_kind<SWZ_READ_BNARROW1>(j, stream);
+        case SWZ_READ_BNARROW2: return launch_kind<SWZ_READ_BNARROW2>(j, stream);
+        case SWZ_READ_BNARROW4: return launch_kind<SWZ_READ_BNARROW4>(j, stream);
+        case SWZ_READ_BNARROW8: return launch_kind<SWZ_READ_BNARROW8>(j, stream);
+        case SWZ_READ_BNARROW16: return launch_kind<SWZ_READ_BNARROW16>(j, stream);
+        case SWZ_READ_BNARROW32: return launch_kind<SWZ_READ_BNARROW32>(j, stream);
+        case SWZ_READ_BNARROW64: return launch_kind<SWZ_READ_BNARROW64>(j, stream);
         default: return hipErrorInvalidValue;
     }
 }

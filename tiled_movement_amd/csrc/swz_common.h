@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "swz.h"
 
 // Threads per tile of each kernel (tuning knobs; 64 = one wave per tile).
@@ -249,48 +251,105 @@ template <> struct Kind<SWZ_READ_B64_TR8> {
     }
 };
 
-// 4-byte elements in narrow rows of C = 1, 2, 4, 8 or 16 columns, whole rows
-// per tile: TR = 1024 / C rows of C, 4096 bytes, one contiguous stretch of the
-// source.  A row is narrower than a bank row, so the tile is treated as the
-// flat offsets r*C + c and the swizzle's source field comes from the row
-// bits above the ones that make up a 32-element line: it spans several rows
-// ("CUDA 013 - Swizzle 的工作原理", usage example 4, int num[32][8] taken four
-// rows at a time).  Staging: vector v = t + NT*j is flat elements 4v..4v+3
-// (a row piece for C >= 4, several whole rows below), stored as four 4-byte
-// LDS writes.  Read: task
-// u = t + NT*j owns column u / (TR/4) and rows 4(u % (TR/4)) .. +3, read as
-// four 4-byte loads and written as 16 bytes of output row u / (TR/4); each
-// output row is a run of TR elements, 4096 / C bytes.
-template <int C>
+// Narrow rows of C columns, whole rows per tile: TR = (4096 / E) / C rows
+// of C E-byte elements, 4096 bytes, one contiguous stretch of the source.
+// A row is narrower than a bank row, so the tile is treated as the flat
+// offsets r*C + c and the swizzle's source field comes from the row bits
+// above the ones that make up one line of banks: it spans several rows
+// ("CUDA 013 - Swizzle 的工作原理", usage example 4, int num[32][8] taken
+// four rows at a time).  PER = 16 / E elements fill 16 bytes.  Staging:
+// vector v = t + NT*j is flat elements PER*v .. PER*v + PER - 1 (a row piece
+// for wide enough rows, several whole rows below), stored as four 4-byte LDS
+// writes (step i = 4j + w writes the vector's w-th 4-byte word).  Read: task
+// u = t + NT*j owns column u / (TR/PER) and rows PER*(u % (TR/PER)) .. +PER-1,
+// read as PER E-byte loads and written as 16 bytes of output row
+// u / (TR/PER); each output row is a run of TR elements, 4096 / C bytes.
+// E = 4: 1 to 16 columns; E = 2: 1 to 32; E = 1: 1 to 64.
+template <int C, int E>
 struct NarrowKind {
-    static_assert(C == 1 || C == 2 || C == 4 || C == 8 || C == 16, "narrow rows of 1 to 16 elements");
-    static constexpr int ESZ = 4, TR = 1024 / C, TC = C, NT = SWZ_NT_NARROW;
+    static_assert(E == 4 || E == 2 || E == 1, "4-, 2- or 1-byte elements");
+    static_assert(C >= 1 && (C & (C - 1)) == 0 && C * E <= 64, "narrow rows: a power of two up to 64 bytes");
+    static constexpr int ESZ = E, TR = 4096 / E / C, TC = C, NT = SWZ_NT_NARROW;
+    static constexpr int PER = 16 / E;  // elements per 16 bytes
     static constexpr int VEC = 4;
-    static constexpr int RWIDTH = 4;
+    static constexpr int RWIDTH = E;
     static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
     static constexpr int WSTEPS = GLOADS * 4;
-    static constexpr int TASKS = TR * TC / 4 / NT;
-    static constexpr int RSTEPS = TASKS * 4;
+    static constexpr int TASKS = TR * TC / PER / NT;
+    static constexpr int RSTEPS = TASKS * PER;
     __host__ __device__ static constexpr void wcoord(int t, int i, int& r, int& c) {
-        const int e = 4 * (t + NT * (i / 4)) + i % 4;
+        const int e = PER * (t + NT * (i / 4)) + (i % 4) * (4 / E);
         r = e / C;
         c = e % C;
     }
     __host__ __device__ static constexpr void rcoord(int t, int i, int& r, int& c) {
-        const int u = t + NT * (i / 4);
-        r = 4 * (u % (TR / 4)) + i % 4;
-        c = u / (TR / 4);
+        const int u = t + NT * (i / PER);
+        r = PER * (u % (TR / PER)) + i % PER;
+        c = u / (TR / PER);
     }
 };
-template <> struct Kind<SWZ_READ_NARROW1> : NarrowKind<1> {};
-template <> struct Kind<SWZ_READ_NARROW2> : NarrowKind<2> {};
-template <> struct Kind<SWZ_READ_NARROW4> : NarrowKind<4> {};
-template <> struct Kind<SWZ_READ_NARROW8> : NarrowKind<8> {};
-template <> struct Kind<SWZ_READ_NARROW16> : NarrowKind<16> {};
+template <> struct Kind<SWZ_READ_NARROW1> : NarrowKind<1, 4> {};
+template <> struct Kind<SWZ_READ_NARROW2> : NarrowKind<2, 4> {};
+template <> struct Kind<SWZ_READ_NARROW4> : NarrowKind<4, 4> {};
+template <> struct Kind<SWZ_READ_NARROW8> : NarrowKind<8, 4> {};
+template <> struct Kind<SWZ_READ_NARROW16> : NarrowKind<16, 4> {};
+template <> struct Kind<SWZ_READ_HNARROW1> : NarrowKind<1, 2> {};
+template <> struct Kind<SWZ_READ_HNARROW2> : NarrowKind<2, 2> {};
+template <> struct Kind<SWZ_READ_HNARROW4> : NarrowKind<4, 2> {};
+template <> struct Kind<SWZ_READ_HNARROW8> : NarrowKind<8, 2> {};
+template <> struct Kind<SWZ_READ_HNARROW16> : NarrowKind<16, 2> {};
+template <> struct Kind<SWZ_READ_HNARROW32> : NarrowKind<32, 2> {};
+template <> struct Kind<SWZ_READ_BNARROW1> : NarrowKind<1, 1> {};
+template <> struct Kind<SWZ_READ_BNARROW2> : NarrowKind<2, 1> {};
+template <> struct Kind<SWZ_READ_BNARROW4> : NarrowKind<4, 1> {};
+template <> struct Kind<SWZ_READ_BNARROW8> : NarrowKind<8, 1> {};
+template <> struct Kind<SWZ_READ_BNARROW16> : NarrowKind<16, 1> {};
+template <> struct Kind<SWZ_READ_BNARROW32> : NarrowKind<32, 1> {};
+template <> struct Kind<SWZ_READ_BNARROW64> : NarrowKind<64, 1> {};
 
 __host__ __device__ constexpr bool is_narrow(int kind) {
-    return kind >= SWZ_READ_NARROW1 && kind <= SWZ_READ_NARROW16;
+    return kind >= SWZ_READ_NARROW1 && kind <= SWZ_READ_BNARROW64;
 }
+
+// Host dispatch on a run-time read kind: calls f(std::integral_constant<int,
+// KIND>{}) and returns true, or returns false for an unknown kind.
+template <typename F>
+bool with_kind(int kind, F&& f) {
+    switch (kind) {
+#define SWZ_WITH_KIND_CASE(KD)                  \
+    case KD:                                    \
+        f(std::integral_constant<int, KD>{});   \
+        return true;
+        SWZ_WITH_KIND_CASE(SWZ_READ_SCALAR_COL)
+        SWZ_WITH_KIND_CASE(SWZ_READ_B64_4X4)
+        SWZ_WITH_KIND_CASE(SWZ_READ_B128_8X8)
+        SWZ_WITH_KIND_CASE(SWZ_READ_MFMA_16X16X32)
+        SWZ_WITH_KIND_CASE(SWZ_READ_B64_TR16)
+        SWZ_WITH_KIND_CASE(SWZ_READ_B64_TR8)
+        SWZ_WITH_KIND_CASE(SWZ_READ_NARROW1)
+        SWZ_WITH_KIND_CASE(SWZ_READ_NARROW2)
+        SWZ_WITH_KIND_CASE(SWZ_READ_NARROW4)
+        SWZ_WITH_KIND_CASE(SWZ_READ_NARROW8)
+        SWZ_WITH_KIND_CASE(SWZ_READ_NARROW16)
+        SWZ_WITH_KIND_CASE(SWZ_READ_HNARROW1)
+        SWZ_WITH_KIND_CASE(SWZ_READ_HNARROW2)
+        SWZ_WITH_KIND_CASE(SWZ_READ_HNARROW4)
+        SWZ_WITH_KIND_CASE(SWZ_READ_HNARROW8)
+        SWZ_WITH_KIND_CASE(SWZ_READ_HNARROW16)
+        SWZ_WITH_KIND_CASE(SWZ_READ_HNARROW32)
+        SWZ_WITH_KIND_CASE(SWZ_READ_BNARROW1)
+        SWZ_WITH_KIND_CASE(SWZ_READ_BNARROW2)
+        SWZ_WITH_KIND_CASE(SWZ_READ_BNARROW4)
+        SWZ_WITH_KIND_CASE(SWZ_READ_BNARROW8)
+        SWZ_WITH_KIND_CASE(SWZ_READ_BNARROW16)
+        SWZ_WITH_KIND_CASE(SWZ_READ_BNARROW32)
+        SWZ_WITH_KIND_CASE(SWZ_READ_BNARROW64)
+#undef SWZ_WITH_KIND_CASE
+        default:
+            return false;
+    }
+}
+constexpr int kNumKinds = SWZ_READ_BNARROW64 + 1;
 
 // ---------------------------------------------------------------------------
 // Offsets of a lane's later steps from its first one.
@@ -376,12 +435,28 @@ static_assert(steps_decompose<SWZ_READ_B64_TR8, true>(false) && steps_decompose<
 template <int KIND>
 constexpr bool narrow_ok() {
     using K = Kind<KIND>;
-    return even_split<KIND>() && K::TASKS * K::NT * 4 == K::TR * K::TC && steps_decompose<KIND, true>() &&
-           steps_decompose<KIND, false>();
+    return even_split<KIND>() && K::TASKS * K::NT * K::PER == K::TR * K::TC && K::TR % K::PER == 0 &&
+           steps_decompose<KIND, true>() && steps_decompose<KIND, false>();
 }
-static_assert(narrow_ok<SWZ_READ_NARROW1>() && narrow_ok<SWZ_READ_NARROW2>() && narrow_ok<SWZ_READ_NARROW4>() &&
-                  narrow_ok<SWZ_READ_NARROW8>() && narrow_ok<SWZ_READ_NARROW16>(),
-              "narrow-row lane maps and thread counts");
+// one assertion per kind: each evaluation has its own constexpr step budget
+static_assert(narrow_ok<SWZ_READ_NARROW1>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_NARROW2>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_NARROW4>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_NARROW8>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_NARROW16>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_HNARROW1>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_HNARROW2>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_HNARROW4>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_HNARROW8>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_HNARROW16>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_HNARROW32>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_BNARROW1>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_BNARROW2>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_BNARROW4>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_BNARROW8>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_BNARROW16>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_BNARROW32>(), "narrow-row lane map and thread count");
+static_assert(narrow_ok<SWZ_READ_BNARROW64>(), "narrow-row lane map and thread count");
 
 // ---------------------------------------------------------------------------
 // Direct fill (SWZ_LAYOUT_SWIZZLE_DIRECT): the tile goes from HBM straight
@@ -391,8 +466,10 @@ static_assert(narrow_ok<SWZ_READ_NARROW1>() && narrow_ok<SWZ_READ_NARROW2>() && 
 // the swizzled layout keeps there, swizzle^-1(p) = swizzle(p) (S >= B makes
 // the swizzle an involution: the XOR source bits are left as they are).
 // 16-byte loads for 2-byte elements (M >= 3 keeps the 8 elements of a slot
-// consecutive in one tile row); 4-byte loads, one element each, for 4-byte
-// elements, whose swizzle moves single elements.  As with the lane maps,
+// consecutive in one tile row); 4-byte loads otherwise: one element each
+// for 4-byte elements, whose swizzle moves single elements, and 4-byte runs
+// (which M >= 1 resp. M >= 2 keeps together) for the narrow-row kinds of
+// smaller elements and the 8-bit kind.  As with the lane maps,
 // swizzle(EPL*(t + NT*j)) = swizzle(EPL*t) ^ swizzle(EPL*NT*j): the bits of
 // the two terms are disjoint, so each lane keeps one base and every load
 // adds a wave-uniform XOR.
@@ -400,11 +477,12 @@ static_assert(narrow_ok<SWZ_READ_NARROW1>() && narrow_ok<SWZ_READ_NARROW2>() && 
 template <int KIND>
 struct Direct {
     using K = Kind<KIND>;
-    // bytes per lane per load: 16 for 2-byte elements (M >= 3 keeps 8 of
-    // them together); 4 otherwise (one 4-byte element; four 1-byte ones,
-    // whose swizzle keeps only 8-byte runs together and no 8-byte direct
-    // load exists)
-    static constexpr int VB = K::ESZ == 2 ? 16 : 4;
+    // bytes per lane per load: 16 for the 2-byte tile kinds (M >= 3 keeps 8
+    // elements together); 4 otherwise (one 4-byte element; the 4-byte runs
+    // of the narrow-row kinds; four 1-byte ones of the 8-bit kind, whose
+    // swizzle keeps only 8-byte runs together and no 8-byte direct load
+    // exists)
+    static constexpr int VB = K::ESZ == 2 && K::VEC == 16 ? 16 : 4;
     static constexpr int EPL = VB / K::ESZ;          // elements per lane per load
     static constexpr int LOADS = K::TR * K::TC / EPL / K::NT;
 };
@@ -421,7 +499,9 @@ static_assert(direct_split<SWZ_READ_SCALAR_COL>() && direct_split<SWZ_READ_B64_4
                   direct_split<SWZ_READ_B64_TR16>() && direct_split<SWZ_READ_B64_TR8>() &&
                   direct_split<SWZ_READ_NARROW1>() && direct_split<SWZ_READ_NARROW2>() &&
                   direct_split<SWZ_READ_NARROW4>() && direct_split<SWZ_READ_NARROW8>() &&
-                  direct_split<SWZ_READ_NARROW16>(),
+                  direct_split<SWZ_READ_NARROW16>() && direct_split<SWZ_READ_HNARROW1>() &&
+                  direct_split<SWZ_READ_HNARROW32>() && direct_split<SWZ_READ_BNARROW1>() &&
+                  direct_split<SWZ_READ_BNARROW64>(),
               "direct fill split");
 
 }  // namespace swz
