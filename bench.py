@@ -18,7 +18,8 @@ Usage:
       time one workload only (used for profiler runs), optionally rotating over
       exactly P buffer pairs; NAME is one of
       fp32_transpose, fp16_transpose, fp16_transpose_tr, u8_transpose, bf16_convert,
-      bf16_stage, fp32_narrow8, map, copy, copy_128, memcpy_d2d, bf16_gemm, bf16_gemm_fused,
+      bf16_stage, fp32_narrow8, fp16_narrow8, u8_narrow16, map, copy, copy_128, memcpy_d2d, bf16_gemm,
+      bf16_gemm_fused,
       torch_mm_bf16
 """
 
@@ -47,6 +48,8 @@ WORKLOADS = {
     "bf16_convert": "bf16 [64,4096,128] -> [64,128,4096] layout conversion, 64x128 LDS tiles, 16-byte reads of 8x8 blocks",
     "u8_transpose": "1-byte (int8 / fp8 bits) 8192x8192 row-major -> column-major transpose, 128x128 LDS tiles, gfx950 8-bit transpose reads",
     "fp32_narrow8": "fp32 [2097152][8] -> [8][2097152] transpose (64 MiB), whole-row 128x8 LDS tiles, the swizzle spanning rows",
+    "fp16_narrow8": "fp16 [4194304][8] -> [8][4194304] transpose (64 MiB), whole-row 256x8 LDS tiles, 2-byte column reads",
+    "u8_narrow16": "1-byte [4194304][16] -> [16][4194304] transpose (64 MiB), whole-row 256x16 LDS tiles, 1-byte column reads",
     "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
     "bf16_gemm": "C[8192x8192] fp32 = A * B^T from the staged fragments of A[8192x4096] and B[4096x8192] (16x16x32 bf16 MFMA)",
@@ -163,9 +166,14 @@ def build(ctx, name, layout):
     lay = T.LAYOUTS[layout]
     info = {"workload": WORKLOADS[name], "layout": layout}
 
-    if name in ("fp32_transpose", "fp16_transpose", "fp16_transpose_tr", "bf16_convert", "u8_transpose", "fp32_narrow8"):
+    if name in ("fp32_transpose", "fp16_transpose", "fp16_transpose_tr", "bf16_convert", "u8_transpose", "fp32_narrow8",
+                "fp16_narrow8", "u8_narrow16"):
         if name == "fp32_narrow8":
             a, esz, kind, (batch, r, c) = W.fp32_matrix(1 << 21, 8, seed=0), 4, T.READ_NARROW8, (1, 1 << 21, 8)
+        elif name == "fp16_narrow8":
+            a, esz, kind, (batch, r, c) = W.fp16_matrix(1 << 22, 8, seed=0), 2, T.READ_HNARROW8, (1, 1 << 22, 8)
+        elif name == "u8_narrow16":
+            a, esz, kind, (batch, r, c) = W.u8_matrix(1 << 22, 16, seed=0), 1, T.READ_BNARROW16, (1, 1 << 22, 16)
         elif name == "fp32_transpose":
             a, esz, kind, (batch, r, c) = W.fp32_matrix(4096, 4096, seed=0), 4, T.READ_SCALAR_COL, (1, 4096, 4096)
         elif name == "fp16_transpose":
@@ -396,7 +404,8 @@ def main(argv=None):
     extra = {}
     if not args.quick and args.workload is None:
         for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "fp16_transpose_tr",
-                      "u8_transpose", "bf16_convert", "bf16_stage", "fp32_narrow8", "map", "bf16_gemm",
+                      "u8_transpose", "bf16_convert", "bf16_stage", "fp32_narrow8", "fp16_narrow8", "u8_narrow16",
+                      "map", "bf16_gemm",
                       "bf16_gemm_fused", "torch_mm_bf16"):
             for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map", "bf16_gemm", "torch_mm_bf16")
                         else ("swizzle", "plain") if wname == "bf16_gemm_fused"
@@ -461,7 +470,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32_transpose": "f32", "fp32_narrow8": "f32", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
+        "dtype": {"fp32_transpose": "f32", "fp32_narrow8": "f32", "fp16_narrow8": "f16", "u8_narrow16": "u8", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
         "data": "synthetic",
         "config": {k: v for k, v in info.items() if not k.startswith("_")},
         "roofline": {

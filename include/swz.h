@@ -361,12 +361,12 @@ int swz_copy(const void* d_src, void* d_dst, int64_t bytes, void* stream);
 /* LDS bank microbenchmark (diagnostic; used to measure the bank model the
  * chooser relies on).  Launches n_patterns workgroups of `waves` 64-lane
  * waves.  Workgroup g runs pattern g: lane l of every wave accesses LDS byte
- * d_addrs[64*g + l] (masked into the probe's 64 KiB LDS window and aligned
- * down to width_bytes) if bit l of d_masks[g] is set, with ds_read_b32/b64/
- * b128 (is_write = 0) or ds_write_b32/b64/b128 (is_write = 1), 8 accesses
- * per iteration for `iters` iterations, and writes the wave's elapsed
- * shader-clock cycles to d_cycles[g * waves + w].
- *   width_bytes: 4, 8 or 16; waves: 1..16; iters: 1..1<<20.
+ * d_addrs[64*g + l] (taken modulo the probe's 96 KiB LDS window and aligned
+ * down to width_bytes) if bit l of d_masks[g] is set, with ds_read_u8/u16/
+ * b32/b64/b128 (is_write = 0) or ds_write_b8/b16/b32/b64/b128
+ * (is_write = 1), 8 accesses per iteration for `iters` iterations, and
+ * writes the wave's elapsed shader-clock cycles to d_cycles[g * waves + w].
+ *   width_bytes: 1, 2, 4, 8 or 16; waves: 1..16; iters: 1..1<<20.
  * Errors: SWZ_EINVAL on any other value or NULL pointer. */
 int swz_lds_probe(const uint32_t* d_addrs, const uint64_t* d_masks, int32_t n_patterns,
                   int32_t width_bytes, int32_t is_write, int32_t iters, int32_t waves,

@@ -341,7 +341,9 @@ SWZ_API int swz_bank_model_get(swz_bank_model* out) {
 
 SWZ_API int swz_lds_probe(const uint32_t* d_addrs, const uint64_t* d_masks, int32_t n_patterns, int32_t width_bytes,
                           int32_t is_write, int32_t iters, int32_t waves, uint64_t* d_cycles, void* stream) {
-    if (n_patterns < 0 || (width_bytes != 4 && width_bytes != 8 && width_bytes != 16)) return SWZ_EINVAL;
+    if (n_patterns < 0 || (width_bytes != 1 && width_bytes != 2 && width_bytes != 4 && width_bytes != 8 &&
+                           width_bytes != 16))
+        return SWZ_EINVAL;
     if (iters < 1 || iters > (1 << 20) || waves < 1 || waves > 16 || (is_write != 0 && is_write != 1))
         return SWZ_EINVAL;
     if (n_patterns == 0) return SWZ_OK;

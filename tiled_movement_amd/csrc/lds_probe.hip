@@ -17,6 +17,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <int W>
 struct Vec;
 template <>
+struct Vec<1> {
+    using T = uint32_t;
+};
+template <>
+struct Vec<2> {
+    using T = uint32_t;
+};
+template <>
 struct Vec<4> {
     using T = uint32_t;
 };
@@ -32,6 +40,23 @@ struct Vec<16> {
 // Eight back-to-back accesses to the same address, then wait for all of them.
 template <int W>
 __device__ __forceinline__ uint32_t read8(uint32_t a);
+#define SWZ_PROBE_READ8(OP)                                                                                  \
+    uint32_t r0, r1, r2, r3, r4, r5, r6, r7;                                                                 \
+    asm volatile(OP " %0, %8\n\t" OP " %1, %8\n\t" OP " %2, %8\n\t" OP " %3, %8\n\t" OP " %4, %8\n\t" OP   \
+                 " %5, %8\n\t" OP " %6, %8\n\t" OP " %7, %8\n\ts_waitcnt lgkmcnt(0)"                           \
+                 : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)     \
+                 : "v"(a)                                                                                    \
+                 : "memory");                                                                                \
+    return r0 ^ r1 ^ r2 ^ r3 ^ r4 ^ r5 ^ r6 ^ r7;
+template <>
+__device__ __forceinline__ uint32_t read8<1>(uint32_t a) {
+    SWZ_PROBE_READ8("ds_read_u8")
+}
+template <>
+__device__ __forceinline__ uint32_t read8<2>(uint32_t a) {
+    SWZ_PROBE_READ8("ds_read_u16")
+}
+#undef SWZ_PROBE_READ8
 template <>
 __device__ __forceinline__ uint32_t read8<4>(uint32_t a) {
     uint32_t r0, r1, r2, r3, r4, r5, r6, r7;
@@ -73,6 +98,20 @@ __device__ __forceinline__ uint32_t read8<16>(uint32_t a) {
 
 template <int W>
 __device__ __forceinline__ void write8(uint32_t a, typename Vec<W>::T v);
+#define SWZ_PROBE_WRITE8(OP)                                                                                 \
+    asm volatile(OP " %0, %1\n\t" OP " %0, %1\n\t" OP " %0, %1\n\t" OP " %0, %1\n\t" OP " %0, %1\n\t" OP    \
+                 " %0, %1\n\t" OP " %0, %1\n\t" OP " %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a),                  \
+                 "v"(v)                                                                                      \
+                 : "memory");
+template <>
+__device__ __forceinline__ void write8<1>(uint32_t a, uint32_t v) {
+    SWZ_PROBE_WRITE8("ds_write_b8")
+}
+template <>
+__device__ __forceinline__ void write8<2>(uint32_t a, uint32_t v) {
+    SWZ_PROBE_WRITE8("ds_write_b16")
+}
+#undef SWZ_PROBE_WRITE8
 template <>
 __device__ __forceinline__ void write8<4>(uint32_t a, uint32_t v) {
     asm volatile(
@@ -145,7 +184,13 @@ void launch_one(const uint32_t* addrs, const uint64_t* masks, int n, int iters, 
 hipError_t launch_lds_probe(const uint32_t* addrs, const uint64_t* masks, int n, int width, bool write, int iters,
                             int waves, uint64_t* cycles, hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    if (width == 4)
+    if (width == 1)
+        write ? launch_one<1, true>(addrs, masks, n, iters, waves, cycles, stream)
+              : launch_one<1, false>(addrs, masks, n, iters, waves, cycles, stream);
+    else if (width == 2)
+        write ? launch_one<2, true>(addrs, masks, n, iters, waves, cycles, stream)
+              : launch_one<2, false>(addrs, masks, n, iters, waves, cycles, stream);
+    else if (width == 4)
         write ? launch_one<4, true>(addrs, masks, n, iters, waves, cycles, stream)
               : launch_one<4, false>(addrs, masks, n, iters, waves, cycles, stream);
     else if (width == 8)

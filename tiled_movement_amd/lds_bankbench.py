@@ -12,6 +12,10 @@ Pattern families:
           are bank-equal tells the bank count
   stride  all lanes, lane l at byte width*s*l
   kernel  every LDS access of one tile of each kernel, in each layout
+  subword 1- and 2-byte accesses (ds_read_u8/u16, ds_write_b8/b16): the
+          same base, phase (lane 0 with lane j), bank-distance and stride
+          tests, plus lanes 0 and j on two bytes of one 4-byte word (a
+          shared word: no conflict if words, not bytes, are what conflict)
 
 Usage:
   python -m tiled_movement_amd.lds_bankbench --out gpurun_out/lds_bank.json
@@ -77,9 +81,34 @@ def patterns(families):
             for wr in (0, 1):
                 for s in (1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64, 65):
                     out.append(pat(f"stride/{'w' if wr else 'r'}{8 * w}/{s}", w, wr, [w * s * l for l in range(64)]))
+    if "subword" in families:
+        for w in (1, 2):
+            for wr in (0, 1):
+                tag = f"{'w' if wr else 'r'}{8 * w}"
+                out.append(pat(f"subword/{tag}/contig", w, wr, [l * w for l in range(64)]))
+                out.append(pat(f"subword/{tag}/one_lane", w, wr, [0] + [-1] * 63))
+                if not wr:
+                    out.append(pat(f"subword/{tag}/broadcast", w, wr, [0] * 64))
+                for j in range(1, 64):
+                    addrs = [-1] * 64
+                    addrs[0], addrs[j] = 0, 1024  # one bank, two words
+                    out.append(pat(f"subword/{tag}/pair/0/{j}", w, wr, addrs))
+                    addrs = [-1] * 64
+                    addrs[0], addrs[j] = 0, 4  # neighbouring words (control)
+                    out.append(pat(f"subword/{tag}/pairc/0/{j}", w, wr, addrs))
+                    addrs = [-1] * 64
+                    addrs[0], addrs[j] = 0, 4 - w  # two parts of one word
+                    out.append(pat(f"subword/{tag}/sameword/0/{j}", w, wr, addrs))
+                for dist in (64, 128, 256, 512):
+                    addrs = [-1] * 64
+                    addrs[0], addrs[1] = 0, dist
+                    out.append(pat(f"subword/{tag}/bank/{dist}/1", w, wr, addrs))
+                for s_ in (1, 2, 4, 8, 16, 32, 64, 65, 128, 129):
+                    out.append(pat(f"subword/{tag}/stride/{s_}", w, wr, [w * s_ * l for l in range(64)]))
     if "kernel" in families:
         for kind, kname in [(T.READ_SCALAR_COL, "scalar_col"), (T.READ_B64_4X4, "b64_4x4"),
-                            (T.READ_B128_8X8, "b128_8x8"), (T.READ_MFMA_16X16X32, "mfma")]:
+                            (T.READ_B128_8X8, "b128_8x8"), (T.READ_MFMA_16X16X32, "mfma"),
+                            (T.READ_HNARROW8, "hnarrow8"), (T.READ_BNARROW16, "bnarrow16")]:
             for layout in ("swizzle", "pad", "plain"):
                 for wr in (1, 0):
                     for idx, (addrs, width) in enumerate(T.swz_kernel_accesses(kind, layout, None, wr)):
