@@ -49,7 +49,7 @@ WORKLOADS = {
     "u8_transpose": "1-byte (int8 / fp8 bits) 8192x8192 row-major -> column-major transpose, 128x128 LDS tiles, gfx950 8-bit transpose reads",
     "fp32_narrow8": "fp32 [2097152][8] -> [8][2097152] transpose (64 MiB), whole-row 128x8 LDS tiles, the swizzle spanning rows",
     "fp16_narrow8": "fp16 [4194304][8] -> [8][4194304] transpose (64 MiB), whole-row 256x8 LDS tiles, 2-byte column reads",
-    "u8_narrow16": "1-byte [4194304][16] -> [16][4194304] transpose (64 MiB), whole-row 256x16 LDS tiles, 1-byte column reads",
+    "u8_narrow16": "1-byte [4194304][16] -> [16][4194304] transpose (64 MiB), whole-row 1024x16 LDS tiles, 4-byte reads of 16x4 blocks",
     "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
     "bf16_gemm": "C[8192x8192] fp32 = A * B^T from the staged fragments of A[8192x4096] and B[4096x8192] (16x16x32 bf16 MFMA)",

@@ -155,19 +155,25 @@ def restated_accesses(kind, write):
     out = []
     for w in range(nt // 64):
         ts = [64 * w + l for l in range(64)]
-        if kind in NARROW:  # 4096-byte tile of whole rows of C elements of esz bytes
+        if kind in NARROW:  # tile of whole rows of C elements of esz bytes
             esz_, tr_, c_, _ = KIND_GEOM[kind]
-            per = 16 // esz_  # elements per 16 bytes
-            if write:  # vector v: flat elements per*v .., one 4-byte word per store
-                for j in range(256 // nt):
+            per, epw = 16 // esz_, 4 // esz_  # elements per 16 bytes / per 4-byte word
+            words = esz_ != 2 or c_ == 1 or c_ >= 32  # read back as words, else element by element
+            cb = min(c_, epw) if words else 1  # columns per lane block
+            rpw = max(1, epw // c_) if words else 1  # whole rows per load
+            if write:  # vector v = t + nt*j: flat elements per*v .., one 4-byte word per store:
+                # word e, or e ^ (bits 3-4 of the lane) for elements under 4 bytes in rows of 16 or more
+                swap = words and esz_ < 4 and c_ >= 16
+                for j in range(cb):
                     for e in range(4):
-                        coords = [divmod(per * (t + nt * j) + e * (4 // esz_), c_) for t in ts]
+                        coords = [divmod(per * (t + nt * j) + (e ^ ((t >> 3) & 3 if swap else 0)) * epw, c_)
+                                  for t in ts]
                         out.append((coords, 4))
-            else:  # piece u: column u // (TR/per), rows per*(u % (TR/per)) .., one row per load
-                for j in range(256 // nt):
-                    for e in range(per):
-                        coords = [(per * ((t + nt * j) % (tr_ // per)) + e, (t + nt * j) // (tr_ // per)) for t in ts]
-                        out.append((coords, esz_))
+            else:  # lane t: rows per*(t % (TR/per)) .., columns cb*(t // (TR/per)) .., one word (element) per load
+                blocks = tr_ // per
+                for i in range(per // rpw):
+                    coords = [(per * (t % blocks) + rpw * i, cb * (t // blocks)) for t in ts]
+                    out.append((coords, 4 if words else esz_))
         elif kind == T.READ_SCALAR_COL:  # 32x32 4-byte tile
             for j in range(256 // nt):
                 for e in range(4):
@@ -252,8 +258,9 @@ KIND_GEOM = {
     T.READ_NARROW4: (4, 256, 4, 1),
     T.READ_NARROW8: (4, 128, 8, 1),
     T.READ_NARROW16: (4, 64, 16, 1),
-    **{k: (2, 2048 // c, c, 2) for k, c in zip(NARROW2, (1, 2, 4, 8, 16, 32))},
-    **{k: (1, 4096 // c, c, 4) for k, c in zip(NARROW1, (1, 2, 4, 8, 16, 32, 64))},
+    # tile rows from the plan: NT lanes, each a block of 16 bytes of rows x min(C, elements per word) columns
+    **{k: (2, T.swz_plan(0, 4096, c, 2, "swizzle", k)["tile"][0], c, 2) for k, c in zip(NARROW2, (1, 2, 4, 8, 16, 32))},
+    **{k: (1, T.swz_plan(0, 4096, c, 1, "swizzle", k)["tile"][0], c, 4) for k, c in zip(NARROW1, (1, 2, 4, 8, 16, 32, 64))},
 }
 
 
@@ -338,8 +345,9 @@ def test_model_matches_measured_geometry():
     first = [0, 1, 2, 3, 12, 13, 14, 15, 20, 21, 22, 23, 24, 25, 26, 27]
     assert sorted(l for l in range(64) if ph[l] == ph[0]) == first
     assert len(set(ph)) == 4
-    # writes: 16 contiguous lanes for 4- and 8-byte writes, 8 for 16-byte ones
-    assert m[("write", 4)]["phase"] == [l // 16 for l in range(64)]
+    # writes: 32 contiguous lanes for 4-byte writes (the conflict counter's
+    # phases), 16 for 8-byte and 8 for 16-byte ones
+    assert m[("write", 4)]["phase"] == [l // 32 for l in range(64)]
     assert m[("write", 8)]["phase"] == [l // 16 for l in range(64)]
     assert m[("write", 16)]["phase"] == [l // 8 for l in range(64)]
 
@@ -442,7 +450,9 @@ def test_narrow_kind_validation():
         for i, kind in enumerate(kinds):
             c = 1 << i
             p = T.swz_plan(0, 1000, c, esz, "swizzle")
-            assert p["read_kind"] == kind and p["tile"] == (4096 // esz // c, c) and p["lds_bytes"] == 4096
+            cb = min(c, 4 // esz) if esz == 1 or c in (1, 32) else 1  # columns per lane block: the tile is 16 * threads * cb bytes
+            tb = 16 * p["threads"] * cb
+            assert p["read_kind"] == kind and p["tile"] == (tb // esz // c, c) and p["lds_bytes"] == tb
             assert p["vec_bytes"] == 4 and p["params"][1] == {2: 1, 1: 2}[esz]
         assert f(A, B, 1, 256, 2 * c, esz, 0, kinds[-1], None, None) == EINVAL  # width differs
         assert f(A, B, 1, 256, c, 6 - esz, 0, kinds[-1], None, None) == EINVAL  # element size differs

@@ -226,10 +226,10 @@ NARROW_KINDS = ([(k, 4, c) for k, c in zip((T.READ_NARROW1, T.READ_NARROW2, T.RE
 @pytest.mark.parametrize("kind,esz,c", NARROW_KINDS)
 @pytest.mark.parametrize("layout", LAYOUTS + ["direct"])
 def test_narrow_rows(kind, esz, c, layout):
-    """Whole-row tiles of 4096 bytes, the swizzle spanning several rows:
-    whole tiles, ragged last tiles (on and off a 16-byte output pitch),
-    fewer rows than one tile, empty."""
-    tr = 4096 // esz // c
+    """Whole-row tiles, the swizzle spanning several rows: whole tiles,
+    ragged last tiles (on and off a 16-byte output pitch), fewer rows than
+    one tile, empty."""
+    tr = T.swz_plan(0, 4096, c, esz, "swizzle", kind)["tile"][0]
     if layout == "pad" and c * esz < 4:  # rows under one 4-byte LDS store get no pad
         with pytest.raises(T.SwzError):
             check_transpose(GEN[esz](tr, c, seed=0), esz, layout, kind)
@@ -243,7 +243,7 @@ def test_narrow_rows(kind, esz, c, layout):
 
 @pytest.mark.parametrize("kind,esz,c", NARROW_KINDS)
 def test_narrow_auto_unaligned_and_batched(kind, esz, c):
-    rows = 3 * (4096 // esz // c) + 9
+    rows = 3 * T.swz_plan(0, 4096, c, esz, "swizzle", kind)["tile"][0] + 9
     assert T.swz_plan(0, rows, c, esz)["read_kind"] == kind
     a = GEN[esz](rows, c, seed=c)
     announce("narrow auto", esz, c)
@@ -272,9 +272,10 @@ def test_narrow_auto_unaligned_and_batched(kind, esz, c):
 def test_narrow_any_valid_swizzle(kind, esz, c):
     """Every admissible (B, M, S) of either sign moves data only inside LDS
     (M keeps the 4-byte LDS writes whole: M >= log2(4 / esz))."""
-    a = GEN[esz](2 * (4096 // esz // c) + 16, c, seed=30 + c)
+    tr = T.swz_plan(0, 4096, c, esz, "swizzle", kind)["tile"][0]
+    a = GEN[esz](2 * tr + 16, c, seed=30 + c)
     rng = np.random.default_rng(c + 100 * esz)
-    log_tile = (4096 // esz).bit_length() - 1
+    log_tile = (tr * c).bit_length() - 1
     m_min = {4: 0, 2: 1, 1: 2}[esz]
     triples = [(B, M, S) for B in range(1, 6) for M in range(m_min, 5) for S in range(-9, 10)
                if S != 0 and M + B <= log_tile and (M + B if S > 0 else M - S + B) <= log_tile]

@@ -319,15 +319,37 @@ __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ S, int64_t
 template <int KIND, bool PADDED>
 __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const LdsLayout& L, const u32x4* v) {
     using K = Kind<KIND>;
-    if constexpr (K::VEC == 4) {
-        // 4-byte writes: one element each, or a 4-byte run of the narrow-row
-        // kinds' smaller elements (M >= 1 resp. 2 keeps it together)
+    if constexpr (K::VEC == 4 && K::ESZ < 4) {
+        // Narrow rows of 2- or 1-byte elements: 4-byte runs (M >= 1 resp. 2
+        // keeps them together); step 4j + e writes word e ^ s of the vector,
+        // s = bits 3-4 of the lane for the wide rows (SWAP, lane map in
+        // swz_common.h), picked with two 2-way selects.  Those steps combine
+        // by XOR only, so padded rows compute each step's row and column.
+        const int t = threadIdx.x;
+        const bool sw1 = K::SWAP && ((t >> 3) & 1), sw2 = K::SWAP && ((t >> 4) & 1);
+#pragma unroll
+        for (int j = 0; j < K::GLOADS; ++j) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t off;
+                if constexpr (PADDED) {
+                    int r = 0, c = 0;
+                    K::wcoord(t, 4 * j + e, r, c);
+                    off = static_cast<uint32_t>(r) * L.ld + static_cast<uint32_t>(c);
+                } else {
+                    off = step_off<KIND, true, false>(wbase, 4 * j + e, L);
+                }
+                const uint32_t lo = sw1 ? v[j][e ^ 1] : v[j][e], hi = sw1 ? v[j][e ^ 3] : v[j][e ^ 2];
+                *reinterpret_cast<uint32_t*>(lds + K::ESZ * off) = sw2 ? hi : lo;
+            }
+        }
+    } else if constexpr (K::VEC == 4) {
+        // 4-byte elements, one per write
 #pragma unroll
         for (int j = 0; j < K::GLOADS; ++j) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                *reinterpret_cast<uint32_t*>(lds + K::ESZ * step_off<KIND, true, PADDED>(wbase, 4 * j + e, L)) =
-                    v[j][e];
+                reinterpret_cast<uint32_t*>(lds)[step_off<KIND, true, PADDED>(wbase, 4 * j + e, L)] = v[j][e];
         }
     } else if constexpr (K::ESZ == 1) {
         // Two 8-byte writes per 16-byte vector (the swizzle keeps 8-byte
@@ -383,27 +405,51 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             asm volatile("" : "+v"(o));
             store16_edge<EDGE, 4>(D, orow, ocol, cols, rows, o);
         }
+    } else if constexpr (narrow_by_element<KIND>()) {
+        // Narrow rows of 2-byte elements read an element at a time: PER rows
+        // of one column packed into 16 bytes of one output row.
+        constexpr int PER = K::PER;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const uint32_t x = *reinterpret_cast<const uint16_t*>(lds + 2 * step_off<KIND, false, PADDED>(rbase, e, L));
+            w[e / 2] |= x << (16 * (e % 2));
+        }
+        u32x4 o{w[0], w[1], w[2], w[3]};
+        int r = 0, c = 0;
+        K::rcoord(t, 0, r, c);
+        asm volatile("" : "+v"(o));
+        store16_edge<EDGE, 2>(D, c0 + c, r0 + r, cols, rows, o);
     } else if constexpr (is_narrow(KIND)) {
-        // Narrow rows of 2- or 1-byte elements.  Task j: PER rows of one
-        // source column, read one element at a time and packed into 16
-        // bytes of an output row.
-        constexpr int PER = K::PER, EPW = 4 / K::ESZ;  // elements per 16 bytes / per word
+        // Narrow rows of 2- or 1-byte elements: the lane's block of PER rows
+        // and CB columns arrives as RSTEPS whole words (EPW columns of one
+        // row each, or RPW whole rows of C columns); piece j gathers column
+        // CB*g + j of the PER rows, element q from word q / RPW at position
+        // (q % RPW) * C + j, into 16 bytes of one output row.
+        constexpr int E = K::ESZ, PER = K::PER, EPW = K::EPW, CB = K::CB, RPW = K::RPW, C = K::TC;
+        constexpr uint32_t kMask = E == 2 ? 0xffffu : 0xffu;
+        uint32_t w[K::RSTEPS];
 #pragma unroll
-        for (int j = 0; j < K::TASKS; ++j) {
-            uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int i = 0; i < K::RSTEPS; ++i)
+            w[i] = *reinterpret_cast<const uint32_t*>(lds + E * step_off<KIND, false, PADDED>(rbase, i, L));
+        int r = 0, c = 0;
+        K::rcoord(t, 0, r, c);
 #pragma unroll
-            for (int e = 0; e < PER; ++e) {
-                const uint32_t off = K::ESZ * step_off<KIND, false, PADDED>(rbase, PER * j + e, L);
-                const uint32_t x = K::ESZ == 2 ? static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(lds + off))
-                                               : static_cast<uint32_t>(lds[off]);
-                w[e / EPW] |= x << (8 * K::ESZ * (e % EPW));
+        for (int j = 0; j < CB; ++j) {
+            u32x4 o;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t x = 0u;
+#pragma unroll
+                for (int p = 0; p < EPW; ++p) {
+                    const int q = d * EPW + p;  // row within the block
+                    const int pos = (q % RPW) * C + j;
+                    x |= ((w[q / RPW] >> (8 * E * pos)) & kMask) << (8 * E * p);
+                }
+                o[d] = x;
             }
-            u32x4 o{w[0], w[1], w[2], w[3]};
-            int r = 0, c = 0;
-            K::rcoord(t, PER * j, r, c);
-            const int64_t orow = c0 + c, ocol = r0 + r;
             asm volatile("" : "+v"(o));
-            store16_edge<EDGE, K::ESZ>(D, orow, ocol, cols, rows, o);
+            store16_edge<EDGE, E>(D, c0 + c + j, r0 + r, cols, rows, o);
         }
     } else if constexpr (KIND == SWZ_READ_B64_TR8) {
         // Task j: in each of two steps h the 8-bit transpose read gives this

@@ -34,6 +34,12 @@
 #ifndef SWZ_NT_NARROW
 #define SWZ_NT_NARROW 256
 #endif
+#ifndef SWZ_NT_HNARROW
+#define SWZ_NT_HNARROW 256
+#endif
+#ifndef SWZ_NT_BNARROW
+#define SWZ_NT_BNARROW 256
+#endif
 
 namespace swz {
 
@@ -251,41 +257,63 @@ template <> struct Kind<SWZ_READ_B64_TR8> {
     }
 };
 
-// Narrow rows of C columns, whole rows per tile: TR = (4096 / E) / C rows
-// of C E-byte elements, 4096 bytes, one contiguous stretch of the source.
-// A row is narrower than a bank row, so the tile is treated as the flat
-// offsets r*C + c and the swizzle's source field comes from the row bits
-// above the ones that make up one line of banks: it spans several rows
+// Narrow rows of C columns, whole rows per tile: one contiguous stretch of
+// the source.  A row is narrower than a bank row, so the tile is treated as
+// the flat offsets r*C + c and the swizzle's source field comes from the row
+// bits above the ones that make up one line of banks: it spans several rows
 // ("CUDA 013 - Swizzle 的工作原理", usage example 4, int num[32][8] taken
-// four rows at a time).  PER = 16 / E elements fill 16 bytes.  Staging:
-// vector v = t + NT*j is flat elements PER*v .. PER*v + PER - 1 (a row piece
-// for wide enough rows, several whole rows below), stored as four 4-byte LDS
-// writes (step i = 4j + w writes the vector's w-th 4-byte word).  Read: task
-// u = t + NT*j owns column u / (TR/PER) and rows PER*(u % (TR/PER)) .. +PER-1,
-// read as PER E-byte loads and written as 16 bytes of output row
-// u / (TR/PER); each output row is a run of TR elements, 4096 / C bytes.
-// E = 4: 1 to 16 columns; E = 2: 1 to 32; E = 1: 1 to 64.
+// four rows at a time).  PER = 16 / E elements fill 16 bytes, EPW = 4 / E
+// fill one 4-byte LDS word.  Each lane owns a block of PER rows and CB
+// columns and turns it into CB 16-byte pieces of output rows.  With WORDS
+// the block is CB = min(C, EPW) columns read back as whole 4-byte words (a
+// word holds EPW columns of one row, or RPW = EPW / C whole rows when
+// C < EPW); otherwise it is one column read an element at a time (CB = 1,
+// RPW = 1, E-byte loads).  Words take a quarter of the loads for 1-byte
+// elements and are faster there; for 2-byte elements element loads measured
+// faster at 2 to 16 columns (8 loads per piece), words at 1 and 32.  NT
+// lanes (256 by default), so a tile is 16 * NT * CB bytes:
+// TR = 16 * NT * CB / (E * C) rows.  Staging: vector
+// v = t + NT*j (j < CB) is flat elements PER*v .. PER*v + PER - 1, stored
+// as four 4-byte LDS writes; step i = 4j + w writes word w, or, for E < 4
+// and C >= 16, word w ^ ((t >> 3) & 3) (SWAP).  The four quarters of a
+// 32-lane write phase (vectors 8 apart, whose words share banks) then write
+// different banks whatever the swizzle's source bits above the phase; wide
+// rows need that, because their reads put the lanes' row blocks 4C >= 64
+// words apart, so the swizzle's source field must start above the bits a
+// write phase spans.  Read:
+// lane t owns columns CB*g .. CB*g + CB - 1 with g = t / (TR/PER) and rows
+// PER*b .. PER*b + PER - 1 with b = t % (TR/PER); step i reads the word (or
+// element) at row PER*b + RPW*i, column CB*g.  Each output row is a run of
+// TR elements.
+// E = 4: 1 to 16 columns (4096-byte tiles, one word per row and lane, the
+// scalar-column reads); E = 2: 1 to 32; E = 1: 1 to 64.
 template <int C, int E>
 struct NarrowKind {
     static_assert(E == 4 || E == 2 || E == 1, "4-, 2- or 1-byte elements");
     static_assert(C >= 1 && (C & (C - 1)) == 0 && C * E <= 64, "narrow rows: a power of two up to 64 bytes");
-    static constexpr int ESZ = E, TR = 4096 / E / C, TC = C, NT = SWZ_NT_NARROW;
-    static constexpr int PER = 16 / E;  // elements per 16 bytes
+    static constexpr int PER = 16 / E;                   // elements per 16 bytes
+    static constexpr int EPW = 4 / E;                    // elements per 4-byte word
+    static constexpr bool WORDS = E != 2 || C == 1 || C >= 32;
+    static constexpr int CB = !WORDS ? 1 : C < EPW ? C : EPW;   // columns per lane block
+    static constexpr int RPW = WORDS && C < EPW ? EPW / C : 1;  // rows per load
+    static constexpr int NT = E == 4 ? SWZ_NT_NARROW : E == 2 ? SWZ_NT_HNARROW : SWZ_NT_BNARROW;
+    static constexpr int ESZ = E, TR = NT * 16 * CB / E / C, TC = C;
     static constexpr int VEC = 4;
-    static constexpr int RWIDTH = E;
+    static constexpr int RWIDTH = WORDS ? 4 : E;
     static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
     static constexpr int WSTEPS = GLOADS * 4;
-    static constexpr int TASKS = TR * TC / PER / NT;
-    static constexpr int RSTEPS = TASKS * PER;
+    static constexpr int TASKS = 1;
+    static constexpr int RSTEPS = PER / RPW;
+    static constexpr bool SWAP = WORDS && E < 4 && C >= 16;
+    __host__ __device__ static constexpr int wword(int t, int i) { return SWAP ? (i % 4) ^ ((t >> 3) & 3) : i % 4; }
     __host__ __device__ static constexpr void wcoord(int t, int i, int& r, int& c) {
-        const int e = PER * (t + NT * (i / 4)) + (i % 4) * (4 / E);
+        const int e = PER * (t + NT * (i / 4)) + wword(t, i) * EPW;
         r = e / C;
         c = e % C;
     }
     __host__ __device__ static constexpr void rcoord(int t, int i, int& r, int& c) {
-        const int u = t + NT * (i / PER);
-        r = PER * (u % (TR / PER)) + i % PER;
-        c = u / (TR / PER);
+        r = PER * (t % (TR / PER)) + RPW * i;
+        c = CB * (t / (TR / PER));
     }
 };
 template <> struct Kind<SWZ_READ_NARROW1> : NarrowKind<1, 4> {};
@@ -309,6 +337,15 @@ template <> struct Kind<SWZ_READ_BNARROW64> : NarrowKind<64, 1> {};
 
 __host__ __device__ constexpr bool is_narrow(int kind) {
     return kind >= SWZ_READ_NARROW1 && kind <= SWZ_READ_BNARROW64;
+}
+
+// A narrow-row kind whose read-back goes an element at a time (not WORDS).
+template <int KIND>
+__host__ __device__ constexpr bool narrow_by_element() {
+    if constexpr (is_narrow(KIND))
+        return !Kind<KIND>::WORDS;
+    else
+        return false;
 }
 
 // Host dispatch on a run-time read kind: calls f(std::integral_constant<int,
@@ -435,8 +472,10 @@ static_assert(steps_decompose<SWZ_READ_B64_TR8, true>(false) && steps_decompose<
 template <int KIND>
 constexpr bool narrow_ok() {
     using K = Kind<KIND>;
-    return even_split<KIND>() && K::TASKS * K::NT * K::PER == K::TR * K::TC && K::TR % K::PER == 0 &&
-           steps_decompose<KIND, true>() && steps_decompose<KIND, false>();
+    // with SWAP the writes exchange word pairs by lane, so their steps only
+    // combine by XOR (padded rows compute each step's row and column)
+    return even_split<KIND>() && K::NT * K::PER * K::CB == K::TR * K::TC && K::TR % K::PER == 0 &&
+           K::GLOADS == K::CB && steps_decompose<KIND, true>(!K::SWAP) && steps_decompose<KIND, false>();
 }
 // one assertion per kind: each evaluation has its own constexpr step budget
 static_assert(narrow_ok<SWZ_READ_NARROW1>(), "narrow-row lane map and thread count");
