@@ -26,6 +26,7 @@ Usage:
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -52,6 +53,7 @@ WORKLOADS = {
     "u8_narrow16": "1-byte [4194304][16] -> [16][4194304] transpose (64 MiB), whole-row 1024x16 LDS tiles, 4-byte reads of 16x4 blocks",
     "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
+    "map_batch": "Swizzle<B,M,S> of int32 offsets 0..65535 under all 125 triples in one call (8,192,000 outputs)",
     "bf16_gemm": "C[8192x8192] fp32 = A * B^T from the staged fragments of A[8192x4096] and B[4096x8192] (16x16x32 bf16 MFMA)",
     "bf16_gemm_fused": "C[8192x8192] fp32 = A * B^T, A[8192x4096] row-major and B[4096x8192] column-major staged through swizzled 256x64 LDS tiles inside the GEMM (16x16x32 bf16 MFMA)",
     "torch_mm_bf16": "runtime library GEMM (torch.mm, bf16 in and out) of the same 8192x8192x4096 product, for context",
@@ -297,6 +299,25 @@ def build(ctx, name, layout):
         info["_keep"] = (x, y)
         return step, 2 * 65536 * 4, info
 
+    if name == "map_batch":
+        triples = W.map_triples()
+        x = ctx.torch.arange(65536, dtype=ctx.torch.int32, device=ctx.dev)
+        k = n_pairs(4 * 65536 * len(triples))
+        ys = [ctx.torch.empty((len(triples), 65536), dtype=ctx.torch.int32, device=ctx.dev) for _ in range(k)]
+        arr = (T.Params * len(triples))(*[T.Params(*t) for t in triples])
+        xp, yps = x.data_ptr(), [y.data_ptr() for y in ys]
+
+        def step(i):
+            rc = lib.swz_map_batch(xp, yps[i % k], 65536, ctypes.addressof(arr), len(triples), stream)
+            if rc:
+                ctx.check(rc, "swz_map_batch")
+
+        info["_keep"] = (x, ys, arr)
+        info["buffer_pairs"] = k
+        # bytes: one read of the offsets per triple (from cache) is not HBM
+        # traffic; the algorithmic bytes are the input once and every output
+        return step, 4 * 65536 * (1 + len(triples)), info
+
     if name in ("copy", "copy_128", "memcpy_d2d"):
         nbytes = (128 if name == "copy_128" else 64) * 2**20
         k = n_pairs(2 * nbytes)
@@ -415,6 +436,11 @@ def main(argv=None):
                     rate, ms2 = median_rate(s2, nb2, steps=250, warmup=25)
                     extra["map/swizzle"] = {"us_per_call": round(ms2 * 1e3, 3)}
                     log(f"map: {ms2 * 1e3:.2f} us/call")
+                    s3, nb3, _ = build(ctx, "map_batch", "swizzle")
+                    rate3, ms3 = median_rate(s3, nb3, steps=100, warmup=10)
+                    extra["map/swizzle"].update({"batch_us_per_125_triples": round(ms3 * 1e3, 2),
+                                                 "batch_GBps": round(rate3, 1)})
+                    log(f"map batch: {ms3 * 1e3:.2f} us per 125 triples, {rate3:.1f} GB/s")
                     continue
                 if wname in ("bf16_gemm", "bf16_gemm_fused", "torch_mm_bf16"):
                     rate, ms2 = median_rate(s2, nb2, steps=20, warmup=5)
@@ -470,7 +496,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32_transpose": "f32", "fp32_narrow8": "f32", "fp16_narrow8": "f16", "u8_narrow16": "u8", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
+        "dtype": {"fp32_transpose": "f32", "fp32_narrow8": "f32", "fp16_narrow8": "f16", "u8_narrow16": "u8", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "map_batch": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
         "data": "synthetic",
         "config": {k: v for k, v in info.items() if not k.startswith("_")},
         "roofline": {

@@ -8,7 +8,7 @@
  * returns.  Errors are negative return codes, detected on the host before
  * any launch; no call aborts or throws.  All calls are thread-safe.
  *
- * Calls: the swizzle map (swz_map); transposes and batched layout
+ * Calls: the swizzle map (swz_map, swz_map_batch); transposes and batched layout
  * conversions of 1-, 2- and 4-byte elements through swizzled, padded or
  * plain LDS tiles (swz_transpose, swz_convert_layout); GEMM operand staging
  * into matrix-instruction fragments (swz_stage_operand) and their consumer
@@ -177,6 +177,20 @@ typedef struct swz_plan_info {
  * Errors: SWZ_EINVAL for n < 0, NULL with n > 0, partial overlap, or
  * parameters out of range. */
 int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p, void* stream);
+
+/* out[j][i] = Swizzle<B_j,M_j,S_j>(in[i]) for j < n_params, i < n: one
+ * offset range under many triples, one launch per 128 triples (the same
+ * formula as swz_map, whose single-triple calls are launch-bound at small
+ * n).
+ *   d_in     : device int32 array of n elements.
+ *   d_out    : device int32 array [n_params][n]; must not overlap d_in.
+ *   h_params : host array of n_params triples, each in swz_map's range;
+ *              read during the call only.
+ * Errors: SWZ_EINVAL for n < 0, n_params < 0, NULL with work to do,
+ * misalignment, overlap or any triple out of range (then nothing is
+ * launched); SWZ_EHIP if a launch fails (earlier chunks may have run). */
+int swz_map_batch(const int32_t* d_in, int32_t* d_out, int64_t n, const swz_params* h_params, int32_t n_params,
+                  void* stream);
 
 /* dst = transpose of src: src is [rows][cols] row-major, dst is
  * [cols][rows] row-major (the column-major image of src), bit-exact.  Tiles

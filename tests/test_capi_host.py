@@ -62,6 +62,23 @@ def test_map_validation():
     assert lib.swz_map(A, B, 0, P(1, 0, 1), None) == T.SWZ_OK  # nothing to do
 
 
+def test_map_batch_validation():
+    f = lib.swz_map_batch
+    good = (P * 3)(P(1, 0, 1), P(3, 1, -4), P(0, 0, 0))
+    bad = (P * 3)(P(1, 0, 1), P(5, 20, 8), P(0, 0, 0))  # the second triple leaves 32 bits
+    assert f(A, B, -1, good, 3, None) == EINVAL
+    assert f(A, B, 16, good, -1, None) == EINVAL
+    assert f(A, B, 16, None, 3, None) == EINVAL
+    assert f(A, B, 16, bad, 3, None) == EINVAL  # refused before any launch
+    assert f(None, B, 16, good, 3, None) == EINVAL
+    assert f(A + 2, B, 16, good, 3, None) == EINVAL  # not 4-byte aligned
+    assert f(A, A + 32, 16, good, 3, None) == EINVAL  # output rows overlap the input
+    assert f(A + 128, A, 16, good, 3, None) == EINVAL  # input inside the second output row
+    assert f(A, B, 0, good, 3, None) == T.SWZ_OK  # nothing to do
+    assert f(A, B, 16, None, 0, None) == T.SWZ_OK
+    assert f(A, B, 1 << 62, good, 3, None) == EINVAL  # size overflow
+
+
 def test_convert_validation():
     f = lib.swz_convert_layout
     assert f(A, B, 1, 64, 64, 3, 0, -1, None, None) == EINVAL  # element size

@@ -90,6 +90,45 @@ def test_map_negative_shifts():
         assert np.array_equal(from_dev(zout, z), O.swizzle_map(z, *p)), p
 
 
+def test_map_batch_every_triple_one_launch():
+    """The map's workload in one call: 0..65535 under all 125 triples."""
+    announce("map batch 125")
+    x = W.map_offsets()
+    triples = W.map_triples()
+    xin = to_dev(x)
+    out = torch.empty((len(triples), x.size), dtype=xin.dtype, device=DEV)
+    T.swz_map_batch(xin, out, x.size, triples)
+    torch.cuda.synchronize()
+    got = from_dev(out, x).reshape(len(triples), x.size)
+    for j, (B, M, S) in enumerate(triples):
+        assert np.array_equal(got[j], O.swizzle_map(x, B, M, S)), (B, M, S)
+    assert got[triples.index((5, 0, 6))][673] == 683
+
+
+def test_map_batch_chunks_odd_lengths_and_signs():
+    """More triples than one launch takes (300: three launches), either sign
+    of S, odd n (scalar path) and a misaligned input, over 32-bit patterns."""
+    rng = np.random.default_rng(17)
+    triples = []
+    while len(triples) < 300:
+        B, M = int(rng.integers(0, 9)), int(rng.integers(0, 12))
+        S = int(rng.integers(-12, 13))
+        if B + M + abs(S) <= 32:
+            triples.append((B, M, S))
+    z = rng.integers(-(2**31), 2**31, size=1001, dtype=np.int64).astype(np.int32)
+    zin = to_dev(z)
+    for n, src in ((z.size, zin), (z.size - 1, zin[1:])):
+        announce("map batch chunks", n)
+        out = torch.empty((len(triples), n), dtype=zin.dtype, device=DEV)
+        T.swz_map_batch(src, out, n, triples)
+        torch.cuda.synchronize()
+        got = from_dev(out, z).reshape(len(triples), n)
+        ref = z[z.size - n:]
+        for j, p in enumerate(triples):
+            assert np.array_equal(got[j], O.swizzle_map(ref, *p)), p
+    T.swz_map_batch(zin, zin, 0, triples)  # n = 0 is a no-op
+
+
 # ----------------------------------------------------------- transposes
 
 KINDS = [

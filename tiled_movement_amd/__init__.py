@@ -32,6 +32,7 @@ LAYOUTS = {"swizzle": LAYOUT_SWIZZLE, "pad": LAYOUT_PAD, "plain": LAYOUT_PLAIN, 
 
 EXPORTS = (
     "swz_map",
+    "swz_map_batch",
     "swz_transpose",
     "swz_convert_layout",
     "swz_stage_operand",
@@ -112,6 +113,7 @@ def _load() -> ctypes.CDLL:
     i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     P = ctypes.POINTER
     lib.swz_map.argtypes = [vp, vp, i64, Params, vp]
+    lib.swz_map_batch.argtypes = [vp, vp, i64, vp, i32, vp]
     lib.swz_transpose.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_convert_layout.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_stage_operand.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
@@ -181,6 +183,13 @@ def _layout(layout) -> int:
 def swz_map(inp, out, n: int, params, stream=None) -> None:
     B, M, S = params
     _check(lib.swz_map(_ptr(inp), _ptr(out), n, Params(B, M, S), _stream(stream, inp, out)), "swz_map")
+
+
+def swz_map_batch(inp, out, n: int, params_list, stream=None) -> None:
+    """out[j][i] = Swizzle(params_list[j])(inp[i]); out holds len(params_list) rows of n."""
+    arr = (Params * max(len(params_list), 1))(*[Params(*p) for p in params_list])
+    _check(lib.swz_map_batch(_ptr(inp), _ptr(out), n, ctypes.addressof(arr), len(params_list),
+                             _stream(stream, inp, out)), "swz_map_batch")
 
 
 def swz_transpose(src, dst, rows: int, cols: int, elem_bytes: int, layout="swizzle", read_kind: int = READ_AUTO,

@@ -154,6 +154,37 @@ SWZ_API int swz_map(const int32_t* d_in, int32_t* d_out, int64_t n, swz_params p
     return hip_status(swz::launch_map(d_in, d_out, n, p, static_cast<hipStream_t>(stream)));
 }
 
+SWZ_API int swz_map_batch(const int32_t* d_in, int32_t* d_out, int64_t n, const swz_params* h_params,
+                          int32_t n_params, void* stream) {
+    if (n < 0 || n_params < 0) return SWZ_EINVAL;
+    if (n_params > 0 && !h_params) return SWZ_EINVAL;
+    for (int32_t j = 0; j < n_params; ++j) {
+        const swz_params& p = h_params[j];
+        const int64_t abs_s = p.S < 0 ? -static_cast<int64_t>(p.S) : p.S;
+        if (p.B < 0 || p.M < 0 || static_cast<int64_t>(p.B) + p.M + abs_s > 32) return SWZ_EINVAL;
+    }
+    if (n == 0 || n_params == 0) return SWZ_OK;
+    if (!d_in || !d_out) return SWZ_EINVAL;
+    if (reinterpret_cast<uintptr_t>(d_in) % 4 || reinterpret_cast<uintptr_t>(d_out) % 4) return SWZ_EINVAL;
+    int64_t in_bytes, out_elems, out_bytes;
+    if (!mul_ok(n, 4, &in_bytes) || !mul_ok(n, n_params, &out_elems) || !mul_ok(out_elems, 4, &out_bytes))
+        return SWZ_EINVAL;
+    if (overlaps(d_in, in_bytes, d_out, out_bytes)) return SWZ_EINVAL;
+    const auto st = static_cast<hipStream_t>(stream);
+    for (int32_t j0 = 0; j0 < n_params; j0 += swz::kMapBatch) {
+        const int count = n_params - j0 < swz::kMapBatch ? n_params - j0 : swz::kMapBatch;
+        swz::MapParamPack pk{};
+        for (int k = 0; k < count; ++k) {
+            pk.B[k] = static_cast<uint8_t>(h_params[j0 + k].B);
+            pk.M[k] = static_cast<uint8_t>(h_params[j0 + k].M);
+            pk.S[k] = static_cast<int8_t>(h_params[j0 + k].S);
+        }
+        const int rc = hip_status(swz::launch_map_batch(d_in, d_out + static_cast<int64_t>(j0) * n, n, pk, count, st));
+        if (rc != SWZ_OK) return rc;
+    }
+    return SWZ_OK;
+}
+
 SWZ_API int swz_plan(int32_t op, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t layout, int32_t read_kind,
                      const swz_params* p_or_null, swz_plan_info* out) {
     if (!out || (op != 0 && op != 1) || rows < 0 || cols < 0) return SWZ_EINVAL;

@@ -32,6 +32,15 @@ hipError_t launch_gemm_frag(const void* fa, const void* fb, float* c, int64_t m,
 hipError_t launch_gemm_tiles(const void* a, const void* bt, float* c, int64_t m, int64_t n, int64_t k,
                              const LdsLayout& layout, hipStream_t stream);
 hipError_t launch_map(const int32_t* in, int32_t* out, int64_t n, swz_params p, hipStream_t stream);
+
+// Up to kMapBatch triples of one batched-map launch, passed by value.
+constexpr int kMapBatch = 128;
+struct MapParamPack {
+    uint8_t B[kMapBatch], M[kMapBatch];
+    int8_t S[kMapBatch];
+};
+hipError_t launch_map_batch(const int32_t* in, int32_t* out, int64_t n, const MapParamPack& pk, int count,
+                            hipStream_t stream);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 hipError_t launch_lds_probe(const uint32_t* addrs, const uint64_t* masks, int n_patterns, int width, bool write,
                             int iters, int waves, uint64_t* cycles, hipStream_t stream);
