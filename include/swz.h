@@ -10,7 +10,8 @@
  *
  * Calls: the swizzle map (swz_map, swz_map_batch); transposes and batched layout
  * conversions of 1-, 2- and 4-byte elements through swizzled, padded or
- * plain LDS tiles (swz_transpose, swz_convert_layout); GEMM operand staging
+ * plain LDS tiles (swz_transpose, swz_convert_layout), with a per-shape
+ * tile order (swz_set_tile_order, swz_tune_tile_order); GEMM operand staging
  * into matrix-instruction fragments (swz_stage_operand) and their consumer
  * (swz_gemm_frag); the GEMM that stages its own operands through swizzled
  * tiles (swz_gemm); host-only planning, bank-conflict prediction and layout
@@ -222,6 +223,45 @@ int swz_transpose(const void* d_src, void* d_dst, int64_t rows, int64_t cols, in
 int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, int64_t rows, int64_t cols,
                        int32_t elem_bytes, int32_t layout, int32_t read_kind,
                        const swz_params* p_or_null, void* stream);
+
+/* Order in which the workgroups of a transpose / conversion visit the tiles.
+ * Which order the HBM system serves fastest depends on the matrix shape:
+ * each tile writes its rows at the output pitch, and for long output rows
+ * (32 KiB and more) the default diagonal order loses up to 20% at some
+ * shapes while another order does not.  All orders give the same bits. */
+enum swz_tile_order {
+    SWZ_ORDER_DIAGONAL = 0,      /* tile row tr, tile column (q + tr) mod tiles: the default */
+    SWZ_ORDER_HALF_DIAGONAL = 1, /* tile column (q + tr / 2) mod tiles */
+    SWZ_ORDER_COLUMNS = 2,       /* tile column q: every tile row of one tile column in turn */
+    SWZ_ORDER_STEEP_DIAGONAL = 3 /* tile column (q + 3 tr) mod tiles */
+};
+
+/* Pin the tile order of later swz_transpose / swz_convert_layout calls of
+ * this shape (batch, rows, cols, elem_bytes, read kind after AUTO is
+ * resolved), in every layout; order = -1 removes the entry (back to the
+ * diagonal order).  Host only; the table is shared by all threads and
+ * devices of the process.
+ * Errors: SWZ_EINVAL for negative sizes, an order outside -1..3, or an
+ * element size / read kind that swz_convert_layout would refuse. */
+int swz_set_tile_order(int64_t batch, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t read_kind,
+                       int32_t order);
+
+/* Time every tile order on this conversion and pin the fastest: three
+ * interleaved rounds over the orders, each one untimed and `reps` timed
+ * swz_convert_layout calls with these arguments on the caller's buffers and
+ * stream, timed with HIP events; an order counts its best round, and
+ * replaces the diagonal order only when at least 3% faster (the calls reuse
+ * one buffer pair, which the caches partly hold).  Synchronizes the stream;
+ * allocates no device memory.  d_dst ends up holding the conversion of
+ * d_src (every order writes the same bits).
+ *   reps   : 1..1000.
+ *   chosen : receives the pinned order (enum swz_tile_order).
+ * Errors: those of swz_convert_layout (then no order is pinned for the
+ * shape); SWZ_EINVAL for NULL chosen or reps out of range; SWZ_EHIP if an
+ * event call fails. */
+int swz_tune_tile_order(const void* d_src, void* d_dst, int64_t batch, int64_t rows, int64_t cols,
+                        int32_t elem_bytes, int32_t layout, int32_t read_kind, const swz_params* p_or_null,
+                        int32_t reps, int32_t* chosen, void* stream);
 
 /* GEMM operand staging without compute.  d_src is a K-contiguous operand
  * [mn][k] (A row-major, or B column-major, which is B^T row-major), 16-bit

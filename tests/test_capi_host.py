@@ -79,6 +79,26 @@ def test_map_batch_validation():
     assert f(A, B, 1 << 62, good, 3, None) == EINVAL  # size overflow
 
 
+def test_tile_order_validation():
+    f = lib.swz_set_tile_order
+    assert f(-1, 64, 64, 4, -1, 0) == EINVAL
+    assert f(1, 64, 64, 4, -1, 4) == EINVAL  # no such order
+    assert f(1, 64, 64, 4, -1, -2) == EINVAL
+    assert f(1, 64, 64, 3, -1, 0) == EINVAL  # element size
+    assert f(1, 64, 64, 2, T.READ_SCALAR_COL, 0) == EINVAL  # kind for another element size
+    assert f(1, 64, 64, 4, -1, T.ORDER_COLUMNS) == T.SWZ_OK
+    assert f(1, 64, 64, 4, -1, -1) == T.SWZ_OK  # removed
+    assert f(1, 64, 64, 4, -1, -1) == T.SWZ_OK  # removing twice is fine
+    g = lib.swz_tune_tile_order
+    c = ctypes.c_int32(-7)
+    assert g(A, B, 1, 64, 64, 4, 0, -1, None, 10, None, None) == EINVAL  # no output for the choice
+    assert g(A, B, 1, 64, 64, 4, 0, -1, None, 0, ctypes.byref(c), None) == EINVAL  # reps
+    assert g(A, B, 1, 64, 64, 4, 0, -1, None, 1001, ctypes.byref(c), None) == EINVAL
+    assert g(A, B, 1, 64, 64, 3, 0, -1, None, 10, ctypes.byref(c), None) == EINVAL  # element size
+    assert g(A, B, 0, 64, 64, 4, 0, -1, None, 10, ctypes.byref(c), None) == T.SWZ_OK  # nothing to time
+    assert c.value == T.ORDER_DIAGONAL
+
+
 def test_convert_validation():
     f = lib.swz_convert_layout
     assert f(A, B, 1, 64, 64, 3, 0, -1, None, None) == EINVAL  # element size

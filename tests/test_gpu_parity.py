@@ -325,6 +325,51 @@ def test_narrow_any_valid_swizzle(kind, esz, c):
             check_transpose(a, esz, layout, kind, (B, M, S))
 
 
+# ------------------------------------------------------------ tile orders
+
+
+@pytest.mark.parametrize("order", [T.ORDER_DIAGONAL, T.ORDER_HALF_DIAGONAL, T.ORDER_COLUMNS,
+                                   T.ORDER_STEEP_DIAGONAL])
+def test_every_tile_order_gives_the_transpose(order):
+    """Each order visits every tile once: whole and ragged grids, batches,
+    and the 1-D launch (a batch beyond the grid's z limit)."""
+    cases = [(W.fp32_matrix(3 * 96, 160, seed=40).reshape(3, 96, 160), 4, T.READ_SCALAR_COL),
+             (W.fp16_matrix(2 * 130, 200, seed=41).reshape(2, 130, 200), 2, T.READ_B64_TR16),
+             (W.u8_matrix(136, 520, seed=42).reshape(1, 136, 520), 1, T.READ_B64_TR8),
+             (W.fp32_matrix(70000 * 4, 36, seed=43).reshape(70000, 4, 36), 4, T.READ_SCALAR_COL)]
+    for a, esz, kind in cases:
+        b, r, c = a.shape
+        T.swz_set_tile_order(b, r, c, esz, kind, order)
+        try:
+            for layout in LAYOUTS:
+                announce("tile order", order, a.shape, layout)
+                src = to_dev(a)
+                dst = torch.empty((b, c, r), dtype=src.dtype, device=DEV)
+                T.swz_convert_layout(src, dst, b, r, c, esz, layout, kind)
+                torch.cuda.synchronize()
+                assert np.array_equal(from_dev(dst, a), O.convert_layout(a)), (order, a.shape, layout)
+        finally:
+            T.swz_set_tile_order(b, r, c, esz, kind, -1)
+
+
+def test_tune_tile_order_pins_an_order_and_keeps_the_result():
+    a = W.fp32_matrix(2048, 544, seed=44)
+    src = to_dev(a)
+    dst = torch.empty((544, 2048), dtype=src.dtype, device=DEV)
+    announce("tune tile order")
+    try:
+        chosen = T.swz_tune_tile_order(src, dst, 1, 2048, 544, 4, "swizzle", reps=3)
+        assert chosen in (T.ORDER_DIAGONAL, T.ORDER_HALF_DIAGONAL, T.ORDER_COLUMNS, T.ORDER_STEEP_DIAGONAL)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(dst, a), O.transpose(a))
+        dst.zero_()
+        T.swz_transpose(src, dst, 2048, 544, 4, "direct")  # the pinned order serves every layout
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(dst, a), O.transpose(a))
+    finally:
+        T.swz_set_tile_order(1, 2048, 544, 4, T.READ_AUTO, -1)
+
+
 # ------------------------------------------------------- operand staging
 
 

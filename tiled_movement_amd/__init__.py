@@ -28,6 +28,7 @@ READ_HNARROW1, READ_HNARROW2, READ_HNARROW4, READ_HNARROW8, READ_HNARROW16, READ
 READ_BNARROW1, READ_BNARROW2, READ_BNARROW4, READ_BNARROW8, READ_BNARROW16, READ_BNARROW32, READ_BNARROW64 = (
     17, 18, 19, 20, 21, 22, 23)
 FRAG_MFMA_F32_16X16X32_BF16 = 0
+ORDER_DIAGONAL, ORDER_HALF_DIAGONAL, ORDER_COLUMNS, ORDER_STEEP_DIAGONAL = 0, 1, 2, 3
 LAYOUTS = {"swizzle": LAYOUT_SWIZZLE, "pad": LAYOUT_PAD, "plain": LAYOUT_PLAIN, "direct": LAYOUT_SWIZZLE_DIRECT}
 
 EXPORTS = (
@@ -35,6 +36,8 @@ EXPORTS = (
     "swz_map_batch",
     "swz_transpose",
     "swz_convert_layout",
+    "swz_set_tile_order",
+    "swz_tune_tile_order",
     "swz_stage_operand",
     "swz_gemm_frag",
     "swz_gemm",
@@ -116,6 +119,8 @@ def _load() -> ctypes.CDLL:
     lib.swz_map_batch.argtypes = [vp, vp, i64, vp, i32, vp]
     lib.swz_transpose.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_convert_layout.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, P(Params), vp]
+    lib.swz_set_tile_order.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.swz_tune_tile_order.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, P(Params), i32, P(ctypes.c_int32), vp]
     lib.swz_stage_operand.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_gemm_frag.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
     lib.swz_gemm.argtypes = [vp, vp, vp, i64, i64, i64, i32, P(Params), vp]
@@ -183,6 +188,21 @@ def _layout(layout) -> int:
 def swz_map(inp, out, n: int, params, stream=None) -> None:
     B, M, S = params
     _check(lib.swz_map(_ptr(inp), _ptr(out), n, Params(B, M, S), _stream(stream, inp, out)), "swz_map")
+
+
+def swz_set_tile_order(batch: int, rows: int, cols: int, elem_bytes: int, read_kind: int = READ_AUTO,
+                       order: int = ORDER_DIAGONAL) -> None:
+    _check(lib.swz_set_tile_order(batch, rows, cols, elem_bytes, read_kind, order), "swz_set_tile_order")
+
+
+def swz_tune_tile_order(src, dst, batch: int, rows: int, cols: int, elem_bytes: int, layout="swizzle",
+                        read_kind: int = READ_AUTO, params=None, reps: int = 10, stream=None) -> int:
+    """Time every tile order on this conversion, pin the fastest and return it."""
+    chosen = ctypes.c_int32(-1)
+    _check(lib.swz_tune_tile_order(_ptr(src), _ptr(dst), batch, rows, cols, elem_bytes, _layout(layout), read_kind,
+                                   _params(params), reps, ctypes.byref(chosen), _stream(stream, src, dst)),
+           "swz_tune_tile_order")
+    return chosen.value
 
 
 def swz_map_batch(inp, out, n: int, params_list, stream=None) -> None:

@@ -2,6 +2,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "chooser.h"
 #include "launch.h"
@@ -129,6 +132,20 @@ swz::LdsLayout layout_of(const swz_plan_info& pl) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SWZ_OK : SWZ_EHIP; }
 
+// Tile orders pinned per conversion shape (swz_set_tile_order,
+// swz_tune_tile_order); shapes not listed use the diagonal order.
+using ShapeKey = std::tuple<int, int64_t, int64_t, int64_t>;  // read kind, batch, rows, cols
+std::mutex g_order_mu;
+std::map<ShapeKey, int>& order_table() {
+    static std::map<ShapeKey, int> t;
+    return t;
+}
+int pinned_order(int kind, int64_t batch, int64_t rows, int64_t cols) {
+    std::lock_guard<std::mutex> lock(g_order_mu);
+    const auto it = order_table().find(ShapeKey{kind, batch, rows, cols});
+    return it == order_table().end() ? SWZ_ORDER_DIAGONAL : it->second;
+}
+
 }  // namespace
 
 SWZ_API const char* swz_strerror(int status) {
@@ -212,13 +229,89 @@ SWZ_API int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, in
     if (ps % elem_bytes || pd % elem_bytes) return SWZ_EINVAL;
     if (overlaps(d_src, bytes, d_dst, bytes)) return SWZ_EINVAL;
     swz::ConvertJob job{d_src, d_dst, batch, rows, cols, layout_of(pl), pl.aligned != 0,
-                        layout == SWZ_LAYOUT_SWIZZLE_DIRECT};
+                        layout == SWZ_LAYOUT_SWIZZLE_DIRECT, pinned_order(pl.read_kind, batch, rows, cols)};
     return hip_status(swz::launch_convert(pl.read_kind, job, static_cast<hipStream_t>(stream)));
 }
 
 SWZ_API int swz_transpose(const void* d_src, void* d_dst, int64_t rows, int64_t cols, int32_t elem_bytes,
                           int32_t layout, int32_t read_kind, const swz_params* p_or_null, void* stream) {
     return swz_convert_layout(d_src, d_dst, 1, rows, cols, elem_bytes, layout, read_kind, p_or_null, stream);
+}
+
+SWZ_API int swz_set_tile_order(int64_t batch, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t read_kind,
+                               int32_t order) {
+    if (batch < 0 || rows < 0 || cols < 0) return SWZ_EINVAL;
+    if (order < -1 || order > SWZ_ORDER_STEEP_DIAGONAL) return SWZ_EINVAL;
+    swz_plan_info pl;
+    const int st = make_plan(0, rows, cols, elem_bytes, SWZ_LAYOUT_SWIZZLE, read_kind, nullptr, true, true, &pl);
+    if (st != SWZ_OK) return st;
+    std::lock_guard<std::mutex> lock(g_order_mu);
+    const ShapeKey key{pl.read_kind, batch, rows, cols};
+    if (order < 0)
+        order_table().erase(key);
+    else
+        order_table()[key] = order;
+    return SWZ_OK;
+}
+
+SWZ_API int swz_tune_tile_order(const void* d_src, void* d_dst, int64_t batch, int64_t rows, int64_t cols,
+                                int32_t elem_bytes, int32_t layout, int32_t read_kind, const swz_params* p_or_null,
+                                int32_t reps, int32_t* chosen, void* stream) {
+    if (!chosen || reps < 1 || reps > 1000) return SWZ_EINVAL;
+    if (batch < 0 || rows < 0 || cols < 0) return SWZ_EINVAL;
+    swz_plan_info pl;
+    int st = make_plan(0, rows, cols, elem_bytes, layout, read_kind, p_or_null, true, true, &pl);
+    if (st != SWZ_OK) return st;
+    int64_t n, n2, bytes;
+    if (!mul_ok(batch, rows, &n) || !mul_ok(n, cols, &n2) || !mul_ok(n2, elem_bytes, &bytes)) return SWZ_EINVAL;
+    if (bytes == 0) {
+        *chosen = SWZ_ORDER_DIAGONAL;
+        return SWZ_OK;
+    }
+    if (!d_src || !d_dst) return SWZ_EINVAL;
+    const auto strm = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return SWZ_EHIP;
+    }
+    // Three rounds over the orders (interleaved, so slow drifts of clock or
+    // temperature hit them alike), each one untimed and reps timed calls;
+    // an order's time is its best round.
+    constexpr int kOrders = SWZ_ORDER_STEEP_DIAGONAL + 1, kRounds = 3;
+    float t[kOrders];
+    for (int o = 0; o < kOrders; ++o) t[o] = -1.0f;
+    for (int round = 0; round < kRounds && st == SWZ_OK; ++round) {
+        for (int order = 0; order < kOrders && st == SWZ_OK; ++order) {
+            st = swz_set_tile_order(batch, rows, cols, elem_bytes, pl.read_kind, order);
+            for (int r = 0; r <= reps && st == SWZ_OK; ++r) {
+                if (r == 1 && hipEventRecord(e0, strm) != hipSuccess) st = SWZ_EHIP;
+                if (st == SWZ_OK)
+                    st = swz_convert_layout(d_src, d_dst, batch, rows, cols, elem_bytes, layout, read_kind,
+                                            p_or_null, stream);
+            }
+            float ms = 0.0f;
+            if (st == SWZ_OK && (hipEventRecord(e1, strm) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                                 hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+                st = SWZ_EHIP;
+            if (st == SWZ_OK && (t[order] < 0.0f || ms < t[order])) t[order] = ms;
+        }
+    }
+    // Another order replaces the diagonal one only when it is at least 3%
+    // faster: the timed calls reuse one buffer pair, which the caches hold
+    // in part, so small differences need not carry over to other buffers.
+    int best = SWZ_ORDER_DIAGONAL;
+    for (int o = 1; o < kOrders; ++o)
+        if (t[o] >= 0.0f && t[o] < t[best] && (best != SWZ_ORDER_DIAGONAL || t[o] < 0.97f * t[best])) best = o;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != SWZ_OK) {
+        (void)swz_set_tile_order(batch, rows, cols, elem_bytes, pl.read_kind, -1);
+        return st;
+    }
+    // the last call left the result in d_dst; the pinned order gives the same bits
+    *chosen = best;
+    return swz_set_tile_order(batch, rows, cols, elem_bytes, pl.read_kind, best);
 }
 
 SWZ_API int swz_stage_operand(const void* d_src, void* d_frag, int64_t mn, int64_t k, int32_t elem_bytes,

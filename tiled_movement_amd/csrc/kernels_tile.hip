@@ -63,18 +63,23 @@ __device__ __forceinline__ void gstore16(uint8_t* p, u32x4 v) {
 }
 
 // Tile (batch b, tile row tr, tile column tc) of linear tile index t.
-// Diagonal order: t -> tr = t % tiles_r, tc = (t / tiles_r + tr) % tiles_c,
-// one-to-one for any grid shape (for each tr, the map q -> (q + tr) mod
-// tiles_c is a permutation).  Row-major: tc fastest.
+// Diagonal orders: t -> tr = t % tiles_r, tc = (t / tiles_r + f(tr)) %
+// tiles_c with f(tr) = (tr * O.num) >> O.sh: slope 1 (the default), 1/2, 3,
+// or 0 (tile columns in turn).  One-to-one for any grid shape (for each tr,
+// q -> (q + f(tr)) mod tiles_c is a permutation).  Row-major: tc fastest.
+struct TileOrder {
+    uint32_t num, sh;
+};
+
 template <bool DIAGONAL>
-__device__ __forceinline__ void decode_tile(int64_t t, int64_t tiles_r, int64_t tiles_c, int64_t& b, int64_t& tr,
-                                            int64_t& tc) {
+__device__ __forceinline__ void decode_tile(int64_t t, int64_t tiles_r, int64_t tiles_c, TileOrder O, int64_t& b,
+                                            int64_t& tr, int64_t& tc) {
     const int64_t per = tiles_r * tiles_c;
     b = t / per;
     const int64_t w = t - b * per;
     if (DIAGONAL) {
         tr = w % tiles_r;
-        tc = (w / tiles_r + tr) % tiles_c;
+        tc = (w / tiles_r + ((tr * O.num) >> O.sh) % tiles_c) % tiles_c;
     } else {
         tr = w / tiles_c;
         tc = w % tiles_c;
@@ -564,27 +569,28 @@ __device__ __forceinline__ void convert_tile(const uint8_t* __restrict__ S, uint
 // otherwise a 1-D chunk of the linear tile order (grids beyond the
 // hardware's y / z limits).
 template <bool DIAGONAL, bool GRID3D>
-__device__ __forceinline__ void my_tile(int64_t tiles_r, int64_t tiles_c, int64_t tile0, int64_t& b, int64_t& tr,
-                                        int64_t& tc) {
+__device__ __forceinline__ void my_tile(int64_t tiles_r, int64_t tiles_c, int64_t tile0, TileOrder O, int64_t& b,
+                                        int64_t& tr, int64_t& tc) {
     if (GRID3D) {
         b = blockIdx.z;
         if (DIAGONAL) {
+            const uint32_t n = static_cast<uint32_t>(tiles_c);
             tr = blockIdx.x;
-            tc = static_cast<int64_t>((blockIdx.y + blockIdx.x % static_cast<uint32_t>(tiles_c)) %
-                                      static_cast<uint32_t>(tiles_c));
+            tc = static_cast<int64_t>((blockIdx.y + ((blockIdx.x * O.num) >> O.sh) % n) % n);
         } else {
             tc = blockIdx.x;
             tr = blockIdx.y;
         }
     } else {
-        decode_tile<DIAGONAL>(tile0 + blockIdx.x, tiles_r, tiles_c, b, tr, tc);
+        decode_tile<DIAGONAL>(tile0 + blockIdx.x, tiles_r, tiles_c, O, b, tr, tc);
     }
 }
 
 template <int KIND, int FILL, bool ALIGNED, bool GRID3D>
 __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                             int64_t rows, int64_t cols, int64_t tiles_r,
-                                                            int64_t tiles_c, int64_t tile0, LdsLayout L) {
+                                                            int64_t tiles_c, int64_t tile0, LdsLayout L,
+                                                            TileOrder O) {
     using K = Kind<KIND>;
     constexpr bool PADDED = FILL == kPadded;
     static_assert(FILL != kDirect || ALIGNED, "the direct fill needs 16-byte aligned rows");
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __res
     const uint32_t rbase = lane_base<KIND, false, PADDED>(t, L);
 
     int64_t b, tr, tc;
-    my_tile<SWZ_TILE_ORDER != 0, GRID3D>(tiles_r, tiles_c, tile0, b, tr, tc);
+    my_tile<SWZ_TILE_ORDER != 0, GRID3D>(tiles_r, tiles_c, tile0, O, b, tr, tc);
     const int64_t r0 = tr * K::TR, c0 = tc * K::TC;
     const uint8_t* S = src + b * plane;
     uint8_t* D = dst + b * plane;
@@ -669,7 +675,7 @@ __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(cons
     const uint32_t rbase = lane_base<KD, false, PADDED>(t, L);
 
     int64_t b, tm, tk;
-    my_tile<SWZ_STAGE_ORDER != 0, GRID3D>(tiles_m, tiles_k, tile0, b, tm, tk);
+    my_tile<SWZ_STAGE_ORDER != 0, GRID3D>(tiles_m, tiles_k, tile0, TileOrder{1u, 0u}, b, tm, tk);
     const int64_t r0 = tm * K::TR, k0 = tk * K::TC;
     if (r0 + K::TR <= mn && k0 + K::TC <= k)
         stage_tile<FILL, true>(src, frag, mn, k, r0, k0, lds, wbase, rbase, L, t);
@@ -692,17 +698,21 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
     auto* d = static_cast<uint8_t*>(j.dst);
     const bool diag = SWZ_TILE_ORDER != 0;
     const int64_t gx = diag ? tiles_r : tiles_c, gy = diag ? tiles_c : tiles_r;
+    // slope of the diagonal order per SWZ_ORDER_* value: 1, 1/2, 0, 3
+    static constexpr TileOrder kOrders[4] = {{1u, 0u}, {1u, 1u}, {0u, 0u}, {3u, 0u}};
+    const TileOrder O = kOrders[j.order >= 0 && j.order < 4 ? j.order : 0];
     if (fits_3d(gx, gy, j.batch, K::NT)) {
         hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, true>),
                            dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(j.batch)),
-                           dim3(K::NT), occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES), stream, s, d, j.rows, j.cols, tiles_r, tiles_c, int64_t(0), j.layout);
+                           dim3(K::NT), occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES), stream, s, d, j.rows, j.cols,
+                           tiles_r, tiles_c, int64_t(0), j.layout, O);
         return;
     }
     for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
         const int64_t n = n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid;
         hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, false>), dim3(static_cast<unsigned>(n)), dim3(K::NT),
                            occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES),
-                           stream, s, d, j.rows, j.cols, tiles_r, tiles_c, t0, j.layout);
+                           stream, s, d, j.rows, j.cols, tiles_r, tiles_c, t0, j.layout, O);
     }
 }
 

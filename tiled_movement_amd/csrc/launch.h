@@ -15,6 +15,7 @@ struct ConvertJob {
     LdsLayout layout;
     bool aligned;  // 16-byte vector path allowed (pointers and pitches)
     bool direct;   // direct HBM -> LDS fill (needs aligned and an unpadded layout)
+    int order;     // tile order, enum swz_tile_order
 };
 
 struct StageJob {
