@@ -108,14 +108,18 @@ enum swz_layout {
  *               ("CUDA 013 - Swizzle 的工作原理", usage example 4).  Reads as
  *               SCALAR_COL: each lane reads four rows of one column.
  *  HNARROW1 .. HNARROW32 : the same for 2-byte elements in matrices of 1,
- *               2, 4, 8, 16 or 32 columns: 4096-byte tiles of 2048/cols
- *               rows.  Staged as 4-byte LDS writes (so M >= 1); each lane
- *               reads eight rows of one column with 2-byte loads and writes
- *               them as 16 bytes of one output row.
+ *               2, 4, 8, 16 or 32 columns, staged as 4-byte LDS writes (so
+ *               M >= 1).  2 to 16 columns: 4096-byte tiles of 2048/cols
+ *               rows, each lane reading eight rows of one column with 2-byte
+ *               loads into 16 bytes of one output row.  1 and 32 columns:
+ *               each lane reads 4-byte words (eight rows of two columns, or
+ *               of the one column) and splits them in registers; tiles of
+ *               2048 x 1 and 128 x 32.
  *  BNARROW1 .. BNARROW64 : the same for 1-byte elements in matrices of 1 to
- *               64 columns (powers of two): 4096-byte tiles of 4096/cols
- *               rows, 4-byte LDS writes (M >= 2), 16 rows of one column per
- *               lane read with 1-byte loads.
+ *               64 columns (powers of two), 4-byte LDS writes (M >= 2):
+ *               each lane reads 4-byte words of 16 rows and up to 4 columns
+ *               and transposes them in registers into up to four 16-byte
+ *               output pieces; tiles of 4096 * min(cols, 4) bytes.
  *  AUTO       : 4-byte -> NARROW<cols> when cols is 1, 2, 4, 8 or 16, else
  *               SCALAR_COL; 2-byte -> HNARROW<cols> when cols is a power of
  *               two up to 32, else B64_TR16 when cols <= 64, B128_8X8 when
