@@ -18,7 +18,7 @@ Pattern families:
           shared word: no conflict if words, not bytes, are what conflict)
 
 Usage:
-  python -m tiled_movement_amd.lds_bankbench --out gpurun_out/lds_bank.json
+  python -m tiled_movement_amd.lds_bankbench --out lds_bank.json
   python -m tiled_movement_amd.lds_bankbench --per-dispatch --families kernel,bank ...
       (one dispatch per pattern, for rocprofv3 --pmc counter runs)
 """
