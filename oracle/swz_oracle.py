@@ -47,6 +47,7 @@ __all__ = [
     "stage_operand",
     "stage_operand_loops",
     "bf16_to_f64",
+    "f32_to_bf16_bits",
     "gemm_bf16",
     "gemm_error_bound",
     "BankModel",
@@ -253,6 +254,31 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact value of bf16 bit patterns: the upper half of an fp32 word."""
     b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of fp32 values rounded to nearest, ties to the even
+    pattern, by the definition: of the two bf16 values around x (its bit
+    pattern cut to the upper half, and the next one away from zero), take the
+    nearer one; NaN becomes a quiet NaN.  Written out per element in fp64
+    (every fp32 and bf16 value is exact there); the next value past the
+    largest finite bf16 is 2^128, which rounds to infinity."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lo = (u >> 16) << 16
+    hi = lo + (1 << 16)
+    xv = x.astype(np.float64)
+    # NaN inputs (and the patterns past infinity) are sorted out at the end
+    with np.errstate(over="ignore", invalid="ignore"):
+        lov = lo.astype(np.uint32).view(np.float32).astype(np.float64)
+        hiv = hi.astype(np.uint32).view(np.float32).astype(np.float64)
+        hiv = np.where(np.isinf(hiv) & ~np.isinf(lov), np.sign(xv) * 2.0 ** 128, hiv)
+        d_lo, d_hi = np.abs(xv - lov), np.abs(hiv - xv)
+    even_lo = ((lo >> 16) & 1) == 0
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ~even_lo)
+    out = np.where(take_hi, hi >> 16, lo >> 16)
+    out = np.where(np.isnan(xv), (u >> 16) | 0x40, out)
+    return out.astype(np.uint16)
 
 
 def gemm_bf16(a_bits: np.ndarray, bt_bits: np.ndarray) -> np.ndarray:

@@ -498,3 +498,40 @@ def test_fold_matches_brute_force_additivity():
         assert additive == (coll == 0), (B, M, S, active, base)
         seen[coll == 0] += 1
     assert seen[True] > 20 and seen[False] > 20
+
+
+# ------------------------------------------------------ bf16 rounding
+
+
+def test_bf16_rounding_matches_the_library_conversion():
+    """The oracle's nearest-even rounding to bf16 against torch's fp32 ->
+    bfloat16 conversion (round to nearest even) on values of every size,
+    exact ties included."""
+    import torch
+
+    rng = np.random.default_rng(31)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(3.0),
+        (rng.standard_normal(2000) * 1e30).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-30).astype(np.float32),
+        # exact ties: an upper half with the low 16 bits 0x8000
+        ((rng.integers(0x0080, 0x7F00, 2000).astype(np.uint32) << 16) | 0x8000).view(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, np.finfo(np.float32).max, -np.finfo(np.float32).max,
+                  np.finfo(np.float32).tiny, 1e-45], dtype=np.float32),
+    ])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f32_to_bf16_bits(x), ref)
+
+
+def test_bf16_rounding_ties_go_to_even_and_nan_stays_nan():
+    one = np.float32(1.0)
+    half_ulp, ulp = np.float32(2.0 ** -8), np.float32(2.0 ** -7)
+    got = O.f32_to_bf16_bits(np.array([one, one + half_ulp, one + ulp + half_ulp, -(one + half_ulp)],
+                                      dtype=np.float32))
+    assert list(got) == [0x3F80, 0x3F80, 0x3F82, 0xBF80]
+    assert O.f32_to_bf16_bits(np.array([np.finfo(np.float32).max], dtype=np.float32))[0] == 0x7F80  # to infinity
+    nan = O.f32_to_bf16_bits(np.array([np.nan], dtype=np.float32))[0]
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x007F) != 0
+    # the bf16 values themselves are fixed points
+    b = np.arange(0, 0x7F80, 7, dtype=np.uint32)
+    assert np.array_equal(O.f32_to_bf16_bits((b << 16).view(np.float32)), b.astype(np.uint16))
