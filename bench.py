@@ -18,9 +18,8 @@ Usage:
       time one workload only (used for profiler runs), optionally rotating over
       exactly P buffer pairs; NAME is one of
       fp32_transpose, fp16_transpose, fp16_transpose_tr, u8_transpose, bf16_convert,
-      bf16_stage, fp32_narrow8, fp16_narrow8, u8_narrow16, map, copy, copy_128, memcpy_d2d, bf16_gemm,
-      bf16_gemm_fused,
-      torch_mm_bf16
+      bf16_stage, fp32_narrow8, fp16_narrow8, u8_narrow16, map, map_batch, copy, copy_128, memcpy_d2d,
+      bf16_gemm, bf16_gemm_fused, bf16_gemm_fused_bf16c, torch_mm_bf16
 """
 
 from __future__ import annotations
@@ -56,6 +55,7 @@ WORKLOADS = {
     "map_batch": "Swizzle<B,M,S> of int32 offsets 0..65535 under all 125 triples in one call (8,192,000 outputs)",
     "bf16_gemm": "C[8192x8192] fp32 = A * B^T from the staged fragments of A[8192x4096] and B[4096x8192] (16x16x32 bf16 MFMA)",
     "bf16_gemm_fused": "C[8192x8192] fp32 = A * B^T, A[8192x4096] row-major and B[4096x8192] column-major staged through swizzled 256x64 LDS tiles inside the GEMM (16x16x32 bf16 MFMA)",
+    "bf16_gemm_fused_bf16c": "the same fused GEMM with C written as bf16 (rounded to nearest even), like the runtime library GEMM below",
     "torch_mm_bf16": "runtime library GEMM (torch.mm, bf16 in and out) of the same 8192x8192x4096 product, for context",
     "copy": "reference 16-byte vector copy of 64 MiB (read once, write once)",
     "copy_128": "reference 16-byte vector copy of 128 MiB (the byte count of the 256 MiB workloads)",
@@ -251,18 +251,20 @@ def build(ctx, name, layout):
         info["_keep"] = (fa, fb, c)
         return step, 2 * m * n * k, info
 
-    if name == "bf16_gemm_fused":
+    if name in ("bf16_gemm_fused", "bf16_gemm_fused_bf16c"):
         m = n = 8192
         k = 4096
         ao, bo = W.bf16_operands(m, n, k, seed=0)
         a, bt = ctx.copies(ao, 1)[0], ctx.copies(bo, 1)[0]
-        c = ctx.torch.empty((m, n), dtype=ctx.torch.float32, device=ctx.dev)
+        bf16c = name == "bf16_gemm_fused_bf16c"
+        c = ctx.torch.empty((m, n), dtype=ctx.torch.int16 if bf16c else ctx.torch.float32, device=ctx.dev)
         pa, pb, pc = a.data_ptr(), bt.data_ptr(), c.data_ptr()
+        ctype = T.C_BF16 if bf16c else T.C_F32
 
         def step(i):
-            rc = lib.swz_gemm(pa, pb, pc, m, n, k, lay, None, stream)
+            rc = lib.swz_gemm_ex(pa, pb, pc, m, n, k, lay, None, ctype, stream)
             if rc:
-                ctx.check(rc, "swz_gemm")
+                ctx.check(rc, "swz_gemm_ex")
 
         pl = T.swz_plan(1, m, k, 2, "direct" if layout == "swizzle" else layout)
         info.update({"m": m, "n": n, "k": k, "flops_per_step": 2 * m * n * k, "unit_of_value": "TFLOP/s",
@@ -427,8 +429,9 @@ def main(argv=None):
         for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "fp16_transpose_tr",
                       "u8_transpose", "bf16_convert", "bf16_stage", "fp32_narrow8", "fp16_narrow8", "u8_narrow16",
                       "map", "bf16_gemm",
-                      "bf16_gemm_fused", "torch_mm_bf16"):
-            for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map", "bf16_gemm", "torch_mm_bf16")
+                      "bf16_gemm_fused", "bf16_gemm_fused_bf16c", "torch_mm_bf16"):
+            for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map", "bf16_gemm", "torch_mm_bf16",
+                                                  "bf16_gemm_fused_bf16c")
                         else ("swizzle", "plain") if wname == "bf16_gemm_fused"
                         else ("swizzle", "pad", "plain", "direct")):
                 s2, nb2, inf2 = build(ctx, wname, lay)
@@ -442,7 +445,7 @@ def main(argv=None):
                                                  "batch_GBps": round(rate3, 1)})
                     log(f"map batch: {ms3 * 1e3:.2f} us per 125 triples, {rate3:.1f} GB/s")
                     continue
-                if wname in ("bf16_gemm", "bf16_gemm_fused", "torch_mm_bf16"):
+                if wname in ("bf16_gemm", "bf16_gemm_fused", "bf16_gemm_fused_bf16c", "torch_mm_bf16"):
                     rate, ms2 = median_rate(s2, nb2, steps=20, warmup=5)
                     tflops = rate / 1e3  # nb2 counts flops, so rate is GFLOP/s
                     key = f"{wname}/{lay}" if wname == "bf16_gemm_fused" else wname
@@ -512,7 +515,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "extra": extra,
     }
-    if name in ("bf16_gemm", "bf16_gemm_fused", "torch_mm_bf16"):  # a contraction: flops, against the bf16 matrix peak
+    if name in ("bf16_gemm", "bf16_gemm_fused", "bf16_gemm_fused_bf16c", "torch_mm_bf16"):  # a contraction: flops, against the bf16 matrix peak
         tflops = value / 1e3
         line.update({"metric": "bf16 GEMM, TFLOP/s", "value": round(tflops, 1),
                      "unit": "TFLOP/s", "dtype": "bf16"})

@@ -333,6 +333,17 @@ int swz_gemm_frag(const void* d_fa, const void* d_fb, float* d_c, int64_t m, int
 int swz_gemm(const void* d_a, const void* d_bt, float* d_c, int64_t m, int64_t n, int64_t k, int32_t layout,
              const swz_params* p_or_null, void* stream);
 
+/* Element type of the GEMM result. */
+enum swz_c_type { SWZ_C_F32 = 0, SWZ_C_BF16 = 1 };
+
+/* swz_gemm with a choice of result type: c_type SWZ_C_F32 is swz_gemm
+ * (d_c float [m][n]); SWZ_C_BF16 writes d_c as bf16 [m][n] (uint16 bit
+ * patterns), each element the fp32 result of swz_gemm rounded to nearest
+ * with ties to even (NaN stays NaN), half the bytes of C to write.
+ * Errors: those of swz_gemm; SWZ_EINVAL for another c_type. */
+int swz_gemm_ex(const void* d_a, const void* d_bt, void* d_c, int64_t m, int64_t n, int64_t k, int32_t layout,
+                const swz_params* p_or_null, int32_t c_type, void* stream);
+
 /* Host only.  The swizzle the library uses for a tile of tile_rows x
  * tile_cols elements of elem_bytes, staged by vec_bytes-wide stores and read
  * back by read_kind, under the built-in gfx950 LDS bank model:

@@ -514,6 +514,16 @@ def test_narrow_kind_validation():
     assert T.swz_choose(4, 4, 128, 8, T.READ_NARROW8) == (5, 0, 5)
 
 
+def test_fused_gemm_bf16_validation():
+    f = lib.swz_gemm_ex
+    assert f(A, B, C, 32, 32, 32, 0, None, 2, None) == EINVAL  # no such result type
+    assert f(A, B, C, 24, 32, 32, 0, None, T.C_BF16, None) == EINVAL  # m not a multiple of 16
+    assert f(A, B, C, 32, 32, 32, T.LAYOUT_PAD, None, T.C_BF16, None) == EUNSUP
+    assert f(A, B, A + 1024, 32, 32, 32, 0, None, T.C_BF16, None) == EINVAL  # C overlaps A
+    assert f(A, B, C + 8, 32, 32, 32, 0, None, T.C_BF16, None) == EINVAL  # alignment
+    assert f(A, B, C, 0, 32, 32, 0, None, T.C_BF16, None) == T.SWZ_OK  # empty: no launch
+
+
 def test_fused_gemm_validation():
     f = lib.swz_gemm
     assert f(A, B, C, 24, 32, 32, 0, None, None) == EINVAL  # m not a multiple of 16

@@ -161,3 +161,77 @@ def test_fused_full_size_sampled_rows(layout):
     got = c[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
     ref = O.gemm_bf16(a[rows], bt)
     assert np.all(np.abs(got - ref) <= 2 * O.gemm_error_bound(a[rows], bt))
+
+
+# ------------------------------------------------- bf16 result (swz_gemm_ex)
+
+
+def fused_bf16_on_gpu(a, bt, layout="swizzle", params=None):
+    m, k = a.shape
+    n = bt.shape[0]
+    c = torch.full((m, n), -1, dtype=torch.int16, device=DEV)
+    da = torch.from_numpy(a.view(np.int16)).to(DEV)
+    db = torch.from_numpy(bt.view(np.int16)).to(DEV)
+    T.swz_gemm_ex(da, db, c, m, n, k, layout=layout, params=params, c_type=T.C_BF16)
+    torch.cuda.synchronize()
+    return c.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 16, 32), (272, 400, 96), (784, 48, 32), (512, 512, 2080)])
+@pytest.mark.parametrize("layout", ["swizzle", "plain"])
+def test_fused_bf16_result_is_the_rounded_fp32_result(m, n, k, layout):
+    """Same accumulation as the fp32 result, then rounded to nearest even:
+    bit for bit the oracle's rounding of the fp32 kernel's output, and within
+    the fp32 bound plus half a bf16 step of the exact product."""
+    announce("fused gemm bf16", m, n, k, layout)
+    a, bt = W.bf16_operands(m, n, k, seed=m + n + k, std=1.0)
+    c32 = fused_on_gpu(a, bt, layout)
+    c16 = fused_bf16_on_gpu(a, bt, layout)
+    assert np.array_equal(c16, O.f32_to_bf16_bits(c32.astype(np.float32)))
+    exact = O.gemm_bf16(a, bt)
+    got = O.bf16_to_f64(c16)
+    bound = 2 * O.gemm_error_bound(a, bt)
+    assert np.all(np.abs(got - exact) <= bound + 2.0 ** -8 * (np.abs(exact) + bound))
+
+
+def test_fused_bf16_integer_operands_exact():
+    """Integer-valued operands: the fp32 sums are exact, so the bf16 result is
+    the oracle's rounding of the exact product."""
+    rng = np.random.default_rng(21)
+    for m, n, k in [(256, 256, 64), (272, 400, 96), (48, 784, 160)]:
+        announce("fused gemm bf16 integers", m, n, k)
+        ia = (rng.integers(-3, 4, size=(m, k)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        ib = (rng.integers(-3, 4, size=(n, k)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        c16 = fused_bf16_on_gpu(ia, ib)
+        assert np.array_equal(c16, O.f32_to_bf16_bits(O.gemm_bf16(ia, ib).astype(np.float32)))
+
+
+def test_fused_bf16_k_zero_writes_zeros():
+    a = np.zeros((32, 0), dtype=np.uint16)
+    bt = np.zeros((48, 0), dtype=np.uint16)
+    c = torch.full((32, 48), -1, dtype=torch.int16, device=DEV)
+    T.swz_gemm_ex(torch.empty(16, dtype=torch.int16, device=DEV), torch.empty(16, dtype=torch.int16, device=DEV),
+                  c, 32, 48, 0, c_type=T.C_BF16)
+    torch.cuda.synchronize()
+    assert not c.any().item()
+    del a, bt
+
+
+def test_fused_bf16_full_size():
+    """A [8192 x 4096], B^T [8192 x 4096]: the whole bf16 result equals the
+    fp32 result rounded to nearest even (the library's conversion on the
+    GPU, which the oracle's rounding is pinned to), and sampled rows equal
+    the oracle's rounding directly."""
+    announce("fused gemm bf16 full 8192x8192x4096")
+    a, bt = W.bf16_operands(8192, 8192, 4096, seed=0)
+    da = torch.from_numpy(a.view(np.int16)).to(DEV)
+    db = torch.from_numpy(bt.view(np.int16)).to(DEV)
+    c32 = torch.empty((8192, 8192), dtype=torch.float32, device=DEV)
+    c16 = torch.empty((8192, 8192), dtype=torch.int16, device=DEV)
+    T.swz_gemm(da, db, c32, 8192, 8192, 4096)
+    T.swz_gemm_ex(da, db, c16, 8192, 8192, 4096, c_type=T.C_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(c16, c32.to(torch.bfloat16).view(torch.int16))
+    rows = torch.tensor([0, 17, 4095, 8191], device=DEV)
+    got = c16[rows].cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, O.f32_to_bf16_bits(c32[rows].cpu().numpy()))

@@ -29,6 +29,7 @@ READ_BNARROW1, READ_BNARROW2, READ_BNARROW4, READ_BNARROW8, READ_BNARROW16, READ
     17, 18, 19, 20, 21, 22, 23)
 FRAG_MFMA_F32_16X16X32_BF16 = 0
 ORDER_DIAGONAL, ORDER_HALF_DIAGONAL, ORDER_COLUMNS, ORDER_STEEP_DIAGONAL = 0, 1, 2, 3
+C_F32, C_BF16 = 0, 1
 LAYOUTS = {"swizzle": LAYOUT_SWIZZLE, "pad": LAYOUT_PAD, "plain": LAYOUT_PLAIN, "direct": LAYOUT_SWIZZLE_DIRECT}
 
 EXPORTS = (
@@ -41,6 +42,7 @@ EXPORTS = (
     "swz_stage_operand",
     "swz_gemm_frag",
     "swz_gemm",
+    "swz_gemm_ex",
     "swz_fold",
     "swz_choose",
     "swz_predict_conflicts",
@@ -124,6 +126,7 @@ def _load() -> ctypes.CDLL:
     lib.swz_stage_operand.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_gemm_frag.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
     lib.swz_gemm.argtypes = [vp, vp, vp, i64, i64, i64, i32, P(Params), vp]
+    lib.swz_gemm_ex.argtypes = [vp, vp, vp, i64, i64, i64, i32, P(Params), i32, vp]
     lib.swz_fold.argtypes = [P(Params), ctypes.c_uint32, ctypes.c_uint32, P(ctypes.c_uint32), P(ctypes.c_uint32),
                              P(i64)]
     lib.swz_choose.argtypes = [i32, i32, i32, i32, i32, P(Params)]
@@ -239,6 +242,12 @@ def swz_gemm_frag(fa, fb, c, m: int, n: int, k: int, frag_kind: int = FRAG_MFMA_
 def swz_gemm(a, bt, c, m: int, n: int, k: int, layout: str = "swizzle", params=None, stream=None) -> None:
     _check(lib.swz_gemm(_ptr(a), _ptr(bt), _ptr(c), m, n, k, _layout(layout), _params(params),
                         _stream(stream, a, bt, c)), "swz_gemm")
+
+
+def swz_gemm_ex(a, bt, c, m: int, n: int, k: int, layout: str = "swizzle", params=None, c_type: int = C_F32,
+                stream=None) -> None:
+    _check(lib.swz_gemm_ex(_ptr(a), _ptr(bt), _ptr(c), m, n, k, _layout(layout), _params(params), c_type,
+                           _stream(stream, a, bt, c)), "swz_gemm_ex")
 
 
 def swz_fold(params, base: int, active: int):

@@ -349,8 +349,9 @@ SWZ_API int swz_gemm_frag(const void* d_fa, const void* d_fb, float* d_c, int64_
     return hip_status(swz::launch_gemm_frag(d_fa, d_fb, d_c, m, n, k, static_cast<hipStream_t>(stream)));
 }
 
-SWZ_API int swz_gemm(const void* d_a, const void* d_bt, float* d_c, int64_t m, int64_t n, int64_t k, int32_t layout,
-                     const swz_params* p_or_null, void* stream) {
+SWZ_API int swz_gemm_ex(const void* d_a, const void* d_bt, void* d_c, int64_t m, int64_t n, int64_t k,
+                        int32_t layout, const swz_params* p_or_null, int32_t c_type, void* stream) {
+    if (c_type != SWZ_C_F32 && c_type != SWZ_C_BF16) return SWZ_EINVAL;
     if (m < 0 || n < 0 || k < 0 || m % 16 || n % 16 || k % 32) return SWZ_EINVAL;
     if (layout == SWZ_LAYOUT_PAD) return SWZ_EUNSUPPORTED;  // the direct fill writes whole rows
     swz_plan_info pl;
@@ -359,7 +360,8 @@ SWZ_API int swz_gemm(const void* d_a, const void* d_bt, float* d_c, int64_t m, i
     if (st != SWZ_OK) return st;
     int64_t a_elems, b_elems, c_elems, a_bytes, b_bytes, c_bytes;
     if (!mul_ok(m, k, &a_elems) || !mul_ok(n, k, &b_elems) || !mul_ok(m, n, &c_elems)) return SWZ_EINVAL;
-    if (!mul_ok(a_elems, 2, &a_bytes) || !mul_ok(b_elems, 2, &b_bytes) || !mul_ok(c_elems, 4, &c_bytes))
+    if (!mul_ok(a_elems, 2, &a_bytes) || !mul_ok(b_elems, 2, &b_bytes) ||
+        !mul_ok(c_elems, c_type == SWZ_C_BF16 ? 2 : 4, &c_bytes))
         return SWZ_EINVAL;
     if (m == 0 || n == 0) return SWZ_OK;
     if (!d_c) return SWZ_EINVAL;
@@ -368,7 +370,13 @@ SWZ_API int swz_gemm(const void* d_a, const void* d_bt, float* d_c, int64_t m, i
                pc = reinterpret_cast<uintptr_t>(d_c);
     if (pa % 16 || pb % 16 || pc % 16) return SWZ_EINVAL;
     if (k > 0 && (overlaps(d_c, c_bytes, d_a, a_bytes) || overlaps(d_c, c_bytes, d_bt, b_bytes))) return SWZ_EINVAL;
-    return hip_status(swz::launch_gemm_tiles(d_a, d_bt, d_c, m, n, k, layout_of(pl), static_cast<hipStream_t>(stream)));
+    return hip_status(swz::launch_gemm_tiles(d_a, d_bt, d_c, m, n, k, layout_of(pl), c_type == SWZ_C_BF16,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+SWZ_API int swz_gemm(const void* d_a, const void* d_bt, float* d_c, int64_t m, int64_t n, int64_t k, int32_t layout,
+                     const swz_params* p_or_null, void* stream) {
+    return swz_gemm_ex(d_a, d_bt, d_c, m, n, k, layout, p_or_null, SWZ_C_F32, stream);
 }
 
 SWZ_API int swz_fold(const swz_params* p, uint32_t base, uint32_t active, uint32_t* collision,

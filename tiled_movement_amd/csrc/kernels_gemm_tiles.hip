@@ -130,8 +130,9 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[kWbM][kWbN], const bf16x8*
             acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[x], bv[y], acc[x][y], 0, 0, 0);
 }
 
+template <bool BF16C>  // C in bf16 (rounded to nearest even) instead of fp32
 __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restrict__ a, const uint8_t* __restrict__ bt,
-                                                         float* __restrict__ c, int64_t m, int64_t n, int64_t k,
+                                                         void* __restrict__ c, int64_t m, int64_t n, int64_t k,
                                                          int64_t tile_row0, LdsLayout L) {
     __shared__ bf16x8 lds_v[2 * kBufBytes / 16];
     lds_u8* lds = (lds_u8*)(reinterpret_cast<uint8_t*>(lds_v));
@@ -287,22 +288,31 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restri
     // buffers, once every wave is done reading the last stage.
     stage_barrier();
     static_assert(kWaves * epilogue_slice_bytes<kWbN>() <= 2 * kBufBytes, "the epilogue slices fit in LDS");
-    store_c_blocks<kWbM, kWbN>(acc, (lds_f32*)(lds + wave * epilogue_slice_bytes<kWbN>()), c, n, bm0 + wm * kWbM,
-                               bn0 + wn * kWbN, mb, nb, lane);
+    lds_f32* slice = (lds_f32*)(lds + wave * epilogue_slice_bytes<kWbN>());
+    if constexpr (BF16C)
+        store_c_blocks_bf16<kWbM, kWbN>(acc, slice, static_cast<uint16_t*>(c), n, bm0 + wm * kWbM, bn0 + wn * kWbN,
+                                        mb, nb, lane);
+    else
+        store_c_blocks<kWbM, kWbN>(acc, slice, static_cast<float*>(c), n, bm0 + wm * kWbM, bn0 + wn * kWbN, mb, nb,
+                                   lane);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_tiles(const void* a, const void* bt, float* c, int64_t m, int64_t n, int64_t k,
-                             const LdsLayout& layout, hipStream_t stream) {
+hipError_t launch_gemm_tiles(const void* a, const void* bt, void* c, int64_t m, int64_t n, int64_t k,
+                             const LdsLayout& layout, bool bf16c, hipStream_t stream) {
     const int64_t tiles_m = (m + kTileRows - 1) / kTileRows, tiles_n = (n + kTileRows - 1) / kTileRows;
     if (tiles_m == 0 || tiles_n == 0) return hipSuccess;
     if (tiles_n > 0x7fffffff / kThreads) return hipErrorInvalidValue;
     for (int64_t t0 = 0; t0 < tiles_m; t0 += kMaxGridY) {
         const int64_t ny = tiles_m - t0 < kMaxGridY ? tiles_m - t0 : kMaxGridY;
-        hipLaunchKernelGGL(k_gemm_tiles, dim3(static_cast<unsigned>(tiles_n), static_cast<unsigned>(ny)),
-                           dim3(kThreads), 0, stream, static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(bt),
-                           c, m, n, k, t0, layout);
+        const dim3 grid(static_cast<unsigned>(tiles_n), static_cast<unsigned>(ny));
+        const auto* pa = static_cast<const uint8_t*>(a);
+        const auto* pb = static_cast<const uint8_t*>(bt);
+        if (bf16c)
+            hipLaunchKernelGGL(k_gemm_tiles<true>, grid, dim3(kThreads), 0, stream, pa, pb, c, m, n, k, t0, layout);
+        else
+            hipLaunchKernelGGL(k_gemm_tiles<false>, grid, dim3(kThreads), 0, stream, pa, pb, c, m, n, k, t0, layout);
     }
     return hipGetLastError();
 }

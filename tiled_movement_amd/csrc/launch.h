@@ -30,8 +30,8 @@ hipError_t launch_convert(int kind, const ConvertJob& job, hipStream_t stream);
 hipError_t launch_stage(const StageJob& job, hipStream_t stream);
 hipError_t launch_gemm_frag(const void* fa, const void* fb, float* c, int64_t m, int64_t n, int64_t k,
                             hipStream_t stream);
-hipError_t launch_gemm_tiles(const void* a, const void* bt, float* c, int64_t m, int64_t n, int64_t k,
-                             const LdsLayout& layout, hipStream_t stream);
+hipError_t launch_gemm_tiles(const void* a, const void* bt, void* c, int64_t m, int64_t n, int64_t k,
+                             const LdsLayout& layout, bool bf16c, hipStream_t stream);
 hipError_t launch_map(const int32_t* in, int32_t* out, int64_t n, swz_params p, hipStream_t stream);
 
 // Up to kMapBatch triples of one batched-map launch, passed by value.
