@@ -14,7 +14,7 @@
  * tile order (swz_set_tile_order, swz_tune_tile_order); GEMM operand staging
  * into matrix-instruction fragments (swz_stage_operand) and their consumer
  * (swz_gemm_frag); the GEMM that stages its own operands through swizzled
- * tiles (swz_gemm); host-only planning, bank-conflict prediction and layout
+ * tiles (swz_gemm, swz_gemm_ex for a bf16 result); host-only planning, bank-conflict prediction and layout
  * algebra (swz_choose, swz_plan, swz_predict_conflicts, swz_kernel_accesses,
  * swz_bank_model_get, swz_fold); and two diagnostics (swz_copy,
  * swz_lds_probe).
