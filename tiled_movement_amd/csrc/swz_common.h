@@ -37,8 +37,8 @@
 #ifndef SWZ_NT_HNARROW
 #define SWZ_NT_HNARROW 256
 #endif
-#ifndef SWZ_NT_BNARROW
-#define SWZ_NT_BNARROW 256
+#ifndef SWZ_NT_BNARROW  // 0: by row width (64 lanes up to 4 columns, 128 at 8, 256 above)
+#define SWZ_NT_BNARROW 0
 #endif
 
 namespace swz {
@@ -296,7 +296,15 @@ struct NarrowKind {
     static constexpr bool WORDS = E != 2 || C == 1 || C >= 32;
     static constexpr int CB = !WORDS ? 1 : C < EPW ? C : EPW;   // columns per lane block
     static constexpr int RPW = WORDS && C < EPW ? EPW / C : 1;  // rows per load
-    static constexpr int NT = E == 4 ? SWZ_NT_NARROW : E == 2 ? SWZ_NT_HNARROW : SWZ_NT_BNARROW;
+    // Lanes per tile.  Byte rows: a sweep of 64, 128 and 256 lanes on 64 MiB
+    // matrices put the best at 64 up to 4 columns (+2-4%), 128 at 8 (+8%)
+    // and 256 from 16 columns on.
+    static constexpr int NT = E == 4   ? SWZ_NT_NARROW
+                              : E == 2 ? SWZ_NT_HNARROW
+                              : SWZ_NT_BNARROW ? SWZ_NT_BNARROW
+                              : C <= 4 ? 64
+                              : C == 8 ? 128
+                                       : 256;
     static constexpr int ESZ = E, TR = NT * 16 * CB / E / C, TC = C;
     static constexpr int VEC = 4;
     static constexpr int RWIDTH = WORDS ? 4 : E;
