@@ -119,7 +119,8 @@ enum swz_layout {
  *               64 columns (powers of two), 4-byte LDS writes (M >= 2):
  *               each lane reads 4-byte words of 16 rows and up to 4 columns
  *               and transposes them in registers into up to four 16-byte
- *               output pieces; tiles of 4096 * min(cols, 4) bytes.
+ *               output pieces; tiles of 1 KiB per column up to 4 columns,
+ *               8 KiB at 8 and 16 KiB above (64, 128 and 256 lanes).
  *  AUTO       : 4-byte -> NARROW<cols> when cols is 1, 2, 4, 8 or 16, else
  *               SCALAR_COL; 2-byte -> HNARROW<cols> when cols is a power of
  *               two up to 32, else B64_TR16 when cols <= 64, B128_8X8 when
