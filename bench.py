@@ -18,7 +18,8 @@ Usage:
       time one workload only (used for profiler runs), optionally rotating over
       exactly P buffer pairs; NAME is one of
       fp32_transpose, fp16_transpose, fp16_transpose_tr, u8_transpose, bf16_convert,
-      bf16_stage, fp32_narrow8, fp16_narrow8, u8_narrow16, map, map_batch, copy, copy_128, memcpy_d2d,
+      bf16_stage, fp32_narrow8, fp16_narrow8, u8_narrow16, fp32_transpose_long, map, map_batch, copy,
+      copy_128, memcpy_d2d,
       bf16_gemm, bf16_gemm_fused, bf16_gemm_fused_bf16c, torch_mm_bf16
 """
 
@@ -43,6 +44,7 @@ CACHE_DEFEAT_BYTES = 512 * 2**20  # 2x the 256 MB Infinity Cache
 
 WORKLOADS = {
     "fp32_transpose": "fp32 4096x4096 row-major -> column-major transpose, 32x32 LDS tiles, 4-byte column reads",
+    "fp32_transpose_long": "fp32 8192x2048 -> 2048x8192 transpose (64 MiB, 32 KiB output rows), default tile order",
     "fp16_transpose": "fp16 8192x8192 row-major -> column-major transpose, 64x64 LDS tiles, 8-byte reads of 4x4 blocks",
     "fp16_transpose_tr": "fp16 8192x8192 row-major -> column-major transpose, 64x64 LDS tiles, gfx950 8-byte transpose reads",
     "bf16_convert": "bf16 [64,4096,128] -> [64,128,4096] layout conversion, 64x128 LDS tiles, 16-byte reads of 8x8 blocks",
@@ -169,7 +171,7 @@ def build(ctx, name, layout):
     info = {"workload": WORKLOADS[name], "layout": layout}
 
     if name in ("fp32_transpose", "fp16_transpose", "fp16_transpose_tr", "bf16_convert", "u8_transpose", "fp32_narrow8",
-                "fp16_narrow8", "u8_narrow16"):
+                "fp16_narrow8", "u8_narrow16", "fp32_transpose_long"):
         if name == "fp32_narrow8":
             a, esz, kind, (batch, r, c) = W.fp32_matrix(1 << 21, 8, seed=0), 4, T.READ_NARROW8, (1, 1 << 21, 8)
         elif name == "fp16_narrow8":
@@ -178,6 +180,8 @@ def build(ctx, name, layout):
             a, esz, kind, (batch, r, c) = W.u8_matrix(1 << 22, 16, seed=0), 1, T.READ_BNARROW16, (1, 1 << 22, 16)
         elif name == "fp32_transpose":
             a, esz, kind, (batch, r, c) = W.fp32_matrix(4096, 4096, seed=0), 4, T.READ_SCALAR_COL, (1, 4096, 4096)
+        elif name == "fp32_transpose_long":
+            a, esz, kind, (batch, r, c) = W.fp32_matrix(8192, 2048, seed=0), 4, T.READ_SCALAR_COL, (1, 8192, 2048)
         elif name == "fp16_transpose":
             a, esz, kind, (batch, r, c) = W.fp16_matrix(8192, 8192, seed=0), 2, T.READ_B64_4X4, (1, 8192, 8192)
         elif name == "fp16_transpose_tr":
@@ -463,6 +467,21 @@ def main(argv=None):
                 log(f"{wname}/{lay}: {rate:.1f} GB/s")
                 del s2, inf2
                 ctx.torch.cuda.empty_cache()
+        # Long output rows: the default tile order, then the one
+        # swz_tune_tile_order pins for the shape (the pin is removed after).
+        s2, nb2, inf2 = build(ctx, "fp32_transpose_long", "swizzle")
+        rate_d, ms_d = median_rate(s2, nb2)
+        _, srcs2, dsts2, _ = inf2["_io"]
+        T = ctx.T
+        chosen = T.swz_tune_tile_order(srcs2[0], dsts2[0], 1, 8192, 2048, 4, "swizzle", T.READ_SCALAR_COL, reps=10)
+        rate_t, ms_t = median_rate(s2, nb2)
+        T.swz_set_tile_order(1, 8192, 2048, 4, T.READ_SCALAR_COL, -1)
+        extra["fp32_transpose_long/swizzle"] = {"shape": [1, 8192, 2048], "GBps_default_order": round(rate_d, 1),
+                                                "GBps_tuned_order": round(rate_t, 1), "tuned_order": chosen,
+                                                "us_per_step_tuned": round(ms_t * 1e3, 2)}
+        log(f"fp32 8192x2048: {rate_d:.1f} GB/s default order, {rate_t:.1f} GB/s with order {chosen}")
+        del s2, inf2, srcs2, dsts2
+        ctx.torch.cuda.empty_cache()
         # The headline and its copy ceiling again with 16 buffer pairs (2 GiB
         # rotating): no reuse of the Infinity Cache or of address
         # translations between calls of one pair.
@@ -499,7 +518,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32_transpose": "f32", "fp32_narrow8": "f32", "fp16_narrow8": "f16", "u8_narrow16": "u8", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "map_batch": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
+        "dtype": {"fp32_transpose": "f32", "fp32_narrow8": "f32", "fp32_transpose_long": "f32", "fp16_narrow8": "f16", "u8_narrow16": "u8", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "map_batch": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
         "data": "synthetic",
         "config": {k: v for k, v in info.items() if not k.startswith("_")},
         "roofline": {
