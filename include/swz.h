@@ -3,7 +3,8 @@
  *
  * C ABI of libswz.so.  Plain pointers and sizes only.  Every call that moves
  * data is asynchronous on the caller's HIP stream (a hipStream_t passed as
- * void*; NULL is the default stream).  Device buffers belong to the caller;
+ * void*; NULL is the default stream), except swz_tune_tile_order, which
+ * times conversions on it and waits for them.  Device buffers belong to the caller;
  * the library allocates no device memory and keeps no pointer after a call
  * returns.  Errors are negative return codes, detected on the host before
  * any launch; no call aborts or throws.  All calls are thread-safe.
