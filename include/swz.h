@@ -12,7 +12,8 @@
  * Calls: the swizzle map (swz_map, swz_map_batch); transposes and batched layout
  * conversions of 1-, 2- and 4-byte elements through swizzled, padded or
  * plain LDS tiles (swz_transpose, swz_convert_layout), with a per-shape
- * tile order (swz_set_tile_order, swz_tune_tile_order); GEMM operand staging
+ * tile order (swz_set_tile_order, swz_get_tile_order, swz_tune_tile_order);
+ * GEMM operand staging
  * into matrix-instruction fragments (swz_stage_operand) and their consumer
  * (swz_gemm_frag); the GEMM that stages its own operands through swizzled
  * tiles (swz_gemm, swz_gemm_ex for a bf16 result); host-only planning, bank-conflict prediction and layout
@@ -251,6 +252,13 @@ enum swz_tile_order {
  * element size / read kind that swz_convert_layout would refuse. */
 int swz_set_tile_order(int64_t batch, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t read_kind,
                        int32_t order);
+
+/* The tile order later conversions of this shape will use (the pinned one,
+ * or SWZ_ORDER_DIAGONAL), in *order.  Host only.
+ * Errors: SWZ_EINVAL for NULL order or negative sizes; as
+ * swz_set_tile_order for the element size and read kind. */
+int swz_get_tile_order(int64_t batch, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t read_kind,
+                       int32_t* order);
 
 /* Time every tile order on this conversion and pin the fastest: three
  * interleaved rounds over the orders, each one untimed and `reps` timed

@@ -87,7 +87,12 @@ def test_tile_order_validation():
     assert f(1, 64, 64, 3, -1, 0) == EINVAL  # element size
     assert f(1, 64, 64, 2, T.READ_SCALAR_COL, 0) == EINVAL  # kind for another element size
     assert f(1, 64, 64, 4, -1, T.ORDER_COLUMNS) == T.SWZ_OK
+    assert T.swz_get_tile_order(1, 64, 64, 4) == T.ORDER_COLUMNS
+    assert T.swz_get_tile_order(1, 64, 64, 4, T.READ_SCALAR_COL) == T.ORDER_COLUMNS  # AUTO resolves to this kind
+    assert T.swz_get_tile_order(2, 64, 64, 4) == T.ORDER_DIAGONAL  # another shape
+    assert lib.swz_get_tile_order(1, 64, 64, 4, -1, None) == EINVAL
     assert f(1, 64, 64, 4, -1, -1) == T.SWZ_OK  # removed
+    assert T.swz_get_tile_order(1, 64, 64, 4) == T.ORDER_DIAGONAL
     assert f(1, 64, 64, 4, -1, -1) == T.SWZ_OK  # removing twice is fine
     g = lib.swz_tune_tile_order
     c = ctypes.c_int32(-7)

@@ -360,6 +360,7 @@ def test_tune_tile_order_pins_an_order_and_keeps_the_result():
     try:
         chosen = T.swz_tune_tile_order(src, dst, 1, 2048, 544, 4, "swizzle", reps=3)
         assert chosen in (T.ORDER_DIAGONAL, T.ORDER_HALF_DIAGONAL, T.ORDER_COLUMNS, T.ORDER_STEEP_DIAGONAL)
+        assert T.swz_get_tile_order(1, 2048, 544, 4) == chosen
         torch.cuda.synchronize()
         assert np.array_equal(from_dev(dst, a), O.transpose(a))
         dst.zero_()

@@ -38,6 +38,7 @@ EXPORTS = (
     "swz_transpose",
     "swz_convert_layout",
     "swz_set_tile_order",
+    "swz_get_tile_order",
     "swz_tune_tile_order",
     "swz_stage_operand",
     "swz_gemm_frag",
@@ -122,6 +123,7 @@ def _load() -> ctypes.CDLL:
     lib.swz_transpose.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_convert_layout.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_set_tile_order.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.swz_get_tile_order.argtypes = [i64, i64, i64, i32, i32, P(ctypes.c_int32)]
     lib.swz_tune_tile_order.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, P(Params), i32, P(ctypes.c_int32), vp]
     lib.swz_stage_operand.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_gemm_frag.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
@@ -196,6 +198,13 @@ def swz_map(inp, out, n: int, params, stream=None) -> None:
 def swz_set_tile_order(batch: int, rows: int, cols: int, elem_bytes: int, read_kind: int = READ_AUTO,
                        order: int = ORDER_DIAGONAL) -> None:
     _check(lib.swz_set_tile_order(batch, rows, cols, elem_bytes, read_kind, order), "swz_set_tile_order")
+
+
+def swz_get_tile_order(batch: int, rows: int, cols: int, elem_bytes: int, read_kind: int = READ_AUTO) -> int:
+    order = ctypes.c_int32(-1)
+    _check(lib.swz_get_tile_order(batch, rows, cols, elem_bytes, read_kind, ctypes.byref(order)),
+           "swz_get_tile_order")
+    return order.value
 
 
 def swz_tune_tile_order(src, dst, batch: int, rows: int, cols: int, elem_bytes: int, layout="swizzle",

@@ -254,6 +254,16 @@ SWZ_API int swz_set_tile_order(int64_t batch, int64_t rows, int64_t cols, int32_
     return SWZ_OK;
 }
 
+SWZ_API int swz_get_tile_order(int64_t batch, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t read_kind,
+                               int32_t* order) {
+    if (!order || batch < 0 || rows < 0 || cols < 0) return SWZ_EINVAL;
+    swz_plan_info pl;
+    const int st = make_plan(0, rows, cols, elem_bytes, SWZ_LAYOUT_SWIZZLE, read_kind, nullptr, true, true, &pl);
+    if (st != SWZ_OK) return st;
+    *order = pinned_order(pl.read_kind, batch, rows, cols);
+    return SWZ_OK;
+}
+
 SWZ_API int swz_tune_tile_order(const void* d_src, void* d_dst, int64_t batch, int64_t rows, int64_t cols,
                                 int32_t elem_bytes, int32_t layout, int32_t read_kind, const swz_params* p_or_null,
                                 int32_t reps, int32_t* chosen, void* stream) {
