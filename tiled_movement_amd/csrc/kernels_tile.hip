@@ -431,7 +431,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
         // row each, or RPW whole rows of C columns); piece j gathers column
         // CB*g + j of the PER rows, element q from word q / RPW at position
         // (q % RPW) * C + j, into 16 bytes of one output row.
-        constexpr int E = K::ESZ, PER = K::PER, EPW = K::EPW, CB = K::CB, RPW = K::RPW, C = K::TC;
+        constexpr int E = K::ESZ, EPW = K::EPW, CB = K::CB, RPW = K::RPW, C = K::TC;
         constexpr uint32_t kMask = E == 2 ? 0xffffu : 0xffu;
         uint32_t w[K::RSTEPS];
 #pragma unroll
