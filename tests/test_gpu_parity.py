@@ -371,6 +371,19 @@ def test_tune_tile_order_pins_an_order_and_keeps_the_result():
         T.swz_set_tile_order(1, 2048, 544, 4, T.READ_AUTO, -1)
 
 
+def test_tune_tile_order_refusal_pins_nothing():
+    """A conversion the library refuses (a direct fill with a 16-bit row
+    pitch that is not a multiple of 16 bytes) makes the tuner return that
+    error before any launch, and leaves no order pinned for the shape."""
+    src = torch.zeros((64, 100), dtype=torch.int16, device=DEV)
+    dst = torch.zeros((100, 64), dtype=torch.int16, device=DEV)
+    with pytest.raises(T.SwzError) as e:
+        T.swz_tune_tile_order(src, dst, 1, 64, 100, 2, "direct", T.READ_B64_TR16, reps=2)
+    assert e.value.status == T.SWZ_EUNSUPPORTED
+    assert T.swz_get_tile_order(1, 64, 100, 2, T.READ_B64_TR16) == T.ORDER_DIAGONAL
+    assert not dst.any().item()  # nothing was written
+
+
 # ------------------------------------------------------- operand staging
 
 
