@@ -201,6 +201,13 @@ __device__ __forceinline__ void store16_edge(uint8_t* D, int64_t row, int64_t co
 #define SWZ_OCC_NARROW 0
 #endif
 
+// Whole-row tiles: uncapped, except the 16 KiB byte tiles of 32 and 64
+// columns, which a sweep (uncapped, 4 and 8 per CU) put 4% faster at 4;
+// every other narrow kind lost up to 20% when capped.
+#ifndef SWZ_OCC_BNARROW_WIDE
+#define SWZ_OCC_BNARROW_WIDE 4
+#endif
+
 template <int KIND>
 constexpr int occupancy_limit() {
     return KIND == SWZ_READ_SCALAR_COL ? SWZ_OCC_SCALAR
@@ -209,6 +216,7 @@ constexpr int occupancy_limit() {
            : KIND == SWZ_READ_MFMA_16X16X32 ? SWZ_OCC_STAGE
            : KIND == SWZ_READ_B64_TR16 ? SWZ_OCC_TR16
            : KIND == SWZ_READ_B64_TR8  ? SWZ_OCC_TR8
+           : (KIND == SWZ_READ_BNARROW32 || KIND == SWZ_READ_BNARROW64) ? SWZ_OCC_BNARROW_WIDE
                                        : SWZ_OCC_NARROW;
 }
 
