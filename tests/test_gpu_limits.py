@@ -71,3 +71,19 @@ def test_stage_with_more_row_tiles_than_a_grid_dimension():
             x = W.index_pattern_host((mn // 16, 16 * k), blk, 2).reshape(16, k)
             got = f[blk].cpu().numpy().view(np.uint16)
             assert np.array_equal(got, O.stage_operand(x)[0]), (layout, blk)
+
+
+@pytest.mark.parametrize("esz,c", [(4, 8), (2, 1), (2, 32), (1, 4), (1, 64)])
+def test_narrow_rows_batch_beyond_grid_limit(esz, c):
+    """70,000 small narrow-row matrices: a batch beyond the 65,535 grid limit
+    takes the 1-D launch, with whole-row tiles of every element size."""
+    batch, rows = 70000, 24
+    gen = {4: W.fp32_matrix, 2: W.fp16_matrix, 1: W.u8_matrix}[esz]
+    a = gen(batch * rows, c, seed=50 + c).reshape(batch, rows, c)
+    for layout in ("swizzle", "plain"):
+        announce("narrow huge batch", esz, c, layout)
+        src = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+        dst = torch.empty((batch, c, rows), dtype=src.dtype, device=DEV)
+        T.swz_convert_layout(src, dst, batch, rows, c, esz, layout)
+        torch.cuda.synchronize()
+        assert np.array_equal(dst.cpu().numpy(), O.convert_layout(a)), (esz, c, layout)
