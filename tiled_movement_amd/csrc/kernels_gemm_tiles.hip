@@ -27,8 +27,10 @@
 // together.  Running half of the waves half a stage behind (the ping-pong
 // schedule below) took it from 1.15-1.23 to 1.22-1.28 PFLOP/s.  Four waves
 // of 128 x 128 (one per SIMD) ran 1.10; raising the wave priority around the
-// products, letting only the lagging waves issue the loads and giving each
-// XCD a contiguous run of tiles did not help.
+// products, letting only the lagging waves issue the loads, giving each XCD a
+// contiguous run of tiles and scheduling hints (the compiler's MFMA / LDS
+// interleave strategy, or explicit groups of four products per fragment
+// read) did not help.
 #include "gemm_epilogue.h"
 #include "launch.h"
 
