@@ -371,6 +371,29 @@ def test_tune_tile_order_pins_an_order_and_keeps_the_result():
         T.swz_set_tile_order(1, 2048, 544, 4, T.READ_AUTO, -1)
 
 
+def test_tune_tile_order_batched_16bit_pins_per_shape():
+    """The tuner on a batch of ragged fp16 matrices: the pinned order is the
+    one for (batch, rows, cols, read kind) only, and the result it leaves,
+    and a later call with the pin, are the transposes."""
+    a = W.fp16_matrix(3 * 200, 328, seed=45).reshape(3, 200, 328)
+    src = to_dev(a)
+    dst = torch.empty((3, 328, 200), dtype=src.dtype, device=DEV)
+    announce("tune tile order batched fp16")
+    try:
+        chosen = T.swz_tune_tile_order(src, dst, 3, 200, 328, 2, "swizzle", T.READ_B64_TR16, reps=2)
+        assert T.swz_get_tile_order(3, 200, 328, 2, T.READ_B64_TR16) == chosen
+        assert T.swz_get_tile_order(1, 200, 328, 2, T.READ_B64_TR16) == T.ORDER_DIAGONAL
+        assert T.swz_get_tile_order(3, 200, 328, 2, T.READ_B128_8X8) == T.ORDER_DIAGONAL
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(dst, a), O.convert_layout(a))
+        dst.zero_()
+        T.swz_convert_layout(src, dst, 3, 200, 328, 2, "pad", T.READ_B64_TR16)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(dst, a), O.convert_layout(a))
+    finally:
+        T.swz_set_tile_order(3, 200, 328, 2, T.READ_B64_TR16, -1)
+
+
 def test_tune_tile_order_refusal_pins_nothing():
     """A conversion the library refuses (a direct fill with a 16-bit row
     pitch that is not a multiple of 16 bytes) makes the tuner return that
