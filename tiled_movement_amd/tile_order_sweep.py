@@ -1,13 +1,14 @@
-"""Time every tile order of the transposes on matrices of 64 MiB of several
-shapes, and what swz_tune_tile_order picks for each.
+"""Time every tile order of the transposes on matrices of one size (64 MiB
+unless --mib says otherwise) and several shapes, and what
+swz_tune_tile_order picks for each.
 
 Each shape is transposed with each order pinned (swz_set_tile_order),
-rotating over four buffer pairs (512 MiB, twice the Infinity Cache), best
+rotating over four buffer pairs (512 MiB at 64 MiB, twice the Infinity Cache), best
 of three batches of 100 calls timed with HIP events; then the tuner runs on
 one pair and its choice is recorded.  Pins are removed afterwards.
 
 Usage:
-  python -m tiled_movement_amd.tile_order_sweep [--elem-bytes 4 2] [--out sweep.md]
+  python -m tiled_movement_amd.tile_order_sweep [--elem-bytes 4 2] [--mib 64] [--out sweep.md]
 """
 
 from __future__ import annotations
@@ -25,7 +26,7 @@ BYTES = 64 << 20
 PAIRS = 4
 
 
-def time_order(srcs, dsts, rows, cols, esz, stream):
+def time_order(srcs, dsts, rows, cols, esz, stream, nbytes=BYTES):
     sp, dp, sh = [s.data_ptr() for s in srcs], [d.data_ptr() for d in dsts], stream.cuda_stream
 
     def launch(i):  # the C call itself: host overhead far below the kernel time
@@ -44,30 +45,32 @@ def time_order(srcs, dsts, rows, cols, esz, stream):
             launch(i)
         e1.record()
         e1.synchronize()
-        best = max(best, 2.0 * BYTES * 100 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        best = max(best, 2.0 * nbytes * 100 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     return best
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--elem-bytes", type=int, nargs="+", default=[4, 2])
+    ap.add_argument("--mib", type=int, default=BYTES >> 20, help="matrix size in MiB (a power of two)")
     ap.add_argument("--out", default=None)
     args = ap.parse_args(argv)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     lines = ["| elem bytes | rows x cols | output pitch | " + " | ".join(ORDERS.values()) + " | tuned |",
              "|---|---|---|" + "---|" * len(ORDERS) + "---|"]
-    srcs = [torch.full((BYTES,), p + 1, dtype=torch.uint8, device=dev) for p in range(PAIRS)]
-    dsts = [torch.empty((BYTES,), dtype=torch.uint8, device=dev) for _ in range(PAIRS)]
+    nbytes = args.mib << 20
+    srcs = [torch.full((nbytes,), p + 1, dtype=torch.uint8, device=dev) for p in range(PAIRS)]
+    dsts = [torch.empty((nbytes,), dtype=torch.uint8, device=dev) for _ in range(PAIRS)]
     for esz in args.elem_bytes:
-        elems = BYTES // esz
+        elems = nbytes // esz
         rows = 256
         while rows <= elems // 256:
             cols = elems // rows
             rates = {}
             for order, name in ORDERS.items():
                 T.swz_set_tile_order(1, rows, cols, esz, T.READ_AUTO, order)
-                rates[name] = time_order(srcs, dsts, rows, cols, esz, stream)
+                rates[name] = time_order(srcs, dsts, rows, cols, esz, stream, nbytes)
             chosen = T.swz_tune_tile_order(srcs[0], dsts[0], 1, rows, cols, esz, "swizzle", reps=20, stream=stream)
             T.swz_set_tile_order(1, rows, cols, esz, T.READ_AUTO, -1)
             lines.append(f"| {esz} | {rows} x {cols} | {rows * esz} B | "
