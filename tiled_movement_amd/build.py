@@ -8,6 +8,7 @@ may not exist yet.
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -56,6 +57,12 @@ def flags():
         "-target-feature",
         "-Xclang",
         "-packed-fp32-ops",
+        # Kernel arguments arrive in SGPRs (gfx950 kernarg preload; the code
+        # object keeps an entry that loads them itself where the firmware
+        # does not): a tile kernel's wave then needs no scalar memory round
+        # trip before its first global load.
+        "-mllvm",
+        "-amdgpu-kernarg-preload-count=16",
         f"-I{INCLUDE}",
         f"-I{CSRC}",
     ]
@@ -74,15 +81,29 @@ def build_test_helper(verbose: bool = False) -> str:
 
 
 def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
-    """Compile every source into one shared library; returns its path."""
-    cmd = [hipcc()] + flags() + list(extra) + ["-shared", "-o", out + ".tmp"]
+    """Compile every source to an object (in parallel: each is its own
+    translation unit, kernels launched from the file that defines them),
+    then link one shared library; returns its path."""
+    objdir = os.path.join(HERE, "_build", os.path.basename(out) + ".objs")
+    os.makedirs(objdir, exist_ok=True)
+    jobs = []
     for s in SOURCES:
-        path = os.path.join(CSRC, s)
+        obj = os.path.join(objdir, s + ".o")
         # hipcc compiles .cpp as HIP too; the host files include hip_runtime.h.
-        cmd += ["-x", "hip", path]
+        jobs.append((obj, [hipcc()] + flags() + list(extra) + ["-c", "-o", obj, "-x", "hip", os.path.join(CSRC, s)]))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+        for obj, cmd in jobs:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+        for r in pool.map(lambda c: subprocess.run(c, capture_output=True, text=True), [c for _, c in jobs]):
+            if r.stderr:
+                sys.stderr.write(r.stderr)
+            r.check_returncode()
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", out + ".tmp"] + [o for o, _ in jobs]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
     os.replace(out + ".tmp", out)
     return out
 

@@ -32,61 +32,22 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-#ifndef SWZ_GEMM_WAVES_M  // waves along m / n; each wave owns WB_M x WB_N blocks of 16 x 16
-#define SWZ_GEMM_WAVES_M 4
-#endif
-#ifndef SWZ_GEMM_WAVES_N
-#define SWZ_GEMM_WAVES_N 2
-#endif
-#ifndef SWZ_GEMM_WB_M
-#define SWZ_GEMM_WB_M 4
-#endif
-#ifndef SWZ_GEMM_WB_N
-#define SWZ_GEMM_WB_N 8
-#endif
-#ifndef SWZ_GEMM_STAGE_STEPS  // 32-wide k steps per LDS stage
-#define SWZ_GEMM_STAGE_STEPS 1
-#endif
-#ifndef SWZ_GEMM_XCD  // 1: give each of the 8 XCDs (own L2) a contiguous run of tiles
-#define SWZ_GEMM_XCD 0
-#endif
-#ifndef SWZ_GEMM_BUFS  // LDS stage buffers (2 to 4): up to BUFS - 1 stages of loads in flight
-#define SWZ_GEMM_BUFS 2
-#endif
-#ifndef SWZ_GEMM_PINGPONG  // 1: the second half of the waves runs one stage's products behind
-#define SWZ_GEMM_PINGPONG 1
-#endif
-
-constexpr int kWavesM = SWZ_GEMM_WAVES_M, kWavesN = SWZ_GEMM_WAVES_N;
+// Waves along m / n; each wave owns kWbM x kWbN blocks of 16 x 16; one 32-wide
+// k step per stage, two stage buffers.
+constexpr int kWavesM = 4, kWavesN = 2;
 constexpr int kWaves = kWavesM * kWavesN;
 constexpr int kGemmThreads = 64 * kWaves;
-constexpr int kWbM = SWZ_GEMM_WB_M, kWbN = SWZ_GEMM_WB_N;
+constexpr int kWbM = 4, kWbN = 8;
 constexpr int kTileM = kWavesM * kWbM, kTileN = kWavesN * kWbN;  // blocks per workgroup tile
-constexpr int kStageSteps = SWZ_GEMM_STAGE_STEPS;
 constexpr int kFragBytes = 64 * 16;                              // one fragment: 64 lanes x 16 bytes
-constexpr int kStageFragsA = kTileM * kStageSteps, kStageFragsB = kTileN * kStageSteps;
-constexpr int kBufBytes = (kStageFragsA + kStageFragsB) * kFragBytes;  // A and B of one stage
-static_assert((kStageFragsA + kStageFragsB) % kWaves == 0, "stage loads split over the waves");
-constexpr int kBufs = SWZ_GEMM_BUFS;
-constexpr int kPerWave = (kStageFragsA + kStageFragsB) / kWaves;  // direct loads per wave per stage
-static_assert(kBufs >= 2 && kBufs <= 4, "two to four stage buffers");
-// The stage buffers, reused by the epilogue's slices once the last stage is
-// done (the slices may need a little more).
+constexpr int kBufBytes = (kTileM + kTileN) * kFragBytes;        // A and B of one stage
+static_assert((kTileM + kTileN) % kWaves == 0, "stage loads split over the waves");
+constexpr int kPerWave = (kTileM + kTileN) / kWaves;  // direct loads per wave per stage
+// The two stage buffers, reused by the epilogue's slices once the last stage
+// is done (the slices may need a little more).
 constexpr int kSliceBytes = kWaves * epilogue_slice_bytes<kWbN>();
-constexpr int kLdsBytes = kBufs * kBufBytes > kSliceBytes ? kBufs * kBufBytes : kSliceBytes;
+constexpr int kLdsBytes = 2 * kBufBytes > kSliceBytes ? 2 * kBufBytes : kSliceBytes;
 static_assert(kLdsBytes <= 160 * 1024, "the stage buffers fit in LDS");
-static_assert((kBufs - 2) * kPerWave <= 63, "the load counter holds the loads left in flight");
-
-// Wait until at most `later` stages' loads of this wave are still in flight
-// (the counter retires loads in issue order).
-__device__ __forceinline__ void wait_stages(int later) {
-    if (later <= 0)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (later == 1)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPerWave) : "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPerWave) : "memory");
-}
 
 // Workgroup barrier without the memory fence __syncthreads adds: the fence
 // would wait for every direct load in flight, including the later stages
@@ -98,26 +59,21 @@ __device__ __forceinline__ void stage_barrier() {
 }
 constexpr int64_t kMaxGridY = 65535;
 
-// Issue this wave's share of stage s's direct loads into LDS buffer buf.
-// Fragment f < kStageFragsA is A block f % kTileM of k step f / kTileM; the
-// rest are B fragments likewise.  Blocks past the matrix edge load the
-// tile's first block instead (their results are never stored); k steps past
-// the end are never multiplied.
+// Issue this wave's share of stage (k step) s's direct loads into LDS buffer
+// buf.  Fragment f < kTileM is A block f; the rest are B blocks.  Blocks past
+// the matrix edge load the tile's first block instead (their results are
+// never stored).
 __device__ __forceinline__ void load_stage(const uint8_t* __restrict__ fa, const uint8_t* __restrict__ fb,
                                            int64_t bm0, int64_t bn0, int64_t mb, int64_t nb, int64_t kb, int64_t s,
                                            lds_u8* buf, int wave, int lane) {
 #pragma unroll
     for (int q = 0; q < kPerWave; ++q) {
         const int f = wave * kPerWave + q;
-        const bool is_a = f < kStageFragsA;
-        const int g = is_a ? f : f - kStageFragsA;
-        const int tile = is_a ? kTileM : kTileN;
-        const int blk = g % tile, ks = g / tile;
-        int64_t kk = s * kStageSteps + ks;
-        kk = kk < kb ? kk : kb - 1;
+        const bool is_a = f < kTileM;
+        const int blk = is_a ? f : f - kTileM;
         const int64_t b0 = is_a ? bm0 : bn0, lim = is_a ? mb : nb;
         const int64_t row = b0 + blk < lim ? b0 + blk : b0;
-        const uint8_t* src = (is_a ? fa : fb) + (row * kb + kk) * kFragBytes + lane * 16;
+        const uint8_t* src = (is_a ? fa : fb) + (row * kb + s) * kFragBytes + lane * 16;
         __builtin_amdgcn_global_load_lds(src, buf + f * kFragBytes, 16, 0, 0);
     }
 }
@@ -131,29 +87,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __res
     const int lane = threadIdx.x % 64;
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int64_t mb = m / 16, nb = n / 16, kb = k / 32;
-    int64_t ty = blockIdx.y, tx = blockIdx.x;
-    if (SWZ_GEMM_XCD == 1) {
-        // Workgroups are handed to the 8 XCDs in turn; renumber so that the
-        // ones on one XCD cover neighbouring tiles and share operand blocks
-        // in that XCD's L2.
-        const uint32_t nt = gridDim.x * gridDim.y, id = blockIdx.y * gridDim.x + blockIdx.x;
-        if (nt % 8 == 0) {
-            const uint32_t t = (id % 8) * (nt / 8) + id / 8;
-            ty = t / gridDim.x;
-            tx = t % gridDim.x;
-        }
-    } else if (SWZ_GEMM_XCD == 2) {
-        // The same, in 4 x 8 groups of tiles: the workgroups one XCD runs at
-        // a time (one per CU) share 4 bands of A and 8 of B.
-        const uint32_t gx = gridDim.x, gy = gridDim.y, id = blockIdx.y * gx + blockIdx.x;
-        if (gx % 8 == 0 && gy % 4 == 0 && (gx / 8) * (gy / 4) % 8 == 0) {
-            const uint32_t j = id / 8, sb = id % 8 + 8 * (j / 32), w = j % 32;
-            ty = 4 * (sb / (gx / 8)) + w / 8;
-            tx = 8 * (sb % (gx / 8)) + w % 8;
-        }
-    }
+    const int64_t ty = blockIdx.y, tx = blockIdx.x;
     const int64_t bm0 = (tile_row0 + ty) * kTileM, bn0 = tx * kTileN;
-    const int64_t stages = (kb + kStageSteps - 1) / kStageSteps;
+    const int64_t stages = kb;  // one k step per stage
 
     f32x4 acc[kWbM][kWbN];
 #pragma unroll
@@ -161,34 +97,30 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __res
 #pragma unroll
         for (int y = 0; y < kWbN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Prologue: stages 0 .. kBufs-2 in flight (k = 0 issues nothing: C = 0).
-#pragma unroll
-    for (int p = 0; p < kBufs - 1; ++p)
-        if (p < stages) load_stage(fa, fb, bm0, bn0, mb, nb, kb, p, lds + p * kBufBytes, wave, lane);
+    // Prologue: stage 0 in flight (k = 0 issues nothing: C = 0).
+    if (stages > 0) load_stage(fa, fb, bm0, bn0, mb, nb, kb, 0, lds, wave, lane);
 
-#if SWZ_GEMM_PINGPONG
-    static_assert(kStageSteps == 1, "the ping-pong schedule holds one k step over the barrier");
-    // Waves 0-3 and 4-7 share the SIMDs pairwise.  The second half holds
-    // each stage's fragments over the next barrier and multiplies them
-    // while reading the next stage's, so one wave of each SIMD feeds the
-    // matrix unit while the other waits for LDS.  The k steps still
-    // accumulate in increasing order.
+    // Ping-pong schedule.  Waves 0-3 and 4-7 share the SIMDs pairwise.  The
+    // second half holds each stage's fragments over the next barrier and
+    // multiplies them while reading the next stage's, so one wave of each
+    // SIMD feeds the matrix unit while the other waits for LDS.  The k steps
+    // still accumulate in increasing order.
     const bool lag = wave >= kWaves / 2;
+    // Stage s has landed once this wave's loads are done; the barrier then
+    // also says every wave is done with stage s - 1, whose buffer the next
+    // loads reuse.
     auto begin = [&](int64_t s) {
-        const int64_t later = stages - 1 - s < kBufs - 2 ? stages - 1 - s : kBufs - 2;
-        wait_stages(static_cast<int>(later));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // held fragments have arrived
         stage_barrier();
-        if (s + kBufs - 1 < stages)
-            load_stage(fa, fb, bm0, bn0, mb, nb, kb, s + kBufs - 1, lds + ((s + kBufs - 1) % kBufs) * kBufBytes, wave,
-                       lane);
-        return lds + (s % kBufs) * kBufBytes;
+        if (s + 1 < stages) load_stage(fa, fb, bm0, bn0, mb, nb, kb, s + 1, lds + ((s + 1) % 2) * kBufBytes, wave, lane);
+        return lds + (s % 2) * kBufBytes;
     };
     auto frag_a = [&](lds_u8* cur, int x) {
         return *(__attribute__((address_space(3))) bf16x8*)(cur + (wm * kWbM + x) * kFragBytes + lane * 16);
     };
     auto frag_b = [&](lds_u8* cur, int y) {
-        return *(__attribute__((address_space(3))) bf16x8*)(cur + (kStageFragsA + wn * kWbN + y) * kFragBytes + lane * 16);
+        return *(__attribute__((address_space(3))) bf16x8*)(cur + (kTileM + wn * kWbN + y) * kFragBytes + lane * 16);
     };
     if (!lag) {
         for (int64_t s = 0; s < stages; ++s) {
@@ -234,37 +166,6 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_frag(const uint8_t* __res
                     acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[x], hb[y], acc[x][y], 0, 0, 0);
         }
     }
-#else
-    for (int64_t s = 0; s < stages; ++s) {
-        // Stage s has landed once only the later stages' loads are pending;
-        // the barrier then also says every wave is done with stage s - 1,
-        // whose buffer the next loads reuse.
-        const int64_t later = stages - 1 - s < kBufs - 2 ? stages - 1 - s : kBufs - 2;
-        wait_stages(static_cast<int>(later));
-        stage_barrier();
-        if (s + kBufs - 1 < stages)
-            load_stage(fa, fb, bm0, bn0, mb, nb, kb, s + kBufs - 1, lds + ((s + kBufs - 1) % kBufs) * kBufBytes, wave,
-                       lane);
-        lds_u8* cur = lds + (s % kBufs) * kBufBytes;
-#pragma unroll
-        for (int ks = 0; ks < kStageSteps; ++ks) {
-            if (s * kStageSteps + ks >= kb) break;  // uniform: a k tail of one step
-            bf16x8 a[kWbM], b[kWbN];
-#pragma unroll
-            for (int x = 0; x < kWbM; ++x)
-                a[x] = *(__attribute__((address_space(3))) bf16x8*)(cur + (ks * kTileM + wm * kWbM + x) * kFragBytes + lane * 16);
-#pragma unroll
-            for (int y = 0; y < kWbN; ++y)
-                b[y] = *(__attribute__((address_space(3))) bf16x8*)(cur + (kStageFragsA + ks * kTileN + wn * kWbN + y) * kFragBytes + lane * 16);
-#pragma unroll
-            for (int x = 0; x < kWbM; ++x)
-#pragma unroll
-                for (int y = 0; y < kWbN; ++y)
-                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
-        }
-    }
-
-#endif
 
     // Epilogue: through each wave's own LDS slice of the (now idle) stage
     // buffers, once every wave is done reading the last stage.

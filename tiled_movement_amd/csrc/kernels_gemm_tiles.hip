@@ -41,32 +41,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-#ifndef SWZ_GT_XCD  // 1: give each of the 8 XCDs (own L2) a contiguous run of tiles
-#define SWZ_GT_XCD 0
-#endif
-#ifndef SWZ_GT_PRIO  // 1: raise the wave's issue priority while it issues products
-#define SWZ_GT_PRIO 0
-#endif
-#ifndef SWZ_GT_PINGPONG  // 1: the second half of the waves runs half a stage behind the first
-#define SWZ_GT_PINGPONG 1
-#endif
-
-#ifndef SWZ_GT_WAVES_M  // waves along m / n; each wave owns WB_M x WB_N blocks of 16 x 16
-#define SWZ_GT_WAVES_M 4
-#endif
-#ifndef SWZ_GT_WAVES_N
-#define SWZ_GT_WAVES_N 2
-#endif
-#ifndef SWZ_GT_WB_M
-#define SWZ_GT_WB_M 4
-#endif
-#ifndef SWZ_GT_WB_N
-#define SWZ_GT_WB_N 8
-#endif
-
-constexpr int kWavesM = SWZ_GT_WAVES_M, kWavesN = SWZ_GT_WAVES_N, kWaves = kWavesM * kWavesN;
+// Waves along m / n; each wave owns kWbM x kWbN blocks of 16 x 16.
+constexpr int kWavesM = 4, kWavesN = 2, kWaves = kWavesM * kWavesN;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWbM = SWZ_GT_WB_M, kWbN = SWZ_GT_WB_N;  // 16x16 blocks per wave
+constexpr int kWbM = 4, kWbN = 8;
 constexpr int kTileRows = 256;                        // rows of A / of B^T per workgroup tile
 constexpr int kTileK = 64;                            // k per stage (two 32-wide steps)
 constexpr int kTileBytes = kTileRows * kTileK * 2;    // one operand tile: 32 KiB
@@ -143,18 +121,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restri
     const int lane = t % 64;
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int64_t mb = m / 16, nb = n / 16, kb = k / 32;
-    int64_t ty = blockIdx.y, tx = blockIdx.x;
-    if (SWZ_GT_XCD == 1) {
-        // Workgroups are handed to the 8 XCDs in turn; renumber so that the
-        // ones on one XCD cover neighbouring tiles and share operand bands
-        // in that XCD's L2.
-        const uint32_t nt = gridDim.x * gridDim.y, id = blockIdx.y * gridDim.x + blockIdx.x;
-        if (nt % 8 == 0) {
-            const uint32_t u = (id % 8) * (nt / 8) + id / 8;
-            ty = u / gridDim.x;
-            tx = u % gridDim.x;
-        }
-    }
+    const int64_t ty = blockIdx.y, tx = blockIdx.x;
     const int64_t r0a = (tile_row0 + ty) * kTileRows, r0b = tx * kTileRows;
     const int64_t bm0 = r0a / 16, bn0 = r0b / 16;
     const int64_t stages = (k + kTileK - 1) / kTileK;
@@ -189,7 +156,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restri
         }
     };
     const int64_t full = kb / 2;  // stages with both 32-wide k steps
-#if SWZ_GT_PINGPONG
     // Waves 0-3 and 4-7 share the SIMDs pairwise.  The first half starts
     // each stage with its fragment reads; the second half starts it with the
     // products of the previous stage's second k step, whose fragments it
@@ -206,7 +172,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restri
             read_a(ta, 0, wm, fbase, L, a0);
             read_b(tb, 0, wn, fbase, L, bq);
             read_a(ta, 1, wm, fbase, L, a1);
-            if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int y = 0; y < kWbN; ++y) {
 #pragma unroll
@@ -215,7 +180,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restri
                 bq[y] = read_b1(tb, 1, wn, y, fbase, L);
             }
             mma_step(acc, a1, bq);
-            if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(0);
         }
     } else {
         bf16x8 a1[kWbM], bq[kWbN];
@@ -225,7 +189,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restri
             const lds_u8* tb = ta + kTileBytes;
             bf16x8 a0[kWbM];
             read_a(ta, 0, wm, fbase, L, a0);
-            if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(1);
             if (s > 0) {
 #pragma unroll
                 for (int y = 0; y < kWbN; ++y) {
@@ -245,38 +208,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tiles(const uint8_t* __restri
                     acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[x], bq[y], acc[x][y], 0, 0, 0);
                 bq[y] = read_b1(tb, 1, wn, y, fbase, L);
             }
-            if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(0);
             // a1 and bq now hold this stage's second k step, multiplied at
             // the start of the next stage.  Every read of this buffer has
             // returned before the next barrier (begin_stage waits for them).
         }
         if (full > 0) mma_step(acc, a1, bq);
     }
-#else
-    for (int64_t s = 0; s < full; ++s) {
-        begin_stage(s);
-        const lds_u8* ta = lds + (s & 1) * kBufBytes;
-        const lds_u8* tb = ta + kTileBytes;
-        // The second k step's B fragments are requested while the first
-        // step's products run, each into the registers of the first step's
-        // fragment that has just been used for the last time (the products
-        // go column by column); its A fragments before the first product.
-        bf16x8 av[kWbM], bv[kWbN], a1[kWbM];
-        read_a(ta, 0, wm, fbase, L, av);
-        read_b(tb, 0, wn, fbase, L, bv);
-        read_a(ta, 1, wm, fbase, L, a1);
-        if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int y = 0; y < kWbN; ++y) {
-#pragma unroll
-            for (int x = 0; x < kWbM; ++x)
-                acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[x], bv[y], acc[x][y], 0, 0, 0);
-            bv[y] = read_b1(tb, 1, wn, y, fbase, L);
-        }
-        mma_step(acc, a1, bv);
-        if (SWZ_GT_PRIO) __builtin_amdgcn_s_setprio(0);
-    }
-#endif
     if (kb % 2) {  // a last stage with one 32-wide k step
         begin_stage(full);
         const lds_u8* ta = lds + (full & 1) * kBufBytes;

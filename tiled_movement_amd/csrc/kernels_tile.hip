@@ -22,19 +22,6 @@
 
 #include "launch.h"
 
-#ifndef SWZ_TILE_ORDER  // transposes: 1 = diagonal tile order, 0 = row-major
-#define SWZ_TILE_ORDER 1
-#endif
-#ifndef SWZ_STAGE_ORDER  // operand staging: row-major keeps reads and writes contiguous
-#define SWZ_STAGE_ORDER 0
-#endif
-#ifndef SWZ_GRID3D  // 1: 3-D grids (tile row, tile column, batch) where they fit
-#define SWZ_GRID3D 1
-#endif
-#ifndef SWZ_NONTEMPORAL  // 1: non-temporal global loads and stores
-#define SWZ_NONTEMPORAL 1
-#endif
-
 namespace swz {
 namespace {
 
@@ -48,18 +35,13 @@ constexpr int64_t kMaxGrid = int64_t(1) << 22;
 // Cache-policy operand of the direct load for a non-temporal access.
 constexpr int kDirectNT = 2;
 
+// Every byte is read once and written once: non-temporal 16-byte accesses.
 __device__ __forceinline__ u32x4 gload16(const uint8_t* p) {
-    const u32x4* q = reinterpret_cast<const u32x4*>(p);
-    if (SWZ_NONTEMPORAL) return __builtin_nontemporal_load(q);
-    return *q;
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
 __device__ __forceinline__ void gstore16(uint8_t* p, u32x4 v) {
-    u32x4* q = reinterpret_cast<u32x4*>(p);
-    if (SWZ_NONTEMPORAL)
-        __builtin_nontemporal_store(v, q);
-    else
-        *q = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
 // Tile (batch b, tile row tr, tile column tc) of linear tile index t.
@@ -171,6 +153,65 @@ __device__ __forceinline__ void store16_edge(uint8_t* D, int64_t row, int64_t co
     }
 }
 
+// The global side of one tile: its source pieces, in the tile's own
+// coordinates (r, c) = source element (r0 + r, c0 + c), and its output
+// pieces (orow, ocol) = output element (c0 + orow, r0 + ocol).  A whole tile
+// (kFull) keeps two wave-uniform base pointers, the tile's first source and
+// output elements, and 32-bit row pitches from the host: a lane's address is
+// one 32 x 32 -> 64-bit multiply-add.  Edge tiles (and matrices whose sizes
+// need 64 bits) index the matrix with 64-bit products, guarded as EDGE says.
+//
+// Why the whole-tile path is lean: a workgroup lives for one load and one
+// store, and every wave runs the tile's address arithmetic on its CU's one
+// scalar unit before its first load.  Measured on MI355X (fp32 4096^2,
+// 32x32 tiles): adding 32 / 64 / 128 dependent scalar multiplies ahead of
+// the load lengthens the kernel by 1 / 3 / 3.5%, and a general prelude
+// (64-bit tile bases and edge tests, the swizzle of every step from run-time
+// (B, M, S)) cost the same 3.5%.
+template <int EDGE, int ESZ>
+struct TileIo {
+    const uint8_t* S;  // kFull: the tile's first source element; otherwise the source matrix
+    uint8_t* D;        // kFull: the tile's first output element; otherwise the output matrix
+    int64_t rows, cols, r0, c0;
+    uint32_t sp, dp;  // kFull: source / output row pitch in bytes
+
+    __device__ __forceinline__ const uint8_t* src(int r, int c) const {
+        return S + (static_cast<uint64_t>(static_cast<uint32_t>(r)) * sp + static_cast<uint32_t>(c * ESZ));
+    }
+    __device__ __forceinline__ u32x4 load(int r, int c) const {
+        if constexpr (EDGE == kFull) return gload16(src(r, c));
+        else return load16_edge<EDGE, ESZ>(S, r0 + r, c0 + c, rows, cols);
+    }
+    // Whole-row tiles (cols == tile width, c0 = 0): a vector may span rows,
+    // so the edge paths guard the flat index.
+    __device__ __forceinline__ u32x4 load_flat(int r, int c) const {
+        if constexpr (EDGE == kFull) return gload16(src(r, c));
+        else return load16_edge<EDGE, ESZ>(S, 0, (r0 + r) * cols + c0 + c, 1, rows * cols);
+    }
+    __device__ __forceinline__ void store(int orow, int ocol, u32x4 v) const {
+        if constexpr (EDGE == kFull)
+            gstore16(D + (static_cast<uint64_t>(static_cast<uint32_t>(orow)) * dp + static_cast<uint32_t>(ocol * ESZ)), v);
+        else
+            store16_edge<EDGE, ESZ>(D, c0 + orow, r0 + ocol, cols, rows, v);
+    }
+};
+
+// The whole-tile path of a launch, planned on the host: row pitches in bytes
+// and the numbers of tile rows and columns whose tiles lie wholly inside the
+// matrix; all zero (every tile takes a 64-bit edge path) when a size needs
+// more than 32 bits.
+struct FastPath {
+    uint32_t sp, dp, full_r, full_c;
+};
+
+FastPath fast_path(int64_t batch, int64_t rows, int64_t cols, int esz, int tr, int tc) {
+    const int64_t lim = int64_t(1) << 31;
+    if (batch * rows >= lim || batch * cols >= lim || rows * esz >= 2 * lim || cols * esz >= 2 * lim)
+        return FastPath{0u, 0u, 0u, 0u};
+    return FastPath{static_cast<uint32_t>(cols * esz), static_cast<uint32_t>(rows * esz), static_cast<uint32_t>(rows / tr),
+                    static_cast<uint32_t>(cols / tc)};
+}
+
 // Workgroups per CU.  The transposed HBM pattern of the 16-bit and 8-bit
 // tiles runs faster with fewer tiles in flight (measured with an LDS-free
 // probe of the same pattern: 64 x 64 16-bit tiles at 8 to 16 workgroups per
@@ -179,45 +220,15 @@ __device__ __forceinline__ void store16_edge(uint8_t* D, int64_t row, int64_t co
 // Values from a sweep of the kernels themselves (2 to 8 per CU): 4 for the
 // 64-row 16-bit kinds (+3 to +8%), 5 for the byte kind (+4%); the fp32 tile
 // loses bandwidth when limited and staging's 32 KiB tile already sits at 5.
-#ifndef SWZ_OCC_SCALAR
-#define SWZ_OCC_SCALAR 0
-#endif
-#ifndef SWZ_OCC_B64
-#define SWZ_OCC_B64 4
-#endif
-#ifndef SWZ_OCC_B128
-#define SWZ_OCC_B128 4
-#endif
-#ifndef SWZ_OCC_STAGE
-#define SWZ_OCC_STAGE 0
-#endif
-#ifndef SWZ_OCC_TR16
-#define SWZ_OCC_TR16 4
-#endif
-#ifndef SWZ_OCC_TR8
-#define SWZ_OCC_TR8 5
-#endif
-#ifndef SWZ_OCC_NARROW
-#define SWZ_OCC_NARROW 0
-#endif
-
-// Whole-row tiles: uncapped, except the 16 KiB byte tiles of 32 and 64
-// columns, which a sweep (uncapped, 4 and 8 per CU) put 4% faster at 4;
-// every other narrow kind lost up to 20% when capped.
-#ifndef SWZ_OCC_BNARROW_WIDE
-#define SWZ_OCC_BNARROW_WIDE 4
-#endif
-
+// The byte tiles of 32 and 64 columns (16 KiB) are capped at 4 per CU (4%
+// faster in a sweep of uncapped, 4 and 8); every other whole-row kind lost up
+// to 20% when capped.
 template <int KIND>
 constexpr int occupancy_limit() {
-    return KIND == SWZ_READ_SCALAR_COL ? SWZ_OCC_SCALAR
-           : KIND == SWZ_READ_B64_4X4  ? SWZ_OCC_B64
-           : KIND == SWZ_READ_B128_8X8 ? SWZ_OCC_B128
-           : KIND == SWZ_READ_MFMA_16X16X32 ? SWZ_OCC_STAGE
-           : KIND == SWZ_READ_B64_TR16 ? SWZ_OCC_TR16
-           : KIND == SWZ_READ_B64_TR8  ? SWZ_OCC_TR8
-           : (KIND == SWZ_READ_BNARROW32 || KIND == SWZ_READ_BNARROW64) ? SWZ_OCC_BNARROW_WIDE
-                                       : SWZ_OCC_NARROW;
+    return KIND == SWZ_READ_B64_4X4 || KIND == SWZ_READ_B128_8X8 || KIND == SWZ_READ_B64_TR16 ? 4
+           : KIND == SWZ_READ_B64_TR8                                  ? 5
+           : (KIND == SWZ_READ_BNARROW32 || KIND == SWZ_READ_BNARROW64) ? 4
+                                                                        : 0;
 }
 
 constexpr int kLdsPerCu = 160 * 1024;
@@ -248,34 +259,45 @@ struct LdsTile {
     static constexpr int BYTES = K::TR * (K::TC + (FILL == kPadded ? PAD : 0)) * K::ESZ;
 };
 
+// The LDS layout as the tile kernels take it: the row pitch (padded rows)
+// and Swizzle<B,M,S> decoded on the host into x ^ (((x >> src) & mask) <<
+// dst), so no wave re-derives masks and shifts from (B, M, S) (mask 0: plain
+// rows, the identity).
+struct KLayout {
+    uint32_t ld, mask, src, dst;
+};
+
+__device__ __forceinline__ uint32_t kswizzle(uint32_t x, const KLayout& L) {
+    return x ^ (((x >> L.src) & L.mask) << L.dst);
+}
+
+KLayout decode_layout(const LdsLayout& L) {
+    const int32_t S = L.S;
+    const uint32_t up = S >= 0 ? static_cast<uint32_t>(S) : 0u, dn = S >= 0 ? 0u : static_cast<uint32_t>(-S);
+    uint32_t mask = L.B >= 32u ? 0xffffffffu : ((1u << L.B) - 1u);
+    if (L.M + up >= 32u || L.M + dn >= 32u) mask = 0u;  // the moved field lies outside 32 bits: identity
+    return KLayout{L.ld, mask, (L.M + up) & 31u, (L.M + dn) & 31u};
+}
+
 // Element offset in LDS of step i of this lane: the lane's first offset
-// `base` combined with the step's lane-independent move (see steps_decompose).
-// PADDED: rows of L.ld = TC + PAD elements, offsets add.  Otherwise rows of
-// TC elements under Swizzle<B,M,S> (B = 0: plain rows), offsets combine by
-// XOR.  Either way the move is one value shared by the wave; the row pitch
-// is a run-time value in both, so the three layouts issue the same LDS
-// instructions (no pairing into two-address forms for one of them) and
-// differ only in the addresses.
-template <int KIND, bool WRITE, bool PADDED>
-__device__ __forceinline__ uint32_t step_off(uint32_t base, int i, const LdsLayout& L) {
-    using K = Kind<KIND>;
-    int dr = 0, dc = 0;
-    coord<KIND, WRITE>(0, i, dr, dc);
-    if (PADDED) {
-        uint32_t d = static_cast<uint32_t>(dr) * L.ld + static_cast<uint32_t>(dc);
-        asm volatile("" : "+s"(d));  // keep the move opaque: no two-address pairing
-        return base + d;
-    }
-    return base ^ swizzle(static_cast<uint32_t>(dr * K::TC + dc), L.B, L.M, L.S);
+// `base` combined with the step's wave-uniform move (StepMoves, computed on
+// the host).  PADDED: rows of L.ld = TC + PAD elements, offsets add.
+// Otherwise rows of TC elements under Swizzle<B,M,S> (B = 0: plain rows),
+// offsets combine by XOR.  The three layouts issue the same LDS instructions
+// and differ only in the addresses.
+template <bool WRITE, bool PADDED>
+__device__ __forceinline__ uint32_t step_off(uint32_t base, int i, const StepMoves& mv) {
+    const uint32_t m = WRITE ? mv.w[i] : mv.r[i];
+    return PADDED ? base + m : base ^ m;
 }
 
 template <int KIND, bool WRITE, bool PADDED>
-__device__ __forceinline__ uint32_t lane_base(int t, const LdsLayout& L) {
+__device__ __forceinline__ uint32_t lane_base(int t, const KLayout& L) {
     using K = Kind<KIND>;
     int r = 0, c = 0;
     coord<KIND, WRITE>(t, 0, r, c);
     if (PADDED) return static_cast<uint32_t>(r) * L.ld + static_cast<uint32_t>(c);
-    return swizzle(static_cast<uint32_t>(r * K::TC + c), L.B, L.M, L.S);
+    return kswizzle(static_cast<uint32_t>(r * K::TC + c), L);
 }
 
 // Direct fill of one tile (see Direct in swz_common.h): each load writes
@@ -287,21 +309,27 @@ __device__ __forceinline__ uint32_t lane_base(int t, const LdsLayout& L) {
 // stored.  Rows must be 16-byte aligned for 2-byte elements, so a 16-byte
 // slot is wholly inside or wholly outside.  Waits for its own loads; the
 // caller's barrier then publishes the tile.
-template <int KIND, bool FULL>
-__device__ __forceinline__ void direct_fill(const uint8_t* __restrict__ S, int64_t rows, int64_t cols, int64_t r0,
-                                            int64_t c0, uint8_t* lds, const LdsLayout& L, int t) {
+template <int KIND, int EDGE>
+__device__ __forceinline__ void direct_fill(const TileIo<EDGE, Kind<KIND>::ESZ>& io, uint8_t* lds, const KLayout& L,
+                                            const StepMoves& mv, int t) {
     using K = Kind<KIND>;
     using D = Direct<KIND>;
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
-    const uint32_t base = swizzle(static_cast<uint32_t>(D::EPL * t), L.B, L.M, L.S);
+    const uint32_t base = kswizzle(static_cast<uint32_t>(D::EPL * t), L);
     const int wave = __builtin_amdgcn_readfirstlane(t / 64);
 #pragma unroll
     for (int j = 0; j < D::LOADS; ++j) {
-        const uint32_t e = base ^ swizzle(static_cast<uint32_t>(D::EPL * K::NT * j), L.B, L.M, L.S);
-        const int64_t r = r0 + static_cast<int64_t>(e / K::TC), c = c0 + static_cast<int64_t>(e % K::TC);
-        const uint8_t* g = (FULL || (r < rows && c < cols)) ? S + (r * cols + c) * K::ESZ : S + (r0 * cols + c0) * K::ESZ;
+        const uint32_t e = base ^ mv.d[j];
+        const int lr = static_cast<int>(e / K::TC), lc = static_cast<int>(e % K::TC);
+        const uint8_t* g;
+        if constexpr (EDGE == kFull) {
+            g = io.src(lr, lc);
+        } else {
+            const int64_t r = io.r0 + lr, c = io.c0 + lc;
+            g = r < io.rows && c < io.cols ? io.S + (r * io.cols + c) * K::ESZ : io.S + (io.r0 * io.cols + io.c0) * K::ESZ;
+        }
         lds_u8* slot = (lds_u8*)lds + D::VB * (64 * wave + K::NT * j);
-        __builtin_amdgcn_global_load_lds(g, slot, D::VB, 0, SWZ_NONTEMPORAL ? kDirectNT : 0);
+        __builtin_amdgcn_global_load_lds(g, slot, D::VB, 0, kDirectNT);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -313,8 +341,7 @@ __device__ __forceinline__ void direct_fill(const uint8_t* __restrict__ S, int64
 // Global loads of one tile into registers, guarded at the matrix edge as EDGE
 // says (Edge above).
 template <int KIND, int EDGE>
-__device__ __forceinline__ void load_tile(const uint8_t* __restrict__ S, int64_t rows, int64_t cols, int64_t r0,
-                                          int64_t c0, int t, u32x4* v) {
+__device__ __forceinline__ void load_tile(const TileIo<EDGE, Kind<KIND>::ESZ>& io, int t, u32x4* v) {
     using K = Kind<KIND>;
     constexpr int PER = 16 / K::ESZ;  // elements per global load
 #pragma unroll
@@ -322,15 +349,13 @@ __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ S, int64_t
         int r = 0, c = 0;
         K::wcoord(t, j * (K::WSTEPS / K::GLOADS), r, c);
         c -= c % PER;  // the vector's first column
-        if (is_narrow(KIND))  // whole-row tiles: a vector may span rows, guard the flat index
-            v[j] = load16_edge<EDGE, K::ESZ>(S, 0, (r0 + r) * cols + c0 + c, 1, rows * cols);
-        else
-            v[j] = load16_edge<EDGE, K::ESZ>(S, r0 + r, c0 + c, rows, cols);
+        v[j] = is_narrow(KIND) ? io.load_flat(r, c) : io.load(r, c);
     }
 }
 
 template <int KIND, bool PADDED>
-__device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const LdsLayout& L, const u32x4* v) {
+__device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const KLayout& L, const StepMoves& mv,
+                                          const u32x4* v) {
     using K = Kind<KIND>;
     if constexpr (K::VEC == 4 && K::ESZ < 4) {
         // Narrow rows of 2- or 1-byte elements: 4-byte runs (M >= 1 resp. 2
@@ -350,7 +375,7 @@ __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const Ld
                     K::wcoord(t, 4 * j + e, r, c);
                     off = static_cast<uint32_t>(r) * L.ld + static_cast<uint32_t>(c);
                 } else {
-                    off = step_off<KIND, true, false>(wbase, 4 * j + e, L);
+                    off = step_off<true, false>(wbase, 4 * j + e, mv);
                 }
                 const uint32_t lo = sw1 ? v[j][e ^ 1] : v[j][e], hi = sw1 ? v[j][e ^ 3] : v[j][e ^ 2];
                 *reinterpret_cast<uint32_t*>(lds + K::ESZ * off) = sw2 ? hi : lo;
@@ -362,7 +387,7 @@ __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const Ld
         for (int j = 0; j < K::GLOADS; ++j) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                reinterpret_cast<uint32_t*>(lds)[step_off<KIND, true, PADDED>(wbase, 4 * j + e, L)] = v[j][e];
+                reinterpret_cast<uint32_t*>(lds)[step_off<true, PADDED>(wbase, 4 * j + e, mv)] = v[j][e];
         }
     } else if constexpr (K::ESZ == 1) {
         // Two 8-byte writes per 16-byte vector (the swizzle keeps 8-byte
@@ -380,7 +405,7 @@ __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const Ld
                     K::wcoord(t, 2 * j + h, r, c);
                     off = static_cast<uint32_t>(r) * L.ld + static_cast<uint32_t>(c);
                 } else {
-                    off = step_off<KIND, true, false>(wbase, 2 * j + h, L);
+                    off = step_off<true, false>(wbase, 2 * j + h, mv);
                 }
                 int r0 = 0, c0 = 0;
                 K::wcoord(t, 2 * j, r0, c0);
@@ -391,16 +416,15 @@ __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const Ld
     } else {
 #pragma unroll
         for (int j = 0; j < K::GLOADS; ++j)
-            *reinterpret_cast<u32x4*>(lds + 2 * step_off<KIND, true, PADDED>(wbase, j, L)) = v[j];
+            *reinterpret_cast<u32x4*>(lds + 2 * step_off<true, PADDED>(wbase, j, mv)) = v[j];
     }
 }
 
 // Read this thread's pieces of the tile back from LDS, transposed, and store
 // them to the output, guarded at the matrix edge as EDGE says.
 template <int KIND, bool PADDED, int EDGE>
-__device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbase, const LdsLayout& L,
-                                               uint8_t* __restrict__ D, int64_t rows, int64_t cols, int64_t r0,
-                                               int64_t c0, int t) {
+__device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbase, const KLayout& L,
+                                               const StepMoves& mv, const TileIo<EDGE, Kind<KIND>::ESZ>& io, int t) {
     using K = Kind<KIND>;
     if constexpr (K::ESZ == 4 && (KIND == SWZ_READ_SCALAR_COL || is_narrow(KIND))) {
         // Task j: four rows of one source column -> 16 bytes of an output row.
@@ -409,14 +433,13 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                o[e] = reinterpret_cast<const uint32_t*>(lds)[step_off<KIND, false, PADDED>(rbase, 4 * j + e, L)];
+                o[e] = reinterpret_cast<const uint32_t*>(lds)[step_off<false, PADDED>(rbase, 4 * j + e, mv)];
             int r = 0, c = 0;
             K::rcoord(t, 4 * j, r, c);
-            const int64_t orow = c0 + c, ocol = r0 + r;
             // Assembled from four loads, the vector is otherwise rebuilt at
             // the store in a way that drops the store's non-temporal hint.
             asm volatile("" : "+v"(o));
-            store16_edge<EDGE, 4>(D, orow, ocol, cols, rows, o);
+            io.store(c, r, o);
         }
     } else if constexpr (narrow_by_element<KIND>()) {
         // Narrow rows of 2-byte elements read an element at a time: PER rows
@@ -425,14 +448,14 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
         uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            const uint32_t x = *reinterpret_cast<const uint16_t*>(lds + 2 * step_off<KIND, false, PADDED>(rbase, e, L));
+            const uint32_t x = *reinterpret_cast<const uint16_t*>(lds + 2 * step_off<false, PADDED>(rbase, e, mv));
             w[e / 2] |= x << (16 * (e % 2));
         }
         u32x4 o{w[0], w[1], w[2], w[3]};
         int r = 0, c = 0;
         K::rcoord(t, 0, r, c);
         asm volatile("" : "+v"(o));
-        store16_edge<EDGE, 2>(D, c0 + c, r0 + r, cols, rows, o);
+        io.store(c, r, o);
     } else if constexpr (is_narrow(KIND)) {
         // Narrow rows of 2- or 1-byte elements: the lane's block of PER rows
         // and CB columns arrives as RSTEPS whole words (EPW columns of one
@@ -444,7 +467,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
         uint32_t w[K::RSTEPS];
 #pragma unroll
         for (int i = 0; i < K::RSTEPS; ++i)
-            w[i] = *reinterpret_cast<const uint32_t*>(lds + E * step_off<KIND, false, PADDED>(rbase, i, L));
+            w[i] = *reinterpret_cast<const uint32_t*>(lds + E * step_off<false, PADDED>(rbase, i, mv));
         int r = 0, c = 0;
         K::rcoord(t, 0, r, c);
 #pragma unroll
@@ -462,7 +485,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
                 o[d] = x;
             }
             asm volatile("" : "+v"(o));
-            store16_edge<EDGE, E>(D, c0 + c + j, r0 + r, cols, rows, o);
+            io.store(c + j, r, o);
         }
     } else if constexpr (KIND == SWZ_READ_B64_TR8) {
         // Task j: in each of two steps h the 8-bit transpose read gives this
@@ -482,7 +505,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             u32x2 h[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const uint32_t off = step_off<KIND, false, PADDED>(rbase, 2 * j + s, L);
+                const uint32_t off = step_off<false, PADDED>(rbase, 2 * j + s, mv);
                 h[s] = __builtin_bit_cast(
                     u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)((__attribute__((address_space(3))) uint8_t*)lds + off)));
             }
@@ -493,9 +516,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             got[0] = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(send[0]), 0x128, 0xf, 0xf, false));
             got[1] = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(send[1]), 0x128, 0xf, 0xf, false));
             const u32x4 o = upper ? u32x4{got[0], got[1], h[1][0], h[1][1]} : u32x4{h[0][0], h[0][1], got[0], got[1]};
-            const int64_t orow = c0 + 8 * ch + q % 8;
-            const int64_t ocol = r0 + (upper ? 64 : 0) + 16 * g;
-            store16_edge<EDGE, 1>(D, orow, ocol, cols, rows, o);
+            io.store(8 * ch + q % 8, (upper ? 64 : 0) + 16 * g, o);
         }
     } else if constexpr (KIND == SWZ_READ_B64_TR16) {
         // Task j: two transpose reads give this lane 8 consecutive rows of
@@ -518,7 +539,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
                     K::rcoord(0, 2 * j + s, dr, dc);
                     off = static_cast<uint32_t>(lr0 ^ dr) * L.ld + static_cast<uint32_t>(lc0 ^ dc);
                 } else {
-                    off = step_off<KIND, false, false>(rbase, 2 * j + s, L);
+                    off = step_off<false, false>(rbase, 2 * j + s, mv);
                 }
                 const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((__attribute__((address_space(3))) uint8_t*)lds + 2 * off));
                 h[s] = __builtin_bit_cast(u32x2, v);
@@ -526,9 +547,7 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             const u32x2 lo = odd ? h[1] : h[0], hi = odd ? h[0] : h[1];
             const u32x4 o{lo[0], lo[1], hi[0], hi[1]};
             const int ch = t / 64 + (K::NT / 64) * j;
-            const int64_t orow = c0 + 8 * ch + 4 * ((q / 4) % 2) + q % 4;
-            const int64_t ocol = r0 + 16 * g + 8 * (q / 8);
-            store16_edge<EDGE, 2>(D, orow, ocol, cols, rows, o);
+            io.store(8 * ch + 4 * ((q / 4) % 2) + q % 4, 16 * g + 8 * (q / 8), o);
         }
     } else {
         // Task j: 8 rows of a column block; transpose 16-bit elements in
@@ -540,36 +559,48 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
             R x[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s)
-                x[s] = *reinterpret_cast<const R*>(lds + 2 * step_off<KIND, false, PADDED>(rbase, 8 * j + s, L));
+                x[s] = *reinterpret_cast<const R*>(lds + 2 * step_off<false, PADDED>(rbase, 8 * j + s, mv));
             int rb = 0, cb = 0;
             K::rcoord(t, 8 * j, rb, cb);
 #pragma unroll
             for (int q = 0; q < kCols; ++q) {
                 const u32x4 o{pair_col(x[0], x[1], q), pair_col(x[2], x[3], q), pair_col(x[4], x[5], q),
                               pair_col(x[6], x[7], q)};
-                const int64_t orow = c0 + cb + q, ocol = r0 + rb;
-                store16_edge<EDGE, 2>(D, orow, ocol, cols, rows, o);
+                io.store(cb + q, rb, o);
             }
         }
     }
 }
 
+// A workgroup moves one tile and its waves live for one load-store round, so
+// the loads go out first: the lanes' LDS addresses are computed while they
+// are in flight.  (An empty asm on a copy of the thread index, ordered after
+// the loads, keeps the compiler from hoisting that arithmetic above them;
+// issuing the loads ahead of it measured 2% faster on the fp32 tile.)
+__device__ __forceinline__ int after_loads(int t) {
+    asm volatile("" : "+v"(t));
+    __builtin_assume(t >= 0 && t < 1024);  // a thread index: unsigned arithmetic on it
+    return t;
+}
+
 template <int KIND, int FILL, int EDGE>
-__device__ __forceinline__ void convert_tile(const uint8_t* __restrict__ S, uint8_t* __restrict__ D, int64_t rows,
-                                             int64_t cols, int64_t r0, int64_t c0, uint8_t* lds, uint32_t wbase,
-                                             uint32_t rbase, const LdsLayout& L, int t) {
+__device__ __forceinline__ void convert_tile(const TileIo<EDGE, Kind<KIND>::ESZ>& io, uint8_t* lds, const KLayout& L,
+                                             const StepMoves& mv, int t) {
     using K = Kind<KIND>;
     constexpr bool PADDED = FILL == kPadded;
+    int ta = t;
     if constexpr (FILL == kDirect) {
         static_assert(EDGE != kElem, "the direct fill needs 16-byte aligned rows");
-        direct_fill<KIND, EDGE == kFull>(S, rows, cols, r0, c0, lds, L, t);
+        direct_fill<KIND, EDGE>(io, lds, L, mv, t);
     } else {
         u32x4 v[K::GLOADS];
-        load_tile<KIND, EDGE>(S, rows, cols, r0, c0, t, v);
-        lds_store<KIND, PADDED>(lds, wbase, L, v);
+        load_tile<KIND, EDGE>(io, t, v);
+        ta = after_loads(t);
+        lds_store<KIND, PADDED>(lds, lane_base<KIND, true, PADDED>(ta, L), L, mv, v);
     }
+    const uint32_t rbase = lane_base<KIND, false, PADDED>(ta, L);
     __syncthreads();
-    lds_read_store<KIND, PADDED, EDGE>(lds, rbase, L, D, rows, cols, r0, c0, t);
+    lds_read_store<KIND, PADDED, EDGE>(lds, rbase, L, mv, io, t);
 }
 
 // Which tile this workgroup moves.  GRID3D: blockIdx = (tile row, tile
@@ -582,9 +613,16 @@ __device__ __forceinline__ void my_tile(int64_t tiles_r, int64_t tiles_c, int64_
     if (GRID3D) {
         b = blockIdx.z;
         if (DIAGONAL) {
+            // tc = (y + f) mod n with y < n: one conditional subtract, and a
+            // division only when the shift f reaches n (a uniform branch,
+            // laid out of line: the whole path runs without a taken branch)
             const uint32_t n = static_cast<uint32_t>(tiles_c);
+            uint32_t f = (blockIdx.x * O.num) >> O.sh;
+            if (__builtin_expect(f >= n, 0)) f %= n;
+            uint32_t c = blockIdx.y + f;
+            if (c >= n) c -= n;
             tr = blockIdx.x;
-            tc = static_cast<int64_t>((blockIdx.y + ((blockIdx.x * O.num) >> O.sh) % n) % n);
+            tc = static_cast<int64_t>(c);
         } else {
             tc = blockIdx.x;
             tr = blockIdx.y;
@@ -594,33 +632,48 @@ __device__ __forceinline__ void my_tile(int64_t tiles_r, int64_t tiles_c, int64_
     }
 }
 
+// Arguments in the order the kernel needs them: the first thirteen dwords
+// (pointers, tile columns, tile order, the host's FastPath, 32-bit sizes;
+// plain scalars, which is what the build's kernel-argument preload puts in
+// SGPRs) are all a whole tile of a 3-D launch reads before its first load.
 template <int KIND, int FILL, bool ALIGNED, bool GRID3D>
 __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                                            int64_t rows, int64_t cols, int64_t tiles_r,
-                                                            int64_t tiles_c, int64_t tile0, LdsLayout L,
-                                                            TileOrder O) {
+                                                            uint32_t tiles_c32, uint32_t order_num, uint32_t order_sh,
+                                                            uint32_t sp, uint32_t dp, uint32_t full_r, uint32_t full_c,
+                                                            uint32_t rows32, uint32_t cols32, int64_t rows,
+                                                            int64_t cols, int64_t tiles_r, int64_t tile0, KLayout L,
+                                                            StepMoves mv) {
     using K = Kind<KIND>;
-    constexpr bool PADDED = FILL == kPadded;
+    constexpr int E = K::ESZ;
     static_assert(FILL != kDirect || ALIGNED, "the direct fill needs 16-byte aligned rows");
     __shared__ u32x4 lds_v[(LdsTile<KIND, FILL>::BYTES + 15) / 16];
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
     const int t = threadIdx.x;
-    const int64_t plane = rows * cols * K::ESZ;  // bytes of one batch entry
-    const uint32_t wbase = FILL == kDirect ? 0u : lane_base<KIND, true, PADDED>(t, L);
-    const uint32_t rbase = lane_base<KIND, false, PADDED>(t, L);
 
     int64_t b, tr, tc;
-    my_tile<SWZ_TILE_ORDER != 0, GRID3D>(tiles_r, tiles_c, tile0, O, b, tr, tc);
-    const int64_t r0 = tr * K::TR, c0 = tc * K::TC;
-    const uint8_t* S = src + b * plane;
-    uint8_t* D = dst + b * plane;
+    my_tile<true, GRID3D>(tiles_r, tiles_c32, tile0, TileOrder{order_num, order_sh}, b, tr, tc);
     if constexpr (ALIGNED) {
-        if (r0 + K::TR <= rows && c0 + K::TC <= cols)
-            convert_tile<KIND, FILL, kFull>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
-        else
-            convert_tile<KIND, FILL, kVec>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
+        // Edge tiles branch away; whole tiles fall through.
+        if (__builtin_expect(tr >= full_r || tc >= full_c, 0)) {
+            const int64_t plane = rows * cols * E;  // batch entry b
+            convert_tile<KIND, FILL, kVec>(
+                TileIo<kVec, E>{src + b * plane, dst + b * plane, rows, cols, tr * K::TR, tc * K::TC, 0u, 0u}, lds, L,
+                mv, t);
+            return;
+        }
+        // Batch entry b's rows follow entry b - 1's in both matrices, so a
+        // whole tile is (b rows + r0, c0) of the source and (b cols + c0,
+        // r0) of the output, in 32 bits (the host's FastPath says so).
+        const uint32_t b32 = static_cast<uint32_t>(b);
+        const uint32_t r0 = static_cast<uint32_t>(tr) * K::TR, c0 = static_cast<uint32_t>(tc) * K::TC;
+        const TileIo<kFull, E> io{src + (static_cast<uint64_t>(b32 * rows32 + r0) * sp + c0 * E),
+                                  dst + (static_cast<uint64_t>(b32 * cols32 + c0) * dp + r0 * E), 0, 0, 0, 0, sp, dp};
+        convert_tile<KIND, FILL, kFull>(io, lds, L, mv, t);
     } else {
-        convert_tile<KIND, FILL, kElem>(S, D, rows, cols, r0, c0, lds, wbase, rbase, L, t);
+        const int64_t plane = rows * cols * E;
+        convert_tile<KIND, FILL, kElem>(
+            TileIo<kElem, E>{src + b * plane, dst + b * plane, rows, cols, tr * K::TR, tc * K::TC, 0u, 0u}, lds, L, mv,
+            t);
     }
 }
 
@@ -628,75 +681,122 @@ __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __res
 // Operand staging: 256x64 K-tiles of a K-contiguous 16-bit operand, read
 // back as 16x16x32 operand fragments and written out in lane order.
 // ---------------------------------------------------------------------------
+// One 256 x 64 tile of a K-contiguous operand (rows r0.., k columns k0..).
+// A whole tile (FULL) takes src and frag as the tile's own bases (its first
+// element, its first fragment) and addresses its rows and its 16 row blocks
+// of fragments with the 32-bit pitches sp (the operand row, 2k bytes) and fp
+// (one row block of fragments, 32k bytes); an edge tile indexes the whole
+// operand with 64-bit products and guards each 16-byte chunk (mn and k are
+// multiples of 16 and 32, so a chunk is wholly inside or outside).
 template <int FILL, bool FULL>
 __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint8_t* __restrict__ frag, int64_t mn,
-                                           int64_t k, int64_t r0, int64_t k0, uint8_t* lds, uint32_t wbase,
-                                           uint32_t rbase, const LdsLayout& L, int t) {
+                                           int64_t k, int64_t r0, int64_t k0, uint32_t sp, uint32_t fp, uint8_t* lds,
+                                           const KLayout& L, const StepMoves& mv, int t) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
     constexpr bool PADDED = FILL == kPadded;
+    constexpr int EDGE = FULL ? kFull : kVec;
     using K = Kind<KD>;
+    const TileIo<EDGE, 2> io{src, nullptr, mn, k, r0, k0, sp, 0u};
+    int ta = t;
     if constexpr (FILL == kDirect) {
-        direct_fill<KD, FULL>(src, mn, k, r0, k0, lds, L, t);
+        direct_fill<KD, EDGE>(io, lds, L, mv, t);
     } else {
         u32x4 v[K::GLOADS];
 #pragma unroll
         for (int j = 0; j < K::GLOADS; ++j) {
             int r = 0, c = 0;
             K::wcoord(t, j, r, c);
-            // mn and k are multiples of 16 and 32, so a 16-byte chunk is either
-            // wholly inside the operand or wholly outside.
-            v[j] = (FULL || (r0 + r < mn && k0 + c < k)) ? gload16(src + ((r0 + r) * k + k0 + c) * 2)
-                                                         : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (FULL)
+                v[j] = gload16(io.src(r, c));
+            else
+                v[j] = r0 + r < mn && k0 + c < k ? gload16(src + ((r0 + r) * k + k0 + c) * 2) : u32x4{0u, 0u, 0u, 0u};
         }
+        ta = after_loads(t);
+        const uint32_t wbase = lane_base<KD, true, PADDED>(ta, L);
 #pragma unroll
         for (int j = 0; j < K::GLOADS; ++j)
-            *reinterpret_cast<u32x4*>(lds + 2 * step_off<KD, true, PADDED>(wbase, j, L)) = v[j];
+            *reinterpret_cast<u32x4*>(lds + 2 * step_off<true, PADDED>(wbase, j, mv)) = v[j];
     }
+    const uint32_t rbase = lane_base<KD, false, PADDED>(ta, L);
     __syncthreads();
-    const int64_t ksteps = k / 32;
     const int lane = t % 64;
 #pragma unroll
     for (int i = 0; i < K::RSTEPS; ++i) {
         const int f = K::frag_of(t, i);
         const int blk = f % 16, ks = f / 16;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(lds + 2 * step_off<KD, false, PADDED>(rbase, i, L));
-        if (FULL || (r0 + 16 * blk < mn && k0 + 32 * ks < k)) {
-            const int64_t fi = (r0 / 16 + blk) * ksteps + (k0 / 32 + ks);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(lds + 2 * step_off<false, PADDED>(rbase, i, mv));
+        if constexpr (FULL) {
+            gstore16(frag + (static_cast<uint64_t>(static_cast<uint32_t>(blk)) * fp +
+                             static_cast<uint32_t>(ks * 1024 + lane * 16)),
+                     x);
+        } else if (r0 + 16 * blk < mn && k0 + 32 * ks < k) {
+            const int64_t fi = (r0 / 16 + blk) * (k / 32) + (k0 / 32 + ks);
             gstore16(frag + (fi * 64 + lane) * 16, x);
         }
     }
 }
 
+// Arguments as for k_convert: what a whole tile of a 3-D launch reads first.
 template <int FILL, bool GRID3D>
 __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(const uint8_t* __restrict__ src,
-                                                                            uint8_t* __restrict__ frag, int64_t mn,
-                                                                            int64_t k, int64_t tiles_m,
-                                                                            int64_t tiles_k, int64_t tile0,
-                                                                            LdsLayout L) {
+                                                                            uint8_t* __restrict__ frag, uint32_t sp,
+                                                                            uint32_t fp, uint32_t full_m,
+                                                                            uint32_t full_k, int64_t mn, int64_t k,
+                                                                            int64_t tiles_m, int64_t tiles_k,
+                                                                            int64_t tile0, KLayout L, StepMoves mv) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
-    constexpr bool PADDED = FILL == kPadded;
     using K = Kind<KD>;
     __shared__ u32x4 lds_v[LdsTile<KD, FILL>::BYTES / 16];
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
     const int t = threadIdx.x;
-    const uint32_t wbase = FILL == kDirect ? 0u : lane_base<KD, true, PADDED>(t, L);
-    const uint32_t rbase = lane_base<KD, false, PADDED>(t, L);
 
     int64_t b, tm, tk;
-    my_tile<SWZ_STAGE_ORDER != 0, GRID3D>(tiles_m, tiles_k, tile0, TileOrder{1u, 0u}, b, tm, tk);
-    const int64_t r0 = tm * K::TR, k0 = tk * K::TC;
-    if (r0 + K::TR <= mn && k0 + K::TC <= k)
-        stage_tile<FILL, true>(src, frag, mn, k, r0, k0, lds, wbase, rbase, L, t);
-    else
-        stage_tile<FILL, false>(src, frag, mn, k, r0, k0, lds, wbase, rbase, L, t);
+    my_tile<false, GRID3D>(tiles_m, tiles_k, tile0, TileOrder{1u, 0u}, b, tm, tk);
+    // Edge tiles branch away; whole tiles fall through.
+    if (__builtin_expect(tm >= full_m || tk >= full_k, 0)) {
+        stage_tile<FILL, false>(src, frag, mn, k, tm * K::TR, tk * K::TC, 0u, 0u, lds, L, mv, t);
+        return;
+    }
+    // the tile's first element (row 256 tm, k 64 tk) and first fragment (row
+    // block 16 tm, k step 2 tk)
+    const uint32_t r0 = static_cast<uint32_t>(tm) * K::TR, kb0 = static_cast<uint32_t>(tk) * K::TC;
+    stage_tile<FILL, true>(src + (static_cast<uint64_t>(r0) * sp + 2 * kb0),
+                           frag + (static_cast<uint64_t>(r0 / 16) * fp + 32 * kb0), mn, k, 0, 0, sp, fp, lds, L, mv, t);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The launch's StepMoves: each step's move (the lane-0 coordinate of the
+// step, lane 0 starting at (0, 0)) as an LDS element offset of the layout.
+template <int KIND>
+StepMoves step_moves(const LdsLayout& L, bool padded) {
+    using K = Kind<KIND>;
+    static_assert(K::WSTEPS <= kMaxSteps && K::RSTEPS <= kMaxSteps && Direct<KIND>::LOADS <= kMaxSteps,
+                  "the step moves fit in StepMoves");
+    StepMoves mv{};
+    auto move = [&](int dr, int dc) {
+        return padded ? static_cast<uint32_t>(dr) * L.ld + static_cast<uint32_t>(dc)
+                      : swizzle(static_cast<uint32_t>(dr * K::TC + dc), L.B, L.M, L.S);
+    };
+    for (int i = 0; i < K::WSTEPS; ++i) {
+        int dr = 0, dc = 0;
+        coord<KIND, true>(0, i, dr, dc);
+        mv.w[i] = move(dr, dc);
+    }
+    for (int i = 0; i < K::RSTEPS; ++i) {
+        int dr = 0, dc = 0;
+        coord<KIND, false>(0, i, dr, dc);
+        mv.r[i] = move(dr, dc);
+    }
+    for (int j = 0; j < Direct<KIND>::LOADS; ++j)
+        mv.d[j] = swizzle(static_cast<uint32_t>(Direct<KIND>::EPL * K::NT * j), L.B, L.M, L.S);
+    return mv;
+}
+
 // Grid limits of a 3-D launch: work-items along x below 2^31, y and z up to
 // 65535 workgroups.
 bool fits_3d(int64_t x, int64_t y, int64_t z, int threads) {
-    return SWZ_GRID3D && x * threads < (int64_t(1) << 31) && y <= 65535 && z <= 65535;
+    return x * threads < (int64_t(1) << 31) && y <= 65535 && z <= 65535;
 }
 
 template <int KIND, int FILL, bool ALIGNED>
@@ -704,23 +804,28 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
     using K = Kind<KIND>;
     const auto* s = static_cast<const uint8_t*>(j.src);
     auto* d = static_cast<uint8_t*>(j.dst);
-    const bool diag = SWZ_TILE_ORDER != 0;
-    const int64_t gx = diag ? tiles_r : tiles_c, gy = diag ? tiles_c : tiles_r;
+    const int64_t gx = tiles_r, gy = tiles_c;  // diagonal order: x = tile row
     // slope of the diagonal order per SWZ_ORDER_* value: 1, 1/2, 0, 3
     static constexpr TileOrder kOrders[4] = {{1u, 0u}, {1u, 1u}, {0u, 0u}, {3u, 0u}};
     const TileOrder O = kOrders[j.order >= 0 && j.order < 4 ? j.order : 0];
+    const StepMoves mv = step_moves<KIND>(j.layout, FILL == kPadded);
+    const FastPath fp = fast_path(j.batch, j.rows, j.cols, K::ESZ, K::TR, K::TC);
+    // 32-bit sizes for the whole-tile path (only read when FastPath allows it)
+    const auto r32 = static_cast<uint32_t>(j.rows), c32 = static_cast<uint32_t>(j.cols);
+    const auto tc32 = static_cast<uint32_t>(tiles_c);
+    const KLayout kl = decode_layout(j.layout);
     if (fits_3d(gx, gy, j.batch, K::NT)) {
         hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, true>),
                            dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(j.batch)),
-                           dim3(K::NT), occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES), stream, s, d, j.rows, j.cols,
-                           tiles_r, tiles_c, int64_t(0), j.layout, O);
+                           dim3(K::NT), occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES), stream, s, d, tc32, O.num, O.sh,
+                           fp.sp, fp.dp, fp.full_r, fp.full_c, r32, c32, j.rows, j.cols, tiles_r, int64_t(0), kl, mv);
         return;
     }
     for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
         const int64_t n = n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid;
         hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, false>), dim3(static_cast<unsigned>(n)), dim3(K::NT),
-                           occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES),
-                           stream, s, d, j.rows, j.cols, tiles_r, tiles_c, t0, j.layout, O);
+                           occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES), stream, s, d, tc32, O.num, O.sh, fp.sp,
+                           fp.dp, fp.full_r, fp.full_c, r32, c32, j.rows, j.cols, tiles_r, t0, kl, mv);
     }
 }
 
@@ -730,6 +835,7 @@ hipError_t launch_kind(const ConvertJob& j, hipStream_t stream) {
     const int64_t tiles_r = ceil_div(j.rows, K::TR), tiles_c = ceil_div(j.cols, K::TC);
     const int64_t n_tiles = j.batch * tiles_r * tiles_c;
     if (n_tiles == 0) return hipSuccess;
+    if (tiles_c > int64_t(UINT32_MAX)) return hipErrorInvalidValue;  // the kernel takes it as 32 bits
     const bool padded = j.layout.ld != static_cast<uint32_t>(K::TC);
     if (padded && j.layout.ld != static_cast<uint32_t>(K::TC + LdsTile<KIND, kPadded>::PAD)) return hipErrorInvalidValue;
     if (j.direct) {
@@ -760,19 +866,25 @@ void launch_stage_fill(const StageJob& j, int64_t tiles_m, int64_t tiles_k, hipS
     using K = Kind<KD>;
     const auto* s = static_cast<const uint8_t*>(j.src);
     auto* f = static_cast<uint8_t*>(j.frag);
-    const bool diag = SWZ_STAGE_ORDER != 0;
-    const int64_t gx = diag ? tiles_m : tiles_k, gy = diag ? tiles_k : tiles_m;
+    const int64_t gx = tiles_k, gy = tiles_m;  // row-major order: x = tile column
+    const StepMoves mv = step_moves<KD>(j.layout, FILL == kPadded);
+    // Whole tiles address rows of 2k bytes and row blocks of fragments of
+    // 32k bytes with 32-bit pitches: both must fit, else every tile takes
+    // the 64-bit edge path.
+    const bool fit = j.mn < (int64_t(1) << 31) && j.k * 32 < (int64_t(1) << 32);
+    const uint32_t sp = fit ? static_cast<uint32_t>(2 * j.k) : 0u, fpitch = fit ? static_cast<uint32_t>(32 * j.k) : 0u;
+    const uint32_t full_m = fit ? static_cast<uint32_t>(j.mn / K::TR) : 0u, full_k = fit ? static_cast<uint32_t>(j.k / K::TC) : 0u;
     if (fits_3d(gx, gy, 1, K::NT)) {
         hipLaunchKernelGGL((k_stage<FILL, true>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy), 1),
-                           dim3(K::NT), occupancy_pad<KD>(LdsTile<KD, FILL>::BYTES), stream, s, f, j.mn, j.k, tiles_m, tiles_k, int64_t(0), j.layout);
+                           dim3(K::NT), occupancy_pad<KD>(LdsTile<KD, FILL>::BYTES), stream, s, f, sp, fpitch, full_m,
+                           full_k, j.mn, j.k, tiles_m, tiles_k, int64_t(0), decode_layout(j.layout), mv);
         return;
     }
     const int64_t n_tiles = tiles_m * tiles_k;
     for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
         const dim3 grid(static_cast<unsigned>(n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid));
         hipLaunchKernelGGL((k_stage<FILL, false>), grid, dim3(K::NT), occupancy_pad<KD>(LdsTile<KD, FILL>::BYTES), stream,
-                           s, f, j.mn, j.k, tiles_m, tiles_k,
-                           t0, j.layout);
+                           s, f, sp, fpitch, full_m, full_k, j.mn, j.k, tiles_m, tiles_k, t0, decode_layout(j.layout), mv);
     }
 }
 

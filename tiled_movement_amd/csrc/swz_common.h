@@ -12,35 +12,6 @@
 
 #include "swz.h"
 
-// Threads per tile of each kernel (tuning knobs; 64 = one wave per tile).
-#ifndef SWZ_NT_SCALAR
-#define SWZ_NT_SCALAR 256
-#endif
-#ifndef SWZ_NT_B64
-#define SWZ_NT_B64 128
-#endif
-#ifndef SWZ_NT_B128
-#define SWZ_NT_B128 128
-#endif
-#ifndef SWZ_NT_STAGE
-#define SWZ_NT_STAGE 256
-#endif
-#ifndef SWZ_NT_TR16
-#define SWZ_NT_TR16 256
-#endif
-#ifndef SWZ_NT_TR8
-#define SWZ_NT_TR8 256
-#endif
-#ifndef SWZ_NT_NARROW
-#define SWZ_NT_NARROW 256
-#endif
-#ifndef SWZ_NT_HNARROW
-#define SWZ_NT_HNARROW 256
-#endif
-#ifndef SWZ_NT_BNARROW  // 0: by row width (64 lanes up to 4 columns, 128 at 8, 256 above)
-#define SWZ_NT_BNARROW 0
-#endif
-
 namespace swz {
 
 // Swizzle<B,M,S> of a 32-bit element offset: the B-bit field at bit M+S is
@@ -88,7 +59,7 @@ template <int KIND> struct Kind;
 // 4-byte column reads (step i = 4j + e reads row 4(u%8)+e), and writes them
 // as one 16-byte piece of output row u/8.
 template <> struct Kind<SWZ_READ_SCALAR_COL> {
-    static constexpr int ESZ = 4, TR = 32, TC = 32, NT = SWZ_NT_SCALAR;
+    static constexpr int ESZ = 4, TR = 32, TC = 32, NT = 256;
     static constexpr int VEC = 4;                     // LDS store width (bytes)
     static constexpr int RWIDTH = 4;                  // LDS load width (bytes)
     static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;  // 16-byte global loads per thread
@@ -112,7 +83,7 @@ template <> struct Kind<SWZ_READ_SCALAR_COL> {
 // u = t + NT*j owns row block k = u%8 (rows 8k..8k+7) and column group
 // g = u/8 (columns 4g..4g+3); step 8j + s reads the 8 bytes of row 8k+s.
 template <> struct Kind<SWZ_READ_B64_4X4> {
-    static constexpr int ESZ = 2, TR = 64, TC = 64, NT = SWZ_NT_B64;
+    static constexpr int ESZ = 2, TR = 64, TC = 64, NT = 128;
     static constexpr int VEC = 16;
     static constexpr int RWIDTH = 8;
     static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
@@ -135,7 +106,7 @@ template <> struct Kind<SWZ_READ_B64_4X4> {
 // is row v/16, chunk v%16.  Read: task u owns row block rb = u%8 and 16-byte
 // chunk ch = u/8; step 8j + s reads chunk ch of row 8rb+s.
 template <> struct Kind<SWZ_READ_B128_8X8> {
-    static constexpr int ESZ = 2, TR = 64, TC = 128, NT = SWZ_NT_B128;
+    static constexpr int ESZ = 2, TR = 64, TC = 128, NT = 128;
     static constexpr int VEC = 16;
     static constexpr int RWIDTH = 16;
     static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
@@ -160,7 +131,7 @@ template <> struct Kind<SWZ_READ_B128_8X8> {
 // steps); wave w reads fragments f = w + (NT/64)*i; lane l of fragment f
 // reads row 16*(f%16) + l%16, k = 32*(f/16) + 8*(l/16) .. +7.
 template <> struct Kind<SWZ_READ_MFMA_16X16X32> {
-    static constexpr int ESZ = 2, TR = 256, TC = 64, NT = SWZ_NT_STAGE;
+    static constexpr int ESZ = 2, TR = 256, TC = 64, NT = 256;
     static constexpr int VEC = 16;
     static constexpr int RWIDTH = 16;
     static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
@@ -197,7 +168,7 @@ template <> struct Kind<SWZ_READ_MFMA_16X16X32> {
 // 128-byte rows).  The swapped order puts the two groups of one LDS phase
 // on different row bit 2, which the swizzle can turn into different banks.
 template <> struct Kind<SWZ_READ_B64_TR16> {
-    static constexpr int ESZ = 2, TR = 64, TC = 64, NT = SWZ_NT_TR16;
+    static constexpr int ESZ = 2, TR = 64, TC = 64, NT = 256;
     static constexpr int VEC = 16;
     static constexpr int RWIDTH = 8;
     static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
@@ -237,7 +208,7 @@ template <> struct Kind<SWZ_READ_B64_TR16> {
 // five low bits, which a 4-bit swizzle field over 8-byte chunks (source: row
 // bits 1-4) spreads over all 64 banks.
 template <> struct Kind<SWZ_READ_B64_TR8> {
-    static constexpr int ESZ = 1, TR = 128, TC = 128, NT = SWZ_NT_TR8;
+    static constexpr int ESZ = 1, TR = 128, TC = 128, NT = 256;
     static constexpr int VEC = 8;
     static constexpr int RWIDTH = 8;
     static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
@@ -299,9 +270,7 @@ struct NarrowKind {
     // Lanes per tile.  Byte rows: a sweep of 64, 128 and 256 lanes on 64 MiB
     // matrices put the best at 64 up to 4 columns (+2-4%), 128 at 8 (+8%)
     // and 256 from 16 columns on.
-    static constexpr int NT = E == 4   ? SWZ_NT_NARROW
-                              : E == 2 ? SWZ_NT_HNARROW
-                              : SWZ_NT_BNARROW ? SWZ_NT_BNARROW
+    static constexpr int NT = E != 1   ? 256
                               : C <= 4 ? 64
                               : C == 8 ? 128
                                        : 256;
@@ -532,6 +501,20 @@ struct Direct {
     static constexpr int VB = K::ESZ == 2 && K::VEC == 16 ? 16 : 4;
     static constexpr int EPL = VB / K::ESZ;          // elements per lane per load
     static constexpr int LOADS = K::TR * K::TC / EPL / K::NT;
+};
+
+// The wave-uniform part of every LDS access of a tile kernel, in element
+// units, computed on the host once per launch (step_moves): step i of a lane
+// is at base ^ w[i] / r[i] for swizzled and plain rows (the moved bits never
+// overlap the lane's own, and the swizzle is linear over GF(2)) and at
+// base + w[i] / r[i] for padded rows; direct load j fills the slots of lane
+// base ^ d[j].  Kernels get them as an argument, so no wave re-derives
+// swizzle(move) from run-time (B, M, S).
+constexpr int kMaxSteps = 16;
+struct StepMoves {
+    uint32_t w[kMaxSteps];  // LDS stores
+    uint32_t r[kMaxSteps];  // LDS loads
+    uint32_t d[kMaxSteps];  // direct HBM -> LDS loads
 };
 
 template <int KIND>
