@@ -18,6 +18,7 @@
 // diagonal order (consecutive tiles differ in both tile row and tile
 // column), and global loads and stores are non-temporal: every byte is read
 // once and written once.
+#include <tuple>
 #include <type_traits>
 
 #include "launch.h"
@@ -603,40 +604,47 @@ __device__ __forceinline__ void convert_tile(const TileIo<EDGE, Kind<KIND>::ESZ>
     lds_read_store<KIND, PADDED, EDGE>(lds, rbase, L, mv, io, t);
 }
 
-// Which tile this workgroup moves.  GRID3D: blockIdx = (tile row, tile
-// column step, batch entry), the diagonal order needing one 32-bit modulo;
-// otherwise a 1-D chunk of the linear tile order (grids beyond the
-// hardware's y / z limits).
-template <bool DIAGONAL, bool GRID3D>
-__device__ __forceinline__ void my_tile(int64_t tiles_r, int64_t tiles_c, int64_t tile0, TileOrder O, int64_t& b,
-                                        int64_t& tr, int64_t& tc) {
-    if (GRID3D) {
-        b = blockIdx.z;
-        if (DIAGONAL) {
-            // tc = (y + f) mod n with y < n: one conditional subtract, and a
-            // division only when the shift f reaches n (a uniform branch,
-            // laid out of line: the whole path runs without a taken branch)
-            const uint32_t n = static_cast<uint32_t>(tiles_c);
-            uint32_t f = (blockIdx.x * O.num) >> O.sh;
-            if (__builtin_expect(f >= n, 0)) f %= n;
-            uint32_t c = blockIdx.y + f;
-            if (c >= n) c -= n;
-            tr = blockIdx.x;
-            tc = static_cast<int64_t>(c);
-        } else {
-            tc = blockIdx.x;
-            tr = blockIdx.y;
-        }
+// Which tiles a launch covers and how blockIdx names them.
+//   kInterior: a 3-D grid (tile row, tile column step, batch entry) over the
+//              whole tiles only, in diagonal order; no edge test at all.
+//   kEdge:     a 1-D chunk of the edge tiles (the last tile column and the
+//              last tile row of each batch entry, where they stick out).
+//   kAll3D / kAll1D: every tile, 3-D as kInterior or a 1-D chunk of the
+//              linear tile order (grids beyond the hardware's y / z limits,
+//              sizes past the 32-bit whole-tile path, unaligned pitches).
+enum Grid { kAll3D = 0, kAll1D = 1, kInterior = 2, kEdge = 3 };
+
+// Tile (tr, tc) of a 3-D diagonal-order grid with n tile columns: tc = (y +
+// f) mod n, f = (x num) >> sh, y < n.  One conditional subtract, and a
+// division only when f reaches n (a uniform branch laid out of line).
+__device__ __forceinline__ uint32_t diagonal_column(uint32_t n, TileOrder O) {
+    uint32_t f = (blockIdx.x * O.num) >> O.sh;
+    if (__builtin_expect(f >= n, 0)) f %= n;
+    const uint32_t c = blockIdx.y + f;
+    return c >= n ? c - n : c;
+}
+
+// Edge tile e (of one batch entry) of a matrix with full_r x full_c whole
+// tiles and tiles_r x tiles_c tiles in all: first the last tile column next
+// to the whole tile rows, then the whole last tile row.
+__device__ __forceinline__ void edge_tile(int64_t e, int64_t full_r, int64_t full_c, int64_t tiles_r,
+                                          int64_t tiles_c, int64_t& tr, int64_t& tc) {
+    const int64_t right = tiles_c > full_c ? full_r : 0;
+    if (e < right) {
+        tr = e;
+        tc = full_c;
     } else {
-        decode_tile<DIAGONAL>(tile0 + blockIdx.x, tiles_r, tiles_c, O, b, tr, tc);
+        tr = full_r;
+        tc = e - right;
     }
+    (void)tiles_r;
 }
 
 // Arguments in the order the kernel needs them: the first thirteen dwords
 // (pointers, tile columns, tile order, the host's FastPath, 32-bit sizes;
 // plain scalars, which is what the build's kernel-argument preload puts in
 // SGPRs) are all a whole tile of a 3-D launch reads before its first load.
-template <int KIND, int FILL, bool ALIGNED, bool GRID3D>
+template <int KIND, int FILL, bool ALIGNED, int GRID>
 __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                             uint32_t tiles_c32, uint32_t order_num, uint32_t order_sh,
                                                             uint32_t sp, uint32_t dp, uint32_t full_r, uint32_t full_c,
@@ -646,34 +654,56 @@ __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __res
     using K = Kind<KIND>;
     constexpr int E = K::ESZ;
     static_assert(FILL != kDirect || ALIGNED, "the direct fill needs 16-byte aligned rows");
+    static_assert(ALIGNED || GRID == kAll3D || GRID == kAll1D, "unaligned pitches take the element-wise path");
     __shared__ u32x4 lds_v[(LdsTile<KIND, FILL>::BYTES + 15) / 16];
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
     const int t = threadIdx.x;
+    const TileOrder O{order_num, order_sh};
 
-    int64_t b, tr, tc;
-    my_tile<true, GRID3D>(tiles_r, tiles_c32, tile0, TileOrder{order_num, order_sh}, b, tr, tc);
-    if constexpr (ALIGNED) {
-        // Edge tiles branch away; whole tiles fall through.
-        if (__builtin_expect(tr >= full_r || tc >= full_c, 0)) {
-            const int64_t plane = rows * cols * E;  // batch entry b
-            convert_tile<KIND, FILL, kVec>(
-                TileIo<kVec, E>{src + b * plane, dst + b * plane, rows, cols, tr * K::TR, tc * K::TC, 0u, 0u}, lds, L,
-                mv, t);
-            return;
-        }
-        // Batch entry b's rows follow entry b - 1's in both matrices, so a
-        // whole tile is (b rows + r0, c0) of the source and (b cols + c0,
-        // r0) of the output, in 32 bits (the host's FastPath says so).
-        const uint32_t b32 = static_cast<uint32_t>(b);
-        const uint32_t r0 = static_cast<uint32_t>(tr) * K::TR, c0 = static_cast<uint32_t>(tc) * K::TC;
+    // A whole tile: batch entry b's rows follow entry b - 1's in both
+    // matrices, so the tile is (b rows + r0, c0) of the source and (b cols +
+    // c0, r0) of the output, in 32 bits (the host's FastPath says so).
+    auto whole = [&](uint32_t b32, uint32_t tr32, uint32_t tc32) {
+        const uint32_t r0 = tr32 * K::TR, c0 = tc32 * K::TC;
         const TileIo<kFull, E> io{src + (static_cast<uint64_t>(b32 * rows32 + r0) * sp + c0 * E),
                                   dst + (static_cast<uint64_t>(b32 * cols32 + c0) * dp + r0 * E), 0, 0, 0, 0, sp, dp};
         convert_tile<KIND, FILL, kFull>(io, lds, L, mv, t);
-    } else {
+    };
+    // Any tile, with 64-bit indexing and the guards of EDGE.
+    auto guarded = [&](int64_t b, int64_t tr, int64_t tc) {
         const int64_t plane = rows * cols * E;
-        convert_tile<KIND, FILL, kElem>(
-            TileIo<kElem, E>{src + b * plane, dst + b * plane, rows, cols, tr * K::TR, tc * K::TC, 0u, 0u}, lds, L, mv,
+        constexpr int EDGE = ALIGNED ? kVec : kElem;
+        convert_tile<KIND, FILL, EDGE>(
+            TileIo<EDGE, E>{src + b * plane, dst + b * plane, rows, cols, tr * K::TR, tc * K::TC, 0u, 0u}, lds, L, mv,
             t);
+    };
+
+    if constexpr (GRID == kInterior) {
+        whole(blockIdx.z, blockIdx.x, diagonal_column(tiles_c32, O));
+    } else if constexpr (GRID == kEdge) {
+        const int64_t tiles_c = (cols + K::TC - 1) / K::TC;
+        const int64_t per = (tiles_c > full_c ? int64_t(full_r) : 0) + (tiles_r > full_r ? tiles_c : 0);
+        const int64_t idx = tile0 + blockIdx.x;
+        const int64_t b = idx / per;
+        int64_t tr, tc;
+        edge_tile(idx - b * per, full_r, full_c, tiles_r, tiles_c, tr, tc);
+        guarded(b, tr, tc);
+    } else {
+        int64_t b, tr, tc;
+        if constexpr (GRID == kAll3D) {
+            b = blockIdx.z;
+            tr = blockIdx.x;
+            tc = diagonal_column(tiles_c32, O);
+        } else {
+            decode_tile<true>(tile0 + blockIdx.x, tiles_r, tiles_c32, O, b, tr, tc);
+        }
+        if constexpr (ALIGNED) {
+            if (tr < full_r && tc < full_c) {
+                whole(static_cast<uint32_t>(b), static_cast<uint32_t>(tr), static_cast<uint32_t>(tc));
+                return;
+            }
+        }
+        guarded(b, tr, tc);
     }
 }
 
@@ -737,7 +767,9 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint
 }
 
 // Arguments as for k_convert: what a whole tile of a 3-D launch reads first.
-template <int FILL, bool GRID3D>
+// Grids as for k_convert (kInterior: x = k tile, y = row tile, row-major,
+// which keeps both the reads and the fragment writes contiguous; kEdge; kAll1D).
+template <int FILL, int GRID>
 __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(const uint8_t* __restrict__ src,
                                                                             uint8_t* __restrict__ frag, uint32_t sp,
                                                                             uint32_t fp, uint32_t full_m,
@@ -750,18 +782,30 @@ __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(cons
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
     const int t = threadIdx.x;
 
-    int64_t b, tm, tk;
-    my_tile<false, GRID3D>(tiles_m, tiles_k, tile0, TileOrder{1u, 0u}, b, tm, tk);
-    // Edge tiles branch away; whole tiles fall through.
-    if (__builtin_expect(tm >= full_m || tk >= full_k, 0)) {
-        stage_tile<FILL, false>(src, frag, mn, k, tm * K::TR, tk * K::TC, 0u, 0u, lds, L, mv, t);
-        return;
-    }
     // the tile's first element (row 256 tm, k 64 tk) and first fragment (row
     // block 16 tm, k step 2 tk)
-    const uint32_t r0 = static_cast<uint32_t>(tm) * K::TR, kb0 = static_cast<uint32_t>(tk) * K::TC;
-    stage_tile<FILL, true>(src + (static_cast<uint64_t>(r0) * sp + 2 * kb0),
-                           frag + (static_cast<uint64_t>(r0 / 16) * fp + 32 * kb0), mn, k, 0, 0, sp, fp, lds, L, mv, t);
+    auto whole = [&](uint32_t tm, uint32_t tk) {
+        const uint32_t r0 = tm * K::TR, kb0 = tk * K::TC;
+        stage_tile<FILL, true>(src + (static_cast<uint64_t>(r0) * sp + 2 * kb0),
+                               frag + (static_cast<uint64_t>(r0 / 16) * fp + 32 * kb0), mn, k, 0, 0, sp, fp, lds, L,
+                               mv, t);
+    };
+    auto guarded = [&](int64_t tm, int64_t tk) {
+        stage_tile<FILL, false>(src, frag, mn, k, tm * K::TR, tk * K::TC, 0u, 0u, lds, L, mv, t);
+    };
+    if constexpr (GRID == kInterior) {
+        whole(blockIdx.y, blockIdx.x);
+    } else if constexpr (GRID == kEdge) {
+        int64_t tm, tk;
+        edge_tile(tile0 + blockIdx.x, full_m, full_k, tiles_m, tiles_k, tm, tk);
+        guarded(tm, tk);
+    } else {
+        const int64_t idx = tile0 + blockIdx.x, tm = idx / tiles_k, tk = idx - tm * tiles_k;
+        if (tm < full_m && tk < full_k)
+            whole(static_cast<uint32_t>(tm), static_cast<uint32_t>(tk));
+        else
+            guarded(tm, tk);
+    }
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -799,12 +843,17 @@ bool fits_3d(int64_t x, int64_t y, int64_t z, int threads) {
     return x * threads < (int64_t(1) << 31) && y <= 65535 && z <= 65535;
 }
 
+// A 1-D launch of n tiles in chunks of at most kMaxGrid workgroups.
+template <typename F>
+void launch_chunks(int64_t n, F launch) {
+    for (int64_t t0 = 0; t0 < n; t0 += kMaxGrid) launch(t0, n - t0 < kMaxGrid ? n - t0 : kMaxGrid);
+}
+
 template <int KIND, int FILL, bool ALIGNED>
 void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64_t n_tiles, hipStream_t stream) {
     using K = Kind<KIND>;
     const auto* s = static_cast<const uint8_t*>(j.src);
     auto* d = static_cast<uint8_t*>(j.dst);
-    const int64_t gx = tiles_r, gy = tiles_c;  // diagonal order: x = tile row
     // slope of the diagonal order per SWZ_ORDER_* value: 1, 1/2, 0, 3
     static constexpr TileOrder kOrders[4] = {{1u, 0u}, {1u, 1u}, {0u, 0u}, {3u, 0u}};
     const TileOrder O = kOrders[j.order >= 0 && j.order < 4 ? j.order : 0];
@@ -812,21 +861,47 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
     const FastPath fp = fast_path(j.batch, j.rows, j.cols, K::ESZ, K::TR, K::TC);
     // 32-bit sizes for the whole-tile path (only read when FastPath allows it)
     const auto r32 = static_cast<uint32_t>(j.rows), c32 = static_cast<uint32_t>(j.cols);
-    const auto tc32 = static_cast<uint32_t>(tiles_c);
     const KLayout kl = decode_layout(j.layout);
-    if (fits_3d(gx, gy, j.batch, K::NT)) {
-        hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, true>),
-                           dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(j.batch)),
-                           dim3(K::NT), occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES), stream, s, d, tc32, O.num, O.sh,
-                           fp.sp, fp.dp, fp.full_r, fp.full_c, r32, c32, j.rows, j.cols, tiles_r, int64_t(0), kl, mv);
-        return;
+    const unsigned lds_pad = occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES);
+    const dim3 block(K::NT);
+    auto args = [&](uint32_t cols_of_order, int64_t tile0) {
+        return std::make_tuple(s, d, cols_of_order, O.num, O.sh, fp.sp, fp.dp, fp.full_r, fp.full_c, r32, c32, j.rows,
+                               j.cols, tiles_r, tile0, kl, mv);
+    };
+    if constexpr (ALIGNED) {
+        if (fp.full_r > 0 && fp.full_c > 0 && fits_3d(fp.full_r, fp.full_c, j.batch, K::NT)) {
+            // the whole tiles, then (if any) the edge strips
+            std::apply([&](auto... a) {
+                hipLaunchKernelGGL((k_convert<KIND, FILL, true, kInterior>),
+                                   dim3(fp.full_r, fp.full_c, static_cast<unsigned>(j.batch)), block, lds_pad, stream,
+                                   a...);
+            }, args(fp.full_c, 0));
+            const int64_t per = (tiles_c > fp.full_c ? int64_t(fp.full_r) : 0) + (tiles_r > fp.full_r ? tiles_c : 0);
+            launch_chunks(j.batch * per, [&](int64_t t0, int64_t n) {
+                std::apply([&](auto... a) {
+                    hipLaunchKernelGGL((k_convert<KIND, FILL, true, kEdge>), dim3(static_cast<unsigned>(n)), block,
+                                       lds_pad, stream, a...);
+                }, args(static_cast<uint32_t>(tiles_c), t0));
+            });
+            return;
+        }
+    } else {
+        if (fits_3d(tiles_r, tiles_c, j.batch, K::NT)) {
+            std::apply([&](auto... a) {
+                hipLaunchKernelGGL((k_convert<KIND, FILL, false, kAll3D>),
+                                   dim3(static_cast<unsigned>(tiles_r), static_cast<unsigned>(tiles_c),
+                                        static_cast<unsigned>(j.batch)),
+                                   block, lds_pad, stream, a...);
+            }, args(static_cast<uint32_t>(tiles_c), 0));
+            return;
+        }
     }
-    for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
-        const int64_t n = n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid;
-        hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, false>), dim3(static_cast<unsigned>(n)), dim3(K::NT),
-                           occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES), stream, s, d, tc32, O.num, O.sh, fp.sp,
-                           fp.dp, fp.full_r, fp.full_c, r32, c32, j.rows, j.cols, tiles_r, t0, kl, mv);
-    }
+    launch_chunks(n_tiles, [&](int64_t t0, int64_t n) {
+        std::apply([&](auto... a) {
+            hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, kAll1D>), dim3(static_cast<unsigned>(n)), block, lds_pad,
+                               stream, a...);
+        }, args(static_cast<uint32_t>(tiles_c), t0));
+    });
 }
 
 template <int KIND>
@@ -866,26 +941,30 @@ void launch_stage_fill(const StageJob& j, int64_t tiles_m, int64_t tiles_k, hipS
     using K = Kind<KD>;
     const auto* s = static_cast<const uint8_t*>(j.src);
     auto* f = static_cast<uint8_t*>(j.frag);
-    const int64_t gx = tiles_k, gy = tiles_m;  // row-major order: x = tile column
     const StepMoves mv = step_moves<KD>(j.layout, FILL == kPadded);
+    const KLayout kl = decode_layout(j.layout);
     // Whole tiles address rows of 2k bytes and row blocks of fragments of
     // 32k bytes with 32-bit pitches: both must fit, else every tile takes
     // the 64-bit edge path.
     const bool fit = j.mn < (int64_t(1) << 31) && j.k * 32 < (int64_t(1) << 32);
     const uint32_t sp = fit ? static_cast<uint32_t>(2 * j.k) : 0u, fpitch = fit ? static_cast<uint32_t>(32 * j.k) : 0u;
     const uint32_t full_m = fit ? static_cast<uint32_t>(j.mn / K::TR) : 0u, full_k = fit ? static_cast<uint32_t>(j.k / K::TC) : 0u;
-    if (fits_3d(gx, gy, 1, K::NT)) {
-        hipLaunchKernelGGL((k_stage<FILL, true>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy), 1),
-                           dim3(K::NT), occupancy_pad<KD>(LdsTile<KD, FILL>::BYTES), stream, s, f, sp, fpitch, full_m,
-                           full_k, j.mn, j.k, tiles_m, tiles_k, int64_t(0), decode_layout(j.layout), mv);
+    const unsigned lds_pad = occupancy_pad<KD>(LdsTile<KD, FILL>::BYTES);
+    const dim3 block(K::NT);
+    if (full_m > 0 && full_k > 0 && fits_3d(full_k, full_m, 1, K::NT)) {
+        hipLaunchKernelGGL((k_stage<FILL, kInterior>), dim3(full_k, full_m, 1), block, lds_pad, stream, s, f, sp, fpitch,
+                           full_m, full_k, j.mn, j.k, tiles_m, tiles_k, int64_t(0), kl, mv);
+        const int64_t edges = (tiles_k > full_k ? int64_t(full_m) : 0) + (tiles_m > full_m ? tiles_k : 0);
+        launch_chunks(edges, [&](int64_t t0, int64_t n) {
+            hipLaunchKernelGGL((k_stage<FILL, kEdge>), dim3(static_cast<unsigned>(n)), block, lds_pad, stream, s, f, sp,
+                               fpitch, full_m, full_k, j.mn, j.k, tiles_m, tiles_k, t0, kl, mv);
+        });
         return;
     }
-    const int64_t n_tiles = tiles_m * tiles_k;
-    for (int64_t t0 = 0; t0 < n_tiles; t0 += kMaxGrid) {
-        const dim3 grid(static_cast<unsigned>(n_tiles - t0 < kMaxGrid ? n_tiles - t0 : kMaxGrid));
-        hipLaunchKernelGGL((k_stage<FILL, false>), grid, dim3(K::NT), occupancy_pad<KD>(LdsTile<KD, FILL>::BYTES), stream,
-                           s, f, sp, fpitch, full_m, full_k, j.mn, j.k, tiles_m, tiles_k, t0, decode_layout(j.layout), mv);
-    }
+    launch_chunks(tiles_m * tiles_k, [&](int64_t t0, int64_t n) {
+        hipLaunchKernelGGL((k_stage<FILL, kAll1D>), dim3(static_cast<unsigned>(n)), block, lds_pad, stream, s, f, sp,
+                           fpitch, full_m, full_k, j.mn, j.k, tiles_m, tiles_k, t0, kl, mv);
+    });
 }
 
 }  // namespace
