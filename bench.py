@@ -9,8 +9,12 @@ traffic reaches HBM.
 
 Prints ONE JSON line.  Extra fields: the other workloads and layouts
 (swizzle / pad / plain / direct), the library's reference copy of the same
-bytes (the practical read-once / write-once ceiling), the runtime's own
-device copy, and the CPU oracle as a reported baseline.
+bytes (the practical read-once / write-once ceiling; it copies the
+workloads' own random bytes, since an all-zero buffer copies about 4%
+faster), the runtime's own device copy, the LDS bank-conflict counters of
+the kernels (from a record taken with rocprofv3 on the current kernel
+sources), and the CPU oracle timed on every workload as a reported
+baseline, each checked bit for bit against the GPU result.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
@@ -19,8 +23,17 @@ Usage:
       exactly P buffer pairs; NAME is one of
       fp32_transpose, fp16_transpose, fp16_transpose_tr, u8_transpose, bf16_convert,
       bf16_stage, fp32_narrow8, fp16_narrow8, u8_narrow16, fp32_transpose_long, map, map_batch, copy,
-      copy_128, memcpy_d2d,
+      copy_128, copy_zero, memcpy_d2d,
       bf16_gemm, bf16_gemm_fused, bf16_gemm_fused_bf16c, torch_mm_bf16
+  python bench.py --tile-orders [--elem-bytes 4 2] [--mib 64]
+      time every tile order of the transposes on matrices of one size and
+      several shapes, and what swz_tune_tile_order picks for each (a table on
+      stdout instead of the JSON line)
+
+Timing: warm-up steps, then a short spin kernel on the launch stream before
+the start event, so the host has queued the first launches by the time the
+timed region starts (without it the first steps of a short run wait for the
+host); the region between the two HIP events holds exactly the timed steps.
 """
 
 from __future__ import annotations
@@ -59,13 +72,15 @@ WORKLOADS = {
     "bf16_gemm_fused": "C[8192x8192] fp32 = A * B^T, A[8192x4096] row-major and B[4096x8192] column-major staged through swizzled 256x64 LDS tiles inside the GEMM (16x16x32 bf16 MFMA)",
     "bf16_gemm_fused_bf16c": "the same fused GEMM with C written as bf16 (rounded to nearest even), like the runtime library GEMM below",
     "torch_mm_bf16": "runtime library GEMM (torch.mm, bf16 in and out) of the same 8192x8192x4096 product, for context",
-    "copy": "reference 16-byte vector copy of 64 MiB (read once, write once)",
-    "copy_128": "reference 16-byte vector copy of 128 MiB (the byte count of the 256 MiB workloads)",
+    "copy": "reference 16-byte vector copy of 64 MiB (read once, write once) of the fp32 workload's random input",
+    "copy_128": "reference 16-byte vector copy of 128 MiB (the byte count of the 256 MiB workloads) of the fp16 workload's random input",
+    "copy_zero": "the same copy of 64 MiB of zeros (for context: zeros copy faster)",
     "memcpy_d2d": "runtime device-to-device copy (hipMemcpyAsync through torch) of 64 MiB, for context",
 }
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CONFLICT_FILE = os.path.join(ROOT, "profiles", "lds_conflicts.json")
 KERNEL_SOURCES = ("kernels_tile.hip", "kernels_copy.hip", "swz_common.h")
 
 
@@ -86,15 +101,40 @@ def measured_traffic(name):
     """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, each
     scaled by the same counter's reading for the reference copy; None when
     no such record exists or the kernels changed since it was taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            data = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if data.get("kernel_sources_sha256") != kernel_sources_digest():
+    data = _current_record(TRAFFIC_FILE)
+    if data is None:
         return None
     rec = data.get("workloads", {}).get(name)
     return None if rec is None else rec.get("bytes_per_launch")
+
+
+def _current_record(path):
+    """The record in `path` if it was taken on the kernel sources as they are
+    now (same digest), else None."""
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return data if data.get("kernel_sources_sha256") == kernel_sources_digest() else None
+
+
+def measured_conflicts(name):
+    """LDS bank-conflict counters per layout of one workload, from rocprofv3
+    runs (SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_INSTS_LDS per dispatch),
+    as conflict cycles per tile and per LDS instruction; None when no record
+    exists for the workload or the kernels changed since it was taken."""
+    data = _current_record(CONFLICT_FILE)
+    rec = None if data is None else data.get("workloads", {}).get(name)
+    if not rec:
+        return None
+    out = {}
+    for layout, r in rec.items():
+        out[layout] = {"conflict_cycles_per_tile": r["conflict_cycles_per_tile"],
+                       "conflict_cycles_per_lds_instr": r["conflict_cycles_per_lds_instr"],
+                       "SQ_LDS_BANK_CONFLICT": r["SQ_LDS_BANK_CONFLICT"],
+                       "SQ_LDS_IDX_ACTIVE": r["SQ_LDS_IDX_ACTIVE"], "SQ_INSTS_LDS": r["SQ_INSTS_LDS"]}
+    return out
 
 
 PAIRS_OVERRIDE = None  # --pairs: rotate over exactly this many buffer pairs
@@ -106,9 +146,14 @@ def n_pairs(bytes_per_pair):
     return max(2, -(-CACHE_DEFEAT_BYTES // bytes_per_pair))
 
 
+PREFILL_CYCLES = 1_000_000  # spin before the start event: about 0.5 ms at the shader clock
+
+
 def time_steps(step, steps, warmup):
     """Run warmup steps, then time exactly `steps` steps with HIP events on
-    the current stream (the stream the kernels are launched on)."""
+    the current stream (the stream the kernels are launched on).  A spin
+    kernel ahead of the start event keeps the GPU busy while the host queues
+    the first steps, so the timed region is the steps' own run time."""
     import torch
 
     for i in range(warmup):
@@ -116,6 +161,7 @@ def time_steps(step, steps, warmup):
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    torch.cuda._sleep(PREFILL_CYCLES)
     start.record()
     for i in range(steps):
         step(warmup + i)
@@ -232,6 +278,7 @@ def build(ctx, name, layout):
                      "threads": pl["threads"], "buffer_pairs": k, "launches_per_step": 2,
                      "predicted_conflict_cycles_per_tile": {"write": wc, "read": rc_}})
         info["_keep"] = (sa, sb, fa, fb)
+        info["_io"] = (ao, bo, fa[0], fb[0], step)
         return step, 2 * (ao.nbytes + bo.nbytes), info
 
     if name == "bf16_gemm":
@@ -319,15 +366,22 @@ def build(ctx, name, layout):
                 ctx.check(rc, "swz_map_batch")
 
         info["_keep"] = (x, ys, arr)
+        info["_io"] = (W.map_offsets(65536), triples, ys[0], step)
         info["buffer_pairs"] = k
         # bytes: one read of the offsets per triple (from cache) is not HBM
         # traffic; the algorithmic bytes are the input once and every output
         return step, 4 * 65536 * (1 + len(triples)), info
 
-    if name in ("copy", "copy_128", "memcpy_d2d"):
+    if name in ("copy", "copy_128", "copy_zero", "memcpy_d2d"):
+        # the workloads' own input bytes (64 MiB: the fp32 matrix, 128 MiB:
+        # the fp16 one); copy_zero copies zeros
         nbytes = (128 if name == "copy_128" else 64) * 2**20
         k = n_pairs(2 * nbytes)
-        srcs = [ctx.torch.zeros(nbytes // 4, dtype=ctx.torch.int32, device=ctx.dev) for _ in range(k)]
+        if name == "copy_zero":
+            srcs = [ctx.torch.zeros(nbytes // 4, dtype=ctx.torch.int32, device=ctx.dev) for _ in range(k)]
+        else:
+            a = W.fp16_matrix(8192, 8192, seed=0) if name == "copy_128" else W.fp32_matrix(4096, 4096, seed=0)
+            srcs = [t.view(-1) for t in ctx.copies(a, k)]
         dsts = [ctx.torch.empty_like(s) for s in srcs]
         sp, dp = [t.data_ptr() for t in srcs], [t.data_ptr() for t in dsts]
 
@@ -358,17 +412,64 @@ def host_cpu_model():
     return None
 
 
-def cpu_baseline(a, dst_dev, seconds):
-    """The oracle's transpose of the headline input, timed on the host cores
-    and bounded to about `seconds` in all: the plain C oracle with one thread
-    per host core (at most 16, the machine's CPU share), then with one thread,
-    then the NumPy oracle; also checks the GPU result against it."""
+def _oracle_legs(name, info):
+    """For one workload: the plain C oracle (threads -> result), the NumPy
+    oracle (-> result), the GPU's result of step 0 on the host, the
+    algorithmic bytes of one oracle pass, and what one pass is."""
     import numpy as np
+    import torch
 
     import oracle
     from oracle import c_ref
 
-    got = dst_dev.cpu().numpy().view(np.uint32)
+    if name == "map_batch":
+        x, triples, y_dev, step = info["_io"]
+        step(0)
+        torch.cuda.synchronize()
+        got = y_dev.cpu().numpy()
+
+        def c_leg(threads):
+            from concurrent.futures import ThreadPoolExecutor  # ctypes calls release the GIL
+            with ThreadPoolExecutor(threads) as pool:
+                return np.stack(list(pool.map(lambda p: c_ref.swizzle_map(x, *p), triples)))
+
+        def np_leg():
+            return np.stack([oracle.swizzle_map(x, *p) for p in triples])
+
+        return c_leg, np_leg, got, 4 * x.size * (1 + len(triples)), f"the {len(triples)} triples over {x.size} offsets"
+    if name == "bf16_stage":
+        ao, bo, fa, fb, step = info["_io"]
+        step(0)
+        torch.cuda.synchronize()
+        got = np.concatenate([fa.cpu().numpy().view(np.uint16).ravel(), fb.cpu().numpy().view(np.uint16).ravel()])
+
+        def c_leg(threads):
+            return np.concatenate([c_ref.stage_operand(ao, threads).ravel(), c_ref.stage_operand(bo, threads).ravel()])
+
+        def np_leg():
+            return np.concatenate([oracle.stage_operand(ao).ravel(), oracle.stage_operand(bo).ravel()])
+
+        return c_leg, np_leg, got, 2 * (ao.nbytes + bo.nbytes), "A and B staged into fragments"
+    a, srcs, dsts, step = info["_io"]
+    step(0)  # buffer pair 0 holds the result again
+    torch.cuda.synchronize()
+    got = dsts[0].cpu().numpy().view(a.dtype).reshape(-1)
+    return (lambda threads: c_ref.convert_layout(a, threads).reshape(-1),
+            lambda: (oracle.transpose(a) if a.ndim == 2 else oracle.convert_layout(a)).reshape(-1),
+            got, 2 * a.nbytes, "x".join(str(d) for d in a.shape) + " transposed")
+
+
+def cpu_baseline(name, info, seconds):
+    """The oracle on the host cores, bounded to about `seconds` in all: the
+    plain C oracle with one thread per host core (at most 16, the machine's CPU
+    share), then with one thread, then the NumPy oracle; rates in GB/s of the
+    same algorithmic bytes as the GPU figure; the GPU's result checked bit
+    for bit against both oracles."""
+    import numpy as np
+
+    from oracle import c_ref
+
+    c_leg, np_leg, got, nbytes, what = _oracle_legs(name, info)
     threads = max(1, min(16, os.cpu_count() or 1))
 
     def rate(fn, budget):
@@ -378,24 +479,86 @@ def cpu_baseline(a, dst_dev, seconds):
             out = fn()
             t += time.perf_counter() - t1
             reps += 1
-        return a.nbytes * 2 * reps / t / 1e9, reps, t, out
+        return nbytes * reps / t / 1e9, reps, t, out
 
     c_ref.lib()  # compile outside the timed loop
-    v_n, reps_n, t_n, ref = rate(lambda: c_ref.convert_layout(a, threads), 0.5 * seconds)
-    v_1, reps_1, t_1, _ = rate(lambda: c_ref.convert_layout(a, 1), 0.25 * seconds)
-    v_np, reps_np, t_np, ref_np = rate(lambda: oracle.transpose(a), 0.25 * seconds)
+    v_n, reps_n, t_n, ref = rate(lambda: c_leg(threads), 0.5 * seconds)
+    v_1, _, _, _ = rate(lambda: c_leg(1), 0.25 * seconds)
+    v_np, _, _, ref_np = rate(np_leg, 0.25 * seconds)
+    same = lambda r: r.shape == got.shape and bool(np.array_equal(r.view(got.dtype), got))
     return {
         "value": round(v_n, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{reps_n} full 4096x4096 fp32 transposes by the plain C oracle (scalar loops, gcc -O2, "
+        "sample": f"{reps_n} full passes ({what}) by the plain C oracle (scalar loops, gcc -O2, "
                   f"{threads} threads), {t_n:.1f} s",
         "single_thread_GBps": round(v_1, 3),
         "numpy_oracle_GBps": round(v_np, 3),
         "cpu_model": host_cpu_model(),
-        "matches_gpu": bool(np.array_equal(ref.view(np.uint32), got) and np.array_equal(ref_np.view(np.uint32), got)),
+        "matches_gpu": same(ref) and same(ref_np),
     }
+
+
+def tile_order_sweep(elem_bytes, mib):
+    """Every tile order of the transposes on matrices of `mib` MiB and shapes
+    from 256 rows up to 256 columns: each order pinned (swz_set_tile_order),
+    rotating over four buffer pairs, best of three batches of 100 calls
+    timed with HIP events; then what swz_tune_tile_order picks on one pair.
+    Pins are removed afterwards.  Returns the lines of a table."""
+    import torch
+
+    import tiled_movement_amd as T
+
+    orders = {T.ORDER_DIAGONAL: "diagonal", T.ORDER_HALF_DIAGONAL: "half", T.ORDER_COLUMNS: "columns",
+              T.ORDER_STEEP_DIAGONAL: "steep"}
+    pairs, nbytes = 4, mib << 20
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    srcs = [torch.full((nbytes,), p + 1, dtype=torch.uint8, device=dev) for p in range(pairs)]
+    dsts = [torch.empty((nbytes,), dtype=torch.uint8, device=dev) for _ in range(pairs)]
+    sp, dp = [t.data_ptr() for t in srcs], [t.data_ptr() for t in dsts]
+
+    def rate(rows, cols, esz):
+        def launch(i):
+            rc = T.lib.swz_transpose(sp[i % pairs], dp[i % pairs], rows, cols, esz, T.LAYOUT_SWIZZLE, T.READ_AUTO,
+                                     None, stream.cuda_stream)
+            if rc:
+                raise T.SwzError(rc, "swz_transpose")
+
+        best = 0.0
+        for _ in range(3):
+            ms, _ = time_steps(launch, 100, 10)
+            best = max(best, 2.0 * nbytes * 100 / (ms * 1e-3) / 1e9)
+        return best
+
+    lines = ["| elem bytes | rows x cols | output pitch | " + " | ".join(orders.values()) + " | tuned |",
+             "|---|---|---|" + "---|" * len(orders) + "---|"]
+    for esz in elem_bytes:
+        elems, rows = nbytes // esz, 256
+        while rows <= elems // 256:
+            cols = elems // rows
+            rates = {}
+            for order, oname in orders.items():
+                T.swz_set_tile_order(1, rows, cols, esz, T.READ_AUTO, order)
+                rates[oname] = rate(rows, cols, esz)
+            chosen = T.swz_tune_tile_order(srcs[0], dsts[0], 1, rows, cols, esz, "swizzle", reps=20, stream=stream)
+            T.swz_set_tile_order(1, rows, cols, esz, T.READ_AUTO, -1)
+            lines.append(f"| {esz} | {rows} x {cols} | {rows * esz} B | "
+                         + " | ".join(f"{rates[n]:,.0f}" for n in orders.values()) + f" | {orders[chosen]} |")
+            log(lines[-1])
+            rows *= 2
+    return lines
+
+
+# The reference copy whose launch moves the same bytes as one launch of the
+# workload (staging: one operand per launch).
+COPY_OF = {"fp32_transpose": "copy", "fp16_transpose": "copy_128", "fp16_transpose_tr": "copy_128",
+           "u8_transpose": "copy", "bf16_convert": "copy", "bf16_stage": "copy", "fp32_narrow8": "copy",
+           "fp16_narrow8": "copy", "u8_narrow16": "copy"}
+# Workloads whose oracle is timed beside them in the full run (the headline's
+# own is the line's cpu_baseline).
+ORACLE_TIMED = ("fp16_transpose", "bf16_convert", "bf16_stage", "map_batch")
 
 
 def main(argv=None):
@@ -406,9 +569,13 @@ def main(argv=None):
     ap.add_argument("--quick", action="store_true", help="headline only, no other workloads")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=None)
     ap.add_argument("--layout", choices=["swizzle", "pad", "plain", "direct"], default="swizzle")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="budget of the headline's CPU oracle leg (each other workload's gets a quarter)")
     ap.add_argument("--pairs", type=int, default=None,
                     help="rotate over this many source/destination pairs (default: enough for 512 MiB)")
+    ap.add_argument("--tile-orders", action="store_true", help="sweep the transposes' tile orders instead")
+    ap.add_argument("--elem-bytes", type=int, nargs="+", default=[4, 2], help="--tile-orders: element sizes")
+    ap.add_argument("--mib", type=int, default=64, help="--tile-orders: matrix size in MiB (a power of two)")
     args = ap.parse_args(argv)
     global PAIRS_OVERRIDE
     PAIRS_OVERRIDE = args.pairs
@@ -418,6 +585,9 @@ def main(argv=None):
         return 2
 
     ctx = Ctx()
+    if args.tile_orders:
+        print("\n".join(tile_order_sweep(args.elem_bytes, args.mib)), flush=True)
+        return 0
     name = args.workload or "fp32_transpose"
     layout = args.layout if args.workload else "swizzle"
     step, nbytes, info = build(ctx, name, layout)
@@ -428,14 +598,14 @@ def main(argv=None):
     value = nbytes * args.steps / (ms * 1e-3) / 1e9
     log(f"{name}/{layout}: {value:.1f} GB/s, {ms_per_step * 1e3:.2f} us/step, wall {wall:.3f} s")
 
-    extra = {}
+    extra, oracle_timed = {}, {}
     if not args.quick and args.workload is None:
-        for wname in ("copy", "copy_128", "memcpy_d2d", "fp32_transpose", "fp16_transpose", "fp16_transpose_tr",
-                      "u8_transpose", "bf16_convert", "bf16_stage", "fp32_narrow8", "fp16_narrow8", "u8_narrow16",
-                      "map", "bf16_gemm",
-                      "bf16_gemm_fused", "bf16_gemm_fused_bf16c", "torch_mm_bf16"):
-            for lay in (("swizzle",) if wname in ("copy", "copy_128", "memcpy_d2d", "map", "bf16_gemm", "torch_mm_bf16",
-                                                  "bf16_gemm_fused_bf16c")
+        for wname in ("copy", "copy_128", "copy_zero", "memcpy_d2d", "fp32_transpose", "fp16_transpose",
+                      "fp16_transpose_tr", "u8_transpose", "bf16_convert", "bf16_stage", "fp32_narrow8",
+                      "fp16_narrow8", "u8_narrow16", "map", "bf16_gemm", "bf16_gemm_fused", "bf16_gemm_fused_bf16c",
+                      "torch_mm_bf16"):
+            for lay in (("swizzle",) if wname in ("copy", "copy_128", "copy_zero", "memcpy_d2d", "map", "bf16_gemm",
+                                                  "torch_mm_bf16", "bf16_gemm_fused_bf16c")
                         else ("swizzle", "plain") if wname == "bf16_gemm_fused"
                         else ("swizzle", "pad", "plain", "direct")):
                 s2, nb2, inf2 = build(ctx, wname, lay)
@@ -443,11 +613,14 @@ def main(argv=None):
                     rate, ms2 = median_rate(s2, nb2, steps=250, warmup=25)
                     extra["map/swizzle"] = {"us_per_call": round(ms2 * 1e3, 3)}
                     log(f"map: {ms2 * 1e3:.2f} us/call")
-                    s3, nb3, _ = build(ctx, "map_batch", "swizzle")
+                    s3, nb3, inf3 = build(ctx, "map_batch", "swizzle")
                     rate3, ms3 = median_rate(s3, nb3, steps=100, warmup=10)
                     extra["map/swizzle"].update({"batch_us_per_125_triples": round(ms3 * 1e3, 2),
                                                  "batch_GBps": round(rate3, 1)})
                     log(f"map batch: {ms3 * 1e3:.2f} us per 125 triples, {rate3:.1f} GB/s")
+                    oracle_timed["map_batch"] = cpu_baseline("map_batch", inf3, args.cpu_seconds / 4)
+                    log(f"cpu oracle, map: {oracle_timed['map_batch']['value']} GB/s")
+                    del s3, inf3
                     continue
                 if wname in ("bf16_gemm", "bf16_gemm_fused", "bf16_gemm_fused_bf16c", "torch_mm_bf16"):
                     rate, ms2 = median_rate(s2, nb2, steps=20, warmup=5)
@@ -463,8 +636,19 @@ def main(argv=None):
                 rec = {k: v for k, v in inf2.items() if not k.startswith("_") and k != "workload"}
                 rec.update({"GBps": round(rate, 1), "frac": round(rate / HBM_PEAK_GBS, 4),
                             "us_per_step": round(ms2 * 1e3, 2)})
+                ref = extra.get(f"{COPY_OF.get(wname)}/swizzle")
+                if ref:  # share of the reference copy of the same bytes per launch
+                    rec["frac_of_copy"] = round(rate / ref["GBps"], 4)
+                mc = measured_conflicts(wname)
+                if mc and lay in mc:
+                    rec["measured_conflict_cycles_per_tile"] = mc[lay]["conflict_cycles_per_tile"]
+                    rec["measured_conflict_cycles_per_lds_instr"] = mc[lay]["conflict_cycles_per_lds_instr"]
                 extra[f"{wname}/{lay}"] = rec
                 log(f"{wname}/{lay}: {rate:.1f} GB/s")
+                if lay == "swizzle" and wname in ORACLE_TIMED:
+                    oracle_timed[wname] = cpu_baseline(wname, inf2, args.cpu_seconds / 4)
+                    log(f"cpu oracle, {wname}: {oracle_timed[wname]['value']} GB/s, "
+                        f"GPU output matches: {oracle_timed[wname]['matches_gpu']}")
                 del s2, inf2
                 ctx.torch.cuda.empty_cache()
         # Long output rows: the default tile order, then the one
@@ -495,18 +679,19 @@ def main(argv=None):
             del s2, inf2
             ctx.torch.cuda.empty_cache()
         PAIRS_OVERRIDE = saved
+        extra["cpu_baseline"] = oracle_timed
 
     cpu = None
     if name == "fp32_transpose" and "_io" in info:
-        a, srcs, dsts, st = info["_io"]
-        st(0)  # buffer pair 0 holds the transpose of the input again
-        ctx.torch.cuda.synchronize()
         try:
-            cpu = cpu_baseline(a, dsts[0], args.cpu_seconds)
+            cpu = cpu_baseline(name, info, args.cpu_seconds)
             log(f"cpu oracle: {cpu['value']} GB/s; GPU output matches: {cpu['matches_gpu']}")
         except Exception as e:  # a reported baseline only
             log(f"cpu baseline skipped: {e!r}")
 
+    config = {k: v for k, v in info.items() if not k.startswith("_")}
+    if name in COPY_OF or name in ("map", "map_batch"):
+        config["measured_lds_conflicts"] = measured_conflicts(name)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -518,9 +703,9 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32_transpose": "f32", "fp32_narrow8": "f32", "fp32_transpose_long": "f32", "fp16_narrow8": "f16", "u8_narrow16": "u8", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "map_batch": "int32", "copy": "u8", "copy_128": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
+        "dtype": {"fp32_transpose": "f32", "fp32_narrow8": "f32", "fp32_transpose_long": "f32", "fp16_narrow8": "f16", "u8_narrow16": "u8", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "map_batch": "int32", "copy": "u8", "copy_128": "u8", "copy_zero": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
         "data": "synthetic",
-        "config": {k: v for k, v in info.items() if not k.startswith("_")},
+        "config": config,
         "roofline": {
             "bound": "hbm",
             "achieved": round(value, 1),

@@ -13,8 +13,9 @@ import pytest
 import oracle as O
 import workloads as W
 
-torch = pytest.importorskip("torch")
-T = pytest.importorskip("tiled_movement_amd")
+import torch  # noqa: E402  (hard imports: a GPU run without them fails, never skips)
+
+import tiled_movement_amd as T  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"

@@ -1,9 +1,7 @@
-"""Host checks of the diagnostic tools (no GPU): the LDS microbenchmark's
-pattern families and the tile-order sweep's order table."""
+"""Host checks of the diagnostic tool (no GPU): the LDS microbenchmark's
+pattern families."""
 
-import tiled_movement_amd as T
 from tiled_movement_amd import lds_bankbench as LB
-from tiled_movement_amd import tile_order_sweep as TS
 
 
 def test_subword_patterns_cover_both_widths_and_directions():
@@ -24,8 +22,3 @@ def test_subword_patterns_cover_both_widths_and_directions():
 def test_kernel_patterns_include_the_small_element_narrow_kinds():
     names = {p["name"].split("/")[1] for p in LB.patterns({"kernel"})}
     assert {"hnarrow8", "bnarrow16", "scalar_col", "mfma"} <= names
-
-
-def test_sweep_times_every_tile_order():
-    assert set(TS.ORDERS) == {T.ORDER_DIAGONAL, T.ORDER_HALF_DIAGONAL, T.ORDER_COLUMNS, T.ORDER_STEEP_DIAGONAL}
-    assert TS.BYTES == 64 << 20 and TS.PAIRS == 4

@@ -166,6 +166,30 @@ def _ptr(x) -> Optional[int]:
     return x.data_ptr()
 
 
+def _buf(call: str, **bufs) -> None:
+    """Check the device buffers of one call before it reaches the library:
+    every tensor is a contiguous CUDA tensor, all on one device, and holds at
+    least the bytes the call reads or writes there (name=(tensor, bytes)).
+    Raw integer addresses and None pass unchecked (the library checks what
+    it can: NULL, alignment, overlap).  Raises ValueError."""
+    device = None
+    for name, (t, need) in bufs.items():
+        if t is None or isinstance(t, int):
+            continue
+        if not getattr(t, "is_cuda", False):
+            raise ValueError(f"{call}: {name} must be a CUDA tensor (got {type(t).__name__} on "
+                             f"{getattr(t, 'device', 'the host')})")
+        if not t.is_contiguous():
+            raise ValueError(f"{call}: {name} must be contiguous (a strided view is not its own bytes)")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{call}: {name} is on {t.device}, the other buffers on {device}")
+        have = t.numel() * t.element_size()
+        if have < max(int(need), 0):
+            raise ValueError(f"{call}: {name} holds {have} bytes, the call needs {int(need)}")
+
+
 def _stream(stream, *tensors):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -192,6 +216,7 @@ def _layout(layout) -> int:
 
 def swz_map(inp, out, n: int, params, stream=None) -> None:
     B, M, S = params
+    _buf("swz_map", inp=(inp, 4 * n), out=(out, 4 * n))
     _check(lib.swz_map(_ptr(inp), _ptr(out), n, Params(B, M, S), _stream(stream, inp, out)), "swz_map")
 
 
@@ -211,6 +236,8 @@ def swz_tune_tile_order(src, dst, batch: int, rows: int, cols: int, elem_bytes: 
                         read_kind: int = READ_AUTO, params=None, reps: int = 10, stream=None) -> int:
     """Time every tile order on this conversion, pin the fastest and return it."""
     chosen = ctypes.c_int32(-1)
+    nbytes = batch * rows * cols * elem_bytes
+    _buf("swz_tune_tile_order", src=(src, nbytes), dst=(dst, nbytes))
     _check(lib.swz_tune_tile_order(_ptr(src), _ptr(dst), batch, rows, cols, elem_bytes, _layout(layout), read_kind,
                                    _params(params), reps, ctypes.byref(chosen), _stream(stream, src, dst)),
            "swz_tune_tile_order")
@@ -220,41 +247,49 @@ def swz_tune_tile_order(src, dst, batch: int, rows: int, cols: int, elem_bytes: 
 def swz_map_batch(inp, out, n: int, params_list, stream=None) -> None:
     """out[j][i] = Swizzle(params_list[j])(inp[i]); out holds len(params_list) rows of n."""
     arr = (Params * max(len(params_list), 1))(*[Params(*p) for p in params_list])
+    _buf("swz_map_batch", inp=(inp, 4 * n), out=(out, 4 * n * len(params_list)))
     _check(lib.swz_map_batch(_ptr(inp), _ptr(out), n, ctypes.addressof(arr), len(params_list),
                              _stream(stream, inp, out)), "swz_map_batch")
 
 
 def swz_transpose(src, dst, rows: int, cols: int, elem_bytes: int, layout="swizzle", read_kind: int = READ_AUTO,
                   params=None, stream=None) -> None:
+    _buf("swz_transpose", src=(src, rows * cols * elem_bytes), dst=(dst, rows * cols * elem_bytes))
     _check(lib.swz_transpose(_ptr(src), _ptr(dst), rows, cols, elem_bytes, _layout(layout), read_kind,
                              _params(params), _stream(stream, src, dst)), "swz_transpose")
 
 
 def swz_convert_layout(src, dst, batch: int, rows: int, cols: int, elem_bytes: int, layout="swizzle",
                        read_kind: int = READ_AUTO, params=None, stream=None) -> None:
+    nbytes = batch * rows * cols * elem_bytes
+    _buf("swz_convert_layout", src=(src, nbytes), dst=(dst, nbytes))
     _check(lib.swz_convert_layout(_ptr(src), _ptr(dst), batch, rows, cols, elem_bytes, _layout(layout), read_kind,
                                   _params(params), _stream(stream, src, dst)), "swz_convert_layout")
 
 
 def swz_stage_operand(src, frag, mn: int, k: int, elem_bytes: int = 2, frag_kind: int = FRAG_MFMA_F32_16X16X32_BF16,
                       layout="swizzle", params=None, stream=None) -> None:
+    _buf("swz_stage_operand", src=(src, mn * k * elem_bytes), frag=(frag, mn * k * elem_bytes))
     _check(lib.swz_stage_operand(_ptr(src), _ptr(frag), mn, k, elem_bytes, frag_kind, _layout(layout),
                                  _params(params), _stream(stream, src, frag)), "swz_stage_operand")
 
 
 def swz_gemm_frag(fa, fb, c, m: int, n: int, k: int, frag_kind: int = FRAG_MFMA_F32_16X16X32_BF16,
                   stream=None) -> None:
+    _buf("swz_gemm_frag", fa=(fa, 2 * m * k), fb=(fb, 2 * n * k), c=(c, 4 * m * n))
     _check(lib.swz_gemm_frag(_ptr(fa), _ptr(fb), _ptr(c), m, n, k, frag_kind, _stream(stream, fa, fb, c)),
            "swz_gemm_frag")
 
 
 def swz_gemm(a, bt, c, m: int, n: int, k: int, layout: str = "swizzle", params=None, stream=None) -> None:
+    _buf("swz_gemm", a=(a, 2 * m * k), bt=(bt, 2 * n * k), c=(c, 4 * m * n))
     _check(lib.swz_gemm(_ptr(a), _ptr(bt), _ptr(c), m, n, k, _layout(layout), _params(params),
                         _stream(stream, a, bt, c)), "swz_gemm")
 
 
 def swz_gemm_ex(a, bt, c, m: int, n: int, k: int, layout: str = "swizzle", params=None, c_type: int = C_F32,
                 stream=None) -> None:
+    _buf("swz_gemm_ex", a=(a, 2 * m * k), bt=(bt, 2 * n * k), c=(c, (2 if c_type == C_BF16 else 4) * m * n))
     _check(lib.swz_gemm_ex(_ptr(a), _ptr(bt), _ptr(c), m, n, k, _layout(layout), _params(params), c_type,
                            _stream(stream, a, bt, c)), "swz_gemm_ex")
 
@@ -326,11 +361,14 @@ def swz_strerror(status: int) -> str:
 
 def swz_lds_probe(addrs, masks, n_patterns: int, width_bytes: int, is_write: int, iters: int, waves: int, cycles,
                   stream=None) -> None:
+    _buf("swz_lds_probe", addrs=(addrs, 4 * 64 * n_patterns), masks=(masks, 8 * n_patterns),
+         cycles=(cycles, 8 * n_patterns * waves))
     _check(lib.swz_lds_probe(_ptr(addrs), _ptr(masks), n_patterns, width_bytes, is_write, iters, waves,
                              _ptr(cycles), _stream(stream, addrs, masks, cycles)), "swz_lds_probe")
 
 
 def swz_copy(src, dst, nbytes: int, stream=None) -> None:
+    _buf("swz_copy", src=(src, nbytes), dst=(dst, nbytes))
     _check(lib.swz_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream, src, dst)), "swz_copy")
 
 

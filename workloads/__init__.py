@@ -98,8 +98,10 @@ def bf16_operands(m: int, n: int, k: int, seed: int = 0, std: float = 0.02):
 def index_pattern_device(shape, device, elem_bytes: int = 4):
     """A large input made on the GPU without a host copy: element
     (i0, ..., in) of a C-contiguous tensor of `shape` holds
-    (7 * i0 + flat index inside the first dimension) mod 2^(8*elem_bytes - 1),
-    as int32 (elem_bytes 4) or int16 (elem_bytes 2).  Every value is
+    (7 * i0 + 13 * (i0 >> 12) + flat index inside the first dimension) mod
+    2^(8*elem_bytes - 1), as int32 (elem_bytes 4) or int16 (elem_bytes 2); the
+    second term keeps leading indices 2^15 apart (a 15-bit pattern repeats
+    there under 7 * i0 alone) from holding the same values.  Every value is
     recomputable on the host from the element's coordinates, so sampled
     outputs of very large calls can be checked without generating the whole
     input twice.  No randomness: used where the input is too large for the
@@ -111,7 +113,8 @@ def index_pattern_device(shape, device, elem_bytes: int = 4):
     for d in shape[1:]:
         inner *= d
     mask = (1 << (8 * elem_bytes - 1)) - 1
-    base = (torch.arange(first, dtype=torch.int64, device=device) * 7).view(first, 1)
+    i0 = torch.arange(first, dtype=torch.int64, device=device)
+    base = (i0 * 7 + (i0 >> 12) * 13).view(first, 1)
     flat = torch.arange(inner, dtype=torch.int64, device=device).view(1, inner)
     out_dtype = torch.int32 if elem_bytes == 4 else torch.int16
     out = torch.empty((first, inner), dtype=out_dtype, device=device)
@@ -126,5 +129,6 @@ def index_pattern_host(shape, index, elem_bytes: int = 4) -> np.ndarray:
     (a sub-array of shape[1:]), as uint32 / uint16 bits."""
     inner = int(np.prod(shape[1:]))
     mask = (1 << (8 * elem_bytes - 1)) - 1
-    v = (7 * int(index) + np.arange(inner, dtype=np.int64)) & mask
+    i0 = int(index)
+    v = (7 * i0 + 13 * (i0 >> 12) + np.arange(inner, dtype=np.int64)) & mask
     return v.astype(np.uint32 if elem_bytes == 4 else np.uint16).reshape(shape[1:])
