@@ -413,6 +413,75 @@ def test_gemm_error_bound_covers_fp32_accumulation():
     assert np.all(err <= O.gemm_error_bound(a, bt))
 
 
+def _bf16(vals):
+    """bf16 bits of values that bf16 holds exactly."""
+    return (np.asarray(vals, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _adversarial_chunks(k=4096):
+    """One row of A and of B^T whose 32-wide chunk sums are exact in fp32 and
+    whose fp32 accumulation rounds the same way at every step: chunk 0 sums
+    to 2^24 (one fp32 step there is 2), every later chunk to 1 + 2^-8, so each
+    add lands 1 + 2^-8 above an even number and rounds up by 1 - 2^-8."""
+    a, b = np.zeros(k, np.float32), np.zeros(k, np.float32)
+    a[0] = b[0] = 2.0 ** 12
+    for c0 in range(32, k, 32):
+        a[c0] = b[c0] = 1.0
+        a[c0 + 1] = b[c0 + 1] = 2.0 ** -4
+    return _bf16(a[None, :]), _bf16(b[None, :])
+
+
+def _fp32_chunked(a_bits, bt_bits, chunks=None):
+    """fp32 accumulation of 32-wide chunk sums in k order (the matrix
+    instruction's k step), optionally over a subset of the chunks."""
+    av, bv = O.bf16_to_f64(a_bits).astype(np.float32), O.bf16_to_f64(bt_bits).astype(np.float32)
+    k = av.shape[1]
+    acc = np.zeros((av.shape[0], bv.shape[0]), dtype=np.float32)
+    for j in (range(k // 32) if chunks is None else chunks):
+        acc = acc + (av[:, 32 * j:32 * j + 32] @ bv[:, 32 * j:32 * j + 32].T).astype(np.float32)
+    return acc.astype(np.float64)
+
+
+def test_gemm_error_bound_is_reached_within_a_small_factor():
+    """From above: on inputs whose fp32 rounding errors all point one way the
+    observed error comes within 1.3x of the bound (126.5 against 160 at
+    k = 4096), so the bound is not loose by a dropped 2^-24, a step count of
+    k instead of k/32, or any other factor of 1.5 or more."""
+    a, bt = _adversarial_chunks(4096)
+    exact = O.gemm_bf16(a, bt)
+    assert exact[0, 0] == 2.0 ** 24 + 127 * (1 + 2.0 ** -8)  # the chunk sums are what the construction says
+    err = abs(_fp32_chunked(a, bt)[0, 0] - exact[0, 0])
+    bound = O.gemm_error_bound(a, bt)[0, 0]
+    assert err <= bound <= 1.5 * err
+    assert 126 < err < 127
+
+
+def test_loosened_bounds_fail_the_tightness_check():
+    """The check above tells a plausible mistake in the bound apart: the same
+    bound without its 2^-24 factor, or with k steps instead of k/32, is more
+    than 1.5x the adversarial error."""
+    a, bt = _adversarial_chunks(4096)
+    err = abs(_fp32_chunked(a, bt)[0, 0] - O.gemm_bf16(a, bt)[0, 0])
+    bound = O.gemm_error_bound(a, bt)[0, 0]
+    k = 4096
+    for loose in (bound * 2.0 ** 24, bound * (k + 32) / (k // 32 + 32)):
+        assert loose > 1.5 * err
+
+
+def test_a_dropped_chunk_exceeds_the_gemm_error_bound():
+    """The bound is small enough for the GPU GEMM tests to see a lost k chunk:
+    on operands drawn like the staging workload (normal(0, 0.02), k = 4096),
+    leaving one 32-wide chunk out of the fp32 accumulation moves nearly every
+    element by more than the bound."""
+    rng = np.random.default_rng(11)
+    a = _bf16(rng.standard_normal((16, 4096)).astype(np.float32) * np.float32(0.02))
+    bt = _bf16(rng.standard_normal((16, 4096)).astype(np.float32) * np.float32(0.02))
+    exact, bound = O.gemm_bf16(a, bt), O.gemm_error_bound(a, bt)
+    assert np.all(np.abs(_fp32_chunked(a, bt) - exact) <= bound)
+    dropped = _fp32_chunked(a, bt, [j for j in range(128) if j != 77])
+    assert np.mean(np.abs(dropped - exact) > bound) > 0.9
+
+
 # ------------------------------------------------------ negative shifts
 
 
