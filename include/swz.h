@@ -129,6 +129,19 @@ enum swz_layout {
  *               cols <= 128, B64_TR16 above (the faster of the two 64x64
  *               kinds); 1-byte -> BNARROW<cols> when cols is a power of two
  *               up to 64, else B64_TR8. */
+/* The read kind is an argument of its own (read_kind, just before
+ * p_or_null, in swz_transpose, swz_convert_layout, swz_tune_tile_order and
+ * the tile-order calls), and it names a kernel, not a class of read.  The
+ * problem statement fixes only what moves (a row-major tile read back along
+ * columns, or in the matrix-operand pattern); how a column is read back is
+ * the kernel's choice, and on gfx950 there are several for one element size
+ * (8-byte reads with a 4x4 register transpose, the 16-bit transpose read, a
+ * 16-byte 8x8 form, whole-row tiles for narrow matrices), each with its own
+ * lane map and so its own conflict-free swizzle.  A single "vector column"
+ * value could not say which, so that value became these kinds, AUTO picks
+ * one from the element size and width exactly as a caller without the
+ * argument would get, and the operand-fragment kind moved to 3.  Callers
+ * pass SWZ_READ_AUTO for the behaviour of a call without the argument. */
 enum swz_read_kind {
     SWZ_READ_AUTO = -1,
     SWZ_READ_SCALAR_COL = 0,

@@ -601,3 +601,22 @@ def test_fold_validation():
     coll, fb, strides = T.swz_fold((5, 0, 5), 7 * 32, 31)  # row 7: column bits only
     assert coll == 0 and fb == 7 * 32 + 7
     assert strides == {b: (-(1 << b) if (7 >> b) & 1 else (1 << b)) for b in range(5)}
+
+
+def test_auto_read_kind_picks_the_kernels_the_workloads_are_timed_with():
+    """SWZ_READ_AUTO stands for a call without the read-kind argument: for the
+    workloads' shapes it resolves to the kernels the benchmark times (fp32
+    4096^2: 4-byte column reads; fp16 8192^2: the 16-bit transpose read;
+    bf16 [64,4096,128]: 128-wide rows, 16-byte reads of 8x8 blocks; staging:
+    the operand-fragment pattern)."""
+    cases = [
+        (0, 4096, 4096, 4, T.READ_SCALAR_COL),
+        (0, 8192, 8192, 2, T.READ_B64_TR16),
+        (0, 4096, 128, 2, T.READ_B128_8X8),
+        (1, 8192, 4096, 2, T.READ_MFMA_16X16X32),
+        (0, 8192, 8192, 1, T.READ_B64_TR8),
+        (0, 1 << 21, 8, 4, T.READ_NARROW8),
+    ]
+    for op, rows, cols, esz, kind in cases:
+        for layout in ("swizzle", "pad", "plain"):
+            assert T.swz_plan(op, rows, cols, esz, layout, T.READ_AUTO)["read_kind"] == kind, (rows, cols, esz)
