@@ -10,6 +10,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
+import pytest  # noqa: E402
 
 
 def test_more_than_one_gpu_exits_with_a_message():
@@ -38,3 +39,36 @@ def test_traffic_bytes_only_while_the_kernel_sources_match(tmp_path, monkeypatch
     assert bench.measured_traffic("fp32_transpose") is None
     f.write_text("not json")
     assert bench.measured_traffic("fp32_transpose") is None
+
+
+def test_conflict_counters_equal_the_models_prediction_for_every_layout():
+    """The recorded SQ_LDS_BANK_CONFLICT readings (rocprofv3, one record per
+    workload and layout) equal, per tile, what swz_predict_conflicts predicts
+    under the built-in gfx950 bank model -- zero for every swizzled and
+    direct-fill kernel ("CuTe Swizzle 学习手册", ⑥: verify with a measured
+    count that the swizzle removes the conflicts)."""
+    import tiled_movement_amd as T
+
+    with open(bench.CONFLICT_FILE) as f:
+        rec = json.load(f)
+    assert len(rec["workloads"]) == 9
+    for wname, layouts in rec["workloads"].items():
+        assert set(layouts) == {"swizzle", "pad", "plain", "direct"}, wname
+        for layout, r in layouts.items():
+            w, rd = T.swz_predict_conflicts(r["read_kind"], layout)
+            assert r["conflict_cycles_per_tile"] == pytest.approx(w + rd, abs=0.5), (wname, layout)
+            if layout in ("swizzle", "direct"):
+                assert r["SQ_LDS_BANK_CONFLICT"] == 0, (wname, layout)
+
+
+def test_conflicts_reported_only_while_the_kernel_sources_match(tmp_path, monkeypatch):
+    rec = {"workloads": {"fp32_transpose": {"swizzle": {"conflict_cycles_per_tile": 0.0, "conflict_cycles_per_lds_instr": 0.0,
+                                                        "SQ_LDS_BANK_CONFLICT": 0, "SQ_LDS_IDX_ACTIVE": 1,
+                                                        "SQ_INSTS_LDS": 1}}}}
+    f = tmp_path / "lds.json"
+    monkeypatch.setattr(bench, "CONFLICT_FILE", str(f))
+    f.write_text(json.dumps(dict(rec, kernel_sources_sha256=bench.kernel_sources_digest())))
+    assert bench.measured_conflicts("fp32_transpose")["swizzle"]["conflict_cycles_per_tile"] == 0.0
+    assert bench.measured_conflicts("bf16_stage") is None
+    f.write_text(json.dumps(dict(rec, kernel_sources_sha256="0" * 64)))
+    assert bench.measured_conflicts("fp32_transpose") is None
