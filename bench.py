@@ -65,7 +65,7 @@ WORKLOADS = {
     "fp32_narrow8": "fp32 [2097152][8] -> [8][2097152] transpose (64 MiB), whole-row 128x8 LDS tiles, the swizzle spanning rows",
     "fp16_narrow8": "fp16 [4194304][8] -> [8][4194304] transpose (64 MiB), whole-row 256x8 LDS tiles, 2-byte column reads",
     "u8_narrow16": "1-byte [4194304][16] -> [16][4194304] transpose (64 MiB), whole-row 1024x16 LDS tiles, 4-byte reads of 16x4 blocks",
-    "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments",
+    "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments, both in one launch",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
     "map_batch": "Swizzle<B,M,S> of int32 offsets 0..65535 under all 125 triples in one call (8,192,000 outputs)",
     "bf16_gemm": "C[8192x8192] fp32 = A * B^T from the staged fragments of A[8192x4096] and B[4096x8192] (16x16x32 bf16 MFMA)",
@@ -265,17 +265,16 @@ def build(ctx, name, layout):
         pfa, pfb = [t.data_ptr() for t in fa], [t.data_ptr() for t in fb]
         frag = T.FRAG_MFMA_F32_16X16X32_BF16
 
-        def step(i):
+        def step(i):  # both operands in one launch
             j = i % k
-            rc = lib.swz_stage_operand(pa[j], pfa[j], 8192, 4096, 2, frag, lay, None, stream)
-            rc |= lib.swz_stage_operand(pb[j], pfb[j], 8192, 4096, 2, frag, lay, None, stream)
+            rc = lib.swz_stage_operands(pa[j], pfa[j], 8192, pb[j], pfb[j], 8192, 4096, 2, frag, lay, None, stream)
             if rc:
-                ctx.check(rc, "swz_stage_operand")
+                ctx.check(rc, "swz_stage_operands")
 
         pl = T.swz_plan(1, 8192, 4096, 2, layout)
         wc, rc_ = T.swz_predict_conflicts(T.READ_MFMA_16X16X32, layout)
         info.update({"params": list(pl["params"]), "pad_elems": pl["pad_elems"], "lds_bytes": pl["lds_bytes"],
-                     "threads": pl["threads"], "buffer_pairs": k, "launches_per_step": 2,
+                     "threads": pl["threads"], "buffer_pairs": k, "launches_per_step": 1,
                      "predicted_conflict_cycles_per_tile": {"write": wc, "read": rc_}})
         info["_keep"] = (sa, sb, fa, fb)
         info["_io"] = (ao, bo, fa[0], fb[0], step)
@@ -552,9 +551,9 @@ def tile_order_sweep(elem_bytes, mib):
 
 
 # The reference copy whose launch moves the same bytes as one launch of the
-# workload (staging: one operand per launch).
+# workload (staging: both operands, 128 MiB, in one launch).
 COPY_OF = {"fp32_transpose": "copy", "fp16_transpose": "copy_128", "fp16_transpose_tr": "copy_128",
-           "u8_transpose": "copy", "bf16_convert": "copy", "bf16_stage": "copy", "fp32_narrow8": "copy",
+           "u8_transpose": "copy", "bf16_convert": "copy", "bf16_stage": "copy_128", "fp32_narrow8": "copy",
            "fp16_narrow8": "copy", "u8_narrow16": "copy"}
 # Workloads whose oracle is timed beside them in the full run (the headline's
 # own is the line's cpu_baseline).

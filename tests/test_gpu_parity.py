@@ -436,6 +436,50 @@ def test_stage_operand_any_valid_swizzle():
         assert np.array_equal(from_dev(frag, a), ref), p
 
 
+@pytest.mark.parametrize("layout", LAYOUTS + ["direct"])
+def test_stage_operands_pair_in_one_launch(layout):
+    """Both operands of a GEMM staged by one call equal each operand's own
+    staging: unequal m and n, partial 256 x 64 tiles, a k tail, and one side
+    empty (then the call stages the other alone)."""
+    for m, n, k in [(272, 48, 96), (256, 512, 64), (48, 272, 608), (16, 16, 32), (0, 272, 96), (272, 0, 96)]:
+        announce("stage pair", layout, m, n, k)
+        a, bt = W.bf16_operands(max(m, 16), max(n, 16), k, seed=m + 3 * n + k)
+        a, bt = a[:m], bt[:n]
+        da, db = to_dev(a) if m else None, to_dev(bt) if n else None
+        fa = torch.full((max(a.size, 8),), -1, dtype=torch.int16, device=DEV)
+        fb = torch.full((max(bt.size, 8),), -1, dtype=torch.int16, device=DEV)
+        T.swz_stage_operands(da, fa, m, db, fb, n, k, layout=layout)
+        torch.cuda.synchronize()
+        if m:
+            assert np.array_equal(from_dev(fa, a), O.stage_operand(a).reshape(-1)), (m, n, k, layout)
+        else:
+            assert (fa == -1).all().item()  # an empty operand is not touched
+        if n:
+            assert np.array_equal(from_dev(fb, bt), O.stage_operand(bt).reshape(-1)), (m, n, k, layout)
+        else:
+            assert (fb == -1).all().item()
+
+
+def test_stage_operands_rejects_overlaps_and_misalignment():
+    a, bt = W.bf16_operands(256, 256, 64, seed=3)
+    da, db = to_dev(a), to_dev(bt)
+    fa = torch.empty(a.size, dtype=torch.int16, device=DEV)
+    with pytest.raises(T.SwzError) as e:  # fragments of B written over A's source
+        T.swz_stage_operands(da, fa, 256, db, da, 256, 64)
+    assert e.value.status == T.SWZ_EINVAL
+    with pytest.raises(T.SwzError):  # both fragment buffers the same memory
+        T.swz_stage_operands(da, fa, 256, db, fa, 256, 64)
+    with pytest.raises(T.SwzError):  # k not a multiple of 32
+        T.swz_stage_operands(da, fa, 256, db, torch.empty_like(fa), 256, 48)
+    assert T.raw.swz_stage_operands(da.data_ptr() + 2, fa.data_ptr(), 16, db.data_ptr(),
+                                    torch.empty_like(fa).data_ptr(), 16, 32, 2, 0, 0, None, None) == T.SWZ_EINVAL
+    # the sources may share memory (they are only read)
+    fb = torch.empty_like(fa)
+    T.swz_stage_operands(da, fa, 256, da, fb, 256, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(fa, fb)
+
+
 # --------------------------------------------- full sizes of the workloads
 
 
@@ -485,6 +529,20 @@ def test_full_operand_staging(layout):
         torch.cuda.synchronize()
         got = from_dev(frag, op).reshape(op.shape[0] // 16, op.shape[1] // 32, 64, 8)
         assert np.array_equal(got, O.stage_operand(op))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS + ["direct"])
+def test_full_operand_pair_staging(layout):
+    """The staging workload as the benchmark times it: A [8192][4096] and
+    B^T [8192][4096] in one launch."""
+    announce("full pair staging", layout)
+    a, bt = W.bf16_operands(8192, 8192, 4096, seed=0)
+    da, db = to_dev(a), to_dev(bt)
+    fa, fb = torch.empty_like(da), torch.empty_like(db)
+    T.swz_stage_operands(da, fa, 8192, db, fb, 8192, 4096, layout=layout)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(fa, a).reshape(512, 128, 64, 8), O.stage_operand(a))
+    assert np.array_equal(from_dev(fb, bt).reshape(512, 128, 64, 8), O.stage_operand(bt))
 
 
 # ---------------------------------------------------- the reference copy

@@ -41,6 +41,7 @@ EXPORTS = (
     "swz_get_tile_order",
     "swz_tune_tile_order",
     "swz_stage_operand",
+    "swz_stage_operands",
     "swz_gemm_frag",
     "swz_gemm",
     "swz_gemm_ex",
@@ -126,6 +127,7 @@ def _load() -> ctypes.CDLL:
     lib.swz_get_tile_order.argtypes = [i64, i64, i64, i32, i32, P(ctypes.c_int32)]
     lib.swz_tune_tile_order.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, P(Params), i32, P(ctypes.c_int32), vp]
     lib.swz_stage_operand.argtypes = [vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
+    lib.swz_stage_operands.argtypes = [vp, vp, i64, vp, vp, i64, i64, i32, i32, i32, P(Params), vp]
     lib.swz_gemm_frag.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
     lib.swz_gemm.argtypes = [vp, vp, vp, i64, i64, i64, i32, P(Params), vp]
     lib.swz_gemm_ex.argtypes = [vp, vp, vp, i64, i64, i64, i32, P(Params), i32, vp]
@@ -272,6 +274,17 @@ def swz_stage_operand(src, frag, mn: int, k: int, elem_bytes: int = 2, frag_kind
     _buf("swz_stage_operand", src=(src, mn * k * elem_bytes), frag=(frag, mn * k * elem_bytes))
     _check(lib.swz_stage_operand(_ptr(src), _ptr(frag), mn, k, elem_bytes, frag_kind, _layout(layout),
                                  _params(params), _stream(stream, src, frag)), "swz_stage_operand")
+
+
+def swz_stage_operands(a, fa, m: int, bt, fb, n: int, k: int, elem_bytes: int = 2,
+                       frag_kind: int = FRAG_MFMA_F32_16X16X32_BF16, layout="swizzle", params=None,
+                       stream=None) -> None:
+    """Stage A [m][k] into fa and B^T [n][k] into fb in one launch."""
+    _buf("swz_stage_operands", a=(a, m * k * elem_bytes), fa=(fa, m * k * elem_bytes), bt=(bt, n * k * elem_bytes),
+         fb=(fb, n * k * elem_bytes))
+    _check(lib.swz_stage_operands(_ptr(a), _ptr(fa), m, _ptr(bt), _ptr(fb), n, k, elem_bytes, frag_kind,
+                                  _layout(layout), _params(params), _stream(stream, a, fa, bt, fb)),
+           "swz_stage_operands")
 
 
 def swz_gemm_frag(fa, fb, c, m: int, n: int, k: int, frag_kind: int = FRAG_MFMA_F32_16X16X32_BF16,

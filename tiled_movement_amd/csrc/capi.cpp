@@ -341,6 +341,40 @@ SWZ_API int swz_stage_operand(const void* d_src, void* d_frag, int64_t mn, int64
     return hip_status(swz::launch_stage(job, static_cast<hipStream_t>(stream)));
 }
 
+SWZ_API int swz_stage_operands(const void* d_a, void* d_fa, int64_t m, const void* d_bt, void* d_fb, int64_t n,
+                               int64_t k, int32_t elem_bytes, int32_t frag_kind, int32_t layout,
+                               const swz_params* p_or_null, void* stream) {
+    if (m < 0 || n < 0 || k < 0 || m % 16 || n % 16 || k % 32) return SWZ_EINVAL;
+    if (elem_bytes != 2 || frag_kind != SWZ_FRAG_MFMA_F32_16X16X32_BF16) return SWZ_EINVAL;
+    int64_t ea, eb, a_bytes, b_bytes;
+    if (!mul_ok(m, k, &ea) || !mul_ok(ea, 2, &a_bytes) || !mul_ok(n, k, &eb) || !mul_ok(eb, 2, &b_bytes))
+        return SWZ_EINVAL;
+    swz_plan_info pl;
+    const int st = make_plan(1, m > n ? m : n, k, elem_bytes, layout, SWZ_READ_MFMA_16X16X32, p_or_null, true, true, &pl);
+    if (st != SWZ_OK) return st;
+    if (a_bytes == 0 && b_bytes == 0) return SWZ_OK;
+    if ((a_bytes && (!d_a || !d_fa)) || (b_bytes && (!d_bt || !d_fb))) return SWZ_EINVAL;
+    for (const void* q : {d_a, static_cast<const void*>(d_fa), d_bt, static_cast<const void*>(d_fb)})
+        if (reinterpret_cast<uintptr_t>(q) % 16) return SWZ_EINVAL;
+    // each fragment buffer is disjoint from both sources and from the other
+    // one (the sources are only read and may share memory)
+    if (overlaps(d_fa, a_bytes, d_a, a_bytes) || overlaps(d_fa, a_bytes, d_bt, b_bytes) ||
+        overlaps(d_fb, b_bytes, d_a, a_bytes) || overlaps(d_fb, b_bytes, d_bt, b_bytes) ||
+        overlaps(d_fa, a_bytes, d_fb, b_bytes))
+        return SWZ_EINVAL;
+    swz::StageJob job{d_a, d_fa, m, k, layout_of(pl), layout == SWZ_LAYOUT_SWIZZLE_DIRECT};
+    if (a_bytes == 0) {  // only B^T
+        job.src = d_bt;
+        job.frag = d_fb;
+        job.mn = n;
+    } else if (b_bytes > 0) {
+        job.src2 = d_bt;
+        job.frag2 = d_fb;
+        job.mn2 = n;
+    }
+    return hip_status(swz::launch_stage(job, static_cast<hipStream_t>(stream)));
+}
+
 SWZ_API int swz_gemm_frag(const void* d_fa, const void* d_fb, float* d_c, int64_t m, int64_t n, int64_t k,
                           int32_t frag_kind, void* stream) {
     if (m < 0 || n < 0 || k < 0 || m % 16 || n % 16 || k % 32) return SWZ_EINVAL;

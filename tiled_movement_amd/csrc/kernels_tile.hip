@@ -769,13 +769,14 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint
 // Arguments as for k_convert: what a whole tile of a 3-D launch reads first.
 // Grids as for k_convert (kInterior: x = k tile, y = row tile, row-major,
 // which keeps both the reads and the fragment writes contiguous; kEdge; kAll1D).
+// kInterior also stages a second operand of the same k (src2 -> frag2, its
+// full_m2 whole row tiles) as grid z = 1, so both operands of a GEMM take
+// one launch; rows of y at or past an operand's own count do nothing.
 template <int FILL, int GRID>
-__global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(const uint8_t* __restrict__ src,
-                                                                            uint8_t* __restrict__ frag, uint32_t sp,
-                                                                            uint32_t fp, uint32_t full_m,
-                                                                            uint32_t full_k, int64_t mn, int64_t k,
-                                                                            int64_t tiles_m, int64_t tiles_k,
-                                                                            int64_t tile0, KLayout L, StepMoves mv) {
+__global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(
+    const uint8_t* __restrict__ src, uint8_t* __restrict__ frag, uint32_t sp, uint32_t fp, uint32_t full_m,
+    uint32_t full_k, const uint8_t* __restrict__ src2, uint8_t* __restrict__ frag2, uint32_t full_m2, int64_t mn,
+    int64_t k, int64_t tiles_m, int64_t tiles_k, int64_t tile0, KLayout L, StepMoves mv) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
     using K = Kind<KD>;
     __shared__ u32x4 lds_v[LdsTile<KD, FILL>::BYTES / 16];
@@ -784,17 +785,19 @@ __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(cons
 
     // the tile's first element (row 256 tm, k 64 tk) and first fragment (row
     // block 16 tm, k step 2 tk)
-    auto whole = [&](uint32_t tm, uint32_t tk) {
+    auto whole = [&](const uint8_t* s, uint8_t* f, uint32_t tm, uint32_t tk) {
         const uint32_t r0 = tm * K::TR, kb0 = tk * K::TC;
-        stage_tile<FILL, true>(src + (static_cast<uint64_t>(r0) * sp + 2 * kb0),
-                               frag + (static_cast<uint64_t>(r0 / 16) * fp + 32 * kb0), mn, k, 0, 0, sp, fp, lds, L,
-                               mv, t);
+        stage_tile<FILL, true>(s + (static_cast<uint64_t>(r0) * sp + 2 * kb0),
+                               f + (static_cast<uint64_t>(r0 / 16) * fp + 32 * kb0), mn, k, 0, 0, sp, fp, lds, L, mv,
+                               t);
     };
     auto guarded = [&](int64_t tm, int64_t tk) {
         stage_tile<FILL, false>(src, frag, mn, k, tm * K::TR, tk * K::TC, 0u, 0u, lds, L, mv, t);
     };
     if constexpr (GRID == kInterior) {
-        whole(blockIdx.y, blockIdx.x);
+        const bool second = blockIdx.z != 0;
+        if (blockIdx.y >= (second ? full_m2 : full_m)) return;
+        whole(second ? src2 : src, second ? frag2 : frag, blockIdx.y, blockIdx.x);
     } else if constexpr (GRID == kEdge) {
         int64_t tm, tk;
         edge_tile(tile0 + blockIdx.x, full_m, full_k, tiles_m, tiles_k, tm, tk);
@@ -802,7 +805,7 @@ __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(cons
     } else {
         const int64_t idx = tile0 + blockIdx.x, tm = idx / tiles_k, tk = idx - tm * tiles_k;
         if (tm < full_m && tk < full_k)
-            whole(static_cast<uint32_t>(tm), static_cast<uint32_t>(tk));
+            whole(src, frag, static_cast<uint32_t>(tm), static_cast<uint32_t>(tk));
         else
             guarded(tm, tk);
     }
@@ -936,35 +939,57 @@ hipError_t launch_kind(const ConvertJob& j, hipStream_t stream) {
 }
 
 template <int FILL>
-void launch_stage_fill(const StageJob& j, int64_t tiles_m, int64_t tiles_k, hipStream_t stream) {
+void launch_stage_fill(const StageJob& j, hipStream_t stream) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
     using K = Kind<KD>;
-    const auto* s = static_cast<const uint8_t*>(j.src);
-    auto* f = static_cast<uint8_t*>(j.frag);
     const StepMoves mv = step_moves<KD>(j.layout, FILL == kPadded);
     const KLayout kl = decode_layout(j.layout);
+    const unsigned lds_pad = occupancy_pad<KD>(LdsTile<KD, FILL>::BYTES);
+    const dim3 block(K::NT);
+    const bool pair = j.src2 != nullptr;
+    struct Op {
+        const uint8_t* s;
+        uint8_t* f;
+        int64_t mn;
+    };
+    const Op ops[2] = {{static_cast<const uint8_t*>(j.src), static_cast<uint8_t*>(j.frag), j.mn},
+                       {static_cast<const uint8_t*>(j.src2), static_cast<uint8_t*>(j.frag2), pair ? j.mn2 : 0}};
+    const int nops = pair ? 2 : 1;
+    const int64_t tiles_k = ceil_div(j.k, K::TC);
     // Whole tiles address rows of 2k bytes and row blocks of fragments of
     // 32k bytes with 32-bit pitches: both must fit, else every tile takes
     // the 64-bit edge path.
-    const bool fit = j.mn < (int64_t(1) << 31) && j.k * 32 < (int64_t(1) << 32);
+    const bool fit = j.mn < (int64_t(1) << 31) && ops[1].mn < (int64_t(1) << 31) && j.k * 32 < (int64_t(1) << 32);
     const uint32_t sp = fit ? static_cast<uint32_t>(2 * j.k) : 0u, fpitch = fit ? static_cast<uint32_t>(32 * j.k) : 0u;
-    const uint32_t full_m = fit ? static_cast<uint32_t>(j.mn / K::TR) : 0u, full_k = fit ? static_cast<uint32_t>(j.k / K::TC) : 0u;
-    const unsigned lds_pad = occupancy_pad<KD>(LdsTile<KD, FILL>::BYTES);
-    const dim3 block(K::NT);
-    if (full_m > 0 && full_k > 0 && fits_3d(full_k, full_m, 1, K::NT)) {
-        hipLaunchKernelGGL((k_stage<FILL, kInterior>), dim3(full_k, full_m, 1), block, lds_pad, stream, s, f, sp, fpitch,
-                           full_m, full_k, j.mn, j.k, tiles_m, tiles_k, int64_t(0), kl, mv);
-        const int64_t edges = (tiles_k > full_k ? int64_t(full_m) : 0) + (tiles_m > full_m ? tiles_k : 0);
-        launch_chunks(edges, [&](int64_t t0, int64_t n) {
-            hipLaunchKernelGGL((k_stage<FILL, kEdge>), dim3(static_cast<unsigned>(n)), block, lds_pad, stream, s, f, sp,
-                               fpitch, full_m, full_k, j.mn, j.k, tiles_m, tiles_k, t0, kl, mv);
-        });
+    const uint32_t full_k = fit ? static_cast<uint32_t>(j.k / K::TC) : 0u;
+    uint32_t full_m[2] = {0u, 0u};
+    for (int o = 0; o < nops; ++o) full_m[o] = fit ? static_cast<uint32_t>(ops[o].mn / K::TR) : 0u;
+    const uint32_t rows_y = full_m[0] > full_m[1] ? full_m[0] : full_m[1];
+    if (full_k > 0 && rows_y > 0 && fits_3d(full_k, rows_y, nops, K::NT)) {
+        // the whole tiles of every operand in one launch, then each
+        // operand's edge strips
+        hipLaunchKernelGGL((k_stage<FILL, kInterior>), dim3(full_k, rows_y, nops), block, lds_pad, stream, ops[0].s,
+                           ops[0].f, sp, fpitch, full_m[0], full_k, ops[1].s, ops[1].f, full_m[1], j.mn, j.k,
+                           ceil_div(j.mn, K::TR), tiles_k, int64_t(0), kl, mv);
+        for (int o = 0; o < nops; ++o) {
+            const int64_t tiles_m = ceil_div(ops[o].mn, K::TR);
+            const int64_t edges = (tiles_k > full_k ? int64_t(full_m[o]) : 0) + (tiles_m > full_m[o] ? tiles_k : 0);
+            launch_chunks(edges, [&](int64_t t0, int64_t n) {
+                hipLaunchKernelGGL((k_stage<FILL, kEdge>), dim3(static_cast<unsigned>(n)), block, lds_pad, stream,
+                                   ops[o].s, ops[o].f, sp, fpitch, full_m[o], full_k, ops[o].s, ops[o].f, full_m[o],
+                                   ops[o].mn, j.k, tiles_m, tiles_k, t0, kl, mv);
+            });
+        }
         return;
     }
-    launch_chunks(tiles_m * tiles_k, [&](int64_t t0, int64_t n) {
-        hipLaunchKernelGGL((k_stage<FILL, kAll1D>), dim3(static_cast<unsigned>(n)), block, lds_pad, stream, s, f, sp,
-                           fpitch, full_m, full_k, j.mn, j.k, tiles_m, tiles_k, t0, kl, mv);
-    });
+    for (int o = 0; o < nops; ++o) {
+        const int64_t tiles_m = ceil_div(ops[o].mn, K::TR);
+        launch_chunks(tiles_m * tiles_k, [&](int64_t t0, int64_t n) {
+            hipLaunchKernelGGL((k_stage<FILL, kAll1D>), dim3(static_cast<unsigned>(n)), block, lds_pad, stream,
+                               ops[o].s, ops[o].f, sp, fpitch, full_m[o], full_k, ops[o].s, ops[o].f, full_m[o],
+                               ops[o].mn, j.k, tiles_m, tiles_k, t0, kl, mv);
+        });
+    }
 }
 
 }  // namespace
@@ -1001,17 +1026,17 @@ hipError_t launch_convert(int kind, const ConvertJob& j, hipStream_t stream) {
 hipError_t launch_stage(const StageJob& j, hipStream_t stream) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
     using K = Kind<KD>;
-    const int64_t tiles_m = ceil_div(j.mn, K::TR), tiles_k = ceil_div(j.k, K::TC);
-    if (tiles_m * tiles_k == 0) return hipSuccess;
+    const int64_t rows = j.mn + (j.src2 ? j.mn2 : 0);
+    if (rows == 0 || ceil_div(j.k, K::TC) == 0) return hipSuccess;
     const bool padded = j.layout.ld != static_cast<uint32_t>(K::TC);
     if (padded && j.layout.ld != static_cast<uint32_t>(K::TC + LdsTile<KD, kPadded>::PAD)) return hipErrorInvalidValue;
     if (j.direct) {
         if (padded) return hipErrorInvalidValue;
-        launch_stage_fill<kDirect>(j, tiles_m, tiles_k, stream);
+        launch_stage_fill<kDirect>(j, stream);
     } else if (padded) {
-        launch_stage_fill<kPadded>(j, tiles_m, tiles_k, stream);
+        launch_stage_fill<kPadded>(j, stream);
     } else {
-        launch_stage_fill<kRegs>(j, tiles_m, tiles_k, stream);
+        launch_stage_fill<kRegs>(j, stream);
     }
     return hipGetLastError();
 }

@@ -24,6 +24,11 @@ struct StageJob {
     int64_t mn, k;
     LdsLayout layout;
     bool direct;  // direct HBM -> LDS fill
+    // A second operand staged by the same launch (src2 == nullptr: none):
+    // src2 [mn2][k] into frag2, same k, layout and fill.
+    const void* src2 = nullptr;
+    void* frag2 = nullptr;
+    int64_t mn2 = 0;
 };
 
 hipError_t launch_convert(int kind, const ConvertJob& job, hipStream_t stream);
