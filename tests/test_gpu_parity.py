@@ -146,6 +146,7 @@ def shapes_for(tr, tc):
     return [
         (3 * tr, 2 * tc),  # whole tiles
         (2 * tr + 5, 3 * tc + 3),  # ragged tails in both directions
+        (3 * tr + 7, 2 * tc + 5),  # an odd count of whole tile rows, then a ragged one
         (tr - 1, tc + 1),
         (1, 1),
         (1, 5 * tc + 7),

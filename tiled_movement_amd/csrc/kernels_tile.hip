@@ -220,7 +220,8 @@ FastPath fast_path(int64_t batch, int64_t rows, int64_t cols, int esz, int tr, i
 // that a CU holds at most this many workgroups of the kind (0: no limit).
 // Values from a sweep of the kernels themselves (2 to 8 per CU): 4 for the
 // 64-row 16-bit kinds (+3 to +8%), 5 for the byte kind (+4%); the fp32 tile
-// loses bandwidth when limited and staging's 32 KiB tile already sits at 5.
+// loses bandwidth when limited, and staging's interior workgroup (four 32 KiB
+// tiles) fills a CU's LDS by itself.
 // The byte tiles of 32 and 64 columns (16 KiB) are capped at 4 per CU (4%
 // faster in a sweep of uncapped, 4 and 8); every other whole-row kind lost up
 // to 20% when capped.
@@ -232,18 +233,41 @@ constexpr int occupancy_limit() {
                                                                         : 0;
 }
 
+// Whole tiles per workgroup of the interior launch: tiles that follow one
+// another down the source rows, so the workgroup writes each output row's
+// part of them as one run (256 bytes for two 64-row 16-bit tiles).  Two
+// 16-bit 64 x 64 tiles per workgroup, at half the workgroups per CU, ran 4%
+// (4x4 reads) and 3% (transpose reads) faster on fp16 8192 x 8192; stacking
+// the fp32 and byte tiles lost 5% and 2%, the 8x8-read 16-bit tile gained
+// under 1%.
+template <int KIND>
+constexpr int stack_of() {
+    return KIND == SWZ_READ_B64_4X4 || KIND == SWZ_READ_B64_TR16 ? 2 : 1;
+}
+
+// Workgroups per CU of the interior launch (0: no limit): as many tiles in
+// flight per CU as the single-tile limit allows (a sweep of 2 to 4 stacked
+// 16-bit workgroups per CU found 2 and 3 alike, 4 slower).
+template <int KIND>
+constexpr int interior_occupancy_limit() {
+    return occupancy_limit<KIND>() / stack_of<KIND>();
+}
+
 constexpr int kLdsPerCu = 160 * 1024;
 
 // Dynamic LDS to add to a launch whose kernel uses `static_bytes` so that at
-// most occupancy_limit<KIND>() workgroups fit on a CU.
-template <int KIND>
-constexpr unsigned occupancy_pad(int static_bytes) {
-    const int limit = occupancy_limit<KIND>();
+// most `limit` workgroups fit on a CU.
+constexpr unsigned occupancy_pad_to(int static_bytes, int limit) {
     if (limit <= 0) return 0;
     // floor(kLdsPerCu / per_wg) == limit for per_wg = kLdsPerCu / limit, and
     // rounding the pad up can only lower the count further.
     const int per_wg = kLdsPerCu / limit;
     return static_cast<unsigned>(per_wg > static_bytes ? (per_wg - static_bytes + 511) / 512 * 512 : 0);
+}
+
+template <int KIND>
+constexpr unsigned occupancy_pad(int static_bytes) {
+    return occupancy_pad_to(static_bytes, occupancy_limit<KIND>());
 }
 
 // How a kernel fills the LDS tile: through registers into swizzled (or
@@ -624,28 +648,38 @@ __device__ __forceinline__ uint32_t diagonal_column(uint32_t n, TileOrder O) {
     return c >= n ? c - n : c;
 }
 
-// Edge tile e (of one batch entry) of a matrix with full_r x full_c whole
-// tiles and tiles_r x tiles_c tiles in all: first the last tile column next
-// to the whole tile rows, then the whole last tile row.
-__device__ __forceinline__ void edge_tile(int64_t e, int64_t full_r, int64_t full_c, int64_t tiles_r,
-                                          int64_t tiles_c, int64_t& tr, int64_t& tc) {
-    const int64_t right = tiles_c > full_c ? full_r : 0;
+// Edge tile e (of one batch entry) outside the first full_r x full_c tiles
+// of a matrix of tiles_r x tiles_c tiles: first the tile columns from full_c
+// on next to the first full_r tile rows, row by row, then the tile rows from
+// full_r on, whole.
+__host__ __device__ __forceinline__ int64_t edge_tiles(int64_t full_r, int64_t full_c, int64_t tiles_r,
+                                                       int64_t tiles_c) {
+    return (tiles_c - full_c) * full_r + (tiles_r - full_r) * tiles_c;
+}
+
+__device__ __forceinline__ void edge_tile(int64_t e, int64_t full_r, int64_t full_c, int64_t tiles_c, int64_t& tr,
+                                          int64_t& tc) {
+    const int64_t w = tiles_c - full_c, right = w * full_r;
     if (e < right) {
-        tr = e;
-        tc = full_c;
+        tr = e / w;
+        tc = full_c + (e - tr * w);
     } else {
-        tr = full_r;
-        tc = e - right;
+        tr = full_r + (e - right) / tiles_c;
+        tc = (e - right) % tiles_c;
     }
-    (void)tiles_r;
 }
 
 // Arguments in the order the kernel needs them: the first thirteen dwords
 // (pointers, tile columns, tile order, the host's FastPath, 32-bit sizes;
 // plain scalars, which is what the build's kernel-argument preload puts in
 // SGPRs) are all a whole tile of a 3-D launch reads before its first load.
+template <int KIND, int GRID>
+constexpr int stack_in() {
+    return GRID == kInterior ? stack_of<KIND>() : 1;
+}
+
 template <int KIND, int FILL, bool ALIGNED, int GRID>
-__global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+__global__ __launch_bounds__((Kind<KIND>::NT * stack_in<KIND, GRID>())) void k_convert(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                             uint32_t tiles_c32, uint32_t order_num, uint32_t order_sh,
                                                             uint32_t sp, uint32_t dp, uint32_t full_r, uint32_t full_c,
                                                             uint32_t rows32, uint32_t cols32, int64_t rows,
@@ -655,9 +689,14 @@ __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __res
     constexpr int E = K::ESZ;
     static_assert(FILL != kDirect || ALIGNED, "the direct fill needs 16-byte aligned rows");
     static_assert(ALIGNED || GRID == kAll3D || GRID == kAll1D, "unaligned pitches take the element-wise path");
-    __shared__ u32x4 lds_v[(LdsTile<KIND, FILL>::BYTES + 15) / 16];
-    uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
-    const int t = threadIdx.x;
+    constexpr int STACK = stack_in<KIND, GRID>();
+    constexpr int TILE_V = (LdsTile<KIND, FILL>::BYTES + 15) / 16;
+    __shared__ u32x4 lds_v[STACK * TILE_V];
+    // the interior's stacked tiles: each NT threads (whole waves) move one
+    static_assert(STACK == 1 || (K::NT % 64 == 0 && (K::NT & (K::NT - 1)) == 0), "whole waves per tile");
+    const int g = STACK == 1 ? 0 : static_cast<int>(threadIdx.x) / K::NT;
+    uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v + g * TILE_V);
+    const int t = STACK == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) & (K::NT - 1);
     const TileOrder O{order_num, order_sh};
 
     // A whole tile: batch entry b's rows follow entry b - 1's in both
@@ -679,14 +718,14 @@ __global__ __launch_bounds__(Kind<KIND>::NT) void k_convert(const uint8_t* __res
     };
 
     if constexpr (GRID == kInterior) {
-        whole(blockIdx.z, blockIdx.x, diagonal_column(tiles_c32, O));
+        whole(blockIdx.z, blockIdx.x * STACK + g, diagonal_column(tiles_c32, O));
     } else if constexpr (GRID == kEdge) {
         const int64_t tiles_c = (cols + K::TC - 1) / K::TC;
-        const int64_t per = (tiles_c > full_c ? int64_t(full_r) : 0) + (tiles_r > full_r ? tiles_c : 0);
+        const int64_t per = edge_tiles(full_r, full_c, tiles_r, tiles_c);
         const int64_t idx = tile0 + blockIdx.x;
         const int64_t b = idx / per;
         int64_t tr, tc;
-        edge_tile(idx - b * per, full_r, full_c, tiles_r, tiles_c, tr, tc);
+        edge_tile(idx - b * per, full_r, full_c, tiles_c, tr, tc);
         guarded(b, tr, tc);
     } else {
         int64_t b, tr, tc;
@@ -772,16 +811,33 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint
 // kInterior also stages a second operand of the same k (src2 -> frag2, its
 // full_m2 whole row tiles) as grid z = 1, so both operands of a GEMM take
 // one launch; rows of y at or past an operand's own count do nothing.
+// Whole staging tiles per workgroup of the interior launch, side by side
+// along k: the workgroup reads each operand row's part of them as one run
+// (512 bytes for four) and writes each row block's fragments of them as one
+// run (8 KiB).  Staging both 8192 x 4096 bf16 operands ran 3% faster with
+// two tiles per workgroup and 4% with four (1024 threads, one workgroup per
+// CU) than with one.
+constexpr int kStageStack = 4;
+
+template <int GRID>
+constexpr int stage_stack_in() {
+    return GRID == kInterior ? kStageStack : 1;
+}
+
 template <int FILL, int GRID>
-__global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(
+__global__ __launch_bounds__((Kind<SWZ_READ_MFMA_16X16X32>::NT * stage_stack_in<GRID>())) void k_stage(
     const uint8_t* __restrict__ src, uint8_t* __restrict__ frag, uint32_t sp, uint32_t fp, uint32_t full_m,
     uint32_t full_k, const uint8_t* __restrict__ src2, uint8_t* __restrict__ frag2, uint32_t full_m2, int64_t mn,
     int64_t k, int64_t tiles_m, int64_t tiles_k, int64_t tile0, KLayout L, StepMoves mv) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
     using K = Kind<KD>;
-    __shared__ u32x4 lds_v[LdsTile<KD, FILL>::BYTES / 16];
-    uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
-    const int t = threadIdx.x;
+    constexpr int STACK = stage_stack_in<GRID>();
+    constexpr int TILE_V = LdsTile<KD, FILL>::BYTES / 16;
+    __shared__ u32x4 lds_v[STACK * TILE_V];
+    static_assert(K::NT % 64 == 0 && (K::NT & (K::NT - 1)) == 0, "whole waves per tile");
+    const int g = STACK == 1 ? 0 : static_cast<int>(threadIdx.x) / K::NT;
+    uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v + g * TILE_V);
+    const int t = STACK == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) & (K::NT - 1);
 
     // the tile's first element (row 256 tm, k 64 tk) and first fragment (row
     // block 16 tm, k step 2 tk)
@@ -797,10 +853,10 @@ __global__ __launch_bounds__(Kind<SWZ_READ_MFMA_16X16X32>::NT) void k_stage(
     if constexpr (GRID == kInterior) {
         const bool second = blockIdx.z != 0;
         if (blockIdx.y >= (second ? full_m2 : full_m)) return;
-        whole(second ? src2 : src, second ? frag2 : frag, blockIdx.y, blockIdx.x);
+        whole(second ? src2 : src, second ? frag2 : frag, blockIdx.y, blockIdx.x * STACK + g);
     } else if constexpr (GRID == kEdge) {
         int64_t tm, tk;
-        edge_tile(tile0 + blockIdx.x, full_m, full_k, tiles_m, tiles_k, tm, tk);
+        edge_tile(tile0 + blockIdx.x, full_m, full_k, tiles_k, tm, tk);
         guarded(tm, tk);
     } else {
         const int64_t idx = tile0 + blockIdx.x, tm = idx / tiles_k, tk = idx - tm * tiles_k;
@@ -867,24 +923,29 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
     const KLayout kl = decode_layout(j.layout);
     const unsigned lds_pad = occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES);
     const dim3 block(K::NT);
-    auto args = [&](uint32_t cols_of_order, int64_t tile0) {
-        return std::make_tuple(s, d, cols_of_order, O.num, O.sh, fp.sp, fp.dp, fp.full_r, fp.full_c, r32, c32, j.rows,
+    auto args = [&](uint32_t cols_of_order, int64_t tile0, uint32_t full_r) {
+        return std::make_tuple(s, d, cols_of_order, O.num, O.sh, fp.sp, fp.dp, full_r, fp.full_c, r32, c32, j.rows,
                                j.cols, tiles_r, tile0, kl, mv);
     };
     if constexpr (ALIGNED) {
-        if (fp.full_r > 0 && fp.full_c > 0 && fits_3d(fp.full_r, fp.full_c, j.batch, K::NT)) {
-            // the whole tiles, then (if any) the edge strips
+        // the interior covers the whole tile rows in groups of STACK; the
+        // rows past the last group join the edge strips
+        constexpr int STACK = stack_of<KIND>();
+        const uint32_t inner_r = fp.full_r / STACK * STACK;
+        if (inner_r > 0 && fp.full_c > 0 && fits_3d(inner_r / STACK, fp.full_c, j.batch, K::NT * STACK)) {
+            const unsigned inner_pad =
+                occupancy_pad_to(STACK * LdsTile<KIND, FILL>::BYTES, interior_occupancy_limit<KIND>());
             std::apply([&](auto... a) {
                 hipLaunchKernelGGL((k_convert<KIND, FILL, true, kInterior>),
-                                   dim3(fp.full_r, fp.full_c, static_cast<unsigned>(j.batch)), block, lds_pad, stream,
-                                   a...);
-            }, args(fp.full_c, 0));
-            const int64_t per = (tiles_c > fp.full_c ? int64_t(fp.full_r) : 0) + (tiles_r > fp.full_r ? tiles_c : 0);
+                                   dim3(inner_r / STACK, fp.full_c, static_cast<unsigned>(j.batch)),
+                                   dim3(K::NT * STACK), inner_pad, stream, a...);
+            }, args(fp.full_c, 0, inner_r));
+            const int64_t per = edge_tiles(inner_r, fp.full_c, tiles_r, tiles_c);
             launch_chunks(j.batch * per, [&](int64_t t0, int64_t n) {
                 std::apply([&](auto... a) {
                     hipLaunchKernelGGL((k_convert<KIND, FILL, true, kEdge>), dim3(static_cast<unsigned>(n)), block,
                                        lds_pad, stream, a...);
-                }, args(static_cast<uint32_t>(tiles_c), t0));
+                }, args(static_cast<uint32_t>(tiles_c), t0, inner_r));
             });
             return;
         }
@@ -895,7 +956,7 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
                                    dim3(static_cast<unsigned>(tiles_r), static_cast<unsigned>(tiles_c),
                                         static_cast<unsigned>(j.batch)),
                                    block, lds_pad, stream, a...);
-            }, args(static_cast<uint32_t>(tiles_c), 0));
+            }, args(static_cast<uint32_t>(tiles_c), 0, fp.full_r));
             return;
         }
     }
@@ -903,7 +964,7 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
         std::apply([&](auto... a) {
             hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, kAll1D>), dim3(static_cast<unsigned>(n)), block, lds_pad,
                                stream, a...);
-        }, args(static_cast<uint32_t>(tiles_c), t0));
+        }, args(static_cast<uint32_t>(tiles_c), t0, fp.full_r));
     });
 }
 
@@ -965,18 +1026,21 @@ void launch_stage_fill(const StageJob& j, hipStream_t stream) {
     uint32_t full_m[2] = {0u, 0u};
     for (int o = 0; o < nops; ++o) full_m[o] = fit ? static_cast<uint32_t>(ops[o].mn / K::TR) : 0u;
     const uint32_t rows_y = full_m[0] > full_m[1] ? full_m[0] : full_m[1];
-    if (full_k > 0 && rows_y > 0 && fits_3d(full_k, rows_y, nops, K::NT)) {
+    // the interior covers the whole k tiles in groups of kStageStack; the
+    // k tiles past the last group join the edge strips
+    const uint32_t inner_k = full_k / kStageStack * kStageStack;
+    if (inner_k > 0 && rows_y > 0 && fits_3d(inner_k / kStageStack, rows_y, nops, K::NT * kStageStack)) {
         // the whole tiles of every operand in one launch, then each
         // operand's edge strips
-        hipLaunchKernelGGL((k_stage<FILL, kInterior>), dim3(full_k, rows_y, nops), block, lds_pad, stream, ops[0].s,
-                           ops[0].f, sp, fpitch, full_m[0], full_k, ops[1].s, ops[1].f, full_m[1], j.mn, j.k,
-                           ceil_div(j.mn, K::TR), tiles_k, int64_t(0), kl, mv);
+        hipLaunchKernelGGL((k_stage<FILL, kInterior>), dim3(inner_k / kStageStack, rows_y, nops),
+                           dim3(K::NT * kStageStack), 0, stream, ops[0].s, ops[0].f, sp, fpitch, full_m[0], inner_k,
+                           ops[1].s, ops[1].f, full_m[1], j.mn, j.k, ceil_div(j.mn, K::TR), tiles_k, int64_t(0), kl,
+                           mv);
         for (int o = 0; o < nops; ++o) {
             const int64_t tiles_m = ceil_div(ops[o].mn, K::TR);
-            const int64_t edges = (tiles_k > full_k ? int64_t(full_m[o]) : 0) + (tiles_m > full_m[o] ? tiles_k : 0);
-            launch_chunks(edges, [&](int64_t t0, int64_t n) {
+            launch_chunks(edge_tiles(full_m[o], inner_k, tiles_m, tiles_k), [&](int64_t t0, int64_t n) {
                 hipLaunchKernelGGL((k_stage<FILL, kEdge>), dim3(static_cast<unsigned>(n)), block, lds_pad, stream,
-                                   ops[o].s, ops[o].f, sp, fpitch, full_m[o], full_k, ops[o].s, ops[o].f, full_m[o],
+                                   ops[o].s, ops[o].f, sp, fpitch, full_m[o], inner_k, ops[o].s, ops[o].f, full_m[o],
                                    ops[o].mn, j.k, tiles_m, tiles_k, t0, kl, mv);
             });
         }
