@@ -502,8 +502,9 @@ def cpu_baseline(name, info, seconds):
 def tile_order_sweep(elem_bytes, mib):
     """Every tile order of the transposes on matrices of `mib` MiB and shapes
     from 256 rows up to 256 columns: each order pinned (swz_set_tile_order),
-    rotating over four buffer pairs, best of three batches of 100 calls
-    timed with HIP events; then what swz_tune_tile_order picks on one pair.
+    rotating over four buffer pairs of random bytes, best of three batches of
+    100 calls timed with HIP events; then what swz_tune_tile_order picks on
+    one pair.
     Pins are removed afterwards.  Returns the lines of a table."""
     import torch
 
@@ -514,7 +515,9 @@ def tile_order_sweep(elem_bytes, mib):
     pairs, nbytes = 4, mib << 20
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    srcs = [torch.full((nbytes,), p + 1, dtype=torch.uint8, device=dev) for p in range(pairs)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    srcs = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev, generator=gen) for _ in range(pairs)]
     dsts = [torch.empty((nbytes,), dtype=torch.uint8, device=dev) for _ in range(pairs)]
     sp, dp = [t.data_ptr() for t in srcs], [t.data_ptr() for t in dsts]
 

@@ -127,8 +127,9 @@ enum swz_layout {
  *  AUTO       : 4-byte -> NARROW<cols> when cols is 1, 2, 4, 8 or 16, else
  *               SCALAR_COL; 2-byte -> HNARROW<cols> when cols is a power of
  *               two up to 32, else B64_TR16 when cols <= 64, B128_8X8 when
- *               cols <= 128, B64_TR16 above (the faster of the two 64x64
- *               kinds); 1-byte -> BNARROW<cols> when cols is a power of two
+ *               cols <= 128, B64_TR16 when cols <= 256 and B64_4X4 above
+ *               (the faster of the two 64x64 kinds at those widths);
+ *               1-byte -> BNARROW<cols> when cols is a power of two
  *               up to 64, else B64_TR8. */
 /* The read kind is an argument of its own (read_kind, just before
  * p_or_null, in swz_transpose, swz_convert_layout, swz_tune_tile_order and
@@ -185,7 +186,10 @@ typedef struct swz_plan_info {
     int32_t vec_bytes;   /* width of the LDS stores of the staging pass (the
                             direct fill: bytes each lane's load writes) */
     int32_t aligned;     /* 1 if the 16-byte vector path is used */
-    int32_t threads;     /* threads per workgroup (one tile at a time) */
+    int32_t threads;     /* threads per tile */
+    int32_t interior_tiles; /* whole tiles per workgroup of the whole-tile
+                            launch (threads x interior_tiles threads); a
+                            tile on a ragged edge takes a workgroup alone */
 } swz_plan_info;
 
 /* out[i] = Swizzle<B,M,S>(in[i]) for i < n, on the 32-bit bit patterns

@@ -157,12 +157,16 @@ def test_plans():
     p = T.swz_plan(0, 4096, 4096, 4, "swizzle")
     assert p["read_kind"] == T.READ_SCALAR_COL and p["tile"] == (32, 32) and p["lds_bytes"] == 4096
     assert T.swz_plan(0, 4096, 4096, 4, "pad")["lds_bytes"] == 32 * 33 * 4
-    assert T.swz_plan(0, 8192, 8192, 2)["read_kind"] == T.READ_B64_TR16
+    assert T.swz_plan(0, 8192, 8192, 2)["read_kind"] == T.READ_B64_4X4
     assert T.swz_plan(0, 4096, 128, 2)["read_kind"] == T.READ_B128_8X8
     assert T.swz_plan(0, 64, 64, 2, "pad", T.READ_B64_4X4)["lds_bytes"] == 64 * 72 * 2
     assert T.swz_plan(0, 64, 64, 2, "plain", T.READ_B64_4X4)["params"] == (0, 0, 0)
     s = T.swz_plan(1, 8192, 4096, 2)
     assert s["read_kind"] == T.READ_MFMA_16X16X32 and s["tile"] == (256, 64)
+    # tiles per workgroup of the whole-tile launch
+    assert s["interior_tiles"] == 4 and p["interior_tiles"] == 1
+    assert T.swz_plan(0, 8192, 8192, 2)["interior_tiles"] == 2
+    assert T.swz_plan(0, 4096, 128, 2)["interior_tiles"] == 1
     assert T.swz_plan(0, 64, 64, 2, "swizzle", T.READ_B64_4X4, (3, 3, 6))["params"] == (3, 3, 6)
 
 
@@ -606,12 +610,14 @@ def test_fold_validation():
 def test_auto_read_kind_picks_the_kernels_the_workloads_are_timed_with():
     """SWZ_READ_AUTO stands for a call without the read-kind argument: for the
     workloads' shapes it resolves to the kernels the benchmark times (fp32
-    4096^2: 4-byte column reads; fp16 8192^2: the 16-bit transpose read;
+    4096^2: 4-byte column reads; fp16 8192^2: 8-byte reads of 4x4 blocks;
     bf16 [64,4096,128]: 128-wide rows, 16-byte reads of 8x8 blocks; staging:
     the operand-fragment pattern)."""
     cases = [
         (0, 4096, 4096, 4, T.READ_SCALAR_COL),
-        (0, 8192, 8192, 2, T.READ_B64_TR16),
+        (0, 8192, 8192, 2, T.READ_B64_4X4),
+        (0, 1 << 18, 256, 2, T.READ_B64_TR16),  # the widest 16-bit rows that keep transpose reads
+        (0, 4096, 320, 2, T.READ_B64_4X4),
         (0, 4096, 128, 2, T.READ_B128_8X8),
         (1, 8192, 4096, 2, T.READ_MFMA_16X16X32),
         (0, 8192, 8192, 1, T.READ_B64_TR8),

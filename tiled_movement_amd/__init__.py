@@ -90,6 +90,7 @@ class PlanInfo(ctypes.Structure):
         ("vec_bytes", ctypes.c_int32),
         ("aligned", ctypes.c_int32),
         ("threads", ctypes.c_int32),
+        ("interior_tiles", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -103,6 +104,7 @@ class PlanInfo(ctypes.Structure):
             "vec_bytes": self.vec_bytes,
             "aligned": bool(self.aligned),
             "threads": self.threads,
+            "interior_tiles": self.interior_tiles,
         }
 
 

@@ -89,7 +89,8 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
                 kind = narrow        ? SWZ_READ_HNARROW1 + lc
                        : cols <= 64  ? SWZ_READ_B64_TR16
                        : cols <= 128 ? SWZ_READ_B128_8X8
-                                     : SWZ_READ_B64_TR16;
+                       : cols <= 256 ? SWZ_READ_B64_TR16
+                                     : SWZ_READ_B64_4X4;
             else
                 kind = narrow ? SWZ_READ_BNARROW1 + lc : SWZ_READ_B64_TR8;
         }
@@ -121,6 +122,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     out->vec_bytes = layout == SWZ_LAYOUT_SWIZZLE_DIRECT ? (k.esz == 2 ? 16 : 4) : k.vec;
     out->aligned = aligned ? 1 : 0;
     out->threads = k.nt;
+    out->interior_tiles = swz::interior_stack(kind);
     (void)rows;
     return SWZ_OK;
 }

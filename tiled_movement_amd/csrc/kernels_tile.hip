@@ -233,16 +233,11 @@ constexpr int occupancy_limit() {
                                                                         : 0;
 }
 
-// Whole tiles per workgroup of the interior launch: tiles that follow one
-// another down the source rows, so the workgroup writes each output row's
-// part of them as one run (256 bytes for two 64-row 16-bit tiles).  Two
-// 16-bit 64 x 64 tiles per workgroup, at half the workgroups per CU, ran 4%
-// (4x4 reads) and 3% (transpose reads) faster on fp16 8192 x 8192; stacking
-// the fp32 and byte tiles lost 5% and 2%, the 8x8-read 16-bit tile gained
-// under 1%.
+// Whole tiles per workgroup of a transpose's interior launch, one after
+// another down the source rows (interior_stack).
 template <int KIND>
 constexpr int stack_of() {
-    return KIND == SWZ_READ_B64_4X4 || KIND == SWZ_READ_B64_TR16 ? 2 : 1;
+    return interior_stack(KIND);
 }
 
 // Workgroups per CU of the interior launch (0: no limit): as many tiles in
@@ -812,12 +807,8 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint
 // full_m2 whole row tiles) as grid z = 1, so both operands of a GEMM take
 // one launch; rows of y at or past an operand's own count do nothing.
 // Whole staging tiles per workgroup of the interior launch, side by side
-// along k: the workgroup reads each operand row's part of them as one run
-// (512 bytes for four) and writes each row block's fragments of them as one
-// run (8 KiB).  Staging both 8192 x 4096 bf16 operands ran 3% faster with
-// two tiles per workgroup and 4% with four (1024 threads, one workgroup per
-// CU) than with one.
-constexpr int kStageStack = 4;
+// along k (interior_stack; four: 1024 threads, one workgroup per CU).
+constexpr int kStageStack = interior_stack(SWZ_READ_MFMA_16X16X32);
 
 template <int GRID>
 constexpr int stage_stack_in() {

@@ -517,6 +517,20 @@ struct StepMoves {
     uint32_t d[kMaxSteps];  // direct HBM -> LDS loads
 };
 
+// Whole tiles per workgroup of the whole-tile (interior) launch, stacked
+// where that lengthens the HBM runs: for the 64 x 64 16-bit transposes two
+// tiles down the source rows, so each output row gets one 256-byte run of
+// the pair; for staging four 256 x 64 K-tiles side by side along k, so each
+// operand row gives a 512-byte run and each row block of fragments an 8 KiB
+// one.  Measured on fp16 8192 x 8192: +4% (4x4 reads) and +3% (transpose
+// reads); staging both 8192 x 4096 operands: +3% with two, +4% with four.
+// Stacking the fp32 and byte tiles lost 5% and 2%, and the 8x8-read 16-bit
+// tile gained under 1%, so they keep one tile per workgroup.  Edge tiles
+// always take a workgroup each.
+constexpr int interior_stack(int kind) {
+    return kind == SWZ_READ_B64_4X4 || kind == SWZ_READ_B64_TR16 ? 2 : kind == SWZ_READ_MFMA_16X16X32 ? 4 : 1;
+}
+
 template <int KIND>
 constexpr bool direct_split() {
     using D = Direct<KIND>;
