@@ -43,6 +43,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -88,12 +89,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src):
+    """C++ source without its comments, trailing blanks and empty lines: what
+    the compiler sees, up to layout.  (The kernel sources hold no string
+    literal with a comment marker in it.)"""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(ln.rstrip() for ln in src.splitlines() if ln.strip())
+
+
 def kernel_sources_digest():
-    """sha256 of the kernel sources the HBM counters in TRAFFIC_FILE were taken on."""
+    """sha256 of the code of the kernel sources (comments aside) that the
+    counter records (TRAFFIC_FILE, CONFLICT_FILE) were taken on."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "tiled_movement_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "tiled_movement_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

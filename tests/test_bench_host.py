@@ -72,3 +72,12 @@ def test_conflicts_reported_only_while_the_kernel_sources_match(tmp_path, monkey
     assert bench.measured_conflicts("bf16_stage") is None
     f.write_text(json.dumps(dict(rec, kernel_sources_sha256="0" * 64)))
     assert bench.measured_conflicts("fp32_transpose") is None
+
+
+def test_source_digest_follows_code_not_comments():
+    """The counter records stay valid across comment edits of the kernel
+    sources and go stale on any change of the code."""
+    src = "int f(int x) {  // one\n  /* two\n three */ return x ^ 3;\n}\n"
+    assert bench.code_text(src) == bench.code_text(src.replace("// one", "// changed").replace("two", "other"))
+    assert bench.code_text(src) == "int f(int x) {\n   return x ^ 3;\n}"
+    assert bench.code_text(src) != bench.code_text(src.replace("x ^ 3", "x ^ 5"))

@@ -17,7 +17,9 @@
 // writes pile onto a few memory channels.  Tiles are therefore visited in
 // diagonal order (consecutive tiles differ in both tile row and tile
 // column), and global loads and stores are non-temporal: every byte is read
-// once and written once.
+// once and written once.  The whole-tile launch of the 64 x 64 16-bit tiles
+// and of staging moves two or four tiles per workgroup, so that the HBM
+// runs are longer (interior_stack).
 #include <tuple>
 #include <type_traits>
 
@@ -29,8 +31,9 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Tiles per launch; larger jobs are launched in chunks, one tile per
-// workgroup (no loop in the kernel, so nothing is kept live across tiles).
+// Workgroups per 1-D launch; larger jobs are launched in chunks.  A
+// workgroup moves its tile (or the interior's stacked tiles) in one round,
+// with no loop in the kernel, so nothing is kept live across tiles.
 constexpr int64_t kMaxGrid = int64_t(1) << 22;
 
 // Cache-policy operand of the direct load for a non-temporal access.
@@ -592,8 +595,8 @@ __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbas
     }
 }
 
-// A workgroup moves one tile and its waves live for one load-store round, so
-// the loads go out first: the lanes' LDS addresses are computed while they
+// A workgroup's waves live for one load-store round of their tile, so the
+// loads go out first: the lanes' LDS addresses are computed while they
 // are in flight.  (An empty asm on a copy of the thread index, ordered after
 // the loads, keeps the compiler from hoisting that arithmetic above them;
 // issuing the loads ahead of it measured 2% faster on the fp32 tile.)
