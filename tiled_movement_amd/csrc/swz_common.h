@@ -524,7 +524,8 @@ struct StepMoves {
 // operand row gives a 512-byte run and each row block of fragments an 8 KiB
 // one.  Measured on fp16 8192 x 8192: +4% (4x4 reads) and +3% (transpose
 // reads); staging both 8192 x 4096 operands: +3% with two, +4% with four.
-// Stacking the fp32 and byte tiles lost 5% and 2%, and the 8x8-read 16-bit
+// Stacking the fp32 and byte tiles lost 5% and 2%, the whole-row tiles of
+// narrow matrices 2% (fp32, fp16) and 8% (bytes), and the 8x8-read 16-bit
 // tile gained under 1%, so they keep one tile per workgroup.  Edge tiles
 // always take a workgroup each.
 constexpr int interior_stack(int kind) {
