@@ -30,7 +30,9 @@
 // products, letting only the lagging waves issue the loads, giving each XCD a
 // contiguous run of tiles and scheduling hints (the compiler's MFMA / LDS
 // interleave strategy, or explicit groups of four products per fragment
-// read) did not help.
+// read) did not help; neither did 32-wide k stages (1.12, also with four
+// stage buffers and loads three stages ahead) or four-wave 128 x 256
+// workgroups, two per CU (1.07).
 #include "gemm_epilogue.h"
 #include "launch.h"
 
