@@ -49,6 +49,7 @@ def direct_shapes(tr, tc, q):
     return [
         (3 * tr, 2 * tc),
         (2 * tr + q, 3 * tc + 3 * q),  # ragged edge tiles both ways
+        (3 * tr + q, 2 * tc + q),  # an odd count of whole tile rows, then a ragged one
         (tr - q, tc + q),
         (q, q),
         (q, 5 * tc + q),
@@ -118,13 +119,14 @@ def test_direct_stage_operand_shapes():
 
 
 def test_direct_stage_operand_any_involutive_swizzle():
-    a, _ = W.bf16_operands(272, 16, 96, seed=19)
+    # k = 320: four whole k tiles in one stacked workgroup, a fifth in the edge launch
+    a, _ = W.bf16_operands(272, 16, 320, seed=19)
     src = to_dev(a)
     ref = O.stage_operand(a).reshape(-1)
     for p in [(0, 3, 1), (3, 3, 3), (3, 3, 4), (4, 3, 4), (2, 4, 7), (5, 3, 6), (1, 3, 1)]:
         announce("direct stage params", p)
         frag = torch.empty(a.size, dtype=src.dtype, device=DEV)
-        T.swz_stage_operand(src, frag, 272, 96, layout="direct", params=p)
+        T.swz_stage_operand(src, frag, 272, 320, layout="direct", params=p)
         torch.cuda.synchronize()
         assert np.array_equal(from_dev(frag, a), ref), p
 

@@ -427,12 +427,13 @@ def test_stage_operand_shapes(layout):
 
 
 def test_stage_operand_any_valid_swizzle():
-    a, _ = W.bf16_operands(272, 16, 96, seed=12)
+    # k = 320: four whole k tiles in one stacked workgroup, a fifth in the edge launch
+    a, _ = W.bf16_operands(272, 16, 320, seed=12)
     src = to_dev(a)
     ref = O.stage_operand(a).reshape(-1)
     for p in [(3, 3, 3), (3, 3, 4), (4, 3, 4), (2, 4, 7), (5, 3, 6), (1, 3, 1)]:
         frag = torch.empty(a.size, dtype=src.dtype, device=DEV)
-        T.swz_stage_operand(src, frag, 272, 96, params=p)
+        T.swz_stage_operand(src, frag, 272, 320, params=p)
         torch.cuda.synchronize()
         assert np.array_equal(from_dev(frag, a), ref), p
 
