@@ -297,7 +297,7 @@ int swz_tune_tile_order(const void* d_src, void* d_dst, int64_t batch, int64_t r
 
 /* GEMM operand staging without compute.  d_src is a K-contiguous operand
  * [mn][k] (A row-major, or B column-major, which is B^T row-major), 16-bit
- * elements.  Tiles of 256 x 64 are loaded coalesced into LDS in the requested
+ * elements.  Tiles of 64 x 64 are loaded coalesced into LDS in the requested
  * layout and read back in the operand-register pattern of the 16x16x32
  * 16-bit matrix instruction: lane l holds row l%16 of a 16-row block and
  * k = 8*(l/16) .. +7 of a 32-wide k step.  Each 64-lane fragment is written
@@ -308,7 +308,7 @@ int swz_tune_tile_order(const void* d_src, void* d_dst, int64_t batch, int64_t r
  * tile ("NVIDIA CuTe Swizzle", on cp.async and ldmatrix; "CuTe Swizzle
  * 学习手册", usage steps 3 and 5).
  *   elem_bytes must be 2; frag_kind must be SWZ_FRAG_MFMA_F32_16X16X32_BF16.
- *   mn must be a multiple of 16 and k of 32 (partial 256x64 tiles are fine).
+ *   mn must be a multiple of 16 and k of 32 (partial 64x64 tiles are fine).
  *   d_src and d_frag must be 16-byte aligned and must not overlap.
  * Errors: SWZ_EINVAL otherwise. */
 int swz_stage_operand(const void* d_src, void* d_frag, int64_t mn, int64_t k, int32_t elem_bytes,

@@ -162,7 +162,7 @@ def test_plans():
     assert T.swz_plan(0, 64, 64, 2, "pad", T.READ_B64_4X4)["lds_bytes"] == 64 * 72 * 2
     assert T.swz_plan(0, 64, 64, 2, "plain", T.READ_B64_4X4)["params"] == (0, 0, 0)
     s = T.swz_plan(1, 8192, 4096, 2)
-    assert s["read_kind"] == T.READ_MFMA_16X16X32 and s["tile"] == (256, 64)
+    assert s["read_kind"] == T.READ_MFMA_16X16X32 and s["tile"] == (64, 64) and s["threads"] == 256
     # tiles per workgroup of the whole-tile launch
     assert s["interior_tiles"] == 4 and p["interior_tiles"] == 1
     assert T.swz_plan(0, 8192, 8192, 2)["interior_tiles"] == 2
@@ -279,15 +279,15 @@ def restated_accesses(kind, write):
                             h = step ^ (g % 2)
                             coords.append((16 * g + 8 * ((q % 4) // 2) + 4 * h + q // 4, 8 * ch + 4 * (q % 2)))
                         out.append((coords, 8))
-        else:  # operand staging, 256x64 tile
+        else:  # operand staging, 64x64 tile: 4 row blocks x 2 k steps of fragments
             if write:
-                for j in range(2048 // nt):
+                for j in range(64 * 8 // nt):
                     coords = [((t + nt * j) // 8, 8 * ((t + nt * j) % 8)) for t in ts]
                     out.append((coords, 16))
             else:
-                for i in range(32 // (nt // 64)):
+                for i in range(8 // (nt // 64)):
                     f = w + (nt // 64) * i
-                    coords = [(16 * (f % 16) + l % 16, 32 * (f // 16) + 8 * (l // 16)) for l in range(64)]
+                    coords = [(16 * (f % 4) + l % 16, 32 * (f // 4) + 8 * (l // 16)) for l in range(64)]
                     out.append((coords, 16))
     return out
 
@@ -296,7 +296,7 @@ KIND_GEOM = {
     T.READ_SCALAR_COL: (4, 32, 32, 1),
     T.READ_B64_4X4: (2, 64, 64, 8),
     T.READ_B128_8X8: (2, 64, 128, 8),
-    T.READ_MFMA_16X16X32: (2, 256, 64, 8),
+    T.READ_MFMA_16X16X32: (2, 64, 64, 8),
     T.READ_B64_TR16: (2, 64, 64, 8),
     T.READ_B64_TR8: (1, 128, 128, 8),
     T.READ_NARROW1: (4, 1024, 1, 1),
@@ -545,7 +545,7 @@ def test_fused_gemm_validation():
     assert f(A, B, C, 1 << 40, 1 << 40, 32, 0, None, None) == EINVAL  # size overflow
     assert f(A, B, C, 32, 32, 32, 7, None, None) == EINVAL  # layout
     assert f(A, B, C, 32, 32, 32, T.LAYOUT_PAD, None, None) == EUNSUP
-    # |S| < B: the direct fill cannot place it; a field leaving the 256x64 tile
+    # |S| < B: the direct fill cannot place it; a field leaving the 64x64 tile
     assert f(A, B, C, 32, 32, 32, 0, ctypes.byref(P(4, 3, 2)), None) == EINVAL
     assert f(A, B, C, 32, 32, 32, 0, ctypes.byref(P(4, 3, -8)), None) == EINVAL
     for layout in (0, T.LAYOUT_PLAIN, T.LAYOUT_SWIZZLE_DIRECT):

@@ -441,7 +441,7 @@ def test_stage_operand_any_valid_swizzle():
 @pytest.mark.parametrize("layout", LAYOUTS + ["direct"])
 def test_stage_operands_pair_in_one_launch(layout):
     """Both operands of a GEMM staged by one call equal each operand's own
-    staging: unequal m and n, partial 256 x 64 tiles, a k tail, and one side
+    staging: unequal m and n, partial 64 x 64 tiles, a k tail, and one side
     empty (then the call stages the other alone)."""
     for m, n, k in [(272, 48, 96), (256, 512, 64), (48, 272, 608), (16, 16, 32), (0, 272, 96), (272, 0, 96)]:
         announce("stage pair", layout, m, n, k)

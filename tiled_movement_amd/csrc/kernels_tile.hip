@@ -223,8 +223,8 @@ FastPath fast_path(int64_t batch, int64_t rows, int64_t cols, int esz, int tr, i
 // that a CU holds at most this many workgroups of the kind (0: no limit).
 // Values from a sweep of the kernels themselves (2 to 8 per CU): 4 for the
 // 64-row 16-bit kinds (+3 to +8%), 5 for the byte kind (+4%); the fp32 tile
-// loses bandwidth when limited, and staging's interior workgroup (four 32 KiB
-// tiles) fills a CU's LDS by itself.
+// loses bandwidth when limited, and staging's interior workgroups (four
+// 8 KiB tiles, 1,024 threads) are held to two per CU by their waves.
 // The byte tiles of 32 and 64 columns (16 KiB) are capped at 4 per CU (4%
 // faster in a sweep of uncapped, 4 and 8); every other whole-row kind lost up
 // to 20% when capped.
@@ -745,12 +745,12 @@ __global__ __launch_bounds__((Kind<KIND>::NT * stack_in<KIND, GRID>())) void k_c
 }
 
 // ---------------------------------------------------------------------------
-// Operand staging: 256x64 K-tiles of a K-contiguous 16-bit operand, read
+// Operand staging: 64x64 K-tiles of a K-contiguous 16-bit operand, read
 // back as 16x16x32 operand fragments and written out in lane order.
 // ---------------------------------------------------------------------------
-// One 256 x 64 tile of a K-contiguous operand (rows r0.., k columns k0..).
+// One 64 x 64 tile of a K-contiguous operand (rows r0.., k columns k0..).
 // A whole tile (FULL) takes src and frag as the tile's own bases (its first
-// element, its first fragment) and addresses its rows and its 16 row blocks
+// element, its first fragment) and addresses its rows and its 4 row blocks
 // of fragments with the 32-bit pitches sp (the operand row, 2k bytes) and fp
 // (one row block of fragments, 32k bytes); an edge tile indexes the whole
 // operand with 64-bit products and guards each 16-byte chunk (mn and k are
@@ -790,7 +790,7 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint
 #pragma unroll
     for (int i = 0; i < K::RSTEPS; ++i) {
         const int f = K::frag_of(t, i);
-        const int blk = f % 16, ks = f / 16;
+        const int blk = f % K::RB, ks = f / K::RB;
         const u32x4 x = *reinterpret_cast<const u32x4*>(lds + 2 * step_off<false, PADDED>(rbase, i, mv));
         if constexpr (FULL) {
             gstore16(frag + (static_cast<uint64_t>(static_cast<uint32_t>(blk)) * fp +
@@ -810,7 +810,7 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ src, uint
 // full_m2 whole row tiles) as grid z = 1, so both operands of a GEMM take
 // one launch; rows of y at or past an operand's own count do nothing.
 // Whole staging tiles per workgroup of the interior launch, side by side
-// along k (interior_stack; four: 1024 threads, one workgroup per CU).
+// along k (interior_stack; four: 1024 threads, 32 KiB of LDS).
 constexpr int kStageStack = interior_stack(SWZ_READ_MFMA_16X16X32);
 
 template <int GRID>
@@ -833,8 +833,8 @@ __global__ __launch_bounds__((Kind<SWZ_READ_MFMA_16X16X32>::NT * stage_stack_in<
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v + g * TILE_V);
     const int t = STACK == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) & (K::NT - 1);
 
-    // the tile's first element (row 256 tm, k 64 tk) and first fragment (row
-    // block 16 tm, k step 2 tk)
+    // the tile's first element (row TR tm, k 64 tk) and first fragment (row
+    // block TR/16 tm, k step 2 tk)
     auto whole = [&](const uint8_t* s, uint8_t* f, uint32_t tm, uint32_t tk) {
         const uint32_t r0 = tm * K::TR, kb0 = tk * K::TC;
         stage_tile<FILL, true>(s + (static_cast<uint64_t>(r0) * sp + 2 * kb0),

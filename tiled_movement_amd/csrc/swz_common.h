@@ -125,18 +125,22 @@ template <> struct Kind<SWZ_READ_B128_8X8> {
     }
 };
 
-// Operand staging: 2-byte elements, 256x64 tile (256 rows of the MN
-// dimension, 64 of K; 128-byte rows).  Staging: vector v = t + NT*j is row
-// v/8, chunk v%8.  Read: the 32 fragments of the tile (16 row blocks x 2 k
-// steps); wave w reads fragments f = w + (NT/64)*i; lane l of fragment f
-// reads row 16*(f%16) + l%16, k = 32*(f/16) + 8*(l/16) .. +7.
+// Operand staging: 2-byte elements, 64x64 tile (64 rows of the MN
+// dimension, 64 of K; 128-byte rows), 256 threads: two 16-byte loads per
+// thread.  (256 x 64 tiles with four loads per thread, and 128- or 32-row
+// tiles, staged both 8192 x 4096 operands 2-8% slower, stacked four along k
+// as these are.)  Staging: vector v = t + NT*j is row v/8, chunk v%8.  Read:
+// the 8 fragments of the tile (RB = 4 row blocks x 2 k steps); wave w reads
+// fragments f = w + (NT/64)*i; lane l of fragment f reads row
+// 16*(f%RB) + l%16, k = 32*(f/RB) + 8*(l/16) .. +7.
 template <> struct Kind<SWZ_READ_MFMA_16X16X32> {
-    static constexpr int ESZ = 2, TR = 256, TC = 64, NT = 256;
+    static constexpr int ESZ = 2, TR = 64, TC = 64, NT = 256;
     static constexpr int VEC = 16;
     static constexpr int RWIDTH = 16;
+    static constexpr int RB = TR / 16;  // row blocks of 16 rows
     static constexpr int GLOADS = TR * TC * ESZ / 16 / NT;
     static constexpr int WSTEPS = GLOADS;
-    static constexpr int RSTEPS = 32 / (NT / 64);  // fragments per wave
+    static constexpr int RSTEPS = RB * (TC / 32) / (NT / 64);  // fragments per wave
     __host__ __device__ static constexpr int frag_of(int t, int i) { return (t / 64) + (NT / 64) * i; }
     __host__ __device__ static constexpr void wcoord(int t, int i, int& r, int& c) {
         const int v = t + NT * i;
@@ -145,8 +149,8 @@ template <> struct Kind<SWZ_READ_MFMA_16X16X32> {
     }
     __host__ __device__ static constexpr void rcoord(int t, int i, int& r, int& c) {
         const int f = frag_of(t, i), l = t % 64;
-        r = 16 * (f % 16) + l % 16;
-        c = 32 * (f / 16) + 8 * (l / 16);
+        r = 16 * (f % RB) + l % 16;
+        c = 32 * (f / RB) + 8 * (l / 16);
     }
 };
 
@@ -425,7 +429,9 @@ static_assert(even_split<SWZ_READ_B64_4X4>() && Kind<SWZ_READ_B64_4X4>::TASKS * 
               "4x4 thread count");
 static_assert(even_split<SWZ_READ_B128_8X8>() && Kind<SWZ_READ_B128_8X8>::TASKS * Kind<SWZ_READ_B128_8X8>::NT == 128,
               "8x8 thread count");
-static_assert(even_split<SWZ_READ_MFMA_16X16X32>() && Kind<SWZ_READ_MFMA_16X16X32>::RSTEPS * (Kind<SWZ_READ_MFMA_16X16X32>::NT / 64) == 32,
+static_assert(even_split<SWZ_READ_MFMA_16X16X32>() &&
+                  Kind<SWZ_READ_MFMA_16X16X32>::RSTEPS * (Kind<SWZ_READ_MFMA_16X16X32>::NT / 64) ==
+                      Kind<SWZ_READ_MFMA_16X16X32>::RB * 2,
               "fragment thread count");
 
 static_assert(steps_decompose<SWZ_READ_SCALAR_COL, true>() && steps_decompose<SWZ_READ_SCALAR_COL, false>(),
@@ -520,10 +526,11 @@ struct StepMoves {
 // Whole tiles per workgroup of the whole-tile (interior) launch, stacked
 // where that lengthens the HBM runs: for the 64 x 64 16-bit transposes two
 // tiles down the source rows, so each output row gets one 256-byte run of
-// the pair; for staging four 256 x 64 K-tiles side by side along k, so each
+// the pair; for staging four 64 x 64 K-tiles side by side along k, so each
 // operand row gives a 512-byte run and each row block of fragments an 8 KiB
 // one.  Measured on fp16 8192 x 8192: +4% (4x4 reads) and +3% (transpose
-// reads); staging both 8192 x 4096 operands: +3% with two, +4% with four.
+// reads); staging both 8192 x 4096 operands (then in 256 x 64 tiles): +3%
+// with two, +4% with four.
 // Stacking the fp32 and byte tiles lost 5% and 2%, the whole-row tiles of
 // narrow matrices 2% (fp32, fp16) and 8% (bytes), and the 8x8-read 16-bit
 // tile gained under 1%, so they keep one tile per workgroup.  Edge tiles
