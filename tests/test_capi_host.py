@@ -164,7 +164,7 @@ def test_plans():
     s = T.swz_plan(1, 8192, 4096, 2)
     assert s["read_kind"] == T.READ_MFMA_16X16X32 and s["tile"] == (64, 64) and s["threads"] == 256
     # tiles per workgroup of the whole-tile launch
-    assert s["interior_tiles"] == 4 and p["interior_tiles"] == 1
+    assert s["interior_tiles"] == 4 and p["interior_tiles"] == 4  # staging: 4 along k; fp32: 2 x 2
     assert T.swz_plan(0, 8192, 8192, 2)["interior_tiles"] == 2
     assert T.swz_plan(0, 4096, 128, 2)["interior_tiles"] == 1
     assert T.swz_plan(0, 64, 64, 2, "swizzle", T.READ_B64_4X4, (3, 3, 6))["params"] == (3, 3, 6)

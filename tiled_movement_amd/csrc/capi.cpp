@@ -122,7 +122,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     out->vec_bytes = layout == SWZ_LAYOUT_SWIZZLE_DIRECT ? (k.esz == 2 ? 16 : 4) : k.vec;
     out->aligned = aligned ? 1 : 0;
     out->threads = k.nt;
-    out->interior_tiles = swz::interior_stack(kind);
+    out->interior_tiles = swz::interior_stack(kind) * swz::interior_stack_cols(kind);
     (void)rows;
     return SWZ_OK;
 }

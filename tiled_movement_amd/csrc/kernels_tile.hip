@@ -236,11 +236,15 @@ constexpr int occupancy_limit() {
                                                                         : 0;
 }
 
-// Whole tiles per workgroup of a transpose's interior launch, one after
-// another down the source rows (interior_stack).
+// Whole tiles per workgroup of a transpose's interior launch: stack_of()
+// down the source rows times stack_c_of() along them (interior_stack).
 template <int KIND>
 constexpr int stack_of() {
     return interior_stack(KIND);
+}
+template <int KIND>
+constexpr int stack_c_of() {
+    return interior_stack_cols(KIND);
 }
 
 // Workgroups per CU of the interior launch (0: no limit): as many tiles in
@@ -248,7 +252,7 @@ constexpr int stack_of() {
 // 16-bit workgroups per CU found 2 and 3 alike, 4 slower).
 template <int KIND>
 constexpr int interior_occupancy_limit() {
-    return occupancy_limit<KIND>() / stack_of<KIND>();
+    return occupancy_limit<KIND>() / (stack_of<KIND>() * stack_c_of<KIND>());
 }
 
 constexpr int kLdsPerCu = 160 * 1024;
@@ -376,9 +380,11 @@ __device__ __forceinline__ void load_tile(const TileIo<EDGE, Kind<KIND>::ESZ>& i
     }
 }
 
+// t: the thread's index within its tile (a stacked workgroup runs several
+// tiles, each on its own NT threads).
 template <int KIND, bool PADDED>
 __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const KLayout& L, const StepMoves& mv,
-                                          const u32x4* v) {
+                                          const u32x4* v, int t) {
     using K = Kind<KIND>;
     if constexpr (K::VEC == 4 && K::ESZ < 4) {
         // Narrow rows of 2- or 1-byte elements: 4-byte runs (M >= 1 resp. 2
@@ -386,7 +392,6 @@ __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const KL
         // s = bits 3-4 of the lane for the wide rows (SWAP, lane map in
         // swz_common.h), picked with two 2-way selects.  Those steps combine
         // by XOR only, so padded rows compute each step's row and column.
-        const int t = threadIdx.x;
         const bool sw1 = K::SWAP && ((t >> 3) & 1), sw2 = K::SWAP && ((t >> 4) & 1);
 #pragma unroll
         for (int j = 0; j < K::GLOADS; ++j) {
@@ -417,7 +422,6 @@ __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const KL
         // runs); step 2j + h writes half h ^ (row % 2) (lane map in
         // swz_common.h).  The steps combine by XOR only, so padded rows
         // compute each step's row and column.
-        const int t = threadIdx.x;
 #pragma unroll
         for (int j = 0; j < K::GLOADS; ++j) {
 #pragma unroll
@@ -619,7 +623,7 @@ __device__ __forceinline__ void convert_tile(const TileIo<EDGE, Kind<KIND>::ESZ>
         u32x4 v[K::GLOADS];
         load_tile<KIND, EDGE>(io, t, v);
         ta = after_loads(t);
-        lds_store<KIND, PADDED>(lds, lane_base<KIND, true, PADDED>(ta, L), L, mv, v);
+        lds_store<KIND, PADDED>(lds, lane_base<KIND, true, PADDED>(ta, L), L, mv, v, ta);
     }
     const uint32_t rbase = lane_base<KIND, false, PADDED>(ta, L);
     __syncthreads();
@@ -673,7 +677,7 @@ __device__ __forceinline__ void edge_tile(int64_t e, int64_t full_r, int64_t ful
 // SGPRs) are all a whole tile of a 3-D launch reads before its first load.
 template <int KIND, int GRID>
 constexpr int stack_in() {
-    return GRID == kInterior ? stack_of<KIND>() : 1;
+    return GRID == kInterior ? stack_of<KIND>() * stack_c_of<KIND>() : 1;
 }
 
 template <int KIND, int FILL, bool ALIGNED, int GRID>
@@ -716,7 +720,9 @@ __global__ __launch_bounds__((Kind<KIND>::NT * stack_in<KIND, GRID>())) void k_c
     };
 
     if constexpr (GRID == kInterior) {
-        whole(blockIdx.z, blockIdx.x * STACK + g, diagonal_column(tiles_c32, O));
+        // tile g of the workgroup's SR x SC block (tiles_c32: blocks per row)
+        constexpr int SR = stack_of<KIND>(), SC = stack_c_of<KIND>();
+        whole(blockIdx.z, blockIdx.x * SR + g % SR, diagonal_column(tiles_c32, O) * SC + g / SR);
     } else if constexpr (GRID == kEdge) {
         const int64_t tiles_c = (cols + K::TC - 1) / K::TC;
         const int64_t per = edge_tiles(full_r, full_c, tiles_r, tiles_c);
@@ -917,29 +923,29 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
     const KLayout kl = decode_layout(j.layout);
     const unsigned lds_pad = occupancy_pad<KIND>(LdsTile<KIND, FILL>::BYTES);
     const dim3 block(K::NT);
-    auto args = [&](uint32_t cols_of_order, int64_t tile0, uint32_t full_r) {
-        return std::make_tuple(s, d, cols_of_order, O.num, O.sh, fp.sp, fp.dp, full_r, fp.full_c, r32, c32, j.rows,
+    auto args = [&](uint32_t cols_of_order, int64_t tile0, uint32_t full_r, uint32_t full_c) {
+        return std::make_tuple(s, d, cols_of_order, O.num, O.sh, fp.sp, fp.dp, full_r, full_c, r32, c32, j.rows,
                                j.cols, tiles_r, tile0, kl, mv);
     };
     if constexpr (ALIGNED) {
-        // the interior covers the whole tile rows in groups of STACK; the
-        // rows past the last group join the edge strips
-        constexpr int STACK = stack_of<KIND>();
-        const uint32_t inner_r = fp.full_r / STACK * STACK;
-        if (inner_r > 0 && fp.full_c > 0 && fits_3d(inner_r / STACK, fp.full_c, j.batch, K::NT * STACK)) {
+        // the interior covers the whole tiles in blocks of SR x SC; the
+        // whole rows and columns past the last block join the edge strips
+        constexpr int SR = stack_of<KIND>(), SC = stack_c_of<KIND>();
+        const uint32_t inner_r = fp.full_r / SR * SR, inner_c = fp.full_c / SC * SC;
+        if (inner_r > 0 && inner_c > 0 && fits_3d(inner_r / SR, inner_c / SC, j.batch, K::NT * SR * SC)) {
             const unsigned inner_pad =
-                occupancy_pad_to(STACK * LdsTile<KIND, FILL>::BYTES, interior_occupancy_limit<KIND>());
+                occupancy_pad_to(SR * SC * LdsTile<KIND, FILL>::BYTES, interior_occupancy_limit<KIND>());
             std::apply([&](auto... a) {
                 hipLaunchKernelGGL((k_convert<KIND, FILL, true, kInterior>),
-                                   dim3(inner_r / STACK, fp.full_c, static_cast<unsigned>(j.batch)),
-                                   dim3(K::NT * STACK), inner_pad, stream, a...);
-            }, args(fp.full_c, 0, inner_r));
-            const int64_t per = edge_tiles(inner_r, fp.full_c, tiles_r, tiles_c);
+                                   dim3(inner_r / SR, inner_c / SC, static_cast<unsigned>(j.batch)),
+                                   dim3(K::NT * SR * SC), inner_pad, stream, a...);
+            }, args(inner_c / SC, 0, inner_r, inner_c));
+            const int64_t per = edge_tiles(inner_r, inner_c, tiles_r, tiles_c);
             launch_chunks(j.batch * per, [&](int64_t t0, int64_t n) {
                 std::apply([&](auto... a) {
                     hipLaunchKernelGGL((k_convert<KIND, FILL, true, kEdge>), dim3(static_cast<unsigned>(n)), block,
                                        lds_pad, stream, a...);
-                }, args(static_cast<uint32_t>(tiles_c), t0, inner_r));
+                }, args(static_cast<uint32_t>(tiles_c), t0, inner_r, inner_c));
             });
             return;
         }
@@ -950,7 +956,7 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
                                    dim3(static_cast<unsigned>(tiles_r), static_cast<unsigned>(tiles_c),
                                         static_cast<unsigned>(j.batch)),
                                    block, lds_pad, stream, a...);
-            }, args(static_cast<uint32_t>(tiles_c), 0, fp.full_r));
+            }, args(static_cast<uint32_t>(tiles_c), 0, fp.full_r, fp.full_c));
             return;
         }
     }
@@ -958,7 +964,7 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
         std::apply([&](auto... a) {
             hipLaunchKernelGGL((k_convert<KIND, FILL, ALIGNED, kAll1D>), dim3(static_cast<unsigned>(n)), block, lds_pad,
                                stream, a...);
-        }, args(static_cast<uint32_t>(tiles_c), t0, fp.full_r));
+        }, args(static_cast<uint32_t>(tiles_c), t0, fp.full_r, fp.full_c));
     });
 }
 

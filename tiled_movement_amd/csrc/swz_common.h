@@ -524,19 +524,29 @@ struct StepMoves {
 };
 
 // Whole tiles per workgroup of the whole-tile (interior) launch, stacked
-// where that lengthens the HBM runs: for the 64 x 64 16-bit transposes two
-// tiles down the source rows, so each output row gets one 256-byte run of
-// the pair; for staging four 64 x 64 K-tiles side by side along k, so each
-// operand row gives a 512-byte run and each row block of fragments an 8 KiB
-// one.  Measured on fp16 8192 x 8192: +4% (4x4 reads) and +3% (transpose
-// reads); staging both 8192 x 4096 operands (then in 256 x 64 tiles): +3%
-// with two, +4% with four.
-// Stacking the fp32 and byte tiles lost 5% and 2%, the whole-row tiles of
-// narrow matrices 2% (fp32, fp16) and 8% (bytes), and the 8x8-read 16-bit
-// tile gained under 1%, so they keep one tile per workgroup.  Edge tiles
-// always take a workgroup each.
+// where that lengthens the HBM runs or keeps more requests in flight:
+// interior_stack tiles down the source rows times interior_stack_cols tiles
+// along them.  The 64 x 64 16-bit transposes take two tiles down the rows, so
+// each output row gets one 256-byte run of the pair; the fp32 32 x 32
+// transpose takes 2 x 2 tiles (1,024 threads: 256-byte runs on both sides);
+// staging takes four 64 x 64 K-tiles side by side along k (its k runs along
+// the rows of the operand), so each operand row gives a 512-byte run and
+// each row block of fragments an 8 KiB one.  Measured on fp16 8192 x 8192:
+// +4% (4x4 reads) and +3% (transpose reads); fp32 4096 x 4096: +1.5-2% with
+// 2 x 2, -5% with two down the rows, -7% with two along them; staging both
+// 8192 x 4096 operands (then in 256 x 64 tiles): +3% with two, +4% with
+// four.  The byte tile lost 2% (rows) to 10% (2 x 2), the whole-row tiles
+// of narrow matrices 2% (fp32, fp16) and 8% (bytes), and the 8x8-read 16-bit
+// tile gained under 1% down the rows and lost 2% in 2 x 2, so they keep one
+// tile per workgroup.  Edge tiles always take a workgroup each.
 constexpr int interior_stack(int kind) {
-    return kind == SWZ_READ_B64_4X4 || kind == SWZ_READ_B64_TR16 ? 2 : kind == SWZ_READ_MFMA_16X16X32 ? 4 : 1;
+    return kind == SWZ_READ_B64_4X4 || kind == SWZ_READ_B64_TR16 || kind == SWZ_READ_SCALAR_COL ? 2
+           : kind == SWZ_READ_MFMA_16X16X32                                                       ? 4
+                                                                                                   : 1;
+}
+
+constexpr int interior_stack_cols(int kind) {
+    return kind == SWZ_READ_SCALAR_COL ? 2 : 1;
 }
 
 template <int KIND>
