@@ -631,10 +631,12 @@ __device__ __forceinline__ void convert_tile(const TileIo<EDGE, Kind<KIND>::ESZ>
 }
 
 // Which tiles a launch covers and how blockIdx names them.
-//   kInterior: a 3-D grid (tile row, tile column step, batch entry) over the
-//              whole tiles only, in diagonal order; no edge test at all.
-//   kEdge:     a 1-D chunk of the edge tiles (the last tile column and the
-//              last tile row of each batch entry, where they stick out).
+//   kInterior: a 3-D grid (block row, block column step, batch entry) over
+//              whole tiles only, in blocks of stack_of() x stack_c_of()
+//              tiles per workgroup, in diagonal order; no edge test at all.
+//   kEdge:     a 1-D chunk of the edge tiles (the tile columns and rows of
+//              each batch entry past the interior's blocks: whole tiles that
+//              did not fill a block, and those that stick out).
 //   kAll3D / kAll1D: every tile, 3-D as kInterior or a 1-D chunk of the
 //              linear tile order (grids beyond the hardware's y / z limits,
 //              sizes past the 32-bit whole-tile path, unaligned pitches).
