@@ -95,6 +95,8 @@ def test_direct_convert_batches():
         (T.READ_B128_8X8, 2, W.bf16_tensor((2, 64, 96), seed=16)),
         (T.READ_B64_4X4, 2, W.bf16_tensor((2, 72, 136), seed=17)),
         (T.READ_SCALAR_COL, 4, W.fp32_matrix(3 * 40, 52, seed=18).reshape(3, 40, 52)),
+        # 2 x 2 stacked fp32 blocks with a whole tile row and column left over
+        (T.READ_SCALAR_COL, 4, W.fp32_matrix(2 * 100, 104, seed=24).reshape(2, 100, 104)),
     ]
     for kind, esz, a in cases:
         announce("direct convert", kind, a.shape)

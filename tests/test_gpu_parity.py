@@ -229,6 +229,12 @@ def test_convert_layout_batches():
         (T.READ_B64_TR16, 2, W.bf16_tensor((2, 70, 130), seed=10)),
         (T.READ_B64_TR8, 1, W.u8_matrix(3 * 130, 200, seed=11).reshape(3, 130, 200)),
         (T.READ_SCALAR_COL, 4, W.fp32_matrix(3 * 40, 50, seed=8).reshape(3, 40, 50)),
+        # stacked whole-tile blocks per batch entry: 2 x 2 fp32 tiles with a whole tile row and
+        # a whole tile column left over, and two 16-bit tiles down the rows with one left over
+        (T.READ_SCALAR_COL, 4, W.fp32_matrix(2 * 100, 100, seed=20).reshape(2, 100, 100)),
+        (T.READ_SCALAR_COL, 4, W.fp32_matrix(3 * 96, 136, seed=21).reshape(3, 96, 136)),
+        (T.READ_B64_4X4, 2, W.bf16_tensor((3, 200, 136), seed=22)),
+        (T.READ_B64_TR16, 2, W.bf16_tensor((2, 192, 264), seed=23)),
     ]
     for kind, esz, a in cases:
         for layout in LAYOUTS:
