@@ -123,6 +123,9 @@ def test_convert_validation():
     assert f(A, B, 1 << 40, 1 << 20, 1 << 20, 4, 0, -1, None, None) == EINVAL  # size overflow
     for shape in [(0, 64, 64), (3, 0, 64), (3, 64, 0)]:
         assert f(A, B, *shape, 4, 0, -1, None, None) == T.SWZ_OK  # empty: no launch
+    # an empty batch with rows whose byte pitch exceeds int64: checked without overflow
+    assert f(A, B, 0, (1 << 63) - 1, 8, 4, 0, -1, None, None) == T.SWZ_OK
+    assert f(A, B, 0, 8, (1 << 63) - 1, 4, 0, T.READ_SCALAR_COL, None, None) == T.SWZ_OK
     assert lib.swz_transpose(A, B, 64, 64, 8, 0, -1, None, None) == EINVAL
 
 

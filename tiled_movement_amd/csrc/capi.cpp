@@ -28,6 +28,10 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
     return pa < pb + static_cast<uintptr_t>(bbytes) && pb < pa + static_cast<uintptr_t>(abytes);
 }
 
+// Whether n elements of esz bytes make a whole number of 16-byte vectors;
+// unsigned, so that a huge n wraps instead of overflowing (16 divides 2^64).
+bool pitch16(int64_t n, int32_t esz) { return (static_cast<uint64_t>(n) * static_cast<uint64_t>(esz)) % 16 == 0; }
+
 int ilog2(int64_t v) {
     int r = -1;
     while (v > 0) {
@@ -209,8 +213,8 @@ SWZ_API int swz_plan(int32_t op, int64_t rows, int64_t cols, int32_t elem_bytes,
     if (!out || (op != 0 && op != 1) || rows < 0 || cols < 0) return SWZ_EINVAL;
     if (op == 1 && (rows % 16 || cols % 32)) return SWZ_EINVAL;
     // Pointers are taken as 16-byte aligned; the row pitches decide the rest.
-    return make_plan(op, rows, cols, elem_bytes, layout, read_kind, p_or_null, op == 1 || (rows * elem_bytes) % 16 == 0,
-                     op == 1 || (cols * elem_bytes) % 16 == 0, out);
+    return make_plan(op, rows, cols, elem_bytes, layout, read_kind, p_or_null,
+                     op == 1 || pitch16(rows, elem_bytes), op == 1 || pitch16(cols, elem_bytes), out);
 }
 
 SWZ_API int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, int64_t rows, int64_t cols,
@@ -223,8 +227,7 @@ SWZ_API int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, in
     const auto ps = reinterpret_cast<uintptr_t>(d_src), pd = reinterpret_cast<uintptr_t>(d_dst);
     swz_plan_info pl;
     const int st = make_plan(0, rows, cols, elem_bytes, layout, read_kind, p_or_null,
-                             ps % 16 == 0 && pd % 16 == 0 && (rows * elem_bytes) % 16 == 0,
-                             (cols * elem_bytes) % 16 == 0, &pl);
+                             ps % 16 == 0 && pd % 16 == 0 && pitch16(rows, elem_bytes), pitch16(cols, elem_bytes), &pl);
     if (st != SWZ_OK) return st;
     if (bytes == 0) return SWZ_OK;
     if (!d_src || !d_dst) return SWZ_EINVAL;
