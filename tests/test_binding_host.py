@@ -1,7 +1,8 @@
 """Host checks of the Python binding's buffer validation (no GPU): every
 wrapper rejects, before calling the library, a tensor that is not on a CUDA
 device, not contiguous, on another device than the call's other buffers, or
-too small for the bytes the call reads or writes there."""
+too small for the bytes the call reads or writes there, or on a device
+other than the current one."""
 
 import pytest
 import torch
@@ -76,3 +77,9 @@ def test_gemm_buffers_are_sized_from_m_n_k_and_the_result_type():
         T.swz_gemm_ex(a, bt, FakeCuda(2 * 64 * 48 - 2, esz=2), 64, 48, 32, c_type=T.C_BF16)
     with pytest.raises(ValueError, match="fb holds"):
         T.swz_gemm_frag(FakeCuda(2 * 64 * 32), FakeCuda(10), FakeCuda(4 * 64 * 48), 64, 48, 32)
+
+
+def test_buffers_off_the_current_device_are_rejected(monkeypatch):
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    with pytest.raises(ValueError, match="current device is cuda:0"):
+        T.swz_transpose(FakeCuda(16384, device="cuda:1"), FakeCuda(16384, device="cuda:1"), 64, 64, 4)

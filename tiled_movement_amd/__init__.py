@@ -172,8 +172,8 @@ def _ptr(x) -> Optional[int]:
 
 def _buf(call: str, **bufs) -> None:
     """Check the device buffers of one call before it reaches the library:
-    every tensor is a contiguous CUDA tensor, all on one device, and holds at
-    least the bytes the call reads or writes there (name=(tensor, bytes)).
+    every tensor is a contiguous CUDA tensor, all on the current device, and
+    holds at least the bytes the call reads or writes there (name=(tensor, bytes)).
     Raw integer addresses and None pass unchecked (the library checks what
     it can: NULL, alignment, overlap).  Raises ValueError."""
     device = None
@@ -192,6 +192,14 @@ def _buf(call: str, **bufs) -> None:
         have = t.numel() * t.element_size()
         if have < max(int(need), 0):
             raise ValueError(f"{call}: {name} holds {have} bytes, the call needs {int(need)}")
+    if device is not None and device.index is not None:
+        import torch
+
+        # the library launches on, and creates its events on, the current device
+        cur = torch.cuda.current_device()
+        if device.index != cur:
+            raise ValueError(f"{call}: the buffers are on {device}, the current device is cuda:{cur} "
+                             f"(call inside torch.cuda.device({device.index}))")
 
 
 def _stream(stream, *tensors):
