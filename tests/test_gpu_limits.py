@@ -35,6 +35,25 @@ def test_transpose_with_more_tile_columns_than_a_grid_dimension():
         assert np.array_equal(dst.cpu().numpy().view(np.uint32), O.transpose(a))
 
 
+def test_transpose_whose_tile_blocks_overflow_a_grid_dimension():
+    """16-bit rows of 65,536 tiles of 64 (the last one partial): the blocks
+    of the one-launch grid would need 65,536 workgroups along y, so the
+    whole tiles go through the interior launch and the partial column
+    through the 1-D edge launch."""
+    rows, cols = 128, 64 * 65535 + 8
+    a = W.fp16_matrix(rows, cols, seed=41)
+    want = O.transpose(a)
+    for layout in ("swizzle", "direct"):
+        announce("wide 16-bit transpose", layout, rows, cols)
+        src = torch.from_numpy(a.view(np.int16)).to(DEV)
+        dst = torch.empty((cols, rows), dtype=torch.int16, device=DEV)
+        T.swz_transpose(src, dst, rows, cols, 2, layout)
+        torch.cuda.synchronize()
+        assert np.array_equal(dst.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def test_batch_beyond_grid_limit_and_more_than_2_22_tiles():
     """65,537 batch entries of 256 x 256 fp32 = 4,194,368 tiles of 32 x 32:
     a batch beyond the 65,535 grid limit and one tile chunk past 2^22."""

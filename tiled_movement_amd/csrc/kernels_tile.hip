@@ -637,10 +637,16 @@ __device__ __forceinline__ void convert_tile(const TileIo<EDGE, Kind<KIND>::ESZ>
 //   kEdge:     a 1-D chunk of the edge tiles (the tile columns and rows of
 //              each batch entry past the interior's blocks: whole tiles that
 //              did not fill a block, and those that stick out).
+//   kBlocks:   every tile of aligned rows in one 3-D launch of blocks of
+//              stack_of() x stack_c_of() tiles, as kInterior: a tile of the
+//              block that is whole takes the unguarded path, one that sticks
+//              out the guarded path, and one past the matrix only the barrier.
+//              It replaces kInterior + kEdge where the rows leave edge tiles,
+//              so that those cost no launch of their own.
 //   kAll3D / kAll1D: every tile, 3-D as kInterior or a 1-D chunk of the
 //              linear tile order (grids beyond the hardware's y / z limits,
 //              sizes past the 32-bit whole-tile path, unaligned pitches).
-enum Grid { kAll3D = 0, kAll1D = 1, kInterior = 2, kEdge = 3 };
+enum Grid { kAll3D = 0, kAll1D = 1, kInterior = 2, kEdge = 3, kBlocks = 4 };
 
 // Tile (tr, tc) of a 3-D diagonal-order grid with n tile columns: tc = (y +
 // f) mod n, f = (x num) >> sh, y < n.  One conditional subtract, and a
@@ -679,7 +685,7 @@ __device__ __forceinline__ void edge_tile(int64_t e, int64_t full_r, int64_t ful
 // SGPRs) are all a whole tile of a 3-D launch reads before its first load.
 template <int KIND, int GRID>
 constexpr int stack_in() {
-    return GRID == kInterior ? stack_of<KIND>() * stack_c_of<KIND>() : 1;
+    return GRID == kInterior || GRID == kBlocks ? stack_of<KIND>() * stack_c_of<KIND>() : 1;
 }
 
 template <int KIND, int FILL, bool ALIGNED, int GRID>
@@ -725,6 +731,21 @@ __global__ __launch_bounds__((Kind<KIND>::NT * stack_in<KIND, GRID>())) void k_c
         // tile g of the workgroup's SR x SC block (tiles_c32: blocks per row)
         constexpr int SR = stack_of<KIND>(), SC = stack_c_of<KIND>();
         whole(blockIdx.z, blockIdx.x * SR + g % SR, diagonal_column(tiles_c32, O) * SC + g / SR);
+    } else if constexpr (GRID == kBlocks) {
+        // As kInterior over blocks that may reach past the whole tiles
+        // (tiles_c32: blocks per row, rounded up).  The tile test is uniform
+        // across each wave (readfirstlane of g), so every wave branches as a
+        // whole and runs exactly one barrier: its tile's, or its own where
+        // the block reaches past the matrix.
+        constexpr int SR = stack_of<KIND>(), SC = stack_c_of<KIND>();
+        const uint32_t gu = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(g));
+        const uint32_t tr = blockIdx.x * SR + gu % SR, tc = diagonal_column(tiles_c32, O) * SC + gu / SR;
+        if (tr < full_r && tc < full_c)
+            whole(blockIdx.z, tr, tc);
+        else if (tr < tiles_r && tc < (cols + K::TC - 1) / K::TC)
+            guarded(blockIdx.z, tr, tc);
+        else
+            __syncthreads();
     } else if constexpr (GRID == kEdge) {
         const int64_t tiles_c = (cols + K::TC - 1) / K::TC;
         const int64_t per = edge_tiles(full_r, full_c, tiles_r, tiles_c);
@@ -934,9 +955,21 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
         // whole rows and columns past the last block join the edge strips
         constexpr int SR = stack_of<KIND>(), SC = stack_c_of<KIND>();
         const uint32_t inner_r = fp.full_r / SR * SR, inner_c = fp.full_c / SC * SC;
+        const unsigned inner_pad =
+            occupancy_pad_to(SR * SC * LdsTile<KIND, FILL>::BYTES, interior_occupancy_limit<KIND>());
+        const int64_t blocks_r = ceil_div(tiles_r, SR), blocks_c = ceil_div(tiles_c, SC);
+        if ((inner_r != tiles_r || inner_c != tiles_c) && fp.full_r > 0 && fp.full_c > 0 &&
+            fits_3d(blocks_r, blocks_c, j.batch, K::NT * SR * SC)) {
+            // edge tiles: all tiles in one launch of blocks
+            std::apply([&](auto... a) {
+                hipLaunchKernelGGL((k_convert<KIND, FILL, true, kBlocks>),
+                                   dim3(static_cast<unsigned>(blocks_r), static_cast<unsigned>(blocks_c),
+                                        static_cast<unsigned>(j.batch)),
+                                   dim3(K::NT * SR * SC), inner_pad, stream, a...);
+            }, args(static_cast<uint32_t>(blocks_c), 0, fp.full_r, fp.full_c));
+            return;
+        }
         if (inner_r > 0 && inner_c > 0 && fits_3d(inner_r / SR, inner_c / SC, j.batch, K::NT * SR * SC)) {
-            const unsigned inner_pad =
-                occupancy_pad_to(SR * SC * LdsTile<KIND, FILL>::BYTES, interior_occupancy_limit<KIND>());
             std::apply([&](auto... a) {
                 hipLaunchKernelGGL((k_convert<KIND, FILL, true, kInterior>),
                                    dim3(inner_r / SR, inner_c / SC, static_cast<unsigned>(j.batch)),
