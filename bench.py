@@ -29,6 +29,9 @@ Usage:
       time every tile order of the transposes on matrices of one size and
       several shapes, and what swz_tune_tile_order picks for each (a table on
       stdout instead of the JSON line)
+  python bench.py --order-shapes [--elem-bytes 4 2]
+      every tile order and the shape's default order on matrices of 32 to
+      512 MiB with sides from 1,024 to 16,384, as shares of a copy (a table)
 
 Timing: warm-up steps, then a short spin kernel on the launch stream before
 the start event, so the host has queued the first launches by the time the
@@ -522,7 +525,8 @@ def tile_order_sweep(elem_bytes, mib):
     import tiled_movement_amd as T
 
     orders = {T.ORDER_DIAGONAL: "diagonal", T.ORDER_HALF_DIAGONAL: "half", T.ORDER_COLUMNS: "columns",
-              T.ORDER_STEEP_DIAGONAL: "steep"}
+              T.ORDER_STEEP_DIAGONAL: "steep", T.ORDER_SLOPE_8: "1/8", T.ORDER_SLOPE_16: "1/16",
+              T.ORDER_SLOPE_32: "1/32"}
     pairs, nbytes = 4, mib << 20
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -564,6 +568,75 @@ def tile_order_sweep(elem_bytes, mib):
     return lines
 
 
+ORDER_SHAPE_DIMS = (1024, 1536, 2048, 2560, 2944, 3072, 3584, 3968, 4096, 4160, 4608, 5120, 5760, 6144, 6656, 7168,
+                    8128, 8192, 9216, 10240, 12288, 14336, 16384)
+
+
+def order_shape_sweep(elem_bytes, dims=ORDER_SHAPE_DIMS, lo_mib=32, hi_mib=512):
+    """Every tile order, and the shape's default order, on every rows x cols
+    matrix with sides from `dims` and 32 to 512 MiB, as a share of the
+    reference copy of the same bytes: buffers carved from one 1 GiB source
+    and one 1 GiB destination, rotating over as many as fit (at most 512 MiB
+    of them), median of three batches of 20 calls.  Returns the lines of a
+    table, closed by the mean over the shapes of each column."""
+    import torch
+
+    import tiled_movement_amd as T
+
+    names = ["diagonal", "half", "columns", "steep", "1/8", "1/16", "1/32"]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    src = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, device=dev, generator=gen)
+    dst = torch.empty_like(src)
+
+    def rate(fn, pairs, nbytes):
+        rates = []
+        for _ in range(3):
+            ms, _ = time_steps(lambda i: fn(i % pairs), 20, 3)
+            rates.append(2.0 * nbytes * 20 / (ms * 1e-3) / 1e9)
+        return sorted(rates)[1]
+
+    lines = ["| elem bytes | rows x cols | copy GB/s | " + " | ".join(names) + " | default | best |",
+             "|---|---|---|" + "---|" * len(names) + "---|---|"]
+    sums = [0.0] * (len(names) + 2)
+    count = 0
+    for esz in elem_bytes:
+        for rows in dims:
+            for cols in dims:
+                nbytes = rows * cols * esz
+                if not lo_mib << 20 <= nbytes <= hi_mib << 20:
+                    continue
+                per = -(-nbytes // 4096) * 4096
+                pairs = max(1, min((512 << 20) // per, (1 << 30) // per))
+                sp = [src.data_ptr() + i * per for i in range(pairs)]
+                dp = [dst.data_ptr() + i * per for i in range(pairs)]
+                cb = nbytes // 16 * 16
+                copy = rate(lambda j: T.lib.swz_copy(sp[j], dp[j], cb, stream), pairs, cb)
+
+                def conv(j):
+                    rc = T.lib.swz_transpose(sp[j], dp[j], rows, cols, esz, T.LAYOUT_SWIZZLE, T.READ_AUTO, None,
+                                             stream)
+                    if rc:
+                        raise T.SwzError(rc, "swz_transpose")
+
+                dflt = T.swz_get_tile_order(1, rows, cols, esz)
+                shares = []
+                for order in T.ORDERS:
+                    T.swz_set_tile_order(1, rows, cols, esz, T.READ_AUTO, order)
+                    shares.append(rate(conv, pairs, nbytes) / copy)
+                T.swz_set_tile_order(1, rows, cols, esz, T.READ_AUTO, -1)
+                row = shares + [shares[dflt], max(shares)]
+                sums = [a + b for a, b in zip(sums, row)]
+                count += 1
+                lines.append(f"| {esz} | {rows} x {cols} | {copy:,.0f} | " + " | ".join(f"{v:.3f}" for v in shares)
+                             + f" | {names[dflt]} {shares[dflt]:.3f} | {max(shares):.3f} |")
+                log(lines[-1])
+    lines.append(f"| mean of {count} | | | " + " | ".join(f"{v / max(count, 1):.3f}" for v in sums) + " |")
+    return lines
+
+
 # The reference copy whose launch moves the same bytes as one launch of the
 # workload (staging: both operands, 128 MiB, in one launch).
 COPY_OF = {"fp32_transpose": "copy", "fp16_transpose": "copy_128", "fp16_transpose_tr": "copy_128",
@@ -589,6 +662,8 @@ def main(argv=None):
     ap.add_argument("--tile-orders", action="store_true", help="sweep the transposes' tile orders instead")
     ap.add_argument("--elem-bytes", type=int, nargs="+", default=[4, 2], help="--tile-orders: element sizes")
     ap.add_argument("--mib", type=int, default=64, help="--tile-orders: matrix size in MiB (a power of two)")
+    ap.add_argument("--order-shapes", action="store_true",
+                    help="every tile order and the default order on many shapes, as shares of a copy")
     args = ap.parse_args(argv)
     global PAIRS_OVERRIDE
     PAIRS_OVERRIDE = args.pairs
@@ -600,6 +675,9 @@ def main(argv=None):
     ctx = Ctx()
     if args.tile_orders:
         print("\n".join(tile_order_sweep(args.elem_bytes, args.mib)), flush=True)
+        return 0
+    if args.order_shapes:
+        print("\n".join(order_shape_sweep(args.elem_bytes)), flush=True)
         return 0
     name = args.workload or "fp32_transpose"
     layout = args.layout if args.workload else "swizzle"

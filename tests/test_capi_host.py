@@ -82,7 +82,7 @@ def test_map_batch_validation():
 def test_tile_order_validation():
     f = lib.swz_set_tile_order
     assert f(-1, 64, 64, 4, -1, 0) == EINVAL
-    assert f(1, 64, 64, 4, -1, 4) == EINVAL  # no such order
+    assert f(1, 64, 64, 4, -1, 7) == EINVAL  # no such order
     assert f(1, 64, 64, 4, -1, -2) == EINVAL
     assert f(1, 64, 64, 3, -1, 0) == EINVAL  # element size
     assert f(1, 64, 64, 2, T.READ_SCALAR_COL, 0) == EINVAL  # kind for another element size
@@ -102,6 +102,30 @@ def test_tile_order_validation():
     assert g(A, B, 1, 64, 64, 3, 0, -1, None, 10, ctypes.byref(c), None) == EINVAL  # element size
     assert g(A, B, 0, 64, 64, 4, 0, -1, None, 10, ctypes.byref(c), None) == T.SWZ_OK  # nothing to time
     assert c.value == T.ORDER_DIAGONAL
+    assert g(A, B, 0, 96, 64, 4, 0, -1, None, 10, ctypes.byref(c), None) == T.SWZ_OK
+    assert c.value == T.ORDER_SLOPE_8  # the shape's default
+    for order in T.ORDERS:
+        assert f(1, 96, 64, 4, -1, order) == T.SWZ_OK
+        assert T.swz_get_tile_order(1, 96, 64, 4) == order
+    assert f(1, 96, 64, 4, -1, -1) == T.SWZ_OK
+
+
+def test_default_tile_order_by_shape():
+    """Unpinned shapes: fp32 tiles of matrices with a side that is not a
+    power of two and at most 10,240 rows take slope 1/8, everything else the
+    diagonal (other element sizes and read kinds included)."""
+    get = T.swz_get_tile_order
+    assert get(1, 4096, 4096, 4) == T.ORDER_DIAGONAL
+    assert get(1, 8192, 2048, 4) == T.ORDER_DIAGONAL
+    assert get(1, 5760, 5760, 4) == T.ORDER_SLOPE_8
+    assert get(1, 4096, 5760, 4) == T.ORDER_SLOPE_8
+    assert get(7, 3000, 4096, 4) == T.ORDER_SLOPE_8  # per batch entry
+    assert get(1, 10240, 3000, 4) == T.ORDER_SLOPE_8
+    assert get(1, 10241, 3000, 4) == T.ORDER_DIAGONAL
+    assert get(1, 12288, 4096, 4) == T.ORDER_DIAGONAL
+    assert get(1, 5760, 5760, 4, T.READ_SCALAR_COL) == T.ORDER_SLOPE_8
+    assert get(1, 5760, 5760, 2) == T.ORDER_DIAGONAL
+    assert get(1, 5760, 5760, 1) == T.ORDER_DIAGONAL
 
 
 def test_convert_validation():

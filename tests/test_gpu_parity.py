@@ -336,8 +336,7 @@ def test_narrow_any_valid_swizzle(kind, esz, c):
 # ------------------------------------------------------------ tile orders
 
 
-@pytest.mark.parametrize("order", [T.ORDER_DIAGONAL, T.ORDER_HALF_DIAGONAL, T.ORDER_COLUMNS,
-                                   T.ORDER_STEEP_DIAGONAL])
+@pytest.mark.parametrize("order", T.ORDERS)
 def test_every_tile_order_gives_the_transpose(order):
     """Each order visits every tile once: whole and ragged grids, batches,
     and the 1-D launch (a batch beyond the grid's z limit)."""
@@ -367,7 +366,7 @@ def test_tune_tile_order_pins_an_order_and_keeps_the_result():
     announce("tune tile order")
     try:
         chosen = T.swz_tune_tile_order(src, dst, 1, 2048, 544, 4, "swizzle", reps=3)
-        assert chosen in (T.ORDER_DIAGONAL, T.ORDER_HALF_DIAGONAL, T.ORDER_COLUMNS, T.ORDER_STEEP_DIAGONAL)
+        assert chosen in T.ORDERS
         assert T.swz_get_tile_order(1, 2048, 544, 4) == chosen
         torch.cuda.synchronize()
         assert np.array_equal(from_dev(dst, a), O.transpose(a))

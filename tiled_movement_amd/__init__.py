@@ -29,6 +29,8 @@ READ_BNARROW1, READ_BNARROW2, READ_BNARROW4, READ_BNARROW8, READ_BNARROW16, READ
     17, 18, 19, 20, 21, 22, 23)
 FRAG_MFMA_F32_16X16X32_BF16 = 0
 ORDER_DIAGONAL, ORDER_HALF_DIAGONAL, ORDER_COLUMNS, ORDER_STEEP_DIAGONAL = 0, 1, 2, 3
+ORDER_SLOPE_8, ORDER_SLOPE_16, ORDER_SLOPE_32 = 4, 5, 6
+ORDERS = tuple(range(7))
 C_F32, C_BF16 = 0, 1
 LAYOUTS = {"swizzle": LAYOUT_SWIZZLE, "pad": LAYOUT_PAD, "plain": LAYOUT_PLAIN, "direct": LAYOUT_SWIZZLE_DIRECT}
 

@@ -936,9 +936,9 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
     using K = Kind<KIND>;
     const auto* s = static_cast<const uint8_t*>(j.src);
     auto* d = static_cast<uint8_t*>(j.dst);
-    // slope of the diagonal order per SWZ_ORDER_* value: 1, 1/2, 0, 3
-    static constexpr TileOrder kOrders[4] = {{1u, 0u}, {1u, 1u}, {0u, 0u}, {3u, 0u}};
-    const TileOrder O = kOrders[j.order >= 0 && j.order < 4 ? j.order : 0];
+    // slope of the diagonal order per SWZ_ORDER_* value: 1, 1/2, 0, 3, 1/8, 1/16, 1/32
+    static constexpr TileOrder kOrders[7] = {{1u, 0u}, {1u, 1u}, {0u, 0u}, {3u, 0u}, {1u, 3u}, {1u, 4u}, {1u, 5u}};
+    const TileOrder O = kOrders[j.order >= 0 && j.order < 7 ? j.order : 0];
     const StepMoves mv = step_moves<KIND>(j.layout, FILL == kPadded);
     const FastPath fp = fast_path(j.batch, j.rows, j.cols, K::ESZ, K::TR, K::TC);
     // 32-bit sizes for the whole-tile path (only read when FastPath allows it)
