@@ -432,7 +432,7 @@ def test_stage_operand_shapes(layout):
 
 
 def test_stage_operand_any_valid_swizzle():
-    # k = 320: four whole k tiles in one stacked workgroup, a fifth in the edge launch
+    # k = 320: four whole k tiles in one stacked workgroup, a fifth in a block of its own
     a, _ = W.bf16_operands(272, 16, 320, seed=12)
     src = to_dev(a)
     ref = O.stage_operand(a).reshape(-1)

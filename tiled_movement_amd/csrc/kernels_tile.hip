@@ -844,14 +844,14 @@ constexpr int kStageStack = interior_stack(SWZ_READ_MFMA_16X16X32);
 
 template <int GRID>
 constexpr int stage_stack_in() {
-    return GRID == kInterior ? kStageStack : 1;
+    return GRID == kInterior || GRID == kBlocks ? kStageStack : 1;
 }
 
 template <int FILL, int GRID>
 __global__ __launch_bounds__((Kind<SWZ_READ_MFMA_16X16X32>::NT * stage_stack_in<GRID>())) void k_stage(
     const uint8_t* __restrict__ src, uint8_t* __restrict__ frag, uint32_t sp, uint32_t fp, uint32_t full_m,
     uint32_t full_k, const uint8_t* __restrict__ src2, uint8_t* __restrict__ frag2, uint32_t full_m2, int64_t mn,
-    int64_t k, int64_t tiles_m, int64_t tiles_k, int64_t tile0, KLayout L, StepMoves mv) {
+    int64_t k, int64_t tiles_m, int64_t tiles_k, int64_t tile0, KLayout L, StepMoves mv, int64_t mn2) {
     constexpr int KD = SWZ_READ_MFMA_16X16X32;
     using K = Kind<KD>;
     constexpr int STACK = stage_stack_in<GRID>();
@@ -877,6 +877,21 @@ __global__ __launch_bounds__((Kind<SWZ_READ_MFMA_16X16X32>::NT * stage_stack_in<
         const bool second = blockIdx.z != 0;
         if (blockIdx.y >= (second ? full_m2 : full_m)) return;
         whole(second ? src2 : src, second ? frag2 : frag, blockIdx.y, blockIdx.x * STACK + g);
+    } else if constexpr (GRID == kBlocks) {
+        // As kInterior over every tile of both operands: whole tiles
+        // unguarded, partial ones guarded, tiles past the operand only the
+        // barrier (the test is uniform across each wave, as in k_convert).
+        const bool second = blockIdx.z != 0;
+        const uint8_t* s = second ? src2 : src;
+        uint8_t* f = second ? frag2 : frag;
+        const int64_t m = second ? mn2 : mn;
+        const uint32_t tm = blockIdx.y, tk = blockIdx.x * STACK + __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(g));
+        if (tm < (second ? full_m2 : full_m) && tk < full_k)
+            whole(s, f, tm, tk);
+        else if (tm < (m + K::TR - 1) / K::TR && tk < tiles_k)
+            stage_tile<FILL, false>(s, f, m, k, tm * int64_t(K::TR), tk * int64_t(K::TC), 0u, 0u, lds, L, mv, t);
+        else
+            __syncthreads();
     } else if constexpr (GRID == kEdge) {
         int64_t tm, tk;
         edge_tile(tile0 + blockIdx.x, full_m, full_k, tiles_k, tm, tk);
@@ -1064,19 +1079,36 @@ void launch_stage_fill(const StageJob& j, hipStream_t stream) {
     // the interior covers the whole k tiles in groups of kStageStack; the
     // k tiles past the last group join the edge strips
     const uint32_t inner_k = full_k / kStageStack * kStageStack;
+    int64_t tiles_y = 0;  // tile rows of the taller operand
+    bool edges = inner_k != tiles_k;
+    for (int o = 0; o < nops; ++o) {
+        const int64_t tm = ceil_div(ops[o].mn, K::TR);
+        tiles_y = tm > tiles_y ? tm : tiles_y;
+        edges = edges || full_m[o] != tm;
+    }
+    if (edges && fit && fits_3d(ceil_div(tiles_k, kStageStack), tiles_y, nops, K::NT * kStageStack)) {
+        // edge tiles: every tile of every operand in one launch of blocks
+        hipLaunchKernelGGL((k_stage<FILL, kBlocks>),
+                           dim3(static_cast<unsigned>(ceil_div(tiles_k, kStageStack)), static_cast<unsigned>(tiles_y),
+                                nops),
+                           dim3(K::NT * kStageStack), 0, stream, ops[0].s, ops[0].f, sp, fpitch, full_m[0], full_k,
+                           ops[1].s, ops[1].f, full_m[1], j.mn, j.k, ceil_div(j.mn, K::TR), tiles_k, int64_t(0), kl,
+                           mv, ops[1].mn);
+        return;
+    }
     if (inner_k > 0 && rows_y > 0 && fits_3d(inner_k / kStageStack, rows_y, nops, K::NT * kStageStack)) {
         // the whole tiles of every operand in one launch, then each
         // operand's edge strips
         hipLaunchKernelGGL((k_stage<FILL, kInterior>), dim3(inner_k / kStageStack, rows_y, nops),
                            dim3(K::NT * kStageStack), 0, stream, ops[0].s, ops[0].f, sp, fpitch, full_m[0], inner_k,
                            ops[1].s, ops[1].f, full_m[1], j.mn, j.k, ceil_div(j.mn, K::TR), tiles_k, int64_t(0), kl,
-                           mv);
+                           mv, ops[1].mn);
         for (int o = 0; o < nops; ++o) {
             const int64_t tiles_m = ceil_div(ops[o].mn, K::TR);
             launch_chunks(edge_tiles(full_m[o], inner_k, tiles_m, tiles_k), [&](int64_t t0, int64_t n) {
                 hipLaunchKernelGGL((k_stage<FILL, kEdge>), dim3(static_cast<unsigned>(n)), block, lds_pad, stream,
                                    ops[o].s, ops[o].f, sp, fpitch, full_m[o], inner_k, ops[o].s, ops[o].f, full_m[o],
-                                   ops[o].mn, j.k, tiles_m, tiles_k, t0, kl, mv);
+                                   ops[o].mn, j.k, tiles_m, tiles_k, t0, kl, mv, ops[o].mn);
             });
         }
         return;
@@ -1086,7 +1118,7 @@ void launch_stage_fill(const StageJob& j, hipStream_t stream) {
         launch_chunks(tiles_m * tiles_k, [&](int64_t t0, int64_t n) {
             hipLaunchKernelGGL((k_stage<FILL, kAll1D>), dim3(static_cast<unsigned>(n)), block, lds_pad, stream,
                                ops[o].s, ops[o].f, sp, fpitch, full_m[o], full_k, ops[o].s, ops[o].f, full_m[o],
-                               ops[o].mn, j.k, tiles_m, tiles_k, t0, kl, mv);
+                               ops[o].mn, j.k, tiles_m, tiles_k, t0, kl, mv, ops[o].mn);
         });
     }
 }
