@@ -121,7 +121,7 @@ def test_direct_stage_operand_shapes():
 
 
 def test_direct_stage_operand_any_involutive_swizzle():
-    # k = 320: four whole k tiles in one stacked workgroup, a fifth in the edge launch
+    # k = 320: four whole k tiles in one stacked workgroup, a fifth in a block of its own
     a, _ = W.bf16_operands(272, 16, 320, seed=19)
     src = to_dev(a)
     ref = O.stage_operand(a).reshape(-1)
