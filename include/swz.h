@@ -239,7 +239,8 @@ int swz_map_batch(const int32_t* d_in, int32_t* d_out, int64_t n, const swz_para
  * cols); negative S is accepted; SWZ_EUNSUPPORTED for
  * SWZ_LAYOUT_SWIZZLE_DIRECT when a pointer or a row pitch (cols * elem_bytes
  * or rows * elem_bytes; only the latter for the narrow-row kinds) is not a
- * multiple of 16 bytes. */
+ * multiple of 16 bytes, and for SWZ_LAYOUT_PAD with a narrow-row kind whose
+ * rows are narrower than 4 bytes (a padded row needs whole 4-byte writes). */
 int swz_transpose(const void* d_src, void* d_dst, int64_t rows, int64_t cols, int32_t elem_bytes,
                   int32_t layout, int32_t read_kind, const swz_params* p_or_null, void* stream);
 

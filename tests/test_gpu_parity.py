@@ -333,6 +333,53 @@ def test_narrow_any_valid_swizzle(kind, esz, c):
             check_transpose(a, esz, layout, kind, (B, M, S))
 
 
+def test_seeded_random_conversions():
+    """80 seeded random conversions: element size, batch, rows and columns
+    (1-600, so pitches of any alignment, partial tiles and partial stacked
+    blocks in both directions), layout and tile order, each through the
+    AUTO read kind and compared with the oracle."""
+    rng = np.random.default_rng(2026)
+    gen = {4: W.fp32_matrix, 2: W.fp16_matrix, 1: W.u8_matrix}
+    for case in range(80):
+        esz = int(rng.choice([1, 2, 4]))
+        b, r, c = int(rng.integers(1, 4)), int(rng.integers(1, 601)), int(rng.integers(1, 601))
+        layout = str(rng.choice(["swizzle", "pad", "plain", "direct"]))
+        order = int(rng.choice(T.ORDERS))
+        a = gen[esz](b * r, c, seed=case).reshape(b, r, c)
+        announce("random conversion", case, esz, (b, r, c), layout, order)
+        T.swz_set_tile_order(b, r, c, esz, T.READ_AUTO, order)
+        try:
+            src = to_dev(a)
+            dst = torch.empty((b, c, r), dtype=src.dtype, device=DEV)
+            try:
+                T.swz_convert_layout(src, dst, b, r, c, esz, layout)
+            except T.SwzError as e:
+                # a direct fill needs 16-byte row pitches; no padded rows narrower than 4 bytes
+                assert e.status == T.SWZ_EUNSUPPORTED and layout in ("direct", "pad"), (case, e)
+                continue
+            torch.cuda.synchronize()
+            assert np.array_equal(from_dev(dst, a), O.convert_layout(a)), (case, esz, (b, r, c), layout, order)
+        finally:
+            T.swz_set_tile_order(b, r, c, esz, T.READ_AUTO, -1)
+
+
+def test_seeded_random_operand_pairs():
+    """40 seeded random operand pairs (m, n multiples of 16 up to 592, k a
+    multiple of 32 up to 704) staged in one launch in a random layout."""
+    rng = np.random.default_rng(2027)
+    for case in range(40):
+        m, n, k = 16 * int(rng.integers(1, 38)), 16 * int(rng.integers(1, 38)), 32 * int(rng.integers(1, 23))
+        layout = str(rng.choice(["swizzle", "pad", "plain", "direct"]))
+        announce("random pair", case, (m, n, k), layout)
+        a, bt = W.bf16_operands(m, n, k, seed=100 + case)
+        fa = torch.empty(a.size, dtype=torch.int16, device=DEV)
+        fb = torch.empty(bt.size, dtype=torch.int16, device=DEV)
+        T.swz_stage_operands(to_dev(a), fa, m, to_dev(bt), fb, n, k, layout=layout)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(fa, a), O.stage_operand(a).reshape(-1)), (case, m, n, k, layout)
+        assert np.array_equal(from_dev(fb, bt), O.stage_operand(bt).reshape(-1)), (case, m, n, k, layout)
+
+
 # ------------------------------------------------------------ tile orders
 
 
