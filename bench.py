@@ -31,7 +31,8 @@ Usage:
       stdout instead of the JSON line)
   python bench.py --order-shapes [--elem-bytes 4 2]
       every tile order and the shape's default order on matrices of 32 to
-      512 MiB with sides from 1,024 to 16,384, as shares of a copy (a table)
+      512 MiB with sides from 39 values between 1,024 and 16,384, as shares
+      of a copy (a table)
 
 Timing: warm-up steps, then a short spin kernel on the launch stream before
 the start event, so the host has queued the first launches by the time the
@@ -568,8 +569,9 @@ def tile_order_sweep(elem_bytes, mib):
     return lines
 
 
-ORDER_SHAPE_DIMS = (1024, 1536, 2048, 2560, 2944, 3072, 3584, 3968, 4096, 4160, 4608, 5120, 5760, 6144, 6656, 7168,
-                    8128, 8192, 9216, 10240, 12288, 14336, 16384)
+ORDER_SHAPE_DIMS = (1024, 1280, 1536, 1792, 2048, 2304, 2560, 2816, 2944, 3072, 3328, 3584, 3840, 3968, 4096, 4160,
+                    4352, 4608, 4864, 5120, 5376, 5760, 6144, 6400, 6656, 6912, 7168, 7424, 8128, 8192, 8704, 9216,
+                    9728, 10240, 11264, 12288, 13312, 14336, 16384)
 
 
 def order_shape_sweep(elem_bytes, dims=ORDER_SHAPE_DIMS, lo_mib=32, hi_mib=512):

@@ -86,24 +86,24 @@ def test_tile_order_validation():
     assert f(1, 64, 64, 4, -1, -2) == EINVAL
     assert f(1, 64, 64, 3, -1, 0) == EINVAL  # element size
     assert f(1, 64, 64, 2, T.READ_SCALAR_COL, 0) == EINVAL  # kind for another element size
-    assert f(1, 64, 64, 4, -1, T.ORDER_COLUMNS) == T.SWZ_OK
-    assert T.swz_get_tile_order(1, 64, 64, 4) == T.ORDER_COLUMNS
-    assert T.swz_get_tile_order(1, 64, 64, 4, T.READ_SCALAR_COL) == T.ORDER_COLUMNS  # AUTO resolves to this kind
-    assert T.swz_get_tile_order(2, 64, 64, 4) == T.ORDER_DIAGONAL  # another shape
-    assert lib.swz_get_tile_order(1, 64, 64, 4, -1, None) == EINVAL
-    assert f(1, 64, 64, 4, -1, -1) == T.SWZ_OK  # removed
-    assert T.swz_get_tile_order(1, 64, 64, 4) == T.ORDER_DIAGONAL
-    assert f(1, 64, 64, 4, -1, -1) == T.SWZ_OK  # removing twice is fine
+    assert f(1, 64, 1024, 4, -1, T.ORDER_COLUMNS) == T.SWZ_OK
+    assert T.swz_get_tile_order(1, 64, 1024, 4) == T.ORDER_COLUMNS
+    assert T.swz_get_tile_order(1, 64, 1024, 4, T.READ_SCALAR_COL) == T.ORDER_COLUMNS  # AUTO resolves to this kind
+    assert T.swz_get_tile_order(2, 64, 1024, 4) == T.ORDER_DIAGONAL  # another shape
+    assert lib.swz_get_tile_order(1, 64, 1024, 4, -1, None) == EINVAL
+    assert f(1, 64, 1024, 4, -1, -1) == T.SWZ_OK  # removed
+    assert T.swz_get_tile_order(1, 64, 1024, 4) == T.ORDER_DIAGONAL
+    assert f(1, 64, 1024, 4, -1, -1) == T.SWZ_OK  # removing twice is fine
     g = lib.swz_tune_tile_order
     c = ctypes.c_int32(-7)
     assert g(A, B, 1, 64, 64, 4, 0, -1, None, 10, None, None) == EINVAL  # no output for the choice
     assert g(A, B, 1, 64, 64, 4, 0, -1, None, 0, ctypes.byref(c), None) == EINVAL  # reps
     assert g(A, B, 1, 64, 64, 4, 0, -1, None, 1001, ctypes.byref(c), None) == EINVAL
     assert g(A, B, 1, 64, 64, 3, 0, -1, None, 10, ctypes.byref(c), None) == EINVAL  # element size
-    assert g(A, B, 0, 64, 64, 4, 0, -1, None, 10, ctypes.byref(c), None) == T.SWZ_OK  # nothing to time
+    assert g(A, B, 0, 64, 1024, 4, 0, -1, None, 10, ctypes.byref(c), None) == T.SWZ_OK  # nothing to time
     assert c.value == T.ORDER_DIAGONAL
-    assert g(A, B, 0, 96, 64, 4, 0, -1, None, 10, ctypes.byref(c), None) == T.SWZ_OK
-    assert c.value == T.ORDER_SLOPE_8  # the shape's default
+    assert g(A, B, 0, 64, 64, 4, 0, -1, None, 10, ctypes.byref(c), None) == T.SWZ_OK
+    assert c.value == T.ORDER_SLOPE_32  # the shape's default
     for order in T.ORDERS:
         assert f(1, 96, 64, 4, -1, order) == T.SWZ_OK
         assert T.swz_get_tile_order(1, 96, 64, 4) == order
@@ -111,21 +111,34 @@ def test_tile_order_validation():
 
 
 def test_default_tile_order_by_shape():
-    """Unpinned shapes: fp32 tiles of matrices with a side that is not a
-    power of two and at most 10,240 rows take slope 1/8, everything else the
-    diagonal (other element sizes and read kinds included)."""
+    """Unpinned shapes of the 4- and 2-byte kinds: slope 1/32 when the
+    source row pitch (cols x element bytes) is not within 1% of a multiple
+    of 4 KiB; otherwise the diagonal, or slope 1/8 for fp32 matrices with at
+    most 10,240 rows and a side that is not a power of two.  Byte kinds:
+    the diagonal."""
     get = T.swz_get_tile_order
+    # pitch a multiple of 4 KiB
     assert get(1, 4096, 4096, 4) == T.ORDER_DIAGONAL
     assert get(1, 8192, 2048, 4) == T.ORDER_DIAGONAL
-    assert get(1, 5760, 5760, 4) == T.ORDER_SLOPE_8
-    assert get(1, 4096, 5760, 4) == T.ORDER_SLOPE_8
     assert get(7, 3000, 4096, 4) == T.ORDER_SLOPE_8  # per batch entry
-    assert get(1, 10240, 3000, 4) == T.ORDER_SLOPE_8
-    assert get(1, 10241, 3000, 4) == T.ORDER_DIAGONAL
+    assert get(1, 10240, 3072, 4) == T.ORDER_SLOPE_8
+    assert get(1, 10241, 3072, 4) == T.ORDER_DIAGONAL
     assert get(1, 12288, 4096, 4) == T.ORDER_DIAGONAL
-    assert get(1, 5760, 5760, 4, T.READ_SCALAR_COL) == T.ORDER_SLOPE_8
-    assert get(1, 5760, 5760, 2) == T.ORDER_DIAGONAL
+    assert get(1, 8192, 8192, 2) == T.ORDER_DIAGONAL
+    assert get(1, 5760, 6144, 2) == T.ORDER_DIAGONAL
+    # within 1% of a multiple: fp32 8128 columns (32,512 bytes, 256 below 32 KiB), 16-bit 8128 (128 below)
+    assert get(1, 5760, 8128, 4) == T.ORDER_SLOPE_8
+    assert get(1, 16384, 8128, 4) == T.ORDER_DIAGONAL
+    assert get(1, 5760, 8128, 2) == T.ORDER_DIAGONAL
+    # further off: 16-bit 4160 columns (8,320 bytes: 128 over 8 KiB is 1.5%), fp32 5760, 3000
+    assert get(1, 5760, 4160, 2) == T.ORDER_SLOPE_32
+    assert get(1, 5760, 5760, 4) == T.ORDER_SLOPE_32
+    assert get(1, 4096, 5760, 4, T.READ_SCALAR_COL) == T.ORDER_SLOPE_32
+    assert get(1, 16384, 3000, 4) == T.ORDER_SLOPE_32  # whatever the rows
+    assert get(1, 5760, 5760, 2) == T.ORDER_SLOPE_32
+    assert get(1, 8192, 512, 2) == T.ORDER_SLOPE_32  # rows of 1 KiB
     assert get(1, 5760, 5760, 1) == T.ORDER_DIAGONAL
+    assert get(1, 8192, 1000, 1) == T.ORDER_DIAGONAL
 
 
 def test_convert_validation():

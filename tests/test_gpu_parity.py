@@ -433,11 +433,13 @@ def test_tune_tile_order_batched_16bit_pins_per_shape():
     src = to_dev(a)
     dst = torch.empty((3, 328, 200), dtype=src.dtype, device=DEV)
     announce("tune tile order batched fp16")
+    defaults = [T.swz_get_tile_order(1, 200, 328, 2, T.READ_B64_TR16),
+                T.swz_get_tile_order(3, 200, 328, 2, T.READ_B128_8X8)]
     try:
         chosen = T.swz_tune_tile_order(src, dst, 3, 200, 328, 2, "swizzle", T.READ_B64_TR16, reps=2)
         assert T.swz_get_tile_order(3, 200, 328, 2, T.READ_B64_TR16) == chosen
-        assert T.swz_get_tile_order(1, 200, 328, 2, T.READ_B64_TR16) == T.ORDER_DIAGONAL
-        assert T.swz_get_tile_order(3, 200, 328, 2, T.READ_B128_8X8) == T.ORDER_DIAGONAL
+        assert T.swz_get_tile_order(1, 200, 328, 2, T.READ_B64_TR16) == defaults[0]  # other shapes untouched
+        assert T.swz_get_tile_order(3, 200, 328, 2, T.READ_B128_8X8) == defaults[1]
         torch.cuda.synchronize()
         assert np.array_equal(from_dev(dst, a), O.convert_layout(a))
         dst.zero_()
@@ -454,10 +456,11 @@ def test_tune_tile_order_refusal_pins_nothing():
     error before any launch, and leaves no order pinned for the shape."""
     src = torch.zeros((64, 100), dtype=torch.int16, device=DEV)
     dst = torch.zeros((100, 64), dtype=torch.int16, device=DEV)
+    default = T.swz_get_tile_order(1, 64, 100, 2, T.READ_B64_TR16)
     with pytest.raises(T.SwzError) as e:
         T.swz_tune_tile_order(src, dst, 1, 64, 100, 2, "direct", T.READ_B64_TR16, reps=2)
     assert e.value.status == T.SWZ_EUNSUPPORTED
-    assert T.swz_get_tile_order(1, 64, 100, 2, T.READ_B64_TR16) == T.ORDER_DIAGONAL
+    assert T.swz_get_tile_order(1, 64, 100, 2, T.READ_B64_TR16) == default
     assert not dst.any().item()  # nothing was written
 
 

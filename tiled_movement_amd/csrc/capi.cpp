@@ -138,18 +138,31 @@ swz::LdsLayout layout_of(const swz_plan_info& pl) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SWZ_OK : SWZ_EHIP; }
 
-// The order of a shape with none pinned.  The diagonal suits matrices whose
-// sides are powers of two; fp32 matrices with another side did better at
-// slope 1/8 (2 x 2 blocks of 32 x 32 tiles; 444 shapes of 32-512 MiB with
-// sides from 1,024 to 16,384, of which this rule changes 373: their mean rate
-// over a copy of the same bytes 0.86 -> 0.92, 351 faster, 7 slower by 2-5%),
-// except with more than 10,240 rows, where slope 1/8 lost up to 8%.  For the
-// 16-bit kinds no other order beat the diagonal without losing more than 2%
-// on many shapes (357 shapes: the diagonal's mean 0.90, the best other
-// order's 0.91, 55 shapes slower), so they keep it.
+// The order of a shape with none pinned, from sweeps of every order over
+// matrices of 32-512 MiB with sides from 1,024 to 16,384 (bench.py
+// --order-shapes).  What decides is the source row pitch:
+// - not within 1% of a multiple of 4 KiB: slope 1/32.  Workgroups then walk
+//   down the block columns nearly in order, so the output rows are written
+//   in long runs, while the reads, a pitch apart, still spread over the
+//   memory channels.  Over 745 fp32 and 723 16-bit such shapes the mean
+//   rate rose from 0.85 and 0.87 of a copy of the same bytes to 0.95 and
+//   0.96; none lost more than 1%.
+// - within 1% of a multiple of 4 KiB: reads a pitch apart fall on few
+//   channels in that walk and the diagonal is needed; for fp32 matrices
+//   with at most 10,240 rows and a side that is not a power of two, slope
+//   1/8 did better still (462 shapes: 0.85 -> 0.91; 11 lost 2-6%; beyond
+//   10,240 rows it lost up to 8%).
+// The byte kinds were not swept and keep the diagonal.
 int default_order(int kind, int64_t rows, int64_t cols) {
+    const int esz = kind == SWZ_READ_SCALAR_COL ? 4
+                    : kind == SWZ_READ_B64_4X4 || kind == SWZ_READ_B64_TR16 || kind == SWZ_READ_B128_8X8 ? 2
+                                                                                                       : 0;
+    if (esz == 0) return SWZ_ORDER_DIAGONAL;
+    const uint64_t pitch = static_cast<uint64_t>(cols) * static_cast<uint64_t>(esz), r = pitch % 4096;
+    const uint64_t off = r < 4096 - r ? r : 4096 - r;  // distance to the nearest multiple of 4 KiB
+    if (off * 100 > pitch) return SWZ_ORDER_SLOPE_32;
     const bool pow2 = (rows & (rows - 1)) == 0 && (cols & (cols - 1)) == 0;
-    return kind == SWZ_READ_SCALAR_COL && !pow2 && rows <= 10240 ? SWZ_ORDER_SLOPE_8 : SWZ_ORDER_DIAGONAL;
+    return esz == 4 && !pow2 && rows <= 10240 ? SWZ_ORDER_SLOPE_8 : SWZ_ORDER_DIAGONAL;
 }
 
 // Tile orders pinned per conversion shape (swz_set_tile_order,
