@@ -258,13 +258,13 @@ int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, int64_t ro
  * them.  All orders give the same bits.
  *
  * Shapes with no pinned order (swz_set_tile_order) take a default set by the
- * source row pitch (cols * elem_bytes) for the 4- and 2-byte read kinds:
- * SWZ_ORDER_SLOPE_32 when the pitch is not within 1% of a multiple of 4 KiB;
- * otherwise the diagonal, or SWZ_ORDER_SLOPE_8 for fp32 matrices with at
- * most 10,240 rows and a side that is not a power of two.  The byte kinds
- * take the diagonal.  (Measured over 1,273 fp32 and 1,009 16-bit shapes of
- * 32 to 512 MiB against a copy of the same bytes; see swz_get_tile_order to
- * read a shape's order.) */
+ * source row pitch (cols * elem_bytes): SWZ_ORDER_SLOPE_32 when the pitch
+ * is not within 1% of a multiple of 4 KiB; otherwise the diagonal, or
+ * SWZ_ORDER_SLOPE_8 for fp32 matrices with at most 10,240 rows and a side
+ * that is not a power of two.  The whole-row (narrow) kinds take the
+ * diagonal.  (Measured over 1,273 fp32, 1,009 16-bit and 597 byte shapes
+ * of 32 to 512 MiB against a copy of the same bytes; swz_get_tile_order
+ * reads a shape's order.) */
 enum swz_tile_order {
     SWZ_ORDER_DIAGONAL = 0,       /* tile row tr, tile column (q + tr) mod tiles */
     SWZ_ORDER_HALF_DIAGONAL = 1,  /* tile column (q + tr / 2) mod tiles */

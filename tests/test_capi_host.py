@@ -111,11 +111,10 @@ def test_tile_order_validation():
 
 
 def test_default_tile_order_by_shape():
-    """Unpinned shapes of the 4- and 2-byte kinds: slope 1/32 when the
-    source row pitch (cols x element bytes) is not within 1% of a multiple
-    of 4 KiB; otherwise the diagonal, or slope 1/8 for fp32 matrices with at
-    most 10,240 rows and a side that is not a power of two.  Byte kinds:
-    the diagonal."""
+    """Unpinned shapes: slope 1/32 when the source row pitch (cols x element
+    bytes) is not within 1% of a multiple of 4 KiB; otherwise the diagonal,
+    or slope 1/8 for fp32 matrices with at most 10,240 rows and a side that
+    is not a power of two.  Whole-row kinds: the diagonal."""
     get = T.swz_get_tile_order
     # pitch a multiple of 4 KiB
     assert get(1, 4096, 4096, 4) == T.ORDER_DIAGONAL
@@ -137,8 +136,13 @@ def test_default_tile_order_by_shape():
     assert get(1, 16384, 3000, 4) == T.ORDER_SLOPE_32  # whatever the rows
     assert get(1, 5760, 5760, 2) == T.ORDER_SLOPE_32
     assert get(1, 8192, 512, 2) == T.ORDER_SLOPE_32  # rows of 1 KiB
-    assert get(1, 5760, 5760, 1) == T.ORDER_DIAGONAL
-    assert get(1, 8192, 1000, 1) == T.ORDER_DIAGONAL
+    # bytes: the same rule on the 8-bit transpose-read kind; whole-row kinds keep the diagonal
+    assert get(1, 5760, 5760, 1) == T.ORDER_SLOPE_32
+    assert get(1, 8192, 8192, 1) == T.ORDER_DIAGONAL
+    assert get(1, 5760, 8128, 1) == T.ORDER_DIAGONAL  # 64 bytes short of 8 KiB
+    assert get(1, 5760, 4160, 1) == T.ORDER_SLOPE_32  # 64 over 4 KiB: 1.5%
+    assert get(1, 1 << 20, 16, 1) == T.ORDER_DIAGONAL  # one tile column
+    assert get(1, 1 << 20, 8, 4) == T.ORDER_DIAGONAL
 
 
 def test_convert_validation():

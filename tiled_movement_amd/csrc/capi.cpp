@@ -144,19 +144,21 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SWZ_OK : SWZ_EHIP; }
 // - not within 1% of a multiple of 4 KiB: slope 1/32.  Workgroups then walk
 //   down the block columns nearly in order, so the output rows are written
 //   in long runs, while the reads, a pitch apart, still spread over the
-//   memory channels.  Over 745 fp32 and 723 16-bit such shapes the mean
-//   rate rose from 0.85 and 0.87 of a copy of the same bytes to 0.95 and
-//   0.96; none lost more than 1%.
+//   memory channels.  Over 745 fp32, 723 16-bit and 471 byte such shapes
+//   the mean rate rose from 0.85, 0.87 and 0.84 of a copy of the same bytes
+//   to 0.95, 0.96 and 0.90; one shape lost more than 1% (a byte matrix, 2.6%).
 // - within 1% of a multiple of 4 KiB: reads a pitch apart fall on few
 //   channels in that walk and the diagonal is needed; for fp32 matrices
 //   with at most 10,240 rows and a side that is not a power of two, slope
 //   1/8 did better still (462 shapes: 0.85 -> 0.91; 11 lost 2-6%; beyond
 //   10,240 rows it lost up to 8%).
-// The byte kinds were not swept and keep the diagonal.
+// The whole-row kinds have one tile column, where every order is the same,
+// and keep the diagonal.
 int default_order(int kind, int64_t rows, int64_t cols) {
     const int esz = kind == SWZ_READ_SCALAR_COL ? 4
                     : kind == SWZ_READ_B64_4X4 || kind == SWZ_READ_B64_TR16 || kind == SWZ_READ_B128_8X8 ? 2
-                                                                                                       : 0;
+                    : kind == SWZ_READ_B64_TR8                                                          ? 1
+                                                                                                        : 0;
     if (esz == 0) return SWZ_ORDER_DIAGONAL;
     const uint64_t pitch = static_cast<uint64_t>(cols) * static_cast<uint64_t>(esz), r = pitch % 4096;
     const uint64_t off = r < 4096 - r ? r : 4096 - r;  // distance to the nearest multiple of 4 KiB
