@@ -111,17 +111,19 @@ def test_tile_order_validation():
 
 
 def test_default_tile_order_by_shape():
-    """Unpinned shapes: slope 1/32 when the source row pitch (cols x element
-    bytes) is not within 1% of a multiple of 4 KiB; otherwise the diagonal,
-    or slope 1/8 for fp32 matrices with at most 10,240 rows and a side that
-    is not a power of two.  Whole-row kinds: the diagonal."""
+    """Unpinned shapes: whole tile columns when the output rows (rows x
+    element bytes) are not whole 64-byte pieces and there are at least 2,000
+    rows; else slope 1/32 when the source row pitch (cols x element bytes) is
+    not within 1% of a multiple of 4 KiB; otherwise the diagonal, or slope
+    1/8 for fp32 matrices with at most 10,240 rows and a side that is not a
+    power of two.  Whole-row kinds: the diagonal."""
     get = T.swz_get_tile_order
     # pitch a multiple of 4 KiB
     assert get(1, 4096, 4096, 4) == T.ORDER_DIAGONAL
     assert get(1, 8192, 2048, 4) == T.ORDER_DIAGONAL
-    assert get(7, 3000, 4096, 4) == T.ORDER_SLOPE_8  # per batch entry
+    assert get(7, 3072, 4096, 4) == T.ORDER_SLOPE_8  # per batch entry
     assert get(1, 10240, 3072, 4) == T.ORDER_SLOPE_8
-    assert get(1, 10241, 3072, 4) == T.ORDER_DIAGONAL
+    assert get(1, 10256, 3072, 4) == T.ORDER_DIAGONAL  # over 10,240 rows (output rows whole 64-byte pieces)
     assert get(1, 12288, 4096, 4) == T.ORDER_DIAGONAL
     assert get(1, 8192, 8192, 2) == T.ORDER_DIAGONAL
     assert get(1, 5760, 6144, 2) == T.ORDER_DIAGONAL
@@ -138,6 +140,15 @@ def test_default_tile_order_by_shape():
     assert get(1, 8192, 512, 2) == T.ORDER_SLOPE_32  # rows of 1 KiB
     # bytes: the same rule on the 8-bit transpose-read kind; whole-row kinds keep the diagonal
     assert get(1, 5760, 5760, 1) == T.ORDER_SLOPE_32
+    # output rows (rows x element bytes) off the 64-byte pieces, from 2,000 rows: whole tile columns
+    assert get(1, 5800, 5800, 4) == T.ORDER_COLUMNS
+    assert get(3, 3000, 4096, 4) == T.ORDER_COLUMNS
+    assert get(1, 2008, 8192, 4) == T.ORDER_COLUMNS
+    assert get(1, 1000, 8192, 4) == T.ORDER_SLOPE_8  # fewer rows: the pitch rules
+    assert get(1, 5760, 5800, 4) == T.ORDER_SLOPE_32  # only the source pitch is off
+    assert get(1, 4112, 4112, 2) == T.ORDER_COLUMNS
+    assert get(1, 8208, 8208, 1) == T.ORDER_COLUMNS
+    assert get(1, 8208, 16, 1) == T.ORDER_DIAGONAL  # whole-row kind
     assert get(1, 8192, 8192, 1) == T.ORDER_DIAGONAL
     assert get(1, 5760, 8128, 1) == T.ORDER_DIAGONAL  # 64 bytes short of 8 KiB
     assert get(1, 5760, 4160, 1) == T.ORDER_SLOPE_32  # 64 over 4 KiB: 1.5%

@@ -152,14 +152,23 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SWZ_OK : SWZ_EHIP; }
 //   with at most 10,240 rows and a side that is not a power of two, slope
 //   1/8 did better still (462 shapes: 0.85 -> 0.91; 11 lost 2-6%; beyond
 //   10,240 rows it lost up to 8%).
-// The whole-row kinds have one tile column, where every order is the same,
-// and keep the diagonal.
+// Where the output rows are not whole 64-byte pieces (at 2,000 rows and
+// more), whole tile columns in turn: the grid that serves those shapes has
+// workgroups on one XCD take consecutive blocks, and in this order those
+// are the neighbours that share the pieces (fp32, 16-bit and byte matrices
+// of 2,000-9,000 rows: 0.45-0.60 of a copy before, 0.63-0.75 after; slope
+// 1/32 within 1% of it, the diagonal up to 0.17 behind).  The whole-row
+// kinds have one tile column, where every order is the same, and keep the
+// diagonal.
 int default_order(int kind, int64_t rows, int64_t cols) {
     const int esz = kind == SWZ_READ_SCALAR_COL ? 4
                     : kind == SWZ_READ_B64_4X4 || kind == SWZ_READ_B64_TR16 || kind == SWZ_READ_B128_8X8 ? 2
                     : kind == SWZ_READ_B64_TR8                                                          ? 1
                                                                                                         : 0;
     if (esz == 0) return SWZ_ORDER_DIAGONAL;
+    // Output rows off the 64-byte pieces (the XCD-grouped grid): neighbours
+    // down a block column share those pieces, so they go in turn.
+    if (swz::partial_line_output(rows, esz)) return SWZ_ORDER_COLUMNS;
     const uint64_t pitch = static_cast<uint64_t>(cols) * static_cast<uint64_t>(esz), r = pitch % 4096;
     const uint64_t off = r < 4096 - r ? r : 4096 - r;  // distance to the nearest multiple of 4 KiB
     if (off * 100 > pitch) return SWZ_ORDER_SLOPE_32;

@@ -48,6 +48,21 @@ __device__ __forceinline__ void gstore16(uint8_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
+// The same through the caches (CACHED), for matrices whose row pitches are
+// not whole multiples of 64 bytes: two workgroups then share the lines at
+// each tile edge, and the pieces written by one meet the other's in L2
+// (see kBlocksXcd) instead of reaching memory as partial lines.
+template <bool CACHED>
+__device__ __forceinline__ u32x4 gload16c(const uint8_t* p) {
+    if constexpr (CACHED) return *reinterpret_cast<const u32x4*>(p);
+    else return gload16(p);
+}
+template <bool CACHED>
+__device__ __forceinline__ void gstore16c(uint8_t* p, u32x4 v) {
+    if constexpr (CACHED) *reinterpret_cast<u32x4*>(p) = v;
+    else gstore16(p, v);
+}
+
 // Tile (batch b, tile row tr, tile column tc) of linear tile index t.
 // Diagonal orders: t -> tr = t % tiles_r, tc = (t / tiles_r + f(tr)) %
 // tiles_c with f(tr) = (tr * O.num) >> O.sh: slope 1 (the default), 1/2, 3,
@@ -79,11 +94,23 @@ __device__ __forceinline__ uint32_t pair_col(const V& a, const V& b, int j) {
     return (j & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
 }
 
+// 16 bytes of a row whose pitch (or base) is not a multiple of 16 bytes,
+// accessed as one 16-byte vector anyway: compute queues on this GPU run in
+// the unaligned memory access mode, and the compiler emits a single dwordx4
+// for an access that only promises byte alignment.  For 1- and 2-byte
+// elements that replaces 16 or 8 accesses by one (bytes 5800 x 5800: 0.13 ->
+// 0.38 of a copy; fp16 5801 x 5801: 0.20 -> 0.35); 4-byte elements keep
+// their four aligned dword accesses, which measured faster (fp32 4001 x
+// 4001: 0.44 against 0.37).
+typedef u32x4 __attribute__((aligned(1))) u32x4_unaligned;
+
 // 16 bytes = 16/ESZ consecutive elements of one row, zero outside the matrix.
 template <int ESZ>
 __device__ __forceinline__ u32x4 load16_guarded(const uint8_t* S, int64_t row, int64_t col, int64_t rows,
                                                 int64_t cols) {
     constexpr int N = 16 / ESZ;
+    if (ESZ < 4 && row < rows && col + N <= cols)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4_unaligned*>(S + (row * cols + col) * ESZ));
     uint32_t e[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
@@ -114,6 +141,10 @@ template <int ESZ>
 __device__ __forceinline__ void store16_guarded(uint8_t* D, int64_t row, int64_t col, int64_t nrows, int64_t ncols,
                                                 const u32x4& o) {
     if (row >= nrows) return;
+    if (ESZ < 4 && col + 16 / ESZ <= ncols) {
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4_unaligned*>(D + (row * ncols + col) * ESZ));
+        return;
+    }
     if (ESZ == 1) {
 #pragma unroll
         for (int k = 0; k < 16; ++k)
@@ -137,21 +168,22 @@ __device__ __forceinline__ void store16_guarded(uint8_t* D, int64_t row, int64_t
 // pitches that are not multiples of 16 bytes: element by element.
 enum Edge { kFull = 0, kVec = 1, kElem = 2 };
 
-template <int EDGE, int ESZ>
+template <int EDGE, int ESZ, bool CACHED = false>
 __device__ __forceinline__ u32x4 load16_edge(const uint8_t* S, int64_t row, int64_t col, int64_t rows,
                                              int64_t cols) {
-    if constexpr (EDGE == kFull) return gload16(S + (row * cols + col) * ESZ);
-    if constexpr (EDGE == kVec) return row < rows && col < cols ? gload16(S + (row * cols + col) * ESZ) : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (EDGE == kFull) return gload16c<CACHED>(S + (row * cols + col) * ESZ);
+    if constexpr (EDGE == kVec)
+        return row < rows && col < cols ? gload16c<CACHED>(S + (row * cols + col) * ESZ) : u32x4{0u, 0u, 0u, 0u};
     return load16_guarded<ESZ>(S, row, col, rows, cols);
 }
 
-template <int EDGE, int ESZ>
+template <int EDGE, int ESZ, bool CACHED = false>
 __device__ __forceinline__ void store16_edge(uint8_t* D, int64_t row, int64_t col, int64_t nrows, int64_t ncols,
                                              u32x4 v) {
     if constexpr (EDGE == kFull) {
-        gstore16(D + (row * ncols + col) * ESZ, v);
+        gstore16c<CACHED>(D + (row * ncols + col) * ESZ, v);
     } else if constexpr (EDGE == kVec) {
-        if (row < nrows && col < ncols) gstore16(D + (row * ncols + col) * ESZ, v);
+        if (row < nrows && col < ncols) gstore16c<CACHED>(D + (row * ncols + col) * ESZ, v);
     } else {
         store16_guarded<ESZ>(D, row, col, nrows, ncols, v);
     }
@@ -172,7 +204,7 @@ __device__ __forceinline__ void store16_edge(uint8_t* D, int64_t row, int64_t co
 // the load lengthens the kernel by 1 / 3 / 3.5%, and a general prelude
 // (64-bit tile bases and edge tests, the swizzle of every step from run-time
 // (B, M, S)) cost the same 3.5%.
-template <int EDGE, int ESZ>
+template <int EDGE, int ESZ, bool CACHED = false>
 struct TileIo {
     const uint8_t* S;  // kFull: the tile's first source element; otherwise the source matrix
     uint8_t* D;        // kFull: the tile's first output element; otherwise the output matrix
@@ -183,20 +215,20 @@ struct TileIo {
         return S + (static_cast<uint64_t>(static_cast<uint32_t>(r)) * sp + static_cast<uint32_t>(c * ESZ));
     }
     __device__ __forceinline__ u32x4 load(int r, int c) const {
-        if constexpr (EDGE == kFull) return gload16(src(r, c));
-        else return load16_edge<EDGE, ESZ>(S, r0 + r, c0 + c, rows, cols);
+        if constexpr (EDGE == kFull) return gload16c<CACHED>(src(r, c));
+        else return load16_edge<EDGE, ESZ, CACHED>(S, r0 + r, c0 + c, rows, cols);
     }
     // Whole-row tiles (cols == tile width, c0 = 0): a vector may span rows,
     // so the edge paths guard the flat index.
     __device__ __forceinline__ u32x4 load_flat(int r, int c) const {
-        if constexpr (EDGE == kFull) return gload16(src(r, c));
-        else return load16_edge<EDGE, ESZ>(S, 0, (r0 + r) * cols + c0 + c, 1, rows * cols);
+        if constexpr (EDGE == kFull) return gload16c<CACHED>(src(r, c));
+        else return load16_edge<EDGE, ESZ, CACHED>(S, 0, (r0 + r) * cols + c0 + c, 1, rows * cols);
     }
     __device__ __forceinline__ void store(int orow, int ocol, u32x4 v) const {
         if constexpr (EDGE == kFull)
-            gstore16(D + (static_cast<uint64_t>(static_cast<uint32_t>(orow)) * dp + static_cast<uint32_t>(ocol * ESZ)), v);
+            gstore16c<CACHED>(D + (static_cast<uint64_t>(static_cast<uint32_t>(orow)) * dp + static_cast<uint32_t>(ocol * ESZ)), v);
         else
-            store16_edge<EDGE, ESZ>(D, c0 + orow, r0 + ocol, cols, rows, v);
+            store16_edge<EDGE, ESZ, CACHED>(D, c0 + orow, r0 + ocol, cols, rows, v);
     }
 };
 
@@ -336,8 +368,8 @@ __device__ __forceinline__ uint32_t lane_base(int t, const KLayout& L) {
 // stored.  Rows must be 16-byte aligned for 2-byte elements, so a 16-byte
 // slot is wholly inside or wholly outside.  Waits for its own loads; the
 // caller's barrier then publishes the tile.
-template <int KIND, int EDGE>
-__device__ __forceinline__ void direct_fill(const TileIo<EDGE, Kind<KIND>::ESZ>& io, uint8_t* lds, const KLayout& L,
+template <int KIND, int EDGE, bool CACHED>
+__device__ __forceinline__ void direct_fill(const TileIo<EDGE, Kind<KIND>::ESZ, CACHED>& io, uint8_t* lds, const KLayout& L,
                                             const StepMoves& mv, int t) {
     using K = Kind<KIND>;
     using D = Direct<KIND>;
@@ -367,8 +399,8 @@ __device__ __forceinline__ void direct_fill(const TileIo<EDGE, Kind<KIND>::ESZ>&
 
 // Global loads of one tile into registers, guarded at the matrix edge as EDGE
 // says (Edge above).
-template <int KIND, int EDGE>
-__device__ __forceinline__ void load_tile(const TileIo<EDGE, Kind<KIND>::ESZ>& io, int t, u32x4* v) {
+template <int KIND, int EDGE, bool CACHED>
+__device__ __forceinline__ void load_tile(const TileIo<EDGE, Kind<KIND>::ESZ, CACHED>& io, int t, u32x4* v) {
     using K = Kind<KIND>;
     constexpr int PER = 16 / K::ESZ;  // elements per global load
 #pragma unroll
@@ -449,9 +481,10 @@ __device__ __forceinline__ void lds_store(uint8_t* lds, uint32_t wbase, const KL
 
 // Read this thread's pieces of the tile back from LDS, transposed, and store
 // them to the output, guarded at the matrix edge as EDGE says.
-template <int KIND, bool PADDED, int EDGE>
+template <int KIND, bool PADDED, int EDGE, bool CACHED>
 __device__ __forceinline__ void lds_read_store(const uint8_t* lds, uint32_t rbase, const KLayout& L,
-                                               const StepMoves& mv, const TileIo<EDGE, Kind<KIND>::ESZ>& io, int t) {
+                                               const StepMoves& mv, const TileIo<EDGE, Kind<KIND>::ESZ, CACHED>& io,
+                                               int t) {
     using K = Kind<KIND>;
     if constexpr (K::ESZ == 4 && (KIND == SWZ_READ_SCALAR_COL || is_narrow(KIND))) {
         // Task j: four rows of one source column -> 16 bytes of an output row.
@@ -610,8 +643,8 @@ __device__ __forceinline__ int after_loads(int t) {
     return t;
 }
 
-template <int KIND, int FILL, int EDGE>
-__device__ __forceinline__ void convert_tile(const TileIo<EDGE, Kind<KIND>::ESZ>& io, uint8_t* lds, const KLayout& L,
+template <int KIND, int FILL, int EDGE, bool CACHED>
+__device__ __forceinline__ void convert_tile(const TileIo<EDGE, Kind<KIND>::ESZ, CACHED>& io, uint8_t* lds, const KLayout& L,
                                              const StepMoves& mv, int t) {
     using K = Kind<KIND>;
     constexpr bool PADDED = FILL == kPadded;
@@ -643,19 +676,48 @@ __device__ __forceinline__ void convert_tile(const TileIo<EDGE, Kind<KIND>::ESZ>
 //              out the guarded path, and one past the matrix only the barrier.
 //              It replaces kInterior + kEdge where the rows leave edge tiles,
 //              so that those cost no launch of their own.
+//   kBlocksXcd: kBlocks for output row pitches that are not multiples of
+//              64 bytes (partial_line_output).  Tiles then share 64-byte
+//              pieces of output lines with their neighbours, which memory
+//              serves as partial writes unless both halves meet in one L2
+//              first.  Workgroups are dispatched to the eight XCDs (each
+//              with its own L2) in turn, so this grid renumbers them:
+//              workgroups i, i + 8, i + 16, ..., which share an XCD, take
+//              consecutive blocks, and the accesses go through the caches.
 //   kAll3D / kAll1D: every tile, 3-D as kInterior or a 1-D chunk of the
 //              linear tile order (grids beyond the hardware's y / z limits,
 //              sizes past the 32-bit whole-tile path, unaligned pitches).
-enum Grid { kAll3D = 0, kAll1D = 1, kInterior = 2, kEdge = 3, kBlocks = 4 };
+enum Grid { kAll3D = 0, kAll1D = 1, kInterior = 2, kEdge = 3, kBlocks = 4, kBlocksXcd = 5 };
 
 // Tile (tr, tc) of a 3-D diagonal-order grid with n tile columns: tc = (y +
 // f) mod n, f = (x num) >> sh, y < n.  One conditional subtract, and a
 // division only when f reaches n (a uniform branch laid out of line).
-__device__ __forceinline__ uint32_t diagonal_column(uint32_t n, TileOrder O) {
-    uint32_t f = (blockIdx.x * O.num) >> O.sh;
+__device__ __forceinline__ uint32_t diagonal_column_at(uint32_t x, uint32_t y, uint32_t n, TileOrder O) {
+    uint32_t f = (x * O.num) >> O.sh;
     if (__builtin_expect(f >= n, 0)) f %= n;
-    const uint32_t c = blockIdx.y + f;
+    const uint32_t c = y + f;
     return c >= n ? c - n : c;
+}
+__device__ __forceinline__ uint32_t diagonal_column(uint32_t n, TileOrder O) {
+    return diagonal_column_at(blockIdx.x, blockIdx.y, n, O);
+}
+
+// The XCDs of the chip (each with its own L2), which take the workgroups of
+// a launch in turn by their linear number.
+constexpr uint32_t kXcds = 8;
+
+// kBlocksXcd's renumbering of this workgroup's (x, y, z): linear number
+// L = x + gx (y + gy z) on XCD L mod 8 becomes the (L / 8)-th of that XCD's
+// run of consecutive numbers (runs of G / 8, the first G mod 8 one longer),
+// decoded back to (x, y, z).  One-to-one for any grid.
+__device__ __forceinline__ void xcd_renumber(uint32_t& x, uint32_t& y, uint32_t& z) {
+    const uint64_t gx = gridDim.x, gy = gridDim.y, g = gx * gy * gridDim.z;
+    const uint64_t l = blockIdx.x + gx * (blockIdx.y + gy * static_cast<uint64_t>(blockIdx.z));
+    const uint64_t k = l % kXcds, q = g / kXcds, rem = g % kXcds;
+    const uint64_t m = k * q + (k < rem ? k : rem) + l / kXcds;
+    x = static_cast<uint32_t>(m % gx);
+    y = static_cast<uint32_t>((m / gx) % gy);
+    z = static_cast<uint32_t>(m / (gx * gy));
 }
 
 // Edge tile e (of one batch entry) outside the first full_r x full_c tiles
@@ -685,7 +747,7 @@ __device__ __forceinline__ void edge_tile(int64_t e, int64_t full_r, int64_t ful
 // SGPRs) are all a whole tile of a 3-D launch reads before its first load.
 template <int KIND, int GRID>
 constexpr int stack_in() {
-    return GRID == kInterior || GRID == kBlocks ? stack_of<KIND>() * stack_c_of<KIND>() : 1;
+    return GRID == kInterior || GRID == kBlocks || GRID == kBlocksXcd ? stack_of<KIND>() * stack_c_of<KIND>() : 1;
 }
 
 template <int KIND, int FILL, bool ALIGNED, int GRID>
@@ -708,13 +770,14 @@ __global__ __launch_bounds__((Kind<KIND>::NT * stack_in<KIND, GRID>())) void k_c
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v + g * TILE_V);
     const int t = STACK == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) & (K::NT - 1);
     const TileOrder O{order_num, order_sh};
+    constexpr bool CACHED = GRID == kBlocksXcd;
 
     // A whole tile: batch entry b's rows follow entry b - 1's in both
     // matrices, so the tile is (b rows + r0, c0) of the source and (b cols +
     // c0, r0) of the output, in 32 bits (the host's FastPath says so).
     auto whole = [&](uint32_t b32, uint32_t tr32, uint32_t tc32) {
         const uint32_t r0 = tr32 * K::TR, c0 = tc32 * K::TC;
-        const TileIo<kFull, E> io{src + (static_cast<uint64_t>(b32 * rows32 + r0) * sp + c0 * E),
+        const TileIo<kFull, E, CACHED> io{src + (static_cast<uint64_t>(b32 * rows32 + r0) * sp + c0 * E),
                                   dst + (static_cast<uint64_t>(b32 * cols32 + c0) * dp + r0 * E), 0, 0, 0, 0, sp, dp};
         convert_tile<KIND, FILL, kFull>(io, lds, L, mv, t);
     };
@@ -723,7 +786,7 @@ __global__ __launch_bounds__((Kind<KIND>::NT * stack_in<KIND, GRID>())) void k_c
         const int64_t plane = rows * cols * E;
         constexpr int EDGE = ALIGNED ? kVec : kElem;
         convert_tile<KIND, FILL, EDGE>(
-            TileIo<EDGE, E>{src + b * plane, dst + b * plane, rows, cols, tr * K::TR, tc * K::TC, 0u, 0u}, lds, L, mv,
+            TileIo<EDGE, E, CACHED>{src + b * plane, dst + b * plane, rows, cols, tr * K::TR, tc * K::TC, 0u, 0u}, lds, L, mv,
             t);
     };
 
@@ -731,19 +794,21 @@ __global__ __launch_bounds__((Kind<KIND>::NT * stack_in<KIND, GRID>())) void k_c
         // tile g of the workgroup's SR x SC block (tiles_c32: blocks per row)
         constexpr int SR = stack_of<KIND>(), SC = stack_c_of<KIND>();
         whole(blockIdx.z, blockIdx.x * SR + g % SR, diagonal_column(tiles_c32, O) * SC + g / SR);
-    } else if constexpr (GRID == kBlocks) {
+    } else if constexpr (GRID == kBlocks || GRID == kBlocksXcd) {
         // As kInterior over blocks that may reach past the whole tiles
         // (tiles_c32: blocks per row, rounded up).  The tile test is uniform
         // across each wave (readfirstlane of g), so every wave branches as a
         // whole and runs exactly one barrier: its tile's, or its own where
         // the block reaches past the matrix.
         constexpr int SR = stack_of<KIND>(), SC = stack_c_of<KIND>();
+        uint32_t bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+        if constexpr (GRID == kBlocksXcd) xcd_renumber(bx, by, bz);
         const uint32_t gu = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(g));
-        const uint32_t tr = blockIdx.x * SR + gu % SR, tc = diagonal_column(tiles_c32, O) * SC + gu / SR;
+        const uint32_t tr = bx * SR + gu % SR, tc = diagonal_column_at(bx, by, tiles_c32, O) * SC + gu / SR;
         if (tr < full_r && tc < full_c)
-            whole(blockIdx.z, tr, tc);
+            whole(bz, tr, tc);
         else if (tr < tiles_r && tc < (cols + K::TC - 1) / K::TC)
-            guarded(blockIdx.z, tr, tc);
+            guarded(bz, tr, tc);
         else
             __syncthreads();
     } else if constexpr (GRID == kEdge) {
@@ -976,12 +1041,22 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
         if ((inner_r != tiles_r || inner_c != tiles_c) && fp.full_r > 0 && fp.full_c > 0 &&
             fits_3d(blocks_r, blocks_c, j.batch, K::NT * SR * SC)) {
             // edge tiles: all tiles in one launch of blocks
-            std::apply([&](auto... a) {
-                hipLaunchKernelGGL((k_convert<KIND, FILL, true, kBlocks>),
-                                   dim3(static_cast<unsigned>(blocks_r), static_cast<unsigned>(blocks_c),
-                                        static_cast<unsigned>(j.batch)),
-                                   dim3(K::NT * SR * SC), inner_pad, stream, a...);
-            }, args(static_cast<uint32_t>(blocks_c), 0, fp.full_r, fp.full_c));
+            const dim3 grid(static_cast<unsigned>(blocks_r), static_cast<unsigned>(blocks_c),
+                            static_cast<unsigned>(j.batch));
+            const auto a = args(static_cast<uint32_t>(blocks_c), 0, fp.full_r, fp.full_c);
+            if constexpr (FILL != kDirect && !is_narrow(KIND)) {
+                if (partial_line_output(j.rows, K::ESZ)) {
+                    std::apply([&](auto... v) {
+                        hipLaunchKernelGGL((k_convert<KIND, FILL, true, kBlocksXcd>), grid, dim3(K::NT * SR * SC),
+                                           inner_pad, stream, v...);
+                    }, a);
+                    return;
+                }
+            }
+            std::apply([&](auto... v) {
+                hipLaunchKernelGGL((k_convert<KIND, FILL, true, kBlocks>), grid, dim3(K::NT * SR * SC), inner_pad,
+                                   stream, v...);
+            }, a);
             return;
         }
         if (inner_r > 0 && inner_c > 0 && fits_3d(inner_r / SR, inner_c / SC, j.batch, K::NT * SR * SC)) {

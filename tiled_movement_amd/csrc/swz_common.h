@@ -549,6 +549,18 @@ constexpr int interior_stack_cols(int kind) {
     return kind == SWZ_READ_SCALAR_COL ? 2 : 1;
 }
 
+// Whether a transpose of `rows` source rows of esz-byte elements writes its
+// output rows at a pitch that is not a whole number of 64-byte pieces, at a
+// size where the XCD-grouped block grid pays (tile kernels with 16-byte
+// aligned rows).  Output rows 32 bytes off such a piece left each piece
+// half-written by two workgroups and ran at 0.45-0.60 of a copy; grouping
+// the neighbours on one XCD's L2 brought 0.63-0.75 (fp32, 16-bit and byte
+// matrices of 2,000 to 9,000 rows).  With fewer rows the grouping lost up to
+// 13%, and a source pitch off the 64-byte pieces alone did not gain.
+constexpr bool partial_line_output(int64_t rows, int esz) {
+    return (rows * esz) % 64 != 0 && rows >= 2000;
+}
+
 template <int KIND>
 constexpr bool direct_split() {
     using D = Direct<KIND>;
