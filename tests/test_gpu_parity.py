@@ -363,6 +363,37 @@ def test_seeded_random_conversions():
             T.swz_set_tile_order(b, r, c, esz, T.READ_AUTO, -1)
 
 
+def test_misaligned_output_rows_through_the_xcd_grouped_grid():
+    """Output rows that are not whole 64-byte pieces, from 2,000 rows on,
+    run through the XCD-renumbered block grid with cached accesses: every
+    element size, batches (the renumbering spans the z dimension), partial
+    tiles, padded and plain layouts, pinned orders; plus an unaligned-pitch
+    shape of each narrow element size (the unaligned vector accesses)."""
+    cases = [(1, 2008, 1000, 4), (3, 2056, 136, 4), (2, 2008, 520, 2), (1, 2064, 528, 1), (2, 4104, 264, 4)]
+    for b, r, c, esz in cases:
+        gen = {4: W.fp32_matrix, 2: W.fp16_matrix, 1: W.u8_matrix}[esz]
+        a = gen(b * r, c, seed=r + c).reshape(b, r, c)
+        want = O.convert_layout(a)
+        for layout in LAYOUTS:
+            for order in (None, T.ORDER_DIAGONAL, T.ORDER_SLOPE_32):
+                announce("misaligned output rows", (b, r, c, esz), layout, order)
+                if order is not None:
+                    T.swz_set_tile_order(b, r, c, esz, T.READ_AUTO, order)
+                try:
+                    src = to_dev(a)
+                    dst = torch.empty((b, c, r), dtype=src.dtype, device=DEV)
+                    T.swz_convert_layout(src, dst, b, r, c, esz, layout)
+                    torch.cuda.synchronize()
+                    assert np.array_equal(from_dev(dst, a), want), ((b, r, c, esz), layout, order)
+                finally:
+                    T.swz_set_tile_order(b, r, c, esz, T.READ_AUTO, -1)
+    for r, c, esz in [(2001, 1003, 1), (2002, 1001, 2), (3003, 517, 1)]:
+        gen = {2: W.fp16_matrix, 1: W.u8_matrix}[esz]
+        a = gen(r, c, seed=r)
+        announce("unaligned rows", (r, c, esz))
+        check_transpose(a, esz, "swizzle", T.READ_AUTO)
+
+
 def test_seeded_random_operand_pairs():
     """40 seeded random operand pairs (m, n multiples of 16 up to 592, k a
     multiple of 32 up to 704) staged in one launch in a random layout."""
