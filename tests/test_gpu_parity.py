@@ -367,8 +367,9 @@ def test_misaligned_output_rows_through_the_xcd_grouped_grid():
     """Output rows that are not whole 64-byte pieces, from 2,000 rows on,
     run through the XCD-renumbered block grid with cached accesses: every
     element size, batches (the renumbering spans the z dimension), partial
-    tiles, padded and plain layouts, pinned orders; plus an unaligned-pitch
-    shape of each narrow element size (the unaligned vector accesses)."""
+    tiles, padded and plain layouts, pinned orders; plus unaligned pitches
+    of every element size (the element path on the same renumbered grid,
+    with unaligned vector accesses for 1- and 2-byte elements)."""
     cases = [(1, 2008, 1000, 4), (3, 2056, 136, 4), (2, 2008, 520, 2), (1, 2064, 528, 1), (2, 4104, 264, 4)]
     for b, r, c, esz in cases:
         gen = {4: W.fp32_matrix, 2: W.fp16_matrix, 1: W.u8_matrix}[esz]
@@ -387,8 +388,8 @@ def test_misaligned_output_rows_through_the_xcd_grouped_grid():
                     assert np.array_equal(from_dev(dst, a), want), ((b, r, c, esz), layout, order)
                 finally:
                     T.swz_set_tile_order(b, r, c, esz, T.READ_AUTO, -1)
-    for r, c, esz in [(2001, 1003, 1), (2002, 1001, 2), (3003, 517, 1)]:
-        gen = {2: W.fp16_matrix, 1: W.u8_matrix}[esz]
+    for r, c, esz in [(2001, 1003, 1), (2002, 1001, 2), (3003, 517, 1), (2001, 333, 4)]:
+        gen = {4: W.fp32_matrix, 2: W.fp16_matrix, 1: W.u8_matrix}[esz]
         a = gen(r, c, seed=r)
         announce("unaligned rows", (r, c, esz))
         check_transpose(a, esz, "swizzle", T.READ_AUTO)

@@ -105,12 +105,15 @@ __device__ __forceinline__ uint32_t pair_col(const V& a, const V& b, int j) {
 typedef u32x4 __attribute__((aligned(1))) u32x4_unaligned;
 
 // 16 bytes = 16/ESZ consecutive elements of one row, zero outside the matrix.
-template <int ESZ>
+template <int ESZ, bool CACHED = false>
 __device__ __forceinline__ u32x4 load16_guarded(const uint8_t* S, int64_t row, int64_t col, int64_t rows,
                                                 int64_t cols) {
     constexpr int N = 16 / ESZ;
-    if (ESZ < 4 && row < rows && col + N <= cols)
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4_unaligned*>(S + (row * cols + col) * ESZ));
+    if (ESZ < 4 && row < rows && col + N <= cols) {
+        const auto* p = reinterpret_cast<const u32x4_unaligned*>(S + (row * cols + col) * ESZ);
+        if constexpr (CACHED) return *p;
+        else return __builtin_nontemporal_load(p);
+    }
     uint32_t e[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
@@ -137,12 +140,14 @@ __device__ __forceinline__ u32x4 load16_guarded(const uint8_t* S, int64_t row, i
 
 // 16 bytes = 16/ESZ consecutive elements of one output row; only those
 // inside the matrix are written.
-template <int ESZ>
+template <int ESZ, bool CACHED = false>
 __device__ __forceinline__ void store16_guarded(uint8_t* D, int64_t row, int64_t col, int64_t nrows, int64_t ncols,
                                                 const u32x4& o) {
     if (row >= nrows) return;
     if (ESZ < 4 && col + 16 / ESZ <= ncols) {
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4_unaligned*>(D + (row * ncols + col) * ESZ));
+        auto* p = reinterpret_cast<u32x4_unaligned*>(D + (row * ncols + col) * ESZ);
+        if constexpr (CACHED) *p = o;
+        else __builtin_nontemporal_store(o, p);
         return;
     }
     if (ESZ == 1) {
@@ -174,7 +179,7 @@ __device__ __forceinline__ u32x4 load16_edge(const uint8_t* S, int64_t row, int6
     if constexpr (EDGE == kFull) return gload16c<CACHED>(S + (row * cols + col) * ESZ);
     if constexpr (EDGE == kVec)
         return row < rows && col < cols ? gload16c<CACHED>(S + (row * cols + col) * ESZ) : u32x4{0u, 0u, 0u, 0u};
-    return load16_guarded<ESZ>(S, row, col, rows, cols);
+    return load16_guarded<ESZ, CACHED>(S, row, col, rows, cols);
 }
 
 template <int EDGE, int ESZ, bool CACHED = false>
@@ -185,7 +190,7 @@ __device__ __forceinline__ void store16_edge(uint8_t* D, int64_t row, int64_t co
     } else if constexpr (EDGE == kVec) {
         if (row < nrows && col < ncols) gstore16c<CACHED>(D + (row * ncols + col) * ESZ, v);
     } else {
-        store16_guarded<ESZ>(D, row, col, nrows, ncols, v);
+        store16_guarded<ESZ, CACHED>(D, row, col, nrows, ncols, v);
     }
 }
 
@@ -687,7 +692,9 @@ __device__ __forceinline__ void convert_tile(const TileIo<EDGE, Kind<KIND>::ESZ,
 //   kAll3D / kAll1D: every tile, 3-D as kInterior or a 1-D chunk of the
 //              linear tile order (grids beyond the hardware's y / z limits,
 //              sizes past the 32-bit whole-tile path, unaligned pitches).
-enum Grid { kAll3D = 0, kAll1D = 1, kInterior = 2, kEdge = 3, kBlocks = 4, kBlocksXcd = 5 };
+//   kAll3DXcd: kAll3D renumbered and cached as kBlocksXcd, for unaligned
+//              pitches whose output rows are partial_line_output.
+enum Grid { kAll3D = 0, kAll1D = 1, kInterior = 2, kEdge = 3, kBlocks = 4, kBlocksXcd = 5, kAll3DXcd = 6 };
 
 // Tile (tr, tc) of a 3-D diagonal-order grid with n tile columns: tc = (y +
 // f) mod n, f = (x num) >> sh, y < n.  One conditional subtract, and a
@@ -760,7 +767,8 @@ __global__ __launch_bounds__((Kind<KIND>::NT * stack_in<KIND, GRID>())) void k_c
     using K = Kind<KIND>;
     constexpr int E = K::ESZ;
     static_assert(FILL != kDirect || ALIGNED, "the direct fill needs 16-byte aligned rows");
-    static_assert(ALIGNED || GRID == kAll3D || GRID == kAll1D, "unaligned pitches take the element-wise path");
+    static_assert(ALIGNED || GRID == kAll3D || GRID == kAll3DXcd || GRID == kAll1D,
+                  "unaligned pitches take the element-wise path");
     constexpr int STACK = stack_in<KIND, GRID>();
     constexpr int TILE_V = (LdsTile<KIND, FILL>::BYTES + 15) / 16;
     __shared__ u32x4 lds_v[STACK * TILE_V];
@@ -770,7 +778,7 @@ __global__ __launch_bounds__((Kind<KIND>::NT * stack_in<KIND, GRID>())) void k_c
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v + g * TILE_V);
     const int t = STACK == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) & (K::NT - 1);
     const TileOrder O{order_num, order_sh};
-    constexpr bool CACHED = GRID == kBlocksXcd;
+    constexpr bool CACHED = GRID == kBlocksXcd || GRID == kAll3DXcd;
 
     // A whole tile: batch entry b's rows follow entry b - 1's in both
     // matrices, so the tile is (b rows + r0, c0) of the source and (b cols +
@@ -821,10 +829,12 @@ __global__ __launch_bounds__((Kind<KIND>::NT * stack_in<KIND, GRID>())) void k_c
         guarded(b, tr, tc);
     } else {
         int64_t b, tr, tc;
-        if constexpr (GRID == kAll3D) {
-            b = blockIdx.z;
-            tr = blockIdx.x;
-            tc = diagonal_column(tiles_c32, O);
+        if constexpr (GRID == kAll3D || GRID == kAll3DXcd) {
+            uint32_t bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+            if constexpr (GRID == kAll3DXcd) xcd_renumber(bx, by, bz);
+            b = bz;
+            tr = bx;
+            tc = diagonal_column_at(bx, by, tiles_c32, O);
         } else {
             decode_tile<true>(tile0 + blockIdx.x, tiles_r, tiles_c32, O, b, tr, tc);
         }
@@ -1076,12 +1086,21 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
         }
     } else {
         if (fits_3d(tiles_r, tiles_c, j.batch, K::NT)) {
-            std::apply([&](auto... a) {
-                hipLaunchKernelGGL((k_convert<KIND, FILL, false, kAll3D>),
-                                   dim3(static_cast<unsigned>(tiles_r), static_cast<unsigned>(tiles_c),
-                                        static_cast<unsigned>(j.batch)),
-                                   block, lds_pad, stream, a...);
-            }, args(static_cast<uint32_t>(tiles_c), 0, fp.full_r, fp.full_c));
+            const dim3 grid(static_cast<unsigned>(tiles_r), static_cast<unsigned>(tiles_c),
+                            static_cast<unsigned>(j.batch));
+            const auto a = args(static_cast<uint32_t>(tiles_c), 0, fp.full_r, fp.full_c);
+            if constexpr (!is_narrow(KIND)) {
+                if (partial_line_output(j.rows, K::ESZ)) {
+                    std::apply([&](auto... v) {
+                        hipLaunchKernelGGL((k_convert<KIND, FILL, false, kAll3DXcd>), grid, block, lds_pad, stream,
+                                           v...);
+                    }, a);
+                    return;
+                }
+            }
+            std::apply([&](auto... v) {
+                hipLaunchKernelGGL((k_convert<KIND, FILL, false, kAll3D>), grid, block, lds_pad, stream, v...);
+            }, a);
             return;
         }
     }
