@@ -99,9 +99,10 @@ __device__ __forceinline__ uint32_t pair_col(const V& a, const V& b, int j) {
 // the unaligned memory access mode, and the compiler emits a single dwordx4
 // for an access that only promises byte alignment.  For 1- and 2-byte
 // elements that replaces 16 or 8 accesses by one (bytes 5800 x 5800: 0.13 ->
-// 0.38 of a copy; fp16 5801 x 5801: 0.20 -> 0.35); 4-byte elements keep
-// their four aligned dword accesses, which measured faster (fp32 4001 x
-// 4001: 0.44 against 0.37).
+// 0.38 of a copy; fp16 5801 x 5801: 0.20 -> 0.35).  4-byte elements keep
+// their four aligned dword accesses with non-temporal accesses (fp32 4001 x
+// 4001: 0.44 against 0.37 with vectors), but take the vector too on the
+// cached XCD-grouped grid, where it is the faster (0.45 -> 0.64).
 typedef u32x4 __attribute__((aligned(1))) u32x4_unaligned;
 
 // 16 bytes = 16/ESZ consecutive elements of one row, zero outside the matrix.
@@ -109,7 +110,7 @@ template <int ESZ, bool CACHED = false>
 __device__ __forceinline__ u32x4 load16_guarded(const uint8_t* S, int64_t row, int64_t col, int64_t rows,
                                                 int64_t cols) {
     constexpr int N = 16 / ESZ;
-    if (ESZ < 4 && row < rows && col + N <= cols) {
+    if ((ESZ < 4 || CACHED) && row < rows && col + N <= cols) {
         const auto* p = reinterpret_cast<const u32x4_unaligned*>(S + (row * cols + col) * ESZ);
         if constexpr (CACHED) return *p;
         else return __builtin_nontemporal_load(p);
@@ -144,7 +145,7 @@ template <int ESZ, bool CACHED = false>
 __device__ __forceinline__ void store16_guarded(uint8_t* D, int64_t row, int64_t col, int64_t nrows, int64_t ncols,
                                                 const u32x4& o) {
     if (row >= nrows) return;
-    if (ESZ < 4 && col + 16 / ESZ <= ncols) {
+    if ((ESZ < 4 || CACHED) && col + 16 / ESZ <= ncols) {
         auto* p = reinterpret_cast<u32x4_unaligned*>(D + (row * ncols + col) * ESZ);
         if constexpr (CACHED) *p = o;
         else __builtin_nontemporal_store(o, p);
