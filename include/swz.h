@@ -124,13 +124,22 @@ enum swz_layout {
  *               and transposes them in registers into up to four 16-byte
  *               output pieces; tiles of 1 KiB per column up to 4 columns,
  *               8 KiB at 8 and 16 KiB above (64, 128 and 256 lanes).
- *  AUTO       : 4-byte -> NARROW<cols> when cols is 1, 2, 4, 8 or 16, else
- *               SCALAR_COL; 2-byte -> HNARROW<cols> when cols is a power of
- *               two up to 32, else B64_TR16 when cols <= 64, B128_8X8 when
- *               cols <= 128, B64_TR16 when cols <= 256 and B64_4X4 above
- *               (the faster of the two 64x64 kinds at those widths);
- *               1-byte -> BNARROW<cols> when cols is a power of two
- *               up to 64, else B64_TR8. */
+ *  ROWS       : rows of any width up to 64 bytes (any element size):
+ *               tiles of whole rows copied flat into LDS (up to 16 KiB),
+ *               each lane gathering 4 bytes of consecutive rows of one
+ *               column, each wave storing 256 contiguous bytes of an output
+ *               row.  No swizzle (odd widths read conflict-free as they
+ *               are); layouts SWIZZLE and PLAIN only, with no parameters or
+ *               B = 0.  For the widths that are not powers of two.
+ *  AUTO       : 4-byte -> NARROW<cols> when cols is 1, 2, 4, 8 or 16, ROWS
+ *               for the other widths up to 16, else SCALAR_COL; 2-byte ->
+ *               HNARROW<cols> when cols is a power of two up to 32, ROWS
+ *               for the other widths up to 32, else B64_TR16 when
+ *               cols <= 64, B128_8X8 when cols <= 128, B64_TR16 when
+ *               cols <= 256 and B64_4X4 above (the faster of the two 64x64
+ *               kinds at those widths); 1-byte -> BNARROW<cols> when cols
+ *               is a power of two up to 64, ROWS for the other widths up to
+ *               64, else B64_TR8. */
 /* The read kind is an argument of its own (read_kind, just before
  * p_or_null, in swz_transpose, swz_convert_layout, swz_tune_tile_order and
  * the tile-order calls), and it names a kernel, not a class of read.  The
@@ -169,7 +178,8 @@ enum swz_read_kind {
     SWZ_READ_BNARROW8 = 20,
     SWZ_READ_BNARROW16 = 21,
     SWZ_READ_BNARROW32 = 22,
-    SWZ_READ_BNARROW64 = 23
+    SWZ_READ_BNARROW64 = 23,
+    SWZ_READ_ROWS = 24
 };
 
 enum swz_frag_kind { SWZ_FRAG_MFMA_F32_16X16X32_BF16 = 0 };

@@ -11,6 +11,7 @@
 namespace swz {
 
 hipError_t launch_convert(int, const ConvertJob&, hipStream_t) { return hipSuccess; }
+hipError_t launch_rows(int, const ConvertJob&, hipStream_t) { return hipSuccess; }
 hipError_t launch_stage(const StageJob&, hipStream_t) { return hipSuccess; }
 hipError_t launch_gemm_frag(const void*, const void*, float*, int64_t, int64_t, int64_t, hipStream_t) {
     return hipSuccess;

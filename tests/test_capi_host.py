@@ -544,8 +544,10 @@ def test_narrow_kind_validation():
                     (16, T.READ_NARROW16)):
         p = T.swz_plan(0, 1000, c, 4, "swizzle")
         assert p["read_kind"] == kind and p["tile"] == (1024 // c, c) and p["lds_bytes"] == 4096
-    for c in (3, 12, 32, 64):
+    for c in (32, 64, 17):
         assert T.swz_plan(0, 1000, c, 4, "swizzle")["read_kind"] == T.READ_SCALAR_COL
+    for c in (3, 12):  # other widths up to 64 bytes: flat whole rows
+        assert T.swz_plan(0, 1000, c, 4, "swizzle")["read_kind"] == T.READ_ROWS
     # 2- and 1-byte elements: whole-row tiles for rows of up to 64 bytes
     for esz, kinds in ((2, NARROW2), (1, NARROW1)):
         for i, kind in enumerate(kinds):
@@ -559,6 +561,8 @@ def test_narrow_kind_validation():
         assert f(A, B, 1, 256, c, 6 - esz, 0, kinds[-1], None, None) == EINVAL  # element size differs
     assert T.swz_plan(0, 1000, 64, 2)["read_kind"] == T.READ_B64_TR16
     assert T.swz_plan(0, 1000, 48, 2)["read_kind"] == T.READ_B64_TR16
+    assert T.swz_plan(0, 1000, 24, 2)["read_kind"] == T.READ_ROWS
+    assert T.swz_plan(0, 1000, 63, 1)["read_kind"] == T.READ_ROWS
     assert T.swz_plan(0, 1000, 128, 2)["read_kind"] == T.READ_B128_8X8
     assert T.swz_plan(0, 1000, 96, 1)["read_kind"] == T.READ_B64_TR8
     assert T.swz_plan(0, 1000, 128, 1)["read_kind"] == T.READ_B64_TR8
@@ -681,3 +685,38 @@ def test_auto_read_kind_picks_the_kernels_the_workloads_are_timed_with():
     for op, rows, cols, esz, kind in cases:
         for layout in ("swizzle", "pad", "plain"):
             assert T.swz_plan(op, rows, cols, esz, layout, T.READ_AUTO)["read_kind"] == kind, (rows, cols, esz)
+
+
+def test_rows_kind_plan_and_validation():
+    """Flat whole-row tiles (SWZ_READ_ROWS): any width up to 64 bytes, as
+    many rows as fit in 16 KiB in groups of 64 lane-words (4 bytes of rows
+    each), a word-offset swizzle for even widths, SWIZZLE and PLAIN layouts
+    only; an explicit swizzle must have M = 0 and B <= S <= 11."""
+    f = lib.swz_convert_layout
+    for esz, cmax in ((4, 16), (2, 32), (1, 64)):
+        group = 64 * (4 // esz)
+        for c in range(1, cmax + 1):
+            p = T.swz_plan(0, 100000, c, esz, "swizzle", T.READ_ROWS)
+            tr = 16384 // (c * esz) // group * group
+            assert p["read_kind"] == T.READ_ROWS and p["tile"] == (tr, c) and p["lds_bytes"] == tr * c * esz
+            B, M, S = p["params"]
+            if c % 2:  # odd widths read conflict-free unswizzled
+                assert (B, M, S) == (0, 0, 0), (c, p["params"])
+            elif c % 4 == 0:  # a swizzle of word offsets whose source lies above the bank bits
+                assert B >= 2 and M == 0 and B <= S <= 11, (c, p["params"])
+            else:  # the search's pick, whichever it is, a valid word-offset swizzle or none
+                assert M == 0 and (B == 0 or B <= S <= 11), (c, p["params"])
+            assert p["pad_elems"] == 0 and p["threads"] == 256 and p["aligned"]
+            assert tr >= group and tr * c * esz <= 16384
+            plain = T.swz_plan(0, 100000, c, esz, "plain", T.READ_ROWS)
+            assert plain["tile"] == (tr, c) and plain["params"] == (0, 0, 0)
+        assert f(A, B, 1, 256, cmax + 1, esz, 0, T.READ_ROWS, None, None) == EINVAL  # wider than 64 bytes
+        assert f(A, B, 1, 256, 3, esz, T.LAYOUT_PAD, T.READ_ROWS, None, None) == EUNSUP
+        assert f(A, B, 1, 256, 3, esz, T.LAYOUT_SWIZZLE_DIRECT, T.READ_ROWS, None, None) == EUNSUP
+        assert f(A, B, 1, 256, 3, esz, 0, T.READ_ROWS, ctypes.byref(P(3, 2, 3)), None) == EINVAL  # M != 0
+        assert f(A, B, 1, 256, 3, esz, 0, T.READ_ROWS, ctypes.byref(P(3, 0, 2)), None) == EINVAL  # S < B
+        assert f(A, B, 1, 256, 3, esz, 0, T.READ_ROWS, ctypes.byref(P(1, 0, 12)), None) == EINVAL  # S past the tile
+        assert T.swz_plan(0, 256, 6, esz, "swizzle", T.READ_ROWS, (2, 0, 7))["params"] == (2, 0, 7)
+        assert T.swz_plan(0, 256, 3, esz, "swizzle", T.READ_ROWS, (0, 0, 0))["read_kind"] == T.READ_ROWS
+        assert T.swz_plan(0, 257, 3, esz, "swizzle", T.READ_ROWS)["aligned"]  # any pitch takes the same kernel
+    assert lib.swz_choose(4, 4, 32, 32, T.READ_ROWS, ctypes.byref(P())) == EINVAL  # not a swizzled kind

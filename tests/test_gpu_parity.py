@@ -395,6 +395,45 @@ def test_misaligned_output_rows_through_the_xcd_grouped_grid():
         check_transpose(a, esz, "swizzle", T.READ_AUTO)
 
 
+def test_rows_kind_every_width():
+    """Flat whole-row tiles (SWZ_READ_ROWS, and AUTO for widths that are
+    not powers of two): every width up to 64 bytes of every element size,
+    row counts around the lane-word groups and the tile, batches, a base
+    pointer one element off 16 bytes, both layouts."""
+    rng = np.random.default_rng(2028)
+    gen = {4: W.fp32_matrix, 2: W.fp16_matrix, 1: W.u8_matrix}
+    for esz, cmax in ((4, 16), (2, 32), (1, 64)):
+        group = 64 * (4 // esz)
+        for c in range(1, cmax + 1):
+            tr = 16384 // (c * esz) // group * group
+            for rows in sorted({1, group - 1, group + 1, tr, tr + 1, 2 * tr + int(rng.integers(1, group))}):
+                b = 1 + (c + rows) % 3
+                a = gen[esz](b * rows, c, seed=c + rows).reshape(b, rows, c)
+                want = O.convert_layout(a)
+                for layout, kind, off in (("swizzle", T.READ_ROWS, 0), ("plain", T.READ_AUTO, 1)):
+                    if kind == T.READ_AUTO and (c & (c - 1)) == 0:
+                        kind = T.READ_ROWS  # AUTO takes the swizzled kinds for powers of two
+                    announce("rows kind", esz, (b, rows, c), layout, off)
+                    flat = np.concatenate([np.zeros(off, a.dtype), a.reshape(-1)])
+                    src = to_dev(flat)
+                    dst = torch.zeros(off + a.size, dtype=src.dtype, device=DEV)
+                    T.swz_convert_layout(src[off:], dst[off:], b, rows, c, esz, layout, kind)
+                    torch.cuda.synchronize()
+                    got = from_dev(dst, a)
+                    assert np.array_equal(got[off:].reshape(b, c, rows), want), (esz, (b, rows, c), layout, off)
+                    assert not got[:off].any()
+    # caller-given swizzles of word offsets
+    for esz, c in ((4, 12), (2, 6), (2, 24), (1, 48), (1, 10)):
+        a = gen[esz](3000, c, seed=c).reshape(1, 3000, c)
+        for params in ((1, 0, 5), (3, 0, 6), (5, 0, 11), (0, 0, 0)):
+            announce("rows kind params", esz, c, params)
+            src = to_dev(a)
+            dst = torch.empty((1, c, 3000), dtype=src.dtype, device=DEV)
+            T.swz_convert_layout(src, dst, 1, 3000, c, esz, "swizzle", T.READ_ROWS, params)
+            torch.cuda.synchronize()
+            assert np.array_equal(from_dev(dst, a), O.convert_layout(a)), (esz, c, params)
+
+
 def test_seeded_random_operand_pairs():
     """40 seeded random operand pairs (m, n multiples of 16 up to 592, k a
     multiple of 32 up to 704) staged in one launch in a random layout."""

@@ -27,6 +27,7 @@ READ_NARROW1, READ_NARROW2, READ_NARROW4, READ_NARROW8, READ_NARROW16 = 6, 7, 8,
 READ_HNARROW1, READ_HNARROW2, READ_HNARROW4, READ_HNARROW8, READ_HNARROW16, READ_HNARROW32 = 11, 12, 13, 14, 15, 16
 READ_BNARROW1, READ_BNARROW2, READ_BNARROW4, READ_BNARROW8, READ_BNARROW16, READ_BNARROW32, READ_BNARROW64 = (
     17, 18, 19, 20, 21, 22, 23)
+READ_ROWS = 24
 FRAG_MFMA_F32_16X16X32_BF16 = 0
 ORDER_DIAGONAL, ORDER_HALF_DIAGONAL, ORDER_COLUMNS, ORDER_STEEP_DIAGONAL = 0, 1, 2, 3
 ORDER_SLOPE_8, ORDER_SLOPE_16, ORDER_SLOPE_32 = 4, 5, 6

@@ -28,6 +28,7 @@ SOURCES = [
     "kernels_gemm.hip",
     "kernels_gemm_tiles.hip",
     "kernels_map.hip",
+    "kernels_rows.hip",
     "kernels_copy.hip",
     "lds_probe.hip",
 ]

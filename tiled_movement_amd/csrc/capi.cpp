@@ -84,10 +84,14 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     if (op == 0) {
         if (esz != 1 && esz != 2 && esz != 4) return SWZ_EINVAL;
         if (kind == SWZ_READ_AUTO) {
-            // whole-row tiles for rows of 1 to 64 bytes (a power of two)
-            const bool narrow = cols >= 1 && (cols & (cols - 1)) == 0 && cols * esz <= 64;
+            // whole-row tiles for rows of 1 to 64 bytes: the swizzled kinds
+            // for power-of-two widths, flat rows for the others
+            const bool fits = cols >= 1 && cols * esz <= 64;
+            const bool narrow = fits && (cols & (cols - 1)) == 0;
             const int lc = ilog2(cols);
-            if (esz == 4)
+            if (fits && !narrow)
+                kind = SWZ_READ_ROWS;
+            else if (esz == 4)
                 kind = narrow ? SWZ_READ_NARROW1 + lc : SWZ_READ_SCALAR_COL;
             else if (esz == 2)
                 kind = narrow        ? SWZ_READ_HNARROW1 + lc
@@ -99,6 +103,28 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
                 kind = narrow ? SWZ_READ_BNARROW1 + lc : SWZ_READ_B64_TR8;
         }
         if (kind == SWZ_READ_MFMA_16X16X32) return SWZ_EINVAL;
+        if (kind == SWZ_READ_ROWS) {
+            // flat whole rows, swizzled on word offsets (M = 0, B <= S <=
+            // 11: a bit of the 16 KiB tile's word offset XORs into a lower
+            // one), or plain; no padded or direct layout
+            if (cols < 1 || cols * esz > 64) return SWZ_EINVAL;
+            if (layout == SWZ_LAYOUT_PAD || layout == SWZ_LAYOUT_SWIZZLE_DIRECT) return SWZ_EUNSUPPORTED;
+            if (p && p->B != 0 && (p->B < 0 || p->M != 0 || p->S < p->B || p->S > 11)) return SWZ_EINVAL;
+            swz_params q{0, 0, 0};
+            if (layout == SWZ_LAYOUT_SWIZZLE) q = p ? (p->B == 0 ? swz_params{0, 0, 0} : *p) : swz::rows_choice(static_cast<int>(cols));
+            std::memset(out, 0, sizeof(*out));
+            out->params = q;
+            out->read_kind = kind;
+            out->tile_rows = static_cast<int32_t>(swz::rows_tile_rows(cols, esz));
+            out->tile_cols = static_cast<int32_t>(cols);
+            out->layout = layout;
+            out->lds_bytes = out->tile_rows * static_cast<int32_t>(cols) * esz;
+            out->vec_bytes = 16;
+            out->aligned = 1;  // any pitch: unaligned rows take the same accesses
+            out->threads = 256;
+            out->interior_tiles = 1;
+            return SWZ_OK;
+        }
     } else {
         if (esz != 2) return SWZ_EINVAL;
         if (kind != SWZ_READ_AUTO && kind != SWZ_READ_MFMA_16X16X32) return SWZ_EINVAL;
@@ -273,6 +299,8 @@ SWZ_API int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, in
     if (overlaps(d_src, bytes, d_dst, bytes)) return SWZ_EINVAL;
     swz::ConvertJob job{d_src, d_dst, batch, rows, cols, layout_of(pl), pl.aligned != 0,
                         layout == SWZ_LAYOUT_SWIZZLE_DIRECT, pinned_order(pl.read_kind, batch, rows, cols)};
+    if (pl.read_kind == SWZ_READ_ROWS)
+        return hip_status(swz::launch_rows(elem_bytes, job, static_cast<hipStream_t>(stream)));
     return hip_status(swz::launch_convert(pl.read_kind, job, static_cast<hipStream_t>(stream)));
 }
 

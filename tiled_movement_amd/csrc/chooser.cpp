@@ -195,6 +195,60 @@ swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles) {
     return best;
 }
 
+namespace {
+
+uint32_t rows_swz(uint32_t w, uint32_t B, uint32_t S) { return w ^ ((w >> S) & ((1u << B) - 1u)); }
+
+// Extra cycles of the reads and writes of one rows tile under (B, S): four
+// wave steps of every column offset for the reads; four 64-lane groups of
+// 4-byte writes (word j of each lane's 16-byte vector) for a swizzled copy,
+// whose 16-byte vector writes are lane-linear (no conflicts) when B = 0.
+int64_t rows_cost(int cols, uint32_t B, uint32_t S, const BankModel& m) {
+    int64_t cyc = 0;
+    Access a{};
+    a.width = 4;
+    a.write = false;
+    for (int s = 0; s < 4; ++s)
+        for (int k = 0; k < cols; ++k) {
+            for (int t = 0; t < 64; ++t)
+                a.addr[t] = static_cast<int32_t>(4 * rows_swz(static_cast<uint32_t>((64 * s + t) * cols + k), B, S));
+            cyc += conflict_cycles(m, a);
+        }
+    if (B == 0) return cyc;
+    a.write = true;
+    for (int g = 0; g < 4; ++g)
+        for (int j = 0; j < 4; ++j) {
+            for (int t = 0; t < 64; ++t)
+                a.addr[t] = static_cast<int32_t>(4 * rows_swz(static_cast<uint32_t>(4 * (64 * g + t) + j), B, S));
+            cyc += cols * conflict_cycles(m, a) / 4;  // as many write as read instructions per tile
+        }
+    return cyc;
+}
+
+}  // namespace
+
+swz_params rows_choice(int cols) {
+    static std::once_flag once;
+    static swz_params table[65];
+    std::call_once(once, [] {
+        const BankModel& m = gfx950_bank_model();
+        for (int c = 1; c <= 64; ++c) {
+            swz_params best{0, 0, 0};
+            int64_t best_cyc = rows_cost(c, 0, 0, m);
+            for (int B = 1; B <= 5 && best_cyc > 0; ++B)
+                for (int S = B; S <= 8; ++S) {
+                    const int64_t cyc = rows_cost(c, B, S, m);
+                    if (cyc < best_cyc) {
+                        best_cyc = cyc;
+                        best = swz_params{B, 0, S};
+                    }
+                }
+            table[c] = best;
+        }
+    });
+    return cols >= 1 && cols <= 64 ? table[cols] : swz_params{0, 0, 0};
+}
+
 swz_params cached_choice(int kind) {
     static std::once_flag once;
     constexpr int kKinds = kNumKinds;

@@ -21,6 +21,14 @@ bool kind_info(int kind, KindInfo* out);
 void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64_t* wcyc, int64_t* rcyc,
                   bool direct = false);
 
+// Swizzle of SWZ_READ_ROWS tiles (rows of `cols` elements, 1-64, copied
+// flat): word w of the tile lives at w ^ ((w >> S) & (2^B - 1)) (M = 0).
+// Lanes of a read are cols words apart, so an even width meets conflicts
+// that the XOR of bits above the bank bits into the bank bits removes; odd
+// widths need none (B = 0).  Searched against the model's 4-byte reads of
+// that pattern and the 4-byte writes of the flat copy; cached per width.
+swz_params rows_choice(int cols);
+
 // Chooser: see swz_choose in swz.h.  Result cached per kind for the gfx950
 // model; the model argument form is uncached.
 swz_params choose_for_kind(int kind, const BankModel& m, int64_t* cycles);

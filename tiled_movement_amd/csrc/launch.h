@@ -32,6 +32,15 @@ struct StageJob {
 };
 
 hipError_t launch_convert(int kind, const ConvertJob& job, hipStream_t stream);
+// SWZ_READ_ROWS: whole rows of any width up to 64 bytes (kernels_rows.hip).
+// A tile is as many whole rows as fit in kRowsTileBytes of LDS, in groups
+// of 64 lane-words (a lane-word: 4 bytes of consecutive rows of one column).
+hipError_t launch_rows(int esz, const ConvertJob& job, hipStream_t stream);
+constexpr int kRowsTileBytes = 16384;
+inline int64_t rows_tile_rows(int64_t cols, int esz) {
+    const int64_t group = 64 * (4 / esz);
+    return cols <= 0 || cols * esz > kRowsTileBytes ? 0 : kRowsTileBytes / (cols * esz) / group * group;
+}
 hipError_t launch_stage(const StageJob& job, hipStream_t stream);
 hipError_t launch_gemm_frag(const void* fa, const void* fb, float* c, int64_t m, int64_t n, int64_t k,
                             hipStream_t stream);
