@@ -690,15 +690,17 @@ def test_auto_read_kind_picks_the_kernels_the_workloads_are_timed_with():
 def test_rows_kind_plan_and_validation():
     """Flat whole-row tiles (SWZ_READ_ROWS): any width up to 64 bytes, as
     many rows as fit in 16 KiB in groups of 64 lane-words (4 bytes of rows
-    each), a word-offset swizzle for even widths, SWIZZLE and PLAIN layouts
-    only; an explicit swizzle must have M = 0 and B <= S <= 11."""
+    each) plus 64 bytes' worth of halo rows in LDS, a word-offset swizzle
+    for even widths, SWIZZLE and PLAIN layouts only; an explicit swizzle
+    must have M = 0, B <= 10 and B <= S <= 11."""
     f = lib.swz_convert_layout
     for esz, cmax in ((4, 16), (2, 32), (1, 64)):
         group = 64 * (4 // esz)
         for c in range(1, cmax + 1):
             p = T.swz_plan(0, 100000, c, esz, "swizzle", T.READ_ROWS)
             tr = 16384 // (c * esz) // group * group
-            assert p["read_kind"] == T.READ_ROWS and p["tile"] == (tr, c) and p["lds_bytes"] == tr * c * esz
+            assert p["read_kind"] == T.READ_ROWS and p["tile"] == (tr, c)
+            assert p["lds_bytes"] == (tr + 64 // esz) * c * esz <= 16384 + 4096
             B, M, S = p["params"]
             if c % 2:  # odd widths read conflict-free unswizzled
                 assert (B, M, S) == (0, 0, 0), (c, p["params"])
@@ -716,6 +718,8 @@ def test_rows_kind_plan_and_validation():
         assert f(A, B, 1, 256, 3, esz, 0, T.READ_ROWS, ctypes.byref(P(3, 2, 3)), None) == EINVAL  # M != 0
         assert f(A, B, 1, 256, 3, esz, 0, T.READ_ROWS, ctypes.byref(P(3, 0, 2)), None) == EINVAL  # S < B
         assert f(A, B, 1, 256, 3, esz, 0, T.READ_ROWS, ctypes.byref(P(1, 0, 12)), None) == EINVAL  # S past the tile
+        assert f(A, B, 1, 256, 3, esz, 0, T.READ_ROWS, ctypes.byref(P(11, 0, 11)), None) == EINVAL  # B past the LDS
+        assert T.swz_plan(0, 256, 6, esz, "swizzle", T.READ_ROWS, (10, 0, 11))["params"] == (10, 0, 11)
         assert T.swz_plan(0, 256, 6, esz, "swizzle", T.READ_ROWS, (2, 0, 7))["params"] == (2, 0, 7)
         assert T.swz_plan(0, 256, 3, esz, "swizzle", T.READ_ROWS, (0, 0, 0))["read_kind"] == T.READ_ROWS
         assert T.swz_plan(0, 257, 3, esz, "swizzle", T.READ_ROWS)["aligned"]  # any pitch takes the same kernel

@@ -398,19 +398,22 @@ def test_misaligned_output_rows_through_the_xcd_grouped_grid():
 def test_rows_kind_every_width():
     """Flat whole-row tiles (SWZ_READ_ROWS, and AUTO for widths that are
     not powers of two): every width up to 64 bytes of every element size,
-    row counts around the lane-word groups and the tile, batches, a base
-    pointer one element off 16 bytes, both layouts."""
+    row counts around the lane-word groups, the 64-byte output line (h
+    elements), the tile and its halo, batches, base pointers 0 to h - 1
+    elements past a line, both layouts."""
     rng = np.random.default_rng(2028)
     gen = {4: W.fp32_matrix, 2: W.fp16_matrix, 1: W.u8_matrix}
     for esz, cmax in ((4, 16), (2, 32), (1, 64)):
-        group = 64 * (4 // esz)
+        group, h = 64 * (4 // esz), 64 // esz
         for c in range(1, cmax + 1):
             tr = 16384 // (c * esz) // group * group
-            for rows in sorted({1, group - 1, group + 1, tr, tr + 1, 2 * tr + int(rng.integers(1, group))}):
+            counts = {1, h - 1, h + 1, group - 1, group + 1, tr - 1, tr, tr + 1, tr + h - 1, tr + h + 1,
+                      2 * tr + int(rng.integers(1, group))}
+            for rows in sorted(counts):
                 b = 1 + (c + rows) % 3
                 a = gen[esz](b * rows, c, seed=c + rows).reshape(b, rows, c)
                 want = O.convert_layout(a)
-                for layout, kind, off in (("swizzle", T.READ_ROWS, 0), ("plain", T.READ_AUTO, 1)):
+                for layout, kind, off in (("swizzle", T.READ_ROWS, (7 * c + rows) % h), ("plain", T.READ_AUTO, 1)):
                     if kind == T.READ_AUTO and (c & (c - 1)) == 0:
                         kind = T.READ_ROWS  # AUTO takes the swizzled kinds for powers of two
                     announce("rows kind", esz, (b, rows, c), layout, off)

@@ -106,10 +106,12 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
         if (kind == SWZ_READ_ROWS) {
             // flat whole rows, swizzled on word offsets (M = 0, B <= S <=
             // 11: a bit of the 16 KiB tile's word offset XORs into a lower
-            // one), or plain; no padded or direct layout
+            // one; B <= 10, so the XOR stays inside the 20 KiB of LDS that
+            // tile and halo take), or plain; no padded or direct layout
             if (cols < 1 || cols * esz > 64) return SWZ_EINVAL;
             if (layout == SWZ_LAYOUT_PAD || layout == SWZ_LAYOUT_SWIZZLE_DIRECT) return SWZ_EUNSUPPORTED;
-            if (p && p->B != 0 && (p->B < 0 || p->M != 0 || p->S < p->B || p->S > 11)) return SWZ_EINVAL;
+            if (p && p->B != 0 && (p->B < 0 || p->B > 10 || p->M != 0 || p->S < p->B || p->S > 11))
+                return SWZ_EINVAL;
             swz_params q{0, 0, 0};
             if (layout == SWZ_LAYOUT_SWIZZLE) q = p ? (p->B == 0 ? swz_params{0, 0, 0} : *p) : swz::rows_choice(static_cast<int>(cols));
             std::memset(out, 0, sizeof(*out));
@@ -118,7 +120,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
             out->tile_rows = static_cast<int32_t>(swz::rows_tile_rows(cols, esz));
             out->tile_cols = static_cast<int32_t>(cols);
             out->layout = layout;
-            out->lds_bytes = out->tile_rows * static_cast<int32_t>(cols) * esz;
+            out->lds_bytes = static_cast<int32_t>((out->tile_rows + swz::rows_halo_rows(esz)) * cols * esz);
             out->vec_bytes = 16;
             out->aligned = 1;  // any pitch: unaligned rows take the same accesses
             out->threads = 256;

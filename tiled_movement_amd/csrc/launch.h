@@ -35,8 +35,14 @@ hipError_t launch_convert(int kind, const ConvertJob& job, hipStream_t stream);
 // SWZ_READ_ROWS: whole rows of any width up to 64 bytes (kernels_rows.hip).
 // A tile is as many whole rows as fit in kRowsTileBytes of LDS, in groups
 // of 64 lane-words (a lane-word: 4 bytes of consecutive rows of one column).
+// Its run in each output row is shifted to start on a kRowsLine-byte line
+// of the output, so it also loads up to kRowsLine / E rows past its own:
+// the LDS holds kRowsLdsBytes.
 hipError_t launch_rows(int esz, const ConvertJob& job, hipStream_t stream);
 constexpr int kRowsTileBytes = 16384;
+constexpr int kRowsLine = 64;
+constexpr int kRowsLdsBytes = kRowsTileBytes + kRowsLine * 64;  // halo rows are at most 64 bytes wide
+inline int64_t rows_halo_rows(int esz) { return kRowsLine / esz; }
 inline int64_t rows_tile_rows(int64_t cols, int esz) {
     const int64_t group = 64 * (4 / esz);
     return cols <= 0 || cols * esz > kRowsTileBytes ? 0 : kRowsTileBytes / (cols * esz) / group * group;
