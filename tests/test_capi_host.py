@@ -544,9 +544,9 @@ def test_narrow_kind_validation():
                     (16, T.READ_NARROW16)):
         p = T.swz_plan(0, 1000, c, 4, "swizzle")
         assert p["read_kind"] == kind and p["tile"] == (1024 // c, c) and p["lds_bytes"] == 4096
-    for c in (32, 64, 17):
+    for c in (32, 64, 65, 100):
         assert T.swz_plan(0, 1000, c, 4, "swizzle")["read_kind"] == T.READ_SCALAR_COL
-    for c in (3, 12):  # other widths up to 64 bytes: flat whole rows
+    for c in (3, 12, 17, 48, 63):  # other widths up to 64 columns: flat whole rows
         assert T.swz_plan(0, 1000, c, 4, "swizzle")["read_kind"] == T.READ_ROWS
     # 2- and 1-byte elements: whole-row tiles for rows of up to 64 bytes
     for esz, kinds in ((2, NARROW2), (1, NARROW1)):
@@ -560,9 +560,11 @@ def test_narrow_kind_validation():
         assert f(A, B, 1, 256, 2 * c, esz, 0, kinds[-1], None, None) == EINVAL  # width differs
         assert f(A, B, 1, 256, c, 6 - esz, 0, kinds[-1], None, None) == EINVAL  # element size differs
     assert T.swz_plan(0, 1000, 64, 2)["read_kind"] == T.READ_B64_TR16
-    assert T.swz_plan(0, 1000, 48, 2)["read_kind"] == T.READ_B64_TR16
+    assert T.swz_plan(0, 1000, 48, 2)["read_kind"] == T.READ_ROWS
     assert T.swz_plan(0, 1000, 24, 2)["read_kind"] == T.READ_ROWS
     assert T.swz_plan(0, 1000, 63, 1)["read_kind"] == T.READ_ROWS
+    assert T.swz_plan(0, 1000, 65, 2)["read_kind"] == T.READ_B128_8X8
+    assert T.swz_plan(0, 1000, 65, 1)["read_kind"] == T.READ_B64_TR8
     assert T.swz_plan(0, 1000, 128, 2)["read_kind"] == T.READ_B128_8X8
     assert T.swz_plan(0, 1000, 96, 1)["read_kind"] == T.READ_B64_TR8
     assert T.swz_plan(0, 1000, 128, 1)["read_kind"] == T.READ_B64_TR8
@@ -688,13 +690,13 @@ def test_auto_read_kind_picks_the_kernels_the_workloads_are_timed_with():
 
 
 def test_rows_kind_plan_and_validation():
-    """Flat whole-row tiles (SWZ_READ_ROWS): any width up to 64 bytes, as
+    """Flat whole-row tiles (SWZ_READ_ROWS): any width up to 64 columns, as
     many rows as fit in 16 KiB in groups of 64 lane-words (4 bytes of rows
     each) plus 64 bytes' worth of halo rows in LDS, a word-offset swizzle
     for even widths, SWIZZLE and PLAIN layouts only; an explicit swizzle
     must have M = 0, B <= 10 and B <= S <= 11."""
     f = lib.swz_convert_layout
-    for esz, cmax in ((4, 16), (2, 32), (1, 64)):
+    for esz, cmax in ((4, 64), (2, 64), (1, 64)):
         group = 64 * (4 // esz)
         for c in range(1, cmax + 1):
             p = T.swz_plan(0, 100000, c, esz, "swizzle", T.READ_ROWS)
@@ -712,7 +714,7 @@ def test_rows_kind_plan_and_validation():
             assert tr >= group and tr * c * esz <= 16384
             plain = T.swz_plan(0, 100000, c, esz, "plain", T.READ_ROWS)
             assert plain["tile"] == (tr, c) and plain["params"] == (0, 0, 0)
-        assert f(A, B, 1, 256, cmax + 1, esz, 0, T.READ_ROWS, None, None) == EINVAL  # wider than 64 bytes
+        assert f(A, B, 1, 256, cmax + 1, esz, 0, T.READ_ROWS, None, None) == EINVAL  # wider than 64 columns
         assert f(A, B, 1, 256, 3, esz, T.LAYOUT_PAD, T.READ_ROWS, None, None) == EUNSUP
         assert f(A, B, 1, 256, 3, esz, T.LAYOUT_SWIZZLE_DIRECT, T.READ_ROWS, None, None) == EUNSUP
         assert f(A, B, 1, 256, 3, esz, 0, T.READ_ROWS, ctypes.byref(P(3, 2, 3)), None) == EINVAL  # M != 0

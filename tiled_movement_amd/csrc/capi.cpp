@@ -84,12 +84,12 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
     if (op == 0) {
         if (esz != 1 && esz != 2 && esz != 4) return SWZ_EINVAL;
         if (kind == SWZ_READ_AUTO) {
-            // whole-row tiles for rows of 1 to 64 bytes: the swizzled kinds
-            // for power-of-two widths, flat rows for the others
-            const bool fits = cols >= 1 && cols * esz <= 64;
-            const bool narrow = fits && (cols & (cols - 1)) == 0;
+            // whole-row tiles: the swizzled kinds for power-of-two widths of
+            // 1 to 64 bytes, flat rows for the other widths up to 64 columns
+            const bool pow2 = cols >= 1 && (cols & (cols - 1)) == 0;
+            const bool narrow = pow2 && cols * esz <= 64;
             const int lc = ilog2(cols);
-            if (fits && !narrow)
+            if (!pow2 && cols >= 1 && cols <= 64)
                 kind = SWZ_READ_ROWS;
             else if (esz == 4)
                 kind = narrow ? SWZ_READ_NARROW1 + lc : SWZ_READ_SCALAR_COL;
@@ -108,7 +108,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
             // 11: a bit of the 16 KiB tile's word offset XORs into a lower
             // one; B <= 10, so the XOR stays inside the 20 KiB of LDS that
             // tile and halo take), or plain; no padded or direct layout
-            if (cols < 1 || cols * esz > 64) return SWZ_EINVAL;
+            if (cols < 1 || cols > 64) return SWZ_EINVAL;
             if (layout == SWZ_LAYOUT_PAD || layout == SWZ_LAYOUT_SWIZZLE_DIRECT) return SWZ_EUNSUPPORTED;
             if (p && p->B != 0 && (p->B < 0 || p->B > 10 || p->M != 0 || p->S < p->B || p->S > 11))
                 return SWZ_EINVAL;

@@ -1,7 +1,7 @@
-// Transposes of matrices whose rows are narrower than 64 bytes but whose
-// width is not a power of two ([rows][3] coordinates, [rows][12], ...).
-// The 32 x 32 and 64 x 64 tiles would hold a handful of columns each, and
-// the power-of-two whole-row kinds need a width that divides their tiles.
+// Transposes of matrices of up to 64 columns whose width is not a power of
+// two ([rows][3] coordinates, [rows][12], [rows][48], ...).  The 32 x 32 and
+// 64 x 64 tiles would leave many of their columns empty, and the
+// power-of-two whole-row kinds need a width that divides their tiles.
 // Here a tile is TR whole rows, one contiguous stretch of the source, copied
 // flat into LDS with 16-byte loads; then each lane gathers 4 bytes' worth of
 // consecutive rows of one column (1, 2 or 4 elements) and the wave writes

@@ -32,7 +32,7 @@ struct StageJob {
 };
 
 hipError_t launch_convert(int kind, const ConvertJob& job, hipStream_t stream);
-// SWZ_READ_ROWS: whole rows of any width up to 64 bytes (kernels_rows.hip).
+// SWZ_READ_ROWS: whole rows of any width up to 64 columns (kernels_rows.hip).
 // A tile is as many whole rows as fit in kRowsTileBytes of LDS, in groups
 // of 64 lane-words (a lane-word: 4 bytes of consecutive rows of one column).
 // Its run in each output row is shifted to start on a kRowsLine-byte line
@@ -41,7 +41,8 @@ hipError_t launch_convert(int kind, const ConvertJob& job, hipStream_t stream);
 hipError_t launch_rows(int esz, const ConvertJob& job, hipStream_t stream);
 constexpr int kRowsTileBytes = 16384;
 constexpr int kRowsLine = 64;
-constexpr int kRowsLdsBytes = kRowsTileBytes + kRowsLine * 64;  // halo rows are at most 64 bytes wide
+// The halo: at most kRowsLine / E rows of at most 64 E bytes.
+constexpr int kRowsLdsBytes = kRowsTileBytes + kRowsLine * 64;
 inline int64_t rows_halo_rows(int esz) { return kRowsLine / esz; }
 inline int64_t rows_tile_rows(int64_t cols, int esz) {
     const int64_t group = 64 * (4 / esz);
