@@ -124,29 +124,30 @@ enum swz_layout {
  *               and transposes them in registers into up to four 16-byte
  *               output pieces; tiles of 1 KiB per column up to 4 columns,
  *               8 KiB at 8 and 16 KiB above (64, 128 and 256 lanes).
- *  ROWS       : rows of any width up to 64 columns (any element size):
- *               tiles of as many whole rows as fit in 16 KiB (at least 64
- *               lane-words' worth: 256 / esz rows), copied flat into LDS,
- *               each lane gathering 4 bytes of consecutive rows of one
- *               column, each wave storing 256 contiguous bytes of an output
- *               row.  Lanes of a read are cols words apart: odd widths read
- *               conflict-free as they are, even widths through a swizzle of
- *               word offsets, Swizzle<B,0,S> with B <= 10 and B <= S <= 11
- *               (the chooser's per-width pick unless given).  Layouts
- *               SWIZZLE and PLAIN only.  Where output rows are not whole
- *               64-byte lines and a tile's run in an output row is at most
- *               2 KiB, the runs are shifted to start on line boundaries (the
- *               tiles then also read up to 64 / esz rows past their own).
- *  AUTO       : 4-byte -> NARROW<cols> when cols is 1, 2, 4, 8 or 16, ROWS
- *               for the widths up to 64 that are not powers of two, else
- *               SCALAR_COL; 2-byte -> HNARROW<cols> when cols is a power of
- *               two up to 32, ROWS for the widths up to 64 that are not
- *               powers of two, else B64_TR16 when cols <= 64, B128_8X8 when
- *               cols <= 128, B64_TR16 when cols <= 256 and B64_4X4 above
- *               (the faster of the two 64x64 kinds at those widths); 1-byte
- *               -> BNARROW<cols> when cols is a power of two up to 64, ROWS
- *               for the other widths up to
- *               64, else B64_TR8. */
+ *  ROWS       : rows of any width up to 128 columns (any element size):
+ *               tiles of as many whole rows as fit in 16 KiB (up to 64
+ *               columns, 256 threads) or 32 KiB (65 to 128 columns, 512
+ *               threads), at least 64 lane-words' worth (256 / esz rows),
+ *               copied flat into LDS, each lane gathering 4 bytes of
+ *               consecutive rows of one column, each wave storing 256
+ *               contiguous bytes of an output row.  Lanes of a read are cols
+ *               words apart: odd widths read conflict-free as they are, even
+ *               widths through a swizzle of word offsets, Swizzle<B,0,S> with
+ *               B <= 10 and B <= S <= 11 (the chooser's per-width pick unless
+ *               given).  Layouts SWIZZLE and PLAIN only.  Where output rows
+ *               are not whole 64-byte lines and a tile's run in an output row
+ *               is at most 2 KiB, the runs are shifted to start on line
+ *               boundaries (the tiles then also read up to 64 / esz rows
+ *               past their own).
+ *  AUTO       : ROWS for the widths up to 128 that are not powers of two
+ *               (4-byte elements from 96 columns on only where cols % 32 is
+ *               1 to 19); otherwise 4-byte -> NARROW<cols> when cols is 1,
+ *               2, 4, 8 or 16, else SCALAR_COL; 2-byte -> HNARROW<cols> when
+ *               cols is a power of two up to 32, else B64_TR16 when
+ *               cols <= 64, B128_8X8 when cols <= 128, B64_TR16 when
+ *               cols <= 256 and B64_4X4 above (the faster of the two 64x64
+ *               kinds at those widths); 1-byte -> BNARROW<cols> when cols is
+ *               a power of two up to 64, else B64_TR8. */
 /* The read kind is an argument of its own (read_kind, just before
  * p_or_null, in swz_transpose, swz_convert_layout, swz_tune_tile_order and
  * the tile-order calls), and it names a kernel, not a class of read.  The

@@ -544,9 +544,9 @@ def test_narrow_kind_validation():
                     (16, T.READ_NARROW16)):
         p = T.swz_plan(0, 1000, c, 4, "swizzle")
         assert p["read_kind"] == kind and p["tile"] == (1024 // c, c) and p["lds_bytes"] == 4096
-    for c in (32, 64, 65, 100):
+    for c in (32, 64, 96, 120, 127, 128, 129, 200):  # from 96 columns on: fuller last tiles keep the tile kind
         assert T.swz_plan(0, 1000, c, 4, "swizzle")["read_kind"] == T.READ_SCALAR_COL
-    for c in (3, 12, 17, 48, 63):  # other widths up to 64 columns: flat whole rows
+    for c in (3, 12, 17, 48, 63, 65, 95, 97, 100, 115):  # other widths up to 128 columns: flat whole rows
         assert T.swz_plan(0, 1000, c, 4, "swizzle")["read_kind"] == T.READ_ROWS
     # 2- and 1-byte elements: whole-row tiles for rows of up to 64 bytes
     for esz, kinds in ((2, NARROW2), (1, NARROW1)):
@@ -563,10 +563,12 @@ def test_narrow_kind_validation():
     assert T.swz_plan(0, 1000, 48, 2)["read_kind"] == T.READ_ROWS
     assert T.swz_plan(0, 1000, 24, 2)["read_kind"] == T.READ_ROWS
     assert T.swz_plan(0, 1000, 63, 1)["read_kind"] == T.READ_ROWS
-    assert T.swz_plan(0, 1000, 65, 2)["read_kind"] == T.READ_B128_8X8
-    assert T.swz_plan(0, 1000, 65, 1)["read_kind"] == T.READ_B64_TR8
+    assert T.swz_plan(0, 1000, 100, 2)["read_kind"] == T.READ_ROWS
+    assert T.swz_plan(0, 1000, 129, 2)["read_kind"] == T.READ_B64_TR16
+    assert T.swz_plan(0, 1000, 127, 1)["read_kind"] == T.READ_ROWS
+    assert T.swz_plan(0, 1000, 129, 1)["read_kind"] == T.READ_B64_TR8
     assert T.swz_plan(0, 1000, 128, 2)["read_kind"] == T.READ_B128_8X8
-    assert T.swz_plan(0, 1000, 96, 1)["read_kind"] == T.READ_B64_TR8
+    assert T.swz_plan(0, 1000, 256, 1)["read_kind"] == T.READ_B64_TR8
     assert T.swz_plan(0, 1000, 128, 1)["read_kind"] == T.READ_B64_TR8
     # rows under one 4-byte LDS store get no padded layout
     for kind, c, esz in ((T.READ_HNARROW1, 1, 2), (T.READ_BNARROW1, 1, 1), (T.READ_BNARROW2, 2, 1)):
@@ -690,19 +692,21 @@ def test_auto_read_kind_picks_the_kernels_the_workloads_are_timed_with():
 
 
 def test_rows_kind_plan_and_validation():
-    """Flat whole-row tiles (SWZ_READ_ROWS): any width up to 64 columns, as
-    many rows as fit in 16 KiB in groups of 64 lane-words (4 bytes of rows
-    each) plus 64 bytes' worth of halo rows in LDS, a word-offset swizzle
+    """Flat whole-row tiles (SWZ_READ_ROWS): any width up to 128 columns, as
+    many rows as fit in 16 KiB (32 KiB and 512 threads above 64 columns) in
+    groups of 64 lane-words (4 bytes of rows each) plus 64 bytes' worth of
+    halo rows in LDS, a word-offset swizzle
     for even widths, SWIZZLE and PLAIN layouts only; an explicit swizzle
     must have M = 0, B <= 10 and B <= S <= 11."""
     f = lib.swz_convert_layout
-    for esz, cmax in ((4, 64), (2, 64), (1, 64)):
+    for esz, cmax in ((4, 128), (2, 128), (1, 128)):
         group = 64 * (4 // esz)
         for c in range(1, cmax + 1):
             p = T.swz_plan(0, 100000, c, esz, "swizzle", T.READ_ROWS)
-            tr = 16384 // (c * esz) // group * group
+            tb, nt = (16384, 256) if c <= 64 else (32768, 512)  # tile bytes and threads
+            tr = tb // (c * esz) // group * group
             assert p["read_kind"] == T.READ_ROWS and p["tile"] == (tr, c)
-            assert p["lds_bytes"] == (tr + 64 // esz) * c * esz <= 16384 + 4096
+            assert p["lds_bytes"] == (tr + 64 // esz) * c * esz <= tb + tb // 4
             B, M, S = p["params"]
             if c % 2:  # odd widths read conflict-free unswizzled
                 assert (B, M, S) == (0, 0, 0), (c, p["params"])
@@ -710,11 +714,11 @@ def test_rows_kind_plan_and_validation():
                 assert B >= 2 and M == 0 and B <= S <= 11, (c, p["params"])
             else:  # the search's pick, whichever it is, a valid word-offset swizzle or none
                 assert M == 0 and (B == 0 or B <= S <= 11), (c, p["params"])
-            assert p["pad_elems"] == 0 and p["threads"] == 256 and p["aligned"]
-            assert tr >= group and tr * c * esz <= 16384
+            assert p["pad_elems"] == 0 and p["threads"] == nt and p["aligned"]
+            assert tr >= group and tr * c * esz <= tb
             plain = T.swz_plan(0, 100000, c, esz, "plain", T.READ_ROWS)
             assert plain["tile"] == (tr, c) and plain["params"] == (0, 0, 0)
-        assert f(A, B, 1, 256, cmax + 1, esz, 0, T.READ_ROWS, None, None) == EINVAL  # wider than 64 columns
+        assert f(A, B, 1, 256, cmax + 1, esz, 0, T.READ_ROWS, None, None) == EINVAL  # wider than 128 columns
         assert f(A, B, 1, 256, 3, esz, T.LAYOUT_PAD, T.READ_ROWS, None, None) == EUNSUP
         assert f(A, B, 1, 256, 3, esz, T.LAYOUT_SWIZZLE_DIRECT, T.READ_ROWS, None, None) == EUNSUP
         assert f(A, B, 1, 256, 3, esz, 0, T.READ_ROWS, ctypes.byref(P(3, 2, 3)), None) == EINVAL  # M != 0

@@ -397,16 +397,16 @@ def test_misaligned_output_rows_through_the_xcd_grouped_grid():
 
 def test_rows_kind_every_width():
     """Flat whole-row tiles (SWZ_READ_ROWS, and AUTO for widths that are
-    not powers of two): every width up to 64 columns of every element size,
+    not powers of two): every width up to 128 columns of every element size,
     row counts around the lane-word groups, the 64-byte output line (h
     elements), the tile and its halo, batches, base pointers 0 to h - 1
     elements past a line, both layouts."""
     rng = np.random.default_rng(2028)
     gen = {4: W.fp32_matrix, 2: W.fp16_matrix, 1: W.u8_matrix}
-    for esz, cmax in ((4, 64), (2, 64), (1, 64)):
+    for esz, cmax in ((4, 128), (2, 128), (1, 128)):
         group, h = 64 * (4 // esz), 64 // esz
         for c in range(1, cmax + 1):
-            tr = 16384 // (c * esz) // group * group
+            tr = (16384 if c <= 64 else 32768) // (c * esz) // group * group
             counts = {1, h - 1, h + 1, group - 1, group + 1, tr - 1, tr, tr + 1, tr + h - 1, tr + h + 1,
                       2 * tr + int(rng.integers(1, group))}
             for rows in sorted(counts):

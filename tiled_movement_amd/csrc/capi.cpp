@@ -85,11 +85,18 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
         if (esz != 1 && esz != 2 && esz != 4) return SWZ_EINVAL;
         if (kind == SWZ_READ_AUTO) {
             // whole-row tiles: the swizzled kinds for power-of-two widths of
-            // 1 to 64 bytes, flat rows for the other widths up to 64 columns
+            // 1 to 64 bytes, flat rows for the other widths up to 128 columns
+            // (fp32 from 96 columns on only where the last 32 x 32 tile
+            // column would hold at most 19 columns: with fuller tiles the
+            // tile kind ran faster, x 96 0.79 against 0.72 of a copy, x 120
+            // 0.74 against 0.68, x 127 0.69 against 0.58; x 115 0.51
+            // against 0.79)
             const bool pow2 = cols >= 1 && (cols & (cols - 1)) == 0;
             const bool narrow = pow2 && cols * esz <= 64;
             const int lc = ilog2(cols);
-            if (!pow2 && cols >= 1 && cols <= 64)
+            const bool flat_rows = !pow2 && cols >= 1 && cols <= swz::kRowsMaxCols &&
+                                   (esz != 4 || cols < 96 || (cols % 32 >= 1 && cols % 32 <= 19));
+            if (flat_rows)
                 kind = SWZ_READ_ROWS;
             else if (esz == 4)
                 kind = narrow ? SWZ_READ_NARROW1 + lc : SWZ_READ_SCALAR_COL;
@@ -105,10 +112,11 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
         if (kind == SWZ_READ_MFMA_16X16X32) return SWZ_EINVAL;
         if (kind == SWZ_READ_ROWS) {
             // flat whole rows, swizzled on word offsets (M = 0, B <= S <=
-            // 11: a bit of the 16 KiB tile's word offset XORs into a lower
-            // one; B <= 10, so the XOR stays inside the 20 KiB of LDS that
-            // tile and halo take), or plain; no padded or direct layout
-            if (cols < 1 || cols > 64) return SWZ_EINVAL;
+            // 11: a bit of the tile's word offset XORs into a lower one;
+            // B <= 10, so the XOR stays inside the 20 or 40 KiB of LDS, whole
+            // 4 KiB blocks, that tile and halo take), or plain; no padded or
+            // direct layout
+            if (cols < 1 || cols > swz::kRowsMaxCols) return SWZ_EINVAL;
             if (layout == SWZ_LAYOUT_PAD || layout == SWZ_LAYOUT_SWIZZLE_DIRECT) return SWZ_EUNSUPPORTED;
             if (p && p->B != 0 && (p->B < 0 || p->B > 10 || p->M != 0 || p->S < p->B || p->S > 11))
                 return SWZ_EINVAL;
@@ -123,7 +131,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
             out->lds_bytes = static_cast<int32_t>((out->tile_rows + swz::rows_halo_rows(esz)) * cols * esz);
             out->vec_bytes = 16;
             out->aligned = 1;  // any pitch: unaligned rows take the same accesses
-            out->threads = 256;
+            out->threads = swz::rows_threads(cols);
             out->interior_tiles = 1;
             return SWZ_OK;
         }

@@ -228,25 +228,24 @@ int64_t rows_cost(int cols, uint32_t B, uint32_t S, const BankModel& m) {
 }  // namespace
 
 swz_params rows_choice(int cols) {
-    static std::once_flag once;
-    static swz_params table[65];
-    std::call_once(once, [] {
+    if (cols < 1 || cols > kRowsMaxCols) return swz_params{0, 0, 0};
+    static std::once_flag once[kRowsMaxCols + 1];
+    static swz_params table[kRowsMaxCols + 1];
+    std::call_once(once[cols], [cols] {
         const BankModel& m = gfx950_bank_model();
-        for (int c = 1; c <= 64; ++c) {
-            swz_params best{0, 0, 0};
-            int64_t best_cyc = rows_cost(c, 0, 0, m);
-            for (int B = 1; B <= 5 && best_cyc > 0; ++B)
-                for (int S = B; S <= 8; ++S) {
-                    const int64_t cyc = rows_cost(c, B, S, m);
-                    if (cyc < best_cyc) {
-                        best_cyc = cyc;
-                        best = swz_params{B, 0, S};
-                    }
+        swz_params best{0, 0, 0};
+        int64_t best_cyc = rows_cost(cols, 0, 0, m);
+        for (int B = 1; B <= 5 && best_cyc > 0; ++B)
+            for (int S = B; S <= 8; ++S) {
+                const int64_t cyc = rows_cost(cols, B, S, m);
+                if (cyc < best_cyc) {
+                    best_cyc = cyc;
+                    best = swz_params{B, 0, S};
                 }
-            table[c] = best;
-        }
+            }
+        table[cols] = best;
     });
-    return cols >= 1 && cols <= 64 ? table[cols] : swz_params{0, 0, 0};
+    return table[cols];
 }
 
 swz_params cached_choice(int kind) {

@@ -26,7 +26,9 @@ void predict_tile(int kind, const BankModel& m, uint32_t ld, swz_params p, int64
 // Lanes of a read are cols words apart, so an even width meets conflicts
 // that the XOR of bits above the bank bits into the bank bits removes; odd
 // widths need none (B = 0).  Searched against the model's 4-byte reads of
-// that pattern and the 4-byte writes of the flat copy; cached per width.
+// that pattern and the 4-byte writes of the flat copy; cached per width
+// (1 to kRowsMaxCols; none for other widths).
+constexpr int kRowsMaxCols = 128;
 swz_params rows_choice(int cols);
 
 // Chooser: see swz_choose in swz.h.  Result cached per kind for the gfx950

@@ -1,4 +1,4 @@
-// Transposes of matrices of up to 64 columns whose width is not a power of
+// Transposes of matrices of up to 128 columns whose width is not a power of
 // two ([rows][3] coordinates, [rows][12], [rows][48], ...).  The 32 x 32 and
 // 64 x 64 tiles would leave many of their columns empty, and the
 // power-of-two whole-row kinds need a width that divides their tiles.
@@ -26,7 +26,6 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef u32x4v __attribute__((aligned(1))) u32x4_u1;
 typedef uint32_t __attribute__((aligned(1))) u32_u1;
 
-constexpr int kRowsThreads = 256;
 constexpr int64_t kRowsMaxGrid = int64_t(1) << 22;
 constexpr int kRowsUnroll = 4;
 // Tiles whose run in an output row is at most this many bytes shift their
@@ -39,15 +38,16 @@ constexpr int64_t kRowsShiftRun = 2048;
 
 // Tile t (of the batch's tiles in order): entry b, rows r0 .. r0 + nr - 1,
 // and with SHIFT up to `halo` rows past them.  E: element bytes; RL = 4 / E
-// rows per lane-word.
-template <int E, bool SHIFT>
-__global__ __launch_bounds__(kRowsThreads) void k_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+// rows per lane-word; NT threads; LDS the bytes of tile and halo (at most a
+// quarter more).
+template <int E, bool SHIFT, int NT, int LDS>
+__global__ __launch_bounds__(NT) void k_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                        int64_t rows, int32_t cols, int32_t tile_rows,
                                                        int64_t tiles_per_entry, int64_t tile0, uint32_t sw_b,
                                                        uint32_t sw_s, int32_t halo) {
     constexpr int RL = 4 / E;
-    static_assert(kRowsLdsBytes % (4 << 10) == 0, "the word swizzle (B <= 10) stays inside the array");
-    __shared__ u32x4v lds_v[kRowsLdsBytes / 16];
+    static_assert(LDS % (4 << 10) == 0, "the word swizzle (B <= 10) stays inside the array");
+    __shared__ u32x4v lds_v[LDS / 16];
     uint8_t* lds = reinterpret_cast<uint8_t*>(lds_v);
     const int t = threadIdx.x, lane = t % 64;
     const int wave = __builtin_amdgcn_readfirstlane(t / 64);
@@ -68,19 +68,19 @@ __global__ __launch_bounds__(kRowsThreads) void k_rows(const uint8_t* __restrict
     // most kRowsPieces) all loaded before any is written, then the tail.
     // Loads past the last piece re-read that piece (in bounds, not written),
     // so none sits behind a branch and all of them are in flight together.
-    constexpr int kRowsPieces = kRowsLdsBytes / 16 / kRowsThreads;
-    static_assert(kRowsPieces * 16 * kRowsThreads == kRowsLdsBytes, "the array is whole rounds of pieces");
+    constexpr int kRowsPieces = LDS / 16 / NT;
+    static_assert(kRowsPieces * 16 * NT == LDS, "the array is whole rounds of pieces");
     const int whole = nbytes / 16;
     if (whole > 0) {
         u32x4v x[kRowsPieces];
 #pragma unroll
         for (int i = 0; i < kRowsPieces; ++i) {
-            const int v = min(t + i * kRowsThreads, whole - 1);
+            const int v = min(t + i * NT, whole - 1);
             x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_u1*>(S + 16 * v));
         }
 #pragma unroll
         for (int i = 0; i < kRowsPieces; ++i) {
-            const int v = t + i * kRowsThreads;
+            const int v = t + i * NT;
             if (v < whole) {
                 if (sw_b == 0) {
                     lds_v[v] = x[i];
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kRowsThreads) void k_rows(const uint8_t* __restrict
     };
     // The wave's jobs kRowsUnroll at a time: every LDS read of the group is
     // issued before the first store.
-    constexpr int kWaves = kRowsThreads / 64;
+    constexpr int kWaves = NT / 64;
     for (int job0 = wave; job0 < jobs; job0 += kWaves * kRowsUnroll) {
         uint32_t w[kRowsUnroll];
         int c[kRowsUnroll], rb[kRowsUnroll], hi[kRowsUnroll];
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kRowsThreads) void k_rows(const uint8_t* __restrict
     }
     // The entry's first rows before each output row's first line.
     if (SHIFT && r0 == 0) {
-        for (int q = t; q < cols * H; q += kRowsThreads) {
+        for (int q = t; q < cols * H; q += NT) {
             const int c = q / H, i = q - c * H;
             if (i >= shift(c) || i >= rem) continue;
             uint8_t* D = dst + ((b * cols + c) * rows + i) * E;
@@ -190,27 +190,33 @@ int32_t rows_halo(const ConvertJob& j, int64_t tr) {
     return h;
 }
 
-template <int E>
+template <int E, int NT, int LDS>
 hipError_t launch_rows_e(const ConvertJob& j, hipStream_t stream) {
     const int32_t cols = static_cast<int32_t>(j.cols);
     const int64_t tr = rows_tile_rows(j.cols, E);
-    if (tr < 64 * (4 / E)) return hipErrorInvalidValue;  // rows wider than the kind takes
+    if (tr < 64 * (4 / E) || rows_lds_bytes(j.cols) != LDS || rows_threads(j.cols) != NT)
+        return hipErrorInvalidValue;  // rows wider than the kind takes
     const int32_t halo = rows_halo<E>(j, tr);
     const int64_t per = (j.rows + tr - 1) / tr, n = j.batch * per;
     for (int64_t t0 = 0; t0 < n; t0 += kRowsMaxGrid) {
         const int64_t cnt = n - t0 < kRowsMaxGrid ? n - t0 : kRowsMaxGrid;
-        const dim3 grid(static_cast<unsigned>(cnt)), block(kRowsThreads);
+        const dim3 grid(static_cast<unsigned>(cnt)), block(NT);
         const auto* s = static_cast<const uint8_t*>(j.src);
         auto* d = static_cast<uint8_t*>(j.dst);
         const auto sb = static_cast<uint32_t>(j.layout.B), ss = static_cast<uint32_t>(j.layout.S);
         if (halo > 0)
-            hipLaunchKernelGGL((k_rows<E, true>), grid, block, 0, stream, s, d, j.rows, cols, static_cast<int32_t>(tr),
-                               per, t0, sb, ss, halo);
+            hipLaunchKernelGGL((k_rows<E, true, NT, LDS>), grid, block, 0, stream, s, d, j.rows, cols,
+                               static_cast<int32_t>(tr), per, t0, sb, ss, halo);
         else
-            hipLaunchKernelGGL((k_rows<E, false>), grid, block, 0, stream, s, d, j.rows, cols, static_cast<int32_t>(tr),
-                               per, t0, sb, ss, 0);
+            hipLaunchKernelGGL((k_rows<E, false, NT, LDS>), grid, block, 0, stream, s, d, j.rows, cols,
+                               static_cast<int32_t>(tr), per, t0, sb, ss, 0);
     }
     return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_rows_w(const ConvertJob& j, hipStream_t stream) {
+    return j.cols <= 64 ? launch_rows_e<E, 256, 20480>(j, stream) : launch_rows_e<E, 512, 40960>(j, stream);
 }
 
 }  // namespace
@@ -218,9 +224,9 @@ hipError_t launch_rows_e(const ConvertJob& j, hipStream_t stream) {
 hipError_t launch_rows(int esz, const ConvertJob& j, hipStream_t stream) {
     if (j.batch == 0 || j.rows == 0 || j.cols == 0) return hipSuccess;
     switch (esz) {
-        case 4: return launch_rows_e<4>(j, stream);
-        case 2: return launch_rows_e<2>(j, stream);
-        case 1: return launch_rows_e<1>(j, stream);
+        case 4: return launch_rows_w<4>(j, stream);
+        case 2: return launch_rows_w<2>(j, stream);
+        case 1: return launch_rows_w<1>(j, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -32,21 +32,23 @@ struct StageJob {
 };
 
 hipError_t launch_convert(int kind, const ConvertJob& job, hipStream_t stream);
-// SWZ_READ_ROWS: whole rows of any width up to 64 columns (kernels_rows.hip).
-// A tile is as many whole rows as fit in kRowsTileBytes of LDS, in groups
-// of 64 lane-words (a lane-word: 4 bytes of consecutive rows of one column).
-// Its run in each output row is shifted to start on a kRowsLine-byte line
-// of the output, so it also loads up to kRowsLine / E rows past its own:
-// the LDS holds kRowsLdsBytes.
+// SWZ_READ_ROWS: whole rows of any width up to 128 columns (kernels_rows.hip).
+// A tile is as many whole rows as fit in rows_tile_bytes of LDS, in groups
+// of 64 lane-words (a lane-word: 4 bytes of consecutive rows of one column,
+// so a group is 256 / E rows): 16 KiB and 256 threads up to 64 columns,
+// 32 KiB and 512 threads up to 128.  Its run in each output row may be
+// shifted to start on a kRowsLine-byte line of the output; it then also
+// loads up to kRowsLine / E rows past its own (at most a quarter of the
+// tile's bytes), so the LDS holds rows_lds_bytes.
 hipError_t launch_rows(int esz, const ConvertJob& job, hipStream_t stream);
-constexpr int kRowsTileBytes = 16384;
 constexpr int kRowsLine = 64;
-// The halo: at most kRowsLine / E rows of at most 64 E bytes.
-constexpr int kRowsLdsBytes = kRowsTileBytes + kRowsLine * 64;
+inline int rows_tile_bytes(int64_t cols) { return cols <= 64 ? 16384 : 32768; }
+inline int rows_threads(int64_t cols) { return cols <= 64 ? 256 : 512; }
+inline int rows_lds_bytes(int64_t cols) { return rows_tile_bytes(cols) + rows_tile_bytes(cols) / 4; }
 inline int64_t rows_halo_rows(int esz) { return kRowsLine / esz; }
 inline int64_t rows_tile_rows(int64_t cols, int esz) {
     const int64_t group = 64 * (4 / esz);
-    return cols <= 0 || cols * esz > kRowsTileBytes ? 0 : kRowsTileBytes / (cols * esz) / group * group;
+    return cols <= 0 || cols > 128 ? 0 : rows_tile_bytes(cols) / (cols * esz) / group * group;
 }
 hipError_t launch_stage(const StageJob& job, hipStream_t stream);
 hipError_t launch_gemm_frag(const void* fa, const void* fb, float* c, int64_t m, int64_t n, int64_t k,
