@@ -70,6 +70,8 @@ WORKLOADS = {
     "fp32_narrow8": "fp32 [2097152][8] -> [8][2097152] transpose (64 MiB), whole-row 128x8 LDS tiles, the swizzle spanning rows",
     "fp16_narrow8": "fp16 [4194304][8] -> [8][4194304] transpose (64 MiB), whole-row 256x8 LDS tiles, 2-byte column reads",
     "u8_narrow16": "1-byte [4194304][16] -> [16][4194304] transpose (64 MiB), whole-row 1024x16 LDS tiles, 4-byte reads of 16x4 blocks",
+    "fp32_rows3": "fp32 [5592405][3] -> [3][5592405] transpose (64 MiB, output rows off the 64-byte lines), flat whole-row tiles of 1344 rows",
+    "u8_rows48": "1-byte [1398101][48] -> [48][1398101] transpose (64 MiB, output rows off the 64-byte lines), flat whole-row tiles of 256 rows, word swizzle, runs shifted onto the output lines",
     "bf16_stage": "bf16 operand staging A[8192x4096] row-major + B[4096x8192] column-major into 16x16x32 fragments, both in one launch",
     "map": "Swizzle<B,M,S> of int32 offsets 0..65535, one call per (B,M,S), 125 triples",
     "map_batch": "Swizzle<B,M,S> of int32 offsets 0..65535 under all 125 triples in one call (8,192,000 outputs)",
@@ -86,7 +88,7 @@ WORKLOADS = {
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CONFLICT_FILE = os.path.join(ROOT, "profiles", "lds_conflicts.json")
-KERNEL_SOURCES = ("kernels_tile.hip", "kernels_copy.hip", "swz_common.h")
+KERNEL_SOURCES = ("kernels_tile.hip", "kernels_copy.hip", "swz_common.h", "kernels_rows.hip")
 
 
 def log(*a):
@@ -232,8 +234,14 @@ def build(ctx, name, layout):
     info = {"workload": WORKLOADS[name], "layout": layout}
 
     if name in ("fp32_transpose", "fp16_transpose", "fp16_transpose_tr", "bf16_convert", "u8_transpose", "fp32_narrow8",
-                "fp16_narrow8", "u8_narrow16", "fp32_transpose_long"):
-        if name == "fp32_narrow8":
+                "fp16_narrow8", "u8_narrow16", "fp32_transpose_long", "fp32_rows3", "u8_rows48"):
+        if name == "fp32_rows3":
+            r = (64 << 20) // 12
+            a, esz, kind, (batch, r, c) = W.fp32_matrix(r, 3, seed=0), 4, T.READ_ROWS, (1, r, 3)
+        elif name == "u8_rows48":
+            r = (64 << 20) // 48
+            a, esz, kind, (batch, r, c) = W.u8_matrix(r, 48, seed=0), 1, T.READ_ROWS, (1, r, 48)
+        elif name == "fp32_narrow8":
             a, esz, kind, (batch, r, c) = W.fp32_matrix(1 << 21, 8, seed=0), 4, T.READ_NARROW8, (1, 1 << 21, 8)
         elif name == "fp16_narrow8":
             a, esz, kind, (batch, r, c) = W.fp16_matrix(1 << 22, 8, seed=0), 2, T.READ_HNARROW8, (1, 1 << 22, 8)
@@ -263,10 +271,12 @@ def build(ctx, name, layout):
                 ctx.check(rc, "swz_convert_layout")
 
         pl = T.swz_plan(0, r, c, esz, layout, kind)
-        wc, rc_ = T.swz_predict_conflicts(kind, layout)
         info.update({"shape": [batch, r, c], "elem_bytes": esz, "params": list(pl["params"]),
                      "pad_elems": pl["pad_elems"], "lds_bytes": pl["lds_bytes"], "threads": pl["threads"],
-                     "buffer_pairs": k, "predicted_conflict_cycles_per_tile": {"write": wc, "read": rc_}})
+                     "buffer_pairs": k})
+        if kind != T.READ_ROWS:  # the flat-row kind's reads depend on the width, not on the kind alone
+            wc, rc_ = T.swz_predict_conflicts(kind, layout)
+            info["predicted_conflict_cycles_per_tile"] = {"write": wc, "read": rc_}
         info["_io"] = (a, srcs, dsts, step)
         return step, 2 * a.nbytes, info
 
@@ -643,7 +653,7 @@ def order_shape_sweep(elem_bytes, dims=ORDER_SHAPE_DIMS, lo_mib=32, hi_mib=512):
 # workload (staging: both operands, 128 MiB, in one launch).
 COPY_OF = {"fp32_transpose": "copy", "fp16_transpose": "copy_128", "fp16_transpose_tr": "copy_128",
            "u8_transpose": "copy", "bf16_convert": "copy", "bf16_stage": "copy_128", "fp32_narrow8": "copy",
-           "fp16_narrow8": "copy", "u8_narrow16": "copy"}
+           "fp16_narrow8": "copy", "u8_narrow16": "copy", "fp32_rows3": "copy", "u8_rows48": "copy"}
 # Workloads whose oracle is timed beside them in the full run (the headline's
 # own is the line's cpu_baseline).
 ORACLE_TIMED = ("fp16_transpose", "bf16_convert", "bf16_stage", "map_batch")
@@ -695,11 +705,11 @@ def main(argv=None):
     if not args.quick and args.workload is None:
         for wname in ("copy", "copy_128", "copy_zero", "memcpy_d2d", "fp32_transpose", "fp16_transpose",
                       "fp16_transpose_tr", "u8_transpose", "bf16_convert", "bf16_stage", "fp32_narrow8",
-                      "fp16_narrow8", "u8_narrow16", "map", "bf16_gemm", "bf16_gemm_fused", "bf16_gemm_fused_bf16c",
-                      "torch_mm_bf16"):
+                      "fp16_narrow8", "u8_narrow16", "fp32_rows3", "u8_rows48", "map", "bf16_gemm", "bf16_gemm_fused",
+                      "bf16_gemm_fused_bf16c", "torch_mm_bf16"):
             for lay in (("swizzle",) if wname in ("copy", "copy_128", "copy_zero", "memcpy_d2d", "map", "bf16_gemm",
                                                   "torch_mm_bf16", "bf16_gemm_fused_bf16c")
-                        else ("swizzle", "plain") if wname == "bf16_gemm_fused"
+                        else ("swizzle", "plain") if wname in ("bf16_gemm_fused", "fp32_rows3", "u8_rows48")
                         else ("swizzle", "pad", "plain", "direct")):
                 s2, nb2, inf2 = build(ctx, wname, lay)
                 if wname == "map":
@@ -796,7 +806,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32_transpose": "f32", "fp32_narrow8": "f32", "fp32_transpose_long": "f32", "fp16_narrow8": "f16", "u8_narrow16": "u8", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "map_batch": "int32", "copy": "u8", "copy_128": "u8", "copy_zero": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
+        "dtype": {"fp32_transpose": "f32", "fp32_narrow8": "f32", "fp32_rows3": "f32", "u8_rows48": "u8", "fp32_transpose_long": "f32", "fp16_narrow8": "f16", "u8_narrow16": "u8", "fp16_transpose": "f16", "fp16_transpose_tr": "f16", "u8_transpose": "u8", "map": "int32", "map_batch": "int32", "copy": "u8", "copy_128": "u8", "copy_zero": "u8", "memcpy_d2d": "u8"}.get(name, "bf16"),
         "data": "synthetic",
         "config": config,
         "roofline": {

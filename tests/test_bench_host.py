@@ -22,7 +22,8 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_headline_workload_and_units():
     assert "fp32_transpose" in bench.WORKLOADS
-    for name in ("bf16_gemm", "bf16_gemm_fused", "bf16_gemm_fused_bf16c", "map_batch", "u8_narrow16"):
+    for name in ("bf16_gemm", "bf16_gemm_fused", "bf16_gemm_fused_bf16c", "map_batch", "u8_narrow16", "fp32_rows3",
+                 "u8_rows48"):
         assert name in bench.WORKLOADS, name
 
 
