@@ -275,9 +275,12 @@ int swz_convert_layout(const void* d_src, void* d_dst, int64_t batch, int64_t ro
  * the matrix shape, by up to 25% at some shapes; no order is best at all of
  * them.  All orders give the same bits.
  *
- * Shapes with no pinned order (swz_set_tile_order) take a default set by the
- * source row pitch (cols * elem_bytes): SWZ_ORDER_SLOPE_32 when the pitch
- * is not within 1% of a multiple of 4 KiB; otherwise the diagonal, or
+ * Shapes with no pinned order (swz_set_tile_order) take a default.  With
+ * at least 2,000 rows whose output rows (rows * elem_bytes) are not whole
+ * 64-byte pieces: SWZ_ORDER_COLUMNS for matrices at least 16 tiles wide,
+ * SWZ_ORDER_SLOPE_32 for narrower ones.  Otherwise it is set by the source
+ * row pitch (cols * elem_bytes): SWZ_ORDER_SLOPE_32 when the pitch is not
+ * within 1% of a multiple of 4 KiB; otherwise the diagonal, or
  * SWZ_ORDER_SLOPE_8 for fp32 matrices with at most 10,240 rows and a side
  * that is not a power of two.  The whole-row (narrow) kinds take the
  * diagonal.  (Measured over 1,273 fp32, 1,009 16-bit and 597 byte shapes

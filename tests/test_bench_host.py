@@ -52,8 +52,15 @@ def test_conflict_counters_equal_the_models_prediction_for_every_layout():
 
     with open(bench.CONFLICT_FILE) as f:
         rec = json.load(f)
-    assert len(rec["workloads"]) == 9
+    rows = {"fp32_rows3", "u8_rows48"}
+    assert len(rec["workloads"]) == 11 and rows <= set(rec["workloads"])
     for wname, layouts in rec["workloads"].items():
+        if wname in rows:  # the flat-row kind: its reads depend on the width, so no per-kind prediction
+            assert set(layouts) == {"swizzle", "plain"}, wname
+            sw, pl = layouts["swizzle"], layouts["plain"]
+            assert sw["conflict_cycles_per_lds_instr"] < 1e-3, wname
+            assert sw["SQ_LDS_BANK_CONFLICT"] <= pl["SQ_LDS_BANK_CONFLICT"], wname
+            continue
         assert set(layouts) == {"swizzle", "pad", "plain", "direct"}, wname
         for layout, r in layouts.items():
             w, rd = T.swz_predict_conflicts(r["read_kind"], layout)

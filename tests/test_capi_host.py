@@ -112,8 +112,9 @@ def test_tile_order_validation():
 
 def test_default_tile_order_by_shape():
     """Unpinned shapes: whole tile columns when the output rows (rows x
-    element bytes) are not whole 64-byte pieces and there are at least 2,000
-    rows; else slope 1/32 when the source row pitch (cols x element bytes) is
+    element bytes) are not whole 64-byte pieces, there are at least 2,000
+    rows and the matrix is at least 16 tiles wide (slope 1/32 when it is
+    narrower); else slope 1/32 when the source row pitch (cols x element bytes) is
     not within 1% of a multiple of 4 KiB; otherwise the diagonal, or slope
     1/8 for fp32 matrices with at most 10,240 rows and a side that is not a
     power of two.  Whole-row kinds: the diagonal."""
@@ -149,6 +150,13 @@ def test_default_tile_order_by_shape():
     assert get(1, 4112, 4112, 2) == T.ORDER_COLUMNS
     assert get(1, 8208, 8208, 1) == T.ORDER_COLUMNS
     assert get(1, 8208, 16, 1) == T.ORDER_DIAGONAL  # whole-row kind
+    # ... unless the matrix is under 16 tiles wide (32-, 64- and 128-column tiles): slope 1/32
+    assert get(1, 223696, 300, 1) == T.ORDER_SLOPE_32  # 3 tiles of 128 columns
+    assert get(1, 67108, 500, 2) == T.ORDER_SLOPE_32  # 8 of 64
+    assert get(1, 55924, 300, 4) == T.ORDER_SLOPE_32  # 10 of 32
+    assert get(1, 33554, 500, 4) == T.ORDER_COLUMNS  # 16 of 32
+    assert get(1, 33554, 1000, 2) == T.ORDER_COLUMNS  # 16 of 64
+    assert get(1, 33554, 2048, 1) == T.ORDER_COLUMNS  # 16 of 128
     assert get(1, 8192, 8192, 1) == T.ORDER_DIAGONAL
     assert get(1, 5760, 8128, 1) == T.ORDER_DIAGONAL  # 64 bytes short of 8 KiB
     assert get(1, 5760, 4160, 1) == T.ORDER_SLOPE_32  # 64 over 4 KiB: 1.5%

@@ -203,8 +203,17 @@ int default_order(int kind, int64_t rows, int64_t cols) {
                                                                                                         : 0;
     if (esz == 0) return SWZ_ORDER_DIAGONAL;
     // Output rows off the 64-byte pieces (the XCD-grouped grid): neighbours
-    // down a block column share those pieces, so they go in turn.
-    if (swz::partial_line_output(rows, esz)) return SWZ_ORDER_COLUMNS;
+    // down a block column share those pieces, so they go in turn, unless the
+    // matrix is under 16 tiles wide; then the workgroups in flight would
+    // crowd a few output rows, and the shallowest slope spreads them (odd row
+    // counts, share of a copy, columns against slope 1/32: bytes x 300, 3
+    // tiles, 0.30 against 0.42; 2-byte x 500, 8 tiles, 0.50 against 0.63;
+    // bytes x 1000, 8 tiles, 0.50 against 0.59; from 16 tiles columns won or
+    // tied: fp32 x 500 0.63 against 0.61, 2-byte x 1000 0.60 against 0.58).
+    if (swz::partial_line_output(rows, esz)) {
+        const int64_t tile_cols = kind == SWZ_READ_SCALAR_COL ? 32 : esz == 2 && kind != SWZ_READ_B128_8X8 ? 64 : 128;
+        return (cols + tile_cols - 1) / tile_cols < 16 ? SWZ_ORDER_SLOPE_32 : SWZ_ORDER_COLUMNS;
+    }
     const uint64_t pitch = static_cast<uint64_t>(cols) * static_cast<uint64_t>(esz), r = pitch % 4096;
     const uint64_t off = r < 4096 - r ? r : 4096 - r;  // distance to the nearest multiple of 4 KiB
     if (off * 100 > pitch) return SWZ_ORDER_SLOPE_32;
