@@ -106,3 +106,39 @@ def test_narrow_rows_batch_beyond_grid_limit(esz, c):
         T.swz_convert_layout(src, dst, batch, rows, c, esz, layout)
         torch.cuda.synchronize()
         assert np.array_equal(dst.cpu().numpy(), O.convert_layout(a)), (esz, c, layout)
+
+
+@pytest.mark.parametrize("esz,c", [(4, 3), (1, 48), (2, 66)])
+def test_rows_kind_more_than_2_22_tiles(esz, c):
+    """2^22 + 3 entries of 2 rows, one flat-row tile each: more tiles than one
+    launch takes, so the tile numbering carries across launch chunks (bytes
+    x 48 and 2-byte x 66 with runs shifted onto the output lines, the latter
+    in 512-thread tiles)."""
+    batch, rows = (1 << 22) + 3, 2
+    gen = {4: W.fp32_matrix, 2: W.fp16_matrix, 1: W.u8_matrix}[esz]
+    a = gen(batch * rows, c, seed=60 + c).reshape(batch, rows, c)
+    announce("rows kind past 2^22 tiles", esz, c)
+    src = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    dst = torch.empty((batch, c, rows), dtype=src.dtype, device=DEV)
+    T.swz_convert_layout(src, dst, batch, rows, c, esz, "swizzle", T.READ_ROWS)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), O.convert_layout(a)), (esz, c)
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def test_rows_kind_at_the_timed_sizes():
+    """The flat-row transposes the benchmark times, whole: fp32 [5592405][3]
+    (unshifted runs) and bytes [1398101][48] (runs shifted onto the output
+    lines), both layouts, compared element by element with the oracle."""
+    for esz, c, gen in ((4, 3, W.fp32_matrix), (1, 48, W.u8_matrix)):
+        r = (64 << 20) // (c * esz)
+        a = gen(r, c, seed=0)
+        want = O.transpose(a)
+        for layout in ("swizzle", "plain"):
+            announce("rows kind, timed size", esz, (r, c), layout)
+            src = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+            dst = torch.empty((c, r), dtype=src.dtype, device=DEV)
+            T.swz_convert_layout(src, dst, 1, r, c, esz, layout, T.READ_ROWS)
+            torch.cuda.synchronize()
+            assert np.array_equal(dst.cpu().numpy(), want), (esz, c, layout)
