@@ -649,6 +649,69 @@ def order_shape_sweep(elem_bytes, dims=ORDER_SHAPE_DIMS, lo_mib=32, hi_mib=512):
     return lines
 
 
+def random_shape_sweep(n, seed=7, lo_mib=16, hi_mib=96):
+    """AUTO transposes of `n` seeded random shapes (element size 1, 2 or 4;
+    columns log-uniform in 1 .. 16384; rows filling lo_mib .. hi_mib MiB, so
+    the pitches and row counts are mostly not multiples of 16 bytes or 64
+    bytes), each as a share of the reference copy of the same bytes: buffers
+    carved from one 2 GiB source and one 2 GiB destination, rotating over up
+    to 16 pairs, median of three batches of 10 calls.  Returns the lines of
+    a table, closed by the median share per element size."""
+    import random
+    import statistics
+
+    import torch
+
+    import tiled_movement_amd as T
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    src = torch.randint(0, 256, (2 << 30,), dtype=torch.uint8, device=dev, generator=gen)
+    dst = torch.empty_like(src)
+    rng = random.Random(seed)
+
+    def rate(fn, pairs, nbytes):
+        rates = []
+        for _ in range(3):
+            ms, _ = time_steps(lambda i: fn(i % pairs), 10, 2)
+            rates.append(2.0 * nbytes * 10 / (ms * 1e-3) / 1e9)
+        return sorted(rates)[1]
+
+    lines = ["| elem bytes | rows x cols | pitch % 16 | output row % 64 | kind | order | copy GB/s | GB/s | share |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    shares = {1: [], 2: [], 4: []}
+    for _ in range(n):
+        esz = rng.choice((1, 2, 4))
+        mib = rng.uniform(lo_mib, hi_mib)
+        cols = max(1, int(round(2 ** rng.uniform(0, 14))))
+        rows = max(1, int(mib * 2**20 / (cols * esz)))
+        nbytes = rows * cols * esz
+        per = -(-nbytes // 4096) * 4096
+        pairs = max(1, min((2 << 30) // per, 16))
+        sp = [src.data_ptr() + i * per for i in range(pairs)]
+        dp = [dst.data_ptr() + i * per for i in range(pairs)]
+        cb = nbytes // 16 * 16
+        copy = rate(lambda j: T.lib.swz_copy(sp[j], dp[j], cb, stream), pairs, cb)
+
+        def conv(j):
+            rc = T.lib.swz_transpose(sp[j], dp[j], rows, cols, esz, T.LAYOUT_SWIZZLE, T.READ_AUTO, None, stream)
+            if rc:
+                raise T.SwzError(rc, "swz_transpose")
+
+        got = rate(conv, pairs, nbytes)
+        kind = T.swz_plan(0, rows, cols, esz, "swizzle", T.READ_AUTO)["read_kind"]
+        shares[esz].append(got / copy)
+        lines.append(f"| {esz} | {rows} x {cols} | {cols * esz % 16} | {rows * esz % 64} | {kind} | "
+                     f"{T.swz_get_tile_order(1, rows, cols, esz)} | {copy:,.0f} | {got:,.0f} | {got / copy:.3f} |")
+        log(lines[-1])
+    for esz, v in shares.items():
+        if v:
+            lines.append(f"| median of {len(v)}, {esz}-byte | | | | | | | | {statistics.median(v):.3f} |")
+    return lines
+
+
 # The reference copy whose launch moves the same bytes as one launch of the
 # workload (staging: both operands, 128 MiB, in one launch).
 COPY_OF = {"fp32_transpose": "copy", "fp16_transpose": "copy_128", "fp16_transpose_tr": "copy_128",
@@ -676,6 +739,8 @@ def main(argv=None):
     ap.add_argument("--mib", type=int, default=64, help="--tile-orders: matrix size in MiB (a power of two)")
     ap.add_argument("--order-shapes", action="store_true",
                     help="every tile order and the default order on many shapes, as shares of a copy")
+    ap.add_argument("--random-shapes", type=int, default=0,
+                    help="AUTO transposes of this many seeded random shapes, as shares of a copy")
     args = ap.parse_args(argv)
     global PAIRS_OVERRIDE
     PAIRS_OVERRIDE = args.pairs
@@ -690,6 +755,9 @@ def main(argv=None):
         return 0
     if args.order_shapes:
         print("\n".join(order_shape_sweep(args.elem_bytes)), flush=True)
+        return 0
+    if args.random_shapes:
+        print("\n".join(random_shape_sweep(args.random_shapes)), flush=True)
         return 0
     name = args.workload or "fp32_transpose"
     layout = args.layout if args.workload else "swizzle"

@@ -141,7 +141,11 @@ enum swz_layout {
  *               past their own).
  *  AUTO       : ROWS for the widths up to 128 that are not powers of two
  *               (4-byte elements from 96 columns on only where cols % 32 is
- *               1 to 19); otherwise 4-byte -> NARROW<cols> when cols is 1,
+ *               1 to 19), and for the power-of-two widths below whose output
+ *               rows or pointers are not 16-byte aligned (4-byte elements,
+ *               2-byte of 8 to 32 columns, 1-byte of 64: the narrow kinds
+ *               would move them element by element); otherwise 4-byte ->
+ *               NARROW<cols> when cols is 1,
  *               2, 4, 8 or 16, else SCALAR_COL; 2-byte -> HNARROW<cols> when
  *               cols is a power of two up to 32, else B64_TR16 when
  *               cols <= 64, B128_8X8 when cols <= 128, B64_TR16 when

@@ -560,7 +560,7 @@ def test_narrow_kind_validation():
     for esz, kinds in ((2, NARROW2), (1, NARROW1)):
         for i, kind in enumerate(kinds):
             c = 1 << i
-            p = T.swz_plan(0, 1000, c, esz, "swizzle")
+            p = T.swz_plan(0, 1024, c, esz, "swizzle")
             cb = min(c, 4 // esz) if esz == 1 or c in (1, 32) else 1  # columns per lane block: the tile is 16 * threads * cb bytes
             tb = 16 * p["threads"] * cb
             assert p["read_kind"] == kind and p["tile"] == (tb // esz // c, c) and p["lds_bytes"] == tb
@@ -587,7 +587,14 @@ def test_narrow_kind_validation():
     assert f(A, B, 1, 256, 8, 1, 0, T.READ_BNARROW8, ctypes.byref(P(4, 1, 5)), None) == EINVAL
     # whole-row tiles need only the output pitch aligned for the vector path
     assert T.swz_plan(0, 4096, 1, 4, "swizzle")["aligned"] and T.swz_plan(0, 4096, 2, 4, "direct")["aligned"]
-    assert not T.swz_plan(0, 4093, 8, 4, "swizzle")["aligned"]
+    assert not T.swz_plan(0, 4093, 8, 4, "swizzle", T.READ_NARROW8)["aligned"]
+    # ... and where the output rows rule out 16-byte vectors, AUTO takes flat rows for every fp32
+    # width, 2-byte widths of 8 to 32 and bytes x 64 (the narrow kinds would go element by element)
+    for esz, c, kind in ((4, 1, T.READ_ROWS), (4, 16, T.READ_ROWS), (2, 4, T.READ_HNARROW4), (2, 8, T.READ_ROWS),
+                         (2, 32, T.READ_ROWS), (1, 32, T.READ_BNARROW32), (1, 64, T.READ_ROWS)):
+        assert T.swz_plan(0, 4093, c, esz, "swizzle")["read_kind"] == kind, (esz, c)
+        assert T.swz_plan(0, 4096, c, esz, "swizzle")["read_kind"] != T.READ_ROWS, (esz, c)  # aligned rows
+    assert T.swz_get_tile_order(1, 4093, 8, 4) == T.ORDER_DIAGONAL  # resolves to the flat-row kind too
     assert f(A, B, 1, 4093, 8, 4, T.LAYOUT_SWIZZLE_DIRECT, T.READ_NARROW8, None, None) == EUNSUP
     # the flat-offset swizzle spans rows: Swizzle<5,0,5> on a 128x8 tile XORs
     # row bits 2-6 into the element bits (the pages' int num[32][8] example)

@@ -291,7 +291,10 @@ def test_narrow_rows(kind, esz, c, layout):
 @pytest.mark.parametrize("kind,esz,c", NARROW_KINDS)
 def test_narrow_auto_unaligned_and_batched(kind, esz, c):
     rows = 3 * T.swz_plan(0, 4096, c, esz, "swizzle", kind)["tile"][0] + 9
-    assert T.swz_plan(0, rows, c, esz)["read_kind"] == kind
+    # output rows of 9 elements past whole tiles are no multiple of 16 bytes: AUTO takes flat rows for
+    # every fp32 width, 2-byte widths of 8 to 32 and bytes x 64 (the explicit kind is tested below)
+    to_rows = esz == 4 or (esz == 2 and c >= 8) or (esz == 1 and c == 64)
+    assert T.swz_plan(0, rows, c, esz)["read_kind"] == (T.READ_ROWS if to_rows else kind)
     a = GEN[esz](rows, c, seed=c)
     announce("narrow auto", esz, c)
     check_transpose(a, esz, "swizzle", T.READ_AUTO)

@@ -96,7 +96,17 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
             const int lc = ilog2(cols);
             const bool flat_rows = !pow2 && cols >= 1 && cols <= swz::kRowsMaxCols &&
                                    (esz != 4 || cols < 96 || (cols % 32 >= 1 && cols % 32 <= 19));
-            if (flat_rows)
+            // Power-of-two widths whose output rows (or pointers) rule out
+            // 16-byte vectors: the swizzled narrow kinds then move elements
+            // one by one, and flat rows ran faster for every fp32 width,
+            // 2-byte widths of 8 to 32 and bytes x 64 (odd row counts, 64
+            // MiB, share of a copy: fp32 x 1 0.59 -> 0.90, x 8 0.49 -> 0.75,
+            // x 16 0.48 -> 0.74; 2-byte x 16 0.54 -> 0.72; bytes x 64 0.59
+            // -> 0.64; narrower 2-byte and byte widths kept their kinds, at
+            // 0.73-1.0)
+            const bool unaligned_pow2 =
+                narrow && !aligned_out && (esz == 4 || (esz == 2 && cols >= 8) || (esz == 1 && cols == 64));
+            if (flat_rows || unaligned_pow2)
                 kind = SWZ_READ_ROWS;
             else if (esz == 4)
                 kind = narrow ? SWZ_READ_NARROW1 + lc : SWZ_READ_SCALAR_COL;
@@ -333,7 +343,8 @@ SWZ_API int swz_set_tile_order(int64_t batch, int64_t rows, int64_t cols, int32_
     if (batch < 0 || rows < 0 || cols < 0) return SWZ_EINVAL;
     if (order < -1 || order > SWZ_ORDER_SLOPE_32) return SWZ_EINVAL;
     swz_plan_info pl;
-    const int st = make_plan(0, rows, cols, elem_bytes, SWZ_LAYOUT_SWIZZLE, read_kind, nullptr, true, true, &pl);
+    const int st = make_plan(0, rows, cols, elem_bytes, SWZ_LAYOUT_SWIZZLE, read_kind, nullptr,
+                             pitch16(rows, elem_bytes), pitch16(cols, elem_bytes), &pl);
     if (st != SWZ_OK) return st;
     std::lock_guard<std::mutex> lock(g_order_mu);
     const ShapeKey key{pl.read_kind, batch, rows, cols};
@@ -348,7 +359,8 @@ SWZ_API int swz_get_tile_order(int64_t batch, int64_t rows, int64_t cols, int32_
                                int32_t* order) {
     if (!order || batch < 0 || rows < 0 || cols < 0) return SWZ_EINVAL;
     swz_plan_info pl;
-    const int st = make_plan(0, rows, cols, elem_bytes, SWZ_LAYOUT_SWIZZLE, read_kind, nullptr, true, true, &pl);
+    const int st = make_plan(0, rows, cols, elem_bytes, SWZ_LAYOUT_SWIZZLE, read_kind, nullptr,
+                             pitch16(rows, elem_bytes), pitch16(cols, elem_bytes), &pl);
     if (st != SWZ_OK) return st;
     *order = pinned_order(pl.read_kind, batch, rows, cols);
     return SWZ_OK;
@@ -360,7 +372,9 @@ SWZ_API int swz_tune_tile_order(const void* d_src, void* d_dst, int64_t batch, i
     if (!chosen || reps < 1 || reps > 1000) return SWZ_EINVAL;
     if (batch < 0 || rows < 0 || cols < 0) return SWZ_EINVAL;
     swz_plan_info pl;
-    int st = make_plan(0, rows, cols, elem_bytes, layout, read_kind, p_or_null, true, true, &pl);
+    const auto ps = reinterpret_cast<uintptr_t>(d_src), pd = reinterpret_cast<uintptr_t>(d_dst);
+    int st = make_plan(0, rows, cols, elem_bytes, layout, read_kind, p_or_null,
+                       ps % 16 == 0 && pd % 16 == 0 && pitch16(rows, elem_bytes), pitch16(cols, elem_bytes), &pl);
     if (st != SWZ_OK) return st;
     int64_t n, n2, bytes;
     if (!mul_ok(batch, rows, &n) || !mul_ok(n, cols, &n2) || !mul_ok(n2, elem_bytes, &bytes)) return SWZ_EINVAL;
