@@ -711,3 +711,31 @@ def test_reference_copy():
         T.swz_copy(src, dst, nbytes)
         torch.cuda.synchronize()
         assert torch.equal(src, dst), nbytes
+
+
+@pytest.mark.parametrize("esz", [4, 2, 1])
+def test_offset_pointers_through_the_xcd_grouped_grid(esz):
+    """Both pointers 1 to 32 bytes past a 64-byte line (element multiples),
+    from 2,000 rows: every output row then starts off the 64-byte pieces, so
+    the launches take the XCD-grouped grid (aligned block grid for 16 and 32
+    bytes, the element path's for the others; bytes 1 and 2 bytes off keep
+    the plain grid), on matrices with edge tiles and of whole tiles only;
+    every layout of the register fill."""
+    kind = {4: T.READ_SCALAR_COL, 2: T.READ_B64_TR16, 1: T.READ_B64_TR8}[esz]
+    shapes = ((2048, 2048), (2051, 1000)) if esz == 4 else ((2048, 2048), (2083, 700))
+    for rows, cols in shapes:
+        a = GEN[esz](rows, cols, seed=rows + cols + esz)
+        want = O.transpose(a)
+        flat = a.reshape(-1)
+        for off in sorted({1, 2, 4, 16, 32} - {1, 2} if esz == 4 else {1, 2, 4, 16, 32} - ({1} if esz == 2 else set())):
+            n = off // esz  # elements before the matrix in both buffers
+            for layout in LAYOUTS:
+                announce("offset pointers", esz, (rows, cols), off, layout)
+                src = to_dev(np.concatenate([np.zeros(n + 64 // esz, a.dtype), flat]))
+                dst = torch.zeros_like(src)
+                s0 = 64 // esz + n  # 64 bytes in, then the offset
+                T.swz_transpose(src[s0:], dst[s0:], rows, cols, esz, layout, kind)
+                torch.cuda.synchronize()
+                got = from_dev(dst, a)
+                assert np.array_equal(got[s0:].reshape(cols, rows), want), (esz, (rows, cols), off, layout)
+                assert not got[:s0].any()

@@ -1022,6 +1022,21 @@ void launch_chunks(int64_t n, F launch) {
     for (int64_t t0 = 0; t0 < n; t0 += kMaxGrid) launch(t0, n - t0 < kMaxGrid ? n - t0 : kMaxGrid);
 }
 
+// Whether the output rows of a job are not whole 64-byte pieces: their
+// pitch (partial_line_output), or, from the same 2,000 rows, the output
+// pointer, which puts every output row off the pieces alike.  Measured with
+// both pointers 4 or 16 bytes off (share of a copy, the plain grid against
+// the XCD-grouped one): fp32 5760^2 0.44 -> 0.64 and 0.43 -> 0.67, 4096^2
+// 0.44 -> 0.53 and 0.45 -> 0.52; 16-bit 8192^2 0.32 -> 0.43 and 0.45 ->
+// 0.52; bytes 8192^2 0.39 -> 0.46 and 0.38 -> 0.47, but bytes whose output
+// pointer is not 4-byte aligned lost (0.40 -> 0.37), so those keep the
+// plain grid.
+template <int ESZ>
+bool partial_lines(const ConvertJob& j) {
+    const uintptr_t d = reinterpret_cast<uintptr_t>(j.dst);
+    return partial_line_output(j.rows, ESZ) || (j.rows >= 2000 && d % 64 != 0 && (ESZ > 1 || d % 4 == 0));
+}
+
 template <int KIND, int FILL, bool ALIGNED>
 void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64_t n_tiles, hipStream_t stream) {
     using K = Kind<KIND>;
@@ -1049,14 +1064,18 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
         const unsigned inner_pad =
             occupancy_pad_to(SR * SC * LdsTile<KIND, FILL>::BYTES, interior_occupancy_limit<KIND>());
         const int64_t blocks_r = ceil_div(tiles_r, SR), blocks_c = ceil_div(tiles_c, SC);
-        if ((inner_r != tiles_r || inner_c != tiles_c) && fp.full_r > 0 && fp.full_c > 0 &&
+        // output rows off the 64-byte pieces: the XCD-grouped block grid,
+        // with or without edge tiles
+        bool xcd = false;
+        if constexpr (FILL != kDirect && !is_narrow(KIND)) xcd = partial_lines<K::ESZ>(j);
+        if ((inner_r != tiles_r || inner_c != tiles_c || xcd) && fp.full_r > 0 && fp.full_c > 0 &&
             fits_3d(blocks_r, blocks_c, j.batch, K::NT * SR * SC)) {
-            // edge tiles: all tiles in one launch of blocks
+            // edge tiles (or partial output lines): all tiles in one launch of blocks
             const dim3 grid(static_cast<unsigned>(blocks_r), static_cast<unsigned>(blocks_c),
                             static_cast<unsigned>(j.batch));
             const auto a = args(static_cast<uint32_t>(blocks_c), 0, fp.full_r, fp.full_c);
             if constexpr (FILL != kDirect && !is_narrow(KIND)) {
-                if (partial_line_output(j.rows, K::ESZ)) {
+                if (xcd) {
                     std::apply([&](auto... v) {
                         hipLaunchKernelGGL((k_convert<KIND, FILL, true, kBlocksXcd>), grid, dim3(K::NT * SR * SC),
                                            inner_pad, stream, v...);
@@ -1091,7 +1110,7 @@ void launch_variant(const ConvertJob& j, int64_t tiles_r, int64_t tiles_c, int64
                             static_cast<unsigned>(j.batch));
             const auto a = args(static_cast<uint32_t>(tiles_c), 0, fp.full_r, fp.full_c);
             if constexpr (!is_narrow(KIND)) {
-                if (partial_line_output(j.rows, K::ESZ)) {
+                if (partial_lines<K::ESZ>(j)) {
                     std::apply([&](auto... v) {
                         hipLaunchKernelGGL((k_convert<KIND, FILL, false, kAll3DXcd>), grid, block, lds_pad, stream,
                                            v...);
