@@ -144,7 +144,9 @@ enum swz_layout {
  *               1 to 19), and for the power-of-two widths below whose output
  *               rows or pointers are not 16-byte aligned (4-byte elements,
  *               2-byte of 8 to 32 columns, 1-byte of 64: the narrow kinds
- *               would move them element by element); otherwise 4-byte ->
+ *               would move them element by element), in the SWIZZLE and
+ *               PLAIN layouts (PAD and SWIZZLE_DIRECT keep the kinds below);
+ *               otherwise 4-byte ->
  *               NARROW<cols> when cols is 1,
  *               2, 4, 8 or 16, else SCALAR_COL; 2-byte -> HNARROW<cols> when
  *               cols is a power of two up to 32, else B64_TR16 when

@@ -595,6 +595,12 @@ def test_narrow_kind_validation():
         assert T.swz_plan(0, 4093, c, esz, "swizzle")["read_kind"] == kind, (esz, c)
         assert T.swz_plan(0, 4096, c, esz, "swizzle")["read_kind"] != T.READ_ROWS, (esz, c)  # aligned rows
     assert T.swz_get_tile_order(1, 4093, 8, 4) == T.ORDER_DIAGONAL  # resolves to the flat-row kind too
+    # the flat-row kind has no padded or direct layout: AUTO keeps the tile and narrow kinds for those
+    assert T.swz_plan(0, 1000, 3, 4, "pad")["read_kind"] == T.READ_SCALAR_COL
+    assert T.swz_plan(0, 1000, 100, 2, "pad")["read_kind"] == T.READ_B128_8X8
+    assert T.swz_plan(0, 4093, 8, 4, "pad")["read_kind"] == T.READ_NARROW8
+    assert T.swz_plan(0, 1024, 12, 4, "direct")["read_kind"] == T.READ_SCALAR_COL  # 16-byte pitches: direct fill
+    assert f(A, B, 0, 1000, 3, 4, T.LAYOUT_PAD, T.READ_AUTO, None, None) == T.SWZ_OK  # nothing to move: no launch
     assert f(A, B, 1, 4093, 8, 4, T.LAYOUT_SWIZZLE_DIRECT, T.READ_NARROW8, None, None) == EUNSUP
     # the flat-offset swizzle spans rows: Swizzle<5,0,5> on a 128x8 tile XORs
     # row bits 2-6 into the element bits (the pages' int num[32][8] example)

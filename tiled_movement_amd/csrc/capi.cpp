@@ -106,7 +106,10 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
             // 0.73-1.0)
             const bool unaligned_pow2 =
                 narrow && !aligned_out && (esz == 4 || (esz == 2 && cols >= 8) || (esz == 1 && cols == 64));
-            if (flat_rows || unaligned_pow2)
+            // (the flat-row kind has no padded or direct layout: those keep
+            // the tile kinds)
+            const bool rows_layout = layout == SWZ_LAYOUT_SWIZZLE || layout == SWZ_LAYOUT_PLAIN;
+            if ((flat_rows || unaligned_pow2) && rows_layout)
                 kind = SWZ_READ_ROWS;
             else if (esz == 4)
                 kind = narrow ? SWZ_READ_NARROW1 + lc : SWZ_READ_SCALAR_COL;
