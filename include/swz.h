@@ -152,7 +152,10 @@ enum swz_layout {
  *               cols is a power of two up to 32, else B64_TR16 when
  *               cols <= 64, B128_8X8 when cols <= 128, B64_TR16 when
  *               cols <= 256 and B64_4X4 above (the faster of the two 64x64
- *               kinds at those widths); 1-byte -> BNARROW<cols> when cols is
+ *               kinds at those widths), except B64_TR16 above 256 columns
+ *               for an even number of rows whose pitches or pointers are off
+ *               16 bytes or whose output rows are off the 64-byte lines;
+ *               1-byte -> BNARROW<cols> when cols is
  *               a power of two up to 64, else B64_TR8. */
 /* The read kind is an argument of its own (read_kind, just before
  * p_or_null, in swz_transpose, swz_convert_layout, swz_tune_tile_order and

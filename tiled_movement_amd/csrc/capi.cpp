@@ -118,7 +118,15 @@ int make_plan(int op, int64_t rows, int64_t cols, int32_t esz, int32_t layout, i
                        : cols <= 64  ? SWZ_READ_B64_TR16
                        : cols <= 128 ? SWZ_READ_B128_8X8
                        : cols <= 256 ? SWZ_READ_B64_TR16
-                                     : SWZ_READ_B64_4X4;
+                       : rows % 2 == 0 && (!aligned_out || !aligned_in || swz::partial_line_output(rows, esz))
+                           ? SWZ_READ_B64_TR16  // see below
+                           : SWZ_READ_B64_4X4;
+            // (Above 256 columns, for an even number of rows whose pitches
+            // or pointers are off 16 bytes or whose output rows are off the
+            // 64-byte lines, the transpose read ran faster: 4096 x 4100 0.81
+            // -> 0.87 of a copy, 4100 x 4096 0.69 -> 0.73, 67108 x 500 0.63
+            // -> 0.66, 111848 x 300 0.53 -> 0.56; with an odd number of rows
+            // the 4x4 reads stay ahead: 5801 x 5801 0.67 against 0.56.)
             else
                 kind = narrow ? SWZ_READ_BNARROW1 + lc : SWZ_READ_B64_TR8;
         }
