@@ -308,8 +308,11 @@ enum swz_tile_order {
 /* Pin the tile order of later swz_transpose / swz_convert_layout calls of
  * this shape (batch, rows, cols, elem_bytes, read kind after AUTO is
  * resolved), in every layout; order = -1 removes the entry (back to the
- * shape's default order).  Host only; the table is shared by all threads
- * and devices of the process.
+ * shape's default order).  AUTO is resolved here as swz_plan does, for
+ * 16-byte aligned pointers; a call whose pointers are not resolves AUTO
+ * with them and may land on another kind, whose own entry then applies
+ * (swz_tune_tile_order resolves with its buffers' pointers).  Host only;
+ * the table is shared by all threads and devices of the process.
  * Errors: SWZ_EINVAL for negative sizes, an order outside -1..6, or an
  * element size / read kind that swz_convert_layout would refuse. */
 int swz_set_tile_order(int64_t batch, int64_t rows, int64_t cols, int32_t elem_bytes, int32_t read_kind,
